@@ -1,0 +1,190 @@
+"""Throughput of the KDA chunked forward on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload headline]
+
+A step is one kda_chunk_fwd call over the whole workload (gate, in-chunk
+tiles, UT/WY solve, inter-chunk scan, outputs and statistics), inputs already
+resident in HBM.  Prints ONE JSON line on stdout; diagnostics go to stderr.
+
+The default workload is B=1, H=16, T=65536, dk=dv=128, bf16, g_min=-5,
+chunk 16, S0 = 0 (synthetic inputs, seeded).  `roofline` uses the algorithmic
+bytes of one launch (q, k, v, w, beta read, o written: 1282 B per token-head at
+d = 128 in bf16, plus the fp32 final state) over the main kernel's average
+duration, timed with HIP events recorded on the launch stream by the library.
+`cpu_baseline` times the fp64 oracle on the host on a bounded sample of the
+same workload (all heads, the first tokens of the sequence).
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "KDA chunk-fwd tokens/s (H16,d128,T64K,bf16) + % of MFMA/HBM roofline"
+HBM_PEAK_GBS = 8000.0
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def algorithmic_bytes(wl) -> int:
+    esz = 2 if wl.dtype == "bf16" else 4
+    per_token_head = (3 * wl.dk + 2 * wl.dv) * esz + esz       # q, k, w, v in; o out; beta in
+    state = wl.B * wl.H * wl.dk * wl.dv * 4                      # S_final out
+    if wl.s0_sd is not None:
+        state *= 2                                               # S0 in
+    return wl.token_heads * per_token_head + state
+
+
+def mfma_flops(wl) -> float:
+    """Matrix-core work of the chunk-16 form per launch (2 flops per multiply-add):
+    per chunk, Q K^T-style tiles (2 x C*C*dk), W and U~ (C*C*dk + C*C*dv),
+    and the state products W S, Q S, K^T U (3 x C*dk*dv), plus P U (C*C*dv)."""
+    C = 16
+    per_chunk = 2 * (2 * C * C * wl.dk + C * C * wl.dk + C * C * wl.dv + 3 * C * wl.dk * wl.dv + C * C * wl.dv)
+    return per_chunk * wl.B * wl.H * math.ceil(wl.T / C)
+
+
+def cpu_baseline(inp, wl, target_s: float = 15.0):
+    import numpy as np
+    from chunked_gated_delta_amd import inputs as gen
+    from oracle import oracle as orc
+    try:
+        cores = len(os.sched_getaffinity(0))
+    except AttributeError:
+        cores = os.cpu_count() or 1
+    threads = max(1, min(cores, 16, wl.B * wl.H))
+    # sample: every (b, h), the first Ts tokens; Ts sized from a short calibration run
+    cal_T = min(wl.T, 512)
+    f = {k: (None if inp[k] is None else inp[k][:, :, :cal_T].float().cpu().numpy().astype(np.float64))
+         for k in ("q", "k", "v", "w", "beta")}
+    S0 = None if inp["S0"] is None else inp["S0"].cpu().numpy().astype(np.float64)
+    t0 = time.perf_counter()
+    orc.kda_reference(f["q"], f["k"], f["v"], f["w"], f["beta"], S0, wl.g_min, nthreads=threads)
+    cal = time.perf_counter() - t0
+    Ts = int(min(wl.T, max(cal_T, cal_T * target_s / max(cal, 1e-3))))
+    Ts = max(16, (Ts // 16) * 16)
+    f = {k: inp[k][:, :, :Ts].float().cpu().numpy().astype(np.float64) for k in ("q", "k", "v", "w", "beta")}
+    t0 = time.perf_counter()
+    orc.kda_reference(f["q"], f["k"], f["v"], f["w"], f["beta"], S0, wl.g_min, nthreads=threads)
+    dt = time.perf_counter() - t0
+    return {
+        "value": wl.B * Ts / dt,
+        "unit": "tokens/s",
+        "cores": threads,
+        "kind": "oracle",
+        "sample": f"all {wl.B * wl.H} (b,h) recurrences over the first {Ts} of {wl.T} tokens "
+                  f"(fp64 token-by-token, {threads} threads, {dt:.1f} s wall)",
+    }
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", default="headline")
+    ap.add_argument("--path", default="auto", choices=["auto", "vector", "mfma"])
+    ap.add_argument("--seed", type=int, default=0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--force-fallback", action="store_true")
+    ap.add_argument("--copy-calib", action="store_true",
+                    help="run only a plain device copy of known size (for scaling HBM counters)")
+    args = ap.parse_args()
+
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only (got --gpus {args.gpus}); this build has no multi-GPU path.",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    if args.copy_calib:
+        n = 1 << 30
+        x = torch.ones(n, dtype=torch.uint8, device="cuda")
+        y = torch.empty_like(x)
+        for _ in range(3):
+            y.copy_(x)
+        torch.cuda.synchronize()
+        log(f"copy_calib: copied {n} bytes x3")
+        return
+
+    from chunked_gated_delta_amd import HipEvent, chunk_fwd, decode_stats
+    from chunked_gated_delta_amd import inputs as gen
+
+    wl = gen.WORKLOADS[args.workload]
+    log(f"[bench] workload {wl}")
+    inp = gen.make_torch(wl, seed=args.seed, device="cuda")
+    torch.cuda.synchronize()
+    kw = dict(g_min=wl.g_min, path=args.path, force_fallback=args.force_fallback)
+    q, k, v, w, beta, S0 = (inp[n] for n in ("q", "k", "v", "w", "beta", "S0"))
+    o = torch.empty_like(v)
+    S = torch.empty((wl.B, wl.H, wl.dk, wl.dv), dtype=torch.float32, device="cuda")
+    st = None
+    for _ in range(args.warmup):
+        _, _, st = chunk_fwd(q, k, v, w, beta, S0, out=o, S_final=S, **kw)
+    torch.cuda.synchronize()
+    if st is not None:
+        log(f"[bench] warmup stats {decode_stats(st)}")
+
+    evs = [(HipEvent(), HipEvent()) for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        _, _, st = chunk_fwd(q, k, v, w, beta, S0, out=o, S_final=S, events=evs[i], **kw)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    kern_ms = [b.elapsed_ms(e) for b, e in evs]
+    kern_avg = sum(kern_ms) / len(kern_ms)
+    stats = decode_stats(st)
+    log(f"[bench] kernel ms: avg {kern_avg:.4f} min {min(kern_ms):.4f} max {max(kern_ms):.4f}; wall/step "
+        f"{1e3 * wall / args.steps:.4f} ms; stats {stats}")
+
+    ms_per_step = 1e3 * wall / args.steps
+    tokens = wl.B * wl.T
+    value = tokens / (wall / args.steps)
+    abytes = algorithmic_bytes(wl)
+    achieved = abytes / (kern_avg * 1e-3) / 1e9
+    roofline = {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
+                "bytes_per_launch": abytes, "kernel_ms": round(kern_avg, 5),
+                "mfma_tflops": round(mfma_flops(wl) / (kern_avg * 1e-3) / 1e12, 2)}
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        log("[bench] timing the fp64 oracle on the host ...")
+        cpu = cpu_baseline(inp, wl)
+        log(f"[bench] cpu_baseline {cpu}")
+
+    line = {
+        "metric": METRIC,
+        "value": round(value, 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16" if wl.dtype == "bf16" else "f32",
+        "data": "synthetic",
+        "config": {"workload": wl.name, "B": wl.B, "H": wl.H, "T": wl.T, "dk": wl.dk, "dv": wl.dv,
+                   "chunk": wl.chunk, "g_min": wl.g_min if math.isfinite(wl.g_min) else "-inf",
+                   "path": args.path, "parallelism": "single-gpu"},
+        "roofline": roofline,
+        "cpu_baseline": cpu,
+        "stats": stats,
+    }
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

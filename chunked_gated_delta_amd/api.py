@@ -1,0 +1,143 @@
+"""torch-facing wrappers over libkda.so.  Argument marshalling only: every
+step of the computation runs in the library's HIP kernels.  torch provides the
+device memory (outputs, workspace, statistics) and the stream."""
+from __future__ import annotations
+
+import ctypes
+import math
+
+import torch
+
+from . import _lib
+from ._lib import KdaError, KdaOpts, KdaShape
+
+_PATHS = {"auto": 0, "vector": 1, "mfma": 2}
+
+
+def _dtype_code(t: torch.Tensor) -> int:
+    if t.dtype == torch.bfloat16:
+        return _lib.DTYPE_BF16
+    if t.dtype == torch.float32:
+        return _lib.DTYPE_F32
+    raise TypeError(f"unsupported dtype {t.dtype}: use torch.bfloat16 or torch.float32")
+
+
+def _ptr(t):
+    if t is None:
+        return None
+    return ctypes.c_void_p(t.data_ptr()) if t.numel() > 0 else None
+
+
+def _check(t: torch.Tensor, name: str, shape, dtype, device):
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch tensor")
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
+    if t.dtype != dtype:
+        raise TypeError(f"{name} has dtype {t.dtype}, expected {dtype}")
+    if t.device != device:
+        raise ValueError(f"{name} is on {t.device}, expected {device}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+
+
+def make_shape(B, H, T, dk, dv, dtype_code) -> KdaShape:
+    return KdaShape(int(B), int(H), int(T), int(dk), int(dv), int(dtype_code), 0)
+
+
+def workspace_bytes(B, H, T, dk, dv, dtype=torch.bfloat16, chunk=16) -> int:
+    code = _lib.DTYPE_BF16 if dtype == torch.bfloat16 else _lib.DTYPE_F32
+    return _lib.workspace_bytes(make_shape(B, H, T, dk, dv, code), chunk)
+
+
+def chunk_fwd(q, k, v, w, beta, S0=None, g_min: float = -5.0, chunk: int = 16, *,
+              out=None, S_final=None, stats: bool = True, workspace=None, stream=None,
+              disable_fallback: bool = False, force_fallback: bool = False,
+              path: str = "auto", events=None):
+    """KDA chunked forward through kda_chunk_fwd_ex.
+
+    q, k, w: [B,H,T,dk]; v: [B,H,T,dv]; beta: [B,H,T] (all bf16 or all fp32,
+    on one GPU); S0: optional fp32 [B,H,dk,dv].  g_min = -inf selects the
+    unbounded gate.  Returns (o, S_final, stats) with stats an int32[4] device
+    tensor (see decode_stats) or None.  Asynchronous on `stream` (default: the
+    current torch stream).  `events` = (begin, end) HipEvent pair recorded
+    around the main kernel.
+    """
+    if q.dim() != 4:
+        raise ValueError("q must be [B,H,T,dk]")
+    B, H, T, dk = q.shape
+    dv = v.shape[-1]
+    dt = q.dtype
+    dev = q.device
+    if dev.type != "cuda":
+        raise ValueError("inputs must live on a GPU (the library has no CPU path)")
+    _check(q, "q", (B, H, T, dk), dt, dev)
+    _check(k, "k", (B, H, T, dk), dt, dev)
+    _check(w, "w", (B, H, T, dk), dt, dev)
+    _check(v, "v", (B, H, T, dv), dt, dev)
+    _check(beta, "beta", (B, H, T), dt, dev)
+    if S0 is not None:
+        _check(S0, "S0", (B, H, dk, dv), torch.float32, dev)
+    if out is None:
+        out = torch.empty((B, H, T, dv), dtype=dt, device=dev)
+    else:
+        _check(out, "out", (B, H, T, dv), dt, dev)
+    if S_final is None:
+        S_final = torch.empty((B, H, dk, dv), dtype=torch.float32, device=dev)
+    else:
+        _check(S_final, "S_final", (B, H, dk, dv), torch.float32, dev)
+    shape = make_shape(B, H, T, dk, dv, _dtype_code(q))
+    ws_need = _lib.workspace_bytes(shape, chunk)
+    if workspace is None and ws_need > 0:
+        workspace = torch.empty(ws_need, dtype=torch.uint8, device=dev)
+    st = torch.empty(4, dtype=torch.int32, device=dev) if stats else None
+    if stream is None:
+        stream = torch.cuda.current_stream(dev)
+    opts = KdaOpts(int(bool(disable_fallback)), int(bool(force_fallback)), _PATHS[path], 0,
+                   events[0].handle if events else None, events[1].handle if events else None)
+    with torch.cuda.device(dev):
+        rc = _lib.load().kda_chunk_fwd_ex(
+            _ptr(q), _ptr(k), _ptr(v), _ptr(w), _ptr(beta), _ptr(S0),
+            ctypes.c_float(g_min), int(chunk), ctypes.byref(shape),
+            _ptr(out), _ptr(S_final), _ptr(workspace),
+            0 if workspace is None else workspace.numel() * workspace.element_size(),
+            _ptr(st), ctypes.c_void_p(stream.cuda_stream), ctypes.byref(opts))
+    if rc != 0:
+        raise KdaError(rc, "kda_chunk_fwd_ex", _lib.last_hip_error() if rc == _lib.KDA_ERR_HIP else "")
+    return out, S_final, st
+
+
+def decode_stats(st: torch.Tensor) -> dict:
+    """int32[4] device tensor -> dict (synchronises)."""
+    a = st.cpu()
+    return {
+        "n_chunks": int(a[0].item()) & 0xFFFFFFFF,
+        "n_flagged": int(a[1].item()) & 0xFFFFFFFF,
+        "n_nonfinite": int(a[2].item()) & 0xFFFFFFFF,
+        "min_span": float(a[3:4].view(torch.float32).item()),
+    }
+
+
+def gate_prefix(w, g_min: float = -5.0, chunk: int = 16, stream=None):
+    """Gate / in-chunk prefix stage alone: returns (g, G, span, flags) device tensors."""
+    B, H, T, dk = w.shape
+    dev = w.device
+    NC = (T + chunk - 1) // chunk
+    g = torch.empty((B, H, T, dk), dtype=torch.float32, device=dev)
+    G = torch.empty_like(g)
+    span = torch.empty((B, H, NC), dtype=torch.float32, device=dev)
+    flags = torch.empty((B, H, NC), dtype=torch.uint8, device=dev)
+    shape = make_shape(B, H, T, dk, dk, _dtype_code(w))
+    if stream is None:
+        stream = torch.cuda.current_stream(dev)
+    with torch.cuda.device(dev):
+        rc = _lib.load().kda_gate_prefix(_ptr(w), ctypes.c_float(g_min), int(chunk), ctypes.byref(shape),
+                                         _ptr(g), _ptr(G), _ptr(span), _ptr(flags),
+                                         ctypes.c_void_p(stream.cuda_stream))
+    if rc != 0:
+        raise KdaError(rc, "kda_gate_prefix", _lib.last_hip_error() if rc == _lib.KDA_ERR_HIP else "")
+    return g, G, span, flags
+
+
+def is_unbounded(g_min: float) -> bool:
+    return math.isinf(g_min) and g_min < 0

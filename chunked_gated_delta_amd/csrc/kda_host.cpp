@@ -1,0 +1,207 @@
+// Host side of libkda.so: argument validation, path selection and launches.
+// Validation runs entirely on the host before any HIP call, so an invalid call
+// returns its error code without touching the device.
+#include <cmath>
+#include <cstdio>
+#include <cstring>
+
+#include "kda_internal.h"
+
+namespace {
+
+thread_local char g_last_hip_error[256] = "";
+
+int hip_fail(hipError_t e) {
+  std::snprintf(g_last_hip_error, sizeof(g_last_hip_error), "%s (%d)", hipGetErrorString(e), (int)e);
+  return KDA_ERR_HIP;
+}
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+struct Range {
+  uintptr_t lo, hi;  // [lo, hi)
+};
+
+Range range_of(const void* p, int64_t bytes) {
+  uintptr_t lo = reinterpret_cast<uintptr_t>(p);
+  return Range{lo, lo + (uintptr_t)bytes};
+}
+
+bool overlap(Range a, Range b) { return a.lo < b.hi && b.lo < a.hi && a.hi > a.lo && b.hi > b.lo; }
+
+// B,H,T,dk,dv sanity and overflow guard (every tensor stays below 2^46 bytes)
+int check_shape(const kda_shape_t* sh) {
+  if (!sh) return KDA_ERR_NULL;
+  if (sh->B < 1 || sh->H < 1 || sh->T < 0 || sh->dk < 1 || sh->dv < 1) return KDA_ERR_SHAPE;
+  const int64_t lim = (int64_t)1 << 44;
+  if (sh->B > lim || sh->H > lim || sh->T > lim || sh->dk > 4096 || sh->dv > 4096) return KDA_ERR_SHAPE;
+  const double elems = (double)sh->B * (double)sh->H * (double)sh->T * (double)(sh->dk > sh->dv ? sh->dk : sh->dv);
+  if (elems * 4.0 > (double)((int64_t)1 << 46)) return KDA_ERR_SHAPE;
+  if ((double)sh->B * sh->H * ((sh->T + 15) / 16) >= 4294967295.0) return KDA_ERR_SHAPE;  // 32-bit chunk counters
+  if (sh->dtype != KDA_DTYPE_F32 && sh->dtype != KDA_DTYPE_BF16) return KDA_ERR_UNSUPPORTED;
+  if (sh->reserved != 0) return KDA_ERR_ARG;
+  auto ok_dim = [](int64_t d) { return d == 32 || d == 64 || d == 128; };
+  if (!ok_dim(sh->dk) || !ok_dim(sh->dv)) return KDA_ERR_UNSUPPORTED;
+  return KDA_OK;
+}
+
+int check_gmin(float g_min) {
+  if (std::isnan(g_min)) return KDA_ERR_ARG;
+  if (g_min > 0.f) return KDA_ERR_ARG;
+  if (std::isinf(g_min) && g_min > 0.f) return KDA_ERR_ARG;
+  return KDA_OK;
+}
+
+int pick_path(const kda::Params& p, const kda_opts_t* opts) {
+  const int req = opts ? opts->path : 0;
+  if (req == 1) return 1;
+  if (req == 2) return kda::mfma_supported(p) ? 2 : -1;
+  return kda::mfma_supported(p) ? 2 : 1;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* kda_strerror(int code) {
+  switch (code) {
+    case KDA_OK: return "ok";
+    case KDA_ERR_NULL: return "a required pointer is NULL";
+    case KDA_ERR_SHAPE: return "invalid shape (B, H >= 1, T >= 0, dk, dv >= 1, sizes must not overflow)";
+    case KDA_ERR_UNSUPPORTED: return "unsupported configuration (chunk must be 16; dk, dv in {32, 64, 128}; dtype f32 or bf16; path)";
+    case KDA_ERR_ARG: return "invalid argument (g_min NaN or > 0, misaligned pointer, overlapping buffers, workspace too small, reserved field set)";
+    case KDA_ERR_HIP: return "HIP runtime error (see kda_last_hip_error)";
+    default: return "unknown error code";
+  }
+}
+
+const char* kda_last_hip_error(void) { return g_last_hip_error; }
+
+int kda_version(void) { return KDA_VERSION; }
+
+size_t kda_workspace_bytes(const kda_shape_t* shape, int chunk) {
+  if (check_shape(shape) != KDA_OK || chunk != kda::kChunk) return (size_t)-1;
+  if (shape->dtype == KDA_DTYPE_BF16)
+    return kda::mfma_workspace_bytes(shape->B, shape->H, shape->T, shape->dk, shape->dv);
+  return 0;
+}
+
+int kda_chunk_fwd_ex(const void* q, const void* k, const void* v, const void* w, const void* beta,
+                     const float* S0, float g_min, int chunk, const kda_shape_t* shape,
+                     void* o, float* S_final, void* workspace, size_t workspace_bytes,
+                     kda_stats_t* stats, void* stream, const kda_opts_t* opts) {
+  int rc = check_shape(shape);
+  if (rc != KDA_OK) return rc;
+  if (chunk != kda::kChunk) return KDA_ERR_UNSUPPORTED;
+  if ((rc = check_gmin(g_min)) != KDA_OK) return rc;
+  if (opts) {
+    if (opts->reserved != 0) return KDA_ERR_ARG;
+    if (opts->disable_fallback && opts->force_fallback) return KDA_ERR_ARG;
+    if (opts->path < 0 || opts->path > 2) return KDA_ERR_UNSUPPORTED;
+  }
+  const int64_t B = shape->B, H = shape->H, T = shape->T, dk = shape->dk, dv = shape->dv;
+  const int64_t esz = shape->dtype == KDA_DTYPE_BF16 ? 2 : 4;
+  if (!S_final) return KDA_ERR_NULL;
+  if (T > 0 && (!q || !k || !v || !w || !beta || !o)) return KDA_ERR_NULL;
+
+  const void* ptrs[] = {q, k, v, w, beta, S0, o, S_final, workspace, stats};
+  for (const void* p : ptrs)
+    if (p && !aligned16(p)) return KDA_ERR_ARG;
+
+  // overlap rules: outputs (o, S_final, workspace, stats) must not touch inputs or each other,
+  // except S_final == S0 exactly
+  const int64_t BH = B * H;
+  const Range r_q = range_of(q, T > 0 ? BH * T * dk * esz : 0);
+  const Range r_k = range_of(k, T > 0 ? BH * T * dk * esz : 0);
+  const Range r_v = range_of(v, T > 0 ? BH * T * dv * esz : 0);
+  const Range r_w = range_of(w, T > 0 ? BH * T * dk * esz : 0);
+  const Range r_b = range_of(beta, T > 0 ? BH * T * esz : 0);
+  const Range r_s0 = range_of(S0, S0 ? BH * dk * dv * 4 : 0);
+  const Range r_o = range_of(o, T > 0 ? BH * T * dv * esz : 0);
+  const Range r_sf = range_of(S_final, BH * dk * dv * 4);
+  const size_t need_ws = kda_workspace_bytes(shape, chunk);
+  const Range r_ws = range_of(workspace, workspace ? (int64_t)workspace_bytes : 0);
+  const Range r_st = range_of(stats, stats ? (int64_t)sizeof(kda_stats_t) : 0);
+  const Range ins[] = {r_q, r_k, r_v, r_w, r_b};
+  const Range outs[] = {r_o, r_sf, r_ws, r_st};
+  for (const Range& a : outs)
+    for (const Range& b : ins)
+      if (overlap(a, b)) return KDA_ERR_ARG;
+  for (int i = 0; i < 4; ++i)
+    for (int j = i + 1; j < 4; ++j)
+      if (overlap(outs[i], outs[j])) return KDA_ERR_ARG;
+  if (S0 && S0 != S_final && overlap(r_s0, r_sf)) return KDA_ERR_ARG;
+  if (overlap(r_s0, r_o) || overlap(r_s0, r_ws) || overlap(r_s0, r_st)) return KDA_ERR_ARG;
+
+  kda::Params p{};
+  p.q = q; p.k = k; p.v = v; p.w = w; p.beta = beta; p.S0 = S0;
+  p.unbounded = std::isinf(g_min) ? 1 : 0;
+  p.g_min = p.unbounded ? 0.f : g_min;
+  p.B = B; p.H = H; p.T = T; p.dk = dk; p.dv = dv; p.dtype = shape->dtype;
+  p.o = o; p.S_final = S_final; p.workspace = workspace; p.workspace_bytes = workspace_bytes;
+  p.stats = stats;
+  p.disable_fallback = opts ? opts->disable_fallback : 0;
+  p.force_fallback = opts ? opts->force_fallback : 0;
+
+  const int path = T > 0 ? pick_path(p, opts) : 1;
+  if (path < 0) return KDA_ERR_UNSUPPORTED;
+  if (path == 2 && need_ws > 0 && (!workspace || workspace_bytes < need_ws)) return KDA_ERR_ARG;
+
+  // ---- launches (first HIP call of the entry point)
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  hipEvent_t ev0 = opts ? reinterpret_cast<hipEvent_t>(opts->ev_begin) : nullptr;
+  hipEvent_t ev1 = opts ? reinterpret_cast<hipEvent_t>(opts->ev_end) : nullptr;
+  hipError_t e;
+  if (stats && (e = kda::launch_stats_init(stats, s)) != hipSuccess) return hip_fail(e);
+  if (T == 0) {
+    if (ev0 && (e = hipEventRecord(ev0, s)) != hipSuccess) return hip_fail(e);
+    if ((e = kda::launch_state_copy(p, s)) != hipSuccess) return hip_fail(e);
+    if (ev1 && (e = hipEventRecord(ev1, s)) != hipSuccess) return hip_fail(e);
+    return KDA_OK;
+  }
+  if (path == 2) {
+    if ((e = kda::launch_mfma(p, s, ev0, ev1)) != hipSuccess) return hip_fail(e);
+  } else {
+    if (ev0 && (e = hipEventRecord(ev0, s)) != hipSuccess) return hip_fail(e);
+    if ((e = kda::launch_vec(p, s)) != hipSuccess) return hip_fail(e);
+    if (ev1 && (e = hipEventRecord(ev1, s)) != hipSuccess) return hip_fail(e);
+  }
+  return KDA_OK;
+}
+
+int kda_chunk_fwd(const void* q, const void* k, const void* v, const void* w, const void* beta,
+                  const float* S0, float g_min, int chunk, const kda_shape_t* shape,
+                  void* o, float* S_final, void* workspace, size_t workspace_bytes,
+                  kda_stats_t* stats, void* stream) {
+  return kda_chunk_fwd_ex(q, k, v, w, beta, S0, g_min, chunk, shape, o, S_final, workspace,
+                          workspace_bytes, stats, stream, nullptr);
+}
+
+int kda_gate_prefix(const void* w, float g_min, int chunk, const kda_shape_t* shape,
+                    float* g, float* G, float* span, uint8_t* flags, void* stream) {
+  int rc = check_shape(shape);
+  if (rc != KDA_OK) return rc;
+  if (chunk != kda::kChunk) return KDA_ERR_UNSUPPORTED;
+  if ((rc = check_gmin(g_min)) != KDA_OK) return rc;
+  const int64_t B = shape->B, H = shape->H, T = shape->T, dk = shape->dk;
+  if (T > 0 && !w) return KDA_ERR_NULL;
+  const void* ptrs[] = {w, g, G, span, flags};
+  for (const void* p : ptrs)
+    if (p && !aligned16(p)) return KDA_ERR_ARG;
+  const int64_t esz = shape->dtype == KDA_DTYPE_BF16 ? 2 : 4;
+  const int64_t NC = (T + 15) / 16;
+  const Range r_w = range_of(w, B * H * T * dk * esz);
+  const Range outs[] = {range_of(g, g ? B * H * T * dk * 4 : 0), range_of(G, G ? B * H * T * dk * 4 : 0),
+                        range_of(span, span ? B * H * NC * 4 : 0), range_of(flags, flags ? B * H * NC : 0)};
+  for (int i = 0; i < 4; ++i) {
+    if (overlap(outs[i], r_w)) return KDA_ERR_ARG;
+    for (int j = i + 1; j < 4; ++j)
+      if (overlap(outs[i], outs[j])) return KDA_ERR_ARG;
+  }
+  const int unbounded = std::isinf(g_min) ? 1 : 0;
+  hipError_t e = kda::launch_gate_prefix(w, unbounded ? 0.f : g_min, unbounded, B, H, T, dk, shape->dtype,
+                                         g, G, span, flags, reinterpret_cast<hipStream_t>(stream));
+  return e == hipSuccess ? KDA_OK : hip_fail(e);
+}
+
+}  // extern "C"

@@ -1,0 +1,74 @@
+// Internal declarations shared by the HIP sources of libkda.so (not installed, not part of the ABI).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "kda.h"
+
+namespace kda {
+
+constexpr int kChunk = 16;          // tokens per chunk (the tile the bounded gate is sized for)
+constexpr float kSpanLimit = -80.f; // 16 * g_min for g_min = -5: below it exp(-G) may overflow
+
+struct Params {
+  const void *q, *k, *v, *w, *beta;
+  const float* S0;
+  float g_min;      // used when !unbounded
+  int unbounded;    // 1: g = -softplus(w)
+  int64_t B, H, T, dk, dv;
+  int dtype;        // kda_dtype_t
+  void* o;
+  float* S_final;
+  void* workspace;
+  size_t workspace_bytes;
+  kda_stats_t* stats;
+  int disable_fallback, force_fallback;
+  __host__ __device__ int64_t n_chunks() const { return (T + kChunk - 1) / kChunk; }
+};
+
+// Launchers (each returns the hipError_t of its launch).
+hipError_t launch_stats_init(kda_stats_t* stats, hipStream_t s);
+hipError_t launch_state_copy(const Params& p, hipStream_t s);          // T == 0
+hipError_t launch_gate_prefix(const void* w, float g_min, int unbounded, int64_t B, int64_t H,
+                              int64_t T, int64_t dk, int dtype, float* g, float* G, float* span,
+                              uint8_t* flags, hipStream_t s);
+hipError_t launch_vec(const Params& p, hipStream_t s);                 // plain fp32 vector path
+bool mfma_supported(const Params& p);                                   // matrix-core path available?
+size_t mfma_workspace_bytes(int64_t B, int64_t H, int64_t T, int64_t dk, int64_t dv);
+hipError_t launch_mfma(const Params& p, hipStream_t s, hipEvent_t ev_begin, hipEvent_t ev_end);
+
+// ---------------------------------------------------------------- device helpers
+
+__device__ __forceinline__ float bf16_to_f32(uint16_t x) { return __uint_as_float((uint32_t)x << 16); }
+
+__device__ __forceinline__ uint16_t f32_to_bf16(float f) {  // round to nearest even, NaN kept quiet
+  uint32_t u = __float_as_uint(f);
+  if ((u & 0x7fffffffu) > 0x7f800000u) return (uint16_t)((u >> 16) | 0x40u);
+  u += 0x7fffu + ((u >> 16) & 1u);
+  return (uint16_t)(u >> 16);
+}
+
+template <typename T> __device__ __forceinline__ float load_f32(const T* p, int64_t i);
+template <> __device__ __forceinline__ float load_f32<float>(const float* p, int64_t i) { return p[i]; }
+template <> __device__ __forceinline__ float load_f32<uint16_t>(const uint16_t* p, int64_t i) { return bf16_to_f32(p[i]); }
+
+template <typename T> __device__ __forceinline__ void store_f32(T* p, int64_t i, float x);
+template <> __device__ __forceinline__ void store_f32<float>(float* p, int64_t i, float x) { p[i] = x; }
+template <> __device__ __forceinline__ void store_f32<uint16_t>(uint16_t* p, int64_t i, float x) { p[i] = f32_to_bf16(x); }
+
+// log-decay of one gate pre-activation: g_min * sigmoid(w), or -softplus(w)
+__device__ __forceinline__ float gate_f32(float w, float g_min, int unbounded) {
+  if (unbounded) return -(fmaxf(w, 0.f) + log1pf(expf(-fabsf(w))));
+  return g_min / (1.f + expf(-w));
+}
+
+__device__ __forceinline__ void atomic_min_float(float* addr, float v) {
+  if (v != v) return;
+  if (v >= 0.f) atomicMin(reinterpret_cast<int*>(addr), __float_as_int(v));
+  else atomicMax(reinterpret_cast<unsigned int*>(addr), __float_as_uint(v));
+}
+
+__device__ __forceinline__ bool not_finite(float x) { return !(fabsf(x) <= 3.402823466e38f); }
+
+}  // namespace kda

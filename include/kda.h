@@ -1,0 +1,166 @@
+/*
+ * kda.h -- C ABI of libkda.so: the chunk-parallel forward pass of Kimi Delta
+ * Attention (KDA) on AMD Instinct MI355X (gfx950).
+ *
+ * The operation (per batch b and head h, independently):
+ *
+ *   state S (dk x dv, fp32), starting at S0 (zeros when S0 is NULL);
+ *   for every token t:
+ *     g_t = g_min * sigmoid(w_t)          bounded log-decay, one value per key channel
+ *           or -softplus(w_t)             the unbounded form, when g_min = -INFINITY
+ *     S   = Diag(exp(g_t)) S              forget
+ *     u_t = beta_t (v_t - S^T k_t)        delta-rule correction
+ *     S   = S + k_t u_t^T                 write
+ *     o_t = S^T q_t                       read (inclusive of token t)
+ *   S_final = S.
+ *
+ * Sources.  "From Numerical Stability to Load Balancing: A Technical Breakdown
+ * of LLM Architecture Innovations", section 2.1: a fixed-shape state, decayed
+ * per step and written with key/value outer products; chunked evaluation with
+ * a serial recurrence between chunks and matrix products inside a chunk; the
+ * in-chunk scaling between positions i >= j is exp(G_i - G_j) with G the
+ * cumulative log-decay.  Section 2.2 of the same page, section 2.2 of
+ * "Architecting Long-Context LLMs ..." and of "Architecture Analysis of
+ * Ultra-Long Context Sparse MoE Models", and Breakthrough 1 part 2 of
+ * "Demystifying Trillion-Parameter MoE Models ...": the bounded gate
+ * g = g_min * sigmoid(w) with g_min = -5 keeps a 16-token chunk's span at or
+ * above -80, so its reciprocal scaling exp(80) stays finite and the diagonal
+ * tile runs as a dense matrix product.  The delta rule itself is only named on
+ * the pages (Delta networks / Delta Net-like / delta-rule-based models); the
+ * form above is the plainest reading with per-key-channel decay.
+ *
+ * Evaluation.  Chunks of 16 tokens.  Inside a chunk the library uses the
+ * exp(+-G) reciprocal form (dense tiles) when the chunk's span, the minimum
+ * over key channels of the chunk-local sum of g, is at or above -80; a chunk
+ * whose span falls below -80 (possible only with the unbounded gate or
+ * g_min < -5) is detected and evaluated with per-position-pair decay factors
+ * exp(G_r - G_j) instead (the per-position path the pages describe as the
+ * fallback implementations are forced into).
+ *
+ * Layouts.  All tensors are dense row-major with no padding:
+ *   q, k, w : [B, H, T, dk]      dtype = shape->dtype
+ *   v, o    : [B, H, T, dv]      dtype = shape->dtype
+ *   beta    : [B, H, T]          dtype = shape->dtype
+ *   S0, S_final : [B, H, dk, dv] always fp32
+ * bf16 means IEEE-754 binary32 truncated to its upper 16 bits; o is rounded to
+ * nearest-even.  The library applies no scaling or normalisation to q or k.
+ *
+ * Ownership and memory.  Every pointer argument (except `shape`, `opts` and
+ * the returned strings) is a DEVICE pointer on the current HIP device, owned
+ * by the caller and aligned to 16 bytes.  The library allocates nothing on
+ * these entry points: any scratch memory comes in through `workspace`.
+ * Outputs must not overlap inputs or each other, except that S_final may be
+ * exactly S0 (in-place state update).
+ *
+ * Errors.  Arguments are validated on the host before any HIP call; an invalid
+ * call returns a negative code and launches nothing.  Launches are
+ * asynchronous on `stream` (a hipStream_t; NULL is the default stream):
+ * faults inside kernels surface at the caller's next synchronisation.
+ */
+#ifndef KDA_H
+#define KDA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define KDA_VERSION 100 /* 1.0.0 */
+
+#if defined(__GNUC__) || defined(__clang__)
+#define KDA_API __attribute__((visibility("default")))
+#else
+#define KDA_API
+#endif
+
+typedef enum {
+  KDA_DTYPE_F32 = 0,  /* inputs and o in fp32; arithmetic in fp32 */
+  KDA_DTYPE_BF16 = 1  /* inputs and o in bf16; bf16 matrix-core operands, fp32 accumulation and state */
+} kda_dtype_t;
+
+typedef struct {
+  int64_t B, H, T, dk, dv; /* B, H >= 1; T >= 0; dk, dv in {32, 64, 128} */
+  int32_t dtype;           /* a kda_dtype_t */
+  int32_t reserved;        /* must be 0 */
+} kda_shape_t;
+
+/* Device-resident counters, written with atomics by the kernels of one call.
+ * The library resets them at the start of the call (stream-ordered).           */
+typedef struct {
+  uint32_t n_chunks;     /* B * H * ceil(T / 16) */
+  uint32_t n_flagged;    /* chunks whose span fell below -80 (detected, whatever path ran) */
+  uint32_t n_nonfinite;  /* non-finite values written to o or S_final */
+  float min_span;        /* minimum chunk span seen; +INFINITY when T = 0 */
+} kda_stats_t;
+
+/* Measurement knobs for kda_chunk_fwd_ex. Zero-initialised means "default". */
+typedef struct {
+  int32_t disable_fallback; /* 1: flagged chunks still take the dense exp(+-G) path (shows the overflow) */
+  int32_t force_fallback;   /* 1: every chunk takes the per-position path (measures its cost) */
+  int32_t path;             /* 0 auto, 1 the plain fp32 vector path, 2 the matrix-core path */
+  int32_t reserved;         /* must be 0 */
+  void* ev_begin;           /* optional hipEvent_t recorded on `stream` right before the main kernel */
+  void* ev_end;             /* optional hipEvent_t recorded on `stream` right after the main kernel */
+} kda_opts_t;
+
+enum {
+  KDA_OK = 0,
+  KDA_ERR_NULL = -1,        /* a required pointer is NULL */
+  KDA_ERR_SHAPE = -2,       /* B, H < 1, T < 0, dk or dv < 1, or sizes overflow */
+  KDA_ERR_UNSUPPORTED = -3, /* chunk != 16, dk or dv not in {32, 64, 128}, unknown dtype or path */
+  KDA_ERR_ARG = -4,         /* g_min NaN or > 0, misaligned pointer, forbidden overlap,
+                               workspace too small, non-zero reserved field, both opts set */
+  KDA_ERR_HIP = -5          /* a HIP call failed; kda_last_hip_error() has the text */
+};
+
+/* Forward pass.  Computes o and S_final as defined above.
+ *   g_min   finite and <= 0 selects g = g_min * sigmoid(w); -INFINITY selects
+ *           g = -softplus(w).  NaN or > 0 is KDA_ERR_ARG.
+ *   chunk   must be 16 (the tile the pages fix for g_min = -5).
+ *   S0      may be NULL (zero initial state).
+ *   workspace / workspace_bytes: device scratch of at least
+ *           kda_workspace_bytes(shape, chunk) bytes (may be NULL when that is 0).
+ *   stats   optional device pointer (NULL: no statistics).
+ *   stream  hipStream_t to launch on.
+ * When T = 0, o is not touched and S_final receives S0 (or zeros).         */
+KDA_API int kda_chunk_fwd(const void* q, const void* k, const void* v, const void* w, const void* beta,
+                  const float* S0, float g_min, int chunk, const kda_shape_t* shape,
+                  void* o, float* S_final, void* workspace, size_t workspace_bytes,
+                  kda_stats_t* stats, void* stream);
+
+/* Same as kda_chunk_fwd, with measurement options (opts may be NULL). */
+KDA_API int kda_chunk_fwd_ex(const void* q, const void* k, const void* v, const void* w, const void* beta,
+                     const float* S0, float g_min, int chunk, const kda_shape_t* shape,
+                     void* o, float* S_final, void* workspace, size_t workspace_bytes,
+                     kda_stats_t* stats, void* stream, const kda_opts_t* opts);
+
+/* Gate and in-chunk prefix stage on its own (for checking that stage).
+ * Outputs (device, fp32 unless noted):
+ *   g     [B,H,T,dk]   the per-step log-decay
+ *   G     [B,H,T,dk]   inclusive prefix of g, restarted at every 16-token chunk
+ *   span  [B,H,NC]     min over key channels of the chunk's total (NC = ceil(T/16))
+ *   flags [B,H,NC]     uint8: 1 when span < -80
+ * Any output pointer may be NULL to skip it.  Same validation and error codes. */
+KDA_API int kda_gate_prefix(const void* w, float g_min, int chunk, const kda_shape_t* shape,
+                    float* g, float* G, float* span, uint8_t* flags, void* stream);
+
+/* Scratch bytes kda_chunk_fwd needs for this shape (0 means none). Returns
+ * (size_t)-1 for an invalid shape or chunk. Host-only, no HIP call.          */
+KDA_API size_t kda_workspace_bytes(const kda_shape_t* shape, int chunk);
+
+/* Static description of an error code. Host-only. */
+KDA_API const char* kda_strerror(int code);
+
+/* Text of the last HIP error seen by this thread ("" if none). Host-only. */
+KDA_API const char* kda_last_hip_error(void);
+
+/* KDA_VERSION of the loaded library. Host-only. */
+KDA_API int kda_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* KDA_H */

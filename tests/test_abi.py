@@ -1,0 +1,136 @@
+"""The C ABI on the host: the library loads, exports what include/kda.h
+declares, and rejects invalid calls with the documented codes before any HIP
+call (so these run without a GPU)."""
+import ctypes
+import math
+
+import pytest
+
+from chunked_gated_delta_amd import _lib
+from chunked_gated_delta_amd._lib import KdaShape, KdaOpts
+
+lib = _lib.load()
+FAKE = 0x7F0000000000          # an aligned address validation never dereferences
+ST = 1 << 40                   # per-tensor stride between fake buffers (no overlaps)
+
+
+def ptrs(n=10):
+    return [ctypes.c_void_p(FAKE + i * ST) for i in range(n)]
+
+
+def shape(B=1, H=2, T=64, dk=128, dv=128, dtype=1, reserved=0):
+    return KdaShape(B, H, T, dk, dv, dtype, reserved)
+
+
+def call(sh=None, g_min=-5.0, chunk=16, ws_bytes=1 << 30, opts=None, **over):
+    p = ptrs()
+    args = dict(q=p[0], k=p[1], v=p[2], w=p[3], beta=p[4], S0=None, o=p[5], S_final=p[6],
+                workspace=p[7], stats=p[8])
+    args.update(over)
+    sh = shape() if sh is None else sh
+    return lib.kda_chunk_fwd_ex(args["q"], args["k"], args["v"], args["w"], args["beta"], args["S0"],
+                                ctypes.c_float(g_min), chunk, ctypes.byref(sh), args["o"], args["S_final"],
+                                args["workspace"], ws_bytes, args["stats"], None,
+                                ctypes.byref(opts) if opts is not None else None)
+
+
+def test_exports_every_declared_symbol():
+    names = _lib.declared_symbols()
+    assert {"kda_chunk_fwd", "kda_chunk_fwd_ex", "kda_workspace_bytes", "kda_strerror",
+            "kda_version", "kda_gate_prefix", "kda_last_hip_error"} <= set(names)
+    for n in names:
+        assert hasattr(lib, n), n
+
+
+def test_version_and_strings():
+    assert _lib.version() == 100
+    for code in (0, -1, -2, -3, -4, -5):
+        assert len(_lib.strerror(code)) >= 2
+    assert _lib.strerror(-99) == "unknown error code"
+    assert isinstance(_lib.last_hip_error(), str)
+
+
+def test_workspace_bytes():
+    assert lib.kda_workspace_bytes(ctypes.byref(shape(dtype=0)), 16) == 0
+    n = lib.kda_workspace_bytes(ctypes.byref(shape()), 16)
+    assert n < (1 << 40)
+    assert lib.kda_workspace_bytes(ctypes.byref(shape()), 32) == ctypes.c_size_t(-1).value
+    assert lib.kda_workspace_bytes(ctypes.byref(shape(dk=48)), 16) == ctypes.c_size_t(-1).value
+    assert lib.kda_workspace_bytes(None, 16) == ctypes.c_size_t(-1).value
+
+
+@pytest.mark.parametrize("sh,code", [
+    (shape(B=0), -2), (shape(H=0), -2), (shape(T=-1), -2), (shape(dk=0), -2), (shape(dv=-3), -2),
+    (shape(dk=48), -3), (shape(dv=256), -3), (shape(dtype=7), -3), (shape(reserved=1), -4),
+    (shape(B=1 << 30, H=1 << 30, T=1 << 30), -2)])
+def test_shape_errors(sh, code):
+    assert call(sh) == code
+
+
+def test_null_shape():
+    p = ptrs()
+    assert lib.kda_chunk_fwd(p[0], p[1], p[2], p[3], p[4], None, ctypes.c_float(-5.0), 16, None,
+                             p[5], p[6], p[7], 0, None, None) == -1
+
+
+@pytest.mark.parametrize("name", ["q", "k", "v", "w", "beta", "o", "S_final"])
+def test_null_pointers(name):
+    assert call(**{name: None}) == -1
+
+
+def test_null_inputs_allowed_when_empty():
+    # T = 0 needs only S_final; this reaches the launch, so only check the NULL rule on S_final here
+    assert call(shape(T=0), S_final=None, q=None, k=None, v=None, w=None, beta=None, o=None) == -1
+
+
+@pytest.mark.parametrize("chunk", [0, 8, 15, 17, 32, 64])
+def test_chunk_must_be_16(chunk):
+    assert call(chunk=chunk) == -3
+
+
+@pytest.mark.parametrize("g_min", [float("nan"), 0.5, 1e-30, float("inf")])
+def test_bad_g_min(g_min):
+    assert call(g_min=g_min) == -4
+
+
+def test_misaligned_pointer():
+    p = ptrs()
+    assert call(q=ctypes.c_void_p(p[0].value + 2)) == -4
+    assert call(S_final=ctypes.c_void_p(p[6].value + 8)) == -4
+
+
+def test_overlaps_rejected():
+    p = ptrs()
+    assert call(o=p[0]) == -4                                   # output aliases q
+    assert call(S_final=ctypes.c_void_p(p[2].value + 1024)) == -4   # S_final inside v
+    assert call(workspace=p[5]) == -4                            # workspace aliases o
+    assert call(stats=p[6]) == -4                                # stats aliases S_final
+    assert call(S0=ctypes.c_void_p(p[6].value + 16)) == -4       # S0 partly overlaps S_final
+
+
+def test_workspace_too_small():
+    need = lib.kda_workspace_bytes(ctypes.byref(shape()), 16)
+    if need == 0:
+        pytest.skip("this shape needs no workspace")
+    assert call(ws_bytes=need - 1) == -4
+    assert call(workspace=None, ws_bytes=0) == -4
+
+
+def test_opts_validation():
+    assert call(opts=KdaOpts(1, 1, 0, 0, None, None)) == -4     # both knobs
+    assert call(opts=KdaOpts(0, 0, 0, 5, None, None)) == -4     # reserved
+    assert call(opts=KdaOpts(0, 0, 7, 0, None, None)) == -3     # unknown path
+
+
+def test_gate_prefix_validation():
+    p = ptrs()
+    sh = shape()
+    f = lambda **kw: lib.kda_gate_prefix(kw.get("w", p[0]), ctypes.c_float(kw.get("g_min", -5.0)),
+                                         kw.get("chunk", 16), ctypes.byref(kw.get("sh", sh)),
+                                         kw.get("g", p[1]), kw.get("G", p[2]), kw.get("span", p[3]),
+                                         kw.get("flags", p[4]), None)
+    assert f(chunk=8) == -3
+    assert f(g_min=float("nan")) == -4
+    assert f(w=None) == -1
+    assert f(g=p[0]) == -4
+    assert f(sh=shape(dk=100)) == -3

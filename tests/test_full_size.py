@@ -1,0 +1,75 @@
+"""Parity at the workloads' full sizes, in the launch configuration bench.py
+times: the whole workload runs on the GPU; the oracle recomputes sampled
+(b, h) recurrences in full (each (b, h) is an independent recurrence, so a
+sampled head is checked over its whole sequence and final state)."""
+import numpy as np
+import pytest
+
+from chunked_gated_delta_amd import inputs as gen
+from oracle import oracle as orc
+from kda_testutil import TOL, rel_err, say
+
+pytestmark = pytest.mark.gpu
+torch = pytest.importorskip("torch")
+if not torch.cuda.is_available():
+    pytest.skip("no GPU", allow_module_level=True)
+
+
+def run_full(name, heads, seed=0, path="auto"):
+    from chunked_gated_delta_amd import chunk_fwd, decode_stats
+    wl = gen.WORKLOADS[name]
+    say(f"[case] full-size {wl} sampled heads {heads} path={path}")
+    inp = gen.make_torch(wl, seed=seed, device="cuda")
+    o, S, st = chunk_fwd(inp["q"], inp["k"], inp["v"], inp["w"], inp["beta"], inp["S0"],
+                         g_min=wl.g_min, path=path)
+    torch.cuda.synchronize()
+    stats = decode_stats(st)
+    say(f"   stats {stats}")
+    assert stats["n_chunks"] == wl.B * wl.H * ((wl.T + 15) // 16)
+    worst = (0.0, 0.0)
+    for (b, h) in heads:
+        f = gen.head_to_f64(inp, b, h)
+        o_ref, S_ref = orc.kda_reference(f["q"], f["k"], f["v"], f["w"], f["beta"], f["S0"], wl.g_min,
+                                         nthreads=1)
+        eo = rel_err(o[b:b + 1, h:h + 1].float().cpu().numpy(), o_ref)
+        es = rel_err(S[b:b + 1, h:h + 1].cpu().numpy(), S_ref)
+        say(f"   head ({b},{h}): err_o={eo:.3e} err_S={es:.3e}")
+        worst = (max(worst[0], eo), max(worst[1], es))
+    tol_o, tol_s = TOL[wl.dtype]
+    assert worst[0] <= tol_o and worst[1] <= tol_s
+    return wl, stats, inp
+
+
+def test_bf16_4k_full():
+    wl, stats, _ = run_full("bf16_4k", [(0, 0), (1, 15), (0, 7)])
+    assert stats["n_nonfinite"] == 0 and stats["n_flagged"] == 0
+
+
+def test_unbounded_full():
+    wl, stats, inp = run_full("unbounded", [(0, 3), (1, 12)])
+    assert stats["n_nonfinite"] == 0
+    spans = orc.chunk_spans(inp["w"].float().cpu().numpy(), wl.g_min, 16)
+    pred = spans < -80.0
+    ties = np.abs(spans + 80.0) <= 1e-3
+    say(f"   flagged {stats['n_flagged']} predicted {int(pred.sum())} ({pred.mean():.3f}) ties {int(ties.sum())}")
+    assert abs(stats["n_flagged"] - int(pred.sum())) <= int(ties.sum())
+
+
+def test_headline_full():
+    _, stats, _ = run_full("headline", [(0, 0), (0, 9)])
+    assert stats["n_nonfinite"] == 0 and stats["n_flagged"] == 0
+
+
+def test_decay_stress_full():
+    _, stats, _ = run_full("decay_stress", [(0, 5), (0, 31)])
+    assert stats["n_nonfinite"] == 0 and stats["n_flagged"] == 0
+    assert -80.0 <= stats["min_span"] < -79.5
+
+
+@pytest.mark.timeout(600)
+def test_million_token_share_full():
+    from kda_testutil import mfma_available
+    if not mfma_available():
+        pytest.skip("the million-token share runs on the matrix-core path")
+    _, stats, _ = run_full("million", [(0, 11)])
+    assert stats["n_nonfinite"] == 0 and stats["n_flagged"] == 0
