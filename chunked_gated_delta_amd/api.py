@@ -87,7 +87,7 @@ def chunk_fwd(q, k, v, w, beta, S0=None, g_min: float = -5.0, chunk: int = 16, *
     else:
         _check(S_final, "S_final", (B, H, dk, dv), torch.float32, dev)
     shape = make_shape(B, H, T, dk, dv, _dtype_code(q))
-    ws_need = _lib.workspace_bytes(shape, chunk)
+    ws_need = 0 if path == "vector" else _lib.workspace_bytes(shape, chunk)
     if workspace is None and ws_need > 0:
         workspace = torch.empty(ws_need, dtype=torch.uint8, device=dev)
     st = torch.empty(4, dtype=torch.int32, device=dev) if stats else None
