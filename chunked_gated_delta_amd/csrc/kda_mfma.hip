@@ -49,7 +49,8 @@ constexpr int kOffKt = 16384;    // Ktil^T, [t 8] blocks
 constexpr int kOffTb = 24576;    // T diag(beta), [mt 2] blocks
 constexpr int kOffPh = 26624;    // Phat, [mt 2] blocks
 constexpr int kOffEg = 28672;    // e^{Gam} per key channel, grouped by lane group: [g 4][t 8][r 4] fp32
-constexpr int kRecBytes = 29184;
+constexpr int kOffMeta = 29184;  // StepMeta (16 B), then padding
+constexpr int kRecBytes = 29696; // 29 KiB: the scan copies a record with 29 wave-wide 16-byte-per-lane loads
 
 struct StepMeta {           // per (b, h, step)
   float span[2];            // chunk spans (natural log units); +inf for a chunk with no tokens
@@ -88,6 +89,7 @@ struct PrepShared {
   alignas(16) __bf16 WnT[D][STEP + 8];          // (-W)^T
   alignas(16) float A[STEP][STEP + 1], P[STEP][STEP + 1], T[STEP][STEP + 1], X[16][17];
   alignas(16) __bf16 Tb[STEP][STEP + 8];        // T diag(beta)
+  alignas(16) __bf16 TbT[STEP][STEP + 8];       // (T diag(beta))^T
   alignas(16) __bf16 Pb[STEP][STEP + 8];        // P
   alignas(16) __bf16 Ph[STEP][STEP + 8];        // P T diag(beta)
   alignas(16) float Gam[2][D];                  // chunk spans per channel, log2 units
@@ -111,22 +113,28 @@ __global__ __launch_bounds__(256) void prep_kernel(Params p, int64_t n_steps) {
   const uint16_t* w = (const uint16_t*)p.w + bh * T * D;
   const uint16_t* beta = (const uint16_t*)p.beta + bh * T;
   unsigned char* rec = (unsigned char*)p.workspace + (bh * n_steps + s) * (int64_t)kRecBytes;
-  StepMeta* meta = reinterpret_cast<StepMeta*>((unsigned char*)p.workspace + p.B * p.H * n_steps * (int64_t)kRecBytes);
 
   // ---- phase 1: gate, chunk-local prefix, scaled operands.  Thread = (channel, chunk).
   const int ch = tid & (D - 1);
   const int c = tid >> 7;
-  float qv[16], kv[16], eL[16];
+  float qv[16], kv[16], eL[16], wv[16];
+  // all loads first (addresses clamped into the sequence), so they are in flight together
+#pragma unroll
+  for (int l = 0; l < 16; ++l) {
+    const int64_t t = t0 + 16 * c + l;
+    const int64_t tc = t < T ? t : T - 1;
+    wv[l] = bf(w, tc * D + ch);
+    qv[l] = bf(q, tc * D + ch);
+    kv[l] = bf(k, tc * D + ch);
+  }
   float Lp = 0.f;
 #pragma unroll
   for (int l = 0; l < 16; ++l) {
     const int pp = 16 * c + l;
-    const int64_t t = t0 + pp;
-    const bool ok = t < T;
-    const float wv = ok ? bf(w, t * D + ch) : 0.f;
-    qv[l] = ok ? bf(q, t * D + ch) : 0.f;
-    kv[l] = ok ? bf(k, t * D + ch) : 0.f;
-    Lp += ok ? gate_log2(wv, p.g_min, p.unbounded) : 0.f;
+    const bool ok = t0 + pp < T;
+    qv[l] = ok ? qv[l] : 0.f;
+    kv[l] = ok ? kv[l] : 0.f;
+    Lp += ok ? gate_log2(wv[l], p.g_min, p.unbounded) : 0.f;
     sm.L[pp][ch] = Lp;
     eL[l] = __builtin_amdgcn_exp2f(Lp);
     const float emL = __builtin_amdgcn_exp2f(-Lp);
@@ -159,7 +167,7 @@ __global__ __launch_bounds__(256) void prep_kernel(Params p, int64_t n_steps) {
     mt.span[1] = valid1 ? span1 : __int_as_float(0x7f800000);
     mt.n_valid = (valid0 ? 1u : 0u) + (valid1 ? 1u : 0u);
     mt.n_flagged = (flag0 ? 1u : 0u) + (flag1 ? 1u : 0u);
-    meta[bh * n_steps + s] = mt;
+    *reinterpret_cast<StepMeta*>(rec + kOffMeta) = mt;
   }
   // step-level quantities (G referenced to the start of the step)
   {
@@ -248,40 +256,57 @@ __global__ __launch_bounds__(256) void prep_kernel(Params p, int64_t n_steps) {
   }
   __syncthreads();
 
-  // ---- phase 3: T = (I + A)^{-1}: diagonal blocks by forward substitution (one column per lane) ...
+  // ---- phase 3: T = (I + A)^{-1}.  Diagonal blocks by forward substitution, one column per lane,
+  // the column kept in registers (fully unrolled, no dependent shared-memory round trips) ...
   if (tid < STEP) {
     const int j = tid, b0 = (j < 16) ? 0 : 16;
-    for (int r = b0; r < b0 + 16; ++r) {
-      float x = (r == j) ? 1.f : 0.f;
-      for (int i = j; i < r; ++i) x -= sm.A[r][i] * sm.T[i][j];
-      sm.T[r][j] = (r < j) ? 0.f : x;
+    float col[16];
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      float x = (b0 + r == j) ? 1.f : 0.f;
+#pragma unroll
+      for (int i = 0; i < r; ++i) x -= sm.A[b0 + r][b0 + i] * col[i];
+      col[r] = (b0 + r < j) ? 0.f : x;
     }
-    for (int r = 0; r < 16; ++r) if (j >= 16) sm.T[r][j] = 0.f;     // upper-right block
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      sm.T[b0 + r][j] = col[r];
+      if (b0 == 16) sm.T[r][j] = 0.f;                 // upper-right block
+    }
   }
   __syncthreads();
-  // ... then the coupling block T_10 = -T_11 A_10 T_00
+  // ... then the coupling block T_10 = -T_11 (A_10 T_00)   (entries outside the triangles are zero)
   {
-    const int r = tid >> 4, j = tid & 15;                  // X = A_10 T_00
+    const int r = tid >> 4, j = tid & 15;
     float x = 0.f;
-    for (int n = j; n < 16; ++n) x += sm.A[16 + r][n] * sm.T[n][j];
+#pragma unroll
+    for (int n = 0; n < 16; ++n) x += sm.A[16 + r][n] * sm.T[n][j];
     sm.X[r][j] = x;
   }
   __syncthreads();
   {
     const int r = tid >> 4, j = tid & 15;
     float x = 0.f;
-    for (int mm = 0; mm <= r; ++mm) x += sm.T[16 + r][16 + mm] * sm.X[mm][j];
+#pragma unroll
+    for (int mm = 0; mm < 16; ++mm) x += sm.T[16 + r][16 + mm] * sm.X[mm][j];
     sm.T[16 + r][j] = -x;
   }
   __syncthreads();
-  // T diag(beta) and P in bf16 (row-major), Phat = P T diag(beta)
+  // T diag(beta) (row-major and transposed) and P in bf16
   for (int e = tid; e < STEP * STEP; e += 256) {
     const int r = e >> 5, j = e & 31;
-    sm.Tb[r][j] = (__bf16)(sm.T[r][j] * sm.beta[j]);
+    const __bf16 tb = (__bf16)(sm.T[r][j] * sm.beta[j]);
+    sm.Tb[r][j] = tb;
+    sm.TbT[j][r] = tb;
     sm.Pb[r][j] = (__bf16)sm.P[r][j];
-    float x = 0.f;
-    for (int mm = j; mm <= r; ++mm) x += sm.P[r][mm] * sm.T[mm][j];
-    sm.Ph[r][j] = (__bf16)(x * sm.beta[j]);
+  }
+  __syncthreads();
+  // Phat = P T diag(beta) on MFMA: wave w computes the 16x16 tile (w >> 1, w & 1)
+  {
+    const int mt = wave >> 1, nt = wave & 1;
+    const floatx4 d = mfma(ld8(&sm.Pb[16 * mt + li][8 * lg]), ld8(&sm.TbT[16 * nt + li][8 * lg]), floatx4{0, 0, 0, 0});
+#pragma unroll
+    for (int r = 0; r < 4; ++r) sm.Ph[16 * mt + 4 * lg + r][16 * nt + li] = (__bf16)d[r];
   }
   __syncthreads();
 
@@ -355,8 +380,47 @@ __device__ __forceinline__ bf16x8 pack2(floatx4 a, floatx4 b) {
   return o;
 }
 
-__global__ __launch_bounds__(64) void scan_kernel(Params p, int64_t n_steps, int xcd_map) {
-  const int lane = threadIdx.x;
+// Ring of records in LDS: each slot holds one step's record followed by the
+// 32 x 16 slice of V for that step.  Three loader wavefronts keep the next
+// kRing-1 steps in flight with direct-to-LDS 16-byte loads; the compute
+// wavefront never waits on global memory.
+constexpr int kRing = 5;
+constexpr int kSlotBytes = kRecBytes + 1024;
+constexpr int kLoadsPerStep = kRecBytes / 1024 + 1;   // 29 record chunks + 1 V chunk
+constexpr int kLoaders = 3;
+constexpr int kLoadsPerLoader = kLoadsPerStep / kLoaders;
+static_assert(kLoadsPerStep % kLoaders == 0, "loads must split evenly over the loader waves");
+static_assert(kLoadsPerLoader * (kRing - 1) <= 63, "outstanding loads must fit the vmcnt counter");
+
+typedef __attribute__((address_space(3))) void lds_void;
+
+__device__ __forceinline__ void compiler_fence() { __atomic_signal_fence(__ATOMIC_SEQ_CST); }
+
+__device__ __forceinline__ void block_barrier() {
+  compiler_fence();
+  __builtin_amdgcn_s_barrier();
+  compiler_fence();
+}
+
+// s_waitcnt with only vmcnt constrained (expcnt and lgkmcnt left at their maxima)
+template <int N> __device__ __forceinline__ void wait_vm() {
+  static_assert(N >= 0 && N <= 63, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 0xF) | ((N >> 4) << 14) | (0x7 << 4) | (0xF << 8));
+}
+
+__device__ __forceinline__ void wait_vm_dyn(int n) {   // n in multiples of kLoadsPerLoader
+  switch (n) {
+    case 0: wait_vm<0>(); break;
+    case 1: wait_vm<kLoadsPerLoader>(); break;
+    case 2: wait_vm<2 * kLoadsPerLoader>(); break;
+    default: wait_vm<3 * kLoadsPerLoader>(); break;
+  }
+}
+
+__global__ __launch_bounds__(256) void scan_kernel(Params p, int64_t n_steps, int xcd_map) {
+  extern __shared__ __align__(16) unsigned char ring[];
+  const int tid = threadIdx.x;
+  const int lane = tid & 63, wave = tid >> 6;
   const int li = lane & 15, lg = lane >> 4;
   const int64_t BH = p.B * p.H;
   int64_t bh;
@@ -369,35 +433,70 @@ __global__ __launch_bounds__(64) void scan_kernel(Params p, int64_t n_steps, int
     bh = blockIdx.x >> 3;
     slice = (int)(blockIdx.x & 7);
   }
-  if (bh >= BH) return;
+  if (bh >= BH) return;   // uniform over the workgroup
   const int64_t T = p.T;
   const int d0 = slice * 16;
-  const uint16_t* v = (const uint16_t*)p.v + bh * T * D;
-  uint16_t* o = (uint16_t*)p.o + bh * T * D;
   const unsigned char* recs = (const unsigned char*)p.workspace + bh * n_steps * (int64_t)kRecBytes;
-  const StepMeta* meta = reinterpret_cast<const StepMeta*>((const unsigned char*)p.workspace + BH * n_steps * (int64_t)kRecBytes) + bh * n_steps;
+  const uint16_t* v = (const uint16_t*)p.v + bh * T * D;
 
+  if (wave > 0) {
+    // ---------------- loader wavefronts
+    const int L = wave - 1;
+    auto issue = [&](int64_t st) {
+      unsigned char* slot = ring + (st % kRing) * kSlotBytes;
+      const unsigned char* src = recs + st * (int64_t)kRecBytes;
+#pragma unroll
+      for (int x = 0; x < kLoadsPerLoader; ++x) {
+        const int j = L + kLoaders * x;
+        if (j < kLoadsPerStep - 1) {
+          __builtin_amdgcn_global_load_lds((const void*)(src + j * 1024 + lane * 16), (lds_void*)(slot + j * 1024), 16, 0, 0);
+        } else {   // V rows: lane -> (row, 16-byte half); rows past the end read the last row (masked later)
+          int64_t t = st * STEP + (lane >> 1);
+          t = t < T ? t : T - 1;
+          __builtin_amdgcn_global_load_lds((const void*)(v + t * D + d0 + (lane & 1) * 8), (lds_void*)(slot + kRecBytes), 16, 0, 0);
+        }
+      }
+    };
+    for (int64_t st = 0; st < kRing - 1 && st < n_steps; ++st) issue(st);
+    for (int64_t s = 0; s < n_steps; ++s) {
+      const int64_t issued_max = (s + kRing - 2 < n_steps - 1) ? s + kRing - 2 : n_steps - 1;
+      wait_vm_dyn((int)(issued_max - s));
+      block_barrier();
+      if (s + kRing - 1 < n_steps) issue(s + kRing - 1);
+    }
+    return;
+  }
+
+  // ---------------- compute wavefront
+  uint16_t* o = (uint16_t*)p.o + bh * T * D;
   floatx4 S[8];
+  if (p.S0) {
 #pragma unroll
-  for (int t = 0; t < 8; ++t)
+    for (int t = 0; t < 8; ++t)
 #pragma unroll
-    for (int r = 0; r < 4; ++r)
-      S[t][r] = p.S0 ? p.S0[(bh * D + 16 * t + 4 * lg + r) * D + d0 + li] : 0.f;
+      for (int r = 0; r < 4; ++r) S[t][r] = p.S0[(bh * D + 16 * t + 4 * lg + r) * D + d0 + li];
+  } else {
+#pragma unroll
+    for (int t = 0; t < 8; ++t) S[t] = floatx4{0, 0, 0, 0};
+  }
 
   uint32_t nonfinite = 0, n_valid = 0, n_flagged = 0;
   float min_span = __int_as_float(0x7f800000);
   const floatx4 zero = {0, 0, 0, 0};
 
   for (int64_t s = 0; s < n_steps; ++s) {
-    const unsigned char* rec = recs + s * (int64_t)kRecBytes;
+    block_barrier();   // slot s % kRing is loaded; the previous slot is free for reuse
+    const unsigned char* rec = ring + (s % kRing) * kSlotBytes;
     const int64_t t0 = s * STEP;
-    // V operand: positions {4g+r, 16+4g+r}, column d0 + li
+    // V operand: positions {4g+r, 16+4g+r}, column d0 + li (rows past the end are zero)
+    const __bf16* vr = (const __bf16*)(rec + kRecBytes);
     bf16x8 vb;
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
-      const int64_t ta = t0 + 4 * lg + r, tb = t0 + 16 + 4 * lg + r;
-      vb[r] = (ta < T) ? __builtin_bit_cast(__bf16, v[ta * D + d0 + li]) : (__bf16)0.f;
-      vb[4 + r] = (tb < T) ? __builtin_bit_cast(__bf16, v[tb * D + d0 + li]) : (__bf16)0.f;
+      const int pa = 4 * lg + r, pb = 16 + 4 * lg + r;
+      const __bf16 xa = vr[pa * 16 + li], xb = vr[pb * 16 + li];
+      vb[r] = (t0 + pa < T) ? xa : (__bf16)0.f;
+      vb[4 + r] = (t0 + pb < T) ? xb : (__bf16)0.f;
     }
     bf16x8 sb[4];
 #pragma unroll
@@ -407,25 +506,11 @@ __global__ __launch_bounds__(64) void scan_kernel(Params p, int64_t n_steps, int
 #pragma unroll
     for (int mt = 0; mt < 2; ++mt) {
       U[mt] = mfma(ld8((const __bf16*)(rec + kOffTb + (mt * 64 + lane) * 16)), vb, zero);
-      O[mt] = mfma(ld8((const __bf16*)(rec + kOffPh + (mt * 64 + lane) * 16)), vb, zero);
 #pragma unroll
-      for (int u = 0; u < 4; ++u) {
+      for (int u = 0; u < 4; ++u)
         U[mt] = mfma(ld8((const __bf16*)(rec + kOffWn + ((mt * 4 + u) * 64 + lane) * 16)), sb[u], U[mt]);
-        O[mt] = mfma(ld8((const __bf16*)(rec + kOffQh + ((mt * 4 + u) * 64 + lane) * 16)), sb[u], O[mt]);
-      }
     }
-    // outputs
-#pragma unroll
-    for (int mt = 0; mt < 2; ++mt)
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int64_t t = t0 + 16 * mt + 4 * lg + r;
-        if (t < T) {
-          o[t * D + d0 + li] = f32_to_bf16(O[mt][r]);
-          nonfinite += not_finite(O[mt][r]) ? 1u : 0u;
-        }
-      }
-    // state update
+    // state update (the critical chain), then the outputs
     const bf16x8 ub = pack2(U[0], U[1]);
     const float* eg = reinterpret_cast<const float*>(rec + kOffEg) + lg * 32;
 #pragma unroll
@@ -436,8 +521,25 @@ __global__ __launch_bounds__(64) void scan_kernel(Params p, int64_t n_steps, int
       for (int r = 0; r < 4; ++r) cdec[r] = S[t][r] * e[r];
       S[t] = mfma(ld8((const __bf16*)(rec + kOffKt + (t * 64 + lane) * 16)), ub, cdec);
     }
-    if (slice == 0 && lane == 0) {
-      const StepMeta m = meta[s];
+#pragma unroll
+    for (int mt = 0; mt < 2; ++mt) {
+      O[mt] = mfma(ld8((const __bf16*)(rec + kOffPh + (mt * 64 + lane) * 16)), vb, zero);
+#pragma unroll
+      for (int u = 0; u < 4; ++u)
+        O[mt] = mfma(ld8((const __bf16*)(rec + kOffQh + ((mt * 4 + u) * 64 + lane) * 16)), sb[u], O[mt]);
+    }
+#pragma unroll
+    for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int64_t t = t0 + 16 * mt + 4 * lg + r;
+        if (t < T) {
+          o[t * D + d0 + li] = f32_to_bf16(O[mt][r]);
+          nonfinite += not_finite(O[mt][r]) ? 1u : 0u;
+        }
+      }
+    if (slice == 0) {
+      const StepMeta m = *reinterpret_cast<const StepMeta*>(rec + kOffMeta);
       n_valid += m.n_valid;
       n_flagged += m.n_flagged;
       min_span = fminf(min_span, fminf(m.span[0], m.span[1]));
@@ -475,16 +577,19 @@ bool mfma_supported(const Params& p) {
 size_t mfma_workspace_bytes(int64_t B, int64_t H, int64_t T, int64_t dk, int64_t dv) {
   if (dk != D || dv != D) return 0;
   const int64_t n_steps = (T + STEP - 1) / STEP;
-  return (size_t)(B * H * n_steps) * (kRecBytes + sizeof(StepMeta));
+  return (size_t)(B * H * n_steps) * kRecBytes;
 }
 
 hipError_t launch_mfma(const Params& p, hipStream_t s, hipEvent_t ev_begin, hipEvent_t ev_end) {
   const int64_t n_steps = (p.T + STEP - 1) / STEP;
   const int64_t BH = p.B * p.H;
   const size_t smem = sizeof(PrepShared);
+  const size_t smem_scan = (size_t)kRing * kSlotBytes;
   static bool attr_set = false;
   if (!attr_set) {
     hipError_t e = hipFuncSetAttribute((const void*)prep_kernel, hipFuncAttributeMaxDynamicSharedMemorySize, (int)smem);
+    if (e != hipSuccess) return e;
+    e = hipFuncSetAttribute((const void*)scan_kernel, hipFuncAttributeMaxDynamicSharedMemorySize, (int)smem_scan);
     if (e != hipSuccess) return e;
     attr_set = true;
   }
@@ -493,7 +598,7 @@ hipError_t launch_mfma(const Params& p, hipStream_t s, hipEvent_t ev_begin, hipE
   hipLaunchKernelGGL(prep_kernel, dim3((unsigned)(BH * n_steps)), dim3(256), smem, s, p, n_steps);
   if ((e = hipGetLastError()) != hipSuccess) return e;
   const int xcd_map = (BH % 8 == 0) ? 1 : 0;
-  hipLaunchKernelGGL(scan_kernel, dim3((unsigned)(BH * 8)), dim3(64), 0, s, p, n_steps, xcd_map);
+  hipLaunchKernelGGL(scan_kernel, dim3((unsigned)(BH * 8)), dim3(256), smem_scan, s, p, n_steps, xcd_map);
   if ((e = hipGetLastError()) != hipSuccess) return e;
   if (ev_end && (e = hipEventRecord(ev_end, s)) != hipSuccess) return e;
   return hipSuccess;
