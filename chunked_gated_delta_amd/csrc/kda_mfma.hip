@@ -381,23 +381,40 @@ __device__ __forceinline__ bf16x8 pack2(floatx4 a, floatx4 b) {
 }
 
 // Ring of records in LDS: each slot holds one step's record followed by the
-// 32 x 16 slice of V for that step.  Three loader wavefronts keep the next
-// kRing-1 steps in flight with direct-to-LDS 16-byte loads; the compute
-// wavefront never waits on global memory.
+// 32 x 16 slice of V for that step.  Six loader wavefronts keep kRing-1 steps
+// in flight with direct-to-LDS 16-byte loads (one wavefront sustains only
+// ~17 GB/s of such loads, so the stream is spread over several), and
+// guarantee that the two oldest slots are complete at every step barrier, so
+// the compute wavefronts can read step s+1's operands while step s is still
+// computing.  The step's work is split over two
+// compute wavefronts on different SIMDs (one wavefront's vector ALU issues too
+// slowly for both halves):
+//   chain wave   U = T diag(beta) V - W S;  S <- diag(e^Gam) S + Ktil^T U;
+//                publishes the bf16 copy of the state entering each step
+//   output wave  O = Qhat S + Phat V from that copy; stores o
 constexpr int kRing = 5;
 constexpr int kSlotBytes = kRecBytes + 1024;
 constexpr int kLoadsPerStep = kRecBytes / 1024 + 1;   // 29 record chunks + 1 V chunk
-constexpr int kLoaders = 3;
+constexpr int kLoaders = 6;
 constexpr int kLoadsPerLoader = kLoadsPerStep / kLoaders;
+constexpr int kStateBufBytes = 4 * 64 * 16;          // bf16 state operands, [u 4][lane 64] x 16 B
 static_assert(kLoadsPerStep % kLoaders == 0, "loads must split evenly over the loader waves");
 static_assert(kLoadsPerLoader * (kRing - 1) <= 63, "outstanding loads must fit the vmcnt counter");
+static_assert(kRing >= 4, "two complete slots plus two in flight");
+constexpr size_t kScanSmem = (size_t)kRing * kSlotBytes + 2 * kStateBufBytes;
+static_assert(kScanSmem <= 163840, "LDS budget");
+constexpr int kScanThreads = 64 * (2 + kLoaders);
 
 typedef __attribute__((address_space(3))) void lds_void;
 
 __device__ __forceinline__ void compiler_fence() { __atomic_signal_fence(__ATOMIC_SEQ_CST); }
 
+// Workgroup barrier without a memory fence on global memory: waits only for this wave's
+// shared-memory operations (so its LDS writes are visible after the barrier), never for the
+// loaders' in-flight global loads or the output stores.
 __device__ __forceinline__ void block_barrier() {
   compiler_fence();
+  __builtin_amdgcn_s_waitcnt(0xF | (0x3 << 14) | (0x7 << 4) | (0x0 << 8));   // lgkmcnt(0)
   __builtin_amdgcn_s_barrier();
   compiler_fence();
 }
@@ -417,8 +434,66 @@ __device__ __forceinline__ void wait_vm_dyn(int n) {   // n in multiples of kLoa
   }
 }
 
-__global__ __launch_bounds__(256) void scan_kernel(Params p, int64_t n_steps, int xcd_map) {
+// V operand rows {4g+r, 16+4g+r}, column li, from the slot's 32 x 16 V tile; rows at or past nrows are zero
+__device__ __forceinline__ bf16x8 v_operand(const unsigned char* slot, int lg, int li, int nrows) {
+  const __bf16* vr = (const __bf16*)(slot + kRecBytes);
+  bf16x8 vb;
+#pragma unroll
+  for (int r = 0; r < 4; ++r) {
+    vb[r] = vr[(4 * lg + r) * 16 + li];
+    vb[4 + r] = vr[(16 + 4 * lg + r) * 16 + li];
+  }
+  if (nrows < STEP) {
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      if (4 * lg + r >= nrows) vb[r] = (__bf16)0.f;
+      if (16 + 4 * lg + r >= nrows) vb[4 + r] = (__bf16)0.f;
+    }
+  }
+  return vb;
+}
+
+__device__ __forceinline__ uint32_t abs_bits(float x) { return __float_as_uint(x) & 0x7fffffffu; }
+
+struct ChainOps {
+  bf16x8 tb[2], wn[8], kt[8], vb;
+  floatx4 eg[8];
+};
+
+__device__ __forceinline__ void load_chain_ops(ChainOps& c, const unsigned char* rec, int lane, int lg, int li, int nrows) {
+#pragma unroll
+  for (int mt = 0; mt < 2; ++mt) c.tb[mt] = ld8((const __bf16*)(rec + kOffTb + (mt * 64 + lane) * 16));
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    c.wn[i] = ld8((const __bf16*)(rec + kOffWn + (i * 64 + lane) * 16));
+    c.kt[i] = ld8((const __bf16*)(rec + kOffKt + (i * 64 + lane) * 16));
+    c.eg[i] = *reinterpret_cast<const floatx4*>(rec + kOffEg + (lg * 32 + 4 * i) * 4);
+  }
+  c.vb = v_operand(rec, lg, li, nrows);
+}
+
+struct OutOps {
+  bf16x8 ph[2], qh[8], vb;
+  StepMeta meta;
+};
+
+__device__ __forceinline__ void load_out_ops(OutOps& c, const unsigned char* rec, int lane, int lg, int li, int nrows) {
+#pragma unroll
+  for (int mt = 0; mt < 2; ++mt) c.ph[mt] = ld8((const __bf16*)(rec + kOffPh + (mt * 64 + lane) * 16));
+#pragma unroll
+  for (int i = 0; i < 8; ++i) c.qh[i] = ld8((const __bf16*)(rec + kOffQh + (i * 64 + lane) * 16));
+  c.vb = v_operand(rec, lg, li, nrows);
+  c.meta = *reinterpret_cast<const StepMeta*>(rec + kOffMeta);
+}
+
+__device__ __forceinline__ int rows_of(int64_t T, int64_t st) {
+  const int64_t rem = T - st * STEP;
+  return rem < STEP ? (int)rem : STEP;
+}
+
+__global__ __launch_bounds__(kScanThreads) void scan_kernel(Params p, int64_t n_steps, int xcd_map) {
   extern __shared__ __align__(16) unsigned char ring[];
+  unsigned char* sbuf = ring + (size_t)kRing * kSlotBytes;   // two state buffers
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
   const int li = lane & 15, lg = lane >> 4;
@@ -438,10 +513,11 @@ __global__ __launch_bounds__(256) void scan_kernel(Params p, int64_t n_steps, in
   const int d0 = slice * 16;
   const unsigned char* recs = (const unsigned char*)p.workspace + bh * n_steps * (int64_t)kRecBytes;
   const uint16_t* v = (const uint16_t*)p.v + bh * T * D;
+  const floatx4 zero = {0, 0, 0, 0};
 
-  if (wave > 0) {
+  if (wave >= 2) {
     // ---------------- loader wavefronts
-    const int L = wave - 1;
+    const int L = wave - 2;
     auto issue = [&](int64_t st) {
       unsigned char* slot = ring + (st % kRing) * kSlotBytes;
       const unsigned char* src = recs + st * (int64_t)kRecBytes;
@@ -459,101 +535,124 @@ __global__ __launch_bounds__(256) void scan_kernel(Params p, int64_t n_steps, in
     };
     for (int64_t st = 0; st < kRing - 1 && st < n_steps; ++st) issue(st);
     for (int64_t s = 0; s < n_steps; ++s) {
+      // at barrier s, slots s and s+1 must be complete
       const int64_t issued_max = (s + kRing - 2 < n_steps - 1) ? s + kRing - 2 : n_steps - 1;
-      wait_vm_dyn((int)(issued_max - s));
+      const int64_t need = (s + 1 < n_steps - 1) ? s + 1 : n_steps - 1;
+      wait_vm_dyn((int)(issued_max - need));
       block_barrier();
       if (s + kRing - 1 < n_steps) issue(s + kRing - 1);
     }
     return;
   }
 
-  // ---------------- compute wavefront
-  uint16_t* o = (uint16_t*)p.o + bh * T * D;
-  floatx4 S[8];
-  if (p.S0) {
+  if (wave == 0) {
+    // ---------------- chain wavefront: the state slice lives here, in fp32
+    floatx4 S[8];
+    if (p.S0) {
 #pragma unroll
-    for (int t = 0; t < 8; ++t)
+      for (int t = 0; t < 8; ++t)
 #pragma unroll
-      for (int r = 0; r < 4; ++r) S[t][r] = p.S0[(bh * D + 16 * t + 4 * lg + r) * D + d0 + li];
-  } else {
+        for (int r = 0; r < 4; ++r) S[t][r] = p.S0[(bh * D + 16 * t + 4 * lg + r) * D + d0 + li];
+    } else {
 #pragma unroll
-    for (int t = 0; t < 8; ++t) S[t] = floatx4{0, 0, 0, 0};
-  }
-
-  uint32_t nonfinite = 0, n_valid = 0, n_flagged = 0;
-  float min_span = __int_as_float(0x7f800000);
-  const floatx4 zero = {0, 0, 0, 0};
-
-  for (int64_t s = 0; s < n_steps; ++s) {
-    block_barrier();   // slot s % kRing is loaded; the previous slot is free for reuse
-    const unsigned char* rec = ring + (s % kRing) * kSlotBytes;
-    const int64_t t0 = s * STEP;
-    // V operand: positions {4g+r, 16+4g+r}, column d0 + li (rows past the end are zero)
-    const __bf16* vr = (const __bf16*)(rec + kRecBytes);
-    bf16x8 vb;
-#pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const int pa = 4 * lg + r, pb = 16 + 4 * lg + r;
-      const __bf16 xa = vr[pa * 16 + li], xb = vr[pb * 16 + li];
-      vb[r] = (t0 + pa < T) ? xa : (__bf16)0.f;
-      vb[4 + r] = (t0 + pb < T) ? xb : (__bf16)0.f;
+      for (int t = 0; t < 8; ++t) S[t] = zero;
     }
     bf16x8 sb[4];
 #pragma unroll
-    for (int u = 0; u < 4; ++u) sb[u] = pack2(S[2 * u], S[2 * u + 1]);
+    for (int u = 0; u < 4; ++u) {
+      sb[u] = pack2(S[2 * u], S[2 * u + 1]);
+      *reinterpret_cast<bf16x8*>(sbuf + (u * 64 + lane) * 16) = sb[u];
+    }
+    ChainOps cur;
+    for (int64_t s = 0; s < n_steps; ++s) {
+      block_barrier();
+      if (s == 0) load_chain_ops(cur, ring, lane, lg, li, rows_of(T, 0));
+      floatx4 cdec[8];
+#pragma unroll
+      for (int t = 0; t < 8; ++t)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) cdec[t][r] = S[t][r] * cur.eg[t][r];
+      floatx4 U[2];
+#pragma unroll
+      for (int mt = 0; mt < 2; ++mt) U[mt] = mfma(cur.tb[mt], cur.vb, zero);
+#pragma unroll
+      for (int u = 0; u < 4; ++u)
+#pragma unroll
+        for (int mt = 0; mt < 2; ++mt) U[mt] = mfma(cur.wn[mt * 4 + u], sb[u], U[mt]);
+      const bf16x8 ub = pack2(U[0], U[1]);
+#pragma unroll
+      for (int t = 0; t < 8; ++t) S[t] = mfma(cur.kt[t], ub, cdec[t]);
+      // operands of the next step (its slot is complete since this step's barrier)
+      if (s + 1 < n_steps) load_chain_ops(cur, ring + ((s + 1) % kRing) * kSlotBytes, lane, lg, li, rows_of(T, s + 1));
+      unsigned char* nb = sbuf + ((s + 1) & 1) * kStateBufBytes;
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        sb[u] = pack2(S[2 * u], S[2 * u + 1]);
+        *reinterpret_cast<bf16x8*>(nb + (u * 64 + lane) * 16) = sb[u];
+      }
+    }
+    uint32_t nonfinite = 0;
+#pragma unroll
+    for (int t = 0; t < 8; ++t)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        p.S_final[(bh * D + 16 * t + 4 * lg + r) * D + d0 + li] = S[t][r];
+        nonfinite += not_finite(S[t][r]) ? 1u : 0u;
+      }
+    if (p.stats) {
+#pragma unroll
+      for (int off = 32; off > 0; off >>= 1) nonfinite += __shfl_xor(nonfinite, off);
+      if (lane == 0 && nonfinite) atomicAdd(&p.stats->n_nonfinite, nonfinite);
+    }
+    return;
+  }
 
-    floatx4 U[2], O[2];
+  // ---------------- output wavefront
+  uint16_t* o = (uint16_t*)p.o + bh * T * D + (4 * lg) * D + d0 + li;
+  uint32_t nonfinite = 0, n_valid = 0, n_flagged = 0;
+  float min_span = __int_as_float(0x7f800000);
+  OutOps cur;
+  for (int64_t s = 0; s < n_steps; ++s) {
+    block_barrier();
+    if (s == 0) load_out_ops(cur, ring, lane, lg, li, rows_of(T, 0));
+    const int nrows = rows_of(T, s);
+    const unsigned char* cb = sbuf + (s & 1) * kStateBufBytes;
+    bf16x8 sb[4];
 #pragma unroll
-    for (int mt = 0; mt < 2; ++mt) {
-      U[mt] = mfma(ld8((const __bf16*)(rec + kOffTb + (mt * 64 + lane) * 16)), vb, zero);
+    for (int u = 0; u < 4; ++u) sb[u] = ld8((const __bf16*)(cb + (u * 64 + lane) * 16));
+    floatx4 O[2];
 #pragma unroll
-      for (int u = 0; u < 4; ++u)
-        U[mt] = mfma(ld8((const __bf16*)(rec + kOffWn + ((mt * 4 + u) * 64 + lane) * 16)), sb[u], U[mt]);
+    for (int mt = 0; mt < 2; ++mt) O[mt] = mfma(cur.ph[mt], cur.vb, zero);
+#pragma unroll
+    for (int u = 0; u < 4; ++u)
+#pragma unroll
+      for (int mt = 0; mt < 2; ++mt) O[mt] = mfma(cur.qh[mt * 4 + u], sb[u], O[mt]);
+    if (slice == 0) {
+      n_valid += cur.meta.n_valid;
+      n_flagged += cur.meta.n_flagged;
+      min_span = fminf(min_span, fminf(cur.meta.span[0], cur.meta.span[1]));
     }
-    // state update (the critical chain), then the outputs
-    const bf16x8 ub = pack2(U[0], U[1]);
-    const float* eg = reinterpret_cast<const float*>(rec + kOffEg) + lg * 32;
-#pragma unroll
-    for (int t = 0; t < 8; ++t) {
-      const floatx4 e = *reinterpret_cast<const floatx4*>(eg + 4 * t);
-      floatx4 cdec;
-#pragma unroll
-      for (int r = 0; r < 4; ++r) cdec[r] = S[t][r] * e[r];
-      S[t] = mfma(ld8((const __bf16*)(rec + kOffKt + (t * 64 + lane) * 16)), ub, cdec);
-    }
-#pragma unroll
-    for (int mt = 0; mt < 2; ++mt) {
-      O[mt] = mfma(ld8((const __bf16*)(rec + kOffPh + (mt * 64 + lane) * 16)), vb, zero);
-#pragma unroll
-      for (int u = 0; u < 4; ++u)
-        O[mt] = mfma(ld8((const __bf16*)(rec + kOffQh + ((mt * 4 + u) * 64 + lane) * 16)), sb[u], O[mt]);
-    }
+    if (s + 1 < n_steps) load_out_ops(cur, ring + ((s + 1) % kRing) * kSlotBytes, lane, lg, li, rows_of(T, s + 1));
+    uint16_t* os = o + s * STEP * D;
+    uint32_t mx = 0;
 #pragma unroll
     for (int mt = 0; mt < 2; ++mt)
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
-        const int64_t t = t0 + 16 * mt + 4 * lg + r;
-        if (t < T) {
-          o[t * D + d0 + li] = f32_to_bf16(O[mt][r]);
-          nonfinite += not_finite(O[mt][r]) ? 1u : 0u;
+        const int row = 16 * mt + 4 * lg + r;
+        if (nrows == STEP || row < nrows) {
+          os[(16 * mt + r) * D] = __builtin_bit_cast(uint16_t, (__bf16)O[mt][r]);
+          mx = max(mx, abs_bits(O[mt][r]));
         }
       }
-    if (slice == 0) {
-      const StepMeta m = *reinterpret_cast<const StepMeta*>(rec + kOffMeta);
-      n_valid += m.n_valid;
-      n_flagged += m.n_flagged;
-      min_span = fminf(min_span, fminf(m.span[0], m.span[1]));
+    if (mx >= 0x7f800000u) {   // rare: count exactly
+#pragma unroll
+      for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+        for (int r = 0; r < 4; ++r)
+          nonfinite += ((nrows == STEP || 16 * mt + 4 * lg + r < nrows) && abs_bits(O[mt][r]) >= 0x7f800000u) ? 1u : 0u;
     }
   }
-
-#pragma unroll
-  for (int t = 0; t < 8; ++t)
-#pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      p.S_final[(bh * D + 16 * t + 4 * lg + r) * D + d0 + li] = S[t][r];
-      nonfinite += not_finite(S[t][r]) ? 1u : 0u;
-    }
-
   if (p.stats) {
 #pragma unroll
     for (int off = 32; off > 0; off >>= 1) nonfinite += __shfl_xor(nonfinite, off);
@@ -584,7 +683,7 @@ hipError_t launch_mfma(const Params& p, hipStream_t s, hipEvent_t ev_begin, hipE
   const int64_t n_steps = (p.T + STEP - 1) / STEP;
   const int64_t BH = p.B * p.H;
   const size_t smem = sizeof(PrepShared);
-  const size_t smem_scan = (size_t)kRing * kSlotBytes;
+  const size_t smem_scan = kScanSmem;
   static bool attr_set = false;
   if (!attr_set) {
     hipError_t e = hipFuncSetAttribute((const void*)prep_kernel, hipFuncAttributeMaxDynamicSharedMemorySize, (int)smem);
@@ -598,7 +697,7 @@ hipError_t launch_mfma(const Params& p, hipStream_t s, hipEvent_t ev_begin, hipE
   hipLaunchKernelGGL(prep_kernel, dim3((unsigned)(BH * n_steps)), dim3(256), smem, s, p, n_steps);
   if ((e = hipGetLastError()) != hipSuccess) return e;
   const int xcd_map = (BH % 8 == 0) ? 1 : 0;
-  hipLaunchKernelGGL(scan_kernel, dim3((unsigned)(BH * 8)), dim3(256), smem_scan, s, p, n_steps, xcd_map);
+  hipLaunchKernelGGL(scan_kernel, dim3((unsigned)(BH * 8)), dim3(kScanThreads), smem_scan, s, p, n_steps, xcd_map);
   if ((e = hipGetLastError()) != hipSuccess) return e;
   if (ev_end && (e = hipEventRecord(ev_end, s)) != hipSuccess) return e;
   return hipSuccess;
