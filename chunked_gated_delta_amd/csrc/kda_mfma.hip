@@ -74,33 +74,78 @@ __device__ __forceinline__ float gate_log2(float w, float g_min, int unbounded) 
 __device__ __forceinline__ float bf(const uint16_t* p, int64_t i) { return bf16_to_f32(p[i]); }
 
 // ------------------------------------------------------------------ prep kernel
+//
+// Thread layout of the elementwise phase: tid = c*128 + pair*2 + half; the
+// thread owns channels 2*pair, 2*pair+1 of chunk c at positions
+// 16c + 8*half + j (j < 8).  The in-chunk prefix crosses the two halves with
+// one lane shuffle.  Shared memory is ~70 KB so two workgroups share a CU;
+// arrays of the later phases alias ones that are dead by then.
+
+constexpr int kRow = D + 8;        // padded row of a [position][channel] bf16 array
+constexpr int kRowT = STEP + 8;    // padded row of a [channel][position] bf16 array
 
 struct PrepShared {
-  alignas(16) float L[STEP][D];                 // in-chunk inclusive prefix, log2 units (per-pair fallback)
-  alignas(16) __bf16 Qraw[STEP][D + 8];         // raw q, k (bf16 exact) for the per-pair fallback
-  alignas(16) __bf16 Kraw[STEP][D + 8];
-  alignas(16) __bf16 Qb[STEP][D + 8];           // q e^{L}      (chunk-local)
-  alignas(16) __bf16 Kb[STEP][D + 8];           // k e^{L}
-  alignas(16) __bf16 Kh[STEP][D + 8];           // k e^{-L}     (diagonal blocks only)
-  alignas(16) __bf16 Kt0[16][D + 8];            // k e^{Gam_0 - L}, chunk 0 (block coupling chunk 1 to chunk 0)
-  alignas(16) float Qbar[STEP][D + 4];          // q e^{G}      (G referenced to the step start)
-  alignas(16) __bf16 KbarT[D][STEP + 8];        // (k e^{G})^T
-  alignas(16) __bf16 KtilT[D][STEP + 8];        // (k e^{Gam_step - G})^T
-  alignas(16) __bf16 WnT[D][STEP + 8];          // (-W)^T
-  alignas(16) float A[STEP][STEP + 1], P[STEP][STEP + 1], T[STEP][STEP + 1], X[16][17];
-  alignas(16) __bf16 Tb[STEP][STEP + 8];        // T diag(beta)
-  alignas(16) __bf16 TbT[STEP][STEP + 8];       // (T diag(beta))^T
-  alignas(16) __bf16 Pb[STEP][STEP + 8];        // P
-  alignas(16) __bf16 Ph[STEP][STEP + 8];        // P T diag(beta)
-  alignas(16) float Gam[2][D];                  // chunk spans per channel, log2 units
+  // ---- live from the elementwise phase through the tile phase
+  alignas(16) __bf16 Qb[STEP][kRow];     // q e^{L} (chunk-local), kept for Qbar = Qb e^{Gam_0 [chunk 1]}
+  alignas(16) __bf16 Kb[STEP][kRow];     // k e^{L}      | per-pair fallback: raw k of a flagged chunk
+  alignas(16) __bf16 Kh[STEP][kRow];     // k e^{-L}     | per-pair fallback: raw q of a flagged chunk
+  alignas(16) __bf16 Kt0[16][kRow];      // k e^{Gam_0 - L}, chunk 0 (block coupling chunk 1 to chunk 0)
+  alignas(16) __bf16 KbarT[D][kRowT];    // (k e^{G})^T, G referenced to the step start | later (-W)^T
+  alignas(16) __bf16 KtilT[D][kRowT];    // (k e^{Gam_step - G})^T
+  alignas(16) float L[16][D];            // in-chunk prefix (log2 units) of one flagged chunk
+  alignas(16) float A[STEP][STEP + 1], P[STEP][STEP + 1];
+  alignas(16) float Gam[2][D];           // chunk spans per channel, log2 units
+  alignas(16) float eGam0[D];            // e^{Gam_0}
   alignas(16) float beta[STEP];
   alignas(16) float red[4];
   alignas(16) int pairwise[2];
 };
 
-__global__ __launch_bounds__(256) void prep_kernel(Params p, int64_t n_steps) {
+// arrays of the solve phase, placed over Kb / Kh / Kt0 (dead after the tile phase)
+struct SolveShared {
+  alignas(16) float T[STEP][STEP + 1];
+  alignas(16) float X[16][17];
+  alignas(16) __bf16 Tb[STEP][kRowT];    // T diag(beta)
+  alignas(16) __bf16 TbT[STEP][kRowT];   // (T diag(beta))^T
+  alignas(16) __bf16 Pb[STEP][kRowT];    // P
+  alignas(16) __bf16 Ph[STEP][kRowT];    // P T diag(beta)
+};
+static_assert(sizeof(SolveShared) <= sizeof(__bf16) * (2 * STEP + 16) * kRow, "solve arrays must fit over Kb, Kh, Kt0");
+
+__device__ __forceinline__ uint32_t pk_bf16(float lo, float hi) {
+  return (uint32_t)__builtin_bit_cast(uint16_t, (__bf16)lo) | ((uint32_t)__builtin_bit_cast(uint16_t, (__bf16)hi) << 16);
+}
+__device__ __forceinline__ float lo_bf16(uint32_t x) { return __uint_as_float(x << 16); }
+__device__ __forceinline__ float hi_bf16(uint32_t x) { return __uint_as_float(x & 0xffff0000u); }
+
+// diagonal block of chunk cc from per-pair factors exp(L_r - L_j) <= 1 (no reciprocal); raw q in Kh rows,
+// raw k in Kb rows, L of the chunk in L[][]
+__device__ void pairwise_block(PrepShared& sm, int cc, int lane) {
+  for (int pr = lane; pr < 136; pr += 64) {
+    int r = 0;
+    while ((r + 1) * (r + 2) / 2 <= pr) ++r;
+    const int j = pr - r * (r + 1) / 2;                 // j <= r
+    const int R = 16 * cc + r, J = 16 * cc + j;
+    float a = 0.f, pq = 0.f;
+    for (int x = 0; x < D; ++x) {
+      const float e = __builtin_amdgcn_exp2f(sm.L[r][x] - sm.L[j][x]);
+      const float kj = (float)sm.Kb[J][x] * e;
+      a += (float)sm.Kb[R][x] * kj;
+      pq += (float)sm.Kh[R][x] * kj;
+    }
+    sm.A[R][J] = (j < r) ? sm.beta[R] * a : 0.f;
+    sm.P[R][J] = pq;
+  }
+  for (int pr = lane; pr < 256; pr += 64) {            // upper triangle of the block
+    const int r = pr >> 4, j = pr & 15;
+    if (j > r) { sm.A[16 * cc + r][16 * cc + j] = 0.f; sm.P[16 * cc + r][16 * cc + j] = 0.f; }
+  }
+}
+
+__global__ __launch_bounds__(256, 2) void prep_kernel(Params p, int64_t n_steps) {
   extern __shared__ __align__(16) unsigned char smem_raw[];
   PrepShared& sm = *reinterpret_cast<PrepShared*>(smem_raw);
+  SolveShared& so = *reinterpret_cast<SolveShared*>(&sm.Kb[0][0]);
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
   const int li = lane & 15, lg = lane >> 4;
@@ -114,43 +159,53 @@ __global__ __launch_bounds__(256) void prep_kernel(Params p, int64_t n_steps) {
   const uint16_t* beta = (const uint16_t*)p.beta + bh * T;
   unsigned char* rec = (unsigned char*)p.workspace + (bh * n_steps + s) * (int64_t)kRecBytes;
 
-  // ---- phase 1: gate, chunk-local prefix, scaled operands.  Thread = (channel, chunk).
-  const int ch = tid & (D - 1);
-  const int c = tid >> 7;
-  float qv[16], kv[16], eL[16], wv[16];
-  // all loads first (addresses clamped into the sequence), so they are in flight together
+  // ---- phase 1: gate, chunk-local prefix, scaled operands
+  const int c = tid >> 7, pair = (tid >> 1) & 63, half = tid & 1;
+  const int ch = 2 * pair;
+  const int pos0 = 16 * c + 8 * half;
+  uint32_t qq[8], kk[8], ww[8];
 #pragma unroll
-  for (int l = 0; l < 16; ++l) {
-    const int64_t t = t0 + 16 * c + l;
+  for (int j = 0; j < 8; ++j) {     // all loads in flight together; addresses clamped into the sequence
+    const int64_t t = t0 + pos0 + j;
     const int64_t tc = t < T ? t : T - 1;
-    wv[l] = bf(w, tc * D + ch);
-    qv[l] = bf(q, tc * D + ch);
-    kv[l] = bf(k, tc * D + ch);
+    qq[j] = *reinterpret_cast<const uint32_t*>(q + tc * D + ch);
+    kk[j] = *reinterpret_cast<const uint32_t*>(k + tc * D + ch);
+    ww[j] = *reinterpret_cast<const uint32_t*>(w + tc * D + ch);
   }
-  float Lp = 0.f;
-#pragma unroll
-  for (int l = 0; l < 16; ++l) {
-    const int pp = 16 * c + l;
-    const bool ok = t0 + pp < T;
-    qv[l] = ok ? qv[l] : 0.f;
-    kv[l] = ok ? kv[l] : 0.f;
-    Lp += ok ? gate_log2(wv[l], p.g_min, p.unbounded) : 0.f;
-    sm.L[pp][ch] = Lp;
-    eL[l] = __builtin_amdgcn_exp2f(Lp);
-    const float emL = __builtin_amdgcn_exp2f(-Lp);
-    sm.Qraw[pp][ch] = (__bf16)qv[l];
-    sm.Kraw[pp][ch] = (__bf16)kv[l];
-    sm.Qb[pp][ch] = (__bf16)(qv[l] * eL[l]);
-    sm.Kb[pp][ch] = (__bf16)(kv[l] * eL[l]);
-    sm.Kh[pp][ch] = (__bf16)(kv[l] * emL);
-  }
-  sm.Gam[c][ch] = Lp;
   if (tid < STEP) sm.beta[tid] = (t0 + tid < T) ? bf(beta, t0 + tid) : 0.f;
-  // span of this chunk: min over channels (each half of the block owns one chunk)
-  float m = Lp;
+  float L0[8], L1[8];               // prefix within this thread's 8 positions, channels ch and ch+1
+  float a0 = 0.f, a1 = 0.f;
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    const bool ok = t0 + pos0 + j < T;
+    if (!ok) { qq[j] = 0u; kk[j] = 0u; }
+    a0 += ok ? gate_log2(lo_bf16(ww[j]), p.g_min, p.unbounded) : 0.f;
+    a1 += ok ? gate_log2(hi_bf16(ww[j]), p.g_min, p.unbounded) : 0.f;
+    L0[j] = a0;
+    L1[j] = a1;
+  }
+  const float o0 = __shfl_xor(a0, 1), o1 = __shfl_xor(a1, 1);   // the other half's total
+  const float base0 = half ? o0 : 0.f, base1 = half ? o1 : 0.f;
+  const float gam0 = a0 + o0, gam1 = a1 + o1;                   // chunk span per channel (log2 units)
+#pragma unroll
+  for (int j = 0; j < 8; ++j) { L0[j] += base0; L1[j] += base1; }
+  if (half == 0) { sm.Gam[c][ch] = gam0; sm.Gam[c][ch + 1] = gam1; }
+  float m = fminf(gam0, gam1);
 #pragma unroll
   for (int off = 32; off > 0; off >>= 1) m = fminf(m, __shfl_xor(m, off));
   if (lane == 0) sm.red[wave] = m;
+  float eL0[8], eL1[8];
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    const int pp = pos0 + j;
+    eL0[j] = __builtin_amdgcn_exp2f(L0[j]);
+    eL1[j] = __builtin_amdgcn_exp2f(L1[j]);
+    const float q0 = lo_bf16(qq[j]), q1 = hi_bf16(qq[j]), k0 = lo_bf16(kk[j]), k1 = hi_bf16(kk[j]);
+    *reinterpret_cast<uint32_t*>(&sm.Qb[pp][ch]) = pk_bf16(q0 * eL0[j], q1 * eL1[j]);
+    *reinterpret_cast<uint32_t*>(&sm.Kb[pp][ch]) = pk_bf16(k0 * eL0[j], k1 * eL1[j]);
+    *reinterpret_cast<uint32_t*>(&sm.Kh[pp][ch]) =
+        pk_bf16(k0 * __builtin_amdgcn_exp2f(-L0[j]), k1 * __builtin_amdgcn_exp2f(-L1[j]));
+  }
   __syncthreads();
 
   const bool valid0 = t0 < T;
@@ -159,9 +214,9 @@ __global__ __launch_bounds__(256) void prep_kernel(Params p, int64_t n_steps) {
   const float span1 = fminf(sm.red[2], sm.red[3]) * kLn2;
   const bool flag0 = valid0 && span0 < kSpanLimit;
   const bool flag1 = valid1 && span1 < kSpanLimit;
+  const bool pw0 = p.force_fallback || (flag0 && !p.disable_fallback);
+  const bool pw1 = p.force_fallback || (flag1 && !p.disable_fallback);
   if (tid == 0) {
-    sm.pairwise[0] = (p.force_fallback || (flag0 && !p.disable_fallback)) ? 1 : 0;
-    sm.pairwise[1] = (p.force_fallback || (flag1 && !p.disable_fallback)) ? 1 : 0;
     StepMeta mt;
     mt.span[0] = valid0 ? span0 : __int_as_float(0x7f800000);
     mt.span[1] = valid1 ? span1 : __int_as_float(0x7f800000);
@@ -171,88 +226,109 @@ __global__ __launch_bounds__(256) void prep_kernel(Params p, int64_t n_steps) {
   }
   // step-level quantities (G referenced to the start of the step)
   {
-    const float Gam0 = sm.Gam[0][ch], Gam1 = sm.Gam[1][ch];
-    const float base = (c == 0) ? 0.f : Gam0;               // G = base + L
-    const float egBase = __builtin_amdgcn_exp2f(base);       // e^{Gam_0} for chunk 1
-    const float eGam1 = __builtin_amdgcn_exp2f(Gam1);
+    const float G00 = sm.Gam[0][ch], G01 = sm.Gam[0][ch + 1];      // Gam_0 of my two channels
+    const float G10 = sm.Gam[1][ch], G11 = sm.Gam[1][ch + 1];      // Gam_1
+    const float gc0 = c ? G10 : G00, gc1 = c ? G11 : G01;           // Gam of my chunk
+    const float e00 = __builtin_amdgcn_exp2f(G00), e01 = __builtin_amdgcn_exp2f(G01);
+    const float s0 = c ? e00 : 1.f, s1 = c ? e01 : 1.f;            // e^{G - L}: 1 in chunk 0, e^{Gam_0} in chunk 1
+    const float u0 = c ? 1.f : __builtin_amdgcn_exp2f(G10), u1 = c ? 1.f : __builtin_amdgcn_exp2f(G11);  // e^{Gam_1} for chunk 0
+    uint32_t kb0[4], kb1[4], kt0[4], kt1[4];
 #pragma unroll
-    for (int l = 0; l < 16; ++l) {
-      const int pp = 16 * c + l;
-      const float Lq = sm.L[pp][ch];
-      const float eG = eL[l] * egBase;                       // e^{G} (both factors <= 1)
-      sm.Qbar[pp][ch] = qv[l] * eG;
-      sm.KbarT[ch][pp] = (__bf16)(kv[l] * eG);
-      const float eGamL = __builtin_amdgcn_exp2f(sm.Gam[c][ch] - Lq);   // e^{Gam_c - L} <= 1
-      if (c == 0) {
-        sm.Kt0[l][ch] = (__bf16)(kv[l] * eGamL);
-        sm.KtilT[ch][pp] = (__bf16)(kv[l] * eGamL * eGam1);        // e^{Gam_0 + Gam_1 - G}
+    for (int j = 0; j < 8; ++j) {
+      const float k0 = lo_bf16(kk[j]), k1 = hi_bf16(kk[j]);
+      const float eg0 = __builtin_amdgcn_exp2f(gc0 - L0[j]), eg1 = __builtin_amdgcn_exp2f(gc1 - L1[j]);   // e^{Gam_c - L} <= 1
+      const float kbar0 = k0 * eL0[j] * s0, kbar1 = k1 * eL1[j] * s1;
+      const float ktil0 = k0 * eg0 * u0, ktil1 = k1 * eg1 * u1;
+      if (j & 1) {
+        kb0[j >> 1] |= (uint32_t)__builtin_bit_cast(uint16_t, (__bf16)kbar0) << 16;
+        kb1[j >> 1] |= (uint32_t)__builtin_bit_cast(uint16_t, (__bf16)kbar1) << 16;
+        kt0[j >> 1] |= (uint32_t)__builtin_bit_cast(uint16_t, (__bf16)ktil0) << 16;
+        kt1[j >> 1] |= (uint32_t)__builtin_bit_cast(uint16_t, (__bf16)ktil1) << 16;
       } else {
-        sm.KtilT[ch][pp] = (__bf16)(kv[l] * eGamL);
+        kb0[j >> 1] = __builtin_bit_cast(uint16_t, (__bf16)kbar0);
+        kb1[j >> 1] = __builtin_bit_cast(uint16_t, (__bf16)kbar1);
+        kt0[j >> 1] = __builtin_bit_cast(uint16_t, (__bf16)ktil0);
+        kt1[j >> 1] = __builtin_bit_cast(uint16_t, (__bf16)ktil1);
+      }
+      if (c == 0) *reinterpret_cast<uint32_t*>(&sm.Kt0[pos0 + j][ch]) = pk_bf16(k0 * eg0, k1 * eg1);
+    }
+    typedef __attribute__((__vector_size__(16))) uint32_t u32x4;
+    *reinterpret_cast<u32x4*>(&sm.KbarT[ch][pos0]) = u32x4{kb0[0], kb0[1], kb0[2], kb0[3]};
+    *reinterpret_cast<u32x4*>(&sm.KbarT[ch + 1][pos0]) = u32x4{kb1[0], kb1[1], kb1[2], kb1[3]};
+    *reinterpret_cast<u32x4*>(&sm.KtilT[ch][pos0]) = u32x4{kt0[0], kt0[1], kt0[2], kt0[3]};
+    *reinterpret_cast<u32x4*>(&sm.KtilT[ch + 1][pos0]) = u32x4{kt1[0], kt1[1], kt1[2], kt1[3]};
+    if (c == 0 && half == 0) {
+      sm.eGam0[ch] = e00;
+      sm.eGam0[ch + 1] = e01;
+      // e^{Gam_step}, grouped by the scan's lane groups: index g*32 + t*4 + r <-> channel 16t + 4g + r
+      float* eg = reinterpret_cast<float*>(rec + kOffEg);
+#pragma unroll
+      for (int x = 0; x < 2; ++x) {
+        const int cx = ch + x, t = cx >> 4, g = (cx >> 2) & 3, r = cx & 3;
+        eg[g * 32 + t * 4 + r] = __builtin_amdgcn_exp2f(x ? G01 + G11 : G00 + G10);
       }
     }
-    if (c == 0) {   // e^{Gam_step}, grouped by the scan's lane groups: index g*32 + t*4 + r <-> channel 16t + 4g + r
-      const int t = ch >> 4, g = (ch >> 2) & 3, r = ch & 3;
-      reinterpret_cast<float*>(rec + kOffEg)[g * 32 + t * 4 + r] = __builtin_amdgcn_exp2f(Gam0 + Gam1);
+    if (pw0 && c == 0) {   // per-pair fallback inputs for chunk 0: L, raw k (in Kb rows), raw q (in Kh rows)
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        const int l = 8 * half + j;
+        sm.L[l][ch] = L0[j]; sm.L[l][ch + 1] = L1[j];
+        *reinterpret_cast<uint32_t*>(&sm.Kb[l][ch]) = kk[j];
+        *reinterpret_cast<uint32_t*>(&sm.Kh[l][ch]) = qq[j];
+      }
     }
   }
   __syncthreads();
 
   // ---- phase 2: the 32x32 tiles.  wave 0: diagonal block of chunk 0 (A and P), wave 1: chunk 1,
   // wave 2: A coupling chunk 1 to chunk 0, wave 3: P coupling chunk 1 to chunk 0.
-  {
-    const int cc = (wave == 0) ? 0 : 1;
-    if (wave <= 1 && sm.pairwise[cc]) {
-      // per-pair decay factors exp(L_r - L_j) <= 1 (no reciprocal), vector ALUs
-      for (int pr = lane; pr < 136; pr += 64) {
-        int r = 0;
-        while ((r + 1) * (r + 2) / 2 <= pr) ++r;
-        const int j = pr - r * (r + 1) / 2;             // j <= r
-        const int R = 16 * cc + r, J = 16 * cc + j;
-        float a = 0.f, pq = 0.f;
-        for (int x = 0; x < D; ++x) {
-          const float e = __builtin_amdgcn_exp2f(sm.L[R][x] - sm.L[J][x]);
-          const float kj = (float)sm.Kraw[J][x] * e;
-          a += (float)sm.Kraw[R][x] * kj;
-          pq += (float)sm.Qraw[R][x] * kj;
-        }
-        sm.A[R][J] = (j < r) ? sm.beta[R] * a : 0.f;
-        sm.P[R][J] = pq;
-      }
-      for (int pr = lane; pr < 256; pr += 64) {         // upper triangle of the block
-        const int r = pr >> 4, j = pr & 15;
-        if (j > r) { sm.A[16 * cc + r][16 * cc + j] = 0.f; sm.P[16 * cc + r][16 * cc + j] = 0.f; }
-      }
-    } else if (wave <= 1) {
-      floatx4 accA = {0, 0, 0, 0}, accP = {0, 0, 0, 0};
+  if (wave == 0 && pw0) {
+    pairwise_block(sm, 0, lane);
+  } else if (wave <= 1 && !(wave == 1 && pw1)) {
+    const int cc = wave;
+    floatx4 accA = {0, 0, 0, 0}, accP = {0, 0, 0, 0};
 #pragma unroll
-      for (int kk = 0; kk < 4; ++kk) {
-        const int col = 32 * kk + 8 * lg;
-        const bf16x8 bk = ld8(&sm.Kh[16 * cc + li][col]);
-        accA = mfma(ld8(&sm.Kb[16 * cc + li][col]), bk, accA);
-        accP = mfma(ld8(&sm.Qb[16 * cc + li][col]), bk, accP);
-      }
+    for (int kk4 = 0; kk4 < 4; ++kk4) {
+      const int col = 32 * kk4 + 8 * lg;
+      const bf16x8 bk = ld8(&sm.Kh[16 * cc + li][col]);
+      accA = mfma(ld8(&sm.Kb[16 * cc + li][col]), bk, accA);
+      accP = mfma(ld8(&sm.Qb[16 * cc + li][col]), bk, accP);
+    }
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int row = 4 * lg + r;                     // D[row][li]
-        const int R = 16 * cc + row, J = 16 * cc + li;
-        sm.A[R][J] = (li < row) ? sm.beta[R] * accA[r] : 0.f;
-        sm.P[R][J] = (li <= row) ? accP[r] : 0.f;
-      }
-    } else {
-      floatx4 acc = {0, 0, 0, 0};
+    for (int r = 0; r < 4; ++r) {
+      const int row = 4 * lg + r;                     // D[row][li]
+      const int R = 16 * cc + row, J = 16 * cc + li;
+      sm.A[R][J] = (li < row) ? sm.beta[R] * accA[r] : 0.f;
+      sm.P[R][J] = (li <= row) ? accP[r] : 0.f;
+    }
+  } else if (wave >= 2) {
+    floatx4 acc = {0, 0, 0, 0};
 #pragma unroll
-      for (int kk = 0; kk < 4; ++kk) {
-        const int col = 32 * kk + 8 * lg;
-        const bf16x8 a = (wave == 2) ? ld8(&sm.Kb[16 + li][col]) : ld8(&sm.Qb[16 + li][col]);
-        acc = mfma(a, ld8(&sm.Kt0[li][col]), acc);
-      }
+    for (int kk4 = 0; kk4 < 4; ++kk4) {
+      const int col = 32 * kk4 + 8 * lg;
+      const bf16x8 a = (wave == 2) ? ld8(&sm.Kb[16 + li][col]) : ld8(&sm.Qb[16 + li][col]);
+      acc = mfma(a, ld8(&sm.Kt0[li][col]), acc);
+    }
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int R = 16 + 4 * lg + r;
-        if (wave == 2) { sm.A[R][li] = sm.beta[R] * acc[r]; sm.A[4 * lg + r][16 + li] = 0.f; }
-        else { sm.P[R][li] = acc[r]; sm.P[4 * lg + r][16 + li] = 0.f; }
+    for (int r = 0; r < 4; ++r) {
+      const int R = 16 + 4 * lg + r;
+      if (wave == 2) { sm.A[R][li] = sm.beta[R] * acc[r]; sm.A[4 * lg + r][16 + li] = 0.f; }
+      else { sm.P[R][li] = acc[r]; sm.P[4 * lg + r][16 + li] = 0.f; }
+    }
+  }
+  if (pw1) {   // chunk 1's diagonal block per pair, once its dense operands are no longer needed
+    __syncthreads();
+    if (c == 1) {
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        const int l = 8 * half + j;
+        sm.L[l][ch] = L0[j]; sm.L[l][ch + 1] = L1[j];
+        *reinterpret_cast<uint32_t*>(&sm.Kb[16 + l][ch]) = kk[j];
+        *reinterpret_cast<uint32_t*>(&sm.Kh[16 + l][ch]) = qq[j];
       }
     }
+    __syncthreads();
+    if (wave == 1) pairwise_block(sm, 1, lane);
   }
   __syncthreads();
 
@@ -270,8 +346,8 @@ __global__ __launch_bounds__(256) void prep_kernel(Params p, int64_t n_steps) {
     }
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
-      sm.T[b0 + r][j] = col[r];
-      if (b0 == 16) sm.T[r][j] = 0.f;                 // upper-right block
+      so.T[b0 + r][j] = col[r];
+      if (b0 == 16) so.T[r][j] = 0.f;                 // upper-right block
     }
   }
   __syncthreads();
@@ -280,58 +356,68 @@ __global__ __launch_bounds__(256) void prep_kernel(Params p, int64_t n_steps) {
     const int r = tid >> 4, j = tid & 15;
     float x = 0.f;
 #pragma unroll
-    for (int n = 0; n < 16; ++n) x += sm.A[16 + r][n] * sm.T[n][j];
-    sm.X[r][j] = x;
+    for (int n = 0; n < 16; ++n) x += sm.A[16 + r][n] * so.T[n][j];
+    so.X[r][j] = x;
   }
   __syncthreads();
   {
     const int r = tid >> 4, j = tid & 15;
     float x = 0.f;
 #pragma unroll
-    for (int mm = 0; mm < 16; ++mm) x += sm.T[16 + r][16 + mm] * sm.X[mm][j];
-    sm.T[16 + r][j] = -x;
+    for (int mm = 0; mm < 16; ++mm) x += so.T[16 + r][16 + mm] * so.X[mm][j];
+    so.T[16 + r][j] = -x;
   }
   __syncthreads();
   // T diag(beta) (row-major and transposed) and P in bf16
   for (int e = tid; e < STEP * STEP; e += 256) {
     const int r = e >> 5, j = e & 31;
-    const __bf16 tb = (__bf16)(sm.T[r][j] * sm.beta[j]);
-    sm.Tb[r][j] = tb;
-    sm.TbT[j][r] = tb;
-    sm.Pb[r][j] = (__bf16)sm.P[r][j];
+    const __bf16 tb = (__bf16)(so.T[r][j] * sm.beta[j]);
+    so.Tb[r][j] = tb;
+    so.TbT[j][r] = tb;
+    so.Pb[r][j] = (__bf16)sm.P[r][j];
   }
   __syncthreads();
   // Phat = P T diag(beta) on MFMA: wave w computes the 16x16 tile (w >> 1, w & 1)
   {
     const int mt = wave >> 1, nt = wave & 1;
-    const floatx4 d = mfma(ld8(&sm.Pb[16 * mt + li][8 * lg]), ld8(&sm.TbT[16 * nt + li][8 * lg]), floatx4{0, 0, 0, 0});
+    const floatx4 d = mfma(ld8(&so.Pb[16 * mt + li][8 * lg]), ld8(&so.TbT[16 * nt + li][8 * lg]), floatx4{0, 0, 0, 0});
 #pragma unroll
-    for (int r = 0; r < 4; ++r) sm.Ph[16 * mt + 4 * lg + r][16 * nt + li] = (__bf16)d[r];
+    for (int r = 0; r < 4; ++r) so.Ph[16 * mt + 4 * lg + r][16 * nt + li] = (__bf16)d[r];
   }
-  __syncthreads();
 
   // ---- phase 4: W^T = Kbar^T (T diag(beta))^T on MFMA; wave owns channel tiles 2w, 2w+1
+  floatx4 wd[2][2];
   {
     const int u = wave;
 #pragma unroll
-    for (int mt = 0; mt < 2; ++mt) {
-      floatx4 d[2];
+    for (int mt = 0; mt < 2; ++mt)
 #pragma unroll
       for (int h = 0; h < 2; ++h) {
         const int nt = 2 * u + h;
-        d[h] = mfma(ld8(&sm.KbarT[16 * nt + li][8 * lg]), ld8(&sm.Tb[16 * mt + li][8 * lg]), floatx4{0, 0, 0, 0});
-#pragma unroll
-        for (int r = 0; r < 4; ++r) sm.WnT[16 * nt + 4 * lg + r][16 * mt + li] = (__bf16)(-d[h][r]);
+        wd[mt][h] = mfma(ld8(&sm.KbarT[16 * nt + li][8 * lg]), ld8(&so.Tb[16 * mt + li][8 * lg]), floatx4{0, 0, 0, 0});
       }
+#pragma unroll
+    for (int mt = 0; mt < 2; ++mt) {
       bf16x8 o;
 #pragma unroll
-      for (int r = 0; r < 4; ++r) { o[r] = (__bf16)(-d[0][r]); o[4 + r] = (__bf16)(-d[1][r]); }
+      for (int r = 0; r < 4; ++r) { o[r] = (__bf16)(-wd[mt][0][r]); o[4 + r] = (__bf16)(-wd[mt][1][r]); }
       *reinterpret_cast<bf16x8*>(rec + kOffWn + ((mt * 4 + u) * 64 + lane) * 16) = o;
     }
   }
+  __syncthreads();   // every wave is done reading Kbar^T: (-W)^T goes over it
+  __bf16 (*WnT)[kRowT] = sm.KbarT;
+  {
+    const int u = wave;
+#pragma unroll
+    for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+      for (int h = 0; h < 2; ++h)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) WnT[16 * (2 * u + h) + 4 * lg + r][16 * mt + li] = (__bf16)(-wd[mt][h][r]);
+  }
   __syncthreads();
 
-  // ---- phase 5: Qhat^T = Qbar^T - W^T P^T on MFMA
+  // ---- phase 5: Qhat^T = Qbar^T - W^T P^T on MFMA, Qbar = Qb (chunk 0) or Qb e^{Gam_0} (chunk 1)
   {
     const int u = wave;
 #pragma unroll
@@ -340,8 +426,15 @@ __global__ __launch_bounds__(256) void prep_kernel(Params p, int64_t n_steps) {
 #pragma unroll
       for (int h = 0; h < 2; ++h) {
         const int nt = 2 * u + h;
-        const floatx4 cq = *reinterpret_cast<const floatx4*>(&sm.Qbar[16 * mt + li][16 * nt + 4 * lg]);
-        d[h] = mfma(ld8(&sm.WnT[16 * nt + li][8 * lg]), ld8(&sm.Pb[16 * mt + li][8 * lg]), cq);
+        const int c0 = 16 * nt + 4 * lg;
+        const uint2 qv = *reinterpret_cast<const uint2*>(&sm.Qb[16 * mt + li][c0]);
+        floatx4 cq = {lo_bf16(qv.x), hi_bf16(qv.x), lo_bf16(qv.y), hi_bf16(qv.y)};
+        if (mt == 1) {
+          const floatx4 e = *reinterpret_cast<const floatx4*>(&sm.eGam0[c0]);
+#pragma unroll
+          for (int r = 0; r < 4; ++r) cq[r] *= e[r];
+        }
+        d[h] = mfma(ld8(&WnT[16 * nt + li][8 * lg]), ld8(&so.Pb[16 * mt + li][8 * lg]), cq);
       }
       bf16x8 o;
 #pragma unroll
@@ -353,21 +446,18 @@ __global__ __launch_bounds__(256) void prep_kernel(Params p, int64_t n_steps) {
   // ---- phase 6: the remaining operands, arranged per lane: 8 values = positions {4g..4g+3, 16+4g..16+4g+3}
   for (int e = tid; e < 8 * 64; e += 256) {           // Ktil^T, 8 channel tiles
     const int t = e >> 6, ln = e & 63, i = ln & 15, g = ln >> 4;
-    bf16x8 o;
-#pragma unroll
-    for (int r = 0; r < 4; ++r) { o[r] = sm.KtilT[16 * t + i][4 * g + r]; o[4 + r] = sm.KtilT[16 * t + i][16 + 4 * g + r]; }
-    *reinterpret_cast<bf16x8*>(rec + kOffKt + e * 16) = o;
+    const uint2 x0 = *reinterpret_cast<const uint2*>(&sm.KtilT[16 * t + i][4 * g]);
+    const uint2 x1 = *reinterpret_cast<const uint2*>(&sm.KtilT[16 * t + i][16 + 4 * g]);
+    *reinterpret_cast<uint4*>(rec + kOffKt + e * 16) = uint4{x0.x, x0.y, x1.x, x1.y};
   }
   if (tid < 128) {                                    // T diag(beta) and Phat, 2 row tiles each
     const int mt = tid >> 6, ln = tid & 63, i = ln & 15, g = ln >> 4;
-    bf16x8 o1, o2;
-#pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      o1[r] = sm.Tb[16 * mt + i][4 * g + r]; o1[4 + r] = sm.Tb[16 * mt + i][16 + 4 * g + r];
-      o2[r] = sm.Ph[16 * mt + i][4 * g + r]; o2[4 + r] = sm.Ph[16 * mt + i][16 + 4 * g + r];
-    }
-    *reinterpret_cast<bf16x8*>(rec + kOffTb + tid * 16) = o1;
-    *reinterpret_cast<bf16x8*>(rec + kOffPh + tid * 16) = o2;
+    const uint2 a0 = *reinterpret_cast<const uint2*>(&so.Tb[16 * mt + i][4 * g]);
+    const uint2 a1 = *reinterpret_cast<const uint2*>(&so.Tb[16 * mt + i][16 + 4 * g]);
+    const uint2 b0 = *reinterpret_cast<const uint2*>(&so.Ph[16 * mt + i][4 * g]);
+    const uint2 b1 = *reinterpret_cast<const uint2*>(&so.Ph[16 * mt + i][16 + 4 * g]);
+    *reinterpret_cast<uint4*>(rec + kOffTb + tid * 16) = uint4{a0.x, a0.y, a1.x, a1.y};
+    *reinterpret_cast<uint4*>(rec + kOffPh + tid * 16) = uint4{b0.x, b0.y, b1.x, b1.y};
   }
 }
 
