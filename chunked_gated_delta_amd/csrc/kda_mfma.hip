@@ -698,7 +698,7 @@ __global__ __launch_bounds__(kScanThreads) void scan_kernel(Params p, int64_t n_
   }
 
   // ---------------- output wavefront
-  uint16_t* o = (uint16_t*)p.o + bh * T * D + (4 * lg) * D + d0 + li;
+  uint16_t* o = (uint16_t*)p.o + bh * T * D + li * D + d0 + 4 * lg;
   uint32_t nonfinite = 0, n_valid = 0, n_flagged = 0;
   float min_span = __int_as_float(0x7f800000);
   OutOps cur;
@@ -710,13 +710,15 @@ __global__ __launch_bounds__(kScanThreads) void scan_kernel(Params p, int64_t n_
     bf16x8 sb[4];
 #pragma unroll
     for (int u = 0; u < 4; ++u) sb[u] = ld8((const __bf16*)(cb + (u * 64 + lane) * 16));
+    // O^T = V^T Phat^T + S^T Qhat^T: the same registers with the operand roles swapped, so each lane
+    // ends up with four consecutive columns of one output row (one 8-byte store per row tile)
     floatx4 O[2];
 #pragma unroll
-    for (int mt = 0; mt < 2; ++mt) O[mt] = mfma(cur.ph[mt], cur.vb, zero);
+    for (int mt = 0; mt < 2; ++mt) O[mt] = mfma(cur.vb, cur.ph[mt], zero);
 #pragma unroll
     for (int u = 0; u < 4; ++u)
 #pragma unroll
-      for (int mt = 0; mt < 2; ++mt) O[mt] = mfma(cur.qh[mt * 4 + u], sb[u], O[mt]);
+      for (int mt = 0; mt < 2; ++mt) O[mt] = mfma(sb[u], cur.qh[mt * 4 + u], O[mt]);
     if (slice == 0) {
       n_valid += cur.meta.n_valid;
       n_flagged += cur.meta.n_flagged;
@@ -726,21 +728,19 @@ __global__ __launch_bounds__(kScanThreads) void scan_kernel(Params p, int64_t n_
     uint16_t* os = o + s * STEP * D;
     uint32_t mx = 0;
 #pragma unroll
-    for (int mt = 0; mt < 2; ++mt)
+    for (int mt = 0; mt < 2; ++mt) {
+      if (nrows == STEP || 16 * mt + li < nrows) {
+        *reinterpret_cast<uint2*>(os + (16 * mt) * D) = uint2{pk_bf16(O[mt][0], O[mt][1]), pk_bf16(O[mt][2], O[mt][3])};
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int row = 16 * mt + 4 * lg + r;
-        if (nrows == STEP || row < nrows) {
-          os[(16 * mt + r) * D] = __builtin_bit_cast(uint16_t, (__bf16)O[mt][r]);
-          mx = max(mx, abs_bits(O[mt][r]));
-        }
+        for (int r = 0; r < 4; ++r) mx = max(mx, abs_bits(O[mt][r]));
       }
+    }
     if (mx >= 0x7f800000u) {   // rare: count exactly
 #pragma unroll
       for (int mt = 0; mt < 2; ++mt)
 #pragma unroll
         for (int r = 0; r < 4; ++r)
-          nonfinite += ((nrows == STEP || 16 * mt + 4 * lg + r < nrows) && abs_bits(O[mt][r]) >= 0x7f800000u) ? 1u : 0u;
+          nonfinite += ((nrows == STEP || 16 * mt + li < nrows) && abs_bits(O[mt][r]) >= 0x7f800000u) ? 1u : 0u;
     }
   }
   if (p.stats) {
