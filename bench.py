@@ -9,8 +9,10 @@ resident in HBM.  Prints ONE JSON line on stdout; diagnostics go to stderr.
 The default workload is B=1, H=16, T=65536, dk=dv=128, bf16, g_min=-5,
 chunk 16, S0 = 0 (synthetic inputs, seeded).  `roofline` uses the algorithmic
 bytes of one launch (q, k, v, w, beta read, o written: 1282 B per token-head at
-d = 128 in bf16, plus the fp32 final state) over the main kernel's average
-duration, timed with HIP events recorded on the launch stream by the library.
+d = 128 in bf16, plus the fp32 final state) over the average duration of the
+call's kernels (prep and scan, which run back to back on one stream), timed
+with HIP events that the library records on the launch stream before the first
+kernel and after the last.
 `cpu_baseline` times the fp64 oracle on the host on a bounded sample of the
 same workload (all heads, the first tokens of the sequence).
 """
@@ -29,6 +31,64 @@ if ROOT not in sys.path:
 
 METRIC = "KDA chunk-fwd tokens/s (H16,d128,T64K,bf16) + % of MFMA/HBM roofline"
 HBM_PEAK_GBS = 8000.0
+PROFILES = os.path.join(ROOT, "profiles")
+KERNEL_SOURCES = ["chunked_gated_delta_amd/csrc/kda_mfma.hip", "chunked_gated_delta_amd/csrc/kda_common.hip",
+                  "chunked_gated_delta_amd/csrc/kda_host.cpp", "chunked_gated_delta_amd/csrc/kda_internal.h"]
+
+
+def source_hash() -> str:
+    import hashlib
+    h = hashlib.sha256()
+    for rel in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, rel), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def _pmc_per_kernel(csv_path, counter):
+    """{kernel short name: value of `counter` in the last dispatch, summed over its instances}."""
+    import csv
+    import collections
+    per = collections.defaultdict(lambda: collections.defaultdict(float))
+    for r in csv.DictReader(open(csv_path)):
+        if r["Counter_Name"] != counter:
+            continue
+        name = r["Kernel_Name"]
+        short = ("scan_kernel" if "scan_kernel" in name else "prep_kernel" if "prep_kernel" in name
+                 else "copy" if ("copyBuffer" in name or "elementwise_kernel<16" in name) else None)
+        if short:
+            per[short][int(r["Dispatch_Id"])] += float(r["Counter_Value"])
+    return {k: v[max(v)] for k, v in per.items()}
+
+
+def summarize_pmc(fetch_csv, write_csv, copy_fetch_csv, copy_write_csv, out_json, workload):
+    """Scale FETCH_SIZE / WRITE_SIZE (KiB per dispatch) by what they read for a 1 GiB copy, and store
+    the HBM bytes per forward call (both kernels) together with the kernel source hash."""
+    fetch = _pmc_per_kernel(fetch_csv, "FETCH_SIZE")
+    write = _pmc_per_kernel(write_csv, "WRITE_SIZE")
+    copy_bytes = float(1 << 30)
+    f_scale = copy_bytes / (1024.0 * _pmc_per_kernel(copy_fetch_csv, "FETCH_SIZE")["copy"])
+    w_scale = copy_bytes / (1024.0 * _pmc_per_kernel(copy_write_csv, "WRITE_SIZE")["copy"])
+    kernels = {}
+    for k in ("prep_kernel", "scan_kernel"):
+        kernels[k] = {"fetch_bytes": fetch.get(k, 0.0) * 1024 * f_scale, "write_bytes": write.get(k, 0.0) * 1024 * w_scale}
+    total = sum(v["fetch_bytes"] + v["write_bytes"] for v in kernels.values())
+    out = {"workload": workload, "source_hash": source_hash(), "fetch_scale": f_scale, "write_scale": w_scale,
+           "kernels": kernels, "bytes_per_call": total}
+    with open(out_json, "w") as f:
+        json.dump(out, f, indent=1)
+    print(json.dumps(out, indent=1))
+
+
+def measured_traffic(workload):
+    """HBM bytes per call from the committed counter summary, if it matches the current kernels."""
+    path = os.path.join(PROFILES, f"traffic_{workload}.json")
+    if not os.path.exists(path):
+        return None
+    d = json.load(open(path))
+    if d.get("source_hash") != source_hash() or d.get("workload") != workload:
+        return None
+    return d["bytes_per_call"]
 
 
 def log(*a):
@@ -98,7 +158,13 @@ def main():
     ap.add_argument("--force-fallback", action="store_true")
     ap.add_argument("--copy-calib", action="store_true",
                     help="run only a plain device copy of known size (for scaling HBM counters)")
+    ap.add_argument("--summarize-pmc", nargs=4, metavar=("FETCH_CSV", "WRITE_CSV", "COPY_FETCH_CSV", "COPY_WRITE_CSV"),
+                    help="turn rocprofv3 counter CSVs into profiles/traffic_<workload>.json")
     args = ap.parse_args()
+
+    if args.summarize_pmc:
+        summarize_pmc(*args.summarize_pmc, os.path.join(PROFILES, f"traffic_{args.workload}.json"), args.workload)
+        return
 
     if args.gpus != 1:
         print(f"bench.py measures one GPU only (got --gpus {args.gpus}); this build has no multi-GPU path.",
@@ -152,8 +218,9 @@ def main():
     value = tokens / (wall / args.steps)
     abytes = algorithmic_bytes(wl)
     achieved = abytes / (kern_avg * 1e-3) / 1e9
+    traffic = measured_traffic(wl.name) if args.path != "vector" else None
     roofline = {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
+                "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None if traffic is None else round(traffic),
                 "bytes_per_launch": abytes, "kernel_ms": round(kern_avg, 5),
                 "mfma_tflops": round(mfma_flops(wl) / (kern_avg * 1e-3) / 1e12, 2)}
 

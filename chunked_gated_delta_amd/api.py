@@ -61,7 +61,7 @@ def chunk_fwd(q, k, v, w, beta, S0=None, g_min: float = -5.0, chunk: int = 16, *
     unbounded gate.  Returns (o, S_final, stats) with stats an int32[4] device
     tensor (see decode_stats) or None.  Asynchronous on `stream` (default: the
     current torch stream).  `events` = (begin, end) HipEvent pair recorded
-    around the main kernel.
+    before the first kernel of the call and after its last.
     """
     if q.dim() != 4:
         raise ValueError("q must be [B,H,T,dk]")
