@@ -34,7 +34,7 @@ class KdaStats(ctypes.Structure):
 
 class KdaOpts(ctypes.Structure):
     _fields_ = [("disable_fallback", ctypes.c_int32), ("force_fallback", ctypes.c_int32),
-                ("path", ctypes.c_int32), ("reserved", ctypes.c_int32),
+                ("path", ctypes.c_int32), ("seg_steps", ctypes.c_int32),
                 ("ev_begin", ctypes.c_void_p), ("ev_end", ctypes.c_void_p)]
 
 

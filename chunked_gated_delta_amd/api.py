@@ -53,7 +53,7 @@ def workspace_bytes(B, H, T, dk, dv, dtype=torch.bfloat16, chunk=16) -> int:
 def chunk_fwd(q, k, v, w, beta, S0=None, g_min: float = -5.0, chunk: int = 16, *,
               out=None, S_final=None, stats: bool = True, workspace=None, stream=None,
               disable_fallback: bool = False, force_fallback: bool = False,
-              path: str = "auto", events=None):
+              path: str = "auto", events=None, seg_steps: int = 0):
     """KDA chunked forward through kda_chunk_fwd_ex.
 
     q, k, w: [B,H,T,dk]; v: [B,H,T,dv]; beta: [B,H,T] (all bf16 or all fp32,
@@ -61,7 +61,8 @@ def chunk_fwd(q, k, v, w, beta, S0=None, g_min: float = -5.0, chunk: int = 16, *
     unbounded gate.  Returns (o, S_final, stats) with stats an int32[4] device
     tensor (see decode_stats) or None.  Asynchronous on `stream` (default: the
     current torch stream).  `events` = (begin, end) HipEvent pair recorded
-    before the first kernel of the call and after its last.
+    before the first kernel of the call and after its last.  `seg_steps` > 0
+    fixes the matrix-core path's sequence segment length (in 32-token steps).
     """
     if q.dim() != 4:
         raise ValueError("q must be [B,H,T,dk]")
@@ -93,7 +94,7 @@ def chunk_fwd(q, k, v, w, beta, S0=None, g_min: float = -5.0, chunk: int = 16, *
     st = torch.empty(4, dtype=torch.int32, device=dev) if stats else None
     if stream is None:
         stream = torch.cuda.current_stream(dev)
-    opts = KdaOpts(int(bool(disable_fallback)), int(bool(force_fallback)), _PATHS[path], 0,
+    opts = KdaOpts(int(bool(disable_fallback)), int(bool(force_fallback)), _PATHS[path], int(seg_steps),
                    events[0].handle if events else None, events[1].handle if events else None)
     with torch.cuda.device(dev):
         rc = _lib.load().kda_chunk_fwd_ex(

@@ -95,7 +95,7 @@ int kda_chunk_fwd_ex(const void* q, const void* k, const void* v, const void* w,
   if (chunk != kda::kChunk) return KDA_ERR_UNSUPPORTED;
   if ((rc = check_gmin(g_min)) != KDA_OK) return rc;
   if (opts) {
-    if (opts->reserved != 0) return KDA_ERR_ARG;
+    if (opts->seg_steps < 0) return KDA_ERR_ARG;
     if (opts->disable_fallback && opts->force_fallback) return KDA_ERR_ARG;
     if (opts->path < 0 || opts->path > 2) return KDA_ERR_UNSUPPORTED;
   }
@@ -142,10 +142,12 @@ int kda_chunk_fwd_ex(const void* q, const void* k, const void* v, const void* w,
   p.stats = stats;
   p.disable_fallback = opts ? opts->disable_fallback : 0;
   p.force_fallback = opts ? opts->force_fallback : 0;
+  p.seg_steps = opts ? opts->seg_steps : 0;
 
   const int path = T > 0 ? pick_path(p, opts) : 1;
   if (path < 0) return KDA_ERR_UNSUPPORTED;
   if (path == 2 && need_ws > 0 && (!workspace || workspace_bytes < need_ws)) return KDA_ERR_ARG;
+  if (path == 2 && !kda::mfma_seg_steps_ok(T, p.seg_steps)) return KDA_ERR_ARG;
 
   // ---- launches (first HIP call of the entry point)
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);

@@ -24,6 +24,7 @@ struct Params {
   size_t workspace_bytes;
   kda_stats_t* stats;
   int disable_fallback, force_fallback;
+  int64_t seg_steps;   // matrix-core path: steps of 32 tokens per segment, 0 = automatic
   __host__ __device__ int64_t n_chunks() const { return (T + kChunk - 1) / kChunk; }
 };
 
@@ -36,6 +37,7 @@ hipError_t launch_gate_prefix(const void* w, float g_min, int unbounded, int64_t
 hipError_t launch_vec(const Params& p, hipStream_t s);                 // plain fp32 vector path
 bool mfma_supported(const Params& p);                                   // matrix-core path available?
 size_t mfma_workspace_bytes(int64_t B, int64_t H, int64_t T, int64_t dk, int64_t dv);
+bool mfma_seg_steps_ok(int64_t T, int64_t seg_steps);                    // forced segment length allowed?
 hipError_t launch_mfma(const Params& p, hipStream_t s, hipEvent_t ev_begin, hipEvent_t ev_end);
 
 // ---------------------------------------------------------------- device helpers

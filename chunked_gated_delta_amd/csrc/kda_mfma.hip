@@ -461,47 +461,53 @@ __global__ __launch_bounds__(256, 2) void prep_kernel(Params p, int64_t n_steps)
   }
 }
 
-// ------------------------------------------------------------------ scan kernel
+// ------------------------------------------------------------------ segmented scan
+//
+// Given the records, the step map S -> diag(e^{Gam}) S + Ktil^T (T diag(beta) V - W S) is affine in S,
+// so the map of a run of steps is S_end = M S_start + X, with M (dk x dk) the product of the step
+// transitions diag(e^{Gam}) - Ktil^T W and X the run's result from a zero state.  The steps of every
+// (b, h) are cut into P segments of L steps:
+//   seg_state_kernel    (b, h, segment j < P-1): X_j and M_j, both carried as 128 state columns through
+//                       the step recurrence (M from the identity, with no V term)
+//   seg_combine_kernel  (b, h, 16-column slice): S_start(j+1) = M_j S_start(j) + X_j, serially over j
+//   seg_out_kernel      (b, h, segment j): the recurrence from S_start(j) with the outputs
+//                       O = Qhat S + Phat V; the last segment writes S_final
+// Every workgroup keeps all 128 columns of its segment's state, so each record is read from memory
+// once per segment.  Within a workgroup, wavefront w owns the 16-column slice w (seg_state: one slice
+// of X and one of M); all wavefronts also stream the records into a ring of LDS slots with
+// direct-to-LDS 16-byte loads, kRingSlots-1 steps ahead of the compute.
 
-__device__ __forceinline__ bf16x8 pack2(floatx4 a, floatx4 b) {
-  bf16x8 o;
-#pragma unroll
-  for (int r = 0; r < 4; ++r) { o[r] = (__bf16)a[r]; o[4 + r] = (__bf16)b[r]; }
-  return o;
-}
+constexpr int kRingSlots = 4;
+constexpr int kSegWaves = 8;
+constexpr int kSegThreads = 64 * kSegWaves;
+constexpr int kVTileBytes = STEP * D * 2;                    // one step of V, all 128 columns, row-major
+constexpr int kSegState = D * D * 4;                         // bytes of one 128 x 128 fp32 block (64 KiB)
+constexpr int kMaxSeg = 32;                                  // segments per (b, h)
 
-// Ring of records in LDS: each slot holds one step's record followed by the
-// 32 x 16 slice of V for that step.  Six loader wavefronts keep kRing-1 steps
-// in flight with direct-to-LDS 16-byte loads (one wavefront sustains only
-// ~17 GB/s of such loads, so the stream is spread over several), and
-// guarantee that the two oldest slots are complete at every step barrier, so
-// the compute wavefronts can read step s+1's operands while step s is still
-// computing.  The step's work is split over two
-// compute wavefronts on different SIMDs (one wavefront's vector ALU issues too
-// slowly for both halves):
-//   chain wave   U = T diag(beta) V - W S;  S <- diag(e^Gam) S + Ktil^T U;
-//                publishes the bf16 copy of the state entering each step
-//   output wave  O = Qhat S + Phat V from that copy; stores o
-constexpr int kRing = 5;
-constexpr int kSlotBytes = kRecBytes + 1024;
-constexpr int kLoadsPerStep = kRecBytes / 1024 + 1;   // 29 record chunks + 1 V chunk
-constexpr int kLoaders = 6;
-constexpr int kLoadsPerLoader = kLoadsPerStep / kLoaders;
-constexpr int kStateBufBytes = 4 * 64 * 16;          // bf16 state operands, [u 4][lane 64] x 16 B
-static_assert(kLoadsPerStep % kLoaders == 0, "loads must split evenly over the loader waves");
-static_assert(kLoadsPerLoader * (kRing - 1) <= 63, "outstanding loads must fit the vmcnt counter");
-static_assert(kRing >= 4, "two complete slots plus two in flight");
-constexpr size_t kScanSmem = (size_t)kRing * kSlotBytes + 2 * kStateBufBytes;
-static_assert(kScanSmem <= 163840, "LDS budget");
-constexpr int kScanThreads = 64 * (2 + kLoaders);
+// seg_out slot: the whole record, then V
+constexpr int kOutSlot = kRecBytes + kVTileBytes;
+constexpr int kOutChunks = kOutSlot / 1024;                  // 37
+// seg_state slot: -W, Ktil^T, T diag(beta), e^{Gam} (+ meta), then V
+constexpr int kStWn = 0, kStKt = 8192, kStTb = 16384, kStEg = 18432, kStV = 19456;
+constexpr int kStSlot = kStV + kVTileBytes;
+constexpr int kStChunks = kStSlot / 1024;                    // 27
+constexpr size_t kOutSmem = (size_t)kRingSlots * kOutSlot;
+constexpr size_t kStSmem = (size_t)kRingSlots * kStSlot;
+static_assert(kOutSmem <= 163840 && kStSmem <= 163840, "LDS budget");
+static_assert(kOutSlot % 1024 == 0 && kStSlot % 1024 == 0, "slots are whole 1 KiB chunks");
+static_assert((kOutChunks / kSegWaves + 1) * (kRingSlots - 1) + 4 <= 63, "outstanding loads fit the vmcnt counter");
+
+struct SegPlan {
+  int64_t P, L;            // segments per (b, h) and steps per segment (the last one may be shorter)
+  int64_t off_x, off_m, off_s;   // workspace byte offsets of the X, M and S_start blocks
+};
 
 typedef __attribute__((address_space(3))) void lds_void;
 
 __device__ __forceinline__ void compiler_fence() { __atomic_signal_fence(__ATOMIC_SEQ_CST); }
 
-// Workgroup barrier without a memory fence on global memory: waits only for this wave's
-// shared-memory operations (so its LDS writes are visible after the barrier), never for the
-// loaders' in-flight global loads or the output stores.
+// Workgroup barrier that waits only for this wave's LDS operations (so its LDS writes are visible
+// after it), not for global loads in flight.
 __device__ __forceinline__ void block_barrier() {
   compiler_fence();
   __builtin_amdgcn_s_waitcnt(0xF | (0x3 << 14) | (0x7 << 4) | (0x0 << 8));   // lgkmcnt(0)
@@ -515,23 +521,35 @@ template <int N> __device__ __forceinline__ void wait_vm() {
   __builtin_amdgcn_s_waitcnt((N & 0xF) | ((N >> 4) << 14) | (0x7 << 4) | (0xF << 8));
 }
 
-__device__ __forceinline__ void wait_vm_dyn(int n) {   // n in multiples of kLoadsPerLoader
-  switch (n) {
-    case 0: wait_vm<0>(); break;
-    case 1: wait_vm<kLoadsPerLoader>(); break;
-    case 2: wait_vm<2 * kLoadsPerLoader>(); break;
-    default: wait_vm<3 * kLoadsPerLoader>(); break;
-  }
+// wait until at most k * PER of this wave's memory operations are outstanding (k = steps in flight
+// beyond the one needed, each of at least PER loads; later stores only make the wait longer)
+template <int PER> __device__ __forceinline__ void wait_steps(int64_t k) {
+  if (k <= 0) wait_vm<0>();
+  else if (k == 1) wait_vm<PER>();
+  else wait_vm<2 * PER>();
+}
+static_assert(kRingSlots - 2 <= 2, "wait_steps covers at most two steps in flight");
+
+__device__ __forceinline__ void lds_load16(const void* g, unsigned char* lds) {
+  __builtin_amdgcn_global_load_lds(g, (lds_void*)lds, 16, 0, 0);
 }
 
-// V operand rows {4g+r, 16+4g+r}, column li, from the slot's 32 x 16 V tile; rows at or past nrows are zero
-__device__ __forceinline__ bf16x8 v_operand(const unsigned char* slot, int lg, int li, int nrows) {
-  const __bf16* vr = (const __bf16*)(slot + kRecBytes);
+// one 1 KiB chunk (rows 4c..4c+3) of a step's V tile; rows at or past T re-read row T-1 (masked later)
+__device__ __forceinline__ void load_v_chunk(const uint16_t* v, int64_t T, int64_t step, int c, int lane,
+                                             unsigned char* dst) {
+  int64_t t = step * STEP + 4 * c + (lane >> 4);
+  t = t < T ? t : T - 1;
+  lds_load16(v + t * D + (lane & 15) * 8, dst);
+}
+
+// B operand of V for columns col (rows {4g+r, 16+4g+r}); rows at or past nrows are zero
+__device__ __forceinline__ bf16x8 v_operand(const unsigned char* vt, int lg, int col, int nrows) {
+  const __bf16* vr = (const __bf16*)vt;
   bf16x8 vb;
 #pragma unroll
   for (int r = 0; r < 4; ++r) {
-    vb[r] = vr[(4 * lg + r) * 16 + li];
-    vb[4 + r] = vr[(16 + 4 * lg + r) * 16 + li];
+    vb[r] = vr[(4 * lg + r) * D + col];
+    vb[4 + r] = vr[(16 + 4 * lg + r) * D + col];
   }
   if (nrows < STEP) {
 #pragma unroll
@@ -543,189 +561,266 @@ __device__ __forceinline__ bf16x8 v_operand(const unsigned char* slot, int lg, i
   return vb;
 }
 
+__device__ __forceinline__ bf16x8 pack2(floatx4 a, floatx4 b) {
+  bf16x8 o;
+#pragma unroll
+  for (int r = 0; r < 4; ++r) { o[r] = (__bf16)a[r]; o[4 + r] = (__bf16)b[r]; }
+  return o;
+}
+
 __device__ __forceinline__ uint32_t abs_bits(float x) { return __float_as_uint(x) & 0x7fffffffu; }
-
-struct ChainOps {
-  bf16x8 tb[2], wn[8], kt[8], vb;
-  floatx4 eg[8];
-};
-
-__device__ __forceinline__ void load_chain_ops(ChainOps& c, const unsigned char* rec, int lane, int lg, int li, int nrows) {
-#pragma unroll
-  for (int mt = 0; mt < 2; ++mt) c.tb[mt] = ld8((const __bf16*)(rec + kOffTb + (mt * 64 + lane) * 16));
-#pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    c.wn[i] = ld8((const __bf16*)(rec + kOffWn + (i * 64 + lane) * 16));
-    c.kt[i] = ld8((const __bf16*)(rec + kOffKt + (i * 64 + lane) * 16));
-    c.eg[i] = *reinterpret_cast<const floatx4*>(rec + kOffEg + (lg * 32 + 4 * i) * 4);
-  }
-  c.vb = v_operand(rec, lg, li, nrows);
-}
-
-struct OutOps {
-  bf16x8 ph[2], qh[8], vb;
-  StepMeta meta;
-};
-
-__device__ __forceinline__ void load_out_ops(OutOps& c, const unsigned char* rec, int lane, int lg, int li, int nrows) {
-#pragma unroll
-  for (int mt = 0; mt < 2; ++mt) c.ph[mt] = ld8((const __bf16*)(rec + kOffPh + (mt * 64 + lane) * 16));
-#pragma unroll
-  for (int i = 0; i < 8; ++i) c.qh[i] = ld8((const __bf16*)(rec + kOffQh + (i * 64 + lane) * 16));
-  c.vb = v_operand(rec, lg, li, nrows);
-  c.meta = *reinterpret_cast<const StepMeta*>(rec + kOffMeta);
-}
 
 __device__ __forceinline__ int rows_of(int64_t T, int64_t st) {
   const int64_t rem = T - st * STEP;
   return rem < STEP ? (int)rem : STEP;
 }
 
-__global__ __launch_bounds__(kScanThreads) void scan_kernel(Params p, int64_t n_steps, int xcd_map) {
+// 128 x 16 fp32 slice in D layout (lane (li, lg), tile t, register r <-> row 16t+4lg+r, column li),
+// stored as [t][lane] float4 blocks
+__device__ __forceinline__ void store_slice(float* dst, const floatx4 (&S)[8], int lane) {
+#pragma unroll
+  for (int t = 0; t < 8; ++t) *reinterpret_cast<floatx4*>(dst + (t * 64 + lane) * 4) = S[t];
+}
+__device__ __forceinline__ void load_slice(floatx4 (&S)[8], const float* src, int lane) {
+#pragma unroll
+  for (int t = 0; t < 8; ++t) S[t] = *reinterpret_cast<const floatx4*>(src + (t * 64 + lane) * 4);
+}
+
+// ---- seg_state_kernel: X_j and M_j of segment j < P-1
+__global__ __launch_bounds__(kSegThreads) void seg_state_kernel(Params p, int64_t n_steps, SegPlan sg) {
   extern __shared__ __align__(16) unsigned char ring[];
-  unsigned char* sbuf = ring + (size_t)kRing * kSlotBytes;   // two state buffers
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
   const int li = lane & 15, lg = lane >> 4;
-  const int64_t BH = p.B * p.H;
-  int64_t bh;
-  int slice;
-  if (xcd_map) {   // keep the 8 slices of one (b,h) on the same XCD (workgroups are dealt round-robin over 8 XCDs)
-    const int64_t id = blockIdx.x, x = id & 7, j = id >> 3;
-    bh = (j >> 3) * 8 + x;
-    slice = (int)(j & 7);
-  } else {
-    bh = blockIdx.x >> 3;
-    slice = (int)(blockIdx.x & 7);
-  }
-  if (bh >= BH) return;   // uniform over the workgroup
+  const int64_t nseg = sg.P - 1;
+  const int64_t bh = blockIdx.x / nseg, j = blockIdx.x % nseg;
+  const int64_t s0 = j * sg.L;
+  const int64_t ns = sg.L;                 // never the last segment, so always a full one
   const int64_t T = p.T;
-  const int d0 = slice * 16;
-  const unsigned char* recs = (const unsigned char*)p.workspace + bh * n_steps * (int64_t)kRecBytes;
+  const unsigned char* recs = (const unsigned char*)p.workspace + (bh * n_steps + s0) * (int64_t)kRecBytes;
   const uint16_t* v = (const uint16_t*)p.v + bh * T * D;
+  constexpr int kPer = kStChunks / kSegWaves;          // loads per step of the wave with the fewest
+  auto issue = [&](int64_t i) {
+    unsigned char* slot = ring + (i % kRingSlots) * kStSlot;
+    const unsigned char* src = recs + i * (int64_t)kRecBytes;
+#pragma unroll
+    for (int x = 0; x < (kStChunks + kSegWaves - 1) / kSegWaves; ++x) {
+      const int c = wave + kSegWaves * x;
+      if (c < 18) {                         // -W (record chunks 0..7), Ktil^T and T diag(beta) (16..25)
+        const int rc = c < 8 ? c : c + 8;
+        lds_load16(src + rc * 1024 + lane * 16, slot + c * 1024);
+      } else if (c == 18) {                 // e^{Gam} and meta (record chunk 28)
+        lds_load16(src + 28 * 1024 + lane * 16, slot + kStEg);
+      } else if (c < kStChunks) {
+        load_v_chunk(v, T, s0 + i, c - 19, lane, slot + kStV + (c - 19) * 1024);
+      }
+    }
+  };
+  for (int64_t i = 0; i < kRingSlots - 1 && i < ns; ++i) issue(i);
+
   const floatx4 zero = {0, 0, 0, 0};
-
-  if (wave >= 2) {
-    // ---------------- loader wavefronts
-    const int L = wave - 2;
-    auto issue = [&](int64_t st) {
-      unsigned char* slot = ring + (st % kRing) * kSlotBytes;
-      const unsigned char* src = recs + st * (int64_t)kRecBytes;
+  floatx4 X[8], M[8];
 #pragma unroll
-      for (int x = 0; x < kLoadsPerLoader; ++x) {
-        const int j = L + kLoaders * x;
-        if (j < kLoadsPerStep - 1) {
-          __builtin_amdgcn_global_load_lds((const void*)(src + j * 1024 + lane * 16), (lds_void*)(slot + j * 1024), 16, 0, 0);
-        } else {   // V rows: lane -> (row, 16-byte half); rows past the end read the last row (masked later)
-          int64_t t = st * STEP + (lane >> 1);
-          t = t < T ? t : T - 1;
-          __builtin_amdgcn_global_load_lds((const void*)(v + t * D + d0 + (lane & 1) * 8), (lds_void*)(slot + kRecBytes), 16, 0, 0);
-        }
-      }
-    };
-    for (int64_t st = 0; st < kRing - 1 && st < n_steps; ++st) issue(st);
-    for (int64_t s = 0; s < n_steps; ++s) {
-      // at barrier s, slots s and s+1 must be complete
-      const int64_t issued_max = (s + kRing - 2 < n_steps - 1) ? s + kRing - 2 : n_steps - 1;
-      const int64_t need = (s + 1 < n_steps - 1) ? s + 1 : n_steps - 1;
-      wait_vm_dyn((int)(issued_max - need));
-      block_barrier();
-      if (s + kRing - 1 < n_steps) issue(s + kRing - 1);
-    }
-    return;
+  for (int t = 0; t < 8; ++t) {
+    X[t] = zero;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) M[t][r] = (16 * t + 4 * lg + r == 16 * wave + li) ? 1.f : 0.f;
   }
+  bf16x8 xb[4], mb[4];
+#pragma unroll
+  for (int u = 0; u < 4; ++u) { xb[u] = pack2(X[2 * u], X[2 * u + 1]); mb[u] = pack2(M[2 * u], M[2 * u + 1]); }
 
-  if (wave == 0) {
-    // ---------------- chain wavefront: the state slice lives here, in fp32
-    floatx4 S[8];
-    if (p.S0) {
-#pragma unroll
-      for (int t = 0; t < 8; ++t)
-#pragma unroll
-        for (int r = 0; r < 4; ++r) S[t][r] = p.S0[(bh * D + 16 * t + 4 * lg + r) * D + d0 + li];
-    } else {
-#pragma unroll
-      for (int t = 0; t < 8; ++t) S[t] = zero;
-    }
-    bf16x8 sb[4];
-#pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      sb[u] = pack2(S[2 * u], S[2 * u + 1]);
-      *reinterpret_cast<bf16x8*>(sbuf + (u * 64 + lane) * 16) = sb[u];
-    }
-    ChainOps cur;
-    for (int64_t s = 0; s < n_steps; ++s) {
-      block_barrier();
-      if (s == 0) load_chain_ops(cur, ring, lane, lg, li, rows_of(T, 0));
-      floatx4 cdec[8];
-#pragma unroll
-      for (int t = 0; t < 8; ++t)
-#pragma unroll
-        for (int r = 0; r < 4; ++r) cdec[t][r] = S[t][r] * cur.eg[t][r];
-      floatx4 U[2];
-#pragma unroll
-      for (int mt = 0; mt < 2; ++mt) U[mt] = mfma(cur.tb[mt], cur.vb, zero);
-#pragma unroll
-      for (int u = 0; u < 4; ++u)
-#pragma unroll
-        for (int mt = 0; mt < 2; ++mt) U[mt] = mfma(cur.wn[mt * 4 + u], sb[u], U[mt]);
-      const bf16x8 ub = pack2(U[0], U[1]);
-#pragma unroll
-      for (int t = 0; t < 8; ++t) S[t] = mfma(cur.kt[t], ub, cdec[t]);
-      // operands of the next step (its slot is complete since this step's barrier)
-      if (s + 1 < n_steps) load_chain_ops(cur, ring + ((s + 1) % kRing) * kSlotBytes, lane, lg, li, rows_of(T, s + 1));
-      unsigned char* nb = sbuf + ((s + 1) & 1) * kStateBufBytes;
-#pragma unroll
-      for (int u = 0; u < 4; ++u) {
-        sb[u] = pack2(S[2 * u], S[2 * u + 1]);
-        *reinterpret_cast<bf16x8*>(nb + (u * 64 + lane) * 16) = sb[u];
-      }
-    }
-    uint32_t nonfinite = 0;
-#pragma unroll
-    for (int t = 0; t < 8; ++t)
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        p.S_final[(bh * D + 16 * t + 4 * lg + r) * D + d0 + li] = S[t][r];
-        nonfinite += not_finite(S[t][r]) ? 1u : 0u;
-      }
-    if (p.stats) {
-#pragma unroll
-      for (int off = 32; off > 0; off >>= 1) nonfinite += __shfl_xor(nonfinite, off);
-      if (lane == 0 && nonfinite) atomicAdd(&p.stats->n_nonfinite, nonfinite);
-    }
-    return;
-  }
-
-  // ---------------- output wavefront
-  uint16_t* o = (uint16_t*)p.o + bh * T * D + li * D + d0 + 4 * lg;
-  uint32_t nonfinite = 0, n_valid = 0, n_flagged = 0;
-  float min_span = __int_as_float(0x7f800000);
-  OutOps cur;
-  for (int64_t s = 0; s < n_steps; ++s) {
+  for (int64_t i = 0; i < ns; ++i) {
+    const int64_t issued = (i + kRingSlots - 2 < ns - 1) ? i + kRingSlots - 2 : ns - 1;
+    wait_steps<kPer>(issued - i);
     block_barrier();
-    if (s == 0) load_out_ops(cur, ring, lane, lg, li, rows_of(T, 0));
-    const int nrows = rows_of(T, s);
-    const unsigned char* cb = sbuf + (s & 1) * kStateBufBytes;
-    bf16x8 sb[4];
+    if (i + kRingSlots - 1 < ns) issue(i + kRingSlots - 1);
+    const unsigned char* slot = ring + (i % kRingSlots) * kStSlot;
+    const bf16x8 vb = v_operand(slot + kStV, lg, 16 * wave + li, rows_of(T, s0 + i));
 #pragma unroll
-    for (int u = 0; u < 4; ++u) sb[u] = ld8((const __bf16*)(cb + (u * 64 + lane) * 16));
-    // O^T = V^T Phat^T + S^T Qhat^T: the same registers with the operand roles swapped, so each lane
-    // ends up with four consecutive columns of one output row (one 8-byte store per row tile)
-    floatx4 O[2];
+    for (int t = 0; t < 8; ++t) {
+      const floatx4 eg = *reinterpret_cast<const floatx4*>(slot + kStEg + (lg * 32 + 4 * t) * 4);
 #pragma unroll
-    for (int mt = 0; mt < 2; ++mt) O[mt] = mfma(cur.vb, cur.ph[mt], zero);
+      for (int r = 0; r < 4; ++r) { X[t][r] *= eg[r]; M[t][r] *= eg[r]; }
+    }
+    floatx4 UX[2], UM[2];
+#pragma unroll
+    for (int mt = 0; mt < 2; ++mt) {
+      UX[mt] = mfma(ld8((const __bf16*)(slot + kStTb + (mt * 64 + lane) * 16)), vb, zero);
+      UM[mt] = zero;
+    }
 #pragma unroll
     for (int u = 0; u < 4; ++u)
 #pragma unroll
-      for (int mt = 0; mt < 2; ++mt) O[mt] = mfma(sb[u], cur.qh[mt * 4 + u], O[mt]);
-    if (slice == 0) {
-      n_valid += cur.meta.n_valid;
-      n_flagged += cur.meta.n_flagged;
-      min_span = fminf(min_span, fminf(cur.meta.span[0], cur.meta.span[1]));
+      for (int mt = 0; mt < 2; ++mt) {
+        const bf16x8 wn = ld8((const __bf16*)(slot + kStWn + ((mt * 4 + u) * 64 + lane) * 16));
+        UX[mt] = mfma(wn, xb[u], UX[mt]);
+        UM[mt] = mfma(wn, mb[u], UM[mt]);
+      }
+    const bf16x8 ux = pack2(UX[0], UX[1]), um = pack2(UM[0], UM[1]);
+#pragma unroll
+    for (int t = 0; t < 8; ++t) {
+      const bf16x8 kt = ld8((const __bf16*)(slot + kStKt + (t * 64 + lane) * 16));
+      X[t] = mfma(kt, ux, X[t]);
+      M[t] = mfma(kt, um, M[t]);
     }
-    if (s + 1 < n_steps) load_out_ops(cur, ring + ((s + 1) % kRing) * kSlotBytes, lane, lg, li, rows_of(T, s + 1));
-    uint16_t* os = o + s * STEP * D;
+#pragma unroll
+    for (int u = 0; u < 4; ++u) { xb[u] = pack2(X[2 * u], X[2 * u + 1]); mb[u] = pack2(M[2 * u], M[2 * u + 1]); }
+  }
+  // X_j in slice-major D layout; M_j arranged as the combine's A operands:
+  // [mo 8][mt 8][lane 64][r 4] <-> M[16 mo + (lane & 15)][16 mt + 4 (lane >> 4) + r]
+  const int64_t blk = (bh * sg.P + j) * (int64_t)(kSegState / 4);
+  float* xo = (float*)((unsigned char*)p.workspace + sg.off_x) + blk + wave * 8 * 64 * 4;
+  store_slice(xo, X, lane);
+  float* mo = (float*)((unsigned char*)p.workspace + sg.off_m) + blk;
+#pragma unroll
+  for (int t = 0; t < 8; ++t)
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      // element M[16t + 4lg + r][16 wave + li]
+      const int lane_c = (4 * lg + r) + 16 * (li >> 2);
+      mo[((t * 8 + wave) * 64 + lane_c) * 4 + (li & 3)] = M[t][r];
+    }
+}
+
+// ---- seg_combine_kernel: S_start(j+1) = M_j S_start(j) + X_j for one 16-column slice, in fp32 on the
+// matrix cores (16x16x4 f32).  Wavefront w owns the output row tiles 2w, 2w+1; the contraction runs
+// over k-steps (mt, r) <-> rows {16 mt + 4 g + r} of S, so the D-layout tiles of S are the B operands.
+__global__ __launch_bounds__(256) void seg_combine_kernel(Params p, SegPlan sg) {
+  __shared__ floatx4 Sx[2][8][64];
+  const int tid = threadIdx.x;
+  const int lane = tid & 63, wave = tid >> 6;
+  const int li = lane & 15, lg = lane >> 4;
+  const int64_t bh = blockIdx.x >> 3;
+  const int slice = blockIdx.x & 7;
+  floatx4 cur[2];
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    const int mo = 2 * wave + h;
+#pragma unroll
+    for (int r = 0; r < 4; ++r)
+      cur[h][r] = p.S0 ? p.S0[(bh * D + 16 * mo + 4 * lg + r) * D + 16 * slice + li] : 0.f;
+  }
+  const float* xs = (const float*)((const unsigned char*)p.workspace + sg.off_x);
+  const float* ms = (const float*)((const unsigned char*)p.workspace + sg.off_m);
+  float* ss = (float*)((unsigned char*)p.workspace + sg.off_s);
+  for (int64_t j = 0; j + 1 < sg.P; ++j) {
+    floatx4 (*sx)[64] = Sx[j & 1];
+#pragma unroll
+    for (int h = 0; h < 2; ++h) sx[2 * wave + h][lane] = cur[h];
+    __syncthreads();
+    floatx4 b[8];
+#pragma unroll
+    for (int mt = 0; mt < 8; ++mt) b[mt] = sx[mt][lane];
+    const int64_t blk = (bh * sg.P + j) * (int64_t)(kSegState / 4);
+    const float* xj = xs + blk + slice * 8 * 64 * 4;
+    const float* mj = ms + blk;
+    float* sn = ss + (bh * sg.P + j + 1) * (int64_t)(kSegState / 4) + slice * 8 * 64 * 4;
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const int mo = 2 * wave + h;
+      floatx4 acc = *reinterpret_cast<const floatx4*>(xj + (mo * 64 + lane) * 4);
+#pragma unroll
+      for (int mt = 0; mt < 8; ++mt) {
+        const floatx4 a = *reinterpret_cast<const floatx4*>(mj + ((mo * 8 + mt) * 64 + lane) * 4);
+#pragma unroll
+        for (int r = 0; r < 4; ++r) acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a[r], b[mt][r], acc, 0, 0, 0);
+      }
+      cur[h] = acc;
+      *reinterpret_cast<floatx4*>(sn + (mo * 64 + lane) * 4) = acc;
+    }
+  }
+}
+
+// ---- seg_out_kernel: segment j from S_start(j), with the outputs
+__global__ __launch_bounds__(kSegThreads) void seg_out_kernel(Params p, int64_t n_steps, SegPlan sg) {
+  extern __shared__ __align__(16) unsigned char ring[];
+  const int tid = threadIdx.x;
+  const int lane = tid & 63, wave = tid >> 6;
+  const int li = lane & 15, lg = lane >> 4;
+  const int64_t bh = blockIdx.x / sg.P, j = blockIdx.x % sg.P;
+  const int64_t s0 = j * sg.L;
+  const int64_t ns = (n_steps - s0 < sg.L) ? n_steps - s0 : sg.L;
+  const int64_t T = p.T;
+  const int d0 = 16 * wave;
+  const unsigned char* recs = (const unsigned char*)p.workspace + (bh * n_steps + s0) * (int64_t)kRecBytes;
+  const uint16_t* v = (const uint16_t*)p.v + bh * T * D;
+  constexpr int kPer = kOutChunks / kSegWaves;
+  auto issue = [&](int64_t i) {
+    unsigned char* slot = ring + (i % kRingSlots) * kOutSlot;
+    const unsigned char* src = recs + i * (int64_t)kRecBytes;
+#pragma unroll
+    for (int x = 0; x < (kOutChunks + kSegWaves - 1) / kSegWaves; ++x) {
+      const int c = wave + kSegWaves * x;
+      if (c < kRecBytes / 1024) lds_load16(src + c * 1024 + lane * 16, slot + c * 1024);
+      else if (c < kOutChunks) load_v_chunk(v, T, s0 + i, c - kRecBytes / 1024, lane, slot + c * 1024);
+    }
+  };
+  for (int64_t i = 0; i < kRingSlots - 1 && i < ns; ++i) issue(i);
+
+  const floatx4 zero = {0, 0, 0, 0};
+  floatx4 S[8];
+  if (j > 0) {
+    load_slice(S, (const float*)((const unsigned char*)p.workspace + sg.off_s) +
+                      (bh * sg.P + j) * (int64_t)(kSegState / 4) + wave * 8 * 64 * 4, lane);
+  } else if (p.S0) {
+#pragma unroll
+    for (int t = 0; t < 8; ++t)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) S[t][r] = p.S0[(bh * D + 16 * t + 4 * lg + r) * D + d0 + li];
+  } else {
+#pragma unroll
+    for (int t = 0; t < 8; ++t) S[t] = zero;
+  }
+  bf16x8 sb[4];
+#pragma unroll
+  for (int u = 0; u < 4; ++u) sb[u] = pack2(S[2 * u], S[2 * u + 1]);
+
+  uint16_t* o = (uint16_t*)p.o + bh * T * D + li * D + d0 + 4 * lg;
+  uint32_t nonfinite = 0, n_valid = 0, n_flagged = 0;
+  float min_span = __int_as_float(0x7f800000);
+  for (int64_t i = 0; i < ns; ++i) {
+    const int64_t issued = (i + kRingSlots - 2 < ns - 1) ? i + kRingSlots - 2 : ns - 1;
+    wait_steps<kPer>(issued - i);
+    block_barrier();
+    if (i + kRingSlots - 1 < ns) issue(i + kRingSlots - 1);
+    const unsigned char* slot = ring + (i % kRingSlots) * kOutSlot;
+    const int64_t st = s0 + i;
+    const int nrows = rows_of(T, st);
+    const bf16x8 vb = v_operand(slot + kRecBytes, lg, d0 + li, nrows);
+#pragma unroll
+    for (int t = 0; t < 8; ++t) {
+      const floatx4 eg = *reinterpret_cast<const floatx4*>(slot + kOffEg + (lg * 32 + 4 * t) * 4);
+#pragma unroll
+      for (int r = 0; r < 4; ++r) S[t][r] *= eg[r];
+    }
+    floatx4 U[2], O[2];
+#pragma unroll
+    for (int mt = 0; mt < 2; ++mt) {
+      U[mt] = mfma(ld8((const __bf16*)(slot + kOffTb + (mt * 64 + lane) * 16)), vb, zero);
+      // O^T = V^T Phat^T + S^T Qhat^T: operand roles swapped so each lane holds four consecutive
+      // columns of one output row (one 8-byte store per row tile)
+      O[mt] = mfma(vb, ld8((const __bf16*)(slot + kOffPh + (mt * 64 + lane) * 16)), zero);
+    }
+#pragma unroll
+    for (int u = 0; u < 4; ++u)
+#pragma unroll
+      for (int mt = 0; mt < 2; ++mt) {
+        U[mt] = mfma(ld8((const __bf16*)(slot + kOffWn + ((mt * 4 + u) * 64 + lane) * 16)), sb[u], U[mt]);
+        O[mt] = mfma(sb[u], ld8((const __bf16*)(slot + kOffQh + ((mt * 4 + u) * 64 + lane) * 16)), O[mt]);
+      }
+    const bf16x8 ub = pack2(U[0], U[1]);
+#pragma unroll
+    for (int t = 0; t < 8; ++t) S[t] = mfma(ld8((const __bf16*)(slot + kOffKt + (t * 64 + lane) * 16)), ub, S[t]);
+#pragma unroll
+    for (int u = 0; u < 4; ++u) sb[u] = pack2(S[2 * u], S[2 * u + 1]);
+    if (wave == 0) {
+      const StepMeta meta = *reinterpret_cast<const StepMeta*>(slot + kOffMeta);
+      n_valid += meta.n_valid;
+      n_flagged += meta.n_flagged;
+      min_span = fminf(min_span, fminf(meta.span[0], meta.span[1]));
+    }
+    uint16_t* os = o + st * STEP * D;
     uint32_t mx = 0;
 #pragma unroll
     for (int mt = 0; mt < 2; ++mt) {
@@ -743,18 +838,56 @@ __global__ __launch_bounds__(kScanThreads) void scan_kernel(Params p, int64_t n_
           nonfinite += ((nrows == STEP || 16 * mt + li < nrows) && abs_bits(O[mt][r]) >= 0x7f800000u) ? 1u : 0u;
     }
   }
+  if (j == sg.P - 1) {
+#pragma unroll
+    for (int t = 0; t < 8; ++t)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        p.S_final[(bh * D + 16 * t + 4 * lg + r) * D + d0 + li] = S[t][r];
+        nonfinite += not_finite(S[t][r]) ? 1u : 0u;
+      }
+  }
   if (p.stats) {
 #pragma unroll
     for (int off = 32; off > 0; off >>= 1) nonfinite += __shfl_xor(nonfinite, off);
     if (lane == 0) {
       if (nonfinite) atomicAdd(&p.stats->n_nonfinite, nonfinite);
-      if (slice == 0) {
+      if (wave == 0) {
         atomicAdd(&p.stats->n_chunks, n_valid);
         if (n_flagged) atomicAdd(&p.stats->n_flagged, n_flagged);
         if (n_valid) atomic_min_float(&p.stats->min_span, min_span);
       }
     }
   }
+}
+
+int64_t n_steps_of(int64_t T) { return (T + STEP - 1) / STEP; }
+
+// Segment plan.  Automatic: about 256 workgroups (one per compute unit) over (b, h, segment), at least
+// 8 steps per segment and at most kMaxSeg segments.  seg_steps > 0 fixes the segment length.
+SegPlan make_plan(int64_t BH, int64_t T, int64_t seg_steps) {
+  const int64_t n = n_steps_of(T);
+  SegPlan sg{};
+  int64_t P;
+  if (seg_steps > 0) {
+    sg.L = seg_steps;
+    P = (n + seg_steps - 1) / seg_steps;
+  } else {
+    P = 256 / BH;
+    const int64_t by_len = n / 8;
+    P = P < by_len ? P : by_len;
+    P = P < kMaxSeg ? P : kMaxSeg;
+    P = P < 1 ? 1 : P;
+    sg.L = (n + P - 1) / P;
+    P = (n + sg.L - 1) / sg.L;
+  }
+  sg.P = P;
+  const int64_t recs = BH * n * (int64_t)kRecBytes;
+  const int64_t blk = BH * (int64_t)(n < kMaxSeg ? n : kMaxSeg) * kSegState;
+  sg.off_x = recs;
+  sg.off_m = recs + blk;
+  sg.off_s = recs + 2 * blk;
+  return sg;
 }
 
 }  // namespace
@@ -765,29 +898,45 @@ bool mfma_supported(const Params& p) {
 
 size_t mfma_workspace_bytes(int64_t B, int64_t H, int64_t T, int64_t dk, int64_t dv) {
   if (dk != D || dv != D) return 0;
-  const int64_t n_steps = (T + STEP - 1) / STEP;
-  return (size_t)(B * H * n_steps) * kRecBytes;
+  const int64_t n = n_steps_of(T);
+  const int64_t nseg = n < kMaxSeg ? n : kMaxSeg;
+  return (size_t)(B * H * n) * kRecBytes + (size_t)(3 * B * H * nseg) * kSegState;
+}
+
+bool mfma_seg_steps_ok(int64_t T, int64_t seg_steps) {
+  if (seg_steps < 0) return false;
+  if (seg_steps == 0) return true;
+  const int64_t n = n_steps_of(T);
+  return (n + seg_steps - 1) / seg_steps <= kMaxSeg;
 }
 
 hipError_t launch_mfma(const Params& p, hipStream_t s, hipEvent_t ev_begin, hipEvent_t ev_end) {
-  const int64_t n_steps = (p.T + STEP - 1) / STEP;
+  const int64_t n_steps = n_steps_of(p.T);
   const int64_t BH = p.B * p.H;
-  const size_t smem = sizeof(PrepShared);
-  const size_t smem_scan = kScanSmem;
+  const SegPlan sg = make_plan(BH, p.T, p.seg_steps);
   static bool attr_set = false;
   if (!attr_set) {
-    hipError_t e = hipFuncSetAttribute((const void*)prep_kernel, hipFuncAttributeMaxDynamicSharedMemorySize, (int)smem);
+    hipError_t e = hipFuncSetAttribute((const void*)prep_kernel, hipFuncAttributeMaxDynamicSharedMemorySize,
+                                       (int)sizeof(PrepShared));
     if (e != hipSuccess) return e;
-    e = hipFuncSetAttribute((const void*)scan_kernel, hipFuncAttributeMaxDynamicSharedMemorySize, (int)smem_scan);
+    e = hipFuncSetAttribute((const void*)seg_state_kernel, hipFuncAttributeMaxDynamicSharedMemorySize, (int)kStSmem);
+    if (e != hipSuccess) return e;
+    e = hipFuncSetAttribute((const void*)seg_out_kernel, hipFuncAttributeMaxDynamicSharedMemorySize, (int)kOutSmem);
     if (e != hipSuccess) return e;
     attr_set = true;
   }
   hipError_t e;
   if (ev_begin && (e = hipEventRecord(ev_begin, s)) != hipSuccess) return e;
-  hipLaunchKernelGGL(prep_kernel, dim3((unsigned)(BH * n_steps)), dim3(256), smem, s, p, n_steps);
+  hipLaunchKernelGGL(prep_kernel, dim3((unsigned)(BH * n_steps)), dim3(256), sizeof(PrepShared), s, p, n_steps);
   if ((e = hipGetLastError()) != hipSuccess) return e;
-  const int xcd_map = (BH % 8 == 0) ? 1 : 0;
-  hipLaunchKernelGGL(scan_kernel, dim3((unsigned)(BH * 8)), dim3(kScanThreads), smem_scan, s, p, n_steps, xcd_map);
+  if (sg.P > 1) {
+    hipLaunchKernelGGL(seg_state_kernel, dim3((unsigned)(BH * (sg.P - 1))), dim3(kSegThreads), kStSmem, s, p,
+                       n_steps, sg);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+    hipLaunchKernelGGL(seg_combine_kernel, dim3((unsigned)(BH * 8)), dim3(256), 0, s, p, sg);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+  }
+  hipLaunchKernelGGL(seg_out_kernel, dim3((unsigned)(BH * sg.P)), dim3(kSegThreads), kOutSmem, s, p, n_steps, sg);
   if ((e = hipGetLastError()) != hipSuccess) return e;
   if (ev_end && (e = hipEventRecord(ev_end, s)) != hipSuccess) return e;
   return hipSuccess;

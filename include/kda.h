@@ -100,9 +100,10 @@ typedef struct {
   int32_t disable_fallback; /* 1: flagged chunks still take the dense exp(+-G) path (shows the overflow) */
   int32_t force_fallback;   /* 1: every chunk takes the per-position path (measures its cost) */
   int32_t path;             /* 0 auto, 1 the plain fp32 vector path, 2 the matrix-core path */
-  int32_t reserved;         /* must be 0 */
-  void* ev_begin;           /* optional hipEvent_t recorded on `stream` right before the main kernel */
-  void* ev_end;             /* optional hipEvent_t recorded on `stream` right after the main kernel */
+  int32_t seg_steps;        /* matrix-core path: steps of 32 tokens per sequence segment (0 = automatic;
+                               < 0, or more than 32 segments per sequence, is KDA_ERR_ARG) */
+  void* ev_begin;           /* optional hipEvent_t recorded on `stream` before the call's first kernel */
+  void* ev_end;             /* optional hipEvent_t recorded on `stream` after the call's last kernel */
 } kda_opts_t;
 
 enum {
@@ -111,7 +112,8 @@ enum {
   KDA_ERR_SHAPE = -2,       /* B, H < 1, T < 0, dk or dv < 1, or sizes overflow */
   KDA_ERR_UNSUPPORTED = -3, /* chunk != 16, dk or dv not in {32, 64, 128}, unknown dtype or path */
   KDA_ERR_ARG = -4,         /* g_min NaN or > 0, misaligned pointer, forbidden overlap,
-                               workspace too small, non-zero reserved field, both opts set */
+                               workspace too small, non-zero reserved field, both opts set,
+                               bad seg_steps */
   KDA_ERR_HIP = -5          /* a HIP call failed; kda_last_hip_error() has the text */
 };
 

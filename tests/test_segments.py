@@ -1,0 +1,82 @@
+"""Sequence segments of the matrix-core path.  Each (b, h) sequence is cut into
+segments.  Each segment's affine state map S_end = M S_start + X is computed in
+parallel, and the maps are then chained.  A forced segment length
+(`seg_steps`, in 32-token steps) exercises plans with many segments at sizes the
+oracle finishes in seconds.  The ragged tail always falls in the last segment."""
+import numpy as np
+import pytest
+
+from chunked_gated_delta_amd import inputs as gen
+from oracle import oracle as orc
+from kda_testutil import TOL, compare, rel_err, say, gpu_run, need_path
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+if not torch.cuda.is_available():
+    pytest.skip("no GPU", allow_module_level=True)
+
+BF16 = gen.WORKLOADS["bf16_4k"]
+
+
+def check(wl, seed, **kw):
+    need_path("mfma")
+    eo, es, st, *_ = compare(wl, seed=seed, path="mfma", **kw)
+    tol_o, tol_s = TOL[wl.dtype]
+    say(f"   err_o={eo:.3e} (tol {tol_o})  err_S={es:.3e} (tol {tol_s})  stats={st}")
+    assert eo <= tol_o and es <= tol_s
+    assert st["n_nonfinite"] == 0
+    assert st["n_chunks"] == wl.B * wl.H * ((wl.T + 15) // 16)
+    return st
+
+
+@pytest.mark.parametrize("T,seg", [(64, 1), (300, 1), (300, 2), (300, 3), (1000, 1), (1000, 5), (1000, 7)])
+def test_forced_segments(T, seg):
+    check(BF16.with_(B=1, H=2, T=T), seed=200 + T + seg, seg_steps=seg)
+
+
+@pytest.mark.parametrize("seg", [1, 4])
+def test_segments_with_initial_state(seg):
+    """Decay-stress gates with S0 ~ N(0, 0.1): the first segment starts from S0."""
+    st = check(gen.WORKLOADS["decay_stress"].with_(H=2, T=1000), seed=3, seg_steps=seg)
+    assert st["n_flagged"] == 0
+
+
+def test_segments_no_decay():
+    """g_min = 0: nothing is forgotten, so each segment transition is a pure
+    product of (I - beta k k^T) factors, far from zero.  A nonzero S0 flows
+    through every transition."""
+    check(BF16.with_(B=1, H=2, T=640, g_min=0.0, s0_sd=0.5), seed=14, seg_steps=2)
+
+
+def test_segments_pure_decay():
+    """beta = 0: X = 0 and M = diag(prod e^g), so the state is S0, decayed.  The decay is
+    slow (w ~ N(-5, 0.5), about -0.034 per token), so the decayed S0 stays well inside fp32's range."""
+    wl = BF16.with_(B=1, H=2, T=800, s0_sd=0.5, w_mu=-5.0, w_sd=0.5)
+    check(wl, seed=15, seg_steps=3, mutate=lambda inp: inp["beta"].fill(0.0))
+
+
+def test_segments_with_flagged_chunks():
+    """g_min = -8: chunks past the span limit take the per-position path inside segments."""
+    wl = BF16.with_(B=1, H=2, T=700, g_min=-8.0, w_mu=4.0, w_sd=1.0)
+    st = check(wl, seed=16, seg_steps=3)
+    pred = orc.predicted_flags(gen.make_numpy(wl, 16)["w"], -8.0)
+    assert st["n_flagged"] == int(pred.sum()) and st["n_flagged"] > 0
+
+
+def test_automatic_plan_several_heads():
+    """B2 H4 T2048: the automatic plan cuts each sequence into 8 segments of 8 steps."""
+    check(BF16.with_(B=2, H=4, T=2048), seed=17)
+
+
+def test_segment_plans_agree():
+    """Different segment plans change only the rounding."""
+    need_path("mfma")
+    wl = BF16.with_(B=1, H=2, T=900, s0_sd=0.3)
+    t = gen.numpy_to_torch(gen.make_numpy(wl, 18), "cuda")
+    say(f"[case] segment plans {wl}")
+    outs = [gpu_run(t, wl.g_min, path="mfma", seg_steps=s) for s in (0, 2, 3, 29)]
+    o0, S0_, _ = outs[0]
+    for o, S, _ in outs[1:]:
+        assert rel_err(o.float().cpu().numpy(), o0.float().cpu().numpy()) < 1e-2
+        assert rel_err(S.cpu().numpy(), S0_.cpu().numpy()) < 5e-3
