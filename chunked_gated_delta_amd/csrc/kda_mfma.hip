@@ -483,6 +483,8 @@ constexpr int kSegThreads = 64 * kSegWaves;
 constexpr int kVTileBytes = STEP * D * 2;                    // one step of V, all 128 columns, row-major
 constexpr int kSegState = D * D * 4;                         // bytes of one 128 x 128 fp32 block (64 KiB)
 constexpr int kMaxSeg = 32;                                  // segments per (b, h)
+constexpr int kMHalf = 8 * 4 * 64 * 16;                      // bytes of one bf16 part of M (32 KiB)
+static_assert(2 * kMHalf == kSegState, "hi + lo parts of M fill one block");
 
 // seg_out slot: the whole record, then V
 constexpr int kOutSlot = kRecBytes + kVTileBytes;
@@ -667,25 +669,47 @@ __global__ __launch_bounds__(kSegThreads) void seg_state_kernel(Params p, int64_
 #pragma unroll
     for (int u = 0; u < 4; ++u) { xb[u] = pack2(X[2 * u], X[2 * u + 1]); mb[u] = pack2(M[2 * u], M[2 * u + 1]); }
   }
-  // X_j in slice-major D layout; M_j arranged as the combine's A operands:
-  // [mo 8][mt 8][lane 64][r 4] <-> M[16 mo + (lane & 15)][16 mt + 4 (lane >> 4) + r]
-  const int64_t blk = (bh * sg.P + j) * (int64_t)(kSegState / 4);
-  float* xo = (float*)((unsigned char*)p.workspace + sg.off_x) + blk + wave * 8 * 64 * 4;
+  // X_j in slice-major D layout; M_j split into bf16 hi + lo parts, each arranged as the combine's
+  // A operands: [mo 8][u 4][lane 64][8] <-> M[16 mo + (lane & 15)][32 u + {0, 16} + 4 (lane >> 4) + r]
+  const int64_t blk = bh * sg.P + j;
+  float* xo = (float*)((unsigned char*)p.workspace + sg.off_x + blk * (int64_t)kSegState) + wave * 8 * 64 * 4;
   store_slice(xo, X, lane);
-  float* mo = (float*)((unsigned char*)p.workspace + sg.off_m) + blk;
+  __bf16* mh = (__bf16*)((unsigned char*)p.workspace + sg.off_m + blk * (int64_t)kSegState);
+  __bf16* ml = mh + kMHalf / 2;
+  const int u = wave >> 1, pos = (wave & 1) * 4 + (li & 3);
 #pragma unroll
   for (int t = 0; t < 8; ++t)
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
       // element M[16t + 4lg + r][16 wave + li]
       const int lane_c = (4 * lg + r) + 16 * (li >> 2);
-      mo[((t * 8 + wave) * 64 + lane_c) * 4 + (li & 3)] = M[t][r];
+      const int e = ((t * 4 + u) * 64 + lane_c) * 8 + pos;
+      const __bf16 hi = (__bf16)M[t][r];
+      mh[e] = hi;
+      ml[e] = (__bf16)(M[t][r] - (float)hi);
     }
 }
 
-// ---- seg_combine_kernel: S_start(j+1) = M_j S_start(j) + X_j for one 16-column slice, in fp32 on the
-// matrix cores (16x16x4 f32).  Wavefront w owns the output row tiles 2w, 2w+1; the contraction runs
-// over k-steps (mt, r) <-> rows {16 mt + 4 g + r} of S, so the D-layout tiles of S are the B operands.
+// ---- seg_combine_kernel: S_start(j+1) = M_j S_start(j) + X_j for one 16-column slice.  The product
+// runs on bf16 MFMA in three passes, Mhi Shi + Mhi Slo + Mlo Shi (hi/lo: bf16 value and bf16 residual),
+// which leaves a relative error near 2^-16, with fp32 accumulation.  Wavefront w owns the output row
+// tiles 2w, 2w+1; the D-layout tiles of S feed the B operands directly through the permuted
+// contraction order.  M_j and X_j are fetched two segments ahead.
+__device__ __forceinline__ void split_bf16(floatx4 a, floatx4 b, bf16x8& hi, bf16x8& lo) {
+#pragma unroll
+  for (int r = 0; r < 4; ++r) {
+    hi[r] = (__bf16)a[r];
+    hi[4 + r] = (__bf16)b[r];
+    lo[r] = (__bf16)(a[r] - (float)hi[r]);
+    lo[4 + r] = (__bf16)(b[r] - (float)hi[4 + r]);
+  }
+}
+
+struct CombineOps {
+  bf16x8 mh[2][4], ml[2][4];
+  floatx4 x[2];
+};
+
 __global__ __launch_bounds__(256) void seg_combine_kernel(Params p, SegPlan sg) {
   __shared__ floatx4 Sx[2][8][64];
   const int tid = threadIdx.x;
@@ -693,6 +717,7 @@ __global__ __launch_bounds__(256) void seg_combine_kernel(Params p, SegPlan sg) 
   const int li = lane & 15, lg = lane >> 4;
   const int64_t bh = blockIdx.x >> 3;
   const int slice = blockIdx.x & 7;
+  const int64_t nseg = sg.P - 1;
   floatx4 cur[2];
 #pragma unroll
   for (int h = 0; h < 2; ++h) {
@@ -701,33 +726,55 @@ __global__ __launch_bounds__(256) void seg_combine_kernel(Params p, SegPlan sg) 
     for (int r = 0; r < 4; ++r)
       cur[h][r] = p.S0 ? p.S0[(bh * D + 16 * mo + 4 * lg + r) * D + 16 * slice + li] : 0.f;
   }
-  const float* xs = (const float*)((const unsigned char*)p.workspace + sg.off_x);
-  const float* ms = (const float*)((const unsigned char*)p.workspace + sg.off_m);
-  float* ss = (float*)((unsigned char*)p.workspace + sg.off_s);
-  for (int64_t j = 0; j + 1 < sg.P; ++j) {
+  const unsigned char* ws = (const unsigned char*)p.workspace;
+  auto fetch = [&](CombineOps& c, int64_t j) {
+    const int64_t blk = bh * sg.P + j;
+    const unsigned char* mb = ws + sg.off_m + blk * (int64_t)kSegState;
+    const float* xj = (const float*)(ws + sg.off_x + blk * (int64_t)kSegState) + slice * 8 * 64 * 4;
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const int mo = 2 * wave + h;
+      c.x[h] = *reinterpret_cast<const floatx4*>(xj + (mo * 64 + lane) * 4);
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const int off = ((mo * 4 + u) * 64 + lane) * 16;
+        c.mh[h][u] = *reinterpret_cast<const bf16x8*>(mb + off);
+        c.ml[h][u] = *reinterpret_cast<const bf16x8*>(mb + kMHalf + off);
+      }
+    }
+  };
+  auto step = [&](const CombineOps& c, int64_t j) {
     floatx4 (*sx)[64] = Sx[j & 1];
 #pragma unroll
     for (int h = 0; h < 2; ++h) sx[2 * wave + h][lane] = cur[h];
     __syncthreads();
-    floatx4 b[8];
+    bf16x8 sh[4], sl[4];
 #pragma unroll
-    for (int mt = 0; mt < 8; ++mt) b[mt] = sx[mt][lane];
-    const int64_t blk = (bh * sg.P + j) * (int64_t)(kSegState / 4);
-    const float* xj = xs + blk + slice * 8 * 64 * 4;
-    const float* mj = ms + blk;
-    float* sn = ss + (bh * sg.P + j + 1) * (int64_t)(kSegState / 4) + slice * 8 * 64 * 4;
+    for (int u = 0; u < 4; ++u) split_bf16(sx[2 * u][lane], sx[2 * u + 1][lane], sh[u], sl[u]);
+    float* sn = (float*)((unsigned char*)p.workspace + sg.off_s + (bh * sg.P + j + 1) * (int64_t)kSegState) +
+                slice * 8 * 64 * 4;
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
-      const int mo = 2 * wave + h;
-      floatx4 acc = *reinterpret_cast<const floatx4*>(xj + (mo * 64 + lane) * 4);
+      floatx4 acc = c.x[h];
 #pragma unroll
-      for (int mt = 0; mt < 8; ++mt) {
-        const floatx4 a = *reinterpret_cast<const floatx4*>(mj + ((mo * 8 + mt) * 64 + lane) * 4);
-#pragma unroll
-        for (int r = 0; r < 4; ++r) acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a[r], b[mt][r], acc, 0, 0, 0);
+      for (int u = 0; u < 4; ++u) {
+        acc = mfma(c.ml[h][u], sh[u], acc);
+        acc = mfma(c.mh[h][u], sl[u], acc);
+        acc = mfma(c.mh[h][u], sh[u], acc);
       }
       cur[h] = acc;
-      *reinterpret_cast<floatx4*>(sn + (mo * 64 + lane) * 4) = acc;
+      *reinterpret_cast<floatx4*>(sn + ((2 * wave + h) * 64 + lane) * 4) = acc;
+    }
+  };
+  CombineOps c0, c1;
+  fetch(c0, 0);
+  if (nseg > 1) fetch(c1, 1);
+  for (int64_t j = 0; j < nseg; j += 2) {
+    step(c0, j);
+    if (j + 2 < nseg) fetch(c0, j + 2);
+    if (j + 1 < nseg) {
+      step(c1, j + 1);
+      if (j + 3 < nseg) fetch(c1, j + 3);
     }
   }
 }
