@@ -32,7 +32,8 @@ if ROOT not in sys.path:
 METRIC = "KDA chunk-fwd tokens/s (H16,d128,T64K,bf16) + % of MFMA/HBM roofline"
 HBM_PEAK_GBS = 8000.0
 PROFILES = os.path.join(ROOT, "profiles")
-KERNEL_SOURCES = ["chunked_gated_delta_amd/csrc/kda_mfma.hip", "chunked_gated_delta_amd/csrc/kda_common.hip",
+KERNEL_SOURCES = ["chunked_gated_delta_amd/csrc/kda_mfma.hip", "chunked_gated_delta_amd/csrc/kda_fused.hip",
+                  "chunked_gated_delta_amd/csrc/kda_mfma_util.h", "chunked_gated_delta_amd/csrc/kda_common.hip",
                   "chunked_gated_delta_amd/csrc/kda_host.cpp", "chunked_gated_delta_amd/csrc/kda_internal.h"]
 
 
@@ -152,7 +153,7 @@ def main():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default="headline")
-    ap.add_argument("--path", default="auto", choices=["auto", "vector", "mfma"])
+    ap.add_argument("--path", default="auto", choices=["auto", "vector", "mfma", "fused"])
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--force-fallback", action="store_true")

@@ -1,0 +1,731 @@
+// Fused matrix-core path of the chunked KDA forward (bf16 inputs, dk = dv = 128, bf16 MFMA on gfx950).
+//
+// The steps (32 tokens = two 16-token chunks) of every (b, h) sequence are cut into segments; one
+// workgroup of 8 wavefronts owns one segment and builds every step's operands on chip, so only the
+// inputs q, k, v, w, beta and the outputs o cross HBM.  Per segment, the steps run through a
+// software pipeline.  Interval s (two halves, each closed by a workgroup barrier) holds
+//   first half    E1(s+2)  gate, chunk-local inclusive prefix L, chunk totals Gam_c, spans, and every
+//                          operand of step s+2 that needs only its own chunk (all wavefronts)
+//                 S(s+1)   the diagonal blocks of T = (I + A)^{-1} of step s+1 (wavefronts 0, 1),
+//                          the first factor of its coupling block, P of step s+1 to bf16 (wavefront 2)
+//                 C1(s)    R = diag(beta)(V - Kbar S), U = T R and the outputs of step s
+//   second half   E2(s+2)  the operands that need the other chunk's totals, the flags, and the
+//                          per-pair diagonal blocks of flagged chunks
+//                 TL(s+2)  the causal tiles A (and P) of step s+2 on MFMA (wavefronts 0-5)
+//                 S2(s+1)  the coupling block of T and T to bf16 (wavefront 6)
+//                 C2(s)    the state update of step s
+//
+// Per step, with G the in-step prefix referenced to the step start, Kbar = k e^{G}, Qbar = q e^{G},
+// Ktil = k e^{Gam_step - G}, A = strictly-lower diag(beta) Kbar (k e^{-G})^T, P = lower-inclusive
+// Qbar (k e^{-G})^T and T = (I + A)^{-1}, the state S (dk x dv, fp32) advances as
+//   R = diag(beta) (V - Kbar S)        U = T R
+//   O = Qbar S + P U                   S <- diag(e^{Gam_step}) S + Ktil^T U
+// which is the chunk form of the delta rule written out from "From Numerical Stability to Load
+// Balancing ..." section 2.1 (matrix products inside a chunk, a serial state between chunks, in-chunk
+// scaling exp(G_i - G_j) for i >= j) with the UT/WY correction of the delta rule.  The bounded gate
+// (same page section 2.2; "Demystifying Trillion-Parameter MoE Models ..." Breakthrough 1 part 2)
+// keeps each 16-token chunk's span at or above -80, so the reciprocal factors e^{-L} stay below e^80.
+// Only the two diagonal 16 x 16 blocks use e^{+-L} (chunk-local); the block coupling chunk 1 to
+// chunk 0 uses factors referenced to the chunk boundary, e^{L_r} e^{Gam_0 - L_j}, both <= 1.  A
+// chunk whose span falls below -80 gets its diagonal blocks from per-pair factors exp(L_r - L_j) <= 1.
+//
+// Two workgroup kinds share the pipeline (template argument OUT):
+//   OUT = true   a segment from its true entering state, with the outputs o (and S_final at the end)
+//   OUT = false  a segment's affine map S_end = M S_start + X: wavefront w carries column slice w
+//                of X (from zero, with V) and of M (from the identity, without V)
+#include "kda_mfma_util.h"
+
+namespace kda {
+
+namespace {
+
+constexpr int D = 128;
+constexpr int STEP = 32;
+constexpr int kWaves = 8;
+constexpr int kThreads = 64 * kWaves;
+
+// ---- per-step operand record (LDS), arranged so that every MFMA operand is one 16-byte read per lane
+constexpr int rKb = 0;        // -beta Kbar, [mt 2][u 4] x 64 lanes x 16 B: row 16mt + li, channels 32u + {4g+r, 16+4g+r}
+constexpr int rQb = 8192;     // Qbar, same arrangement                                      (OUT only)
+constexpr int rKt = 16384;    // Ktil^T, [t 8] blocks: channel 16t + li, tokens {4g+r, 16+4g+r}
+constexpr int rT = 24576;     // T, [mt 2] blocks: row 16mt + li, tokens {4g+r, 16+4g+r}
+constexpr int rP = 26624;     // P, same arrangement                                         (OUT only)
+constexpr int rEg = 28672;    // e^{Gam_step}: [g 4][t 8][r 4] fp32 <-> channel 16t + 4g + r
+constexpr int rBeta = 29184;  // beta per token, fp32 (zero past the end of the sequence)
+constexpr int rMeta = 29312;  // StepInfo
+constexpr int kRec = 29440;
+constexpr int kRecSlots = 3;  // steps s (C), s+1 (S), s+2 (E, TL)
+
+// ---- tile operands of one step, same per-lane arrangement as rKb ([rt][u] blocks)
+constexpr int oKh = 0;        // k e^{-L}, chunks 0 and 1 [cc 2][u 4]
+constexpr int oKb1 = 8192;    // k e^{L}, chunk 1
+constexpr int oQb1 = 12288;   // q e^{L}, chunk 1                                             (OUT only)
+constexpr int oKt0 = 16384;   // k e^{Gam_0 - L}, chunk 0
+constexpr int kOps = 20480;
+// the per-pair path of a flagged chunk borrows the tile-operand buffer of step s+1 (free during the
+// second half of interval s): L (fp32 [16][128]), raw k and raw q (bf16 [16][128])
+constexpr int pL = 0, pK = 8192, pQ = 12288;
+static_assert(pQ + 4096 <= kOps, "per-pair inputs fit the borrowed buffer");
+
+constexpr int kRowA = 36;     // row stride (floats) of the 32 x 32 fp32 arrays: 16-byte aligned rows
+
+struct StepInfo {
+  float span[2];          // chunk spans, natural-log units (+inf for a chunk with no tokens)
+  uint32_t n_valid;       // chunks with at least one token
+  uint32_t n_flagged;     // of those, spans below -80
+  uint32_t pairwise;      // bit c: chunk c's diagonal blocks come from per-pair factors
+};
+
+struct FusedShared {
+  unsigned char rec[kRecSlots][kRec];
+  unsigned char ops[2][kOps];
+  float AT[STEP][kRowA];                  // A transposed (AT[j][r] = A[r][j]) of the step being solved
+  float P[STEP][kRowA];                   // P of the step being solved
+  float T32[STEP][kRowA];                 // T in fp32 while it is assembled
+  float X[16][20];                        // A_10 T_00
+  float pwA[2][16][16], pwP[2][16][16];   // per-pair diagonal blocks [chunk][r][j]
+  float gam[2][D];                        // chunk totals (log2 units) of the step in E
+  float spanw[kWaves];                    // per-wave minimum of the chunk totals
+};
+constexpr size_t kFusedSmem = sizeof(FusedShared);
+static_assert(kFusedSmem <= 163840, "LDS budget");
+
+// x, hidden from the optimizer: values derived from it inside a loop are recomputed there instead of
+// being hoisted out of the loop and held in registers for its whole length
+__device__ __forceinline__ int opaque(int x) {
+  asm volatile("" : "+v"(x));
+  return x;
+}
+
+__device__ __forceinline__ void lgkm_wait() {
+  compiler_fence();
+  __builtin_amdgcn_s_waitcnt(0xF | (0x3 << 14) | (0x7 << 4) | (0x0 << 8));   // lgkmcnt(0)
+  compiler_fence();
+}
+
+// gate in log2 units (g * log2 e), with the kind of gate fixed at compile time
+template <bool UNB> __device__ __forceinline__ float gate2(float w, float g_min_log2);
+template <> __device__ __forceinline__ float gate2<false>(float w, float g_min_log2) {
+  return g_min_log2 * __builtin_amdgcn_rcpf(1.f + __builtin_amdgcn_exp2f(-w * kLog2e));
+}
+template <> __device__ __forceinline__ float gate2<true>(float w, float) {
+  return -(fmaxf(w, 0.f) + log1pf(expf(-fabsf(w)))) * kLog2e;
+}
+
+// Raw buffer views of one (b, h) slice of a tensor: loads past the end of the slice return zero, so
+// tokens past the end of the sequence read as k = q = v = beta = 0 (their gates are masked in E).
+struct Views {
+  __amdgpu_buffer_rsrc_t k, w, q, beta, v;
+};
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t view(const void* base, int64_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, (int)bytes, 0x00020000);
+}
+
+// ---------------------------------------------------------------- stage E
+// Thread layout: wave w, lane l -> chunk cc = w >> 2, channel pair pr = 16 (w & 3) + (l >> 2)
+// (channels 2pr, 2pr+1), token quarter h = l & 3 (tokens 16cc + 4h + j, j < 4).  The in-chunk prefix
+// runs over j in registers and over h across the four consecutive lanes of the quarter group.
+struct EIn {
+  uint32_t q[4], k[4], w[4];   // two bf16 channels per word, tokens j
+  uint32_t b[4];               // beta of the 4 tokens (bf16 in the low half)
+};
+
+struct EKeep {                 // E's values carried from its first half to its second
+  uint32_t k[4], q[4];
+  float L0[4], L1[4];          // prefix (log2 units), for the per-pair path
+  float f0[4], f1[4];          // chunk 0: e^{Gam_0 - L}; chunk 1: e^{L}
+  float beta[4];
+  float G0, G1;                // chunk totals of the two channels (log2 units)
+};
+
+template <bool OUT>
+__device__ __forceinline__ void e_load(EIn& in, const Views& vw, int64_t step, int voff, int boff) {
+  const int so = (int)(step * STEP * D * 2), sb = (int)(step * STEP * 2);
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    in.k[j] = __builtin_amdgcn_raw_buffer_load_b32(vw.k, voff + j * D * 2, so, 0);
+    in.w[j] = __builtin_amdgcn_raw_buffer_load_b32(vw.w, voff + j * D * 2, so, 0);
+    in.q[j] = OUT ? __builtin_amdgcn_raw_buffer_load_b32(vw.q, voff + j * D * 2, so, 0) : 0u;
+    in.b[j] = __builtin_amdgcn_raw_buffer_load_b16(vw.beta, boff + j * 2, sb, 0);
+  }
+}
+
+// offset of (row li of row tile rt, this thread's channel pair) in a [rt][u] block array
+__device__ __forceinline__ int rowk_off(int rt, int u, int li, int g, int pos) {
+  return ((rt * 4 + u) * 64 + li + 16 * g) * 16 + pos * 2;
+}
+
+template <bool OUT, bool UNB>
+__device__ __forceinline__ void e_first(FusedShared& sm, const EIn& in, EKeep& kp, const Params& p, int64_t step,
+                                        unsigned char* rec, unsigned char* ops, int w, int l) {
+  const int cc = w >> 2, pr = 16 * (w & 3) + (l >> 2), h = l & 3;
+  const int u = w & 3, g = ((l >> 2) & 7) >> 1, pos = (l >> 5) * 4 + 2 * ((l >> 2) & 1);
+  const int c0 = 2 * pr, c1 = 2 * pr + 1;
+  const int64_t tb = step * STEP + 16 * cc + 4 * h;
+  const float gml2 = p.g_min * kLog2e;
+  float a0 = 0.f, a1 = 0.f;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const bool ok = tb + j < p.T;
+    kp.k[j] = in.k[j];
+    kp.q[j] = in.q[j];
+    kp.beta[j] = __uint_as_float(in.b[j] << 16);
+    const float g0 = gate2<UNB>(lo_bf16(in.w[j]), gml2), g1 = gate2<UNB>(hi_bf16(in.w[j]), gml2);
+    a0 += ok ? g0 : 0.f;
+    a1 += ok ? g1 : 0.f;
+    kp.L0[j] = a0;
+    kp.L1[j] = a1;
+  }
+  // prefix across the quarter group (lanes 4m .. 4m+3)
+  float s0 = a0, s1 = a1, t0, t1;
+  t0 = __shfl_up(s0, 1, 4); t1 = __shfl_up(s1, 1, 4);
+  if (h >= 1) { s0 += t0; s1 += t1; }
+  t0 = __shfl_up(s0, 2, 4); t1 = __shfl_up(s1, 2, 4);
+  if (h >= 2) { s0 += t0; s1 += t1; }
+  const float x0 = s0 - a0, x1 = s1 - a1;              // exclusive prefix
+  kp.G0 = __shfl(s0, 3, 4);
+  kp.G1 = __shfl(s1, 3, 4);
+#pragma unroll
+  for (int j = 0; j < 4; ++j) { kp.L0[j] += x0; kp.L1[j] += x1; }
+  if (h == 0) { sm.gam[cc][c0] = kp.G0; sm.gam[cc][c1] = kp.G1; }
+  float m = fminf(kp.G0, kp.G1);
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) m = fminf(m, __shfl_xor(m, off));
+  if (l == 0) sm.spanw[w] = m;
+  if ((w & 3) == 0 && (l >> 2) == 0) {
+    float* bt = reinterpret_cast<float*>(rec + rBeta);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) bt[16 * cc + 4 * h + j] = kp.beta[j];
+  }
+  uint32_t kt0[2], kt1[2];     // Ktil^T of this thread's channels in chunk 1
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const int li = 4 * h + j;
+    const float k0 = lo_bf16(kp.k[j]), k1 = hi_bf16(kp.k[j]);
+    const float e0 = __builtin_amdgcn_exp2f(kp.L0[j]), e1 = __builtin_amdgcn_exp2f(kp.L1[j]);
+    const float g0 = __builtin_amdgcn_exp2f(kp.G0 - kp.L0[j]), g1 = __builtin_amdgcn_exp2f(kp.G1 - kp.L1[j]);  // <= 1
+    *reinterpret_cast<uint32_t*>(ops + oKh + rowk_off(cc, u, li, g, pos)) =
+        pk_bf16(k0 * __builtin_amdgcn_exp2f(-kp.L0[j]), k1 * __builtin_amdgcn_exp2f(-kp.L1[j]));
+    if (cc == 1) {
+      kp.f0[j] = e0; kp.f1[j] = e1;
+      *reinterpret_cast<uint32_t*>(ops + oKb1 + rowk_off(0, u, li, g, pos)) = pk_bf16(k0 * e0, k1 * e1);
+      if (OUT)
+        *reinterpret_cast<uint32_t*>(ops + oQb1 + rowk_off(0, u, li, g, pos)) =
+            pk_bf16(lo_bf16(kp.q[j]) * e0, hi_bf16(kp.q[j]) * e1);
+      const uint32_t a = __builtin_bit_cast(uint16_t, (__bf16)(k0 * g0)), b = __builtin_bit_cast(uint16_t, (__bf16)(k1 * g1));
+      if (j & 1) { kt0[j >> 1] |= a << 16; kt1[j >> 1] |= b << 16; } else { kt0[j >> 1] = a; kt1[j >> 1] = b; }
+    } else {
+      kp.f0[j] = g0; kp.f1[j] = g1;
+      const float nb = -kp.beta[j];
+      *reinterpret_cast<uint32_t*>(rec + rKb + rowk_off(0, u, li, g, pos)) = pk_bf16(nb * k0 * e0, nb * k1 * e1);
+      if (OUT)
+        *reinterpret_cast<uint32_t*>(rec + rQb + rowk_off(0, u, li, g, pos)) =
+            pk_bf16(lo_bf16(kp.q[j]) * e0, hi_bf16(kp.q[j]) * e1);
+      *reinterpret_cast<uint32_t*>(ops + oKt0 + rowk_off(0, u, li, g, pos)) = pk_bf16(k0 * g0, k1 * g1);
+    }
+  }
+  if (cc == 1) {   // channel c -> block c >> 4, lane (c & 15) + 16 h, positions 4 .. 7
+    *reinterpret_cast<uint2*>(rec + rKt + ((c0 >> 4) * 64 + (c0 & 15) + 16 * h) * 16 + 8) = uint2{kt0[0], kt0[1]};
+    *reinterpret_cast<uint2*>(rec + rKt + ((c1 >> 4) * 64 + (c1 & 15) + 16 * h) * 16 + 8) = uint2{kt1[0], kt1[1]};
+  }
+}
+
+__device__ __forceinline__ void pair_of(int pr, int& r, int& j) {   // pr -> (r, j), j <= r < 16
+  r = 0;
+  while ((r + 1) * (r + 2) / 2 <= pr) ++r;
+  j = pr - r * (r + 1) / 2;
+}
+
+// returns the per-pair mask of the step (bit c: chunk c), the same in every thread
+template <bool OUT>
+__device__ __forceinline__ uint32_t e_second(FusedShared& sm, const EKeep& kp, const Params& p, int64_t step,
+                                             unsigned char* rec, unsigned char* scratch, int w, int l) {
+  const int tid = w * 64 + l;
+  const int cc = w >> 2, pr = 16 * (w & 3) + (l >> 2), h = l & 3;
+  const int u = w & 3, g = ((l >> 2) & 7) >> 1, pos = (l >> 5) * 4 + 2 * ((l >> 2) & 1);
+  const int c0 = 2 * pr, c1 = 2 * pr + 1;
+  if (cc == 1) {   // step-referenced operands of chunk 1: G = Gam_0 + L
+    const float x0 = __builtin_amdgcn_exp2f(sm.gam[0][c0]), x1 = __builtin_amdgcn_exp2f(sm.gam[0][c1]);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int li = 4 * h + j;
+      const float k0 = lo_bf16(kp.k[j]), k1 = hi_bf16(kp.k[j]);
+      const float nb = -kp.beta[j];
+      *reinterpret_cast<uint32_t*>(rec + rKb + rowk_off(1, u, li, g, pos)) =
+          pk_bf16(nb * k0 * kp.f0[j] * x0, nb * k1 * kp.f1[j] * x1);
+      if (OUT)
+        *reinterpret_cast<uint32_t*>(rec + rQb + rowk_off(1, u, li, g, pos)) =
+            pk_bf16(lo_bf16(kp.q[j]) * kp.f0[j] * x0, hi_bf16(kp.q[j]) * kp.f1[j] * x1);
+    }
+  } else {         // chunk 0: Ktil = k e^{Gam_0 - L} e^{Gam_1}; e^{Gam_step}
+    const float G10 = sm.gam[1][c0], G11 = sm.gam[1][c1];
+    const float y0 = __builtin_amdgcn_exp2f(G10), y1 = __builtin_amdgcn_exp2f(G11);
+    uint32_t kt0[2], kt1[2];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const uint32_t a = __builtin_bit_cast(uint16_t, (__bf16)(lo_bf16(kp.k[j]) * kp.f0[j] * y0));
+      const uint32_t b = __builtin_bit_cast(uint16_t, (__bf16)(hi_bf16(kp.k[j]) * kp.f1[j] * y1));
+      if (j & 1) { kt0[j >> 1] |= a << 16; kt1[j >> 1] |= b << 16; } else { kt0[j >> 1] = a; kt1[j >> 1] = b; }
+    }
+    *reinterpret_cast<uint2*>(rec + rKt + ((c0 >> 4) * 64 + (c0 & 15) + 16 * h) * 16) = uint2{kt0[0], kt0[1]};
+    *reinterpret_cast<uint2*>(rec + rKt + ((c1 >> 4) * 64 + (c1 & 15) + 16 * h) * 16) = uint2{kt1[0], kt1[1]};
+    if (h == 0) {
+      float* eg = reinterpret_cast<float*>(rec + rEg);
+      eg[((c0 >> 2) & 3) * 32 + (c0 >> 4) * 4 + (c0 & 3)] = __builtin_amdgcn_exp2f(kp.G0 + G10);
+      eg[((c1 >> 2) & 3) * 32 + (c1 >> 4) * 4 + (c1 & 3)] = __builtin_amdgcn_exp2f(kp.G1 + G11);
+    }
+  }
+  // spans and flags (every thread reads the same shared values, so the decisions are uniform)
+  const int64_t t0 = step * STEP;
+  const bool valid0 = t0 < p.T, valid1 = t0 + 16 < p.T;
+  const float span0 = fminf(fminf(sm.spanw[0], sm.spanw[1]), fminf(sm.spanw[2], sm.spanw[3])) * kLn2;
+  const float span1 = fminf(fminf(sm.spanw[4], sm.spanw[5]), fminf(sm.spanw[6], sm.spanw[7])) * kLn2;
+  const bool flag0 = valid0 && span0 < kSpanLimit, flag1 = valid1 && span1 < kSpanLimit;
+  const bool pw0 = p.force_fallback || (flag0 && !p.disable_fallback);
+  const bool pw1 = p.force_fallback || (flag1 && !p.disable_fallback);
+  if (tid == 0) {
+    StepInfo si;
+    si.span[0] = valid0 ? span0 : __int_as_float(0x7f800000);
+    si.span[1] = valid1 ? span1 : __int_as_float(0x7f800000);
+    si.n_valid = (valid0 ? 1u : 0u) + (valid1 ? 1u : 0u);
+    si.n_flagged = (flag0 ? 1u : 0u) + (flag1 ? 1u : 0u);
+    si.pairwise = (pw0 ? 1u : 0u) | (pw1 ? 2u : 0u);
+    *reinterpret_cast<StepInfo*>(rec + rMeta) = si;
+  }
+  // per-pair diagonal blocks of flagged chunks: A_rj = beta_r sum_c k_rc k_jc exp(L_rc - L_jc) (j < r),
+  // P_rj = sum_c q_rc k_jc exp(L_rc - L_jc) (j <= r), every factor <= 1
+#pragma unroll 1
+  for (int fc = 0; fc < 2; ++fc) {
+    if (!(fc == 0 ? pw0 : pw1)) continue;
+    if (cc == fc) {
+      float* Ls = reinterpret_cast<float*>(scratch + pL);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int row = 4 * h + j;
+        Ls[row * D + c0] = kp.L0[j];
+        Ls[row * D + c1] = kp.L1[j];
+        *reinterpret_cast<uint32_t*>(scratch + pK + (row * D + c0) * 2) = kp.k[j];
+        if (OUT) *reinterpret_cast<uint32_t*>(scratch + pQ + (row * D + c0) * 2) = kp.q[j];
+      }
+    }
+    block_barrier();
+    const float* Ls = reinterpret_cast<const float*>(scratch + pL);
+    const uint16_t* Ks = reinterpret_cast<const uint16_t*>(scratch + pK);
+    const uint16_t* Qs = reinterpret_cast<const uint16_t*>(scratch + pQ);
+    const float* bt = reinterpret_cast<const float*>(rec + rBeta);
+#pragma unroll 1
+    for (int item = tid; item < 2 * kThreads; item += kThreads) {   // 136 pairs x 4 channel quarters; all lanes run the shuffles
+      const int pi = item >> 2, cq = item & 3;
+      float a = 0.f, pq = 0.f;
+      int r = 0, j = 0;
+      if (pi < 136) {
+        pair_of(pi, r, j);
+        for (int c = 32 * cq; c < 32 * cq + 32; ++c) {
+          const float e = __builtin_amdgcn_exp2f(Ls[r * D + c] - Ls[j * D + c]);
+          const float kj = bf16_to_f32(Ks[j * D + c]) * e;
+          a += bf16_to_f32(Ks[r * D + c]) * kj;
+          if (OUT) pq += bf16_to_f32(Qs[r * D + c]) * kj;
+        }
+      }
+      a += __shfl_xor(a, 1); a += __shfl_xor(a, 2);
+      if (OUT) { pq += __shfl_xor(pq, 1); pq += __shfl_xor(pq, 2); }
+      if (pi < 136 && cq == 0) {
+        sm.pwA[fc][r][j] = bt[16 * fc + r] * a;
+        if (OUT) sm.pwP[fc][r][j] = pq;
+      }
+    }
+    block_barrier();
+  }
+  return (pw0 ? 1u : 0u) | (pw1 ? 2u : 0u);
+}
+
+// ---------------------------------------------------------------- stage TL: causal tiles on MFMA
+template <bool OUT>
+__device__ __forceinline__ void tiles(FusedShared& sm, const unsigned char* rec, const unsigned char* ops, uint32_t pwmask,
+                                      int w, int lane) {
+  const int li = lane & 15, lg = lane >> 4;
+  if (w >= (OUT ? 6 : 3)) return;
+  const float* bt = reinterpret_cast<const float*>(rec + rBeta);
+  const unsigned char *a, *b;
+  switch (w) {
+    case 0: a = rec + rKb; b = ops + oKh; break;             // A_00 (rows of -beta Kbar)
+    case 1: a = ops + oKb1; b = ops + oKh + 4096; break;     // A_11
+    case 2: a = ops + oKb1; b = ops + oKt0; break;           // A_10
+    case 3: a = rec + rQb; b = ops + oKh; break;             // P_00
+    case 4: a = ops + oQb1; b = ops + oKh + 4096; break;     // P_11
+    default: a = ops + oQb1; b = ops + oKt0; break;          // P_10
+  }
+  floatx4 acc = {0, 0, 0, 0};
+#pragma unroll
+  for (int u = 0; u < 4; ++u) acc = mfma(ld8(a + (u * 64 + lane) * 16), ld8(b + (u * 64 + lane) * 16), acc);
+  const bool pw0 = pwmask & 1u, pw1 = pwmask & 2u;
+#pragma unroll
+  for (int r = 0; r < 4; ++r) {
+    const int R = 4 * lg + r;   // D[R][li]: row R, column li of the block
+    switch (w) {
+      case 0: sm.AT[li][R] = li < R ? (pw0 ? sm.pwA[0][R][li] : -acc[r]) : 0.f; break;
+      case 1: sm.AT[16 + li][16 + R] = li < R ? (pw1 ? sm.pwA[1][R][li] : bt[16 + R] * acc[r]) : 0.f; break;
+      case 2: sm.AT[li][16 + R] = bt[16 + R] * acc[r]; sm.AT[16 + li][R] = 0.f; break;
+      case 3: sm.P[R][li] = li <= R ? (pw0 ? sm.pwP[0][R][li] : acc[r]) : 0.f; break;
+      case 4: sm.P[16 + R][16 + li] = li <= R ? (pw1 ? sm.pwP[1][R][li] : acc[r]) : 0.f; break;
+      default: sm.P[16 + R][li] = acc[r]; sm.P[R][16 + li] = 0.f; break;
+    }
+  }
+}
+
+// ---------------------------------------------------------------- stage S: T = (I + A)^{-1}
+// Diagonal block b (wavefront b): forward substitution, right-looking, one column per lane
+// (j = lane & 15; the four lane quarters repeat it so that each can then form its rows of A_10 T_00).
+template <int B>
+__device__ __forceinline__ void solve_diag(FusedShared& sm, int lane_in) {
+  const int lane = opaque(lane_in);
+  const int j = lane & 15, rq = lane >> 4;
+  float col[16];
+#pragma unroll
+  for (int r = 0; r < 16; ++r) col[r] = (r == j) ? 1.f : 0.f;
+  // column i of A (row i of AT), read one iteration ahead
+  floatx4 nxt[4];
+#pragma unroll
+  for (int q = 0; q < 4; ++q) nxt[q] = *reinterpret_cast<const floatx4*>(&sm.AT[16 * B][16 * B + 4 * q]);
+#pragma unroll
+  for (int i = 0; i < 15; ++i) {
+    const floatx4 cur[4] = {nxt[0], nxt[1], nxt[2], nxt[3]};
+    if (i + 1 < 15) {
+#pragma unroll
+      for (int q = 0; q < 4; ++q) nxt[q] = *reinterpret_cast<const floatx4*>(&sm.AT[16 * B + i + 1][16 * B + 4 * q]);
+    }
+    const float xi = col[i];
+#pragma unroll
+    for (int r = i + 1; r < 16; ++r) col[r] -= cur[r >> 2][r & 3] * xi;
+  }
+  if (rq == 0) {
+#pragma unroll
+    for (int r = 0; r < 16; ++r) sm.T32[16 * B + r][16 * B + j] = col[r];
+  }
+  if (B == 0) {   // X = A_10 T_00: lane (j, rq) forms rows 4rq .. 4rq+3 of column j
+    // AT[n][16 + 4rq .. 16 + 4rq + 3] holds A_10[4rq + q][n]
+    floatx4 x = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int n = 0; n < 16; ++n) {
+      const floatx4 a = *reinterpret_cast<const floatx4*>(&sm.AT[n][16 + 4 * rq]);
+#pragma unroll
+      for (int q = 0; q < 4; ++q) x[q] += a[q] * col[n];
+    }
+#pragma unroll
+    for (int q = 0; q < 4; ++q) sm.X[4 * rq + q][j] = x[q];
+  }
+}
+
+// Coupling block T_10 = -T_11 X and T to bf16 in per-lane operand order (one wavefront)
+__device__ __forceinline__ void solve_finish(FusedShared& sm, unsigned char* rec, int lane_in) {
+  const int lane = opaque(lane_in);
+  const int j = lane & 15, rq = lane >> 4, li = lane & 15, lg = lane >> 4;
+  float y[4];
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    const int r = 4 * rq + q;
+    float acc = 0.f;
+#pragma unroll
+    for (int m4 = 0; m4 < 4; ++m4) {
+      const floatx4 t = *reinterpret_cast<const floatx4*>(&sm.T32[16 + r][16 + 4 * m4]);
+      acc += t[0] * sm.X[4 * m4][j] + t[1] * sm.X[4 * m4 + 1][j] + t[2] * sm.X[4 * m4 + 2][j] + t[3] * sm.X[4 * m4 + 3][j];
+    }
+    y[q] = acc;
+  }
+#pragma unroll
+  for (int q = 0; q < 4; ++q) sm.T32[16 + 4 * rq + q][j] = -y[q];
+  lgkm_wait();
+#pragma unroll
+  for (int mt = 0; mt < 2; ++mt) {
+    const floatx4 a = *reinterpret_cast<const floatx4*>(&sm.T32[16 * mt + li][4 * lg]);
+    const floatx4 b = mt == 0 ? floatx4{0, 0, 0, 0} : *reinterpret_cast<const floatx4*>(&sm.T32[16 * mt + li][16 + 4 * lg]);
+    *reinterpret_cast<bf16x8*>(rec + rT + (mt * 64 + lane) * 16) = pack2(a, b);
+  }
+}
+
+__device__ __forceinline__ void pack_p(const FusedShared& sm, unsigned char* rec, int lane) {
+  const int li = lane & 15, lg = lane >> 4;
+#pragma unroll
+  for (int mt = 0; mt < 2; ++mt) {
+    const floatx4 a = *reinterpret_cast<const floatx4*>(&sm.P[16 * mt + li][4 * lg]);
+    const floatx4 b = *reinterpret_cast<const floatx4*>(&sm.P[16 * mt + li][16 + 4 * lg]);
+    *reinterpret_cast<bf16x8*>(rec + rP + (mt * 64 + lane) * 16) = pack2(a, b);
+  }
+}
+
+// ---------------------------------------------------------------- stage C helpers
+// V of one step in D layout for column col: rows 16mt + 4lg + r.  Each value is widened to 32 bits as
+// it is loaded: with 16-bit values the compiler packs two loads into one register at once, waiting
+// for them (and for every load issued before them, among them the next step's prefetch).
+__device__ __forceinline__ void v_load(uint32_t (&vin)[8], const Views& vw, int64_t step, int voff) {
+  const int so = (int)(step * STEP * D * 2);
+#pragma unroll
+  for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+    for (int r = 0; r < 4; ++r) vin[mt * 4 + r] = __builtin_amdgcn_raw_buffer_load_b16(vw.v, voff + (16 * mt + r) * D * 2, so, 0);
+}
+
+__device__ __forceinline__ void beta_v(floatx4 (&bv)[2], const uint32_t (&vin)[8], const unsigned char* rec, int lg) {
+  const float* bt = reinterpret_cast<const float*>(rec + rBeta);
+#pragma unroll
+  for (int mt = 0; mt < 2; ++mt) {
+    const floatx4 b = *reinterpret_cast<const floatx4*>(bt + 16 * mt + 4 * lg);
+#pragma unroll
+    for (int r = 0; r < 4; ++r) bv[mt][r] = b[r] * __uint_as_float(vin[mt * 4 + r] << 16);
+  }
+}
+
+__device__ __forceinline__ int rows_left(int64_t T, int64_t step) {
+  const int64_t rem = T - step * STEP;
+  return rem < STEP ? (int)rem : STEP;
+}
+
+// ---------------------------------------------------------------- the kernel
+template <bool OUT, bool UNB>
+__global__ __launch_bounds__(kThreads) void fused_kernel(Params p, int64_t n_steps, SegPlan sg) {
+  extern __shared__ __align__(16) unsigned char smem_raw[];
+  FusedShared& sm = *reinterpret_cast<FusedShared*>(smem_raw);
+  const int tid = threadIdx.x;
+  // the wavefront index through a scalar register: branches on it (and on the chunk and role derived
+  // from it) are then uniform, rather than masked paths that every wavefront would step through
+  const int lane = tid & 63, w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int li = lane & 15, lg = lane >> 4;
+  const int64_t nseg = OUT ? sg.P : sg.P - 1;
+  const int64_t bh = blockIdx.x / nseg, j = blockIdx.x % nseg;
+  const int64_t s0 = j * sg.L;
+  const int64_t ns = (n_steps - s0 < sg.L) ? n_steps - s0 : sg.L;
+  const int64_t T = p.T;
+  const int col = 16 * w + li;
+  const floatx4 zero = {0, 0, 0, 0};
+
+  Views vw;
+  {
+    const int64_t nb = T * D * 2;
+    vw.k = view((const uint16_t*)p.k + bh * T * D, nb);
+    vw.w = view((const uint16_t*)p.w + bh * T * D, nb);
+    vw.q = view((const uint16_t*)p.q + bh * T * D, nb);
+    vw.v = view((const uint16_t*)p.v + bh * T * D, nb);
+    vw.beta = view((const uint16_t*)p.beta + bh * T, T * 2);
+  }
+  const int e_voff = ((16 * (w >> 2) + 4 * (lane & 3)) * D + 2 * (16 * (w & 3) + (lane >> 2))) * 2;
+  const int e_boff = (16 * (w >> 2) + 4 * (lane & 3)) * 2;
+  const int v_voff = ((4 * lg) * D + col) * 2;
+
+  // state: OUT -> S (the slice of the true state); !OUT -> X (from zero) and M (from the identity)
+  floatx4 S[8], M[8];
+  if (OUT) {
+    if (j > 0) {
+      load_slice(S, (const float*)((const unsigned char*)p.workspace + sg.off_s) + (bh * sg.P + j) * (int64_t)(kSegState / 4) +
+                        w * 8 * 64 * 4, lane);
+    } else if (p.S0) {
+#pragma unroll
+      for (int t = 0; t < 8; ++t)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) S[t][r] = p.S0[(bh * D + 16 * t + 4 * lg + r) * D + col];
+    } else {
+#pragma unroll
+      for (int t = 0; t < 8; ++t) S[t] = zero;
+    }
+  } else {
+#pragma unroll
+    for (int t = 0; t < 8; ++t) {
+      S[t] = zero;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) M[t][r] = (16 * t + 4 * lg + r == col) ? 1.f : 0.f;
+    }
+  }
+
+  EIn ein;
+  EKeep ekeep;
+  uint32_t vin[8];
+  e_load<OUT>(ein, vw, s0, e_voff, e_boff);
+  bf16x8 ub, um;
+  uint32_t nonfinite = 0, n_valid = 0, n_flagged = 0;
+  float min_span = __int_as_float(0x7f800000);
+  uint16_t* o = OUT ? (uint16_t*)p.o + bh * T * D + li * D + 16 * w + 4 * lg : nullptr;
+
+#pragma unroll 1
+  for (int64_t it = -2; it < ns; ++it) {
+    const bool doE = it + 2 < ns, doS = it + 1 >= 0 && it + 1 < ns, doC = it >= 0;
+    unsigned char* recC = sm.rec[(it + 3) % kRecSlots];   // step it       ((it + 3) keeps the index non-negative)
+    unsigned char* recS = sm.rec[(it + 4) % kRecSlots];   // step it + 1
+    unsigned char* recE = sm.rec[(it + 5) % kRecSlots];   // step it + 2
+    unsigned char* opsE = sm.ops[(it + 2) & 1];           // step it + 2
+    unsigned char* opsF = sm.ops[(it + 3) & 1];           // step it + 1 (free: its tiles were formed last interval)
+    block_barrier();
+    const int ln = opaque(lane);   // lane-derived offsets are recomputed in the loop rather than held
+    // ---- first half
+    if (doE) e_first<OUT, UNB>(sm, ein, ekeep, p, s0 + it + 2, recE, opsE, w, ln);
+    // prefetches are issued on every path (clamped to the segment's last step) so that the memory
+    // counter waits before their uses stay exact
+    e_load<OUT>(ein, vw, s0 + (it + 3 < ns ? it + 3 : ns - 1), e_voff, e_boff);
+    if (doS) {
+      if (w == 0) solve_diag<0>(sm, ln);
+      else if (w == 1) solve_diag<1>(sm, ln);
+      else if (OUT && w == 2) pack_p(sm, recS, ln);
+    }
+    if (doC) {
+      bf16x8 sb[4], mb[4];   // bf16 copies of the entering state, the B operands of this step
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        sb[u] = pack2(S[2 * u], S[2 * u + 1]);
+        if (!OUT) mb[u] = pack2(M[2 * u], M[2 * u + 1]);
+      }
+      floatx4 bv[2];
+      beta_v(bv, vin, recC, lg);
+      floatx4 R[2], RM[2];
+#pragma unroll
+      for (int mt = 0; mt < 2; ++mt) { R[mt] = bv[mt]; RM[mt] = zero; }
+#pragma unroll
+      for (int u = 0; u < 4; ++u)
+#pragma unroll
+        for (int mt = 0; mt < 2; ++mt) {
+          const bf16x8 kb = ld8(recC + rKb + ((mt * 4 + u) * 64 + ln) * 16);
+          R[mt] = mfma(kb, sb[u], R[mt]);
+          if (!OUT) RM[mt] = mfma(kb, mb[u], RM[mt]);
+        }
+      const bf16x8 rb = pack2(R[0], R[1]);
+      bf16x8 rbm;
+      if (!OUT) rbm = pack2(RM[0], RM[1]);
+      floatx4 U[2], UM[2];
+#pragma unroll
+      for (int mt = 0; mt < 2; ++mt) {
+        const bf16x8 tm = ld8(recC + rT + (mt * 64 + ln) * 16);
+        U[mt] = mfma(tm, rb, zero);
+        if (!OUT) UM[mt] = mfma(tm, rbm, zero);
+      }
+      ub = pack2(U[0], U[1]);
+      if (!OUT) um = pack2(UM[0], UM[1]);
+      if (OUT) {
+        const int64_t st = s0 + it;
+        const int nrows = rows_left(T, st);
+        floatx4 O[2];
+#pragma unroll
+        for (int mt = 0; mt < 2; ++mt) O[mt] = mfma(ub, ld8(recC + rP + (mt * 64 + ln) * 16), zero);
+#pragma unroll
+        for (int u = 0; u < 4; ++u)
+#pragma unroll
+          for (int mt = 0; mt < 2; ++mt) O[mt] = mfma(sb[u], ld8(recC + rQb + ((mt * 4 + u) * 64 + ln) * 16), O[mt]);
+        uint16_t* os = o + st * STEP * D;
+        uint32_t mx = 0;
+#pragma unroll
+        for (int mt = 0; mt < 2; ++mt) {
+          if (nrows == STEP || 16 * mt + li < nrows) {
+            *reinterpret_cast<uint2*>(os + (16 * mt) * D) = uint2{pk_bf16(O[mt][0], O[mt][1]), pk_bf16(O[mt][2], O[mt][3])};
+#pragma unroll
+            for (int r = 0; r < 4; ++r) mx = max(mx, abs_bits(O[mt][r]));
+          }
+        }
+        if (mx >= 0x7f800000u) {   // rare: count exactly
+#pragma unroll
+          for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+            for (int r = 0; r < 4; ++r)
+              nonfinite += ((nrows == STEP || 16 * mt + li < nrows) && abs_bits(O[mt][r]) >= 0x7f800000u) ? 1u : 0u;
+        }
+        if (w == 0) {
+          const StepInfo si = *reinterpret_cast<const StepInfo*>(recC + rMeta);
+          n_valid += si.n_valid;
+          n_flagged += si.n_flagged;
+          min_span = fminf(min_span, fminf(si.span[0], si.span[1]));
+        }
+      }
+    }
+    v_load(vin, vw, s0 + (it + 1 < 0 ? 0 : (it + 1 < ns ? it + 1 : ns - 1)), v_voff);
+    block_barrier();
+    // ---- second half
+    if (doE) {
+      const uint32_t pwmask = e_second<OUT>(sm, ekeep, p, s0 + it + 2, recE, opsF, w, ln);
+      tiles<OUT>(sm, recE, opsE, pwmask, w, ln);
+    }
+    if (doS && w == 6) solve_finish(sm, recS, ln);
+    if (doC) {
+#pragma unroll
+      for (int t = 0; t < 8; ++t) {
+        const floatx4 eg = *reinterpret_cast<const floatx4*>(recC + rEg + (lg * 32 + 4 * t) * 4);
+        const bf16x8 kt = ld8(recC + rKt + (t * 64 + ln) * 16);
+#pragma unroll
+        for (int r = 0; r < 4; ++r) S[t][r] *= eg[r];
+        S[t] = mfma(kt, ub, S[t]);
+        if (!OUT) {
+#pragma unroll
+          for (int r = 0; r < 4; ++r) M[t][r] *= eg[r];
+          M[t] = mfma(kt, um, M[t]);
+        }
+      }
+    }
+  }
+
+  if (OUT) {
+    if (j == sg.P - 1) {
+#pragma unroll
+      for (int t = 0; t < 8; ++t)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          p.S_final[(bh * D + 16 * t + 4 * lg + r) * D + col] = S[t][r];
+          nonfinite += not_finite(S[t][r]) ? 1u : 0u;
+        }
+    }
+    if (p.stats) {
+#pragma unroll
+      for (int off = 32; off > 0; off >>= 1) nonfinite += __shfl_xor(nonfinite, off);
+      if (lane == 0) {
+        if (nonfinite) atomicAdd(&p.stats->n_nonfinite, nonfinite);
+        if (w == 0) {
+          atomicAdd(&p.stats->n_chunks, n_valid);
+          if (n_flagged) atomicAdd(&p.stats->n_flagged, n_flagged);
+          if (n_valid) atomic_min_float(&p.stats->min_span, min_span);
+        }
+      }
+    }
+  } else {
+    // X_j in slice-major D layout; M_j split into bf16 hi + lo parts, each arranged as the chaining
+    // kernel's A operands: [mo 8][u 4][lane 64][8] <-> M[16 mo + (lane & 15)][32 u + {0,16} + 4 (lane >> 4) + r]
+    const int64_t blk = bh * sg.P + j;
+    float* xo = (float*)((unsigned char*)p.workspace + sg.off_x + blk * (int64_t)kSegState) + w * 8 * 64 * 4;
+    store_slice(xo, S, lane);
+    __bf16* mh = (__bf16*)((unsigned char*)p.workspace + sg.off_m + blk * (int64_t)kSegState);
+    __bf16* ml = mh + kMHalf / 2;
+    const int u = w >> 1, pos = (w & 1) * 4 + (li & 3);
+#pragma unroll
+    for (int t = 0; t < 8; ++t)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int lane_c = (4 * lg + r) + 16 * (li >> 2);   // element M[16t + 4lg + r][16 w + li]
+        const int e = ((t * 4 + u) * 64 + lane_c) * 8 + pos;
+        const __bf16 hi = (__bf16)M[t][r];
+        mh[e] = hi;
+        ml[e] = (__bf16)(M[t][r] - (float)hi);
+      }
+  }
+}
+
+template <bool OUT, bool UNB>
+hipError_t launch_one(const Params& p, hipStream_t s, int64_t n_steps, const SegPlan& sg) {
+  static bool attr_set = false;
+  if (!attr_set) {
+    hipError_t e = hipFuncSetAttribute((const void*)fused_kernel<OUT, UNB>, hipFuncAttributeMaxDynamicSharedMemorySize,
+                                       (int)kFusedSmem);
+    if (e != hipSuccess) return e;
+    attr_set = true;
+  }
+  const int64_t nseg = OUT ? sg.P : sg.P - 1;
+  hipLaunchKernelGGL((fused_kernel<OUT, UNB>), dim3((unsigned)(p.B * p.H * nseg)), dim3(kThreads), kFusedSmem, s, p,
+                     n_steps, sg);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+bool fused_supported(const Params& p) {
+  // 32-bit buffer offsets: a (b, h) slice of a [B,H,T,128] bf16 tensor must stay below 2^31 bytes
+  return p.dtype == KDA_DTYPE_BF16 && p.dk == D && p.dv == D && p.T <= ((int64_t)1 << 23);
+}
+
+hipError_t launch_fused_segments(const Params& p, hipStream_t s, int64_t n_steps, const SegPlan& sg, bool out) {
+  if (out) return p.unbounded ? launch_one<true, true>(p, s, n_steps, sg) : launch_one<true, false>(p, s, n_steps, sg);
+  return p.unbounded ? launch_one<false, true>(p, s, n_steps, sg) : launch_one<false, false>(p, s, n_steps, sg);
+}
+
+}  // namespace kda

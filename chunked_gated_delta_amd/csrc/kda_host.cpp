@@ -55,7 +55,7 @@ int check_gmin(float g_min) {
 int pick_path(const kda::Params& p, const kda_opts_t* opts) {
   const int req = opts ? opts->path : 0;
   if (req == 1) return 1;
-  if (req == 2) return kda::mfma_supported(p) ? 2 : -1;
+  if (req == 2 || req == 3) return kda::mfma_supported(p) ? req : -1;
   return kda::mfma_supported(p) ? 2 : 1;
 }
 
@@ -97,7 +97,7 @@ int kda_chunk_fwd_ex(const void* q, const void* k, const void* v, const void* w,
   if (opts) {
     if (opts->seg_steps < 0) return KDA_ERR_ARG;
     if (opts->disable_fallback && opts->force_fallback) return KDA_ERR_ARG;
-    if (opts->path < 0 || opts->path > 2) return KDA_ERR_UNSUPPORTED;
+    if (opts->path < 0 || opts->path > 3) return KDA_ERR_UNSUPPORTED;
   }
   const int64_t B = shape->B, H = shape->H, T = shape->T, dk = shape->dk, dv = shape->dv;
   const int64_t esz = shape->dtype == KDA_DTYPE_BF16 ? 2 : 4;
@@ -146,8 +146,8 @@ int kda_chunk_fwd_ex(const void* q, const void* k, const void* v, const void* w,
 
   const int path = T > 0 ? pick_path(p, opts) : 1;
   if (path < 0) return KDA_ERR_UNSUPPORTED;
-  if (path == 2 && need_ws > 0 && (!workspace || workspace_bytes < need_ws)) return KDA_ERR_ARG;
-  if (path == 2 && !kda::mfma_seg_steps_ok(T, p.seg_steps)) return KDA_ERR_ARG;
+  if (path >= 2 && need_ws > 0 && (!workspace || workspace_bytes < need_ws)) return KDA_ERR_ARG;
+  if (path >= 2 && !kda::mfma_seg_steps_ok(T, p.seg_steps)) return KDA_ERR_ARG;
 
   // ---- launches (first HIP call of the entry point)
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
@@ -161,8 +161,8 @@ int kda_chunk_fwd_ex(const void* q, const void* k, const void* v, const void* w,
     if (ev1 && (e = hipEventRecord(ev1, s)) != hipSuccess) return hip_fail(e);
     return KDA_OK;
   }
-  if (path == 2) {
-    if ((e = kda::launch_mfma(p, s, ev0, ev1)) != hipSuccess) return hip_fail(e);
+  if (path >= 2) {
+    if ((e = kda::launch_mfma(p, s, ev0, ev1, path == 3)) != hipSuccess) return hip_fail(e);
   } else {
     if (ev0 && (e = hipEventRecord(ev0, s)) != hipSuccess) return hip_fail(e);
     if ((e = kda::launch_vec(p, s)) != hipSuccess) return hip_fail(e);

@@ -38,7 +38,7 @@ hipError_t launch_vec(const Params& p, hipStream_t s);                 // plain 
 bool mfma_supported(const Params& p);                                   // matrix-core path available?
 size_t mfma_workspace_bytes(int64_t B, int64_t H, int64_t T, int64_t dk, int64_t dv);
 bool mfma_seg_steps_ok(int64_t T, int64_t seg_steps);                    // forced segment length allowed?
-hipError_t launch_mfma(const Params& p, hipStream_t s, hipEvent_t ev_begin, hipEvent_t ev_end);
+hipError_t launch_mfma(const Params& p, hipStream_t s, hipEvent_t ev_begin, hipEvent_t ev_end, bool fused);
 
 // ---------------------------------------------------------------- device helpers
 

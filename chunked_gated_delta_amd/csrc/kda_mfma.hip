@@ -28,19 +28,14 @@
 // referenced to the chunk boundary, e^{L_r} e^{Gam_0 - L_j}, both <= 1.  A
 // chunk whose span falls below -80 gets its diagonal blocks from per-pair
 // factors exp(L_r - L_j) <= 1 on the vector ALUs instead.
-#include "kda_internal.h"
+#include "kda_mfma_util.h"
 
 namespace kda {
 
 namespace {
 
-typedef __attribute__((__vector_size__(8 * sizeof(__bf16)))) __bf16 bf16x8;
-typedef __attribute__((__vector_size__(4 * sizeof(float)))) float floatx4;
-
 constexpr int D = 128;     // dk = dv
 constexpr int STEP = 32;   // tokens per step (two chunks)
-constexpr float kLog2e = 1.4426950408889634f;
-constexpr float kLn2 = 0.6931471805599453f;
 
 // record layout (bytes) of one (b, h, step)
 constexpr int kOffWn = 0;        // -W,  [mt 2][u 4] blocks of 64 lanes x 16 B
@@ -57,19 +52,6 @@ struct StepMeta {           // per (b, h, step)
   uint32_t n_valid;         // chunks with at least one token (1 or 2)
   uint32_t n_flagged;       // of those, spans below -80
 };
-
-__device__ __forceinline__ floatx4 mfma(bf16x8 a, bf16x8 b, floatx4 c) {
-  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
-}
-
-__device__ __forceinline__ bf16x8 ld8(const __bf16* p) { return *reinterpret_cast<const bf16x8*>(p); }
-
-// gate in log2 units: g * log2(e)
-__device__ __forceinline__ float gate_log2(float w, float g_min, int unbounded) {
-  if (unbounded) return -(fmaxf(w, 0.f) + log1pf(expf(-fabsf(w)))) * kLog2e;
-  const float s = __builtin_amdgcn_rcpf(1.f + __builtin_amdgcn_exp2f(-w * kLog2e));
-  return (g_min * kLog2e) * s;
-}
 
 __device__ __forceinline__ float bf(const uint16_t* p, int64_t i) { return bf16_to_f32(p[i]); }
 
@@ -111,12 +93,6 @@ struct SolveShared {
   alignas(16) __bf16 Ph[STEP][kRowT];    // P T diag(beta)
 };
 static_assert(sizeof(SolveShared) <= sizeof(__bf16) * (2 * STEP + 16) * kRow, "solve arrays must fit over Kb, Kh, Kt0");
-
-__device__ __forceinline__ uint32_t pk_bf16(float lo, float hi) {
-  return (uint32_t)__builtin_bit_cast(uint16_t, (__bf16)lo) | ((uint32_t)__builtin_bit_cast(uint16_t, (__bf16)hi) << 16);
-}
-__device__ __forceinline__ float lo_bf16(uint32_t x) { return __uint_as_float(x << 16); }
-__device__ __forceinline__ float hi_bf16(uint32_t x) { return __uint_as_float(x & 0xffff0000u); }
 
 // diagonal block of chunk cc from per-pair factors exp(L_r - L_j) <= 1 (no reciprocal); raw q in Kh rows,
 // raw k in Kb rows, L of the chunk in L[][]
@@ -481,9 +457,6 @@ constexpr int kRingSlots = 4;
 constexpr int kSegWaves = 8;
 constexpr int kSegThreads = 64 * kSegWaves;
 constexpr int kVTileBytes = STEP * D * 2;                    // one step of V, all 128 columns, row-major
-constexpr int kSegState = D * D * 4;                         // bytes of one 128 x 128 fp32 block (64 KiB)
-constexpr int kMaxSeg = 32;                                  // segments per (b, h)
-constexpr int kMHalf = 8 * 4 * 64 * 16;                      // bytes of one bf16 part of M (32 KiB)
 static_assert(2 * kMHalf == kSegState, "hi + lo parts of M fill one block");
 
 // seg_out slot: the whole record, then V
@@ -498,24 +471,6 @@ constexpr size_t kStSmem = (size_t)kRingSlots * kStSlot;
 static_assert(kOutSmem <= 163840 && kStSmem <= 163840, "LDS budget");
 static_assert(kOutSlot % 1024 == 0 && kStSlot % 1024 == 0, "slots are whole 1 KiB chunks");
 static_assert((kOutChunks / kSegWaves + 1) * (kRingSlots - 1) + 4 <= 63, "outstanding loads fit the vmcnt counter");
-
-struct SegPlan {
-  int64_t P, L;            // segments per (b, h) and steps per segment (the last one may be shorter)
-  int64_t off_x, off_m, off_s;   // workspace byte offsets of the X, M and S_start blocks
-};
-
-typedef __attribute__((address_space(3))) void lds_void;
-
-__device__ __forceinline__ void compiler_fence() { __atomic_signal_fence(__ATOMIC_SEQ_CST); }
-
-// Workgroup barrier that waits only for this wave's LDS operations (so its LDS writes are visible
-// after it), not for global loads in flight.
-__device__ __forceinline__ void block_barrier() {
-  compiler_fence();
-  __builtin_amdgcn_s_waitcnt(0xF | (0x3 << 14) | (0x7 << 4) | (0x0 << 8));   // lgkmcnt(0)
-  __builtin_amdgcn_s_barrier();
-  compiler_fence();
-}
 
 // s_waitcnt with only vmcnt constrained (expcnt and lgkmcnt left at their maxima)
 template <int N> __device__ __forceinline__ void wait_vm() {
@@ -563,29 +518,9 @@ __device__ __forceinline__ bf16x8 v_operand(const unsigned char* vt, int lg, int
   return vb;
 }
 
-__device__ __forceinline__ bf16x8 pack2(floatx4 a, floatx4 b) {
-  bf16x8 o;
-#pragma unroll
-  for (int r = 0; r < 4; ++r) { o[r] = (__bf16)a[r]; o[4 + r] = (__bf16)b[r]; }
-  return o;
-}
-
-__device__ __forceinline__ uint32_t abs_bits(float x) { return __float_as_uint(x) & 0x7fffffffu; }
-
 __device__ __forceinline__ int rows_of(int64_t T, int64_t st) {
   const int64_t rem = T - st * STEP;
   return rem < STEP ? (int)rem : STEP;
-}
-
-// 128 x 16 fp32 slice in D layout (lane (li, lg), tile t, register r <-> row 16t+4lg+r, column li),
-// stored as [t][lane] float4 blocks
-__device__ __forceinline__ void store_slice(float* dst, const floatx4 (&S)[8], int lane) {
-#pragma unroll
-  for (int t = 0; t < 8; ++t) *reinterpret_cast<floatx4*>(dst + (t * 64 + lane) * 4) = S[t];
-}
-__device__ __forceinline__ void load_slice(floatx4 (&S)[8], const float* src, int lane) {
-#pragma unroll
-  for (int t = 0; t < 8; ++t) S[t] = *reinterpret_cast<const floatx4*>(src + (t * 64 + lane) * 4);
 }
 
 // ---- seg_state_kernel: X_j and M_j of segment j < P-1
@@ -911,8 +846,9 @@ __global__ __launch_bounds__(kSegThreads) void seg_out_kernel(Params p, int64_t 
 int64_t n_steps_of(int64_t T) { return (T + STEP - 1) / STEP; }
 
 // Segment plan.  Automatic: about 256 workgroups (one per compute unit) over (b, h, segment), at least
-// 8 steps per segment and at most kMaxSeg segments.  seg_steps > 0 fixes the segment length.
-SegPlan make_plan(int64_t BH, int64_t T, int64_t seg_steps) {
+// 8 steps per segment and at most kMaxSeg segments.  seg_steps > 0 fixes the segment length.  With
+// `records`, the per-step records precede the segment blocks in the workspace.
+SegPlan make_plan(int64_t BH, int64_t T, int64_t seg_steps, bool records) {
   const int64_t n = n_steps_of(T);
   SegPlan sg{};
   int64_t P;
@@ -929,7 +865,7 @@ SegPlan make_plan(int64_t BH, int64_t T, int64_t seg_steps) {
     P = (n + sg.L - 1) / sg.L;
   }
   sg.P = P;
-  const int64_t recs = BH * n * (int64_t)kRecBytes;
+  const int64_t recs = records ? BH * n * (int64_t)kRecBytes : 0;
   const int64_t blk = BH * (int64_t)(n < kMaxSeg ? n : kMaxSeg) * kSegState;
   sg.off_x = recs;
   sg.off_m = recs + blk;
@@ -957,10 +893,23 @@ bool mfma_seg_steps_ok(int64_t T, int64_t seg_steps) {
   return (n + seg_steps - 1) / seg_steps <= kMaxSeg;
 }
 
-hipError_t launch_mfma(const Params& p, hipStream_t s, hipEvent_t ev_begin, hipEvent_t ev_end) {
+hipError_t launch_mfma(const Params& p, hipStream_t s, hipEvent_t ev_begin, hipEvent_t ev_end, bool fused) {
   const int64_t n_steps = n_steps_of(p.T);
   const int64_t BH = p.B * p.H;
-  const SegPlan sg = make_plan(BH, p.T, p.seg_steps);
+  fused = fused && fused_supported(p);
+  const SegPlan sg = make_plan(BH, p.T, p.seg_steps, !fused);
+  if (fused) {
+    hipError_t e;
+    if (ev_begin && (e = hipEventRecord(ev_begin, s)) != hipSuccess) return e;
+    if (sg.P > 1) {
+      if ((e = launch_fused_segments(p, s, n_steps, sg, false)) != hipSuccess) return e;
+      hipLaunchKernelGGL(seg_combine_kernel, dim3((unsigned)(BH * 8)), dim3(256), 0, s, p, sg);
+      if ((e = hipGetLastError()) != hipSuccess) return e;
+    }
+    if ((e = launch_fused_segments(p, s, n_steps, sg, true)) != hipSuccess) return e;
+    if (ev_end && (e = hipEventRecord(ev_end, s)) != hipSuccess) return e;
+    return hipSuccess;
+  }
   static bool attr_set = false;
   if (!attr_set) {
     hipError_t e = hipFuncSetAttribute((const void*)prep_kernel, hipFuncAttributeMaxDynamicSharedMemorySize,

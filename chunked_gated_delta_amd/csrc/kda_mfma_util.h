@@ -1,0 +1,86 @@
+// Device helpers shared by the matrix-core kernels (bf16 MFMA 16x16x32 on gfx950).
+//
+// Operand layouts of v_mfma_f32_16x16x32_bf16 (lane l, li = l & 15, g = l >> 4):
+//   A (16 x 32): lane holds A[li][8g .. 8g+7]      B (32 x 16): lane holds B[8g .. 8g+7][li]
+//   D (16 x 16): lane holds D[4g + r][li], r = 0..3
+// The kernels contract over a permuted K order, {4g + r, 16 + 4g + r}: with it, the D-layout
+// tiles of rows 0-15 and 16-31 packed side by side are directly the B operand of the next product.
+#pragma once
+
+#include "kda_internal.h"
+
+namespace kda {
+
+typedef __attribute__((__vector_size__(8 * sizeof(__bf16)))) __bf16 bf16x8;
+typedef __attribute__((__vector_size__(4 * sizeof(float)))) float floatx4;
+typedef __attribute__((address_space(3))) void lds_void;
+
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+
+__device__ __forceinline__ floatx4 mfma(bf16x8 a, bf16x8 b, floatx4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+
+__device__ __forceinline__ bf16x8 ld8(const void* p) { return *reinterpret_cast<const bf16x8*>(p); }
+
+// gate in log2 units: g * log2(e)
+__device__ __forceinline__ float gate_log2(float w, float g_min, int unbounded) {
+  if (unbounded) return -(fmaxf(w, 0.f) + log1pf(expf(-fabsf(w)))) * kLog2e;
+  const float s = __builtin_amdgcn_rcpf(1.f + __builtin_amdgcn_exp2f(-w * kLog2e));
+  return (g_min * kLog2e) * s;
+}
+
+__device__ __forceinline__ uint32_t pk_bf16(float lo, float hi) {
+  return (uint32_t)__builtin_bit_cast(uint16_t, (__bf16)lo) | ((uint32_t)__builtin_bit_cast(uint16_t, (__bf16)hi) << 16);
+}
+__device__ __forceinline__ float lo_bf16(uint32_t x) { return __uint_as_float(x << 16); }
+__device__ __forceinline__ float hi_bf16(uint32_t x) { return __uint_as_float(x & 0xffff0000u); }
+
+__device__ __forceinline__ bf16x8 pack2(floatx4 a, floatx4 b) {
+  bf16x8 o;
+#pragma unroll
+  for (int r = 0; r < 4; ++r) { o[r] = (__bf16)a[r]; o[4 + r] = (__bf16)b[r]; }
+  return o;
+}
+
+__device__ __forceinline__ uint32_t abs_bits(float x) { return __float_as_uint(x) & 0x7fffffffu; }
+
+__device__ __forceinline__ void compiler_fence() { __atomic_signal_fence(__ATOMIC_SEQ_CST); }
+
+// Workgroup barrier that waits only for this wave's LDS operations (so its LDS writes are visible
+// after it), not for global memory operations in flight.
+__device__ __forceinline__ void block_barrier() {
+  compiler_fence();
+  __builtin_amdgcn_s_waitcnt(0xF | (0x3 << 14) | (0x7 << 4) | (0x0 << 8));   // lgkmcnt(0)
+  __builtin_amdgcn_s_barrier();
+  compiler_fence();
+}
+
+// 128 x 16 fp32 slice in D layout (lane (li, lg), tile t, register r <-> row 16t+4lg+r, column li),
+// stored as [t][lane] float4 blocks
+__device__ __forceinline__ void store_slice(float* dst, const floatx4 (&S)[8], int lane) {
+#pragma unroll
+  for (int t = 0; t < 8; ++t) *reinterpret_cast<floatx4*>(dst + (t * 64 + lane) * 4) = S[t];
+}
+__device__ __forceinline__ void load_slice(floatx4 (&S)[8], const float* src, int lane) {
+#pragma unroll
+  for (int t = 0; t < 8; ++t) S[t] = *reinterpret_cast<const floatx4*>(src + (t * 64 + lane) * 4);
+}
+
+// Segment plan shared by the scan kernels: P segments of L steps (32 tokens) per (b, h); workspace
+// byte offsets of the per-segment X, M and S_start blocks (128 x 128 fp32 each).
+struct SegPlan {
+  int64_t P, L;
+  int64_t off_x, off_m, off_s;
+};
+constexpr int kSegState = 128 * 128 * 4;    // bytes of one block (64 KiB)
+constexpr int kMHalf = 8 * 4 * 64 * 16;     // bytes of one bf16 part (hi or lo) of a transition M
+constexpr int kMaxSeg = 32;                 // segments per (b, h)
+
+// the fused segment kernels take this configuration (bf16, dk = dv = 128, 32-bit buffer offsets)
+bool fused_supported(const Params& p);
+// the fused segment kernels (one launch: every segment's map when !out, every segment's outputs when out)
+hipError_t launch_fused_segments(const Params& p, hipStream_t s, int64_t n_steps, const SegPlan& sg, bool out);
+
+}  // namespace kda

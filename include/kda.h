@@ -99,7 +99,8 @@ typedef struct {
 typedef struct {
   int32_t disable_fallback; /* 1: flagged chunks still take the dense exp(+-G) path (shows the overflow) */
   int32_t force_fallback;   /* 1: every chunk takes the per-position path (measures its cost) */
-  int32_t path;             /* 0 auto, 1 the plain fp32 vector path, 2 the matrix-core path */
+  int32_t path;             /* 0 auto, 1 the plain fp32 vector path, 2 the matrix-core path with
+                               per-step records in the workspace, 3 the fused matrix-core path */
   int32_t seg_steps;        /* matrix-core path: steps of 32 tokens per sequence segment (0 = automatic;
                                < 0, or more than 32 segments per sequence, is KDA_ERR_ARG) */
   void* ev_begin;           /* optional hipEvent_t recorded on `stream` before the call's first kernel */

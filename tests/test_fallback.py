@@ -17,7 +17,7 @@ if not torch.cuda.is_available():
     pytest.skip("no GPU", allow_module_level=True)
 
 UNB = gen.WORKLOADS["unbounded"]
-PATHS = ["vector", "mfma"]
+PATHS = ["vector", "mfma", "fused"]
 
 
 @pytest.mark.parametrize("path", PATHS)

@@ -40,13 +40,15 @@ def run_full(name, heads, seed=0, path="auto"):
     return wl, stats, inp
 
 
-def test_bf16_4k_full():
-    wl, stats, _ = run_full("bf16_4k", [(0, 0), (1, 15), (0, 7)])
+@pytest.mark.parametrize("path", ["auto", "fused"])
+def test_bf16_4k_full(path):
+    wl, stats, _ = run_full("bf16_4k", [(0, 0), (1, 15), (0, 7)], path=path)
     assert stats["n_nonfinite"] == 0 and stats["n_flagged"] == 0
 
 
-def test_unbounded_full():
-    wl, stats, inp = run_full("unbounded", [(0, 3), (1, 12)])
+@pytest.mark.parametrize("path", ["auto", "fused"])
+def test_unbounded_full(path):
+    wl, stats, inp = run_full("unbounded", [(0, 3), (1, 12)], path=path)
     assert stats["n_nonfinite"] == 0
     spans = orc.chunk_spans(inp["w"].float().cpu().numpy(), wl.g_min, 16)
     pred = spans < -80.0
@@ -55,13 +57,15 @@ def test_unbounded_full():
     assert abs(stats["n_flagged"] - int(pred.sum())) <= int(ties.sum())
 
 
-def test_headline_full():
-    _, stats, _ = run_full("headline", [(0, 0), (0, 9)])
+@pytest.mark.parametrize("path", ["auto", "fused"])
+def test_headline_full(path):
+    _, stats, _ = run_full("headline", [(0, 0), (0, 9)], path=path)
     assert stats["n_nonfinite"] == 0 and stats["n_flagged"] == 0
 
 
-def test_decay_stress_full():
-    _, stats, _ = run_full("decay_stress", [(0, 5), (0, 31)])
+@pytest.mark.parametrize("path", ["auto", "fused"])
+def test_decay_stress_full(path):
+    _, stats, _ = run_full("decay_stress", [(0, 5), (0, 31)], path=path)
     assert stats["n_nonfinite"] == 0 and stats["n_flagged"] == 0
     assert -80.0 <= stats["min_span"] < -79.5
 

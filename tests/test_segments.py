@@ -19,9 +19,12 @@ if not torch.cuda.is_available():
 BF16 = gen.WORKLOADS["bf16_4k"]
 
 
-def check(wl, seed, **kw):
-    need_path("mfma")
-    eo, es, st, *_ = compare(wl, seed=seed, path="mfma", **kw)
+SEG_PATHS = ["mfma", "fused"]
+
+
+def check(wl, seed, path, **kw):
+    need_path(path)
+    eo, es, st, *_ = compare(wl, seed=seed, path=path, **kw)
     tol_o, tol_s = TOL[wl.dtype]
     say(f"   err_o={eo:.3e} (tol {tol_o})  err_S={es:.3e} (tol {tol_s})  stats={st}")
     assert eo <= tol_o and es <= tol_s
@@ -30,52 +33,59 @@ def check(wl, seed, **kw):
     return st
 
 
+@pytest.mark.parametrize("path", SEG_PATHS)
 @pytest.mark.parametrize("T,seg", [(64, 1), (300, 1), (300, 2), (300, 3), (1000, 1), (1000, 5), (1000, 7)])
-def test_forced_segments(T, seg):
-    check(BF16.with_(B=1, H=2, T=T), seed=200 + T + seg, seg_steps=seg)
+def test_forced_segments(T, seg, path):
+    check(BF16.with_(B=1, H=2, T=T), seed=200 + T + seg, path=path, seg_steps=seg)
 
 
+@pytest.mark.parametrize("path", SEG_PATHS)
 @pytest.mark.parametrize("seg", [1, 4])
-def test_segments_with_initial_state(seg):
+def test_segments_with_initial_state(seg, path):
     """Decay-stress gates with S0 ~ N(0, 0.1): the first segment starts from S0."""
-    st = check(gen.WORKLOADS["decay_stress"].with_(H=2, T=1000), seed=3, seg_steps=seg)
+    st = check(gen.WORKLOADS["decay_stress"].with_(H=2, T=1000), seed=3, path=path, seg_steps=seg)
     assert st["n_flagged"] == 0
 
 
-def test_segments_no_decay():
+@pytest.mark.parametrize("path", SEG_PATHS)
+def test_segments_no_decay(path):
     """g_min = 0: nothing is forgotten, so each segment transition is a pure
     product of (I - beta k k^T) factors, far from zero.  A nonzero S0 flows
     through every transition."""
-    check(BF16.with_(B=1, H=2, T=640, g_min=0.0, s0_sd=0.5), seed=14, seg_steps=2)
+    check(BF16.with_(B=1, H=2, T=640, g_min=0.0, s0_sd=0.5), seed=14, path=path, seg_steps=2)
 
 
-def test_segments_pure_decay():
+@pytest.mark.parametrize("path", SEG_PATHS)
+def test_segments_pure_decay(path):
     """beta = 0: X = 0 and M = diag(prod e^g), so the state is S0, decayed.  The decay is
     slow (w ~ N(-5, 0.5), about -0.034 per token), so the decayed S0 stays well inside fp32's range."""
     wl = BF16.with_(B=1, H=2, T=800, s0_sd=0.5, w_mu=-5.0, w_sd=0.5)
-    check(wl, seed=15, seg_steps=3, mutate=lambda inp: inp["beta"].fill(0.0))
+    check(wl, seed=15, path=path, seg_steps=3, mutate=lambda inp: inp["beta"].fill(0.0))
 
 
-def test_segments_with_flagged_chunks():
+@pytest.mark.parametrize("path", SEG_PATHS)
+def test_segments_with_flagged_chunks(path):
     """g_min = -8: chunks past the span limit take the per-position path inside segments."""
     wl = BF16.with_(B=1, H=2, T=700, g_min=-8.0, w_mu=4.0, w_sd=1.0)
-    st = check(wl, seed=16, seg_steps=3)
+    st = check(wl, seed=16, path=path, seg_steps=3)
     pred = orc.predicted_flags(gen.make_numpy(wl, 16)["w"], -8.0)
     assert st["n_flagged"] == int(pred.sum()) and st["n_flagged"] > 0
 
 
-def test_automatic_plan_several_heads():
+@pytest.mark.parametrize("path", SEG_PATHS)
+def test_automatic_plan_several_heads(path):
     """B2 H4 T2048: the automatic plan cuts each sequence into 8 segments of 8 steps."""
-    check(BF16.with_(B=2, H=4, T=2048), seed=17)
+    check(BF16.with_(B=2, H=4, T=2048), seed=17, path=path)
 
 
-def test_segment_plans_agree():
+@pytest.mark.parametrize("path", SEG_PATHS)
+def test_segment_plans_agree(path):
     """Different segment plans change only the rounding."""
-    need_path("mfma")
+    need_path(path)
     wl = BF16.with_(B=1, H=2, T=900, s0_sd=0.3)
     t = gen.numpy_to_torch(gen.make_numpy(wl, 18), "cuda")
-    say(f"[case] segment plans {wl}")
-    outs = [gpu_run(t, wl.g_min, path="mfma", seg_steps=s) for s in (0, 2, 3, 29)]
+    say(f"[case] segment plans {wl} path={path}")
+    outs = [gpu_run(t, wl.g_min, path=path, seg_steps=s) for s in (0, 2, 3, 29)]
     o0, S0_, _ = outs[0]
     for o, S, _ in outs[1:]:
         assert rel_err(o.float().cpu().numpy(), o0.float().cpu().numpy()) < 1e-2
