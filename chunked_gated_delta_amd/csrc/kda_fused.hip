@@ -41,27 +41,35 @@ namespace {
 
 constexpr int D = 128;
 constexpr int STEP = 32;
-constexpr int kWaves = 8;
-constexpr int kThreads = 64 * kWaves;
+constexpr int kCWaves = 8;                    // wavefronts 0-7: state slices, tiles, solve
+constexpr int kEWaves = 8;                    // wavefronts 8-15: the E stage
+constexpr int kThreads = 64 * (kCWaves + kEWaves);
+
+// ---- operand blocks: one MFMA operand (64 lanes x 16 B), with a 16-byte pad after every 16 lanes,
+// so that the 4-byte writes of the E stage (16 lanes 256 B apart) land in distinct LDS banks, while a
+// 16-byte-per-lane read stays contiguous within each group of 16 lanes
+constexpr int kBlk = 68 * 16;                                           // bytes of one block
+__device__ __forceinline__ int slot16(int lane) { return (lane + (lane >> 4)) * 16; }
 
 // ---- per-step operand record (LDS), arranged so that every MFMA operand is one 16-byte read per lane
-constexpr int rKb = 0;        // -beta Kbar, [mt 2][u 4] x 64 lanes x 16 B: row 16mt + li, channels 32u + {4g+r, 16+4g+r}
-constexpr int rQb = 8192;     // Qbar, same arrangement                                      (OUT only)
-constexpr int rKt = 16384;    // Ktil^T, [t 8] blocks: channel 16t + li, tokens {4g+r, 16+4g+r}
-constexpr int rT = 24576;     // T, [mt 2] blocks: row 16mt + li, tokens {4g+r, 16+4g+r}
-constexpr int rP = 26624;     // P, same arrangement                                         (OUT only)
-constexpr int rEg = 28672;    // e^{Gam_step}: [g 4][t 8][r 4] fp32 <-> channel 16t + 4g + r
-constexpr int rBeta = 29184;  // beta per token, fp32 (zero past the end of the sequence)
-constexpr int rMeta = 29312;  // StepInfo
-constexpr int kRec = 29440;
-constexpr int kRecSlots = 3;  // steps s (C), s+1 (S), s+2 (E, TL)
+constexpr int rKb = 0;                // -beta Kbar, [mt 2][u 4] blocks: row 16mt + li, channels 32u + {4g+r, 16+4g+r}
+constexpr int rQb = rKb + 8 * kBlk;   // Qbar, same arrangement                                    (OUT only)
+constexpr int rKt = rQb + 8 * kBlk;   // Ktil^T, [t 8] blocks: channel 16t + li, tokens {4g+r, 16+4g+r}
+constexpr int rT = rKt + 8 * kBlk;    // T, [mt 2] blocks: row 16mt + li, tokens {4g+r, 16+4g+r}
+constexpr int rP = rT + 2 * kBlk;     // P, same arrangement                                       (OUT only)
+constexpr int rEg = rP + 2 * kBlk;    // e^{Gam_step}: [g 4][t 8][r 4] fp32 <-> channel 16t + 4g + r
+constexpr int rBeta = rEg + 512;      // beta per token, fp32 (zero past the end of the sequence)
+constexpr int rMeta = rBeta + 128;    // StepInfo
+constexpr int kRec = rMeta + 32;
+constexpr int kRecSlots = 3;          // steps s (C), s+1 (S), s+2 (E, TL)
+static_assert(kRec % 16 == 0, "record slots stay 16-byte aligned");
 
 // ---- tile operands of one step, same per-lane arrangement as rKb ([rt][u] blocks)
-constexpr int oKh = 0;        // k e^{-L}, chunks 0 and 1 [cc 2][u 4]
-constexpr int oKb1 = 8192;    // k e^{L}, chunk 1
-constexpr int oQb1 = 12288;   // q e^{L}, chunk 1                                             (OUT only)
-constexpr int oKt0 = 16384;   // k e^{Gam_0 - L}, chunk 0
-constexpr int kOps = 20480;
+constexpr int oKh = 0;                // k e^{-L}, chunks 0 and 1 [cc 2][u 4]
+constexpr int oKb1 = oKh + 8 * kBlk;  // k e^{L}, chunk 1
+constexpr int oQb1 = oKb1 + 4 * kBlk; // q e^{L}, chunk 1                                          (OUT only)
+constexpr int oKt0 = oQb1 + 4 * kBlk; // k e^{Gam_0 - L}, chunk 0
+constexpr int kOps = oKt0 + 4 * kBlk;
 // the per-pair path of a flagged chunk borrows the tile-operand buffer of step s+1 (free during the
 // second half of interval s): L (fp32 [16][128]), raw k and raw q (bf16 [16][128])
 constexpr int pL = 0, pK = 8192, pQ = 12288;
@@ -85,7 +93,7 @@ struct FusedShared {
   float X[16][20];                        // A_10 T_00
   float pwA[2][16][16], pwP[2][16][16];   // per-pair diagonal blocks [chunk][r][j]
   float gam[2][D];                        // chunk totals (log2 units) of the step in E
-  float spanw[kWaves];                    // per-wave minimum of the chunk totals
+  float spanw[kEWaves];                   // per-E-wave minimum of the chunk totals
 };
 constexpr size_t kFusedSmem = sizeof(FusedShared);
 static_assert(kFusedSmem <= 163840, "LDS budget");
@@ -95,6 +103,25 @@ static_assert(kFusedSmem <= 163840, "LDS budget");
 __device__ __forceinline__ int opaque(int x) {
   asm volatile("" : "+v"(x));
   return x;
+}
+
+// DPP moves within a wave (no LDS round trip): quad_perm selects within groups of four lanes;
+// row_shr shifts within rows of 16 lanes (lanes without a source keep `old`); row_bcast:15 / :31
+// carry lane 15 of each row, lane 31, into the following rows
+template <int CTRL, int ROW_MASK = 0xF>
+__device__ __forceinline__ float dpp(float old, float src) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(__float_as_int(old), __float_as_int(src), CTRL, ROW_MASK, 0xF, false));
+}
+
+// minimum over the wave, valid in lane 63
+__device__ __forceinline__ float wave_min_to_63(float m) {
+  m = fminf(m, dpp<0x111>(m, m));   // row_shr:1
+  m = fminf(m, dpp<0x112>(m, m));   // row_shr:2
+  m = fminf(m, dpp<0x114>(m, m));   // row_shr:4
+  m = fminf(m, dpp<0x118>(m, m));   // row_shr:8  -> lane 15 of each row holds the row minimum
+  m = fminf(m, dpp<0x142, 0xA>(m, m));   // row_bcast:15 into rows 1 and 3
+  m = fminf(m, dpp<0x143, 0xC>(m, m));   // row_bcast:31 into rows 2 and 3
+  return m;
 }
 
 __device__ __forceinline__ void lgkm_wait() {
@@ -153,8 +180,10 @@ __device__ __forceinline__ void e_load(EIn& in, const Views& vw, int64_t step, i
 
 // offset of (row li of row tile rt, this thread's channel pair) in a [rt][u] block array
 __device__ __forceinline__ int rowk_off(int rt, int u, int li, int g, int pos) {
-  return ((rt * 4 + u) * 64 + li + 16 * g) * 16 + pos * 2;
+  return (rt * 4 + u) * kBlk + (li + 17 * g) * 16 + pos * 2;
 }
+// offset of (channel c, token quarter h, chunk cc) in the Ktil^T blocks
+__device__ __forceinline__ int kt_off(int c, int h, int cc) { return (c >> 4) * kBlk + ((c & 15) + 17 * h) * 16 + cc * 8; }
 
 template <bool OUT, bool UNB>
 __device__ __forceinline__ void e_first(FusedShared& sm, const EIn& in, EKeep& kp, const Params& p, int64_t step,
@@ -177,44 +206,46 @@ __device__ __forceinline__ void e_first(FusedShared& sm, const EIn& in, EKeep& k
     kp.L0[j] = a0;
     kp.L1[j] = a1;
   }
-  // prefix across the quarter group (lanes 4m .. 4m+3)
-  float s0 = a0, s1 = a1, t0, t1;
-  t0 = __shfl_up(s0, 1, 4); t1 = __shfl_up(s1, 1, 4);
-  if (h >= 1) { s0 += t0; s1 += t1; }
-  t0 = __shfl_up(s0, 2, 4); t1 = __shfl_up(s1, 2, 4);
-  if (h >= 2) { s0 += t0; s1 += t1; }
+  // prefix across the quarter group (lanes 4m .. 4m+3) with quad permutes
+  float s0 = a0, s1 = a1;
+  {
+    const float t0 = dpp<0x90>(0.f, s0), t1 = dpp<0x90>(0.f, s1);   // quad_perm [0,0,1,2]: lane h <- h-1
+    if (h >= 1) { s0 += t0; s1 += t1; }
+    const float u0 = dpp<0x40>(0.f, s0), u1 = dpp<0x40>(0.f, s1);   // quad_perm [0,0,0,1]: lane h <- h-2
+    if (h >= 2) { s0 += u0; s1 += u1; }
+  }
   const float x0 = s0 - a0, x1 = s1 - a1;              // exclusive prefix
-  kp.G0 = __shfl(s0, 3, 4);
-  kp.G1 = __shfl(s1, 3, 4);
+  kp.G0 = dpp<0xFF>(0.f, s0);                          // quad_perm [3,3,3,3]: the chunk totals
+  kp.G1 = dpp<0xFF>(0.f, s1);
 #pragma unroll
   for (int j = 0; j < 4; ++j) { kp.L0[j] += x0; kp.L1[j] += x1; }
   if (h == 0) { sm.gam[cc][c0] = kp.G0; sm.gam[cc][c1] = kp.G1; }
-  float m = fminf(kp.G0, kp.G1);
-#pragma unroll
-  for (int off = 32; off > 0; off >>= 1) m = fminf(m, __shfl_xor(m, off));
-  if (l == 0) sm.spanw[w] = m;
+  const float m = wave_min_to_63(fminf(kp.G0, kp.G1));
+  if (l == 63) sm.spanw[w] = m;
   if ((w & 3) == 0 && (l >> 2) == 0) {
     float* bt = reinterpret_cast<float*>(rec + rBeta);
 #pragma unroll
     for (int j = 0; j < 4; ++j) bt[16 * cc + 4 * h + j] = kp.beta[j];
   }
-  uint32_t kt0[2], kt1[2];     // Ktil^T of this thread's channels in chunk 1
+  float ktv0[4], ktv1[4];      // Ktil of this thread's channels in chunk 1
+  // e^{-L} = e^{Gam - L} e^{-Gam}: finite wherever the dense tile is used (a chunk whose e^{-Gam}
+  // overflows has a span below -80 and takes the per-pair blocks instead)
+  const float iG0 = __builtin_amdgcn_exp2f(-kp.G0), iG1 = __builtin_amdgcn_exp2f(-kp.G1);
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
     const int li = 4 * h + j;
     const float k0 = lo_bf16(kp.k[j]), k1 = hi_bf16(kp.k[j]);
     const float e0 = __builtin_amdgcn_exp2f(kp.L0[j]), e1 = __builtin_amdgcn_exp2f(kp.L1[j]);
     const float g0 = __builtin_amdgcn_exp2f(kp.G0 - kp.L0[j]), g1 = __builtin_amdgcn_exp2f(kp.G1 - kp.L1[j]);  // <= 1
-    *reinterpret_cast<uint32_t*>(ops + oKh + rowk_off(cc, u, li, g, pos)) =
-        pk_bf16(k0 * __builtin_amdgcn_exp2f(-kp.L0[j]), k1 * __builtin_amdgcn_exp2f(-kp.L1[j]));
+    *reinterpret_cast<uint32_t*>(ops + oKh + rowk_off(cc, u, li, g, pos)) = pk_bf16(k0 * g0 * iG0, k1 * g1 * iG1);
     if (cc == 1) {
       kp.f0[j] = e0; kp.f1[j] = e1;
       *reinterpret_cast<uint32_t*>(ops + oKb1 + rowk_off(0, u, li, g, pos)) = pk_bf16(k0 * e0, k1 * e1);
       if (OUT)
         *reinterpret_cast<uint32_t*>(ops + oQb1 + rowk_off(0, u, li, g, pos)) =
             pk_bf16(lo_bf16(kp.q[j]) * e0, hi_bf16(kp.q[j]) * e1);
-      const uint32_t a = __builtin_bit_cast(uint16_t, (__bf16)(k0 * g0)), b = __builtin_bit_cast(uint16_t, (__bf16)(k1 * g1));
-      if (j & 1) { kt0[j >> 1] |= a << 16; kt1[j >> 1] |= b << 16; } else { kt0[j >> 1] = a; kt1[j >> 1] = b; }
+      ktv0[j] = k0 * g0;
+      ktv1[j] = k1 * g1;
     } else {
       kp.f0[j] = g0; kp.f1[j] = g1;
       const float nb = -kp.beta[j];
@@ -226,8 +257,10 @@ __device__ __forceinline__ void e_first(FusedShared& sm, const EIn& in, EKeep& k
     }
   }
   if (cc == 1) {   // channel c -> block c >> 4, lane (c & 15) + 16 h, positions 4 .. 7
-    *reinterpret_cast<uint2*>(rec + rKt + ((c0 >> 4) * 64 + (c0 & 15) + 16 * h) * 16 + 8) = uint2{kt0[0], kt0[1]};
-    *reinterpret_cast<uint2*>(rec + rKt + ((c1 >> 4) * 64 + (c1 & 15) + 16 * h) * 16 + 8) = uint2{kt1[0], kt1[1]};
+    *reinterpret_cast<uint2*>(rec + rKt + kt_off(c0, h, 1)) =
+        uint2{pk_bf16(ktv0[0], ktv0[1]), pk_bf16(ktv0[2], ktv0[3])};
+    *reinterpret_cast<uint2*>(rec + rKt + kt_off(c1, h, 1)) =
+        uint2{pk_bf16(ktv1[0], ktv1[1]), pk_bf16(ktv1[2], ktv1[3])};
   }
 }
 
@@ -237,10 +270,9 @@ __device__ __forceinline__ void pair_of(int pr, int& r, int& j) {   // pr -> (r,
   j = pr - r * (r + 1) / 2;
 }
 
-// returns the per-pair mask of the step (bit c: chunk c), the same in every thread
 template <bool OUT>
-__device__ __forceinline__ uint32_t e_second(FusedShared& sm, const EKeep& kp, const Params& p, int64_t step,
-                                             unsigned char* rec, unsigned char* scratch, int w, int l) {
+__device__ __forceinline__ void e_second(FusedShared& sm, const EKeep& kp, const Params& p, int64_t step,
+                                         unsigned char* rec, int w, int l) {
   const int tid = w * 64 + l;
   const int cc = w >> 2, pr = 16 * (w & 3) + (l >> 2), h = l & 3;
   const int u = w & 3, g = ((l >> 2) & 7) >> 1, pos = (l >> 5) * 4 + 2 * ((l >> 2) & 1);
@@ -261,52 +293,70 @@ __device__ __forceinline__ uint32_t e_second(FusedShared& sm, const EKeep& kp, c
   } else {         // chunk 0: Ktil = k e^{Gam_0 - L} e^{Gam_1}; e^{Gam_step}
     const float G10 = sm.gam[1][c0], G11 = sm.gam[1][c1];
     const float y0 = __builtin_amdgcn_exp2f(G10), y1 = __builtin_amdgcn_exp2f(G11);
-    uint32_t kt0[2], kt1[2];
+    float a[4], b[4];
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-      const uint32_t a = __builtin_bit_cast(uint16_t, (__bf16)(lo_bf16(kp.k[j]) * kp.f0[j] * y0));
-      const uint32_t b = __builtin_bit_cast(uint16_t, (__bf16)(hi_bf16(kp.k[j]) * kp.f1[j] * y1));
-      if (j & 1) { kt0[j >> 1] |= a << 16; kt1[j >> 1] |= b << 16; } else { kt0[j >> 1] = a; kt1[j >> 1] = b; }
+      a[j] = lo_bf16(kp.k[j]) * kp.f0[j] * y0;
+      b[j] = hi_bf16(kp.k[j]) * kp.f1[j] * y1;
     }
-    *reinterpret_cast<uint2*>(rec + rKt + ((c0 >> 4) * 64 + (c0 & 15) + 16 * h) * 16) = uint2{kt0[0], kt0[1]};
-    *reinterpret_cast<uint2*>(rec + rKt + ((c1 >> 4) * 64 + (c1 & 15) + 16 * h) * 16) = uint2{kt1[0], kt1[1]};
+    *reinterpret_cast<uint2*>(rec + rKt + kt_off(c0, h, 0)) = uint2{pk_bf16(a[0], a[1]), pk_bf16(a[2], a[3])};
+    *reinterpret_cast<uint2*>(rec + rKt + kt_off(c1, h, 0)) = uint2{pk_bf16(b[0], b[1]), pk_bf16(b[2], b[3])};
     if (h == 0) {
       float* eg = reinterpret_cast<float*>(rec + rEg);
       eg[((c0 >> 2) & 3) * 32 + (c0 >> 4) * 4 + (c0 & 3)] = __builtin_amdgcn_exp2f(kp.G0 + G10);
       eg[((c1 >> 2) & 3) * 32 + (c1 >> 4) * 4 + (c1 & 3)] = __builtin_amdgcn_exp2f(kp.G1 + G11);
     }
   }
-  // spans and flags (every thread reads the same shared values, so the decisions are uniform)
+  // spans and flags: the step's information record
   const int64_t t0 = step * STEP;
-  const bool valid0 = t0 < p.T, valid1 = t0 + 16 < p.T;
-  const float span0 = fminf(fminf(sm.spanw[0], sm.spanw[1]), fminf(sm.spanw[2], sm.spanw[3])) * kLn2;
-  const float span1 = fminf(fminf(sm.spanw[4], sm.spanw[5]), fminf(sm.spanw[6], sm.spanw[7])) * kLn2;
-  const bool flag0 = valid0 && span0 < kSpanLimit, flag1 = valid1 && span1 < kSpanLimit;
-  const bool pw0 = p.force_fallback || (flag0 && !p.disable_fallback);
-  const bool pw1 = p.force_fallback || (flag1 && !p.disable_fallback);
   if (tid == 0) {
+    const bool valid0 = t0 < p.T, valid1 = t0 + 16 < p.T;
+    const float span0 = fminf(fminf(sm.spanw[0], sm.spanw[1]), fminf(sm.spanw[2], sm.spanw[3])) * kLn2;
+    const float span1 = fminf(fminf(sm.spanw[4], sm.spanw[5]), fminf(sm.spanw[6], sm.spanw[7])) * kLn2;
+    const bool flag0 = valid0 && span0 < kSpanLimit, flag1 = valid1 && span1 < kSpanLimit;
     StepInfo si;
     si.span[0] = valid0 ? span0 : __int_as_float(0x7f800000);
     si.span[1] = valid1 ? span1 : __int_as_float(0x7f800000);
     si.n_valid = (valid0 ? 1u : 0u) + (valid1 ? 1u : 0u);
     si.n_flagged = (flag0 ? 1u : 0u) + (flag1 ? 1u : 0u);
-    si.pairwise = (pw0 ? 1u : 0u) | (pw1 ? 2u : 0u);
+    si.pairwise = (p.force_fallback || (flag0 && !p.disable_fallback) ? 1u : 0u) |
+                  (p.force_fallback || (flag1 && !p.disable_fallback) ? 2u : 0u);
     *reinterpret_cast<StepInfo*>(rec + rMeta) = si;
   }
-  // per-pair diagonal blocks of flagged chunks: A_rj = beta_r sum_c k_rc k_jc exp(L_rc - L_jc) (j < r),
-  // P_rj = sum_c q_rc k_jc exp(L_rc - L_jc) (j <= r), every factor <= 1
+}
+
+// Which chunks of the step in E take the per-pair blocks (bit c: chunk c).  Every thread of the
+// workgroup reads the same shared values, so the answer (and every branch on it) is uniform.
+__device__ __forceinline__ uint32_t pairwise_mask(const FusedShared& sm, const Params& p, int64_t step) {
+  const int64_t t0 = step * STEP;
+  const bool valid0 = t0 < p.T, valid1 = t0 + 16 < p.T;
+  const float span0 = fminf(fminf(sm.spanw[0], sm.spanw[1]), fminf(sm.spanw[2], sm.spanw[3])) * kLn2;
+  const float span1 = fminf(fminf(sm.spanw[4], sm.spanw[5]), fminf(sm.spanw[6], sm.spanw[7])) * kLn2;
+  const bool pw0 = p.force_fallback || (valid0 && span0 < kSpanLimit && !p.disable_fallback);
+  const bool pw1 = p.force_fallback || (valid1 && span1 < kSpanLimit && !p.disable_fallback);
+  return (pw0 ? 1u : 0u) | (pw1 ? 2u : 0u);
+}
+
+// Per-pair diagonal blocks of flagged chunks, by the whole workgroup: A_rj = beta_r sum_c k_rc k_jc
+// exp(L_rc - L_jc) (j < r), P_rj = sum_c q_rc k_jc exp(L_rc - L_jc) (j <= r), every factor <= 1.  The
+// E wavefronts of the chunk first park L, raw k and raw q in `scratch`.
+template <bool OUT, bool IS_E>
+__device__ __forceinline__ void pairwise_blocks(FusedShared& sm, const EKeep* kp, const unsigned char* rec,
+                                                unsigned char* scratch, uint32_t mask, int we, int l, int tid) {
+  const int cc = we >> 2, pr = 16 * (we & 3) + (l >> 2), h = l & 3;
+  const int c0 = 2 * pr, c1 = 2 * pr + 1;
 #pragma unroll 1
   for (int fc = 0; fc < 2; ++fc) {
-    if (!(fc == 0 ? pw0 : pw1)) continue;
-    if (cc == fc) {
+    if (!(mask & (1u << fc))) continue;
+    if (IS_E && cc == fc) {
       float* Ls = reinterpret_cast<float*>(scratch + pL);
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
         const int row = 4 * h + j;
-        Ls[row * D + c0] = kp.L0[j];
-        Ls[row * D + c1] = kp.L1[j];
-        *reinterpret_cast<uint32_t*>(scratch + pK + (row * D + c0) * 2) = kp.k[j];
-        if (OUT) *reinterpret_cast<uint32_t*>(scratch + pQ + (row * D + c0) * 2) = kp.q[j];
+        Ls[row * D + c0] = kp->L0[j];
+        Ls[row * D + c1] = kp->L1[j];
+        *reinterpret_cast<uint32_t*>(scratch + pK + (row * D + c0) * 2) = kp->k[j];
+        if (OUT) *reinterpret_cast<uint32_t*>(scratch + pQ + (row * D + c0) * 2) = kp->q[j];
       }
     }
     block_barrier();
@@ -314,9 +364,8 @@ __device__ __forceinline__ uint32_t e_second(FusedShared& sm, const EKeep& kp, c
     const uint16_t* Ks = reinterpret_cast<const uint16_t*>(scratch + pK);
     const uint16_t* Qs = reinterpret_cast<const uint16_t*>(scratch + pQ);
     const float* bt = reinterpret_cast<const float*>(rec + rBeta);
-#pragma unroll 1
-    for (int item = tid; item < 2 * kThreads; item += kThreads) {   // 136 pairs x 4 channel quarters; all lanes run the shuffles
-      const int pi = item >> 2, cq = item & 3;
+    {   // 136 pairs x 4 channel quarters over the workgroup's threads; all lanes run the shuffles
+      const int pi = tid >> 2, cq = tid & 3;
       float a = 0.f, pq = 0.f;
       int r = 0, j = 0;
       if (pi < 136) {
@@ -337,8 +386,9 @@ __device__ __forceinline__ uint32_t e_second(FusedShared& sm, const EKeep& kp, c
     }
     block_barrier();
   }
-  return (pw0 ? 1u : 0u) | (pw1 ? 2u : 0u);
 }
+
+static_assert(136 * 4 <= kThreads, "one per-pair item per thread");
 
 // ---------------------------------------------------------------- stage TL: causal tiles on MFMA
 template <bool OUT>
@@ -350,15 +400,15 @@ __device__ __forceinline__ void tiles(FusedShared& sm, const unsigned char* rec,
   const unsigned char *a, *b;
   switch (w) {
     case 0: a = rec + rKb; b = ops + oKh; break;             // A_00 (rows of -beta Kbar)
-    case 1: a = ops + oKb1; b = ops + oKh + 4096; break;     // A_11
+    case 1: a = ops + oKb1; b = ops + oKh + 4 * kBlk; break; // A_11
     case 2: a = ops + oKb1; b = ops + oKt0; break;           // A_10
     case 3: a = rec + rQb; b = ops + oKh; break;             // P_00
-    case 4: a = ops + oQb1; b = ops + oKh + 4096; break;     // P_11
+    case 4: a = ops + oQb1; b = ops + oKh + 4 * kBlk; break; // P_11
     default: a = ops + oQb1; b = ops + oKt0; break;          // P_10
   }
   floatx4 acc = {0, 0, 0, 0};
 #pragma unroll
-  for (int u = 0; u < 4; ++u) acc = mfma(ld8(a + (u * 64 + lane) * 16), ld8(b + (u * 64 + lane) * 16), acc);
+  for (int u = 0; u < 4; ++u) acc = mfma(ld8(a + u * kBlk + slot16(lane)), ld8(b + u * kBlk + slot16(lane)), acc);
   const bool pw0 = pwmask & 1u, pw1 = pwmask & 2u;
 #pragma unroll
   for (int r = 0; r < 4; ++r) {
@@ -384,20 +434,16 @@ __device__ __forceinline__ void solve_diag(FusedShared& sm, int lane_in) {
   float col[16];
 #pragma unroll
   for (int r = 0; r < 16; ++r) col[r] = (r == j) ? 1.f : 0.f;
-  // column i of A (row i of AT), read one iteration ahead
-  floatx4 nxt[4];
 #pragma unroll
-  for (int q = 0; q < 4; ++q) nxt[q] = *reinterpret_cast<const floatx4*>(&sm.AT[16 * B][16 * B + 4 * q]);
-#pragma unroll
-  for (int i = 0; i < 15; ++i) {
-    const floatx4 cur[4] = {nxt[0], nxt[1], nxt[2], nxt[3]};
-    if (i + 1 < 15) {
-#pragma unroll
-      for (int q = 0; q < 4; ++q) nxt[q] = *reinterpret_cast<const floatx4*>(&sm.AT[16 * B + i + 1][16 * B + 4 * q]);
-    }
+  for (int i = 0; i < 15; ++i) {   // column i of A is row i of AT
     const float xi = col[i];
 #pragma unroll
-    for (int r = i + 1; r < 16; ++r) col[r] -= cur[r >> 2][r & 3] * xi;
+    for (int q = (i + 1) >> 2; q < 4; ++q) {
+      const floatx4 a = *reinterpret_cast<const floatx4*>(&sm.AT[16 * B + i][16 * B + 4 * q]);
+#pragma unroll
+      for (int rr = 0; rr < 4; ++rr)
+        if (4 * q + rr > i) col[4 * q + rr] -= a[rr] * xi;
+    }
   }
   if (rq == 0) {
 #pragma unroll
@@ -440,7 +486,7 @@ __device__ __forceinline__ void solve_finish(FusedShared& sm, unsigned char* rec
   for (int mt = 0; mt < 2; ++mt) {
     const floatx4 a = *reinterpret_cast<const floatx4*>(&sm.T32[16 * mt + li][4 * lg]);
     const floatx4 b = mt == 0 ? floatx4{0, 0, 0, 0} : *reinterpret_cast<const floatx4*>(&sm.T32[16 * mt + li][16 + 4 * lg]);
-    *reinterpret_cast<bf16x8*>(rec + rT + (mt * 64 + lane) * 16) = pack2(a, b);
+    *reinterpret_cast<bf16x8*>(rec + rT + mt * kBlk + slot16(lane)) = pack2(a, b);
   }
 }
 
@@ -450,7 +496,7 @@ __device__ __forceinline__ void pack_p(const FusedShared& sm, unsigned char* rec
   for (int mt = 0; mt < 2; ++mt) {
     const floatx4 a = *reinterpret_cast<const floatx4*>(&sm.P[16 * mt + li][4 * lg]);
     const floatx4 b = *reinterpret_cast<const floatx4*>(&sm.P[16 * mt + li][16 + 4 * lg]);
-    *reinterpret_cast<bf16x8*>(rec + rP + (mt * 64 + lane) * 16) = pack2(a, b);
+    *reinterpret_cast<bf16x8*>(rec + rP + mt * kBlk + slot16(lane)) = pack2(a, b);
   }
 }
 
@@ -482,6 +528,8 @@ __device__ __forceinline__ int rows_left(int64_t T, int64_t step) {
 }
 
 // ---------------------------------------------------------------- the kernel
+// Wavefronts 0-7 (C) own the state slices (slice w: 16 columns) and run the tiles and the solve;
+// wavefronts 8-15 (E) run the E stage.  Both kinds meet at the same two barriers per interval.
 template <bool OUT, bool UNB>
 __global__ __launch_bounds__(kThreads) void fused_kernel(Params p, int64_t n_steps, SegPlan sg) {
   extern __shared__ __align__(16) unsigned char smem_raw[];
@@ -490,13 +538,15 @@ __global__ __launch_bounds__(kThreads) void fused_kernel(Params p, int64_t n_ste
   // the wavefront index through a scalar register: branches on it (and on the chunk and role derived
   // from it) are then uniform, rather than masked paths that every wavefront would step through
   const int lane = tid & 63, w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const bool is_e = w >= kCWaves;
+  const int we = w - kCWaves;                 // E wavefront index (valid when is_e)
   const int li = lane & 15, lg = lane >> 4;
   const int64_t nseg = OUT ? sg.P : sg.P - 1;
   const int64_t bh = blockIdx.x / nseg, j = blockIdx.x % nseg;
   const int64_t s0 = j * sg.L;
   const int64_t ns = (n_steps - s0 < sg.L) ? n_steps - s0 : sg.L;
   const int64_t T = p.T;
-  const int col = 16 * w + li;
+  const int col = 16 * (w & 7) + li;
   const floatx4 zero = {0, 0, 0, 0};
 
   Views vw;
@@ -508,11 +558,45 @@ __global__ __launch_bounds__(kThreads) void fused_kernel(Params p, int64_t n_ste
     vw.v = view((const uint16_t*)p.v + bh * T * D, nb);
     vw.beta = view((const uint16_t*)p.beta + bh * T, T * 2);
   }
-  const int e_voff = ((16 * (w >> 2) + 4 * (lane & 3)) * D + 2 * (16 * (w & 3) + (lane >> 2))) * 2;
-  const int e_boff = (16 * (w >> 2) + 4 * (lane & 3)) * 2;
+  const int e_voff = ((16 * (we >> 2) + 4 * (lane & 3)) * D + 2 * (16 * (we & 3) + (lane >> 2))) * 2;
+  const int e_boff = (16 * (we >> 2) + 4 * (lane & 3)) * 2;
   const int v_voff = ((4 * lg) * D + col) * 2;
 
-  // state: OUT -> S (the slice of the true state); !OUT -> X (from zero) and M (from the identity)
+  // The two kinds of wavefront run separate copies of the step loop (same trip count, same barriers in
+  // the same order), so that each copy holds only its own kind's values in registers.
+  if (is_e) {
+    EIn ein;
+    EKeep ekeep;
+    e_load<OUT>(ein, vw, s0, e_voff, e_boff);
+#pragma unroll 1
+    for (int64_t it = -2; it < ns; ++it) {
+      const bool doE = it + 2 < ns, doS = it + 1 >= 0 && it + 1 < ns;
+      unsigned char* recS = sm.rec[(it + 4) % kRecSlots];   // step it + 1
+      unsigned char* recE = sm.rec[(it + 5) % kRecSlots];   // step it + 2
+      unsigned char* opsE = sm.ops[(it + 2) & 1];           // step it + 2
+      unsigned char* opsF = sm.ops[(it + 3) & 1];           // step it + 1 (free: its tiles were formed last interval)
+      block_barrier();
+      const int ln = opaque(lane);   // lane-derived offsets are recomputed in the loop rather than held
+      if (doE) e_first<OUT, UNB>(sm, ein, ekeep, p, s0 + it + 2, recE, opsE, we, ln);
+      // prefetches are issued on every path (clamped to the segment's last step) so that the memory
+      // counter waits before their uses stay exact
+      if (doS) {
+        if (we == 0) solve_diag<0>(sm, ln);
+        else if (we == 1) solve_diag<1>(sm, ln);
+        else if (OUT && we == 2) pack_p(sm, recS, ln);
+      }
+      e_load<OUT>(ein, vw, s0 + (it + 3 < ns ? it + 3 : ns - 1), e_voff, e_boff);
+      block_barrier();
+      if (doE) {
+        e_second<OUT>(sm, ekeep, p, s0 + it + 2, recE, we, ln);
+        const uint32_t pwmask = pairwise_mask(sm, p, s0 + it + 2);
+        if (pwmask) pairwise_blocks<OUT, true>(sm, &ekeep, recE, opsF, pwmask, we, ln, tid);
+      }
+    }
+    return;
+  }
+
+  // C wavefronts: OUT -> S (the slice of the true state); !OUT -> X (from zero) and M (from the identity)
   floatx4 S[8], M[8];
   if (OUT) {
     if (j > 0) {
@@ -535,12 +619,7 @@ __global__ __launch_bounds__(kThreads) void fused_kernel(Params p, int64_t n_ste
       for (int r = 0; r < 4; ++r) M[t][r] = (16 * t + 4 * lg + r == col) ? 1.f : 0.f;
     }
   }
-
-  EIn ein;
-  EKeep ekeep;
   uint32_t vin[8];
-  e_load<OUT>(ein, vw, s0, e_voff, e_boff);
-  bf16x8 ub, um;
   uint32_t nonfinite = 0, n_valid = 0, n_flagged = 0;
   float min_span = __int_as_float(0x7f800000);
   uint16_t* o = OUT ? (uint16_t*)p.o + bh * T * D + li * D + 16 * w + 4 * lg : nullptr;
@@ -552,61 +631,39 @@ __global__ __launch_bounds__(kThreads) void fused_kernel(Params p, int64_t n_ste
     unsigned char* recS = sm.rec[(it + 4) % kRecSlots];   // step it + 1
     unsigned char* recE = sm.rec[(it + 5) % kRecSlots];   // step it + 2
     unsigned char* opsE = sm.ops[(it + 2) & 1];           // step it + 2
-    unsigned char* opsF = sm.ops[(it + 3) & 1];           // step it + 1 (free: its tiles were formed last interval)
+    unsigned char* opsF = sm.ops[(it + 3) & 1];           // step it + 1
     block_barrier();
-    const int ln = opaque(lane);   // lane-derived offsets are recomputed in the loop rather than held
-    // ---- first half
-    if (doE) e_first<OUT, UNB>(sm, ein, ekeep, p, s0 + it + 2, recE, opsE, w, ln);
-    // prefetches are issued on every path (clamped to the segment's last step) so that the memory
-    // counter waits before their uses stay exact
-    e_load<OUT>(ein, vw, s0 + (it + 3 < ns ? it + 3 : ns - 1), e_voff, e_boff);
-    if (doS) {
-      if (w == 0) solve_diag<0>(sm, ln);
-      else if (w == 1) solve_diag<1>(sm, ln);
-      else if (OUT && w == 2) pack_p(sm, recS, ln);
-    }
+    const int ln = opaque(lane);
+    const int sl = slot16(ln);
+    // ---- first half: the whole recurrence step of step it
     if (doC) {
-      bf16x8 sb[4], mb[4];   // bf16 copies of the entering state, the B operands of this step
+      bf16x8 sb[4];   // bf16 copies of the entering state, the B operands of this step
 #pragma unroll
-      for (int u = 0; u < 4; ++u) {
-        sb[u] = pack2(S[2 * u], S[2 * u + 1]);
-        if (!OUT) mb[u] = pack2(M[2 * u], M[2 * u + 1]);
-      }
+      for (int u = 0; u < 4; ++u) sb[u] = pack2(S[2 * u], S[2 * u + 1]);
       floatx4 bv[2];
       beta_v(bv, vin, recC, lg);
-      floatx4 R[2], RM[2];
+      floatx4 R[2];
 #pragma unroll
-      for (int mt = 0; mt < 2; ++mt) { R[mt] = bv[mt]; RM[mt] = zero; }
+      for (int mt = 0; mt < 2; ++mt) R[mt] = bv[mt];
 #pragma unroll
       for (int u = 0; u < 4; ++u)
 #pragma unroll
-        for (int mt = 0; mt < 2; ++mt) {
-          const bf16x8 kb = ld8(recC + rKb + ((mt * 4 + u) * 64 + ln) * 16);
-          R[mt] = mfma(kb, sb[u], R[mt]);
-          if (!OUT) RM[mt] = mfma(kb, mb[u], RM[mt]);
-        }
+        for (int mt = 0; mt < 2; ++mt) R[mt] = mfma(ld8(recC + rKb + (mt * 4 + u) * kBlk + sl), sb[u], R[mt]);
       const bf16x8 rb = pack2(R[0], R[1]);
-      bf16x8 rbm;
-      if (!OUT) rbm = pack2(RM[0], RM[1]);
-      floatx4 U[2], UM[2];
+      floatx4 U[2];
 #pragma unroll
-      for (int mt = 0; mt < 2; ++mt) {
-        const bf16x8 tm = ld8(recC + rT + (mt * 64 + ln) * 16);
-        U[mt] = mfma(tm, rb, zero);
-        if (!OUT) UM[mt] = mfma(tm, rbm, zero);
-      }
-      ub = pack2(U[0], U[1]);
-      if (!OUT) um = pack2(UM[0], UM[1]);
+      for (int mt = 0; mt < 2; ++mt) U[mt] = mfma(ld8(recC + rT + mt * kBlk + sl), rb, zero);
+      const bf16x8 ub = pack2(U[0], U[1]);
       if (OUT) {
         const int64_t st = s0 + it;
         const int nrows = rows_left(T, st);
         floatx4 O[2];
 #pragma unroll
-        for (int mt = 0; mt < 2; ++mt) O[mt] = mfma(ub, ld8(recC + rP + (mt * 64 + ln) * 16), zero);
+        for (int mt = 0; mt < 2; ++mt) O[mt] = mfma(ub, ld8(recC + rP + mt * kBlk + sl), zero);
 #pragma unroll
         for (int u = 0; u < 4; ++u)
 #pragma unroll
-          for (int mt = 0; mt < 2; ++mt) O[mt] = mfma(sb[u], ld8(recC + rQb + ((mt * 4 + u) * 64 + ln) * 16), O[mt]);
+          for (int mt = 0; mt < 2; ++mt) O[mt] = mfma(sb[u], ld8(recC + rQb + (mt * 4 + u) * kBlk + sl), O[mt]);
         uint16_t* os = o + st * STEP * D;
         uint32_t mx = 0;
 #pragma unroll
@@ -631,30 +688,48 @@ __global__ __launch_bounds__(kThreads) void fused_kernel(Params p, int64_t n_ste
           min_span = fminf(min_span, fminf(si.span[0], si.span[1]));
         }
       }
-    }
-    v_load(vin, vw, s0 + (it + 1 < 0 ? 0 : (it + 1 < ns ? it + 1 : ns - 1)), v_voff);
-    block_barrier();
-    // ---- second half
-    if (doE) {
-      const uint32_t pwmask = e_second<OUT>(sm, ekeep, p, s0 + it + 2, recE, opsF, w, ln);
-      tiles<OUT>(sm, recE, opsE, pwmask, w, ln);
-    }
-    if (doS && w == 6) solve_finish(sm, recS, ln);
-    if (doC) {
+      // state update: S <- diag(e^{Gam}) S + Ktil^T U
 #pragma unroll
       for (int t = 0; t < 8; ++t) {
         const floatx4 eg = *reinterpret_cast<const floatx4*>(recC + rEg + (lg * 32 + 4 * t) * 4);
-        const bf16x8 kt = ld8(recC + rKt + (t * 64 + ln) * 16);
 #pragma unroll
         for (int r = 0; r < 4; ++r) S[t][r] *= eg[r];
-        S[t] = mfma(kt, ub, S[t]);
-        if (!OUT) {
+        S[t] = mfma(ld8(recC + rKt + t * kBlk + sl), ub, S[t]);
+      }
+      if (!OUT) {   // the transition slice, after the state slice so that the two need not be live at once
+        // fresh offsets: reusing the state slice's loads would keep them live across both slices
+        const int sl = opaque(slot16(ln)), lgm = opaque(lg);
+        bf16x8 mb[4];
+#pragma unroll
+        for (int u = 0; u < 4; ++u) mb[u] = pack2(M[2 * u], M[2 * u + 1]);
+        floatx4 RM[2] = {zero, zero};
+#pragma unroll
+        for (int u = 0; u < 4; ++u)
+#pragma unroll
+          for (int mt = 0; mt < 2; ++mt) RM[mt] = mfma(ld8(recC + rKb + (mt * 4 + u) * kBlk + sl), mb[u], RM[mt]);
+        const bf16x8 rbm = pack2(RM[0], RM[1]);
+        floatx4 UM[2];
+#pragma unroll
+        for (int mt = 0; mt < 2; ++mt) UM[mt] = mfma(ld8(recC + rT + mt * kBlk + sl), rbm, zero);
+        const bf16x8 um = pack2(UM[0], UM[1]);
+#pragma unroll
+        for (int t = 0; t < 8; ++t) {
+          const floatx4 eg = *reinterpret_cast<const floatx4*>(recC + rEg + (lgm * 32 + 4 * t) * 4);
 #pragma unroll
           for (int r = 0; r < 4; ++r) M[t][r] *= eg[r];
-          M[t] = mfma(kt, um, M[t]);
+          M[t] = mfma(ld8(recC + rKt + t * kBlk + sl), um, M[t]);
         }
       }
     }
+    v_load(vin, vw, s0 + (it + 1 < 0 ? 0 : (it + 1 < ns ? it + 1 : ns - 1)), v_voff);
+    block_barrier();
+    // ---- second half: per-pair blocks (if any), tiles of step it + 2, the coupling block of step it + 1
+    if (doE) {
+      const uint32_t pwmask = pairwise_mask(sm, p, s0 + it + 2);
+      if (pwmask) pairwise_blocks<OUT, false>(sm, nullptr, recE, opsF, pwmask, 0, ln, tid);
+      tiles<OUT>(sm, recE, opsE, pwmask, w, ln);
+    }
+    if (doS && w == 6) solve_finish(sm, recS, ln);
   }
 
   if (OUT) {

@@ -31,17 +31,21 @@ __device__ __forceinline__ float gate_log2(float w, float g_min, int unbounded) 
   return (g_min * kLog2e) * s;
 }
 
+typedef __bf16 bf16x2v __attribute__((ext_vector_type(2)));
+typedef float float2v __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x8v __attribute__((ext_vector_type(8)));
+typedef float float8v __attribute__((ext_vector_type(8)));
+
+// two floats to packed bf16 (round to nearest even), one v_cvt_pk_bf16_f32
 __device__ __forceinline__ uint32_t pk_bf16(float lo, float hi) {
-  return (uint32_t)__builtin_bit_cast(uint16_t, (__bf16)lo) | ((uint32_t)__builtin_bit_cast(uint16_t, (__bf16)hi) << 16);
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector((float2v){lo, hi}, bf16x2v));
 }
 __device__ __forceinline__ float lo_bf16(uint32_t x) { return __uint_as_float(x << 16); }
 __device__ __forceinline__ float hi_bf16(uint32_t x) { return __uint_as_float(x & 0xffff0000u); }
 
 __device__ __forceinline__ bf16x8 pack2(floatx4 a, floatx4 b) {
-  bf16x8 o;
-#pragma unroll
-  for (int r = 0; r < 4; ++r) { o[r] = (__bf16)a[r]; o[4 + r] = (__bf16)b[r]; }
-  return o;
+  const float8v f = {a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
+  return __builtin_bit_cast(bf16x8, __builtin_convertvector(f, bf16x8v));
 }
 
 __device__ __forceinline__ uint32_t abs_bits(float x) { return __float_as_uint(x) & 0x7fffffffu; }
