@@ -10,9 +10,10 @@ The default workload is B=1, H=16, T=65536, dk=dv=128, bf16, g_min=-5,
 chunk 16, S0 = 0 (synthetic inputs, seeded).  `roofline` uses the algorithmic
 bytes of one launch (q, k, v, w, beta read, o written: 1282 B per token-head at
 d = 128 in bf16, plus the fp32 final state) over the average duration of the
-call's kernels (prep and scan, which run back to back on one stream), timed
-with HIP events that the library records on the launch stream before the first
-kernel and after the last.
+call's kernels (on the fused path: the segment-map pass, the segment chaining
+and the output pass, back to back on one stream), timed with HIP events that
+the library records on the launch stream before the first kernel and after the
+last.
 `cpu_baseline` times the fp64 oracle on the host on a bounded sample of the
 same workload (all heads, the first tokens of the sequence).
 """
@@ -46,6 +47,18 @@ def source_hash() -> str:
     return h.hexdigest()[:16]
 
 
+def kernel_short_name(name):
+    """Short name of a library kernel (or of the calibration copy) in a rocprofv3 record."""
+    for key, short in (("fused_kernel<true", "fused_out"), ("fused_kernel<false", "fused_state"),
+                       ("seg_combine_kernel", "seg_combine"), ("seg_state_kernel", "seg_state"),
+                       ("seg_out_kernel", "seg_out"), ("prep_kernel", "prep"), ("vec_", "vector")):
+        if key in name:
+            return short
+    if "copyBuffer" in name or "elementwise_kernel<16" in name:
+        return "copy"
+    return None
+
+
 def _pmc_per_kernel(csv_path, counter):
     """{kernel short name: value of `counter` in the last dispatch, summed over its instances}."""
     import csv
@@ -54,9 +67,7 @@ def _pmc_per_kernel(csv_path, counter):
     for r in csv.DictReader(open(csv_path)):
         if r["Counter_Name"] != counter:
             continue
-        name = r["Kernel_Name"]
-        short = ("scan_kernel" if "scan_kernel" in name else "prep_kernel" if "prep_kernel" in name
-                 else "copy" if ("copyBuffer" in name or "elementwise_kernel<16" in name) else None)
+        short = kernel_short_name(r["Kernel_Name"])
         if short:
             per[short][int(r["Dispatch_Id"])] += float(r["Counter_Value"])
     return {k: v[max(v)] for k, v in per.items()}
@@ -64,14 +75,14 @@ def _pmc_per_kernel(csv_path, counter):
 
 def summarize_pmc(fetch_csv, write_csv, copy_fetch_csv, copy_write_csv, out_json, workload):
     """Scale FETCH_SIZE / WRITE_SIZE (KiB per dispatch) by what they read for a 1 GiB copy, and store
-    the HBM bytes per forward call (both kernels) together with the kernel source hash."""
+    the HBM bytes per forward call (every kernel of the call) together with the kernel source hash."""
     fetch = _pmc_per_kernel(fetch_csv, "FETCH_SIZE")
     write = _pmc_per_kernel(write_csv, "WRITE_SIZE")
     copy_bytes = float(1 << 30)
     f_scale = copy_bytes / (1024.0 * _pmc_per_kernel(copy_fetch_csv, "FETCH_SIZE")["copy"])
     w_scale = copy_bytes / (1024.0 * _pmc_per_kernel(copy_write_csv, "WRITE_SIZE")["copy"])
     kernels = {}
-    for k in ("prep_kernel", "scan_kernel"):
+    for k in sorted((set(fetch) | set(write)) - {"copy"}):
         kernels[k] = {"fetch_bytes": fetch.get(k, 0.0) * 1024 * f_scale, "write_bytes": write.get(k, 0.0) * 1024 * w_scale}
     total = sum(v["fetch_bytes"] + v["write_bytes"] for v in kernels.values())
     out = {"workload": workload, "source_hash": source_hash(), "fetch_scale": f_scale, "write_scale": w_scale,

@@ -73,6 +73,8 @@ def load():
     lib.kda_gate_prefix.restype = i32
     lib.kda_workspace_bytes.argtypes = [ctypes.POINTER(KdaShape), i32]
     lib.kda_workspace_bytes.restype = sz
+    lib.kda_workspace_bytes_ex.argtypes = [ctypes.POINTER(KdaShape), i32, ctypes.POINTER(KdaOpts)]
+    lib.kda_workspace_bytes_ex.restype = sz
     lib.kda_strerror.argtypes = [i32]
     lib.kda_strerror.restype = ctypes.c_char_p
     lib.kda_last_hip_error.argtypes = []
@@ -95,10 +97,10 @@ def version() -> int:
     return load().kda_version()
 
 
-def workspace_bytes(shape: KdaShape, chunk: int = 16) -> int:
-    n = load().kda_workspace_bytes(ctypes.byref(shape), int(chunk))
+def workspace_bytes(shape: KdaShape, chunk: int = 16, opts: KdaOpts | None = None) -> int:
+    n = load().kda_workspace_bytes_ex(ctypes.byref(shape), int(chunk), None if opts is None else ctypes.byref(opts))
     if n == ctypes.c_size_t(-1).value:
-        raise KdaError(KDA_ERR_SHAPE, "kda_workspace_bytes")
+        raise KdaError(KDA_ERR_SHAPE, "kda_workspace_bytes_ex")
     return n
 
 

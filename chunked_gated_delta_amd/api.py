@@ -45,9 +45,10 @@ def make_shape(B, H, T, dk, dv, dtype_code) -> KdaShape:
     return KdaShape(int(B), int(H), int(T), int(dk), int(dv), int(dtype_code), 0)
 
 
-def workspace_bytes(B, H, T, dk, dv, dtype=torch.bfloat16, chunk=16) -> int:
+def workspace_bytes(B, H, T, dk, dv, dtype=torch.bfloat16, chunk=16, path: str = "auto") -> int:
     code = _lib.DTYPE_BF16 if dtype == torch.bfloat16 else _lib.DTYPE_F32
-    return _lib.workspace_bytes(make_shape(B, H, T, dk, dv, code), chunk)
+    opts = KdaOpts(0, 0, _PATHS[path], 0, None, None)
+    return _lib.workspace_bytes(make_shape(B, H, T, dk, dv, code), chunk, opts)
 
 
 def chunk_fwd(q, k, v, w, beta, S0=None, g_min: float = -5.0, chunk: int = 16, *,
@@ -88,14 +89,14 @@ def chunk_fwd(q, k, v, w, beta, S0=None, g_min: float = -5.0, chunk: int = 16, *
     else:
         _check(S_final, "S_final", (B, H, dk, dv), torch.float32, dev)
     shape = make_shape(B, H, T, dk, dv, _dtype_code(q))
-    ws_need = 0 if path == "vector" else _lib.workspace_bytes(shape, chunk)
+    opts = KdaOpts(int(bool(disable_fallback)), int(bool(force_fallback)), _PATHS[path], int(seg_steps),
+                   events[0].handle if events else None, events[1].handle if events else None)
+    ws_need = _lib.workspace_bytes(shape, chunk, opts)
     if workspace is None and ws_need > 0:
         workspace = torch.empty(ws_need, dtype=torch.uint8, device=dev)
     st = torch.empty(4, dtype=torch.int32, device=dev) if stats else None
     if stream is None:
         stream = torch.cuda.current_stream(dev)
-    opts = KdaOpts(int(bool(disable_fallback)), int(bool(force_fallback)), _PATHS[path], int(seg_steps),
-                   events[0].handle if events else None, events[1].handle if events else None)
     with torch.cuda.device(dev):
         rc = _lib.load().kda_chunk_fwd_ex(
             _ptr(q), _ptr(k), _ptr(v), _ptr(w), _ptr(beta), _ptr(S0),

@@ -1,19 +1,17 @@
 // Fused matrix-core path of the chunked KDA forward (bf16 inputs, dk = dv = 128, bf16 MFMA on gfx950).
 //
 // The steps (32 tokens = two 16-token chunks) of every (b, h) sequence are cut into segments; one
-// workgroup of 8 wavefronts owns one segment and builds every step's operands on chip, so only the
-// inputs q, k, v, w, beta and the outputs o cross HBM.  Per segment, the steps run through a
-// software pipeline.  Interval s (two halves, each closed by a workgroup barrier) holds
-//   first half    E1(s+2)  gate, chunk-local inclusive prefix L, chunk totals Gam_c, spans, and every
-//                          operand of step s+2 that needs only its own chunk (all wavefronts)
-//                 S(s+1)   the diagonal blocks of T = (I + A)^{-1} of step s+1 (wavefronts 0, 1),
-//                          the first factor of its coupling block, P of step s+1 to bf16 (wavefront 2)
-//                 C1(s)    R = diag(beta)(V - Kbar S), U = T R and the outputs of step s
-//   second half   E2(s+2)  the operands that need the other chunk's totals, the flags, and the
-//                          per-pair diagonal blocks of flagged chunks
-//                 TL(s+2)  the causal tiles A (and P) of step s+2 on MFMA (wavefronts 0-5)
-//                 S2(s+1)  the coupling block of T and T to bf16 (wavefront 6)
-//                 C2(s)    the state update of step s
+// workgroup of 16 wavefronts owns one segment and builds every step's operands on chip, so only the
+// inputs q, k, v, w, beta and the outputs o cross HBM.  Wavefronts 0-7 (C) each carry a 16-column
+// slice of the state; wavefronts 8-15 (E) build the operands, four per chunk.  Per segment the steps
+// run through a software pipeline.  Interval s has two halves, each closed by a workgroup barrier:
+//   first half    C(s)      R = diag(beta)(V - Kbar S), U = T R, the outputs and the state update of step s
+//                 TL(s+1)   the causal tiles of step s+1 on MFMA (wavefronts 0-5): the diagonal blocks of
+//                           A go to the solver, -A_10 and P straight into their operand places
+//                 E1(s+2)   gates, chunk-local inclusive prefix L, chunk totals Gam_c, spans, beta, e^{L}
+//   second half   E2(s+2)   every operand of step s+2 built from k, q and the gate factors, the flags,
+//                           and the per-pair diagonal blocks of flagged chunks (whole workgroup)
+//                 S(s+1)    the diagonal blocks of T = (I + A)^{-1} of step s+1 (wavefront 7)
 //
 // Per step, with G the in-step prefix referenced to the step start, Kbar = k e^{G}, Qbar = q e^{G},
 // Ktil = k e^{Gam_step - G}, A = strictly-lower diag(beta) Kbar (k e^{-G})^T, P = lower-inclusive
@@ -22,7 +20,9 @@
 //   O = Qbar S + P U                   S <- diag(e^{Gam_step}) S + Ktil^T U
 // which is the chunk form of the delta rule written out from "From Numerical Stability to Load
 // Balancing ..." section 2.1 (matrix products inside a chunk, a serial state between chunks, in-chunk
-// scaling exp(G_i - G_j) for i >= j) with the UT/WY correction of the delta rule.  The bounded gate
+// scaling exp(G_i - G_j) for i >= j) with the UT/WY correction of the delta rule.  U is formed by
+// 16-row blocks, U_0 = T_00 R_0 and U_1 = T_11 (R_1 - A_10 U_0), so only the diagonal blocks of T are
+// inverted.  The bounded gate
 // (same page section 2.2; "Demystifying Trillion-Parameter MoE Models ..." Breakthrough 1 part 2)
 // keeps each 16-token chunk's span at or above -80, so the reciprocal factors e^{-L} stay below e^80.
 // Only the two diagonal 16 x 16 blocks use e^{+-L} (chunk-local); the block coupling chunk 1 to
@@ -55,8 +55,9 @@ __device__ __forceinline__ int slot16(int lane) { return (lane + (lane >> 4)) * 
 constexpr int rKb = 0;                // -beta Kbar, [mt 2][u 4] blocks: row 16mt + li, channels 32u + {4g+r, 16+4g+r}
 constexpr int rQb = rKb + 8 * kBlk;   // Qbar, same arrangement                                    (OUT only)
 constexpr int rKt = rQb + 8 * kBlk;   // Ktil^T, [t 8] blocks: channel 16t + li, tokens {4g+r, 16+4g+r}
-constexpr int rT = rKt + 8 * kBlk;    // T, [mt 2] blocks: row 16mt + li, tokens {4g+r, 16+4g+r}
-constexpr int rP = rT + 2 * kBlk;     // P, same arrangement                                       (OUT only)
+constexpr int rT = rKt + 8 * kBlk;    // T_00, T_11, -A_10: three K = 16 A operands (64 lanes x 4 bf16):
+                                      // lane (li, g) holds row li, columns 4g .. 4g+3 of the block
+constexpr int rP = rT + 2 * kBlk;     // P, [mt 2] blocks: row 16mt + li, tokens {4g+r, 16+4g+r}  (OUT only)
 constexpr int rEg = rP + 2 * kBlk;    // e^{Gam_step}: [g 4][t 8][r 4] fp32 <-> channel 16t + 4g + r
 constexpr int rBeta = rEg + 512;      // beta per token, fp32 (zero past the end of the sequence)
 constexpr int rMeta = rBeta + 128;    // StepInfo
@@ -75,7 +76,9 @@ constexpr int kOps = oKt0 + 4 * kBlk;
 constexpr int pL = 0, pK = 8192, pQ = 12288;
 static_assert(pQ + 4096 <= kOps, "per-pair inputs fit the borrowed buffer");
 
-constexpr int kRowA = 36;     // row stride (floats) of the 32 x 32 fp32 arrays: 16-byte aligned rows
+constexpr int kOpT00 = 0, kOpT11 = 512, kOpA10 = 1024;   // byte offsets of the three blocks within rT
+static_assert(kOpA10 + 512 <= 2 * kBlk, "the T operands fit their region");
+constexpr int kRowA = 20;     // row stride (floats) of the fp32 diagonal blocks: 16-byte aligned rows
 
 struct StepInfo {
   float span[2];          // chunk spans, natural-log units (+inf for a chunk with no tokens)
@@ -87,10 +90,7 @@ struct StepInfo {
 struct FusedShared {
   unsigned char rec[kRecSlots][kRec];
   unsigned char ops[2][kOps];
-  float AT[STEP][kRowA];                  // A transposed (AT[j][r] = A[r][j]) of the step being solved
-  float P[STEP][kRowA];                   // P of the step being solved
-  float T32[STEP][kRowA];                 // T in fp32 while it is assembled
-  float X[16][20];                        // A_10 T_00
+  float A[2][STEP][kRowA];                // diagonal blocks of A (rows 0-15: A_00, 16-31: A_11), by step parity
   float pwA[2][16][16], pwP[2][16][16];   // per-pair diagonal blocks [chunk][r][j]
   float gam[2][D];                        // chunk totals (log2 units) of the step in E
   float spanw[kEWaves];                   // per-E-wave minimum of the chunk totals
@@ -111,17 +111,6 @@ __device__ __forceinline__ int opaque(int x) {
 template <int CTRL, int ROW_MASK = 0xF>
 __device__ __forceinline__ float dpp(float old, float src) {
   return __int_as_float(__builtin_amdgcn_update_dpp(__float_as_int(old), __float_as_int(src), CTRL, ROW_MASK, 0xF, false));
-}
-
-// minimum over the wave, valid in lane 63
-__device__ __forceinline__ float wave_min_to_63(float m) {
-  m = fminf(m, dpp<0x111>(m, m));   // row_shr:1
-  m = fminf(m, dpp<0x112>(m, m));   // row_shr:2
-  m = fminf(m, dpp<0x114>(m, m));   // row_shr:4
-  m = fminf(m, dpp<0x118>(m, m));   // row_shr:8  -> lane 15 of each row holds the row minimum
-  m = fminf(m, dpp<0x142, 0xA>(m, m));   // row_bcast:15 into rows 1 and 3
-  m = fminf(m, dpp<0x143, 0xC>(m, m));   // row_bcast:31 into rows 2 and 3
-  return m;
 }
 
 __device__ __forceinline__ void lgkm_wait() {
@@ -159,9 +148,9 @@ struct EIn {
 };
 
 struct EKeep {                 // E's values carried from its first half to its second
-  uint32_t k[4], q[4];
-  float L0[4], L1[4];          // prefix (log2 units), for the per-pair path
-  float f0[4], f1[4];          // chunk 0: e^{Gam_0 - L}; chunk 1: e^{L}
+  uint32_t k[4], q[4];         // two bf16 channels per word, tokens j
+  float L0[4], L1[4];          // chunk-local inclusive prefix (log2 units)
+  float eL0[4], eL1[4];        // e^{L}
   float beta[4];
   float G0, G1;                // chunk totals of the two channels (log2 units)
 };
@@ -185,24 +174,37 @@ __device__ __forceinline__ int rowk_off(int rt, int u, int li, int g, int pos) {
 // offset of (channel c, token quarter h, chunk cc) in the Ktil^T blocks
 __device__ __forceinline__ int kt_off(int c, int h, int cc) { return (c >> 4) * kBlk + ((c & 15) + 17 * h) * 16 + cc * 8; }
 
-template <bool OUT, bool UNB>
+// Minimum of the chunk totals over the wave, valid in lane 63.  Gates are never positive, so on the
+// float bits an unsigned maximum is the minimum; the four lanes of a quarter group hold the same
+// totals, so the reduction runs over the quarter groups only.
+__device__ __forceinline__ float wave_min_totals(float g0, float g1) {
+  uint32_t m = max(__float_as_uint(g0), __float_as_uint(g1));
+  m = max(m, (uint32_t)__builtin_amdgcn_update_dpp((int)m, (int)m, 0x114, 0xF, 0xF, false));   // row_shr:4
+  m = max(m, (uint32_t)__builtin_amdgcn_update_dpp((int)m, (int)m, 0x118, 0xF, 0xF, false));   // row_shr:8
+  m = max(m, (uint32_t)__builtin_amdgcn_update_dpp((int)m, (int)m, 0x142, 0xA, 0xF, false));   // row_bcast:15
+  m = max(m, (uint32_t)__builtin_amdgcn_update_dpp((int)m, (int)m, 0x143, 0xC, 0xF, false));   // row_bcast:31
+  return __uint_as_float(m);
+}
+
+// First half of E for chunk CC of the step: gates, the in-chunk prefix L, the chunk totals, the span
+// of the wave's channels, beta, and e^{L}.
+template <bool UNB, int CC>
 __device__ __forceinline__ void e_first(FusedShared& sm, const EIn& in, EKeep& kp, const Params& p, int64_t step,
-                                        unsigned char* rec, unsigned char* ops, int w, int l) {
-  const int cc = w >> 2, pr = 16 * (w & 3) + (l >> 2), h = l & 3;
-  const int u = w & 3, g = ((l >> 2) & 7) >> 1, pos = (l >> 5) * 4 + 2 * ((l >> 2) & 1);
+                                        unsigned char* rec, int w, int l) {
+  const int pr = 16 * (w & 3) + (l >> 2), h = l & 3;
   const int c0 = 2 * pr, c1 = 2 * pr + 1;
-  const int64_t tb = step * STEP + 16 * cc + 4 * h;
+  const int64_t rem = p.T - (step * STEP + 16 * CC + 4 * h);
+  const int nv = rem <= 0 ? 0 : (rem >= 4 ? 4 : (int)rem);   // this lane's tokens inside the sequence
   const float gml2 = p.g_min * kLog2e;
   float a0 = 0.f, a1 = 0.f;
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
-    const bool ok = tb + j < p.T;
     kp.k[j] = in.k[j];
     kp.q[j] = in.q[j];
     kp.beta[j] = __uint_as_float(in.b[j] << 16);
     const float g0 = gate2<UNB>(lo_bf16(in.w[j]), gml2), g1 = gate2<UNB>(hi_bf16(in.w[j]), gml2);
-    a0 += ok ? g0 : 0.f;
-    a1 += ok ? g1 : 0.f;
+    a0 += j < nv ? g0 : 0.f;
+    a1 += j < nv ? g1 : 0.f;
     kp.L0[j] = a0;
     kp.L1[j] = a1;
   }
@@ -218,49 +220,19 @@ __device__ __forceinline__ void e_first(FusedShared& sm, const EIn& in, EKeep& k
   kp.G0 = dpp<0xFF>(0.f, s0);                          // quad_perm [3,3,3,3]: the chunk totals
   kp.G1 = dpp<0xFF>(0.f, s1);
 #pragma unroll
-  for (int j = 0; j < 4; ++j) { kp.L0[j] += x0; kp.L1[j] += x1; }
-  if (h == 0) { sm.gam[cc][c0] = kp.G0; sm.gam[cc][c1] = kp.G1; }
-  const float m = wave_min_to_63(fminf(kp.G0, kp.G1));
+  for (int j = 0; j < 4; ++j) {
+    kp.L0[j] += x0;
+    kp.L1[j] += x1;
+    kp.eL0[j] = __builtin_amdgcn_exp2f(kp.L0[j]);
+    kp.eL1[j] = __builtin_amdgcn_exp2f(kp.L1[j]);
+  }
+  if (h == 0) { sm.gam[CC][c0] = kp.G0; sm.gam[CC][c1] = kp.G1; }
+  const float m = wave_min_totals(kp.G0, kp.G1);
   if (l == 63) sm.spanw[w] = m;
   if ((w & 3) == 0 && (l >> 2) == 0) {
     float* bt = reinterpret_cast<float*>(rec + rBeta);
 #pragma unroll
-    for (int j = 0; j < 4; ++j) bt[16 * cc + 4 * h + j] = kp.beta[j];
-  }
-  float ktv0[4], ktv1[4];      // Ktil of this thread's channels in chunk 1
-  // e^{-L} = e^{Gam - L} e^{-Gam}: finite wherever the dense tile is used (a chunk whose e^{-Gam}
-  // overflows has a span below -80 and takes the per-pair blocks instead)
-  const float iG0 = __builtin_amdgcn_exp2f(-kp.G0), iG1 = __builtin_amdgcn_exp2f(-kp.G1);
-#pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    const int li = 4 * h + j;
-    const float k0 = lo_bf16(kp.k[j]), k1 = hi_bf16(kp.k[j]);
-    const float e0 = __builtin_amdgcn_exp2f(kp.L0[j]), e1 = __builtin_amdgcn_exp2f(kp.L1[j]);
-    const float g0 = __builtin_amdgcn_exp2f(kp.G0 - kp.L0[j]), g1 = __builtin_amdgcn_exp2f(kp.G1 - kp.L1[j]);  // <= 1
-    *reinterpret_cast<uint32_t*>(ops + oKh + rowk_off(cc, u, li, g, pos)) = pk_bf16(k0 * g0 * iG0, k1 * g1 * iG1);
-    if (cc == 1) {
-      kp.f0[j] = e0; kp.f1[j] = e1;
-      *reinterpret_cast<uint32_t*>(ops + oKb1 + rowk_off(0, u, li, g, pos)) = pk_bf16(k0 * e0, k1 * e1);
-      if (OUT)
-        *reinterpret_cast<uint32_t*>(ops + oQb1 + rowk_off(0, u, li, g, pos)) =
-            pk_bf16(lo_bf16(kp.q[j]) * e0, hi_bf16(kp.q[j]) * e1);
-      ktv0[j] = k0 * g0;
-      ktv1[j] = k1 * g1;
-    } else {
-      kp.f0[j] = g0; kp.f1[j] = g1;
-      const float nb = -kp.beta[j];
-      *reinterpret_cast<uint32_t*>(rec + rKb + rowk_off(0, u, li, g, pos)) = pk_bf16(nb * k0 * e0, nb * k1 * e1);
-      if (OUT)
-        *reinterpret_cast<uint32_t*>(rec + rQb + rowk_off(0, u, li, g, pos)) =
-            pk_bf16(lo_bf16(kp.q[j]) * e0, hi_bf16(kp.q[j]) * e1);
-      *reinterpret_cast<uint32_t*>(ops + oKt0 + rowk_off(0, u, li, g, pos)) = pk_bf16(k0 * g0, k1 * g1);
-    }
-  }
-  if (cc == 1) {   // channel c -> block c >> 4, lane (c & 15) + 16 h, positions 4 .. 7
-    *reinterpret_cast<uint2*>(rec + rKt + kt_off(c0, h, 1)) =
-        uint2{pk_bf16(ktv0[0], ktv0[1]), pk_bf16(ktv0[2], ktv0[3])};
-    *reinterpret_cast<uint2*>(rec + rKt + kt_off(c1, h, 1)) =
-        uint2{pk_bf16(ktv1[0], ktv1[1]), pk_bf16(ktv1[2], ktv1[3])};
+    for (int j = 0; j < 4; ++j) bt[16 * CC + 4 * h + j] = kp.beta[j];
   }
 }
 
@@ -270,58 +242,76 @@ __device__ __forceinline__ void pair_of(int pr, int& r, int& j) {   // pr -> (r,
   j = pr - r * (r + 1) / 2;
 }
 
-template <bool OUT>
+// Second half of E for chunk CC: every operand of the step built from k, q and the gate factors.
+//   chunk 0: k e^{-L} (tiles), -beta k e^{L} and q e^{L} (step-referenced = chunk-local), k e^{Gam_0 - L}
+//            (tiles), Ktil = k e^{Gam_0 - L} e^{Gam_1}, and e^{Gam_step}
+//   chunk 1: k e^{-L} (tiles), k e^{L} and q e^{L} (tiles), their step-referenced forms times e^{Gam_0}
+//            (with -beta for k), Ktil = k e^{Gam_1 - L}
+// e^{-L} = e^{Gam - L} e^{-Gam}: finite wherever the dense tile is used (a chunk whose e^{-Gam}
+// overflows has a span below -80 and takes the per-pair blocks instead).
+template <bool OUT, int CC>
 __device__ __forceinline__ void e_second(FusedShared& sm, const EKeep& kp, const Params& p, int64_t step,
-                                         unsigned char* rec, int w, int l) {
-  const int tid = w * 64 + l;
-  const int cc = w >> 2, pr = 16 * (w & 3) + (l >> 2), h = l & 3;
+                                         unsigned char* rec, unsigned char* ops, int w, int l) {
+  const int pr = 16 * (w & 3) + (l >> 2), h = l & 3;
   const int u = w & 3, g = ((l >> 2) & 7) >> 1, pos = (l >> 5) * 4 + 2 * ((l >> 2) & 1);
   const int c0 = 2 * pr, c1 = 2 * pr + 1;
-  if (cc == 1) {   // step-referenced operands of chunk 1: G = Gam_0 + L
-    const float x0 = __builtin_amdgcn_exp2f(sm.gam[0][c0]), x1 = __builtin_amdgcn_exp2f(sm.gam[0][c1]);
+  const float iG0 = __builtin_amdgcn_exp2f(-kp.G0), iG1 = __builtin_amdgcn_exp2f(-kp.G1);
+  // e^{Gam} of the other chunk, per channel
+  const float y0 = __builtin_amdgcn_exp2f(sm.gam[1 - CC][c0]), y1 = __builtin_amdgcn_exp2f(sm.gam[1 - CC][c1]);
+  float ktv0[4], ktv1[4];
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int li = 4 * h + j;
-      const float k0 = lo_bf16(kp.k[j]), k1 = hi_bf16(kp.k[j]);
-      const float nb = -kp.beta[j];
-      *reinterpret_cast<uint32_t*>(rec + rKb + rowk_off(1, u, li, g, pos)) =
-          pk_bf16(nb * k0 * kp.f0[j] * x0, nb * k1 * kp.f1[j] * x1);
+  for (int j = 0; j < 4; ++j) {
+    const int li = 4 * h + j;
+    const float k0 = lo_bf16(kp.k[j]), k1 = hi_bf16(kp.k[j]);
+    const float kg0 = k0 * __builtin_amdgcn_exp2f(kp.G0 - kp.L0[j]), kg1 = k1 * __builtin_amdgcn_exp2f(kp.G1 - kp.L1[j]);
+    const float ke0 = k0 * kp.eL0[j], ke1 = k1 * kp.eL1[j];
+    const float nb = -kp.beta[j];
+    *reinterpret_cast<uint32_t*>(ops + oKh + rowk_off(CC, u, li, g, pos)) = pk_bf16(kg0 * iG0, kg1 * iG1);
+    if (CC == 0) {
+      *reinterpret_cast<uint32_t*>(rec + rKb + rowk_off(0, u, li, g, pos)) = pk_bf16(nb * ke0, nb * ke1);
       if (OUT)
-        *reinterpret_cast<uint32_t*>(rec + rQb + rowk_off(1, u, li, g, pos)) =
-            pk_bf16(lo_bf16(kp.q[j]) * kp.f0[j] * x0, hi_bf16(kp.q[j]) * kp.f1[j] * x1);
-    }
-  } else {         // chunk 0: Ktil = k e^{Gam_0 - L} e^{Gam_1}; e^{Gam_step}
-    const float G10 = sm.gam[1][c0], G11 = sm.gam[1][c1];
-    const float y0 = __builtin_amdgcn_exp2f(G10), y1 = __builtin_amdgcn_exp2f(G11);
-    float a[4], b[4];
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      a[j] = lo_bf16(kp.k[j]) * kp.f0[j] * y0;
-      b[j] = hi_bf16(kp.k[j]) * kp.f1[j] * y1;
-    }
-    *reinterpret_cast<uint2*>(rec + rKt + kt_off(c0, h, 0)) = uint2{pk_bf16(a[0], a[1]), pk_bf16(a[2], a[3])};
-    *reinterpret_cast<uint2*>(rec + rKt + kt_off(c1, h, 0)) = uint2{pk_bf16(b[0], b[1]), pk_bf16(b[2], b[3])};
-    if (h == 0) {
-      float* eg = reinterpret_cast<float*>(rec + rEg);
-      eg[((c0 >> 2) & 3) * 32 + (c0 >> 4) * 4 + (c0 & 3)] = __builtin_amdgcn_exp2f(kp.G0 + G10);
-      eg[((c1 >> 2) & 3) * 32 + (c1 >> 4) * 4 + (c1 & 3)] = __builtin_amdgcn_exp2f(kp.G1 + G11);
+        *reinterpret_cast<uint32_t*>(rec + rQb + rowk_off(0, u, li, g, pos)) =
+            pk_bf16(lo_bf16(kp.q[j]) * kp.eL0[j], hi_bf16(kp.q[j]) * kp.eL1[j]);
+      *reinterpret_cast<uint32_t*>(ops + oKt0 + rowk_off(0, u, li, g, pos)) = pk_bf16(kg0, kg1);
+      ktv0[j] = kg0 * y0;
+      ktv1[j] = kg1 * y1;
+    } else {
+      *reinterpret_cast<uint32_t*>(ops + oKb1 + rowk_off(0, u, li, g, pos)) = pk_bf16(ke0, ke1);
+      *reinterpret_cast<uint32_t*>(rec + rKb + rowk_off(1, u, li, g, pos)) = pk_bf16(nb * ke0 * y0, nb * ke1 * y1);
+      if (OUT) {
+        const float qe0 = lo_bf16(kp.q[j]) * kp.eL0[j], qe1 = hi_bf16(kp.q[j]) * kp.eL1[j];
+        *reinterpret_cast<uint32_t*>(ops + oQb1 + rowk_off(0, u, li, g, pos)) = pk_bf16(qe0, qe1);
+        *reinterpret_cast<uint32_t*>(rec + rQb + rowk_off(1, u, li, g, pos)) = pk_bf16(qe0 * y0, qe1 * y1);
+      }
+      ktv0[j] = kg0;
+      ktv1[j] = kg1;
     }
   }
-  // spans and flags: the step's information record
-  const int64_t t0 = step * STEP;
-  if (tid == 0) {
-    const bool valid0 = t0 < p.T, valid1 = t0 + 16 < p.T;
-    const float span0 = fminf(fminf(sm.spanw[0], sm.spanw[1]), fminf(sm.spanw[2], sm.spanw[3])) * kLn2;
-    const float span1 = fminf(fminf(sm.spanw[4], sm.spanw[5]), fminf(sm.spanw[6], sm.spanw[7])) * kLn2;
-    const bool flag0 = valid0 && span0 < kSpanLimit, flag1 = valid1 && span1 < kSpanLimit;
-    StepInfo si;
-    si.span[0] = valid0 ? span0 : __int_as_float(0x7f800000);
-    si.span[1] = valid1 ? span1 : __int_as_float(0x7f800000);
-    si.n_valid = (valid0 ? 1u : 0u) + (valid1 ? 1u : 0u);
-    si.n_flagged = (flag0 ? 1u : 0u) + (flag1 ? 1u : 0u);
-    si.pairwise = (p.force_fallback || (flag0 && !p.disable_fallback) ? 1u : 0u) |
-                  (p.force_fallback || (flag1 && !p.disable_fallback) ? 2u : 0u);
-    *reinterpret_cast<StepInfo*>(rec + rMeta) = si;
+  // Ktil^T: channel c -> block c >> 4, lane (c & 15) + 16 h, positions 4 CC .. 4 CC + 3
+  *reinterpret_cast<uint2*>(rec + rKt + kt_off(c0, h, CC)) = uint2{pk_bf16(ktv0[0], ktv0[1]), pk_bf16(ktv0[2], ktv0[3])};
+  *reinterpret_cast<uint2*>(rec + rKt + kt_off(c1, h, CC)) = uint2{pk_bf16(ktv1[0], ktv1[1]), pk_bf16(ktv1[2], ktv1[3])};
+  if (CC == 0) {
+    if (h == 0) {
+      float* eg = reinterpret_cast<float*>(rec + rEg);
+      eg[((c0 >> 2) & 3) * 32 + (c0 >> 4) * 4 + (c0 & 3)] = __builtin_amdgcn_exp2f(kp.G0 + sm.gam[1][c0]);
+      eg[((c1 >> 2) & 3) * 32 + (c1 >> 4) * 4 + (c1 & 3)] = __builtin_amdgcn_exp2f(kp.G1 + sm.gam[1][c1]);
+    }
+    // spans and flags: the step's information record
+    if (w == 0 && l == 0) {
+      const int64_t t0 = step * STEP;
+      const bool valid0 = t0 < p.T, valid1 = t0 + 16 < p.T;
+      const float span0 = fminf(fminf(sm.spanw[0], sm.spanw[1]), fminf(sm.spanw[2], sm.spanw[3])) * kLn2;
+      const float span1 = fminf(fminf(sm.spanw[4], sm.spanw[5]), fminf(sm.spanw[6], sm.spanw[7])) * kLn2;
+      const bool flag0 = valid0 && span0 < kSpanLimit, flag1 = valid1 && span1 < kSpanLimit;
+      StepInfo si;
+      si.span[0] = valid0 ? span0 : __int_as_float(0x7f800000);
+      si.span[1] = valid1 ? span1 : __int_as_float(0x7f800000);
+      si.n_valid = (valid0 ? 1u : 0u) + (valid1 ? 1u : 0u);
+      si.n_flagged = (flag0 ? 1u : 0u) + (flag1 ? 1u : 0u);
+      si.pairwise = (p.force_fallback || (flag0 && !p.disable_fallback) ? 1u : 0u) |
+                    (p.force_fallback || (flag1 && !p.disable_fallback) ? 2u : 0u);
+      *reinterpret_cast<StepInfo*>(rec + rMeta) = si;
+    }
   }
 }
 
@@ -391,9 +381,12 @@ __device__ __forceinline__ void pairwise_blocks(FusedShared& sm, const EKeep* kp
 static_assert(136 * 4 <= kThreads, "one per-pair item per thread");
 
 // ---------------------------------------------------------------- stage TL: causal tiles on MFMA
+// Each tile is formed transposed (operands swapped), so that lane (li, g) holds row li, columns
+// 4g .. 4g+3: the diagonal blocks of A go to the solver as fp32 rows, the coupling block -A_10 and
+// the blocks of P go straight into their bf16 operand places.
 template <bool OUT>
-__device__ __forceinline__ void tiles(FusedShared& sm, const unsigned char* rec, const unsigned char* ops, uint32_t pwmask,
-                                      int w, int lane) {
+__device__ __forceinline__ void tiles(FusedShared& sm, unsigned char* rec, const unsigned char* ops, uint32_t pwmask,
+                                      int par, int w, int lane) {
   const int li = lane & 15, lg = lane >> 4;
   if (w >= (OUT ? 6 : 3)) return;
   const float* bt = reinterpret_cast<const float*>(rec + rBeta);
@@ -408,96 +401,64 @@ __device__ __forceinline__ void tiles(FusedShared& sm, const unsigned char* rec,
   }
   floatx4 acc = {0, 0, 0, 0};
 #pragma unroll
-  for (int u = 0; u < 4; ++u) acc = mfma(ld8(a + u * kBlk + slot16(lane)), ld8(b + u * kBlk + slot16(lane)), acc);
+  for (int u = 0; u < 4; ++u) acc = mfma(ld8(b + u * kBlk + slot16(lane)), ld8(a + u * kBlk + slot16(lane)), acc);
   const bool pw0 = pwmask & 1u, pw1 = pwmask & 2u;
+  floatx4 x;
 #pragma unroll
   for (int r = 0; r < 4; ++r) {
-    const int R = 4 * lg + r;   // D[R][li]: row R, column li of the block
+    const int c = 4 * lg + r;   // element (li, c) of the block
     switch (w) {
-      case 0: sm.AT[li][R] = li < R ? (pw0 ? sm.pwA[0][R][li] : -acc[r]) : 0.f; break;
-      case 1: sm.AT[16 + li][16 + R] = li < R ? (pw1 ? sm.pwA[1][R][li] : bt[16 + R] * acc[r]) : 0.f; break;
-      case 2: sm.AT[li][16 + R] = bt[16 + R] * acc[r]; sm.AT[16 + li][R] = 0.f; break;
-      case 3: sm.P[R][li] = li <= R ? (pw0 ? sm.pwP[0][R][li] : acc[r]) : 0.f; break;
-      case 4: sm.P[16 + R][16 + li] = li <= R ? (pw1 ? sm.pwP[1][R][li] : acc[r]) : 0.f; break;
-      default: sm.P[16 + R][li] = acc[r]; sm.P[R][16 + li] = 0.f; break;
+      case 0: x[r] = c < li ? (pw0 ? sm.pwA[0][li][c] : -acc[r]) : 0.f; break;
+      case 1: x[r] = c < li ? (pw1 ? sm.pwA[1][li][c] : bt[16 + li] * acc[r]) : 0.f; break;
+      case 2: x[r] = -bt[16 + li] * acc[r]; break;
+      case 3: x[r] = c <= li ? (pw0 ? sm.pwP[0][li][c] : acc[r]) : 0.f; break;
+      case 4: x[r] = c <= li ? (pw1 ? sm.pwP[1][li][c] : acc[r]) : 0.f; break;
+      default: x[r] = acc[r]; break;
     }
+  }
+  switch (w) {
+    case 0: *reinterpret_cast<floatx4*>(&sm.A[par][li][4 * lg]) = x; break;
+    case 1: *reinterpret_cast<floatx4*>(&sm.A[par][16 + li][4 * lg]) = x; break;
+    case 2: *reinterpret_cast<bf16x4*>(rec + rT + kOpA10 + lane * 8) = pack4(x); break;
+    case 3: *reinterpret_cast<bf16x8*>(rec + rP + slot16(lane)) = pack2(x, floatx4{0, 0, 0, 0}); break;   // P_01 = 0
+    case 4: *reinterpret_cast<bf16x4*>(rec + rP + kBlk + slot16(lane) + 8) = pack4(x); break;
+    default: *reinterpret_cast<bf16x4*>(rec + rP + kBlk + slot16(lane)) = pack4(x); break;
   }
 }
 
 // ---------------------------------------------------------------- stage S: T = (I + A)^{-1}
-// Diagonal block b (wavefront b): forward substitution, right-looking, one column per lane
-// (j = lane & 15; the four lane quarters repeat it so that each can then form its rows of A_10 T_00).
-template <int B>
-__device__ __forceinline__ void solve_diag(FusedShared& sm, int lane_in) {
+// Both diagonal blocks by one wavefront: lanes 0-31 block 0, lanes 32-63 block 1, lane li of each
+// half owning row li of T_bb.  Row t of T satisfies t (I + A) = e_li, so its entries follow from the
+// last one backwards: once t_m is final, t_k -= t_m A[m][k] for every k < m.  The coupling block is
+// not formed: the chain applies it as U_1 = T_11 (R_1 - A_10 U_0).
+__device__ __forceinline__ void solve(FusedShared& sm, unsigned char* rec, int par, int lane_in) {
   const int lane = opaque(lane_in);
-  const int j = lane & 15, rq = lane >> 4;
-  float col[16];
+  const int li = lane & 15, hb = lane >> 5, q = (lane >> 4) & 1;
+  const float* Ab = &sm.A[par][16 * hb][0];
+  float t[16];
 #pragma unroll
-  for (int r = 0; r < 16; ++r) col[r] = (r == j) ? 1.f : 0.f;
+  for (int k = 0; k < 16; ++k) t[k] = (k == li) ? 1.f : 0.f;
 #pragma unroll
-  for (int i = 0; i < 15; ++i) {   // column i of A is row i of AT
-    const float xi = col[i];
+  for (int m = 15; m >= 1; --m) {
+    const float x = t[m];
 #pragma unroll
-    for (int q = (i + 1) >> 2; q < 4; ++q) {
-      const floatx4 a = *reinterpret_cast<const floatx4*>(&sm.AT[16 * B + i][16 * B + 4 * q]);
+    for (int q4 = 0; 4 * q4 < m; ++q4) {
+      const floatx4 a = *reinterpret_cast<const floatx4*>(Ab + m * kRowA + 4 * q4);
 #pragma unroll
       for (int rr = 0; rr < 4; ++rr)
-        if (4 * q + rr > i) col[4 * q + rr] -= a[rr] * xi;
+        if (4 * q4 + rr < m) t[4 * q4 + rr] -= a[rr] * x;
     }
   }
-  if (rq == 0) {
+  // lane (li, 2q + h) of the operand holds row li, columns 8q + 4h .. 8q + 4h + 3
+  floatx4 lo, hi;
 #pragma unroll
-    for (int r = 0; r < 16; ++r) sm.T32[16 * B + r][16 * B + j] = col[r];
+  for (int r = 0; r < 4; ++r) {
+    lo[r] = q ? t[8 + r] : t[r];
+    hi[r] = q ? t[12 + r] : t[4 + r];
   }
-  if (B == 0) {   // X = A_10 T_00: lane (j, rq) forms rows 4rq .. 4rq+3 of column j
-    // AT[n][16 + 4rq .. 16 + 4rq + 3] holds A_10[4rq + q][n]
-    floatx4 x = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int n = 0; n < 16; ++n) {
-      const floatx4 a = *reinterpret_cast<const floatx4*>(&sm.AT[n][16 + 4 * rq]);
-#pragma unroll
-      for (int q = 0; q < 4; ++q) x[q] += a[q] * col[n];
-    }
-#pragma unroll
-    for (int q = 0; q < 4; ++q) sm.X[4 * rq + q][j] = x[q];
-  }
-}
-
-// Coupling block T_10 = -T_11 X and T to bf16 in per-lane operand order (one wavefront)
-__device__ __forceinline__ void solve_finish(FusedShared& sm, unsigned char* rec, int lane_in) {
-  const int lane = opaque(lane_in);
-  const int j = lane & 15, rq = lane >> 4, li = lane & 15, lg = lane >> 4;
-  float y[4];
-#pragma unroll
-  for (int q = 0; q < 4; ++q) {
-    const int r = 4 * rq + q;
-    float acc = 0.f;
-#pragma unroll
-    for (int m4 = 0; m4 < 4; ++m4) {
-      const floatx4 t = *reinterpret_cast<const floatx4*>(&sm.T32[16 + r][16 + 4 * m4]);
-      acc += t[0] * sm.X[4 * m4][j] + t[1] * sm.X[4 * m4 + 1][j] + t[2] * sm.X[4 * m4 + 2][j] + t[3] * sm.X[4 * m4 + 3][j];
-    }
-    y[q] = acc;
-  }
-#pragma unroll
-  for (int q = 0; q < 4; ++q) sm.T32[16 + 4 * rq + q][j] = -y[q];
-  lgkm_wait();
-#pragma unroll
-  for (int mt = 0; mt < 2; ++mt) {
-    const floatx4 a = *reinterpret_cast<const floatx4*>(&sm.T32[16 * mt + li][4 * lg]);
-    const floatx4 b = mt == 0 ? floatx4{0, 0, 0, 0} : *reinterpret_cast<const floatx4*>(&sm.T32[16 * mt + li][16 + 4 * lg]);
-    *reinterpret_cast<bf16x8*>(rec + rT + mt * kBlk + slot16(lane)) = pack2(a, b);
-  }
-}
-
-__device__ __forceinline__ void pack_p(const FusedShared& sm, unsigned char* rec, int lane) {
-  const int li = lane & 15, lg = lane >> 4;
-#pragma unroll
-  for (int mt = 0; mt < 2; ++mt) {
-    const floatx4 a = *reinterpret_cast<const floatx4*>(&sm.P[16 * mt + li][4 * lg]);
-    const floatx4 b = *reinterpret_cast<const floatx4*>(&sm.P[16 * mt + li][16 + 4 * lg]);
-    *reinterpret_cast<bf16x8*>(rec + rP + mt * kBlk + slot16(lane)) = pack2(a, b);
-  }
+  unsigned char* dst = rec + rT + (hb ? kOpT11 : kOpT00);
+  *reinterpret_cast<bf16x4*>(dst + (li + 32 * q) * 8) = pack4(lo);
+  *reinterpret_cast<bf16x4*>(dst + (li + 32 * q + 16) * 8) = pack4(hi);
 }
 
 // ---------------------------------------------------------------- stage C helpers
@@ -525,6 +486,37 @@ __device__ __forceinline__ void beta_v(floatx4 (&bv)[2], const uint32_t (&vin)[8
 __device__ __forceinline__ int rows_left(int64_t T, int64_t step) {
   const int64_t rem = T - step * STEP;
   return rem < STEP ? (int)rem : STEP;
+}
+
+// E wavefronts of chunk CC.  Interval s: first half E1(s+2), second half E2(s+2) and, for a flagged
+// chunk, the per-pair blocks of step s+2.
+template <bool OUT, bool UNB, int CC>
+__device__ __forceinline__ void e_loop(FusedShared& sm, const Params& p, const Views& vw, int64_t s0, int64_t ns, int we,
+                                       int lane, int tid) {
+  const int e_voff = ((16 * CC + 4 * (lane & 3)) * D + 2 * (16 * (we & 3) + (lane >> 2))) * 2;
+  const int e_boff = (16 * CC + 4 * (lane & 3)) * 2;
+  EIn ein;
+  EKeep ekeep;
+  e_load<OUT>(ein, vw, s0, e_voff, e_boff);
+#pragma unroll 1
+  for (int64_t it = -2; it < ns; ++it) {
+    const bool doE = it + 2 < ns;
+    unsigned char* recE = sm.rec[(it + 5) % kRecSlots];   // step it + 2
+    unsigned char* opsE = sm.ops[(it + 2) & 1];           // step it + 2
+    unsigned char* opsF = sm.ops[(it + 3) & 1];           // step it + 1 (free once its tiles are formed)
+    block_barrier();
+    const int ln = opaque(lane);   // lane-derived offsets are recomputed in the loop rather than held
+    if (doE) e_first<UNB, CC>(sm, ein, ekeep, p, s0 + it + 2, recE, we, ln);
+    // prefetches are issued on every path (clamped to the segment's last step) so that the memory
+    // counter waits before their uses stay exact
+    e_load<OUT>(ein, vw, s0 + (it + 3 < ns ? it + 3 : ns - 1), e_voff, e_boff);
+    block_barrier();
+    if (doE) {
+      e_second<OUT, CC>(sm, ekeep, p, s0 + it + 2, recE, opsE, we, ln);
+      const uint32_t pwmask = pairwise_mask(sm, p, s0 + it + 2);
+      if (pwmask) pairwise_blocks<OUT, true>(sm, &ekeep, recE, opsF, pwmask, we, ln, tid);
+    }
+  }
 }
 
 // ---------------------------------------------------------------- the kernel
@@ -558,41 +550,13 @@ __global__ __launch_bounds__(kThreads) void fused_kernel(Params p, int64_t n_ste
     vw.v = view((const uint16_t*)p.v + bh * T * D, nb);
     vw.beta = view((const uint16_t*)p.beta + bh * T, T * 2);
   }
-  const int e_voff = ((16 * (we >> 2) + 4 * (lane & 3)) * D + 2 * (16 * (we & 3) + (lane >> 2))) * 2;
-  const int e_boff = (16 * (we >> 2) + 4 * (lane & 3)) * 2;
   const int v_voff = ((4 * lg) * D + col) * 2;
 
   // The two kinds of wavefront run separate copies of the step loop (same trip count, same barriers in
   // the same order), so that each copy holds only its own kind's values in registers.
   if (is_e) {
-    EIn ein;
-    EKeep ekeep;
-    e_load<OUT>(ein, vw, s0, e_voff, e_boff);
-#pragma unroll 1
-    for (int64_t it = -2; it < ns; ++it) {
-      const bool doE = it + 2 < ns, doS = it + 1 >= 0 && it + 1 < ns;
-      unsigned char* recS = sm.rec[(it + 4) % kRecSlots];   // step it + 1
-      unsigned char* recE = sm.rec[(it + 5) % kRecSlots];   // step it + 2
-      unsigned char* opsE = sm.ops[(it + 2) & 1];           // step it + 2
-      unsigned char* opsF = sm.ops[(it + 3) & 1];           // step it + 1 (free: its tiles were formed last interval)
-      block_barrier();
-      const int ln = opaque(lane);   // lane-derived offsets are recomputed in the loop rather than held
-      if (doE) e_first<OUT, UNB>(sm, ein, ekeep, p, s0 + it + 2, recE, opsE, we, ln);
-      // prefetches are issued on every path (clamped to the segment's last step) so that the memory
-      // counter waits before their uses stay exact
-      if (doS) {
-        if (we == 0) solve_diag<0>(sm, ln);
-        else if (we == 1) solve_diag<1>(sm, ln);
-        else if (OUT && we == 2) pack_p(sm, recS, ln);
-      }
-      e_load<OUT>(ein, vw, s0 + (it + 3 < ns ? it + 3 : ns - 1), e_voff, e_boff);
-      block_barrier();
-      if (doE) {
-        e_second<OUT>(sm, ekeep, p, s0 + it + 2, recE, we, ln);
-        const uint32_t pwmask = pairwise_mask(sm, p, s0 + it + 2);
-        if (pwmask) pairwise_blocks<OUT, true>(sm, &ekeep, recE, opsF, pwmask, we, ln, tid);
-      }
-    }
+    if (we < 4) e_loop<OUT, UNB, 0>(sm, p, vw, s0, ns, we, lane, tid);
+    else e_loop<OUT, UNB, 1>(sm, p, vw, s0, ns, we, lane, tid);
     return;
   }
 
@@ -630,7 +594,6 @@ __global__ __launch_bounds__(kThreads) void fused_kernel(Params p, int64_t n_ste
     unsigned char* recC = sm.rec[(it + 3) % kRecSlots];   // step it       ((it + 3) keeps the index non-negative)
     unsigned char* recS = sm.rec[(it + 4) % kRecSlots];   // step it + 1
     unsigned char* recE = sm.rec[(it + 5) % kRecSlots];   // step it + 2
-    unsigned char* opsE = sm.ops[(it + 2) & 1];           // step it + 2
     unsigned char* opsF = sm.ops[(it + 3) & 1];           // step it + 1
     block_barrier();
     const int ln = opaque(lane);
@@ -649,21 +612,21 @@ __global__ __launch_bounds__(kThreads) void fused_kernel(Params p, int64_t n_ste
       for (int u = 0; u < 4; ++u)
 #pragma unroll
         for (int mt = 0; mt < 2; ++mt) R[mt] = mfma(ld8(recC + rKb + (mt * 4 + u) * kBlk + sl), sb[u], R[mt]);
-      const bf16x8 rb = pack2(R[0], R[1]);
-      floatx4 U[2];
-#pragma unroll
-      for (int mt = 0; mt < 2; ++mt) U[mt] = mfma(ld8(recC + rT + mt * kBlk + sl), rb, zero);
-      const bf16x8 ub = pack2(U[0], U[1]);
+      // U = T R blockwise: U_0 = T_00 R_0, U_1 = T_11 (R_1 - A_10 U_0)
+      const floatx4 U0 = mfma16(ld4(recC + rT + kOpT00 + ln * 8), pack4(R[0]), zero);
+      const floatx4 R1 = mfma16(ld4(recC + rT + kOpA10 + ln * 8), pack4(U0), R[1]);
+      const floatx4 U1 = mfma16(ld4(recC + rT + kOpT11 + ln * 8), pack4(R1), zero);
+      const bf16x8 ub = pack2(U0, U1);
       if (OUT) {
         const int64_t st = s0 + it;
         const int nrows = rows_left(T, st);
-        floatx4 O[2];
-#pragma unroll
-        for (int mt = 0; mt < 2; ++mt) O[mt] = mfma(ub, ld8(recC + rP + mt * kBlk + sl), zero);
+        floatx4 O[2] = {zero, zero};
 #pragma unroll
         for (int u = 0; u < 4; ++u)
 #pragma unroll
           for (int mt = 0; mt < 2; ++mt) O[mt] = mfma(sb[u], ld8(recC + rQb + (mt * 4 + u) * kBlk + sl), O[mt]);
+#pragma unroll
+        for (int mt = 0; mt < 2; ++mt) O[mt] = mfma(ub, ld8(recC + rP + mt * kBlk + sl), O[mt]);
         uint16_t* os = o + st * STEP * D;
         uint32_t mx = 0;
 #pragma unroll
@@ -707,11 +670,11 @@ __global__ __launch_bounds__(kThreads) void fused_kernel(Params p, int64_t n_ste
         for (int u = 0; u < 4; ++u)
 #pragma unroll
           for (int mt = 0; mt < 2; ++mt) RM[mt] = mfma(ld8(recC + rKb + (mt * 4 + u) * kBlk + sl), mb[u], RM[mt]);
-        const bf16x8 rbm = pack2(RM[0], RM[1]);
-        floatx4 UM[2];
-#pragma unroll
-        for (int mt = 0; mt < 2; ++mt) UM[mt] = mfma(ld8(recC + rT + mt * kBlk + sl), rbm, zero);
-        const bf16x8 um = pack2(UM[0], UM[1]);
+        const int l8 = opaque(ln * 8);
+        const floatx4 UM0 = mfma16(ld4(recC + rT + kOpT00 + l8), pack4(RM[0]), zero);
+        const floatx4 RM1 = mfma16(ld4(recC + rT + kOpA10 + l8), pack4(UM0), RM[1]);
+        const floatx4 UM1 = mfma16(ld4(recC + rT + kOpT11 + l8), pack4(RM1), zero);
+        const bf16x8 um = pack2(UM0, UM1);
 #pragma unroll
         for (int t = 0; t < 8; ++t) {
           const floatx4 eg = *reinterpret_cast<const floatx4*>(recC + rEg + (lgm * 32 + 4 * t) * 4);
@@ -721,15 +684,16 @@ __global__ __launch_bounds__(kThreads) void fused_kernel(Params p, int64_t n_ste
         }
       }
     }
+    // ---- the causal tiles of step it + 1 (their chunk flags are in its information record)
+    if (doS) tiles<OUT>(sm, recS, opsF, reinterpret_cast<const StepInfo*>(recS + rMeta)->pairwise, (int)((it + 1) & 1), w, ln);
     v_load(vin, vw, s0 + (it + 1 < 0 ? 0 : (it + 1 < ns ? it + 1 : ns - 1)), v_voff);
     block_barrier();
-    // ---- second half: per-pair blocks (if any), tiles of step it + 2, the coupling block of step it + 1
+    // ---- second half: per-pair blocks of step it + 2 (if any), T of step it + 1
     if (doE) {
       const uint32_t pwmask = pairwise_mask(sm, p, s0 + it + 2);
       if (pwmask) pairwise_blocks<OUT, false>(sm, nullptr, recE, opsF, pwmask, 0, ln, tid);
-      tiles<OUT>(sm, recE, opsE, pwmask, w, ln);
     }
-    if (doS && w == 6) solve_finish(sm, recS, ln);
+    if (doS && w == 7) solve(sm, recS, (int)((it + 1) & 1), ln);
   }
 
   if (OUT) {
@@ -793,9 +757,9 @@ hipError_t launch_one(const Params& p, hipStream_t s, int64_t n_steps, const Seg
 
 }  // namespace
 
-bool fused_supported(const Params& p) {
+bool fused_supported(int dtype, int64_t dk, int64_t dv, int64_t T) {
   // 32-bit buffer offsets: a (b, h) slice of a [B,H,T,128] bf16 tensor must stay below 2^31 bytes
-  return p.dtype == KDA_DTYPE_BF16 && p.dk == D && p.dv == D && p.T <= ((int64_t)1 << 23);
+  return dtype == KDA_DTYPE_BF16 && dk == D && dv == D && T < ((int64_t)1 << 23);
 }
 
 hipError_t launch_fused_segments(const Params& p, hipStream_t s, int64_t n_steps, const SegPlan& sg, bool out) {

@@ -52,11 +52,20 @@ int check_gmin(float g_min) {
   return KDA_OK;
 }
 
-int pick_path(const kda::Params& p, const kda_opts_t* opts) {
+// path actually taken for a valid shape: 1 vector, 2 records, 3 fused; -1 for an unsupported request
+int pick_path(const kda_shape_t* sh, const kda_opts_t* opts) {
   const int req = opts ? opts->path : 0;
+  const bool mfma = sh->dtype == KDA_DTYPE_BF16 && sh->dk == 128 && sh->dv == 128;
   if (req == 1) return 1;
-  if (req == 2 || req == 3) return kda::mfma_supported(p) ? req : -1;
-  return kda::mfma_supported(p) ? 2 : 1;
+  if (req == 2) return mfma ? 2 : -1;
+  if (req == 3 && !mfma) return -1;
+  if (!mfma) return 1;
+  return kda::fused_supported(sh->dtype, sh->dk, sh->dv, sh->T) ? 3 : 2;
+}
+
+size_t workspace_for(const kda_shape_t* sh, int path) {
+  if (path < 2) return 0;
+  return kda::mfma_workspace_bytes(sh->B, sh->H, sh->T, sh->dk, sh->dv, path == 2);
 }
 
 }  // namespace
@@ -80,10 +89,14 @@ const char* kda_last_hip_error(void) { return g_last_hip_error; }
 int kda_version(void) { return KDA_VERSION; }
 
 size_t kda_workspace_bytes(const kda_shape_t* shape, int chunk) {
+  return kda_workspace_bytes_ex(shape, chunk, nullptr);
+}
+
+size_t kda_workspace_bytes_ex(const kda_shape_t* shape, int chunk, const kda_opts_t* opts) {
   if (check_shape(shape) != KDA_OK || chunk != kda::kChunk) return (size_t)-1;
-  if (shape->dtype == KDA_DTYPE_BF16)
-    return kda::mfma_workspace_bytes(shape->B, shape->H, shape->T, shape->dk, shape->dv);
-  return 0;
+  if (opts && (opts->path < 0 || opts->path > 3)) return (size_t)-1;
+  const int path = pick_path(shape, opts);
+  return path < 0 ? (size_t)-1 : workspace_for(shape, path);
 }
 
 int kda_chunk_fwd_ex(const void* q, const void* k, const void* v, const void* w, const void* beta,
@@ -119,7 +132,6 @@ int kda_chunk_fwd_ex(const void* q, const void* k, const void* v, const void* w,
   const Range r_s0 = range_of(S0, S0 ? BH * dk * dv * 4 : 0);
   const Range r_o = range_of(o, T > 0 ? BH * T * dv * esz : 0);
   const Range r_sf = range_of(S_final, BH * dk * dv * 4);
-  const size_t need_ws = kda_workspace_bytes(shape, chunk);
   const Range r_ws = range_of(workspace, workspace ? (int64_t)workspace_bytes : 0);
   const Range r_st = range_of(stats, stats ? (int64_t)sizeof(kda_stats_t) : 0);
   const Range ins[] = {r_q, r_k, r_v, r_w, r_b};
@@ -144,9 +156,10 @@ int kda_chunk_fwd_ex(const void* q, const void* k, const void* v, const void* w,
   p.force_fallback = opts ? opts->force_fallback : 0;
   p.seg_steps = opts ? opts->seg_steps : 0;
 
-  const int path = T > 0 ? pick_path(p, opts) : 1;
+  const int path = T > 0 ? pick_path(shape, opts) : 1;
   if (path < 0) return KDA_ERR_UNSUPPORTED;
-  if (path >= 2 && need_ws > 0 && (!workspace || workspace_bytes < need_ws)) return KDA_ERR_ARG;
+  const size_t need_ws = workspace_for(shape, path);
+  if (need_ws > 0 && (!workspace || workspace_bytes < need_ws)) return KDA_ERR_ARG;
   if (path >= 2 && !kda::mfma_seg_steps_ok(T, p.seg_steps)) return KDA_ERR_ARG;
 
   // ---- launches (first HIP call of the entry point)

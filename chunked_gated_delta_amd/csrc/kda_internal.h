@@ -35,8 +35,10 @@ hipError_t launch_gate_prefix(const void* w, float g_min, int unbounded, int64_t
                               int64_t T, int64_t dk, int dtype, float* g, float* G, float* span,
                               uint8_t* flags, hipStream_t s);
 hipError_t launch_vec(const Params& p, hipStream_t s);                 // plain fp32 vector path
-bool mfma_supported(const Params& p);                                   // matrix-core path available?
-size_t mfma_workspace_bytes(int64_t B, int64_t H, int64_t T, int64_t dk, int64_t dv);
+// workspace of the matrix-core paths: with `records`, the per-step records of path 2 and the
+// segment blocks; without, the segment blocks of the fused path only
+size_t mfma_workspace_bytes(int64_t B, int64_t H, int64_t T, int64_t dk, int64_t dv, bool records);
+bool fused_supported(int dtype, int64_t dk, int64_t dv, int64_t T);
 bool mfma_seg_steps_ok(int64_t T, int64_t seg_steps);                    // forced segment length allowed?
 hipError_t launch_mfma(const Params& p, hipStream_t s, hipEvent_t ev_begin, hipEvent_t ev_end, bool fused);
 

@@ -875,15 +875,11 @@ SegPlan make_plan(int64_t BH, int64_t T, int64_t seg_steps, bool records) {
 
 }  // namespace
 
-bool mfma_supported(const Params& p) {
-  return p.dtype == KDA_DTYPE_BF16 && p.dk == D && p.dv == D;
-}
-
-size_t mfma_workspace_bytes(int64_t B, int64_t H, int64_t T, int64_t dk, int64_t dv) {
+size_t mfma_workspace_bytes(int64_t B, int64_t H, int64_t T, int64_t dk, int64_t dv, bool records) {
   if (dk != D || dv != D) return 0;
   const int64_t n = n_steps_of(T);
   const int64_t nseg = n < kMaxSeg ? n : kMaxSeg;
-  return (size_t)(B * H * n) * kRecBytes + (size_t)(3 * B * H * nseg) * kSegState;
+  return (records ? (size_t)(B * H * n) * kRecBytes : 0) + (size_t)(3 * B * H * nseg) * kSegState;
 }
 
 bool mfma_seg_steps_ok(int64_t T, int64_t seg_steps) {
@@ -896,7 +892,7 @@ bool mfma_seg_steps_ok(int64_t T, int64_t seg_steps) {
 hipError_t launch_mfma(const Params& p, hipStream_t s, hipEvent_t ev_begin, hipEvent_t ev_end, bool fused) {
   const int64_t n_steps = n_steps_of(p.T);
   const int64_t BH = p.B * p.H;
-  fused = fused && fused_supported(p);
+  fused = fused && fused_supported(p.dtype, p.dk, p.dv, p.T);
   const SegPlan sg = make_plan(BH, p.T, p.seg_steps, !fused);
   if (fused) {
     hipError_t e;

@@ -48,6 +48,21 @@ __device__ __forceinline__ bf16x8 pack2(floatx4 a, floatx4 b) {
   return __builtin_bit_cast(bf16x8, __builtin_convertvector(f, bf16x8v));
 }
 
+// v_mfma_f32_16x16x16_bf16 (K = 16): lane holds A[li][4g .. 4g+3], B[4g .. 4g+3][li], D[4g + r][li].
+// A D-layout tile packed to bf16 is directly the B operand of the next product.
+typedef short bf16x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x4v __attribute__((ext_vector_type(4)));
+typedef float float4v __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ floatx4 mfma16(bf16x4 a, bf16x4 b, floatx4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a, b, c, 0, 0, 0);
+}
+__device__ __forceinline__ bf16x4 ld4(const void* p) { return *reinterpret_cast<const bf16x4*>(p); }
+__device__ __forceinline__ bf16x4 pack4(floatx4 a) {
+  const float4v f = {a[0], a[1], a[2], a[3]};
+  return __builtin_bit_cast(bf16x4, __builtin_convertvector(f, bf16x4v));
+}
+
 __device__ __forceinline__ uint32_t abs_bits(float x) { return __float_as_uint(x) & 0x7fffffffu; }
 
 __device__ __forceinline__ void compiler_fence() { __atomic_signal_fence(__ATOMIC_SEQ_CST); }
@@ -83,7 +98,6 @@ constexpr int kMHalf = 8 * 4 * 64 * 16;     // bytes of one bf16 part (hi or lo)
 constexpr int kMaxSeg = 32;                 // segments per (b, h)
 
 // the fused segment kernels take this configuration (bf16, dk = dv = 128, 32-bit buffer offsets)
-bool fused_supported(const Params& p);
 // the fused segment kernels (one launch: every segment's map when !out, every segment's outputs when out)
 hipError_t launch_fused_segments(const Params& p, hipStream_t s, int64_t n_steps, const SegPlan& sg, bool out);
 

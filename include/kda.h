@@ -99,8 +99,10 @@ typedef struct {
 typedef struct {
   int32_t disable_fallback; /* 1: flagged chunks still take the dense exp(+-G) path (shows the overflow) */
   int32_t force_fallback;   /* 1: every chunk takes the per-position path (measures its cost) */
-  int32_t path;             /* 0 auto, 1 the plain fp32 vector path, 2 the matrix-core path with
-                               per-step records in the workspace, 3 the fused matrix-core path */
+  int32_t path;             /* 0 auto (bf16 with dk = dv = 128: the fused matrix-core path, or the
+                               records path past T = 2^23; anything else: the vector path),
+                               1 the plain fp32 vector path, 2 the matrix-core path with per-step
+                               records in the workspace, 3 the fused matrix-core path */
   int32_t seg_steps;        /* matrix-core path: steps of 32 tokens per sequence segment (0 = automatic;
                                < 0, or more than 32 segments per sequence, is KDA_ERR_ARG) */
   void* ev_begin;           /* optional hipEvent_t recorded on `stream` before the call's first kernel */
@@ -124,7 +126,8 @@ enum {
  *   chunk   must be 16 (the tile the pages fix for g_min = -5).
  *   S0      may be NULL (zero initial state).
  *   workspace / workspace_bytes: device scratch of at least
- *           kda_workspace_bytes(shape, chunk) bytes (may be NULL when that is 0).
+ *           kda_workspace_bytes(shape, chunk) bytes (kda_workspace_bytes_ex with the same
+ *           opts for kda_chunk_fwd_ex); may be NULL when that is 0.
  *   stats   optional device pointer (NULL: no statistics).
  *   stream  hipStream_t to launch on.
  * When T = 0, o is not touched and S_final receives S0 (or zeros).         */
@@ -149,9 +152,15 @@ KDA_API int kda_chunk_fwd_ex(const void* q, const void* k, const void* v, const 
 KDA_API int kda_gate_prefix(const void* w, float g_min, int chunk, const kda_shape_t* shape,
                     float* g, float* G, float* span, uint8_t* flags, void* stream);
 
-/* Scratch bytes kda_chunk_fwd needs for this shape (0 means none). Returns
- * (size_t)-1 for an invalid shape or chunk. Host-only, no HIP call.          */
+/* Scratch bytes kda_chunk_fwd needs for this shape (0 means none): on the fused
+ * path, three 64 KiB fp32 blocks per sequence segment (at most 32 segments per
+ * (b, h)); on the records path (opts->path = 2, or T >= 2^23), also a 29 KiB
+ * record per 32 tokens per (b, h).  Returns (size_t)-1 for an invalid shape,
+ * chunk or path. Host-only, no HIP call.                                     */
 KDA_API size_t kda_workspace_bytes(const kda_shape_t* shape, int chunk);
+
+/* Same for kda_chunk_fwd_ex with these options (opts may be NULL: the automatic path). */
+KDA_API size_t kda_workspace_bytes_ex(const kda_shape_t* shape, int chunk, const kda_opts_t* opts);
 
 /* Static description of an error code. Host-only. */
 KDA_API const char* kda_strerror(int code);

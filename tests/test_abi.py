@@ -108,6 +108,22 @@ def test_overlaps_rejected():
     assert call(S0=ctypes.c_void_p(p[6].value + 16)) == -4       # S0 partly overlaps S_final
 
 
+def test_workspace_per_path():
+    ex = lambda sh, path: lib.kda_workspace_bytes_ex(ctypes.byref(sh), 16, ctypes.byref(KdaOpts(0, 0, path, 0, None, None)))
+    sh = shape(B=1, H=2, T=64)                  # 2 steps of 32 tokens per (b, h)
+    seg = 3 * 2 * 2 * 128 * 128 * 4             # X, M, S_start per segment, at most one segment per step
+    assert lib.kda_workspace_bytes(ctypes.byref(sh), 16) == seg      # automatic: the fused path
+    assert ex(sh, 3) == seg
+    assert ex(sh, 2) == seg + 2 * 2 * 29696     # plus a 29 KiB record per step
+    assert ex(sh, 1) == 0
+    assert ex(sh, 7) == ctypes.c_size_t(-1).value
+    assert ex(shape(dk=64, dv=64), 3) == ctypes.c_size_t(-1).value   # no matrix-core path at d = 64
+    assert ex(shape(dk=64, dv=64), 0) == 0
+    assert ex(shape(T=1 << 23), 0) == ex(shape(T=1 << 23), 2)         # past the fused path's range
+    # the records path checks its own, larger size
+    assert call(sh, ws_bytes=seg, opts=KdaOpts(0, 0, 2, 0, None, None)) == -4
+
+
 def test_workspace_too_small():
     need = lib.kda_workspace_bytes(ctypes.byref(shape()), 16)
     if need == 0:
