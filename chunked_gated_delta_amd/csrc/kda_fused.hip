@@ -156,8 +156,8 @@ struct EKeep {                 // E's values carried from its first half to its 
 };
 
 template <bool OUT>
-__device__ __forceinline__ void e_load(EIn& in, const Views& vw, int64_t step, int voff, int boff) {
-  const int so = (int)(step * STEP * D * 2), sb = (int)(step * STEP * 2);
+__device__ __forceinline__ void e_load(EIn& in, const Views& vw, int step, int voff, int boff) {
+  const int so = step * (STEP * D * 2), sb = step * (STEP * 2);
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
     in.k[j] = __builtin_amdgcn_raw_buffer_load_b32(vw.k, voff + j * D * 2, so, 0);
@@ -179,22 +179,25 @@ __device__ __forceinline__ int kt_off(int c, int h, int cc) { return (c >> 4) * 
 // totals, so the reduction runs over the quarter groups only.
 __device__ __forceinline__ float wave_min_totals(float g0, float g1) {
   uint32_t m = max(__float_as_uint(g0), __float_as_uint(g1));
-  m = max(m, (uint32_t)__builtin_amdgcn_update_dpp((int)m, (int)m, 0x114, 0xF, 0xF, false));   // row_shr:4
-  m = max(m, (uint32_t)__builtin_amdgcn_update_dpp((int)m, (int)m, 0x118, 0xF, 0xF, false));   // row_shr:8
-  m = max(m, (uint32_t)__builtin_amdgcn_update_dpp((int)m, (int)m, 0x142, 0xA, 0xF, false));   // row_bcast:15
-  m = max(m, (uint32_t)__builtin_amdgcn_update_dpp((int)m, (int)m, 0x143, 0xC, 0xF, false));   // row_bcast:31
+  // lanes without a source, and rows outside the row mask, read 0: the identity of an unsigned maximum
+  m = max(m, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)m, 0x114, 0xF, 0xF, true));   // row_shr:4
+  m = max(m, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)m, 0x118, 0xF, 0xF, true));   // row_shr:8
+  m = max(m, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)m, 0x142, 0xA, 0xF, true));   // row_bcast:15
+  m = max(m, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)m, 0x143, 0xC, 0xF, true));   // row_bcast:31
   return __uint_as_float(m);
 }
 
 // First half of E for chunk CC of the step: gates, the in-chunk prefix L, the chunk totals, the span
 // of the wave's channels, beta, and e^{L}.
 template <bool UNB, int CC>
-__device__ __forceinline__ void e_first(FusedShared& sm, const EIn& in, EKeep& kp, const Params& p, int64_t step,
+__device__ __forceinline__ void e_first(FusedShared& sm, const EIn& in, EKeep& kp, const Params& p, int step,
                                         unsigned char* rec, int w, int l) {
   const int pr = 16 * (w & 3) + (l >> 2), h = l & 3;
   const int c0 = 2 * pr, c1 = 2 * pr + 1;
-  const int64_t rem = p.T - (step * STEP + 16 * CC + 4 * h);
-  const int nv = rem <= 0 ? 0 : (rem >= 4 ? 4 : (int)rem);   // this lane's tokens inside the sequence
+  // a step that lies wholly inside the sequence (every step but a ragged last one) needs no mask:
+  // the test is uniform, so the common case runs without per-token selects
+  const bool full = (step + 1) * STEP <= (int)p.T;
+  const int nv = full ? 4 : min(max((int)p.T - (step * STEP + 16 * CC + 4 * h), 0), 4);   // this lane's tokens in the sequence
   const float gml2 = p.g_min * kLog2e;
   float a0 = 0.f, a1 = 0.f;
 #pragma unroll
@@ -203,8 +206,13 @@ __device__ __forceinline__ void e_first(FusedShared& sm, const EIn& in, EKeep& k
     kp.q[j] = in.q[j];
     kp.beta[j] = __uint_as_float(in.b[j] << 16);
     const float g0 = gate2<UNB>(lo_bf16(in.w[j]), gml2), g1 = gate2<UNB>(hi_bf16(in.w[j]), gml2);
-    a0 += j < nv ? g0 : 0.f;
-    a1 += j < nv ? g1 : 0.f;
+    if (full) {
+      a0 += g0;
+      a1 += g1;
+    } else {
+      a0 += j < nv ? g0 : 0.f;
+      a1 += j < nv ? g1 : 0.f;
+    }
     kp.L0[j] = a0;
     kp.L1[j] = a1;
   }
@@ -250,7 +258,7 @@ __device__ __forceinline__ void pair_of(int pr, int& r, int& j) {   // pr -> (r,
 // e^{-L} = e^{Gam - L} e^{-Gam}: finite wherever the dense tile is used (a chunk whose e^{-Gam}
 // overflows has a span below -80 and takes the per-pair blocks instead).
 template <bool OUT, int CC>
-__device__ __forceinline__ void e_second(FusedShared& sm, const EKeep& kp, const Params& p, int64_t step,
+__device__ __forceinline__ void e_second(FusedShared& sm, const EKeep& kp, const Params& p, int step,
                                          unsigned char* rec, unsigned char* ops, int w, int l) {
   const int pr = 16 * (w & 3) + (l >> 2), h = l & 3;
   const int u = w & 3, g = ((l >> 2) & 7) >> 1, pos = (l >> 5) * 4 + 2 * ((l >> 2) & 1);
@@ -298,8 +306,8 @@ __device__ __forceinline__ void e_second(FusedShared& sm, const EKeep& kp, const
     }
     // spans and flags: the step's information record
     if (w == 0 && l == 0) {
-      const int64_t t0 = step * STEP;
-      const bool valid0 = t0 < p.T, valid1 = t0 + 16 < p.T;
+      const int t0 = step * STEP;
+      const bool valid0 = t0 < (int)p.T, valid1 = t0 + 16 < (int)p.T;
       const float span0 = fminf(fminf(sm.spanw[0], sm.spanw[1]), fminf(sm.spanw[2], sm.spanw[3])) * kLn2;
       const float span1 = fminf(fminf(sm.spanw[4], sm.spanw[5]), fminf(sm.spanw[6], sm.spanw[7])) * kLn2;
       const bool flag0 = valid0 && span0 < kSpanLimit, flag1 = valid1 && span1 < kSpanLimit;
@@ -317,9 +325,9 @@ __device__ __forceinline__ void e_second(FusedShared& sm, const EKeep& kp, const
 
 // Which chunks of the step in E take the per-pair blocks (bit c: chunk c).  Every thread of the
 // workgroup reads the same shared values, so the answer (and every branch on it) is uniform.
-__device__ __forceinline__ uint32_t pairwise_mask(const FusedShared& sm, const Params& p, int64_t step) {
-  const int64_t t0 = step * STEP;
-  const bool valid0 = t0 < p.T, valid1 = t0 + 16 < p.T;
+__device__ __forceinline__ uint32_t pairwise_mask(const FusedShared& sm, const Params& p, int step) {
+  const int t0 = step * STEP;
+  const bool valid0 = t0 < (int)p.T, valid1 = t0 + 16 < (int)p.T;
   const float span0 = fminf(fminf(sm.spanw[0], sm.spanw[1]), fminf(sm.spanw[2], sm.spanw[3])) * kLn2;
   const float span1 = fminf(fminf(sm.spanw[4], sm.spanw[5]), fminf(sm.spanw[6], sm.spanw[7])) * kLn2;
   const bool pw0 = p.force_fallback || (valid0 && span0 < kSpanLimit && !p.disable_fallback);
@@ -465,8 +473,8 @@ __device__ __forceinline__ void solve(FusedShared& sm, unsigned char* rec, int p
 // V of one step in D layout for column col: rows 16mt + 4lg + r.  Each value is widened to 32 bits as
 // it is loaded: with 16-bit values the compiler packs two loads into one register at once, waiting
 // for them (and for every load issued before them, among them the next step's prefetch).
-__device__ __forceinline__ void v_load(uint32_t (&vin)[8], const Views& vw, int64_t step, int voff) {
-  const int so = (int)(step * STEP * D * 2);
+__device__ __forceinline__ void v_load(uint32_t (&vin)[8], const Views& vw, int step, int voff) {
+  const int so = step * (STEP * D * 2);
 #pragma unroll
   for (int mt = 0; mt < 2; ++mt)
 #pragma unroll
@@ -483,25 +491,27 @@ __device__ __forceinline__ void beta_v(floatx4 (&bv)[2], const uint32_t (&vin)[8
   }
 }
 
-__device__ __forceinline__ int rows_left(int64_t T, int64_t step) {
-  const int64_t rem = T - step * STEP;
-  return rem < STEP ? (int)rem : STEP;
+__device__ __forceinline__ int rows_left(int T, int step) {
+  const int rem = T - step * STEP;
+  return rem < STEP ? rem : STEP;
 }
 
 // E wavefronts of chunk CC.  Interval s: first half E1(s+2), second half E2(s+2) and, for a flagged
 // chunk, the per-pair blocks of step s+2.
 template <bool OUT, bool UNB, int CC>
-__device__ __forceinline__ void e_loop(FusedShared& sm, const Params& p, const Views& vw, int64_t s0, int64_t ns, int we,
+__device__ __forceinline__ void e_loop(FusedShared& sm, const Params& p, const Views& vw, int s0, int ns, int we,
                                        int lane, int tid) {
   const int e_voff = ((16 * CC + 4 * (lane & 3)) * D + 2 * (16 * (we & 3) + (lane >> 2))) * 2;
   const int e_boff = (16 * CC + 4 * (lane & 3)) * 2;
   EIn ein;
   EKeep ekeep;
   e_load<OUT>(ein, vw, s0, e_voff, e_boff);
+  int slotE = 2;   // record slot of step it + 2 (it + 2 mod 3), advanced at the top of each pass
 #pragma unroll 1
-  for (int64_t it = -2; it < ns; ++it) {
+  for (int it = -2; it < ns; ++it) {
     const bool doE = it + 2 < ns;
-    unsigned char* recE = sm.rec[(it + 5) % kRecSlots];   // step it + 2
+    slotE = slotE == kRecSlots - 1 ? 0 : slotE + 1;
+    unsigned char* recE = sm.rec[slotE];                  // step it + 2
     unsigned char* opsE = sm.ops[(it + 2) & 1];           // step it + 2
     unsigned char* opsF = sm.ops[(it + 3) & 1];           // step it + 1 (free once its tiles are formed)
     block_barrier();
@@ -533,10 +543,12 @@ __global__ __launch_bounds__(kThreads) void fused_kernel(Params p, int64_t n_ste
   const bool is_e = w >= kCWaves;
   const int we = w - kCWaves;                 // E wavefront index (valid when is_e)
   const int li = lane & 15, lg = lane >> 4;
-  const int64_t nseg = OUT ? sg.P : sg.P - 1;
-  const int64_t bh = blockIdx.x / nseg, j = blockIdx.x % nseg;
-  const int64_t s0 = j * sg.L;
-  const int64_t ns = (n_steps - s0 < sg.L) ? n_steps - s0 : sg.L;
+  // step indices fit 32 bits (T < 2^23), which keeps the scalar index arithmetic short
+  const int nseg = (int)(OUT ? sg.P : sg.P - 1);
+  const int64_t bh = blockIdx.x / nseg;
+  const int j = blockIdx.x % nseg;
+  const int s0 = j * (int)sg.L;
+  const int ns = ((int)n_steps - s0 < (int)sg.L) ? (int)n_steps - s0 : (int)sg.L;
   const int64_t T = p.T;
   const int col = 16 * (w & 7) + li;
   const floatx4 zero = {0, 0, 0, 0};
@@ -588,12 +600,15 @@ __global__ __launch_bounds__(kThreads) void fused_kernel(Params p, int64_t n_ste
   float min_span = __int_as_float(0x7f800000);
   uint16_t* o = OUT ? (uint16_t*)p.o + bh * T * D + li * D + 16 * w + 4 * lg : nullptr;
 
+  int slotC = 0;   // record slot of step it (it mod 3), advanced at the top of each pass
 #pragma unroll 1
-  for (int64_t it = -2; it < ns; ++it) {
+  for (int it = -2; it < ns; ++it) {
     const bool doE = it + 2 < ns, doS = it + 1 >= 0 && it + 1 < ns, doC = it >= 0;
-    unsigned char* recC = sm.rec[(it + 3) % kRecSlots];   // step it       ((it + 3) keeps the index non-negative)
-    unsigned char* recS = sm.rec[(it + 4) % kRecSlots];   // step it + 1
-    unsigned char* recE = sm.rec[(it + 5) % kRecSlots];   // step it + 2
+    slotC = slotC == kRecSlots - 1 ? 0 : slotC + 1;
+    const int slotS = slotC == kRecSlots - 1 ? 0 : slotC + 1, slotE = slotS == kRecSlots - 1 ? 0 : slotS + 1;
+    unsigned char* recC = sm.rec[slotC];   // step it
+    unsigned char* recS = sm.rec[slotS];   // step it + 1
+    unsigned char* recE = sm.rec[slotE];   // step it + 2
     unsigned char* opsF = sm.ops[(it + 3) & 1];           // step it + 1
     block_barrier();
     const int ln = opaque(lane);
@@ -618,8 +633,8 @@ __global__ __launch_bounds__(kThreads) void fused_kernel(Params p, int64_t n_ste
       const floatx4 U1 = mfma16(ld4(recC + rT + kOpT11 + ln * 8), pack4(R1), zero);
       const bf16x8 ub = pack2(U0, U1);
       if (OUT) {
-        const int64_t st = s0 + it;
-        const int nrows = rows_left(T, st);
+        const int st = s0 + it;
+        const int nrows = rows_left((int)T, st);
         floatx4 O[2] = {zero, zero};
 #pragma unroll
         for (int u = 0; u < 4; ++u)
@@ -627,7 +642,7 @@ __global__ __launch_bounds__(kThreads) void fused_kernel(Params p, int64_t n_ste
           for (int mt = 0; mt < 2; ++mt) O[mt] = mfma(sb[u], ld8(recC + rQb + (mt * 4 + u) * kBlk + sl), O[mt]);
 #pragma unroll
         for (int mt = 0; mt < 2; ++mt) O[mt] = mfma(ub, ld8(recC + rP + mt * kBlk + sl), O[mt]);
-        uint16_t* os = o + st * STEP * D;
+        uint16_t* os = o + (int64_t)st * STEP * D;
         uint32_t mx = 0;
 #pragma unroll
         for (int mt = 0; mt < 2; ++mt) {
