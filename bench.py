@@ -158,6 +158,63 @@ def cpu_baseline(inp, wl, target_s: float = 15.0):
     }
 
 
+def decode_bytes(wl) -> int:
+    """HBM bytes one decode call must move: the fp32 state read and written, plus the token's inputs
+    and output (q, k, w, v, beta in, o out)."""
+    esz = 2 if wl.dtype == "bf16" else 4
+    state = wl.B * wl.H * wl.dk * wl.dv * 4 * 2
+    return state + wl.token_heads * ((3 * wl.dk + 2 * wl.dv) * esz + esz)
+
+
+def bench_decode(args, torch, gen):
+    """Recurrent decode: one kda_decode call per step over a serving batch, states resident."""
+    from chunked_gated_delta_amd import decode
+    wl = gen.WORKLOADS["decode_b512" if args.workload == "headline" else args.workload]
+    log(f"[bench] decode workload {wl}")
+    t = gen.make_torch(wl, seed=args.seed, device="cuda")
+    S = t["S0"].clone()
+    o = torch.empty_like(t["v"])
+    q, k, v, w, beta = (t[n] for n in ("q", "k", "v", "w", "beta"))
+    for _ in range(args.warmup):
+        decode(q, k, v, w, beta, S, g_min=wl.g_min, out=o)
+    torch.cuda.synchronize()
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        evs[i][0].record()
+        decode(q, k, v, w, beta, S, g_min=wl.g_min, out=o)
+        evs[i][1].record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    kern = [a.elapsed_time(b) for a, b in evs]
+    kern_avg = sum(kern) / len(kern)
+    nbytes = decode_bytes(wl)
+    achieved = nbytes / (kern_avg * 1e-3) / 1e9
+    log(f"[bench] decode kernel ms: avg {kern_avg:.5f} min {min(kern):.5f} max {max(kern):.5f}; wall/step "
+        f"{1e3 * wall / args.steps:.5f} ms")
+    line = {
+        "metric": "KDA recurrent decode tokens/s (B512 H16 d128, bf16 in, fp32 state)",
+        "value": round(wl.B * wl.T / (wall / args.steps), 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(1e3 * wall / args.steps, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16" if wl.dtype == "bf16" else "f32",
+        "data": "synthetic",
+        "config": {"workload": wl.name, "B": wl.B, "H": wl.H, "T": wl.T, "dk": wl.dk, "dv": wl.dv,
+                   "g_min": wl.g_min if math.isfinite(wl.g_min) else "-inf", "parallelism": "single-gpu"},
+        "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None, "bytes_per_launch": nbytes,
+                     "kernel_ms": round(kern_avg, 5)},
+        "cpu_baseline": None,
+    }
+    print(json.dumps(line), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -168,6 +225,9 @@ def main():
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--force-fallback", action="store_true")
+    ap.add_argument("--mode", default="forward", choices=["forward", "decode"],
+                    help="forward: the chunked forward (the headline); decode: one recurrent decode "
+                         "step of a serving batch (workload decode_b512 unless --workload is given)")
     ap.add_argument("--copy-calib", action="store_true",
                     help="run only a plain device copy of known size (for scaling HBM counters)")
     ap.add_argument("--summarize-pmc", nargs=4, metavar=("FETCH_CSV", "WRITE_CSV", "COPY_FETCH_CSV", "COPY_WRITE_CSV"),
@@ -196,6 +256,10 @@ def main():
 
     from chunked_gated_delta_amd import HipEvent, chunk_fwd, decode_stats
     from chunked_gated_delta_amd import inputs as gen
+
+    if args.mode == "decode":
+        bench_decode(args, torch, gen)
+        return
 
     wl = gen.WORKLOADS[args.workload]
     log(f"[bench] workload {wl}")

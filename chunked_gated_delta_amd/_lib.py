@@ -69,6 +69,8 @@ def load():
     lib.kda_chunk_fwd.restype = i32
     lib.kda_chunk_fwd_ex.argtypes = fwd_args + [ctypes.POINTER(KdaOpts)]
     lib.kda_chunk_fwd_ex.restype = i32
+    lib.kda_decode.argtypes = [vp, vp, vp, vp, vp, vp, f32, ctypes.POINTER(KdaShape), vp, vp]
+    lib.kda_decode.restype = i32
     lib.kda_gate_prefix.argtypes = [vp, f32, i32, ctypes.POINTER(KdaShape), vp, vp, vp, vp, vp]
     lib.kda_gate_prefix.restype = i32
     lib.kda_workspace_bytes.argtypes = [ctypes.POINTER(KdaShape), i32]

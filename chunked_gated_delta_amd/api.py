@@ -141,5 +141,39 @@ def gate_prefix(w, g_min: float = -5.0, chunk: int = 16, stream=None):
     return g, G, span, flags
 
 
+def decode(q, k, v, w, beta, S, g_min: float = -5.0, *, out=None, stream=None):
+    """Recurrent decode through kda_decode: advances the fp32 state S [B,H,dk,dv] in place by the
+    T tokens of q, k, w [B,H,T,dk], v [B,H,T,dv], beta [B,H,T] (T is typically 1) and returns
+    o [B,H,T,dv].  Asynchronous on `stream` (default: the current torch stream)."""
+    if q.dim() != 4:
+        raise ValueError("q must be [B,H,T,dk]")
+    B, H, T, dk = q.shape
+    dv = v.shape[-1]
+    dt = q.dtype
+    dev = q.device
+    if dev.type != "cuda":
+        raise ValueError("inputs must live on a GPU (the library has no CPU path)")
+    _check(q, "q", (B, H, T, dk), dt, dev)
+    _check(k, "k", (B, H, T, dk), dt, dev)
+    _check(w, "w", (B, H, T, dk), dt, dev)
+    _check(v, "v", (B, H, T, dv), dt, dev)
+    _check(beta, "beta", (B, H, T), dt, dev)
+    _check(S, "S", (B, H, dk, dv), torch.float32, dev)
+    if out is None:
+        out = torch.empty((B, H, T, dv), dtype=dt, device=dev)
+    else:
+        _check(out, "out", (B, H, T, dv), dt, dev)
+    shape = make_shape(B, H, T, dk, dv, _dtype_code(q))
+    if stream is None:
+        stream = torch.cuda.current_stream(dev)
+    with torch.cuda.device(dev):
+        rc = _lib.load().kda_decode(_ptr(q), _ptr(k), _ptr(v), _ptr(w), _ptr(beta), _ptr(S),
+                                    ctypes.c_float(g_min), ctypes.byref(shape), _ptr(out),
+                                    ctypes.c_void_p(stream.cuda_stream))
+    if rc != 0:
+        raise KdaError(rc, "kda_decode", _lib.last_hip_error() if rc == _lib.KDA_ERR_HIP else "")
+    return out
+
+
 def is_unbounded(g_min: float) -> bool:
     return math.isinf(g_min) and g_min < 0

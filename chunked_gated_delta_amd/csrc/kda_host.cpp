@@ -192,6 +192,37 @@ int kda_chunk_fwd(const void* q, const void* k, const void* v, const void* w, co
                           workspace_bytes, stats, stream, nullptr);
 }
 
+int kda_decode(const void* q, const void* k, const void* v, const void* w, const void* beta,
+               float* S, float g_min, const kda_shape_t* shape, void* o, void* stream) {
+  int rc = check_shape(shape);
+  if (rc != KDA_OK) return rc;
+  if ((rc = check_gmin(g_min)) != KDA_OK) return rc;
+  const int64_t B = shape->B, H = shape->H, T = shape->T, dk = shape->dk, dv = shape->dv;
+  const int64_t esz = shape->dtype == KDA_DTYPE_BF16 ? 2 : 4;
+  if (!S) return KDA_ERR_NULL;
+  if (T > 0 && (!q || !k || !v || !w || !beta || !o)) return KDA_ERR_NULL;
+  const void* ptrs[] = {q, k, v, w, beta, S, o};
+  for (const void* p : ptrs)
+    if (p && !aligned16(p)) return KDA_ERR_ARG;
+  const int64_t BH = B * H;
+  const Range r_s = range_of(S, BH * dk * dv * 4);
+  const Range r_o = range_of(o, T > 0 ? BH * T * dv * esz : 0);
+  const Range ins[] = {range_of(q, T > 0 ? BH * T * dk * esz : 0), range_of(k, T > 0 ? BH * T * dk * esz : 0),
+                       range_of(v, T > 0 ? BH * T * dv * esz : 0), range_of(w, T > 0 ? BH * T * dk * esz : 0),
+                       range_of(beta, T > 0 ? BH * T * esz : 0)};
+  for (const Range& a : ins)
+    if (overlap(a, r_s) || overlap(a, r_o)) return KDA_ERR_ARG;
+  if (overlap(r_s, r_o)) return KDA_ERR_ARG;
+  if (T == 0) return KDA_OK;
+  kda::DecodeParams p{};
+  p.q = q; p.k = k; p.v = v; p.w = w; p.beta = beta; p.S = S; p.o = o;
+  p.unbounded = std::isinf(g_min) ? 1 : 0;
+  p.g_min = p.unbounded ? 0.f : g_min;
+  p.B = B; p.H = H; p.T = T; p.dk = dk; p.dv = dv; p.dtype = shape->dtype;
+  hipError_t e = kda::launch_decode(p, reinterpret_cast<hipStream_t>(stream));
+  return e == hipSuccess ? KDA_OK : hip_fail(e);
+}
+
 int kda_gate_prefix(const void* w, float g_min, int chunk, const kda_shape_t* shape,
                     float* g, float* G, float* span, uint8_t* flags, void* stream) {
   int rc = check_shape(shape);

@@ -28,6 +28,17 @@ struct Params {
   __host__ __device__ int64_t n_chunks() const { return (T + kChunk - 1) / kChunk; }
 };
 
+// Recurrent decode step (state in place)
+struct DecodeParams {
+  const void *q, *k, *v, *w, *beta;
+  float* S;
+  void* o;
+  float g_min;
+  int unbounded;
+  int64_t B, H, T, dk, dv;
+  int dtype;
+};
+
 // Launchers (each returns the hipError_t of its launch).
 hipError_t launch_stats_init(kda_stats_t* stats, hipStream_t s);
 hipError_t launch_state_copy(const Params& p, hipStream_t s);          // T == 0
@@ -35,6 +46,7 @@ hipError_t launch_gate_prefix(const void* w, float g_min, int unbounded, int64_t
                               int64_t T, int64_t dk, int dtype, float* g, float* G, float* span,
                               uint8_t* flags, hipStream_t s);
 hipError_t launch_vec(const Params& p, hipStream_t s);                 // plain fp32 vector path
+hipError_t launch_decode(const DecodeParams& p, hipStream_t s);        // per-token recurrence on a resident state
 // workspace of the matrix-core paths: with `records`, the per-step records of path 2 and the
 // segment blocks; without, the segment blocks of the fused path only
 size_t mfma_workspace_bytes(int64_t B, int64_t H, int64_t T, int64_t dk, int64_t dv, bool records);

@@ -62,6 +62,9 @@ WORKLOADS = {
     "unbounded": Workload("unbounded", 2, 16, 4096, 128, 128, "bf16",
                           w_mu=3.0, w_sd=3.0, g_min=-math.inf),
     "headline": Workload("headline", 1, 16, 65536, 128, 128, "bf16"),
+    # recurrent decode: a serving batch advanced by one token, fp32 states resident in HBM (512 MiB of
+    # state, more than the last-level cache, so that each call streams it from HBM)
+    "decode_b512": Workload("decode_b512", 512, 16, 1, 128, 128, "bf16", s0_sd=0.5),
 }
 
 

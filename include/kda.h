@@ -142,6 +142,20 @@ KDA_API int kda_chunk_fwd_ex(const void* q, const void* k, const void* v, const 
                      void* o, float* S_final, void* workspace, size_t workspace_bytes,
                      kda_stats_t* stats, void* stream, const kda_opts_t* opts);
 
+/* Recurrent decode: advance a resident state by shape->T tokens (typically 1), token by
+ * token, in place.  The per-token form of the same gated delta rule ("From Numerical
+ * Stability to Load Balancing ..." section 2.1; the gates of section 2.2), the reuse of the
+ * trained operator's state at inference:
+ *   S <- Diag(e^{g_t}) S;  u = beta_t (v_t - S^T k_t);  S <- S + k_t u^T;  o_t = S^T q_t
+ * Arguments: q, k, w [B,H,T,dk]; v, o [B,H,T,dv]; beta [B,H,T] (all shape->dtype, device);
+ *   S [B,H,dk,dv] fp32, device, read and overwritten (the caller owns it; it must not overlap
+ *   any other argument); g_min as for kda_chunk_fwd; dk, dv in {32, 64, 128}.
+ * No workspace, no statistics (no chunking, hence no reciprocal factors and nothing to flag).
+ * Same validation and error codes as kda_chunk_fwd (T = 0 launches nothing); asynchronous on
+ * stream. */
+KDA_API int kda_decode(const void* q, const void* k, const void* v, const void* w, const void* beta,
+                       float* S, float g_min, const kda_shape_t* shape, void* o, void* stream);
+
 /* Gate and in-chunk prefix stage on its own (for checking that stage).
  * Outputs (device, fp32 unless noted):
  *   g     [B,H,T,dk]   the per-step log-decay

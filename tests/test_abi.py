@@ -140,6 +140,30 @@ def test_opts_validation():
     assert call(opts=KdaOpts(0, 0, 7, 0, None, None)) == -3     # unknown path
 
 
+def decode_call(sh=None, g_min=-5.0, **over):
+    p = ptrs()
+    a = dict(q=p[0], k=p[1], v=p[2], w=p[3], beta=p[4], S=p[5], o=p[6])
+    a.update(over)
+    sh = shape() if sh is None else sh
+    return lib.kda_decode(a["q"], a["k"], a["v"], a["w"], a["beta"], a["S"], ctypes.c_float(g_min),
+                          ctypes.byref(sh), a["o"], None)
+
+
+def test_decode_validation():
+    assert decode_call(shape(B=0)) == -2
+    assert decode_call(shape(dk=48)) == -3
+    assert decode_call(g_min=float("nan")) == -4
+    assert decode_call(S=None) == -1
+    for name in ("q", "k", "v", "w", "beta", "o"):
+        assert decode_call(**{name: None}) == -1, name
+    p = ptrs()
+    assert decode_call(S=ctypes.c_void_p(p[5].value + 4)) == -4        # misaligned state
+    assert decode_call(o=ctypes.c_void_p(p[5].value + 1024)) == -4     # output inside the state
+    assert decode_call(S=p[0]) == -4                                    # state aliases q
+    # T = 0: nothing to do, no launch (so this runs without a GPU); only the state is required
+    assert decode_call(shape(T=0), q=None, k=None, v=None, w=None, beta=None, o=None) == 0
+
+
 def test_gate_prefix_validation():
     p = ptrs()
     sh = shape()
