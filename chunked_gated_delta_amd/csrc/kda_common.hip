@@ -37,15 +37,15 @@ hipError_t launch_state_copy(const Params& p, hipStream_t s) {
 // g = gate(w); G = inclusive prefix of g within the chunk; span = min_c G[last row, c].
 template <typename TIn>
 __global__ __launch_bounds__(128) void gate_prefix_kernel(const TIn* __restrict__ w, float g_min, int unbounded,
-                                                          int64_t T, int dk, int64_t NC,
+                                                          int64_t T, int dk, int chunk, int64_t NC,
                                                           float* __restrict__ g_out, float* __restrict__ G_out,
                                                           float* __restrict__ span_out, uint8_t* __restrict__ flags) {
   __shared__ float red[128];
   const int64_t bh = blockIdx.x / NC;
   const int64_t n = blockIdx.x % NC;
   const int c = threadIdx.x;
-  const int64_t t0 = n * kChunk;
-  const int len = (int)((T - t0) < kChunk ? (T - t0) : kChunk);
+  const int64_t t0 = n * chunk;
+  const int len = (int)((T - t0) < chunk ? (T - t0) : chunk);
   float G = 0.f;
   if (c < dk) {
     for (int r = 0; r < len; ++r) {
@@ -69,17 +69,17 @@ __global__ __launch_bounds__(128) void gate_prefix_kernel(const TIn* __restrict_
 }
 
 hipError_t launch_gate_prefix(const void* w, float g_min, int unbounded, int64_t B, int64_t H, int64_t T,
-                              int64_t dk, int dtype, float* g, float* G, float* span, uint8_t* flags,
+                              int64_t dk, int dtype, int chunk, float* g, float* G, float* span, uint8_t* flags,
                               hipStream_t s) {
-  const int64_t NC = (T + kChunk - 1) / kChunk;
+  const int64_t NC = (T + chunk - 1) / chunk;
   const int64_t blocks = B * H * NC;
   if (blocks == 0) return hipSuccess;
   if (dtype == KDA_DTYPE_BF16)
     hipLaunchKernelGGL(gate_prefix_kernel<uint16_t>, dim3((unsigned)blocks), dim3(128), 0, s,
-                       (const uint16_t*)w, g_min, unbounded, T, (int)dk, NC, g, G, span, flags);
+                       (const uint16_t*)w, g_min, unbounded, T, (int)dk, chunk, NC, g, G, span, flags);
   else
     hipLaunchKernelGGL(gate_prefix_kernel<float>, dim3((unsigned)blocks), dim3(128), 0, s,
-                       (const float*)w, g_min, unbounded, T, (int)dk, NC, g, G, span, flags);
+                       (const float*)w, g_min, unbounded, T, (int)dk, chunk, NC, g, G, span, flags);
   return hipGetLastError();
 }
 

@@ -227,7 +227,7 @@ int kda_gate_prefix(const void* w, float g_min, int chunk, const kda_shape_t* sh
                     float* g, float* G, float* span, uint8_t* flags, void* stream) {
   int rc = check_shape(shape);
   if (rc != KDA_OK) return rc;
-  if (chunk != kda::kChunk) return KDA_ERR_UNSUPPORTED;
+  if (chunk != 16 && chunk != 32 && chunk != 64) return KDA_ERR_UNSUPPORTED;
   if ((rc = check_gmin(g_min)) != KDA_OK) return rc;
   const int64_t B = shape->B, H = shape->H, T = shape->T, dk = shape->dk;
   if (T > 0 && !w) return KDA_ERR_NULL;
@@ -235,7 +235,7 @@ int kda_gate_prefix(const void* w, float g_min, int chunk, const kda_shape_t* sh
   for (const void* p : ptrs)
     if (p && !aligned16(p)) return KDA_ERR_ARG;
   const int64_t esz = shape->dtype == KDA_DTYPE_BF16 ? 2 : 4;
-  const int64_t NC = (T + 15) / 16;
+  const int64_t NC = (T + chunk - 1) / chunk;
   const Range r_w = range_of(w, B * H * T * dk * esz);
   const Range outs[] = {range_of(g, g ? B * H * T * dk * 4 : 0), range_of(G, G ? B * H * T * dk * 4 : 0),
                         range_of(span, span ? B * H * NC * 4 : 0), range_of(flags, flags ? B * H * NC : 0)};
@@ -245,7 +245,7 @@ int kda_gate_prefix(const void* w, float g_min, int chunk, const kda_shape_t* sh
       if (overlap(outs[i], outs[j])) return KDA_ERR_ARG;
   }
   const int unbounded = std::isinf(g_min) ? 1 : 0;
-  hipError_t e = kda::launch_gate_prefix(w, unbounded ? 0.f : g_min, unbounded, B, H, T, dk, shape->dtype,
+  hipError_t e = kda::launch_gate_prefix(w, unbounded ? 0.f : g_min, unbounded, B, H, T, dk, shape->dtype, chunk,
                                          g, G, span, flags, reinterpret_cast<hipStream_t>(stream));
   return e == hipSuccess ? KDA_OK : hip_fail(e);
 }

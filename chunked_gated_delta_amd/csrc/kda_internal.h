@@ -43,7 +43,7 @@ struct DecodeParams {
 hipError_t launch_stats_init(kda_stats_t* stats, hipStream_t s);
 hipError_t launch_state_copy(const Params& p, hipStream_t s);          // T == 0
 hipError_t launch_gate_prefix(const void* w, float g_min, int unbounded, int64_t B, int64_t H,
-                              int64_t T, int64_t dk, int dtype, float* g, float* G, float* span,
+                              int64_t T, int64_t dk, int dtype, int chunk, float* g, float* G, float* span,
                               uint8_t* flags, hipStream_t s);
 hipError_t launch_vec(const Params& p, hipStream_t s);                 // plain fp32 vector path
 hipError_t launch_decode(const DecodeParams& p, hipStream_t s);        // per-token recurrence on a resident state

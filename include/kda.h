@@ -156,12 +156,14 @@ KDA_API int kda_chunk_fwd_ex(const void* q, const void* k, const void* v, const 
 KDA_API int kda_decode(const void* q, const void* k, const void* v, const void* w, const void* beta,
                        float* S, float g_min, const kda_shape_t* shape, void* o, void* stream);
 
-/* Gate and in-chunk prefix stage on its own (for checking that stage).
+/* Gate and in-chunk prefix stage on its own (for checking that stage, and for the chunk-size
+ * co-design sweep: chunk may be 16, 32 or 64 here; kda_chunk_fwd evaluates 16-token chunks).
  * Outputs (device, fp32 unless noted):
  *   g     [B,H,T,dk]   the per-step log-decay
- *   G     [B,H,T,dk]   inclusive prefix of g, restarted at every 16-token chunk
- *   span  [B,H,NC]     min over key channels of the chunk's total (NC = ceil(T/16))
- *   flags [B,H,NC]     uint8: 1 when span < -80
+ *   G     [B,H,T,dk]   inclusive prefix of g, restarted at every chunk
+ *   span  [B,H,NC]     min over key channels of the chunk's total (NC = ceil(T/chunk))
+ *   flags [B,H,NC]     uint8: 1 when span < -80 (the chunk's reciprocal factor e^{-G} could pass
+ *                      e^{80}: "Demystifying ..." Breakthrough 1 part 2, whatever the chunk size)
  * Any output pointer may be NULL to skip it.  Same validation and error codes. */
 KDA_API int kda_gate_prefix(const void* w, float g_min, int chunk, const kda_shape_t* shape,
                     float* g, float* G, float* span, uint8_t* flags, void* stream);

@@ -172,6 +172,7 @@ def test_gate_prefix_validation():
                                          kw.get("g", p[1]), kw.get("G", p[2]), kw.get("span", p[3]),
                                          kw.get("flags", p[4]), None)
     assert f(chunk=8) == -3
+    assert f(chunk=48) == -3
     assert f(g_min=float("nan")) == -4
     assert f(w=None) == -1
     assert f(g=p[0]) == -4

@@ -133,24 +133,25 @@ def test_empty_sequence():
 
 # ---------------------------------------------------------------- stage: gate and in-chunk prefix
 
-@pytest.mark.parametrize("g_min,mu,sd", [(-5.0, 0.0, 2.0), (-5.0, 6.0, 1.0), (-math.inf, 3.0, 3.0)])
-def test_gate_prefix_stage(g_min, mu, sd):
+@pytest.mark.parametrize("chunk", [16, 32, 64])
+@pytest.mark.parametrize("g_min,mu,sd", [(-5.0, 0.0, 2.0), (-5.0, 6.0, 1.0), (-math.inf, 3.0, 3.0), (-3.0, 0.0, 2.0)])
+def test_gate_prefix_stage(g_min, mu, sd, chunk):
     from chunked_gated_delta_amd import gate_prefix
     wl = BF16.with_(B=1, H=2, T=333, w_mu=mu, w_sd=sd, g_min=g_min)
     inp = gen.make_numpy(wl, 21)
-    say(f"[case] gate_prefix {wl}")
+    say(f"[case] gate_prefix {wl} chunk={chunk}")
     w_t = gen.numpy_to_torch(inp, "cuda")["w"]
-    g, G, span, flags = gate_prefix(w_t, g_min)
+    g, G, span, flags = gate_prefix(w_t, g_min, chunk=chunk)
     torch.cuda.synchronize()
     w64 = inp["w"].astype(np.float64)
     g_ref = orc.gate(w64, g_min)
     assert np.max(np.abs(g.cpu().numpy() - g_ref)) <= 2e-6 * max(1.0, np.max(np.abs(g_ref)))
     T = wl.T
     G_ref = np.empty_like(g_ref)
-    for n in range(0, T, 16):
-        G_ref[:, :, n:n + 16] = np.cumsum(g_ref[:, :, n:n + 16], axis=2)
+    for n in range(0, T, chunk):
+        G_ref[:, :, n:n + chunk] = np.cumsum(g_ref[:, :, n:n + chunk], axis=2)
     assert np.max(np.abs(G.cpu().numpy() - G_ref)) <= 2e-5 * max(1.0, np.max(np.abs(G_ref)))
-    sp_ref = orc.chunk_spans(w64, g_min, 16)
+    sp_ref = orc.chunk_spans(w64, g_min, chunk)
     assert np.max(np.abs(span.cpu().numpy() - sp_ref)) <= 2e-5 * max(1.0, np.max(np.abs(sp_ref)))
     fl = flags.cpu().numpy().astype(bool)
     pred = sp_ref < -80.0
