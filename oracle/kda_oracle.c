@@ -171,6 +171,190 @@ int kda_oracle_f64(const double* q, const double* k, const double* v, const doub
   return 0;
 }
 
+/* ---------------------------------------------------------------- backward (adjoint of the recurrence)
+ *
+ * Gradients of a scalar loss L with dL/do = dO and dL/dS_final = dSf (NULL: zero), by reverse-mode
+ * differentiation of the token recurrence above, one step at a time from the last token back:
+ *
+ *   o_t = S_t^T q_t                 dq_t  = S_t do_t;          dS_t += q_t do_t^T
+ *   S_t = S' + k_t u^T              dk_t += dS_t u;            du    = dS_t^T k_t;       dS' = dS_t
+ *   u   = beta_t (v_t - S'^T k_t)   dbeta_t = du . (v_t - S'^T k_t);  dv_t = beta_t du;
+ *                                   z = -beta_t du:  dS' += k_t z^T;  dk_t += S' z
+ *   S'  = Diag(e^{g_t}) S_{t-1}     dS_{t-1} = Diag(e^{g_t}) dS';  dg_tc = sum_j dS'[c][j] S'[c][j]
+ *   g_t = gate(w_t)                 dw_tc = dg_tc gate'(w_tc):  g_min sigma (1 - sigma), or -sigma
+ *
+ * and dS0 = dS_0 at the end.  The forward states S_0 .. S_T of each head are kept ((T + 1) dk dv
+ * doubles per head in flight), so this is for the small sizes the tests use.
+ */
+
+/* d gate / d w */
+static double gate_deriv(double w, double g_min) {
+  const double s = sigmoid(w);
+  if (isinf(g_min) && g_min < 0.0) return -s;
+  return g_min * s * (1.0 - s);
+}
+
+typedef struct {
+  const double *q, *k, *v, *w, *beta, *S0, *dO, *dSf;
+  double g_min;
+  int64_t B, H, T, dk, dv;
+  double *dq, *dk_, *dv_, *dw, *dbeta, *dS0;
+  int64_t next;
+  int failed;
+  pthread_mutex_t lock;
+} bjob_t;
+
+static int run_head_bwd(const bjob_t* J, int64_t bh) {
+  const int64_t T = J->T, dk = J->dk, dv = J->dv, n = dk * dv;
+  const double* q = J->q + bh * T * dk;
+  const double* k = J->k + bh * T * dk;
+  const double* v = J->v + bh * T * dv;
+  const double* w = J->w + bh * T * dk;
+  const double* beta = J->beta + bh * T;
+  const double* dO = J->dO + bh * T * dv;
+  double* hist = (double*)malloc(sizeof(double) * n * (T + 1));   /* S_0 .. S_T */
+  double* Sp = (double*)malloc(sizeof(double) * n);                /* S' of the step being undone */
+  double* dS = (double*)malloc(sizeof(double) * n);
+  double* eg = (double*)malloc(sizeof(double) * dk);
+  double* kS = (double*)malloc(sizeof(double) * dv);
+  double* u = (double*)malloc(sizeof(double) * dv);
+  double* du = (double*)malloc(sizeof(double) * dv);
+  if (!hist || !Sp || !dS || !eg || !kS || !u || !du) {
+    free(hist); free(Sp); free(dS); free(eg); free(kS); free(u); free(du);
+    return -1;
+  }
+  /* forward, keeping every state */
+  if (J->S0) memcpy(hist, J->S0 + bh * n, sizeof(double) * n);
+  else memset(hist, 0, sizeof(double) * n);
+  for (int64_t t = 0; t < T; ++t) {
+    const double* Sprev = hist + t * n;
+    double* S = hist + (t + 1) * n;
+    for (int64_t c = 0; c < dk; ++c) {
+      const double d = exp(kda_oracle_gate(w[t * dk + c], J->g_min));
+      for (int64_t j = 0; j < dv; ++j) S[c * dv + j] = d * Sprev[c * dv + j];
+    }
+    for (int64_t j = 0; j < dv; ++j) kS[j] = 0.0;
+    for (int64_t c = 0; c < dk; ++c)
+      for (int64_t j = 0; j < dv; ++j) kS[j] += k[t * dk + c] * S[c * dv + j];
+    for (int64_t j = 0; j < dv; ++j) u[j] = beta[t] * (v[t * dv + j] - kS[j]);
+    for (int64_t c = 0; c < dk; ++c)
+      for (int64_t j = 0; j < dv; ++j) S[c * dv + j] += k[t * dk + c] * u[j];
+  }
+  /* backward */
+  if (J->dSf) memcpy(dS, J->dSf + bh * n, sizeof(double) * n);
+  else memset(dS, 0, sizeof(double) * n);
+  for (int64_t t = T - 1; t >= 0; --t) {
+    const double* Sprev = hist + t * n;
+    const double* St = hist + (t + 1) * n;
+    const double* qt = q + t * dk;
+    const double* kt = k + t * dk;
+    const double* dot = dO + t * dv;
+    double* dqt = J->dq + (bh * T + t) * dk;
+    double* dkt = J->dk_ + (bh * T + t) * dk;
+    double* dvt = J->dv_ + (bh * T + t) * dv;
+    double* dwt = J->dw + (bh * T + t) * dk;
+    /* recompute this step's S' and u */
+    for (int64_t c = 0; c < dk; ++c) {
+      eg[c] = exp(kda_oracle_gate(w[t * dk + c], J->g_min));
+      for (int64_t j = 0; j < dv; ++j) Sp[c * dv + j] = eg[c] * Sprev[c * dv + j];
+    }
+    for (int64_t j = 0; j < dv; ++j) kS[j] = 0.0;
+    for (int64_t c = 0; c < dk; ++c)
+      for (int64_t j = 0; j < dv; ++j) kS[j] += kt[c] * Sp[c * dv + j];
+    for (int64_t j = 0; j < dv; ++j) u[j] = beta[t] * (v[t * dv + j] - kS[j]);
+    /* read */
+    for (int64_t c = 0; c < dk; ++c) {
+      double a = 0.0;
+      for (int64_t j = 0; j < dv; ++j) a += St[c * dv + j] * dot[j];
+      dqt[c] = a;
+      for (int64_t j = 0; j < dv; ++j) dS[c * dv + j] += qt[c] * dot[j];
+    }
+    /* write */
+    for (int64_t c = 0; c < dk; ++c) {
+      double a = 0.0;
+      for (int64_t j = 0; j < dv; ++j) a += dS[c * dv + j] * u[j];
+      dkt[c] = a;
+    }
+    for (int64_t j = 0; j < dv; ++j) {
+      double a = 0.0;
+      for (int64_t c = 0; c < dk; ++c) a += dS[c * dv + j] * kt[c];
+      du[j] = a;
+    }
+    /* delta-rule error (dS now stands for dS') */
+    double db = 0.0;
+    for (int64_t j = 0; j < dv; ++j) {
+      db += du[j] * (v[t * dv + j] - kS[j]);
+      dvt[j] = beta[t] * du[j];
+      du[j] = -beta[t] * du[j];   /* z */
+    }
+    J->dbeta[bh * T + t] = db;
+    for (int64_t c = 0; c < dk; ++c) {
+      double a = 0.0;
+      for (int64_t j = 0; j < dv; ++j) {
+        a += Sp[c * dv + j] * du[j];
+        dS[c * dv + j] += kt[c] * du[j];
+      }
+      dkt[c] += a;
+    }
+    /* forget */
+    for (int64_t c = 0; c < dk; ++c) {
+      double a = 0.0;
+      for (int64_t j = 0; j < dv; ++j) {
+        a += dS[c * dv + j] * Sp[c * dv + j];
+        dS[c * dv + j] *= eg[c];
+      }
+      dwt[c] = a * gate_deriv(w[t * dk + c], J->g_min);
+    }
+  }
+  if (J->dS0) memcpy(J->dS0 + bh * n, dS, sizeof(double) * n);
+  free(hist); free(Sp); free(dS); free(eg); free(kS); free(u); free(du);
+  return 0;
+}
+
+static void* bworker(void* arg) {
+  bjob_t* J = (bjob_t*)arg;
+  for (;;) {
+    pthread_mutex_lock(&J->lock);
+    int64_t bh = J->next++;
+    pthread_mutex_unlock(&J->lock);
+    if (bh >= J->B * J->H) break;
+    if (run_head_bwd(J, bh) != 0) {
+      pthread_mutex_lock(&J->lock);
+      J->failed = 1;
+      pthread_mutex_unlock(&J->lock);
+    }
+  }
+  return NULL;
+}
+
+/* Gradients [same layouts as the inputs]; dSf and dS0 may be NULL.  Returns 0, or -1 on bad
+ * arguments or when the state history does not fit in memory. */
+int kda_oracle_bwd_f64(const double* q, const double* k, const double* v, const double* w,
+                       const double* beta, const double* S0, double g_min,
+                       int64_t B, int64_t H, int64_t T, int64_t dk, int64_t dv,
+                       const double* dO, const double* dSf,
+                       double* dq, double* dk_out, double* dv_out, double* dw, double* dbeta, double* dS0,
+                       int nthreads) {
+  if (B < 1 || H < 1 || T < 0 || dk < 1 || dv < 1) return -1;
+  if (T > 0 && (!q || !k || !v || !w || !beta || !dO || !dq || !dk_out || !dv_out || !dw || !dbeta)) return -1;
+  if (isnan(g_min) || g_min > 0.0) return -1;
+  bjob_t J;
+  J.q = q; J.k = k; J.v = v; J.w = w; J.beta = beta; J.S0 = S0; J.dO = dO; J.dSf = dSf;
+  J.g_min = g_min; J.B = B; J.H = H; J.T = T; J.dk = dk; J.dv = dv;
+  J.dq = dq; J.dk_ = dk_out; J.dv_ = dv_out; J.dw = dw; J.dbeta = dbeta; J.dS0 = dS0;
+  J.next = 0; J.failed = 0;
+  pthread_mutex_init(&J.lock, NULL);
+  int64_t nt = nthreads < 1 ? 1 : nthreads;
+  if (nt > B * H) nt = B * H;
+  pthread_t* th = (pthread_t*)malloc(sizeof(pthread_t) * nt);
+  for (int64_t i = 1; i < nt; ++i) pthread_create(&th[i], NULL, bworker, &J);
+  bworker(&J);
+  for (int64_t i = 1; i < nt; ++i) pthread_join(th[i], NULL);
+  free(th);
+  pthread_mutex_destroy(&J.lock);
+  return J.failed ? -1 : 0;
+}
+
 /* spans[b,h,n] = min over key channels c of the sum of g over the tokens of chunk n. */
 int kda_oracle_spans_f64(const double* w, double g_min, int64_t B, int64_t H, int64_t T,
                          int64_t dk, int64_t chunk, double* spans) {

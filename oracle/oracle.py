@@ -51,6 +51,9 @@ def _load():
         lib.kda_oracle_spans_f64.restype = ctypes.c_int
         lib.kda_oracle_gate_array.argtypes = [dp, i64, ctypes.c_double, dp]
         lib.kda_oracle_gate_array.restype = ctypes.c_int
+        lib.kda_oracle_bwd_f64.argtypes = [dp, dp, dp, dp, dp, dp, ctypes.c_double, i64, i64, i64, i64, i64,
+                                           dp, dp, dp, dp, dp, dp, dp, dp, ctypes.c_int]
+        lib.kda_oracle_bwd_f64.restype = ctypes.c_int
         _lib = lib
     return _lib
 
@@ -83,6 +86,26 @@ def kda_reference(q, k, v, w, beta, S0=None, g_min=-5.0, nthreads=None):
     if rc != 0:
         raise ValueError("kda_oracle_f64 rejected its arguments")
     return o, S
+
+
+def kda_backward(q, k, v, w, beta, S0, g_min, dO, dSf=None, nthreads=None):
+    """fp64 gradients of <dO, o> + <dSf, S_final> by the adjoint of the token recurrence.
+    Returns (dq, dk, dv, dw, dbeta, dS0)."""
+    q, k, v, w, beta, S0, dO, dSf = (_f64(x) for x in (q, k, v, w, beta, S0, dO, dSf))
+    B, H, T, dk = q.shape
+    dv = v.shape[-1]
+    assert dO.shape == (B, H, T, dv)
+    out = dict(dq=np.zeros((B, H, T, dk)), dk=np.zeros((B, H, T, dk)), dv=np.zeros((B, H, T, dv)),
+               dw=np.zeros((B, H, T, dk)), dbeta=np.zeros((B, H, T)), dS0=np.zeros((B, H, dk, dv)))
+    if nthreads is None:
+        nthreads = os.cpu_count() or 1
+    rc = _load().kda_oracle_bwd_f64(_ptr(q), _ptr(k), _ptr(v), _ptr(w), _ptr(beta), _ptr(S0), float(g_min),
+                                    B, H, T, dk, dv, _ptr(dO), _ptr(dSf),
+                                    _ptr(out["dq"]), _ptr(out["dk"]), _ptr(out["dv"]), _ptr(out["dw"]),
+                                    _ptr(out["dbeta"]), _ptr(out["dS0"]), int(nthreads))
+    if rc != 0:
+        raise ValueError("kda_oracle_bwd_f64 rejected its arguments")
+    return out["dq"], out["dk"], out["dv"], out["dw"], out["dbeta"], out["dS0"]
 
 
 def gate(w, g_min=-5.0):

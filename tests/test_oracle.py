@@ -379,3 +379,109 @@ def test_planted_mistakes_are_caught(tmp_path, name):
     assert rc == 0
     o_ref, S_ref = brute_quadratic(q, k, v, w, b, S0, -5.0)
     assert rel(o, o_ref) > 1e-6 or rel(S, S_ref) > 1e-6, f"pin failed to catch mutation {name}"
+
+
+# ---------------------------------------------------------------- backward (adjoint) pins
+
+def _fd_grads(args, g_min, dO, dSf, h=1e-6):
+    """Central finite differences of <dO, o> + <dSf, S_final> with respect to every input."""
+    def loss(a):
+        o, S = orc.kda_reference(*a, g_min, nthreads=1)
+        return float((o * dO).sum() + (S * dSf).sum())
+    out = []
+    for ai, x in enumerate(args):
+        fd = np.zeros_like(x)
+        for idx in np.ndindex(x.shape):
+            ap = [a.copy() for a in args]
+            am = [a.copy() for a in args]
+            ap[ai][idx] += h
+            am[ai][idx] -= h
+            fd[idx] = (loss(ap) - loss(am)) / (2 * h)
+        out.append(fd)
+    return out
+
+
+def _bwd_case(seed, T=7, dk=4, dv=3):
+    rng = np.random.default_rng(seed)
+    q, k, w = (rng.normal(size=(1, 2, T, dk)) for _ in range(3))
+    k /= np.linalg.norm(k, axis=-1, keepdims=True)
+    v = rng.normal(size=(1, 2, T, dv))
+    beta = 1.0 / (1.0 + np.exp(-rng.normal(size=(1, 2, T))))
+    S0 = 0.3 * rng.normal(size=(1, 2, dk, dv))
+    dO = rng.normal(size=(1, 2, T, dv))
+    dSf = rng.normal(size=(1, 2, dk, dv))
+    return [q, k, v, w, beta, S0], dO, dSf
+
+
+@pytest.mark.parametrize("g_min", [-5.0, -8.0, -math.inf, 0.0])
+def test_backward_matches_finite_differences(g_min):
+    """The adjoint recurrence against central differences of the forward oracle, every input."""
+    args, dO, dSf = _bwd_case(7)
+    grads = orc.kda_backward(*args, g_min, dO, dSf, nthreads=1)
+    fds = _fd_grads(args, g_min, dO, dSf)
+    for name, g, fd in zip(("q", "k", "v", "w", "beta", "S0"), grads, fds):
+        scale = max(1e-12, np.max(np.abs(fd)))
+        assert np.max(np.abs(g - fd)) / scale < 1e-6, name
+
+
+def test_backward_closed_form_no_writes():
+    """beta = 0 and a zero gate: o_t = S0^T q_t, so dq_t = S0 do_t, dS0 = sum_t q_t do_t^T + dSf, and
+    dk = dv = dbeta = 0 except dbeta_t = do-weighted error, which the next pin covers."""
+    rng = np.random.default_rng(3)
+    T, dk, dv = 9, 5, 4
+    q = rng.normal(size=(1, 1, T, dk))
+    k = rng.normal(size=(1, 1, T, dk))
+    v = rng.normal(size=(1, 1, T, dv))
+    w = rng.normal(size=(1, 1, T, dk))
+    beta = np.zeros((1, 1, T))
+    S0 = rng.normal(size=(1, 1, dk, dv))
+    dO = rng.normal(size=(1, 1, T, dv))
+    dSf = rng.normal(size=(1, 1, dk, dv))
+    dq, dk_, dv_, dw, db, dS0 = orc.kda_backward(q, k, v, w, beta, S0, 0.0, dO, dSf, nthreads=1)
+    assert np.allclose(dq[0, 0], dO[0, 0] @ S0[0, 0].T, atol=1e-12)
+    assert np.allclose(dS0[0, 0], q[0, 0].T @ dO[0, 0] + dSf[0, 0], atol=1e-12)
+    assert np.allclose(dk_, 0.0) and np.allclose(dv_, 0.0) and np.allclose(dw, 0.0)
+    # dbeta_t = (v_t - S0^T k_t) . (S0^T-side adjoint): with S constant, du_t = (dSf + sum_{t'>=t} q do^T)^T k_t
+    dS = dSf[0, 0] + np.zeros_like(S0[0, 0])
+    want = np.zeros(T)
+    for t in range(T - 1, -1, -1):
+        dS = dS + np.outer(q[0, 0, t], dO[0, 0, t])
+        want[t] = (dS.T @ k[0, 0, t]) @ (v[0, 0, t] - S0[0, 0].T @ k[0, 0, t])
+    assert np.allclose(db[0, 0], want, atol=1e-10)
+
+
+BWD_MUTATIONS = {
+    "read_adjoint_dropped": ("for (int64_t j = 0; j < dv; ++j) dS[c * dv + j] += qt[c] * dot[j];", ""),
+    "erase_adjoint_sign": ("du[j] = -beta[t] * du[j];   /* z */", "du[j] = beta[t] * du[j];   /* z */"),
+    "gate_derivative": ("return g_min * s * (1.0 - s);", "return g_min * s;"),
+    "decay_adjoint_missing": ("dS[c * dv + j] *= eg[c];", "dS[c * dv + j] *= 1.0;"),
+}
+
+
+@pytest.mark.parametrize("name", sorted(BWD_MUTATIONS))
+def test_backward_planted_mistakes_are_caught(tmp_path, name):
+    src = open(os.path.join(os.path.dirname(orc.__file__), "kda_oracle.c")).read()
+    old, new = BWD_MUTATIONS[name]
+    assert src.count(old) == 1, name
+    path = tmp_path / f"bmut_{name}.c"
+    path.write_text(src.replace(old, new))
+    so = tmp_path / f"bmut_{name}.so"
+    subprocess.check_call(["gcc", "-O1", "-std=c99", "-fPIC", "-shared", "-o", str(so), str(path), "-lm", "-lpthread"])
+    lib = ctypes.CDLL(str(so))
+    dp = ctypes.POINTER(ctypes.c_double)
+    i64 = ctypes.c_int64
+    lib.kda_oracle_bwd_f64.argtypes = [dp, dp, dp, dp, dp, dp, ctypes.c_double, i64, i64, i64, i64, i64,
+                                       dp, dp, dp, dp, dp, dp, dp, dp, ctypes.c_int]
+    args, dO, dSf = _bwd_case(11)
+    B, H, T, dk = args[0].shape
+    dv = args[2].shape[-1]
+    outs = [np.zeros((B, H, T, dk)), np.zeros((B, H, T, dk)), np.zeros((B, H, T, dv)), np.zeros((B, H, T, dk)),
+            np.zeros((B, H, T)), np.zeros((B, H, dk, dv))]
+    ptr = lambda a: np.ascontiguousarray(a).ctypes.data_as(dp)
+    arrs = [np.ascontiguousarray(a, np.float64) for a in args]
+    rc = lib.kda_oracle_bwd_f64(*[ptr(a) for a in arrs], -5.0, B, H, T, dk, dv, ptr(dO), ptr(dSf),
+                                *[ptr(o) for o in outs], 1)
+    assert rc == 0
+    fds = _fd_grads(args, -5.0, dO, dSf)
+    worst = max(np.max(np.abs(g - fd)) / max(1e-12, np.max(np.abs(fd))) for g, fd in zip(outs, fds))
+    assert worst > 1e-4, f"finite differences failed to catch backward mutation {name}"
