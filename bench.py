@@ -16,6 +16,11 @@ the library records on the launch stream before the first kernel and after the
 last.
 `cpu_baseline` times the fp64 oracle on the host on a bounded sample of the
 same workload (all heads, the first tokens of the sequence).
+
+Other modes print a line of the same form for other entry points:
+`--mode decode` one recurrent decode call over a serving batch (kda_decode,
+HBM roofline over the state read and written), `--mode bwd` one backward call
+(kda_chunk_bwd, fp32 vector-ALU roofline over the state-sized contractions).
 """
 from __future__ import annotations
 
@@ -32,6 +37,8 @@ if ROOT not in sys.path:
 
 METRIC = "KDA chunk-fwd tokens/s (H16,d128,T64K,bf16) + % of MFMA/HBM roofline"
 HBM_PEAK_GBS = 8000.0
+# fp32 vector peak: 256 CUs x 2.4 GHz x 128 fp32 FMA lanes per CU per clock x 2 flops
+FP32_VALU_PEAK_TFLOPS = 157.3
 PROFILES = os.path.join(ROOT, "profiles")
 KERNEL_SOURCES = ["chunked_gated_delta_amd/csrc/kda_mfma.hip", "chunked_gated_delta_amd/csrc/kda_fused.hip",
                   "chunked_gated_delta_amd/csrc/kda_mfma_util.h", "chunked_gated_delta_amd/csrc/kda_common.hip",
@@ -215,6 +222,124 @@ def bench_decode(args, torch, gen):
     print(json.dumps(line), flush=True)
 
 
+def bwd_flops(wl) -> float:
+    """Arithmetic of the chunk-form backward per launch (2 flops per multiply-add), counting only the
+    state-sized contractions, per 16-token chunk and C*dk*dv each: the state chain recomputed
+    (E = V - Kbar S and S' = e^Gam S + Ktil^T U: 2), dU's Ktil dS', dQbar = dO S^T,
+    dKbar = dR S^T, dKtil = U dS'^T (4) and dS = Qbar^T dO - Kbar^T dR (2): 8 C dk dv multiply-adds.
+    The C x C blocks (X, P, T, dA, dP) add under 10% at d = 128 and are left out."""
+    C = 16
+    return 2.0 * 8 * C * wl.dk * wl.dv * wl.B * wl.H * math.ceil(wl.T / C)
+
+
+def bwd_bytes(wl) -> int:
+    """HBM bytes a backward call must move: q, k, w, v, beta and dO in (input dtype), dq, dk, dw,
+    dv and dbeta out (fp32), and the state-sized S0, dS_final in and dS0 out."""
+    esz = 2 if wl.dtype == "bf16" else 4
+    per_token_head = (3 * wl.dk + 2 * wl.dv + 1) * esz + (3 * wl.dk + wl.dv + 1) * 4
+    state = wl.B * wl.H * wl.dk * wl.dv * 4 * (3 if wl.s0_sd is not None else 2)
+    return wl.token_heads * per_token_head + state
+
+
+def cpu_baseline_bwd(inp, dO, dSf, wl, target_s: float = 15.0):
+    import numpy as np
+    from oracle import oracle as orc
+    try:
+        cores = len(os.sched_getaffinity(0))
+    except AttributeError:
+        cores = os.cpu_count() or 1
+    threads = max(1, min(cores, 16, wl.B * wl.H))
+
+    def run(Ts):
+        f = {k: inp[k][:, :, :Ts].float().cpu().numpy().astype(np.float64) for k in ("q", "k", "v", "w", "beta")}
+        S0 = None if inp["S0"] is None else inp["S0"].cpu().numpy().astype(np.float64)
+        d = dO[:, :, :Ts].float().cpu().numpy().astype(np.float64)
+        t0 = time.perf_counter()
+        orc.kda_backward(f["q"], f["k"], f["v"], f["w"], f["beta"], S0, wl.g_min, d,
+                         dSf.cpu().numpy().astype(np.float64), nthreads=threads)
+        return time.perf_counter() - t0
+
+    # the oracle keeps every state of a head (T * dk * dv * 8 bytes per thread), so the sample is the
+    # first Ts <= 1024 tokens of every head, run `reps` times back to back for a stable timing
+    Ts = max(16, (min(wl.T, 1024) // 16) * 16)
+    cal = run(Ts)
+    reps = int(max(1, min(200, target_s / max(cal, 1e-3))))
+    dt = sum(run(Ts) for _ in range(reps))
+    return {
+        "value": wl.B * Ts * reps / dt,
+        "unit": "tokens/s",
+        "cores": threads,
+        "kind": "oracle",
+        "sample": f"all {wl.B * wl.H} (b,h) adjoint recurrences over the first {Ts} of {wl.T} tokens, "
+                  f"{reps} runs (fp64, states kept per token, {threads} threads, {dt:.1f} s wall)",
+    }
+
+
+def bench_bwd(args, torch, gen):
+    """Backward of the chunked forward: one kda_chunk_bwd call per step on the headline shape."""
+    from chunked_gated_delta_amd import chunk_bwd
+    wl = gen.WORKLOADS[args.workload]
+    log(f"[bench] backward workload {wl}")
+    inp = gen.make_torch(wl, seed=args.seed, device="cuda")
+    g = torch.Generator(device="cuda").manual_seed(args.seed + 1)
+    dO = torch.randn((wl.B, wl.H, wl.T, wl.dv), generator=g, device="cuda").to(gen.torch_dtype(wl.dtype))
+    dSf = torch.randn((wl.B, wl.H, wl.dk, wl.dv), generator=g, device="cuda")
+    q, k, v, w, beta, S0 = (inp[n] for n in ("q", "k", "v", "w", "beta", "S0"))
+    ws = torch.empty(gen_bwd_ws(wl), dtype=torch.uint8, device="cuda")
+    for _ in range(args.warmup):
+        chunk_bwd(q, k, v, w, beta, dO, S0=S0, dS_final=dSf, g_min=wl.g_min, workspace=ws)
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        chunk_bwd(q, k, v, w, beta, dO, S0=S0, dS_final=dSf, g_min=wl.g_min, workspace=ws, stream=stream,
+                  events=evs[i])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    kern = [a.elapsed_time(b) for a, b in evs]
+    kern_avg = sum(kern) / len(kern)
+    log(f"[bench] backward call ms: avg {kern_avg:.4f} min {min(kern):.4f} max {max(kern):.4f}; wall/step "
+        f"{1e3 * wall / args.steps:.4f} ms")
+    flops = bwd_flops(wl)
+    tflops = flops / (kern_avg * 1e-3) / 1e12
+    cpu = None
+    if not args.no_cpu_baseline:
+        log("[bench] timing the fp64 oracle backward on the host ...")
+        cpu = cpu_baseline_bwd(inp, dO, dSf, wl)
+        log(f"[bench] cpu_baseline {cpu}")
+    line = {
+        "metric": "KDA chunked backward tokens/s (B1 H16 T65536 d128, bf16 in, fp32 gradients)",
+        "value": round(wl.B * wl.T / (wall / args.steps), 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(1e3 * wall / args.steps, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {"workload": wl.name, "B": wl.B, "H": wl.H, "T": wl.T, "dk": wl.dk, "dv": wl.dv,
+                   "chunk": 16, "g_min": wl.g_min if math.isfinite(wl.g_min) else "-inf",
+                   "inputs": wl.dtype, "parallelism": "single-gpu"},
+        "roofline": {"bound": "alu", "achieved": round(tflops, 3), "peak": FP32_VALU_PEAK_TFLOPS,
+                     "unit": "TFLOP/s", "frac": round(tflops / FP32_VALU_PEAK_TFLOPS, 4), "traffic": None,
+                     "flops_per_launch": flops, "kernel_ms": round(kern_avg, 5),
+                     "hbm_gbs": round(bwd_bytes(wl) / (kern_avg * 1e-3) / 1e9, 2)},
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(line), flush=True)
+
+
+def gen_bwd_ws(wl) -> int:
+    from chunked_gated_delta_amd import _lib
+    from chunked_gated_delta_amd.api import make_shape
+    code = _lib.DTYPE_BF16 if wl.dtype == "bf16" else _lib.DTYPE_F32
+    return max(1, _lib.bwd_workspace_bytes(make_shape(wl.B, wl.H, wl.T, wl.dk, wl.dv, code), 16))
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -225,9 +350,10 @@ def main():
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--force-fallback", action="store_true")
-    ap.add_argument("--mode", default="forward", choices=["forward", "decode"],
+    ap.add_argument("--mode", default="forward", choices=["forward", "decode", "bwd"],
                     help="forward: the chunked forward (the headline); decode: one recurrent decode "
-                         "step of a serving batch (workload decode_b512 unless --workload is given)")
+                         "step of a serving batch (workload decode_b512 unless --workload is given); "
+                         "bwd: the backward of the chunked forward on the same workload")
     ap.add_argument("--copy-calib", action="store_true",
                     help="run only a plain device copy of known size (for scaling HBM counters)")
     ap.add_argument("--summarize-pmc", nargs=4, metavar=("FETCH_CSV", "WRITE_CSV", "COPY_FETCH_CSV", "COPY_WRITE_CSV"),
@@ -259,6 +385,9 @@ def main():
 
     if args.mode == "decode":
         bench_decode(args, torch, gen)
+        return
+    if args.mode == "bwd":
+        bench_bwd(args, torch, gen)
         return
 
     wl = gen.WORKLOADS[args.workload]

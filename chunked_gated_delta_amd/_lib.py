@@ -71,6 +71,11 @@ def load():
     lib.kda_chunk_fwd_ex.restype = i32
     lib.kda_decode.argtypes = [vp, vp, vp, vp, vp, vp, f32, ctypes.POINTER(KdaShape), vp, vp]
     lib.kda_decode.restype = i32
+    lib.kda_chunk_bwd.argtypes = [vp, vp, vp, vp, vp, vp, f32, i32, ctypes.POINTER(KdaShape), vp, vp,
+                                  vp, vp, vp, vp, vp, vp, vp, sz, vp]
+    lib.kda_chunk_bwd.restype = i32
+    lib.kda_bwd_workspace_bytes.argtypes = [ctypes.POINTER(KdaShape), i32]
+    lib.kda_bwd_workspace_bytes.restype = sz
     lib.kda_gate_prefix.argtypes = [vp, f32, i32, ctypes.POINTER(KdaShape), vp, vp, vp, vp, vp]
     lib.kda_gate_prefix.restype = i32
     lib.kda_workspace_bytes.argtypes = [ctypes.POINTER(KdaShape), i32]
@@ -103,6 +108,13 @@ def workspace_bytes(shape: KdaShape, chunk: int = 16, opts: KdaOpts | None = Non
     n = load().kda_workspace_bytes_ex(ctypes.byref(shape), int(chunk), None if opts is None else ctypes.byref(opts))
     if n == ctypes.c_size_t(-1).value:
         raise KdaError(KDA_ERR_SHAPE, "kda_workspace_bytes_ex")
+    return n
+
+
+def bwd_workspace_bytes(shape: KdaShape, chunk: int = 16) -> int:
+    n = load().kda_bwd_workspace_bytes(ctypes.byref(shape), int(chunk))
+    if n == ctypes.c_size_t(-1).value:
+        raise KdaError(KDA_ERR_SHAPE, "kda_bwd_workspace_bytes")
     return n
 
 

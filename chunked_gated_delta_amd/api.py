@@ -175,5 +175,60 @@ def decode(q, k, v, w, beta, S, g_min: float = -5.0, *, out=None, stream=None):
     return out
 
 
+def chunk_bwd(q, k, v, w, beta, dO, S0=None, dS_final=None, g_min: float = -5.0, chunk: int = 16, *,
+              want_dS0: bool = True, workspace=None, stream=None, events=None):
+    """Gradients of the chunked forward through kda_chunk_bwd, given dO = dL/do [B,H,T,dv] (the
+    inputs' dtype) and dS_final = dL/dS_final (fp32 [B,H,dk,dv] or None for zero).  Returns fp32
+    (dq, dk, dv, dw, dbeta, dS0); dS0 is None when want_dS0 is False.  Asynchronous on `stream`.
+    `events` = (begin, end) torch.cuda.Event pair recorded on `stream` around the library call (the
+    library launches on that stream, so the pair brackets exactly its kernels)."""
+    if q.dim() != 4:
+        raise ValueError("q must be [B,H,T,dk]")
+    B, H, T, dk = q.shape
+    dv = v.shape[-1]
+    dt = q.dtype
+    dev = q.device
+    if dev.type != "cuda":
+        raise ValueError("inputs must live on a GPU (the library has no CPU path)")
+    _check(q, "q", (B, H, T, dk), dt, dev)
+    _check(k, "k", (B, H, T, dk), dt, dev)
+    _check(w, "w", (B, H, T, dk), dt, dev)
+    _check(v, "v", (B, H, T, dv), dt, dev)
+    _check(beta, "beta", (B, H, T), dt, dev)
+    _check(dO, "dO", (B, H, T, dv), dt, dev)
+    if S0 is not None:
+        _check(S0, "S0", (B, H, dk, dv), torch.float32, dev)
+    if dS_final is not None:
+        _check(dS_final, "dS_final", (B, H, dk, dv), torch.float32, dev)
+    shape = make_shape(B, H, T, dk, dv, _dtype_code(q))
+    f32 = dict(dtype=torch.float32, device=dev)
+    dq = torch.empty((B, H, T, dk), **f32)
+    dk_ = torch.empty((B, H, T, dk), **f32)
+    dv_ = torch.empty((B, H, T, dv), **f32)
+    dw = torch.empty((B, H, T, dk), **f32)
+    dbeta = torch.empty((B, H, T), **f32)
+    dS0 = torch.empty((B, H, dk, dv), **f32) if want_dS0 else None
+    need = _lib.bwd_workspace_bytes(shape, chunk)
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
+    elif workspace.numel() * workspace.element_size() < need:
+        raise ValueError(f"workspace holds {workspace.numel() * workspace.element_size()} bytes, {need} needed")
+    if stream is None:
+        stream = torch.cuda.current_stream(dev)
+    with torch.cuda.device(dev):
+        if events is not None:
+            events[0].record(stream)
+        rc = _lib.load().kda_chunk_bwd(_ptr(q), _ptr(k), _ptr(v), _ptr(w), _ptr(beta), _ptr(S0),
+                                       ctypes.c_float(g_min), int(chunk), ctypes.byref(shape), _ptr(dO),
+                                       _ptr(dS_final), _ptr(dq), _ptr(dk_), _ptr(dv_), _ptr(dw), _ptr(dbeta),
+                                       _ptr(dS0), _ptr(workspace), ctypes.c_size_t(need),
+                                       ctypes.c_void_p(stream.cuda_stream))
+        if events is not None:
+            events[1].record(stream)
+    if rc != 0:
+        raise KdaError(rc, "kda_chunk_bwd", _lib.last_hip_error() if rc == _lib.KDA_ERR_HIP else "")
+    return dq, dk_, dv_, dw, dbeta, dS0
+
+
 def is_unbounded(g_min: float) -> bool:
     return math.isinf(g_min) and g_min < 0

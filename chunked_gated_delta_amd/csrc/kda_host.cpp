@@ -223,6 +223,65 @@ int kda_decode(const void* q, const void* k, const void* v, const void* w, const
   return e == hipSuccess ? KDA_OK : hip_fail(e);
 }
 
+size_t kda_bwd_workspace_bytes(const kda_shape_t* shape, int chunk) {
+  if (check_shape(shape) != KDA_OK || chunk != kda::kChunk) return (size_t)-1;
+  return kda::bwd_workspace_bytes(shape->B, shape->H, shape->T, shape->dk, shape->dv);
+}
+
+int kda_chunk_bwd(const void* q, const void* k, const void* v, const void* w, const void* beta,
+                  const float* S0, float g_min, int chunk, const kda_shape_t* shape,
+                  const void* dO, const float* dS_final, float* dq, float* dk, float* dv, float* dw,
+                  float* dbeta, float* dS0, void* workspace, size_t workspace_bytes, void* stream) {
+  int rc = check_shape(shape);
+  if (rc != KDA_OK) return rc;
+  if (chunk != kda::kChunk) return KDA_ERR_UNSUPPORTED;
+  if ((rc = check_gmin(g_min)) != KDA_OK) return rc;
+  const int64_t B = shape->B, H = shape->H, T = shape->T, dkk = shape->dk, dvv = shape->dv;
+  const int64_t esz = shape->dtype == KDA_DTYPE_BF16 ? 2 : 4;
+  if (T > 0 && (!q || !k || !v || !w || !beta || !dO || !dq || !dk || !dv || !dw || !dbeta)) return KDA_ERR_NULL;
+  const void* ptrs[] = {q, k, v, w, beta, S0, dO, dS_final, dq, dk, dv, dw, dbeta, dS0, workspace};
+  for (const void* p : ptrs)
+    if (p && !aligned16(p)) return KDA_ERR_ARG;
+  const int64_t BH = B * H;
+  const size_t need_ws = kda::bwd_workspace_bytes(B, H, T, dkk, dvv);
+  if (T > 0 && (!workspace || workspace_bytes < need_ws)) return KDA_ERR_ARG;
+  const Range ins[] = {range_of(q, T > 0 ? BH * T * dkk * esz : 0), range_of(k, T > 0 ? BH * T * dkk * esz : 0),
+                       range_of(v, T > 0 ? BH * T * dvv * esz : 0), range_of(w, T > 0 ? BH * T * dkk * esz : 0),
+                       range_of(beta, T > 0 ? BH * T * esz : 0), range_of(S0, S0 ? BH * dkk * dvv * 4 : 0),
+                       range_of(dO, T > 0 ? BH * T * dvv * esz : 0),
+                       range_of(dS_final, dS_final ? BH * dkk * dvv * 4 : 0)};
+  const Range outs[] = {range_of(dq, T > 0 ? BH * T * dkk * 4 : 0), range_of(dk, T > 0 ? BH * T * dkk * 4 : 0),
+                        range_of(dv, T > 0 ? BH * T * dvv * 4 : 0), range_of(dw, T > 0 ? BH * T * dkk * 4 : 0),
+                        range_of(dbeta, T > 0 ? BH * T * 4 : 0), range_of(dS0, dS0 ? BH * dkk * dvv * 4 : 0),
+                        range_of(workspace, T > 0 ? (int64_t)need_ws : 0)};
+  for (const Range& a : outs)
+    for (const Range& b : ins)
+      if (overlap(a, b)) return KDA_ERR_ARG;
+  for (size_t i = 0; i < sizeof(outs) / sizeof(outs[0]); ++i)
+    for (size_t j = i + 1; j < sizeof(outs) / sizeof(outs[0]); ++j)
+      if (overlap(outs[i], outs[j])) return KDA_ERR_ARG;
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  hipError_t e;
+  if (T == 0) {   // no tokens: dS0 = dS_final
+    if (dS0) {
+      kda::Params cp{};
+      cp.S0 = dS_final; cp.S_final = dS0; cp.B = B; cp.H = H; cp.dk = dkk; cp.dv = dvv;
+      if ((e = kda::launch_state_copy(cp, s)) != hipSuccess) return hip_fail(e);
+    }
+    return KDA_OK;
+  }
+  kda::BwdParams b{};
+  kda::Params& p = b.p;
+  p.q = q; p.k = k; p.v = v; p.w = w; p.beta = beta; p.S0 = S0;
+  p.unbounded = std::isinf(g_min) ? 1 : 0;
+  p.g_min = p.unbounded ? 0.f : g_min;
+  p.B = B; p.H = H; p.T = T; p.dk = dkk; p.dv = dvv; p.dtype = shape->dtype;
+  p.workspace = workspace; p.workspace_bytes = workspace_bytes;
+  b.dO = dO; b.dSf = dS_final; b.dq = dq; b.dk = dk; b.dv = dv; b.dw = dw; b.dbeta = dbeta; b.dS0 = dS0;
+  if ((e = kda::launch_bwd(b, s)) != hipSuccess) return hip_fail(e);
+  return KDA_OK;
+}
+
 int kda_gate_prefix(const void* w, float g_min, int chunk, const kda_shape_t* shape,
                     float* g, float* G, float* span, uint8_t* flags, void* stream) {
   int rc = check_shape(shape);

@@ -39,6 +39,14 @@ struct DecodeParams {
   int dtype;
 };
 
+// Backward pass: gradients (fp32) of a loss given dO (input dtype) and dS_final (fp32, nullable)
+struct BwdParams {
+  Params p;          // forward arguments (workspace: the chunk entering states)
+  const void* dO;
+  const float* dSf;
+  float *dq, *dk, *dv, *dw, *dbeta, *dS0;   // dS0 nullable
+};
+
 // Launchers (each returns the hipError_t of its launch).
 hipError_t launch_stats_init(kda_stats_t* stats, hipStream_t s);
 hipError_t launch_state_copy(const Params& p, hipStream_t s);          // T == 0
@@ -47,6 +55,8 @@ hipError_t launch_gate_prefix(const void* w, float g_min, int unbounded, int64_t
                               uint8_t* flags, hipStream_t s);
 hipError_t launch_vec(const Params& p, hipStream_t s);                 // plain fp32 vector path
 hipError_t launch_decode(const DecodeParams& p, hipStream_t s);        // per-token recurrence on a resident state
+size_t bwd_workspace_bytes(int64_t B, int64_t H, int64_t T, int64_t dk, int64_t dv);
+hipError_t launch_bwd(const BwdParams& b, hipStream_t s);              // backward, fp32 vector ALUs
 // workspace of the matrix-core paths: with `records`, the per-step records of path 2 and the
 // segment blocks; without, the segment blocks of the fused path only
 size_t mfma_workspace_bytes(int64_t B, int64_t H, int64_t T, int64_t dk, int64_t dv, bool records);

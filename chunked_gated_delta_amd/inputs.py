@@ -112,6 +112,22 @@ def make_numpy(wl: Workload, seed: int = 0) -> dict:
     return dict(q=q, k=k, v=v, w=w, beta=beta, S0=S0, dtype=wl.dtype, g_min=wl.g_min)
 
 
+def make_cotangents(wl: Workload, seed: int = 0, with_dSf: bool = True) -> dict:
+    """Seeded adjoints for a backward pass: dO ~ N(0, 1) [B,H,T,dv] rounded to the workload dtype,
+    and dS_final ~ N(0, 1) fp32 [B,H,dk,dv] (or None).  Streams are per (b, h) and distinct from
+    make_numpy's."""
+    B, H, T, dk, dv = wl.B, wl.H, wl.T, wl.dk, wl.dv
+    dO = np.empty((B, H, T, dv), np.float32)
+    dSf = np.empty((B, H, dk, dv), np.float32) if with_dSf else None
+    for b in range(B):
+        for h in range(H):
+            rng = np.random.default_rng([seed, b, h, 7])
+            dO[b, h] = _round(rng.standard_normal((T, dv)), wl.dtype)
+            if dSf is not None:
+                dSf[b, h] = rng.standard_normal((dk, dv)).astype(np.float32)
+    return dict(dO=dO, dSf=dSf)
+
+
 def torch_dtype(dtype: str):
     import torch
     return torch.bfloat16 if dtype == "bf16" else torch.float32

@@ -156,6 +156,27 @@ KDA_API int kda_chunk_fwd_ex(const void* q, const void* k, const void* v, const 
 KDA_API int kda_decode(const void* q, const void* k, const void* v, const void* w, const void* beta,
                        float* S, float g_min, const kda_shape_t* shape, void* o, void* stream);
 
+/* Backward pass of the chunked forward: gradients of a loss L given dL/do and dL/dS_final.
+ * The reverse mode of the chunk form (each 16-token chunk's in-chunk blocks formed pair by pair
+ * with factors exp(G_r - G_j) <= 1, so no chunk needs a span check), evaluated in fp32 on the
+ * vector ALUs from the chunk entering states that a first pass recomputes into the workspace.
+ * Arguments: the forward's q, k, v, w, beta, S0 (nullable), g_min, chunk (16) and shape (dk in
+ *   {32, 64, 128}, dv in {32, 64, 128});
+ *   dO [B,H,T,dv] in shape->dtype; dS_final [B,H,dk,dv] fp32 or NULL (zero);
+ *   outputs, fp32, device: dq, dk, dw [B,H,T,dk]; dv [B,H,T,dv]; dbeta [B,H,T];
+ *   dS0 [B,H,dk,dv] or NULL (not wanted);
+ *   workspace of at least kda_bwd_workspace_bytes(shape, chunk) bytes.
+ * Outputs must not overlap inputs or each other.  Same validation and error codes as
+ * kda_chunk_fwd; asynchronous on stream. */
+KDA_API int kda_chunk_bwd(const void* q, const void* k, const void* v, const void* w, const void* beta,
+                          const float* S0, float g_min, int chunk, const kda_shape_t* shape,
+                          const void* dO, const float* dS_final, float* dq, float* dk, float* dv, float* dw,
+                          float* dbeta, float* dS0, void* workspace, size_t workspace_bytes, void* stream);
+
+/* Scratch bytes kda_chunk_bwd needs: the fp32 entering state of every 16-token chunk,
+ * B*H*ceil(T/16)*dk*dv*4.  (size_t)-1 for an invalid shape or chunk.  Host-only. */
+KDA_API size_t kda_bwd_workspace_bytes(const kda_shape_t* shape, int chunk);
+
 /* Gate and in-chunk prefix stage on its own (for checking that stage, and for the chunk-size
  * co-design sweep: chunk may be 16, 32 or 64 here; kda_chunk_fwd evaluates 16-token chunks).
  * Outputs (device, fp32 unless noted):

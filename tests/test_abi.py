@@ -177,3 +177,42 @@ def test_gate_prefix_validation():
     assert f(w=None) == -1
     assert f(g=p[0]) == -4
     assert f(sh=shape(dk=100)) == -3
+
+
+def bwd_call(sh=None, g_min=-5.0, chunk=16, ws_bytes=1 << 40, **over):
+    p = ptrs(16)
+    a = dict(q=p[0], k=p[1], v=p[2], w=p[3], beta=p[4], S0=None, dO=p[5], dSf=None, dq=p[6], dk=p[7],
+             dv=p[8], dw=p[9], dbeta=p[10], dS0=p[11], workspace=p[12])
+    a.update(over)
+    sh = shape() if sh is None else sh
+    return lib.kda_chunk_bwd(a["q"], a["k"], a["v"], a["w"], a["beta"], a["S0"], ctypes.c_float(g_min), chunk,
+                             ctypes.byref(sh), a["dO"], a["dSf"], a["dq"], a["dk"], a["dv"], a["dw"], a["dbeta"],
+                             a["dS0"], a["workspace"], ws_bytes, None)
+
+
+def test_bwd_workspace_bytes():
+    sh = shape(B=2, H=3, T=33, dk=64, dv=32)
+    assert lib.kda_bwd_workspace_bytes(ctypes.byref(sh), 16) == 2 * 3 * 3 * 64 * 32 * 4
+    assert lib.kda_bwd_workspace_bytes(ctypes.byref(sh), 32) == ctypes.c_size_t(-1).value
+    assert lib.kda_bwd_workspace_bytes(ctypes.byref(shape(dv=48)), 16) == ctypes.c_size_t(-1).value
+    assert lib.kda_bwd_workspace_bytes(None, 16) == ctypes.c_size_t(-1).value
+
+
+def test_bwd_validation():
+    assert bwd_call(shape(B=0)) == -2
+    assert bwd_call(shape(dk=48)) == -3
+    assert bwd_call(chunk=32) == -3
+    assert bwd_call(g_min=float("nan")) == -4
+    assert bwd_call(g_min=1.0) == -4
+    for name in ("q", "k", "v", "w", "beta", "dO", "dq", "dk", "dv", "dw", "dbeta"):
+        assert bwd_call(**{name: None}) == -1, name
+    p = ptrs(16)
+    assert bwd_call(ws_bytes=16) == -4                                      # workspace too small
+    assert bwd_call(workspace=None) == -4
+    assert bwd_call(dq=ctypes.c_void_p(p[6].value + 4)) == -4               # misaligned output
+    assert bwd_call(dk=p[6]) == -4                                          # two outputs alias
+    assert bwd_call(dv=p[5]) == -4                                          # output aliases dO
+    assert bwd_call(dS0=p[0]) == -4                                         # output aliases q
+    # T = 0 with no dS0 wanted: nothing to do, no launch, no pointers needed
+    assert bwd_call(shape(T=0), q=None, k=None, v=None, w=None, beta=None, dO=None, dq=None, dk=None, dv=None,
+                    dw=None, dbeta=None, dS0=None, workspace=None, ws_bytes=0) == 0
