@@ -11,17 +11,24 @@
 // factor exp(G_r - G_j) <= 1 (the per-position form the pages give for chunks whose reciprocal
 // factors would overflow), so the backward needs no span check and no reciprocal at all.
 //
-// Reverse mode through that chunk, given dO and dS' (one block of value columns at a time: the map
-// is linear in the adjoint, so blocks of columns contribute independently and their contributions
-// to the key-side gradients add up):
+// With W = T diag(beta) Kbar and U0 = T diag(beta) V (the WY form: U = U0 - W S) the two chains
+// through the chunks are affine and cheap:
+//   S'      = e^{Gam} S + Ktil^T (U0 - W S)                                   (forward)
+//   dS      = e^{Gam} dS' + Qbar^T dO - W^T (P^T dO + Ktil dS')                (reverse)
+// and, given S and dS' of a chunk, everything else is local to it:
 //   dU = P^T dO + Ktil dS'        dR = T^T dU        dv = diag(beta) dR
 //   dT = dU R^T  ->  dA = -T^T dT T^T (strictly lower)      dP = dO U^T (lower, diagonal included)
 //   dbeta_r = sum_d dR[r][d] E[r][d] + sum_j dA[r][j] X[r][j]
 //   X, P pair by pair -> dk, dq, dG;   dQbar = dO S^T,  dKbar = -diag(beta) dR S^T,  dKtil = U dS'^T
-//   dGam += e^{Gam} . rowsum(dS' o S) + colsum(dKtil o Ktil)
-//   dS = e^{Gam} dS' + Qbar^T dO - Kbar^T diag(beta) dR
+//   dGam = e^{Gam} . rowsum(dS' o S) + colsum(dKtil o Ktil)
 //   dg = reverse prefix of dG (+ dGam on every row),  dw = dg gate'(w)
-// The chunk's entering states come from a first pass of the same forward, kept in the workspace.
+//
+// Four launches:
+//   prep   (one workgroup per chunk)            G, X, P, T -> W, Ktil, Qbar, U0, P^T dO, e^{Gam} records
+//   state  (one per head and 16 value columns)  forward chain, stores every chunk's entering state
+//   dstate (one per head and 16 value columns)  reverse chain, stores every chunk's exit adjoint, dS0
+//   grad   (one per chunk)                      all gradients of the chunk, written once (no atomics)
+// Only the two chains are sequential, and each does two small contractions per chunk.
 #include "kda_internal.h"
 
 namespace kda {
@@ -29,25 +36,34 @@ namespace kda {
 namespace {
 
 constexpr int C = kChunk;      // 16
-constexpr int NT = 256;        // threads per workgroup
-constexpr int CS = 32;         // value columns per workgroup
 constexpr int NPAIR = C * (C + 1) / 2;
+constexpr int CH = 16;         // value columns per chain workgroup
+constexpr int kDepth = 3;      // chunks of chain operands in flight (LDS ring of kDepth + 1 slots)
+constexpr int NTP = 256;       // prep threads
+constexpr int NTG = 512;       // grad threads
+constexpr int CG = 32;         // value columns per pass of the grad kernel
 
-template <int DK>
-struct BwdShared {
-  float S[DK][CS], dS[DK][CS];
-  float q[C][DK], k[C][DK], G[C][DK];
-  float dq[C][DK], dk[C][DK], dG[C][DK];
-  float gam[DK], dgam[DK];
-  float V[C][CS], dO[C][CS], E[C][CS], R[C][CS], U[C][CS], dU[C][CS], dR[C][CS];
-  float X[C][C + 1], P[C][C + 1], T[C][C + 1], dA[C][C + 1], dP[C][C + 1], dT[C][C + 1], M[C][C + 1];
-  float beta[C];
+// Record of one chunk (fp32): W [C][dk], Ktil [C][dk], Qbar [C][dk], U0 [C][dv], Z0 = P^T dO [C][dv],
+// e^{Gam} [dk]
+__host__ __device__ __forceinline__ int64_t rec_floats(int64_t dk, int64_t dv) {
+  return 3 * C * dk + 2 * C * dv + dk;
+}
+__host__ __device__ __forceinline__ int64_t off_kt(int64_t dk) { return C * dk; }
+__host__ __device__ __forceinline__ int64_t off_qb(int64_t dk) { return 2 * C * dk; }
+__host__ __device__ __forceinline__ int64_t off_u0(int64_t dk) { return 3 * C * dk; }
+__host__ __device__ __forceinline__ int64_t off_z0(int64_t dk, int64_t dv) { return 3 * C * dk + C * dv; }
+__host__ __device__ __forceinline__ int64_t off_eg(int64_t dk, int64_t dv) { return 3 * C * dk + 2 * C * dv; }
+
+struct WsLayout {
+  float *recs, *states, *dstates;
 };
 
-__device__ __forceinline__ void pair_of(int pr, int& r, int& j) {   // pr -> (r, j), j <= r < 16
-  r = 0;
-  while ((r + 1) * (r + 2) / 2 <= pr) ++r;
-  j = pr - r * (r + 1) / 2;
+__host__ __device__ __forceinline__ WsLayout ws_layout(void* ws, int64_t BH, int64_t NC, int64_t dk, int64_t dv) {
+  WsLayout L;
+  L.recs = (float*)ws;
+  L.states = L.recs + BH * NC * rec_floats(dk, dv);
+  L.dstates = L.states + BH * NC * dk * dv;
+  return L;
 }
 
 // gate derivative d g / d w: g_min sigma (1 - sigma), or -sigma for -softplus
@@ -56,289 +72,640 @@ __device__ __forceinline__ float gate_deriv(float w, float g_min, int unbounded)
   return unbounded ? -s : g_min * s * (1.f - s);
 }
 
-// Loads chunk n (rows past the end are zero: k = q = v = beta = 0 and g = 0, which reproduces the
-// shorter last chunk exactly), forms the prefix G and Gam, then X, P (pair by pair), T, E, R, U.
-template <typename TIn, int DK>
-__device__ void chunk_forward(BwdShared<DK>& sm, const Params& p, int64_t bh, int64_t n, int d0, int dvs) {
+__device__ __forceinline__ void pair_of(int pr, int& r, int& j) {   // pr -> (r, j), j <= r < 16
+  r = 0;
+  while ((r + 1) * (r + 2) / 2 <= pr) ++r;
+  j = pr - r * (r + 1) / 2;
+}
+
+template <int DK>
+struct ChunkCore {
+  float q[C][DK], k[C][DK], G[C][DK];
+  float gam[DK];
+  float beta[C];
+  float X[C][C + 1], P[C][C + 1], T[C][C + 1];
+};
+
+// Loads chunk n (rows past the end are zero: k = q = beta = 0 and g = 0, which reproduces the
+// shorter last chunk exactly), forms the prefix G and Gam, X and P pair by pair, and T by forward
+// substitution.  Ends with a barrier.
+template <typename TIn, int DK, int NT>
+__device__ void chunk_setup(ChunkCore<DK>& cc, const Params& p, int64_t bh, int64_t n, int len) {
   const int tid = threadIdx.x;
   const int64_t T = p.T, t0 = n * C;
-  const int len = (int)((T - t0) < C ? (T - t0) : C);
-  const int dv = (int)p.dv;
   const TIn* q = (const TIn*)p.q + bh * T * DK;
   const TIn* k = (const TIn*)p.k + bh * T * DK;
   const TIn* w = (const TIn*)p.w + bh * T * DK;
-  const TIn* v = (const TIn*)p.v + bh * T * dv;
   const TIn* beta = (const TIn*)p.beta + bh * T;
   for (int i = tid; i < C * DK; i += NT) {
     const int r = i / DK, c = i % DK;
     const bool ok = r < len;
     const int64_t idx = (t0 + r) * DK + c;
-    sm.q[r][c] = ok ? load_f32(q, idx) : 0.f;
-    sm.k[r][c] = ok ? load_f32(k, idx) : 0.f;
-    sm.G[r][c] = ok ? gate_f32(load_f32(w, idx), p.g_min, p.unbounded) : 0.f;
+    cc.q[r][c] = ok ? load_f32(q, idx) : 0.f;
+    cc.k[r][c] = ok ? load_f32(k, idx) : 0.f;
+    cc.G[r][c] = ok ? gate_f32(load_f32(w, idx), p.g_min, p.unbounded) : 0.f;
   }
-  for (int i = tid; i < C * CS; i += NT) {
-    const int r = i / CS, d = i % CS;
-    sm.V[r][d] = (r < len && d < dvs) ? load_f32(v, (t0 + r) * dv + d0 + d) : 0.f;
-  }
-  if (tid < C) sm.beta[tid] = tid < len ? load_f32(beta, t0 + tid) : 0.f;
+  if (tid < C) cc.beta[tid] = tid < len ? load_f32(beta, t0 + tid) : 0.f;
   __syncthreads();
   if (tid < DK) {
     float g = 0.f;
-    for (int r = 0; r < C; ++r) { g += sm.G[r][tid]; sm.G[r][tid] = g; }
-    sm.gam[tid] = g;
+    for (int r = 0; r < C; ++r) { g += cc.G[r][tid]; cc.G[r][tid] = g; }
+    cc.gam[tid] = g;
   }
   __syncthreads();
-  // X and P, one (r, j) pair per thread over every key channel
   if (tid < NPAIR) {
     int r, j;
     pair_of(tid, r, j);
     float x = 0.f, pp = 0.f;
     for (int c = 0; c < DK; ++c) {
-      const float kj = sm.k[j][c] * expf(sm.G[r][c] - sm.G[j][c]);
-      x += sm.k[r][c] * kj;
-      pp += sm.q[r][c] * kj;
+      const float kj = cc.k[j][c] * expf(cc.G[r][c] - cc.G[j][c]);
+      x += cc.k[r][c] * kj;
+      pp += cc.q[r][c] * kj;
     }
-    sm.X[r][j] = j < r ? x : 0.f;
-    sm.P[r][j] = pp;
-    if (j < r) { sm.X[j][r] = 0.f; sm.P[j][r] = 0.f; }
+    cc.X[r][j] = j < r ? x : 0.f;
+    cc.P[r][j] = pp;
+    if (j < r) { cc.X[j][r] = 0.f; cc.P[j][r] = 0.f; }
   }
   __syncthreads();
-  // T = (I + A)^{-1}, A = diag(beta) X: forward substitution, one column per thread
-  if (tid < C) {
+  if (tid < C) {   // T = (I + diag(beta) X)^{-1}, one column per thread
     const int j = tid;
     for (int r = 0; r < C; ++r) {
       float x = (r == j) ? 1.f : 0.f;
-      for (int i = j; i < r; ++i) x -= sm.beta[r] * sm.X[r][i] * sm.T[i][j];
-      sm.T[r][j] = (r < j) ? 0.f : x;
+      for (int i = j; i < r; ++i) x -= cc.beta[r] * cc.X[r][i] * cc.T[i][j];
+      cc.T[r][j] = (r < j) ? 0.f : x;
     }
-  }
-  // E = V - Kbar S,  R = diag(beta) E
-  for (int i = tid; i < C * CS; i += NT) {
-    const int r = i / CS, d = i % CS;
-    float acc = sm.V[r][d];
-    for (int c = 0; c < DK; ++c) acc -= sm.k[r][c] * expf(sm.G[r][c]) * sm.S[c][d];
-    sm.E[r][d] = acc;
-    sm.R[r][d] = sm.beta[r] * acc;
-  }
-  __syncthreads();
-  for (int i = tid; i < C * CS; i += NT) {
-    const int r = i / CS, d = i % CS;
-    float acc = 0.f;
-    for (int j = 0; j <= r; ++j) acc += sm.T[r][j] * sm.R[j][d];
-    sm.U[r][d] = acc;
   }
   __syncthreads();
 }
+
+// ---------------------------------------------------------------- prep: one workgroup per chunk
+template <int DK>
+struct PrepShared {
+  ChunkCore<DK> cc;
+  float kb[C][DK];      // diag(beta) Kbar
+  float bv[C][128];     // diag(beta) V
+  float go[C][128];     // dO
+};
 
 template <typename TIn, int DK>
-__global__ __launch_bounds__(NT) void bwd_kernel(Params p, const void* dO_in, const float* dSf, float* dq, float* dk,
-                                                  float* dvo, float* dw, float* dbeta, float* dS0) {
-  extern __shared__ __align__(16) unsigned char smem_raw[];
-  BwdShared<DK>& sm = *reinterpret_cast<BwdShared<DK>*>(smem_raw);
+__global__ __launch_bounds__(NTP) void bwd_prep_kernel(Params p, const void* __restrict__ dO_in, float* __restrict__ recs) {
+  __shared__ PrepShared<DK> sm;
   const int tid = threadIdx.x;
+  const int64_t NC = p.n_chunks();
+  const int64_t bh = blockIdx.x / NC, n = blockIdx.x % NC;
+  const int64_t T = p.T, t0 = n * C;
+  const int len = (int)((T - t0) < C ? (T - t0) : C);
   const int dv = (int)p.dv;
-  const int nslices = dv / CS;
-  const int64_t bh = blockIdx.x / nslices;
-  const int slice = blockIdx.x % nslices;
-  const int d0 = slice * CS, dvs = CS;
-  const int64_t T = p.T, NC = p.n_chunks();
-  float* states = (float*)p.workspace + ((bh * nslices + slice) * NC) * (int64_t)(DK * CS);
+  chunk_setup<TIn, DK, NTP>(sm.cc, p, bh, n, len);
+  float* rec = recs + (bh * NC + n) * rec_floats(DK, dv);
+  const TIn* v = (const TIn*)p.v + bh * T * dv;
   const TIn* dO = (const TIn*)dO_in + bh * T * dv;
-  const TIn* w = (const TIn*)p.w + bh * T * DK;
-
-  // ---- pass 1: entering state of every chunk
-  for (int i = tid; i < DK * CS; i += NT) {
-    const int c = i / CS, d = i % CS;
-    sm.S[c][d] = p.S0 ? p.S0[(bh * DK + c) * dv + d0 + d] : 0.f;
+  for (int i = tid; i < C * DK; i += NTP) {
+    const int r = i / DK, c = i % DK;
+    const float G = sm.cc.G[r][c], eG = expf(G);
+    sm.kb[r][c] = sm.cc.beta[r] * sm.cc.k[r][c] * eG;
+    rec[off_kt(DK) + i] = sm.cc.k[r][c] * expf(sm.cc.gam[c] - G);
+    rec[off_qb(DK) + i] = sm.cc.q[r][c] * eG;
   }
+  for (int i = tid; i < C * dv; i += NTP) {
+    const int r = i / dv, d = i % dv;
+    sm.bv[r][d] = r < len ? sm.cc.beta[r] * load_f32(v, (t0 + r) * dv + d) : 0.f;
+    sm.go[r][d] = r < len ? load_f32(dO, (t0 + r) * dv + d) : 0.f;
+  }
+  if (tid < DK) rec[off_eg(DK, dv) + tid] = expf(sm.cc.gam[tid]);
   __syncthreads();
+  for (int i = tid; i < C * DK; i += NTP) {
+    const int r = i / DK, c = i % DK;
+    float acc = 0.f;
+    for (int j = 0; j <= r; ++j) acc += sm.cc.T[r][j] * sm.kb[j][c];
+    rec[i] = acc;
+  }
+  for (int i = tid; i < C * dv; i += NTP) {
+    const int r = i / dv, d = i % dv;
+    float acc = 0.f;
+    for (int j = 0; j <= r; ++j) acc += sm.cc.T[r][j] * sm.bv[j][d];
+    rec[off_u0(DK) + i] = acc;
+    float z = 0.f;
+    for (int j = r; j < C; ++j) z += sm.cc.P[j][r] * sm.go[j][d];
+    rec[off_z0(DK, dv) + i] = z;
+  }
+}
+
+// ---------------------------------------------------------------- chains
+// One workgroup per (head, 16 value columns); wavefront w holds rows 16w .. 16w + 15 of the block as
+// an fp32 matrix-core accumulator tile (lane l: rows 16w + 4(l/16) + i, i < 4, column l % 16).  Per
+// chunk: a 16 x 16 x 16 product per wavefront into LDS, a cross-wavefront sum, then the update as
+// one more product on the tile.  The K index of each 16 x 16 x 4 step is taken in the order the
+// accumulator already holds its rows (row 4(l/16) + i at step i), so the state needs no reshuffle.
+//
+// Roles: compute wavefronts do the products and store the chain's states (stores only, never
+// waited on); loader wavefronts copy each chunk's operands from its record straight into a ring of
+// LDS slots (16-byte global-to-LDS loads, kDepth chunks ahead) and wait for exactly the oldest chunk
+// in flight.  Both roles meet at two barriers per chunk.
+//
+// Operand matrices [16][dk] sit in a slot as float4 units, row r's unit c4 at r * dk/4 + (c4 ^ r % (dk/4)),
+// so that the 16 rows a matrix-core operand read touches fall on distinct LDS banks.
+//
+// States are stored in the accumulator's own order: the [dk][16] block of (head, chunk, columns
+// 16j .. 16j + 15) is contiguous, element (row 16w + 4g + i, column cl) at w*256 + i*64 + g*16 + cl.
+
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) void lds_void;
+typedef __attribute__((address_space(1))) void gbl_void;
+
+__device__ __forceinline__ f32x4 mfma4(float a, float b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
+}
+
+__device__ __forceinline__ void compiler_fence() { __atomic_signal_fence(__ATOMIC_SEQ_CST); }
+
+// barrier that waits for this wave's LDS operations only (global loads and stores stay in flight)
+__device__ __forceinline__ void lds_barrier() {
+  compiler_fence();
+  __builtin_amdgcn_s_waitcnt(0xF | (0x3 << 14) | (0x7 << 4) | (0x0 << 8));   // lgkmcnt(0)
+  __builtin_amdgcn_s_barrier();
+  compiler_fence();
+}
+
+// wait until at most N of this wave's vector-memory operations are outstanding
+template <int N>
+__device__ __forceinline__ void vm_wait() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  compiler_fence();
+  __builtin_amdgcn_s_waitcnt((N & 0xF) | ((N >> 4) << 14) | (0x7 << 4) | (0xF << 8));
+  compiler_fence();
+}
+
+// 16 bytes from global memory to LDS: lane j of the wave writes dst_base + 16 j
+__device__ __forceinline__ void dma16(const void* src, void* dst_base) {
+  __builtin_amdgcn_global_load_lds((gbl_void*)src, (lds_void*)dst_base, 16, 0, 0);
+}
+
+// blocks of one head on one XCD (consecutive block ids go round-robin over the 8 XCDs)
+__device__ __forceinline__ int64_t xcd_block(int64_t nblocks) {
+  const int64_t b = blockIdx.x;
+  return (nblocks % 8) ? b : (b % 8) * (nblocks / 8) + b / 8;
+}
+
+template <int DK>
+__device__ __forceinline__ int swz(int r, int c4) {   // float4 unit of (r, c4) in a [16][DK] matrix
+  constexpr int Q = DK / 4;
+  return r * Q + (c4 ^ (r % Q));
+}
+
+// Per-chunk slot contents (float4 units), for the two chains
+template <int DK, int NMAT, bool WITH_DO, typename TIn>
+struct ChainSlot {
+  static constexpr int Q = DK / 4;
+  static constexpr int MAT = C * Q;                               // units of one [16][DK] matrix
+  static constexpr int VEC = C * CH / 4;                          // U0 or Z0 slice, [16][16] fp32
+  static constexpr int DOU = WITH_DO ? C * CH * (int)sizeof(TIn) / 16 : 0;   // dO slice
+  static constexpr int EG = Q;                                    // e^{Gam}
+  static constexpr int UNITS = NMAT * MAT + VEC + DOU + EG;
+  static constexpr int O_VEC = NMAT * MAT, O_DO = O_VEC + VEC, O_EG = O_DO + DOU;
+  static constexpr int NI = (UNITS + 63) / 64;                    // wave instructions per chunk
+};
+
+template <int DK>
+struct ChainDims {
+  static constexpr int NW = DK / 16;          // compute wavefronts (one 16-row tile each)
+  static constexpr int NL = 4;                // loader wavefronts
+  static constexpr int NT = (NW + NL) * 64;
+};
+
+// Issues this loader wave's share of one chunk's operand copies into LDS slot `slot` (float4 units).
+// Unit u of the slot comes from: matrix rows of the record (un-swizzled), the 16 x 16 vector block
+// (U0 or Z0), the dO rows of tokens t0 .. t0 + 15 (clamped to the last token; the compute side
+// ignores rows past the end), e^{Gam}.  Every loader wave issues exactly PER instructions, one per
+// unrolled iteration, with the source chosen without branches.
+template <int DK, int NMAT, bool WITH_DO, typename TIn>
+__device__ __forceinline__ void load_slot(float4* slot, const float* rec, int64_t off_vec, int64_t off_eg,
+                                          const TIn* dO_head, int64_t t0, int64_t T, int dv, int d0, int lw,
+                                          int lane) {
+  using SL = ChainSlot<DK, NMAT, WITH_DO, TIn>;
+  constexpr int Q = SL::Q, NL = ChainDims<DK>::NL;
+  constexpr int PER = (SL::NI + NL - 1) / NL;
+  constexpr int UPR = CH * (int)sizeof(TIn) / 16;          // dO units per row
+#pragma unroll
+  for (int k = 0; k < PER; ++k) {
+    int ins = lw + k * NL;
+    if (ins >= SL::NI) ins = SL::NI - 1;       // the last instruction again: same bytes, same place
+    const int u = ins * 64 + lane;
+    const int um = u < SL::O_VEC ? u : 0;
+    const int mat = um / SL::MAT, vm = um % SL::MAT, r = vm / Q, c4 = (vm % Q) ^ (r % Q);
+    const char* s_mat = reinterpret_cast<const char*>(rec + (int64_t)mat * C * DK + r * DK + 4 * c4);
+    const int vv = min(max(u - SL::O_VEC, 0), SL::VEC - 1);
+    const char* s_vec = reinterpret_cast<const char*>(rec + off_vec + (vv / 4) * dv + d0 + 4 * (vv % 4));
+    const char* s_do = s_vec;
+    if (WITH_DO) {
+      const int vd = min(max(u - SL::O_DO, 0), (SL::DOU > 0 ? SL::DOU : 1) - 1);
+      const int64_t t = min(t0 + vd / UPR, T - 1);
+      s_do = reinterpret_cast<const char*>(dO_head + t * dv + d0) + 16 * (vd % UPR);
+    }
+    const int ve = min(max(u - SL::O_EG, 0), Q - 1);
+    const char* s_eg = reinterpret_cast<const char*>(rec + off_eg + 4 * ve);
+    const char* src = u < SL::O_VEC ? s_mat : (u < SL::O_DO ? s_vec : (u < SL::O_EG ? s_do : s_eg));
+    if (u < SL::UNITS) dma16(src, slot + ins * 64);
+  }
+}
+
+// forward chain: states[n] = S entering chunk n
+template <int DK>
+__global__ __launch_bounds__(ChainDims<DK>::NT) void bwd_state_kernel(Params p, const float* __restrict__ recs,
+                                                                     float* __restrict__ states) {
+  using Dm = ChainDims<DK>;
+  using SL = ChainSlot<DK, 2, false, float>;
+  constexpr int NW = Dm::NW, NL = Dm::NL, NCT = NW * 64, R = kDepth + 1;
+  constexpr int PER = (SL::NI + NL - 1) / NL;
+  __shared__ __align__(16) float4 ring[R][SL::UNITS];
+  __shared__ float part[NW][C][CH + 1];
+  __shared__ float Y[C][CH + 1];
+  const int tid = threadIdx.x, lane = tid % 64, w = tid / 64;
+  const bool loader = w >= NW;
+  const int dv = (int)p.dv, nsl = dv / CH;
+  const int64_t nblk = p.B * p.H * nsl, L = xcd_block(nblk);
+  const int64_t bh = L / nsl;
+  const int sl = (int)(L % nsl), d0 = sl * CH;
+  const int64_t NC = p.n_chunks();
+  const int64_t RF = rec_floats(DK, dv);
+  const float* rec_bh = recs + bh * NC * RF;
+  const int col = lane % 16, g = lane / 16;
+
+  f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+  if (!loader && p.S0) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) acc[i] = p.S0[(bh * DK + 16 * w + 4 * g + i) * dv + d0 + col];
+  }
+  auto issue = [&](int64_t m) {             // loader: chunk m (clamped) into its ring slot
+    const int64_t mc = m < NC ? m : NC - 1;
+    load_slot<DK, 2, false, float>(ring[m % R], rec_bh + mc * RF, off_u0(DK), off_eg(DK, dv), (const float*)nullptr,
+                                   0, 1, dv, d0, w - NW, lane);
+  };
+
+  if (loader) {
+#pragma unroll
+    for (int k = 0; k < kDepth; ++k) issue(k);
+    vm_wait<PER * (kDepth - 1)>();
+  }
+  lds_barrier();
   for (int64_t n = 0; n < NC; ++n) {
-    for (int i = tid; i < DK * CS; i += NT) states[n * DK * CS + i] = (&sm.S[0][0])[i];
-    chunk_forward<TIn, DK>(sm, p, bh, n, d0, dvs);
-    for (int i = tid; i < DK * CS; i += NT) {
-      const int c = i / CS, d = i % CS;
-      float acc = expf(sm.gam[c]) * sm.S[c][d];
-      for (int r = 0; r < C; ++r) acc += sm.k[r][c] * expf(sm.gam[c] - sm.G[r][c]) * sm.U[r][d];
-      sm.S[c][d] = acc;
+    const float4* sv = ring[n % R];
+    const float* sf = reinterpret_cast<const float*>(sv);
+    if (!loader) {
+      float* st = states + ((bh * NC + n) * nsl + sl) * DK * CH + w * 256 + lane;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) st[i * 64] = acc[i];
+      const float4 wv = sv[swz<DK>(col, 4 * w + g)];
+      f32x4 yp = {0.f, 0.f, 0.f, 0.f};
+      yp = mfma4(wv.x, acc[0], yp);
+      yp = mfma4(wv.y, acc[1], yp);
+      yp = mfma4(wv.z, acc[2], yp);
+      yp = mfma4(wv.w, acc[3], yp);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) part[w][4 * g + i][col] = yp[i];
     }
-    __syncthreads();
+    lds_barrier();
+    if (!loader) {
+      for (int e = tid; e < C * CH; e += NCT) {
+        const int r = e / CH, d = e % CH;
+        float y = sf[4 * SL::O_VEC + e];
+#pragma unroll
+        for (int v = 0; v < NW; ++v) y -= part[v][r][d];
+        Y[r][d] = y;
+      }
+    } else {
+      issue(n + kDepth);
+      vm_wait<PER * (kDepth - 1)>();           // chunk n + 1 has landed
+    }
+    lds_barrier();
+    if (!loader) {
+      const float* eg = sf + 4 * SL::O_EG;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) acc[i] *= eg[16 * w + 4 * g + i];
+      const float* kt = sf + 4 * SL::MAT;
+#pragma unroll
+      for (int s4 = 0; s4 < 4; ++s4) {
+        const int r = 4 * s4 + g, c = 16 * w + col;
+        acc = mfma4(kt[4 * swz<DK>(r, c / 4) + c % 4], Y[r][col], acc);
+      }
+    }
+  }
+  if (loader) vm_wait<0>();
+}
+
+// reverse chain: dstates[n] = dL/dS leaving chunk n; dS0 = dL/dS entering chunk 0
+template <typename TIn, int DK>
+__global__ __launch_bounds__(ChainDims<DK>::NT) void bwd_dstate_kernel(Params p, const void* __restrict__ dO_in,
+                                                                      const float* __restrict__ dSf,
+                                                                      const float* __restrict__ recs,
+                                                                      float* __restrict__ dstates,
+                                                                      float* __restrict__ dS0) {
+  using Dm = ChainDims<DK>;
+  using SL = ChainSlot<DK, 3, true, TIn>;
+  constexpr int NW = Dm::NW, NL = Dm::NL, NCT = NW * 64, R = kDepth + 1;
+  constexpr int PER = (SL::NI + NL - 1) / NL;
+  __shared__ __align__(16) float4 ring[R][SL::UNITS];
+  __shared__ float part[NW][C][CH + 1];
+  __shared__ float Z[C][CH + 1];
+  const int tid = threadIdx.x, lane = tid % 64, w = tid / 64;
+  const bool loader = w >= NW;
+  const int dv = (int)p.dv, nsl = dv / CH;
+  const int64_t nblk = p.B * p.H * nsl, L = xcd_block(nblk);
+  const int64_t bh = L / nsl;
+  const int sl = (int)(L % nsl), d0 = sl * CH;
+  const int64_t T = p.T, NC = p.n_chunks();
+  const int64_t RF = rec_floats(DK, dv);
+  const float* rec_bh = recs + bh * NC * RF;
+  const TIn* dO = (const TIn*)dO_in + bh * T * dv;
+  const int col = lane % 16, g = lane / 16;
+
+  f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+  if (!loader && dSf) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) acc[i] = dSf[(bh * DK + 16 * w + 4 * g + i) * dv + d0 + col];
+  }
+  auto issue = [&](int64_t it) {            // loader: step it (chunk NC - 1 - it, clamped)
+    int64_t m = NC - 1 - it;
+    if (m < 0) m = 0;
+    load_slot<DK, 3, true, TIn>(ring[it % R], rec_bh + m * RF, off_z0(DK, dv), off_eg(DK, dv), dO, m * C, T, dv, d0,
+                                w - NW, lane);
+  };
+
+  if (loader) {
+#pragma unroll
+    for (int k = 0; k < kDepth; ++k) issue(k);
+    vm_wait<PER * (kDepth - 1)>();
+  }
+  lds_barrier();
+  for (int64_t it = 0; it < NC; ++it) {
+    const int64_t n = NC - 1 - it;
+    const float4* sv = ring[it % R];
+    const float* sf = reinterpret_cast<const float*>(sv);
+    if (!loader) {
+      float* st = dstates + ((bh * NC + n) * nsl + sl) * DK * CH + w * 256 + lane;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) st[i * 64] = acc[i];
+      const float4 kv = sv[SL::MAT + swz<DK>(col, 4 * w + g)];
+      f32x4 zp = {0.f, 0.f, 0.f, 0.f};
+      zp = mfma4(kv.x, acc[0], zp);
+      zp = mfma4(kv.y, acc[1], zp);
+      zp = mfma4(kv.z, acc[2], zp);
+      zp = mfma4(kv.w, acc[3], zp);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) part[w][4 * g + i][col] = zp[i];
+    }
+    lds_barrier();
+    if (!loader) {
+      for (int e = tid; e < C * CH; e += NCT) {
+        const int r = e / CH, d = e % CH;
+        float z = sf[4 * SL::O_VEC + e];
+#pragma unroll
+        for (int v = 0; v < NW; ++v) z += part[v][r][d];
+        Z[r][d] = z;
+      }
+    } else {
+      issue(it + kDepth);
+      vm_wait<PER * (kDepth - 1)>();           // the next step's chunk has landed
+    }
+    lds_barrier();
+    if (!loader) {
+      const float* eg = sf + 4 * SL::O_EG;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) acc[i] *= eg[16 * w + 4 * g + i];
+      const float* qb = sf + 4 * 2 * SL::MAT;
+      const float* wm = sf;
+      const TIn* dOl = reinterpret_cast<const TIn*>(sv + SL::O_DO);
+      const int64_t t0 = n * C;
+#pragma unroll
+      for (int s4 = 0; s4 < 4; ++s4) {
+        const int r = 4 * s4 + g, c = 16 * w + col;
+        const float o = t0 + r < T ? load_f32(dOl, r * CH + col) : 0.f;
+        acc = mfma4(qb[4 * swz<DK>(r, c / 4) + c % 4], o, acc);
+      }
+#pragma unroll
+      for (int s4 = 0; s4 < 4; ++s4) {
+        const int r = 4 * s4 + g, c = 16 * w + col;
+        acc = mfma4(-wm[4 * swz<DK>(r, c / 4) + c % 4], Z[r][col], acc);
+      }
+    }
+  }
+  if (loader) vm_wait<0>();
+  if (dS0 && !loader) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) dS0[(bh * DK + 16 * w + 4 * g + i) * dv + d0 + col] = acc[i];
+  }
+}
+
+// ---------------------------------------------------------------- grad: one workgroup per chunk
+template <int DK>
+struct GradShared {
+  ChunkCore<DK> cc;
+  float kbar[C][DK], ktil[C][DK];
+  float dq[C][DK], dk[C][DK], dG[C][DK];
+  float S[DK][CG + 1], dS[DK][CG + 1];
+  float dO[C][CG + 1], E[C][CG + 1], U[C][CG + 1], dU[C][CG + 1], dR[C][CG + 1];
+  float dT[C][C + 1], dP[C][C + 1], M[C][C + 1];
+  float red[NTG];
+};
+
+template <typename TIn, int DK>
+__global__ __launch_bounds__(NTG) void bwd_grad_kernel(Params p, const void* __restrict__ dO_in,
+                                                      const float* __restrict__ states,
+                                                      const float* __restrict__ dstates, float* __restrict__ dq,
+                                                      float* __restrict__ dk, float* __restrict__ dvo,
+                                                      float* __restrict__ dw, float* __restrict__ dbeta) {
+  extern __shared__ __align__(16) unsigned char smem_raw[];
+  GradShared<DK>& sm = *reinterpret_cast<GradShared<DK>*>(smem_raw);
+  constexpr int EPT = C * DK / NTG;     // (r, c) elements per thread: r = tid / DK + (NTG / DK) m
+  const int tid = threadIdx.x;
+  const int64_t NC = p.n_chunks();
+  const int64_t bh = blockIdx.x / NC, n = blockIdx.x % NC;
+  const int64_t T = p.T, t0 = n * C;
+  const int len = (int)((T - t0) < C ? (T - t0) : C);
+  const int dv = (int)p.dv;
+  const TIn* v = (const TIn*)p.v + bh * T * dv;
+  const TIn* dO = (const TIn*)dO_in + bh * T * dv;
+  const float* Sg = states + (bh * NC + n) * DK * dv;      // nsl tiles of [dk][16] in stored order
+  const float* dSg = dstates + (bh * NC + n) * DK * dv;
+
+  chunk_setup<TIn, DK, NTG>(sm.cc, p, bh, n, len);
+  for (int i = tid; i < C * DK; i += NTG) {
+    const int r = i / DK, c = i % DK;
+    const float G = sm.cc.G[r][c];
+    sm.kbar[r][c] = sm.cc.k[r][c] * expf(G);
+    sm.ktil[r][c] = sm.cc.k[r][c] * expf(sm.cc.gam[c] - G);
   }
 
-  // ---- pass 2: chunks in reverse
-  for (int i = tid; i < DK * CS; i += NT) {
-    const int c = i / CS, d = i % CS;
-    sm.dS[c][d] = dSf ? dSf[(bh * DK + c) * dv + d0 + d] : 0.f;
-  }
-  for (int64_t n = NC - 1; n >= 0; --n) {
-    const int64_t t0 = n * C;
-    const int len = (int)((T - t0) < C ? (T - t0) : C);
-    for (int i = tid; i < DK * CS; i += NT) (&sm.S[0][0])[i] = states[n * DK * CS + i];
-    for (int i = tid; i < C * CS; i += NT) {
-      const int r = i / CS, d = i % CS;
-      sm.dO[r][d] = r < len ? load_f32(dO, (t0 + r) * dv + d0 + d) : 0.f;
-    }
-    for (int i = tid; i < C * DK; i += NT) {
-      (&sm.dq[0][0])[i] = 0.f;
-      (&sm.dk[0][0])[i] = 0.f;
-      (&sm.dG[0][0])[i] = 0.f;
-    }
-    if (tid < DK) sm.dgam[tid] = 0.f;
-    __syncthreads();
-    chunk_forward<TIn, DK>(sm, p, bh, n, d0, dvs);
+  float accT = 0.f, accP = 0.f, accB = 0.f, accRS = 0.f;
+  float aQ[EPT], aK[EPT], aT[EPT];
+#pragma unroll
+  for (int m = 0; m < EPT; ++m) aQ[m] = aK[m] = aT[m] = 0.f;
 
-    // dU = P^T dO + Ktil dS'
-    for (int i = tid; i < C * CS; i += NT) {
-      const int j = i / CS, d = i % CS;
-      float acc = 0.f;
-      for (int r = j; r < C; ++r) acc += sm.P[r][j] * sm.dO[r][d];
-      for (int c = 0; c < DK; ++c) acc += sm.k[j][c] * expf(sm.gam[c] - sm.G[j][c]) * sm.dS[c][d];
-      sm.dU[j][d] = acc;
+  for (int s0 = 0; s0 < dv; s0 += CG) {
+    for (int i = tid; i < DK * CG; i += NTG) {   // two [dk][16] tiles per pass, read in stored order
+      const int j = i / (DK * CH), e = i % (DK * CH);
+      const int c = 16 * (e / 256) + 4 * ((e % 64) / 16) + (e % 256) / 64, d = CH * j + e % 16;
+      const int64_t o = (int64_t)((s0 / CH + j) * DK * CH + e);
+      sm.S[c][d] = Sg[o];
+      sm.dS[c][d] = dSg[o];
     }
-    __syncthreads();
-    // dR = T^T dU, dv = diag(beta) dR
-    for (int i = tid; i < C * CS; i += NT) {
-      const int j = i / CS, d = i % CS;
-      float acc = 0.f;
-      for (int r = j; r < C; ++r) acc += sm.T[r][j] * sm.dU[r][d];
-      sm.dR[j][d] = acc;
-      if (j < len) dvo[(bh * T + t0 + j) * dv + d0 + d] = sm.beta[j] * acc;
-    }
-    __syncthreads();
-    // dT = dU R^T (lower part), dP = dO U^T (lower, diagonal included)
+    float vrd;
     {
+      const int r = tid / CG, d = tid % CG;      // C * CG = NTG
+      sm.dO[r][d] = r < len ? load_f32(dO, (t0 + r) * dv + s0 + d) : 0.f;
+      vrd = r < len ? load_f32(v, (t0 + r) * dv + s0 + d) : 0.f;
+    }
+    __syncthreads();
+    {   // E = V - Kbar S
+      const int r = tid / CG, d = tid % CG;
+      float acc = vrd;
+      for (int c = 0; c < DK; ++c) acc -= sm.kbar[r][c] * sm.S[c][d];
+      sm.E[r][d] = acc;
+    }
+    __syncthreads();
+    {   // U = T diag(beta) E;  dU = P^T dO + Ktil dS'
+      const int r = tid / CG, d = tid % CG;
+      float u = 0.f;
+      for (int j = 0; j <= r; ++j) u += sm.cc.T[r][j] * sm.cc.beta[j] * sm.E[j][d];
+      sm.U[r][d] = u;
+      float du = 0.f;
+      for (int i = r; i < C; ++i) du += sm.cc.P[i][r] * sm.dO[i][d];
+      for (int c = 0; c < DK; ++c) du += sm.ktil[r][c] * sm.dS[c][d];
+      sm.dU[r][d] = du;
+    }
+    __syncthreads();
+    {   // dR = T^T dU;  dv = diag(beta) dR
+      const int j = tid / CG, d = tid % CG;
+      float acc = 0.f;
+      for (int r = j; r < C; ++r) acc += sm.cc.T[r][j] * sm.dU[r][d];
+      sm.dR[j][d] = acc;
+      if (j < len) dvo[(bh * T + t0 + j) * dv + s0 + d] = sm.cc.beta[j] * acc;
+    }
+    __syncthreads();
+    if (tid < C * C) {   // dT = dU R^T, dP = dO U^T (lower part)
       const int r = tid / C, j = tid % C;
-      float a = 0.f, b = 0.f;
       if (j <= r) {
-        for (int d = 0; d < CS; ++d) {
-          a += sm.dU[r][d] * sm.R[j][d];
+        float a = 0.f, b = 0.f;
+        for (int d = 0; d < CG; ++d) {
+          a += sm.dU[r][d] * sm.E[j][d];
           b += sm.dO[r][d] * sm.U[j][d];
         }
+        accT += sm.cc.beta[j] * a;
+        accP += b;
       }
-      sm.dT[r][j] = j <= r ? a : 0.f;
-      sm.dP[r][j] = j <= r ? b : 0.f;
     }
-    __syncthreads();
-    // M = T^T dT, then dA = -(M T^T), strictly lower
-    {
-      const int a = tid / C, b = tid % C;
-      float acc = 0.f;
-      for (int r = 0; r < C; ++r) acc += sm.T[r][a] * sm.dT[r][b];
-      sm.M[a][b] = acc;
-    }
-    __syncthreads();
-    {
-      const int a = tid / C, b = tid % C;
-      float acc = 0.f;
-      for (int j = 0; j < C; ++j) acc += sm.M[a][j] * sm.T[b][j];
-      sm.dA[a][b] = b < a ? -acc : 0.f;
-    }
-    __syncthreads();
-    // dbeta_r = sum_d dR E + sum_j dA X (this block of columns' share)
     if (tid < C) {
-      const int r = tid;
-      float acc = 0.f;
-      for (int d = 0; d < CS; ++d) acc += sm.dR[r][d] * sm.E[r][d];
-      for (int j = 0; j < r; ++j) acc += sm.dA[r][j] * sm.X[r][j];
-      if (r < len) atomicAdd(&dbeta[bh * T + t0 + r], acc);
+      for (int d = 0; d < CG; ++d) accB += sm.dR[tid][d] * sm.E[tid][d];
     }
-    // pair-by-pair terms of X (weighted beta_r dA) and P (weighted dP): one key channel per thread,
-    // which owns column c of the gradient blocks
     if (tid < DK) {
-      const int c = tid;
-      for (int r = 0; r < C; ++r) {
-        const float kr = sm.k[r][c], qr = sm.q[r][c], Gr = sm.G[r][c];
-        for (int j = 0; j <= r; ++j) {
-          const float e = expf(Gr - sm.G[j][c]);
-          const float kj = sm.k[j][c];
-          const float wa = j < r ? sm.beta[r] * sm.dA[r][j] : 0.f;
-          const float wp = sm.dP[r][j];
-          // X: d/dk_r = k_j e, d/dk_j = k_r e, d/dG_r = k_r k_j e = -d/dG_j
-          // P: d/dq_r = k_j e, d/dk_j = q_r e, d/dG_r = q_r k_j e = -d/dG_j
-          sm.dk[r][c] += wa * kj * e;
-          sm.dk[j][c] += (wa * kr + wp * qr) * e;
-          sm.dq[r][c] += wp * kj * e;
-          const float t = (wa * kr + wp * qr) * kj * e;
-          sm.dG[r][c] += t;
-          sm.dG[j][c] -= t;
-        }
-      }
+      for (int d = 0; d < CG; ++d) accRS += sm.dS[tid][d] * sm.S[tid][d];
     }
-    __syncthreads();
-    // dQbar = dO S^T, dKbar = -diag(beta) dR S^T, dKtil = U dS'^T, through the scalings
-    for (int i = tid; i < C * DK; i += NT) {
-      const int r = i / DK, c = i % DK;
+#pragma unroll
+    for (int m = 0; m < EPT; ++m) {   // dQbar, the dR S^T part of dKbar, dKtil
+      const int r = tid / DK + (NTG / DK) * m, c = tid % DK;
       float a = 0.f, b = 0.f, t = 0.f;
-      for (int d = 0; d < CS; ++d) {
-        a += sm.dO[r][d] * sm.S[c][d];
-        b += sm.dR[r][d] * sm.S[c][d];
+      for (int d = 0; d < CG; ++d) {
+        const float sv = sm.S[c][d];
+        a += sm.dO[r][d] * sv;
+        b += sm.dR[r][d] * sv;
         t += sm.U[r][d] * sm.dS[c][d];
       }
-      const float eg = expf(sm.G[r][c]), et = expf(sm.gam[c] - sm.G[r][c]);
-      const float dKbar = -sm.beta[r] * b;
-      sm.dq[r][c] += a * eg;
-      sm.dk[r][c] += dKbar * eg + t * et;
-      sm.dG[r][c] += a * sm.q[r][c] * eg + dKbar * sm.k[r][c] * eg - t * sm.k[r][c] * et;
-    }
-    __syncthreads();
-    // dGam = e^{Gam} rowsum(dS' o S) + sum_r dKtil o Ktil
-    if (tid < DK) {
-      const int c = tid;
-      float acc = 0.f;
-      for (int d = 0; d < CS; ++d) acc += sm.dS[c][d] * sm.S[c][d];
-      acc *= expf(sm.gam[c]);
-      for (int r = 0; r < C; ++r) {
-        float t = 0.f;
-        for (int d = 0; d < CS; ++d) t += sm.U[r][d] * sm.dS[c][d];
-        acc += t * sm.k[r][c] * expf(sm.gam[c] - sm.G[r][c]);
-      }
-      sm.dgam[c] = acc;
-    }
-    __syncthreads();
-    // dS <- e^{Gam} dS' + Qbar^T dO - Kbar^T diag(beta) dR
-    for (int i = tid; i < DK * CS; i += NT) {
-      const int c = i / CS, d = i % CS;
-      float acc = expf(sm.gam[c]) * sm.dS[c][d];
-      for (int r = 0; r < C; ++r) {
-        const float eg = expf(sm.G[r][c]);
-        acc += sm.q[r][c] * eg * sm.dO[r][d] - sm.k[r][c] * eg * sm.beta[r] * sm.dR[r][d];
-      }
-      sm.dS[c][d] = acc;
-    }
-    // dg = reverse prefix of dG plus dGam; dw = dg gate'(w); this block's shares of dq, dk, dw
-    if (tid < DK) {
-      const int c = tid;
-      float acc = sm.dgam[c];
-      for (int r = C - 1; r >= 0; --r) {
-        acc += sm.dG[r][c];
-        if (r < len) {
-          const int64_t idx = (bh * T + t0 + r) * DK + c;
-          atomicAdd(&dw[idx], acc * gate_deriv(load_f32(w, idx - bh * T * DK), p.g_min, p.unbounded));
-          atomicAdd(&dq[idx], sm.dq[r][c]);
-          atomicAdd(&dk[idx], sm.dk[r][c]);
-        }
-      }
+      aQ[m] += a;
+      aK[m] += b;
+      aT[m] += t;
     }
     __syncthreads();
   }
-  if (dS0) {
-    for (int i = tid; i < DK * CS; i += NT) {
-      const int c = i / CS, d = i % CS;
-      dS0[(bh * DK + c) * dv + d0 + d] = sm.dS[c][d];
+
+  if (tid < C * C) {
+    sm.dT[tid / C][tid % C] = accT;
+    sm.dP[tid / C][tid % C] = accP;
+  }
+  __syncthreads();
+  if (tid < C * C) {   // M = T^T dT
+    const int a = tid / C, b = tid % C;
+    float acc = 0.f;
+    for (int r = 0; r < C; ++r) acc += sm.cc.T[r][a] * sm.dT[r][b];
+    sm.M[a][b] = acc;
+  }
+  __syncthreads();
+  if (tid < C * C) {   // dA = -(M T^T), strictly lower, into dT
+    const int a = tid / C, b = tid % C;
+    float acc = 0.f;
+    for (int j = 0; j < C; ++j) acc += sm.M[a][j] * sm.cc.T[b][j];
+    sm.dT[a][b] = b < a ? -acc : 0.f;
+  }
+  __syncthreads();
+  if (tid < C) {
+    const int r = tid;
+    float acc = accB;
+    for (int j = 0; j < r; ++j) acc += sm.dT[r][j] * sm.cc.X[r][j];
+    if (r < len) dbeta[bh * T + t0 + r] = acc;
+  }
+  {   // pair-by-pair terms of X (weights beta_r dA) and P (weights dP); thread (c, part) owns the rows
+      // x = part (mod NTG / DK) of channel c and sums every pair touching them
+    constexpr int NPART = NTG / DK;
+    const int c = tid % DK, part = tid / DK;
+    for (int x = part; x < C; x += NPART) {
+      const float kx = sm.cc.k[x][c], qx = sm.cc.q[x][c], Gx = sm.cc.G[x][c];
+      float dkx = 0.f, dqx = 0.f, dGx = 0.f;
+      for (int j = 0; j <= x; ++j) {      // pairs (x, j): x is the later row
+        const float e = expf(Gx - sm.cc.G[j][c]);
+        const float kj = sm.cc.k[j][c];
+        const float wa = j < x ? sm.cc.beta[x] * sm.dT[x][j] : 0.f;
+        const float wp = sm.dP[x][j];
+        dkx += wa * kj * e;
+        dqx += wp * kj * e;
+        dGx += (wa * kx + wp * qx) * kj * e;
+      }
+      for (int r = x; r < C; ++r) {       // pairs (r, x): x is the earlier row
+        const float e = expf(sm.cc.G[r][c] - Gx);
+        const float wa = x < r ? sm.cc.beta[r] * sm.dT[r][x] : 0.f;
+        const float wp = sm.dP[r][x];
+        const float f = (wa * sm.cc.k[r][c] + wp * sm.cc.q[r][c]) * e;
+        dkx += f;
+        dGx -= f * kx;
+      }
+      sm.dk[x][c] = dkx;
+      sm.dq[x][c] = dqx;
+      sm.dG[x][c] = dGx;
     }
   }
-}
-
-__global__ void fill_zero_kernel(float* __restrict__ x, int64_t n) {
-  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += (int64_t)gridDim.x * blockDim.x) x[i] = 0.f;
-}
-
-hipError_t zero(float* x, int64_t n, hipStream_t s) {
-  if (n <= 0) return hipSuccess;
-  int64_t blocks = (n + 255) / 256;
-  if (blocks > 4096) blocks = 4096;
-  hipLaunchKernelGGL(fill_zero_kernel, dim3((unsigned)blocks), dim3(256), 0, s, x, n);
-  return hipGetLastError();
+  __syncthreads();
+  {   // scalings of Qbar, Kbar, Ktil
+    const int c = tid % DK;
+    float red = 0.f;
+#pragma unroll
+    for (int m = 0; m < EPT; ++m) {
+      const int r = tid / DK + (NTG / DK) * m;
+      const float G = sm.cc.G[r][c];
+      const float eg = expf(G), et = expf(sm.cc.gam[c] - G);
+      const float dKbar = -sm.cc.beta[r] * aK[m];
+      const float kr = sm.cc.k[r][c];
+      sm.dq[r][c] += aQ[m] * eg;
+      sm.dk[r][c] += dKbar * eg + aT[m] * et;
+      sm.dG[r][c] += aQ[m] * sm.cc.q[r][c] * eg + dKbar * kr * eg - aT[m] * kr * et;
+      red += aT[m] * kr * et;
+    }
+    sm.red[tid] = red;
+  }
+  __syncthreads();
+  if (tid < DK) {   // dGam, reverse prefix, outputs
+    const int c = tid;
+    float acc = expf(sm.cc.gam[c]) * accRS;
+    for (int g = 0; g < NTG / DK; ++g) acc += sm.red[g * DK + c];
+    const TIn* w = (const TIn*)p.w + bh * T * DK;
+    for (int r = C - 1; r >= 0; --r) {
+      acc += sm.dG[r][c];
+      if (r < len) {
+        const int64_t idx = (t0 + r) * DK + c;
+        const int64_t o = bh * T * DK + idx;
+        dw[o] = acc * gate_deriv(load_f32(w, idx), p.g_min, p.unbounded);
+        dq[o] = sm.dq[r][c];
+        dk[o] = sm.dk[r][c];
+      }
+    }
+  }
 }
 
 template <typename TIn, int DK>
@@ -346,14 +713,25 @@ hipError_t launch_bwd_dk(const BwdParams& b, hipStream_t s) {
   const Params& p = b.p;
   static bool attr_set = false;
   if (!attr_set) {
-    hipError_t e = hipFuncSetAttribute((const void*)bwd_kernel<TIn, DK>, hipFuncAttributeMaxDynamicSharedMemorySize,
-                                       (int)sizeof(BwdShared<DK>));
+    hipError_t e = hipFuncSetAttribute((const void*)bwd_grad_kernel<TIn, DK>,
+                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)sizeof(GradShared<DK>));
     if (e != hipSuccess) return e;
     attr_set = true;
   }
-  const unsigned grid = (unsigned)(p.B * p.H * (p.dv / CS));
-  hipLaunchKernelGGL((bwd_kernel<TIn, DK>), dim3(grid), dim3(NT), sizeof(BwdShared<DK>), s, p, b.dO, b.dSf, b.dq,
-                     b.dk, b.dv, b.dw, b.dbeta, b.dS0);
+  const int64_t BH = p.B * p.H, NC = p.n_chunks();
+  const WsLayout L = ws_layout(p.workspace, BH, NC, p.dk, p.dv);
+  const unsigned nchunks = (unsigned)(BH * NC), nchain = (unsigned)(BH * (p.dv / CH));
+  hipLaunchKernelGGL((bwd_prep_kernel<TIn, DK>), dim3(nchunks), dim3(NTP), 0, s, p, b.dO, L.recs);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL((bwd_state_kernel<DK>), dim3(nchain), dim3(ChainDims<DK>::NT), 0, s, p, (const float*)L.recs,
+                     L.states);
+  if ((e = hipGetLastError()) != hipSuccess) return e;
+  hipLaunchKernelGGL((bwd_dstate_kernel<TIn, DK>), dim3(nchain), dim3(ChainDims<DK>::NT), 0, s, p, b.dO, b.dSf,
+                     (const float*)L.recs, L.dstates, b.dS0);
+  if ((e = hipGetLastError()) != hipSuccess) return e;
+  hipLaunchKernelGGL((bwd_grad_kernel<TIn, DK>), dim3(nchunks), dim3(NTG), sizeof(GradShared<DK>), s, p, b.dO,
+                     (const float*)L.states, (const float*)L.dstates, b.dq, b.dk, b.dv, b.dw, b.dbeta);
   return hipGetLastError();
 }
 
@@ -370,18 +748,11 @@ hipError_t launch_bwd_t(const BwdParams& b, hipStream_t s) {
 
 size_t bwd_workspace_bytes(int64_t B, int64_t H, int64_t T, int64_t dk, int64_t dv) {
   const int64_t NC = (T + C - 1) / C;
-  return (size_t)(B * H * NC * dk * dv) * sizeof(float);
+  return (size_t)(B * H * NC * (rec_floats(dk, dv) + 2 * dk * dv)) * sizeof(float);
 }
 
 hipError_t launch_bwd(const BwdParams& b, hipStream_t s) {
-  const Params& p = b.p;
-  hipError_t e;
-  const int64_t nk = p.B * p.H * p.T * p.dk;
-  if ((e = zero(b.dq, nk, s)) != hipSuccess) return e;
-  if ((e = zero(b.dk, nk, s)) != hipSuccess) return e;
-  if ((e = zero(b.dw, nk, s)) != hipSuccess) return e;
-  if ((e = zero(b.dbeta, p.B * p.H * p.T, s)) != hipSuccess) return e;
-  return p.dtype == KDA_DTYPE_BF16 ? launch_bwd_t<uint16_t>(b, s) : launch_bwd_t<float>(b, s);
+  return b.p.dtype == KDA_DTYPE_BF16 ? launch_bwd_t<uint16_t>(b, s) : launch_bwd_t<float>(b, s);
 }
 
 }  // namespace kda

@@ -192,7 +192,8 @@ def bwd_call(sh=None, g_min=-5.0, chunk=16, ws_bytes=1 << 40, **over):
 
 def test_bwd_workspace_bytes():
     sh = shape(B=2, H=3, T=33, dk=64, dv=32)
-    assert lib.kda_bwd_workspace_bytes(ctypes.byref(sh), 16) == 2 * 3 * 3 * 64 * 32 * 4
+    rec = 3 * 16 * 64 + 2 * 16 * 32 + 64                # per chunk: W, Ktil, Qbar, U0, P^T dO, e^Gam
+    assert lib.kda_bwd_workspace_bytes(ctypes.byref(sh), 16) == 2 * 3 * 3 * (rec + 2 * 64 * 32) * 4
     assert lib.kda_bwd_workspace_bytes(ctypes.byref(sh), 32) == ctypes.c_size_t(-1).value
     assert lib.kda_bwd_workspace_bytes(ctypes.byref(shape(dv=48)), 16) == ctypes.c_size_t(-1).value
     assert lib.kda_bwd_workspace_bytes(None, 16) == ctypes.c_size_t(-1).value
