@@ -39,9 +39,8 @@ constexpr int C = kChunk;      // 16
 constexpr int NPAIR = C * (C + 1) / 2;
 constexpr int CH = 16;         // value columns per chain workgroup
 constexpr int kDepth = 3;      // chunks of chain operands in flight (LDS ring of kDepth + 1 slots)
-constexpr int NTP = 256;       // prep threads
+constexpr int NTP = 512;       // prep threads
 constexpr int NTG = 512;       // grad threads
-constexpr int CG = 32;         // value columns per pass of the grad kernel
 
 // Record of one chunk (fp32): W [C][dk], Ktil [C][dk], Qbar [C][dk], U0 [C][dv], Z0 = P^T dO [C][dv],
 // e^{Gam} [dk]
@@ -66,9 +65,14 @@ __host__ __device__ __forceinline__ WsLayout ws_layout(void* ws, int64_t BH, int
   return L;
 }
 
+constexpr float kLog2eB = 1.4426950408889634f;
+
+// 2^x on the transcendental unit (one instruction; exponents here are <= 0 or small)
+__device__ __forceinline__ float ex2(float x) { return __builtin_amdgcn_exp2f(x); }
+
 // gate derivative d g / d w: g_min sigma (1 - sigma), or -sigma for -softplus
 __device__ __forceinline__ float gate_deriv(float w, float g_min, int unbounded) {
-  const float s = 1.f / (1.f + expf(-w));
+  const float s = __builtin_amdgcn_rcpf(1.f + ex2(-w * kLog2eB));
   return unbounded ? -s : g_min * s * (1.f - s);
 }
 
@@ -78,61 +82,110 @@ __device__ __forceinline__ void pair_of(int pr, int& r, int& j) {   // pr -> (r,
   j = pr - r * (r + 1) / 2;
 }
 
+// G and gam are kept in log2 units (G * log2 e), so that every factor e^{G...} is one exp2; the
+// gradients stay with respect to the natural-unit G.  Rows are padded by one float so that reads of
+// one channel across rows fall on distinct LDS banks.
 template <int DK>
 struct ChunkCore {
-  float q[C][DK], k[C][DK], G[C][DK];
+  float q[C][DK + 1], k[C][DK + 1], G[C][DK + 1];
   float gam[DK];
   float beta[C];
-  float X[C][C + 1], P[C][C + 1], T[C][C + 1];
+  float X[C][C + 1], P[C][C + 1], T[C][C + 1], Tb[C][C + 1];   // Tb = T diag(beta)
 };
 
 // Loads chunk n (rows past the end are zero: k = q = beta = 0 and g = 0, which reproduces the
-// shorter last chunk exactly), forms the prefix G and Gam, X and P pair by pair, and T by forward
-// substitution.  Ends with a barrier.
+// shorter last chunk exactly), forms the prefix G and Gam, X and P pair by pair (each pair's sums
+// split over four quarters of the key channels, partial sums through `scratch`, 2 * 4 * 256 floats),
+// and T by forward substitution (one column per thread, held in registers).  Ends with a barrier.
 template <typename TIn, int DK, int NT>
-__device__ void chunk_setup(ChunkCore<DK>& cc, const Params& p, int64_t bh, int64_t n, int len) {
+__device__ void chunk_setup(ChunkCore<DK>& cc, float* scratch, const Params& p, int64_t bh, int64_t n, int len) {
+  constexpr int NQ = NT >= 4 * NPAIR ? 4 : (NT >= 3 * NPAIR ? 3 : (NT >= 2 * NPAIR ? 2 : 1));   // channel groups
   const int tid = threadIdx.x;
   const int64_t T = p.T, t0 = n * C;
   const TIn* q = (const TIn*)p.q + bh * T * DK;
   const TIn* k = (const TIn*)p.k + bh * T * DK;
   const TIn* w = (const TIn*)p.w + bh * T * DK;
   const TIn* beta = (const TIn*)p.beta + bh * T;
-  for (int i = tid; i < C * DK; i += NT) {
-    const int r = i / DK, c = i % DK;
-    const bool ok = r < len;
-    const int64_t idx = (t0 + r) * DK + c;
-    cc.q[r][c] = ok ? load_f32(q, idx) : 0.f;
-    cc.k[r][c] = ok ? load_f32(k, idx) : 0.f;
-    cc.G[r][c] = ok ? gate_f32(load_f32(w, idx), p.g_min, p.unbounded) : 0.f;
+  {   // every load issued before the first use (one memory latency, not one per element)
+    constexpr int PER = (C * DK + NT - 1) / NT;
+    float lq[PER], lk[PER], lw[PER];
+#pragma unroll
+    for (int m = 0; m < PER; ++m) {
+      const int i = tid + m * NT;
+      const int r = i / DK, c = i % DK;
+      const bool ok = i < C * DK && r < len;
+      const int64_t idx = ok ? (t0 + r) * DK + c : 0;
+      lq[m] = ok ? load_f32(q, idx) : 0.f;
+      lk[m] = ok ? load_f32(k, idx) : 0.f;
+      lw[m] = ok ? load_f32(w, idx) : 0.f;
+    }
+    const float lb = (tid < C && tid < len) ? load_f32(beta, t0 + tid) : 0.f;
+#pragma unroll
+    for (int m = 0; m < PER; ++m) {
+      const int i = tid + m * NT;
+      if (i < C * DK) {
+        const int r = i / DK, c = i % DK;
+        cc.q[r][c] = lq[m];
+        cc.k[r][c] = lk[m];
+        cc.G[r][c] = r < len ? gate_f32(lw[m], p.g_min, p.unbounded) * kLog2eB : 0.f;
+      }
+    }
+    if (tid < C) cc.beta[tid] = lb;
   }
-  if (tid < C) cc.beta[tid] = tid < len ? load_f32(beta, t0 + tid) : 0.f;
   __syncthreads();
   if (tid < DK) {
+    float gv[C];
+#pragma unroll
+    for (int r = 0; r < C; ++r) gv[r] = cc.G[r][tid];
     float g = 0.f;
-    for (int r = 0; r < C; ++r) { g += cc.G[r][tid]; cc.G[r][tid] = g; }
+#pragma unroll
+    for (int r = 0; r < C; ++r) { g += gv[r]; cc.G[r][tid] = g; }
     cc.gam[tid] = g;
   }
   __syncthreads();
-  if (tid < NPAIR) {
+  float (*xs)[C][C] = reinterpret_cast<float (*)[C][C]>(scratch);              // [NQ][C][C]
+  float (*ps)[C][C] = reinterpret_cast<float (*)[C][C]>(scratch + 4 * C * C);
+  for (int task = tid; task < NPAIR * NQ; task += NT) {
+    const int pr = task % NPAIR, qq = task / NPAIR;
     int r, j;
-    pair_of(tid, r, j);
+    pair_of(pr, r, j);
     float x = 0.f, pp = 0.f;
-    for (int c = 0; c < DK; ++c) {
-      const float kj = cc.k[j][c] * expf(cc.G[r][c] - cc.G[j][c]);
+#pragma unroll 8
+    for (int c = qq; c < DK; c += NQ) {
+      const float kj = cc.k[j][c] * ex2(cc.G[r][c] - cc.G[j][c]);
       x += cc.k[r][c] * kj;
       pp += cc.q[r][c] * kj;
     }
-    cc.X[r][j] = j < r ? x : 0.f;
-    cc.P[r][j] = pp;
-    if (j < r) { cc.X[j][r] = 0.f; cc.P[j][r] = 0.f; }
+    xs[qq][r][j] = x;
+    ps[qq][r][j] = pp;
   }
   __syncthreads();
-  if (tid < C) {   // T = (I + diag(beta) X)^{-1}, one column per thread
+  if (tid < C * C) {
+    const int r = tid / C, j = tid % C;
+    float x = 0.f, pp = 0.f;
+    if (j <= r) {
+#pragma unroll
+      for (int qq = 0; qq < NQ; ++qq) { x += xs[qq][r][j]; pp += ps[qq][r][j]; }
+    }
+    cc.X[r][j] = j < r ? x : 0.f;
+    cc.P[r][j] = pp;
+  }
+  __syncthreads();
+  if (tid < C) {   // T = (I + diag(beta) X)^{-1}, column j
     const int j = tid;
+    float tc[C];
+#pragma unroll
     for (int r = 0; r < C; ++r) {
       float x = (r == j) ? 1.f : 0.f;
-      for (int i = j; i < r; ++i) x -= cc.beta[r] * cc.X[r][i] * cc.T[i][j];
-      cc.T[r][j] = (r < j) ? 0.f : x;
+      const float br = cc.beta[r];
+#pragma unroll
+      for (int i = 0; i < r; ++i) x -= br * cc.X[r][i] * tc[i];   // tc[i] = 0 for i < j
+      tc[r] = (r < j) ? 0.f : x;
+    }
+#pragma unroll
+    for (int r = 0; r < C; ++r) {
+      cc.T[r][j] = tc[r];
+      cc.Tb[r][j] = tc[r] * cc.beta[j];
     }
   }
   __syncthreads();
@@ -156,23 +209,37 @@ __global__ __launch_bounds__(NTP) void bwd_prep_kernel(Params p, const void* __r
   const int64_t T = p.T, t0 = n * C;
   const int len = (int)((T - t0) < C ? (T - t0) : C);
   const int dv = (int)p.dv;
-  chunk_setup<TIn, DK, NTP>(sm.cc, p, bh, n, len);
+  chunk_setup<TIn, DK, NTP>(sm.cc, &sm.bv[0][0], p, bh, n, len);   // bv, go: 2 * 4 * 256 floats of scratch
   float* rec = recs + (bh * NC + n) * rec_floats(DK, dv);
   const TIn* v = (const TIn*)p.v + bh * T * dv;
   const TIn* dO = (const TIn*)dO_in + bh * T * dv;
   for (int i = tid; i < C * DK; i += NTP) {
     const int r = i / DK, c = i % DK;
-    const float G = sm.cc.G[r][c], eG = expf(G);
+    const float G = sm.cc.G[r][c], eG = ex2(G);
     sm.kb[r][c] = sm.cc.beta[r] * sm.cc.k[r][c] * eG;
-    rec[off_kt(DK) + i] = sm.cc.k[r][c] * expf(sm.cc.gam[c] - G);
+    rec[off_kt(DK) + i] = sm.cc.k[r][c] * ex2(sm.cc.gam[c] - G);
     rec[off_qb(DK) + i] = sm.cc.q[r][c] * eG;
   }
-  for (int i = tid; i < C * dv; i += NTP) {
-    const int r = i / dv, d = i % dv;
-    sm.bv[r][d] = r < len ? sm.cc.beta[r] * load_f32(v, (t0 + r) * dv + d) : 0.f;
-    sm.go[r][d] = r < len ? load_f32(dO, (t0 + r) * dv + d) : 0.f;
+  {
+    constexpr int PER = C * 128 / NTP;        // dv <= 128
+    float lv[PER], lo[PER];
+#pragma unroll
+    for (int m = 0; m < PER; ++m) {
+      const int i = tid + m * NTP, r = i / dv, d = i % dv;
+      const bool ok = i < C * dv && r < len;
+      lv[m] = ok ? load_f32(v, (t0 + r) * dv + d) : 0.f;
+      lo[m] = ok ? load_f32(dO, (t0 + r) * dv + d) : 0.f;
+    }
+#pragma unroll
+    for (int m = 0; m < PER; ++m) {
+      const int i = tid + m * NTP, r = i / dv, d = i % dv;
+      if (i < C * dv) {
+        sm.bv[r][d] = sm.cc.beta[r] * lv[m];
+        sm.go[r][d] = lo[m];
+      }
+    }
   }
-  if (tid < DK) rec[off_eg(DK, dv) + tid] = expf(sm.cc.gam[tid]);
+  if (tid < DK) rec[off_eg(DK, dv) + tid] = ex2(sm.cc.gam[tid]);
   __syncthreads();
   for (int i = tid; i < C * DK; i += NTP) {
     const int r = i / DK, c = i % DK;
@@ -497,212 +564,310 @@ __global__ __launch_bounds__(ChainDims<DK>::NT) void bwd_dstate_kernel(Params p,
 }
 
 // ---------------------------------------------------------------- grad: one workgroup per chunk
+// The chunk's value columns are taken one 16-column tile at a time (the stored [dk][16] blocks of
+// S and dS', copied into LDS one tile ahead).  Per tile, on the fp32 matrix cores:
+//   E = V - Kbar S and Ktil dS' (K = dk, split over the wavefronts, partial sums through LDS)
+//   dQbar += dO S^T, dKbar' += dR S^T, dKtil += U dS'^T (K = 16; one (product, 16-key block) task per
+//   wavefront slot, accumulated over the tiles in registers)
+// and on the vector ALUs the 16 x 16 blocks U = T diag(beta) E, dU = Ktil dS' + P^T dO, dR = T^T dU,
+// dv, and the tile's shares of dT, dP, dbeta and rowsum(dS' o S).
 template <int DK>
 struct GradShared {
   ChunkCore<DK> cc;
-  float kbar[C][DK], ktil[C][DK];
-  float dq[C][DK], dk[C][DK], dG[C][DK];
-  float S[DK][CG + 1], dS[DK][CG + 1];
-  float dO[C][CG + 1], E[C][CG + 1], U[C][CG + 1], dU[C][CG + 1], dR[C][CG + 1];
+  union {
+    float tile[2][2][DK * CH];            // [buffer][S, dS'] tiles in stored order, during the tile loop
+    float g3[3][C][DK];                   // dq, dk, dG after it
+  } u;
+  union {
+    float part[8][C][CH];                 // partial E (0..3) and Ktil dS' (4..7) of the tile; the
+                                          // setup's partial pair sums before the tile loop
+    float dgk[DK];                        // sum_r dKtil o Ktil, after the tile loop
+  } v;
+  static_assert(sizeof(float) * 8 * C * CH >= sizeof(float) * 2 * 4 * C * C, "setup scratch");
+  float dO[C][CH + 4], E[C][CH + 4], U[C][CH + 4], dU[C][CH + 4], dR[C][CH + 4];
   float dT[C][C + 1], dP[C][C + 1], M[C][C + 1];
-  float red[NTG];
 };
 
 template <typename TIn, int DK>
-__global__ __launch_bounds__(NTG) void bwd_grad_kernel(Params p, const void* __restrict__ dO_in,
+__global__ __launch_bounds__(NTG) __attribute__((amdgpu_waves_per_eu(4, 4))) void bwd_grad_kernel(Params p, const void* __restrict__ dO_in,
                                                       const float* __restrict__ states,
                                                       const float* __restrict__ dstates, float* __restrict__ dq,
                                                       float* __restrict__ dk, float* __restrict__ dvo,
                                                       float* __restrict__ dw, float* __restrict__ dbeta) {
   extern __shared__ __align__(16) unsigned char smem_raw[];
   GradShared<DK>& sm = *reinterpret_cast<GradShared<DK>*>(smem_raw);
-  constexpr int EPT = C * DK / NTG;     // (r, c) elements per thread: r = tid / DK + (NTG / DK) m
-  const int tid = threadIdx.x;
+  constexpr int NCB = DK / 16;                  // 16-key blocks
+  constexpr int NTASK = 3 * NCB;                // (product, key block) tasks of the K = 16 products
+  constexpr int NI = 8 * DK / 64;               // wave instructions to copy one S + dS' tile pair
+  const int tid = threadIdx.x, lane = tid % 64, w = tid / 64, col = lane % 16, g = lane / 16;
   const int64_t NC = p.n_chunks();
   const int64_t bh = blockIdx.x / NC, n = blockIdx.x % NC;
   const int64_t T = p.T, t0 = n * C;
   const int len = (int)((T - t0) < C ? (T - t0) : C);
-  const int dv = (int)p.dv;
+  const int dv = (int)p.dv, nsl = dv / CH;
   const TIn* v = (const TIn*)p.v + bh * T * dv;
   const TIn* dO = (const TIn*)dO_in + bh * T * dv;
-  const float* Sg = states + (bh * NC + n) * DK * dv;      // nsl tiles of [dk][16] in stored order
+  const float* Sg = states + (bh * NC + n) * DK * dv;      // nsl [dk][16] blocks in stored order
   const float* dSg = dstates + (bh * NC + n) * DK * dv;
 
-  chunk_setup<TIn, DK, NTG>(sm.cc, p, bh, n, len);
-  for (int i = tid; i < C * DK; i += NTG) {
-    const int r = i / DK, c = i % DK;
-    const float G = sm.cc.G[r][c];
-    sm.kbar[r][c] = sm.cc.k[r][c] * expf(G);
-    sm.ktil[r][c] = sm.cc.k[r][c] * expf(sm.cc.gam[c] - G);
+  auto copy_tile = [&](int t, int b) {          // S and dS' tiles t into buffer b
+    float4* dst = reinterpret_cast<float4*>(sm.u.tile[b][0]);
+    for (int ins = w; ins < NI; ins += NTG / 64) {
+      const int u = ins * 64 + lane;            // < 8 DK: first 4 DK units from S, the rest from dS'
+      const float* src = (u < 4 * DK ? Sg : dSg) + (int64_t)t * DK * CH + 4 * (u % (4 * DK));
+      dma16(src, dst + ins * 64);
+    }
+  };
+  copy_tile(0, 0);
+  // V and dO of every tile, element (er, ed) of each (threads < 256), loaded before the setup
+  const int er = (tid % 256) / CH, ed = tid % CH;   // element (row, column) of a 16 x 16 tile
+  constexpr int MAXT = 128 / CH;
+  float vr[MAXT], orr[MAXT], dvr[MAXT];
+#pragma unroll
+  for (int t = 0; t < MAXT; ++t) {
+    vr[t] = orr[t] = dvr[t] = 0.f;
+    if (tid < 256 && t < nsl && er < len) {
+      vr[t] = load_f32(v, (t0 + er) * dv + CH * t + ed);
+      orr[t] = load_f32(dO, (t0 + er) * dv + CH * t + ed);
+    }
+  }
+  chunk_setup<TIn, DK, NTG>(sm.cc, &sm.v.part[0][0][0], p, bh, n, len);   // part: 2 * 4 * 256 floats
+
+  // A operands of the K = dk products: wavefronts 0..3 take Kbar, 4..7 Ktil, on key blocks wq, wq + 4
+  const bool eW = w < 4;
+  const int wq = w % 4;
+  float a1[2][4];
+#pragma unroll
+  for (int b = 0; b < 2; ++b) {
+    const int cb = wq + 4 * b;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      a1[b][i] = 0.f;
+      if (cb < NCB) {
+        const int c = 16 * cb + 4 * g + i;
+        const float G = sm.cc.G[col][c];
+        a1[b][i] = sm.cc.k[col][c] * ex2(eW ? G : sm.cc.gam[c] - G);
+      }
+    }
   }
 
-  float accT = 0.f, accP = 0.f, accB = 0.f, accRS = 0.f;
-  float aQ[EPT], aK[EPT], aT[EPT];
+  f32x4 tacc[3];
 #pragma unroll
-  for (int m = 0; m < EPT; ++m) aQ[m] = aK[m] = aT[m] = 0.f;
+  for (int j = 0; j < 3; ++j) tacc[j] = f32x4{0.f, 0.f, 0.f, 0.f};
+  float accT = 0.f, accB = 0.f, accRS = 0.f;
 
-  for (int s0 = 0; s0 < dv; s0 += CG) {
-    for (int i = tid; i < DK * CG; i += NTG) {   // two [dk][16] tiles per pass, read in stored order
-      const int j = i / (DK * CH), e = i % (DK * CH);
-      const int c = 16 * (e / 256) + 4 * ((e % 64) / 16) + (e % 256) / 64, d = CH * j + e % 16;
-      const int64_t o = (int64_t)((s0 / CH + j) * DK * CH + e);
-      sm.S[c][d] = Sg[o];
-      sm.dS[c][d] = dSg[o];
-    }
-    float vrd;
-    {
-      const int r = tid / CG, d = tid % CG;      // C * CG = NTG
-      sm.dO[r][d] = r < len ? load_f32(dO, (t0 + r) * dv + s0 + d) : 0.f;
-      vrd = r < len ? load_f32(v, (t0 + r) * dv + s0 + d) : 0.f;
-    }
-    __syncthreads();
-    {   // E = V - Kbar S
-      const int r = tid / CG, d = tid % CG;
-      float acc = vrd;
-      for (int c = 0; c < DK; ++c) acc -= sm.kbar[r][c] * sm.S[c][d];
-      sm.E[r][d] = acc;
-    }
-    __syncthreads();
-    {   // U = T diag(beta) E;  dU = P^T dO + Ktil dS'
-      const int r = tid / CG, d = tid % CG;
-      float u = 0.f;
-      for (int j = 0; j <= r; ++j) u += sm.cc.T[r][j] * sm.cc.beta[j] * sm.E[j][d];
-      sm.U[r][d] = u;
-      float du = 0.f;
-      for (int i = r; i < C; ++i) du += sm.cc.P[i][r] * sm.dO[i][d];
-      for (int c = 0; c < DK; ++c) du += sm.ktil[r][c] * sm.dS[c][d];
-      sm.dU[r][d] = du;
-    }
-    __syncthreads();
-    {   // dR = T^T dU;  dv = diag(beta) dR
-      const int j = tid / CG, d = tid % CG;
-      float acc = 0.f;
-      for (int r = j; r < C; ++r) acc += sm.cc.T[r][j] * sm.dU[r][d];
-      sm.dR[j][d] = acc;
-      if (j < len) dvo[(bh * T + t0 + j) * dv + s0 + d] = sm.cc.beta[j] * acc;
-    }
-    __syncthreads();
-    if (tid < C * C) {   // dT = dU R^T, dP = dO U^T (lower part)
-      const int r = tid / C, j = tid % C;
-      if (j <= r) {
-        float a = 0.f, b = 0.f;
-        for (int d = 0; d < CG; ++d) {
-          a += sm.dU[r][d] * sm.E[j][d];
-          b += sm.dO[r][d] * sm.U[j][d];
+  vm_wait<0>();
+  lds_barrier();
+#pragma unroll
+  for (int t = 0; t < MAXT; ++t) {
+    if (t >= nsl) break;
+    const int b = t & 1;
+    const float* St = sm.u.tile[b][0];
+    const float* dSt = sm.u.tile[b][1];
+    if (t + 1 < nsl) copy_tile(t + 1, b ^ 1);
+    const float vrd = vr[t];
+    if (tid < 256) sm.dO[er][ed] = orr[t];
+    {   // partial E (Kbar S) or Ktil dS' over this wavefront's key blocks
+      const float* B = eW ? St : dSt;
+      f32x4 pp = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int bb = 0; bb < 2; ++bb) {
+        const int cb = wq + 4 * bb;
+        if (cb < NCB) {
+#pragma unroll
+          for (int i = 0; i < 4; ++i) pp = mfma4(a1[bb][i], B[cb * 256 + i * 64 + lane], pp);
         }
-        accT += sm.cc.beta[j] * a;
-        accP += b;
       }
-    }
-    if (tid < C) {
-      for (int d = 0; d < CG; ++d) accB += sm.dR[tid][d] * sm.E[tid][d];
-    }
-    if (tid < DK) {
-      for (int d = 0; d < CG; ++d) accRS += sm.dS[tid][d] * sm.S[tid][d];
-    }
 #pragma unroll
-    for (int m = 0; m < EPT; ++m) {   // dQbar, the dR S^T part of dKbar, dKtil
-      const int r = tid / DK + (NTG / DK) * m, c = tid % DK;
-      float a = 0.f, b = 0.f, t = 0.f;
-      for (int d = 0; d < CG; ++d) {
-        const float sv = sm.S[c][d];
-        a += sm.dO[r][d] * sv;
-        b += sm.dR[r][d] * sv;
-        t += sm.U[r][d] * sm.dS[c][d];
-      }
-      aQ[m] += a;
-      aK[m] += b;
-      aT[m] += t;
+      for (int i = 0; i < 4; ++i) sm.v.part[w][4 * g + i][col] = pp[i];
     }
-    __syncthreads();
+    lds_barrier();
+    if (tid < 256) {   // E = V - Kbar S;  dU = Ktil dS' + P^T dO
+      float e = vrd, du = 0.f;
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        e -= sm.v.part[q][er][ed];
+        du += sm.v.part[4 + q][er][ed];
+      }
+#pragma unroll
+      for (int i = 0; i < C; ++i) du += sm.cc.P[i][er] * sm.dO[i][ed];   // P[i][er] = 0 for i < er
+      sm.E[er][ed] = e;
+      sm.dU[er][ed] = du;
+    }
+    lds_barrier();
+    if (tid < 256) {   // U = T diag(beta) E;  dR = T^T dU;  dv = diag(beta) dR
+      float u = 0.f, dr = 0.f;     // T is lower triangular (zeros above the diagonal)
+#pragma unroll
+      for (int j = 0; j < C; ++j) {
+        u += sm.cc.Tb[er][j] * sm.E[j][ed];
+        dr += sm.cc.T[j][er] * sm.dU[j][ed];
+      }
+      sm.U[er][ed] = u;
+      sm.dR[er][ed] = dr;
+      dvr[t] = sm.cc.beta[er] * dr;
+    }
+    lds_barrier();
+    // K = 16 products: task id = w + 8 j -> (product id / NCB, key block id % NCB)
+#pragma unroll
+    for (int j = 0; j < 3; ++j) {
+      const int id = w + 8 * j;
+      if (id < NTASK) {
+        const int pr = id / NCB, cb = id % NCB;
+        const float(*A)[CH + 4] = pr == 0 ? sm.dO : (pr == 1 ? sm.dR : sm.U);
+        const float4 av = *reinterpret_cast<const float4*>(&A[col][4 * g]);
+        const float4 bv = *reinterpret_cast<const float4*>(&(pr == 2 ? dSt : St)[cb * 256 + (col % 4) * 64 + (col / 4) * 16 + 4 * g]);
+        tacc[j] = mfma4(av.x, bv.x, tacc[j]);
+        tacc[j] = mfma4(av.y, bv.y, tacc[j]);
+        tacc[j] = mfma4(av.z, bv.z, tacc[j]);
+        tacc[j] = mfma4(av.w, bv.w, tacc[j]);
+      }
+    }
+    if (tid < 256) {   // dT += dU R^T (lower part)
+      const int r = er, jj = ed;
+      if (jj <= r) {
+        float a = 0.f;
+#pragma unroll
+        for (int d = 0; d < CH; ++d) a += sm.dU[r][d] * sm.E[jj][d];
+        accT += sm.cc.beta[jj] * a;
+      }
+    } else {           // dP += dO U^T (lower part, diagonal included)
+      const int r = er, jj = ed;
+      if (jj <= r) {
+#pragma unroll
+        for (int d = 0; d < CH; ++d) accB += sm.dO[r][d] * sm.U[jj][d];
+      }
+    }
+    if (tid < DK) {    // rowsum(dS' o S) over the tile's columns
+      const int c = tid;
+      const int o = (c / 16) * 256 + (c % 4) * 64 + ((c % 16) / 4) * 16;
+#pragma unroll
+      for (int d = 0; d < CH; ++d) accRS += St[o + d] * dSt[o + d];
+    }
+    if (tid >= 256 && tid < 256 + C) {   // dbeta share: sum_d dR E (kept apart from dP's accumulator)
+      const int r = tid - 256;
+      float a = 0.f;
+#pragma unroll
+      for (int d = 0; d < CH; ++d) a += sm.dR[r][d] * sm.E[r][d];
+      accT += a;
+    }
+    vm_wait<0>();      // the next tile pair has landed
+    lds_barrier();
   }
 
-  if (tid < C * C) {
-    sm.dT[tid / C][tid % C] = accT;
-    sm.dP[tid / C][tid % C] = accP;
+  if (tid < 256 && er < len) {
+#pragma unroll
+    for (int t = 0; t < MAXT; ++t)
+      if (t < nsl) dvo[(bh * T + t0 + er) * dv + CH * t + ed] = dvr[t];
   }
-  __syncthreads();
+  // tid < 256: accT = dT[er][ed];  tid >= 256: accB = dP[er][ed];  tid 256..271: accT = dbeta share
+  if (tid < 256) sm.dT[er][ed] = accT;
+  else sm.dP[er][ed] = accB;
+  if (tid < DK) sm.v.dgk[tid] = 0.f;
+  lds_barrier();
   if (tid < C * C) {   // M = T^T dT
-    const int a = tid / C, b = tid % C;
+    const int a = tid / C, bb = tid % C;
     float acc = 0.f;
-    for (int r = 0; r < C; ++r) acc += sm.cc.T[r][a] * sm.dT[r][b];
-    sm.M[a][b] = acc;
+#pragma unroll
+    for (int r = 0; r < C; ++r) acc += sm.cc.T[r][a] * sm.dT[r][bb];
+    sm.M[a][bb] = acc;
   }
-  __syncthreads();
+  lds_barrier();
   if (tid < C * C) {   // dA = -(M T^T), strictly lower, into dT
-    const int a = tid / C, b = tid % C;
+    const int a = tid / C, bb = tid % C;
     float acc = 0.f;
-    for (int j = 0; j < C; ++j) acc += sm.M[a][j] * sm.cc.T[b][j];
-    sm.dT[a][b] = b < a ? -acc : 0.f;
+#pragma unroll
+    for (int j = 0; j < C; ++j) acc += sm.M[a][j] * sm.cc.T[bb][j];
+    sm.dT[a][bb] = bb < a ? -acc : 0.f;
   }
-  __syncthreads();
-  if (tid < C) {
-    const int r = tid;
-    float acc = accB;
-    for (int j = 0; j < r; ++j) acc += sm.dT[r][j] * sm.cc.X[r][j];
+  lds_barrier();
+  if (tid >= 256 && tid < 256 + C) {
+    const int r = tid - 256;
+    float acc = accT;
+#pragma unroll
+    for (int j = 0; j < C; ++j) acc += sm.dT[r][j] * sm.cc.X[r][j];   // dA is strictly lower
     if (r < len) dbeta[bh * T + t0 + r] = acc;
   }
+  float (*gq)[DK] = sm.u.g3[0];
+  float (*gk)[DK] = sm.u.g3[1];
+  float (*gG)[DK] = sm.u.g3[2];
   {   // pair-by-pair terms of X (weights beta_r dA) and P (weights dP); thread (c, part) owns the rows
       // x = part (mod NTG / DK) of channel c and sums every pair touching them
     constexpr int NPART = NTG / DK;
     const int c = tid % DK, part = tid / DK;
+    float Gc[C], kc[C];
+#pragma unroll
+    for (int r = 0; r < C; ++r) { Gc[r] = sm.cc.G[r][c]; kc[r] = sm.cc.k[r][c]; }
     for (int x = part; x < C; x += NPART) {
-      const float kx = sm.cc.k[x][c], qx = sm.cc.q[x][c], Gx = sm.cc.G[x][c];
+      const float kx = kc[x], qx = sm.cc.q[x][c], Gx = Gc[x], bx = sm.cc.beta[x];
       float dkx = 0.f, dqx = 0.f, dGx = 0.f;
-      for (int j = 0; j <= x; ++j) {      // pairs (x, j): x is the later row
-        const float e = expf(Gx - sm.cc.G[j][c]);
-        const float kj = sm.cc.k[j][c];
-        const float wa = j < x ? sm.cc.beta[x] * sm.dT[x][j] : 0.f;
+      for (int j = 0; j <= x; ++j) {     // pairs (x, j): x is the later row
+        const float e = ex2(Gx - Gc[j]);
+        const float wa = bx * sm.dT[x][j];  // dA is strictly lower: 0 at j = x
         const float wp = sm.dP[x][j];
-        dkx += wa * kj * e;
-        dqx += wp * kj * e;
-        dGx += (wa * kx + wp * qx) * kj * e;
+        dkx += wa * kc[j] * e;
+        dqx += wp * kc[j] * e;
+        dGx += (wa * kx + wp * qx) * kc[j] * e;
       }
-      for (int r = x; r < C; ++r) {       // pairs (r, x): x is the earlier row
-        const float e = expf(sm.cc.G[r][c] - Gx);
-        const float wa = x < r ? sm.cc.beta[r] * sm.dT[r][x] : 0.f;
+      for (int r = x; r < C; ++r) {      // pairs (r, x): x is the earlier row
+        const float e = ex2(Gc[r] - Gx);
+        const float wa = sm.cc.beta[r] * sm.dT[r][x];
         const float wp = sm.dP[r][x];
-        const float f = (wa * sm.cc.k[r][c] + wp * sm.cc.q[r][c]) * e;
+        const float f = (wa * kc[r] + wp * sm.cc.q[r][c]) * e;
         dkx += f;
         dGx -= f * kx;
       }
-      sm.dk[x][c] = dkx;
-      sm.dq[x][c] = dqx;
-      sm.dG[x][c] = dGx;
+      gk[x][c] = dkx;
+      gq[x][c] = dqx;
+      gG[x][c] = dGx;
     }
   }
-  __syncthreads();
-  {   // scalings of Qbar, Kbar, Ktil
-    const int c = tid % DK;
-    float red = 0.f;
+  lds_barrier();
+  // the K = 16 products through the scalings of Qbar, Kbar, Ktil (lane: rows 4g + i, key 16 cb + col)
 #pragma unroll
-    for (int m = 0; m < EPT; ++m) {
-      const int r = tid / DK + (NTG / DK) * m;
-      const float G = sm.cc.G[r][c];
-      const float eg = expf(G), et = expf(sm.cc.gam[c] - G);
-      const float dKbar = -sm.cc.beta[r] * aK[m];
-      const float kr = sm.cc.k[r][c];
-      sm.dq[r][c] += aQ[m] * eg;
-      sm.dk[r][c] += dKbar * eg + aT[m] * et;
-      sm.dG[r][c] += aQ[m] * sm.cc.q[r][c] * eg + dKbar * kr * eg - aT[m] * kr * et;
-      red += aT[m] * kr * et;
+  for (int j = 0; j < 3; ++j) {
+    const int id = w + 8 * j;
+    if (id < NTASK) {
+      const int pr = id / NCB, c = 16 * (id % NCB) + col;
+      const float gm = sm.cc.gam[c];
+      float red = 0.f;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int r = 4 * g + i;
+        const float G = sm.cc.G[r][c], kr = sm.cc.k[r][c], x = tacc[j][i];
+        if (pr == 0) {
+          const float eg = ex2(G);
+          atomicAdd(&gq[r][c], x * eg);
+          atomicAdd(&gG[r][c], x * sm.cc.q[r][c] * eg);
+        } else if (pr == 1) {
+          const float eg = ex2(G), dKbar = -sm.cc.beta[r] * x;
+          atomicAdd(&gk[r][c], dKbar * eg);
+          atomicAdd(&gG[r][c], dKbar * kr * eg);
+        } else {
+          const float et = ex2(gm - G);
+          atomicAdd(&gk[r][c], x * et);
+          atomicAdd(&gG[r][c], -x * kr * et);
+          red += x * kr * et;
+        }
+      }
+      if (pr == 2) atomicAdd(&sm.v.dgk[c], red);
     }
-    sm.red[tid] = red;
   }
-  __syncthreads();
+  lds_barrier();
   if (tid < DK) {   // dGam, reverse prefix, outputs
     const int c = tid;
-    float acc = expf(sm.cc.gam[c]) * accRS;
-    for (int g = 0; g < NTG / DK; ++g) acc += sm.red[g * DK + c];
-    const TIn* w = (const TIn*)p.w + bh * T * DK;
+    float acc = ex2(sm.cc.gam[c]) * accRS + sm.v.dgk[c];
+    const TIn* w_in = (const TIn*)p.w + bh * T * DK;
+    float wr[C];
+#pragma unroll
+    for (int r = 0; r < C; ++r) wr[r] = r < len ? load_f32(w_in, (t0 + r) * DK + c) : 0.f;
+#pragma unroll
     for (int r = C - 1; r >= 0; --r) {
-      acc += sm.dG[r][c];
+      acc += gG[r][c];
       if (r < len) {
-        const int64_t idx = (t0 + r) * DK + c;
-        const int64_t o = bh * T * DK + idx;
-        dw[o] = acc * gate_deriv(load_f32(w, idx), p.g_min, p.unbounded);
-        dq[o] = sm.dq[r][c];
-        dk[o] = sm.dk[r][c];
+        const int64_t o = bh * T * DK + (t0 + r) * DK + c;
+        dw[o] = acc * gate_deriv(wr[r], p.g_min, p.unbounded);
+        dq[o] = gq[r][c];
+        dk[o] = gk[r][c];
       }
     }
   }
