@@ -435,38 +435,41 @@ __device__ __forceinline__ void tiles(FusedShared& sm, unsigned char* rec, const
 }
 
 // ---------------------------------------------------------------- stage S: T = (I + A)^{-1}
-// Both diagonal blocks by one wavefront: lanes 0-31 block 0, lanes 32-63 block 1, lane li of each
-// half owning row li of T_bb.  Row t of T satisfies t (I + A) = e_li, so its entries follow from the
-// last one backwards: once t_m is final, t_k -= t_m A[m][k] for every k < m.  The coupling block is
-// not formed: the chain applies it as U_1 = T_11 (R_1 - A_10 U_0).
-__device__ __forceinline__ void solve(FusedShared& sm, unsigned char* rec, int par, int lane_in) {
+// One wavefront per diagonal block; the four lanes of quad li own row li of T_bb, lane q of the quad
+// columns 4q .. 4q+3.  Row t of T satisfies t (I + A) = e_li, so its entries follow from the last one
+// backwards: once t_m is final (in lane m/4 of the quad, broadcast within the quad), t_k -= t_m A[m][k]
+// for every k < m.  The coupling block is not formed: the chain applies it as U_1 = T_11 (R_1 - A_10 U_0).
+__device__ __forceinline__ float quad_bcast(float v, int src) {   // src is a constant after unrolling
+  switch (src) {
+    case 0: return dpp<0x00>(0.f, v);
+    case 1: return dpp<0x55>(0.f, v);
+    case 2: return dpp<0xAA>(0.f, v);
+    default: return dpp<0xFF>(0.f, v);
+  }
+}
+
+__device__ __forceinline__ void solve_block(FusedShared& sm, unsigned char* rec, int par, int b, int lane_in) {
   const int lane = opaque(lane_in);
-  const int li = lane & 15, hb = lane >> 5, q = (lane >> 4) & 1;
-  const float* Ab = &sm.A[par][16 * hb][0];
-  float t[16];
+  const int li = lane >> 2, q = lane & 3;
+  const float* Ab = &sm.A[par][16 * b][4 * q];
+  floatx4 t;
 #pragma unroll
-  for (int k = 0; k < 16; ++k) t[k] = (k == li) ? 1.f : 0.f;
+  for (int c = 0; c < 4; ++c) t[c] = (li == 4 * q + c) ? 1.f : 0.f;
+  floatx4 a[15];
+#pragma unroll
+  for (int m = 15; m >= 8; --m) a[m - 1] = *reinterpret_cast<const floatx4*>(Ab + m * kRowA);
 #pragma unroll
   for (int m = 15; m >= 1; --m) {
-    const float x = t[m];
+    if (m == 7) {
 #pragma unroll
-    for (int q4 = 0; 4 * q4 < m; ++q4) {
-      const floatx4 a = *reinterpret_cast<const floatx4*>(Ab + m * kRowA + 4 * q4);
-#pragma unroll
-      for (int rr = 0; rr < 4; ++rr)
-        if (4 * q4 + rr < m) t[4 * q4 + rr] -= a[rr] * x;
+      for (int mm = 7; mm >= 1; --mm) a[mm - 1] = *reinterpret_cast<const floatx4*>(Ab + mm * kRowA);
     }
-  }
-  // lane (li, 2q + h) of the operand holds row li, columns 8q + 4h .. 8q + 4h + 3
-  floatx4 lo, hi;
+    const float x = quad_bcast(t[m & 3], m >> 2);   // quad_perm broadcast of lane m/4
 #pragma unroll
-  for (int r = 0; r < 4; ++r) {
-    lo[r] = q ? t[8 + r] : t[r];
-    hi[r] = q ? t[12 + r] : t[4 + r];
+    for (int c = 0; c < 4; ++c) t[c] = (4 * q + c < m) ? t[c] - x * a[m - 1][c] : t[c];
   }
-  unsigned char* dst = rec + rT + (hb ? kOpT11 : kOpT00);
-  *reinterpret_cast<bf16x4*>(dst + (li + 32 * q) * 8) = pack4(lo);
-  *reinterpret_cast<bf16x4*>(dst + (li + 32 * q + 16) * 8) = pack4(hi);
+  // operand lane li + 16 q holds row li, columns 4q .. 4q+3
+  *reinterpret_cast<bf16x4*>(rec + rT + (b ? kOpT11 : kOpT00) + (li + 16 * q) * 8) = pack4(t);
 }
 
 // ---------------------------------------------------------------- stage C helpers
@@ -708,7 +711,7 @@ __global__ __launch_bounds__(kThreads) void fused_kernel(Params p, int64_t n_ste
       const uint32_t pwmask = pairwise_mask(sm, p, s0 + it + 2);
       if (pwmask) pairwise_blocks<OUT, false>(sm, nullptr, recE, opsF, pwmask, 0, ln, tid);
     }
-    if (doS && w == 7) solve(sm, recS, (int)((it + 1) & 1), ln);
+    if (doS && w >= 6) solve_block(sm, recS, (int)((it + 1) & 1), w - 6, ln);
   }
 
   if (OUT) {
