@@ -20,8 +20,9 @@
 //   dT = dU R^T  ->  dA = -T^T dT T^T (strictly lower)      dP = dO U^T (lower, diagonal included)
 //   dbeta_r = sum_d dR[r][d] E[r][d] + sum_j dA[r][j] X[r][j]
 //   X, P pair by pair -> dk, dq, dG;   dQbar = dO S^T,  dKbar = -diag(beta) dR S^T,  dKtil = U dS'^T
-//   dGam = e^{Gam} . rowsum(dS' o S) + colsum(dKtil o Ktil)
-//   dg = reverse prefix of dG (+ dGam on every row),  dw = dg gate'(w)
+//   dg_u = e^{Gam} . rowsum(dS' o S) + sum_{r >= u} dG_r + sum_{r < u} (dKtil o Ktil)_r,  dw = dg gate'(w)
+// (the Ktil scaling's share of dG, -dKtil o Ktil per row, and of dGam, its column sum, are combined
+// into the sum over the earlier rows: in strongly decaying chunks the two long sums nearly cancel)
 //
 // Four launches:
 //   prep   (one workgroup per chunk)            G, X, P, T -> W, Ktil, Qbar, U0, P^T dO, e^{Gam} records
@@ -66,9 +67,18 @@ __host__ __device__ __forceinline__ WsLayout ws_layout(void* ws, int64_t BH, int
 }
 
 constexpr float kLog2eB = 1.4426950408889634f;
+constexpr float kLn2B = 0.6931471805599453f;
 
 // 2^x on the transcendental unit (one instruction; exponents here are <= 0 or small)
 __device__ __forceinline__ float ex2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+// one 16 x 16 x 4 fp32 matrix-core step: lane l supplies A[l % 16][l / 16] and B[l / 16][l % 16]; the
+// accumulator holds D[4 (l / 16) + i][l % 16] in register i
+__device__ __forceinline__ f32x4 mfma4(float a, float b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
+}
 
 // gate derivative d g / d w: g_min sigma (1 - sigma), or -sigma for -softplus
 __device__ __forceinline__ float gate_deriv(float w, float g_min, int unbounded) {
@@ -91,10 +101,12 @@ struct ChunkCore {
   float gam[DK];
   float beta[C];
   float X[C][C + 1], P[C][C + 1], T[C][C + 1], Tb[C][C + 1];   // Tb = T diag(beta)
+  int dense;   // every channel's span >= -80: pair terms as products of e^{+-(G - Gam/2)} factors
 };
 
 // Loads chunk n (rows past the end are zero: k = q = beta = 0 and g = 0, which reproduces the
-// shorter last chunk exactly), forms the prefix G and Gam, X and P pair by pair (each pair's sums
+// shorter last chunk exactly), forms the prefix G and Gam, the chunk's span flag (dense: every
+// channel's span >= -80), X and P pair by pair (each pair's sums
 // split over four quarters of the key channels, partial sums through `scratch`, 2 * 4 * 256 floats),
 // and T by forward substitution (one column per thread, held in registers).  Ends with a barrier.
 template <typename TIn, int DK, int NT>
@@ -141,6 +153,13 @@ __device__ void chunk_setup(ChunkCore<DK>& cc, float* scratch, const Params& p, 
 #pragma unroll
     for (int r = 0; r < C; ++r) { g += gv[r]; cc.G[r][tid] = g; }
     cc.gam[tid] = g;
+  }
+  if (tid < 64) {   // chunk flag: the smallest span over the channels, against the limit
+    float m = 0.f;
+    for (int c = tid; c < DK; c += 64) m = fminf(m, cc.gam[c]);
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) m = fminf(m, __shfl_xor(m, off));
+    if (tid == 0) cc.dense = m * kLn2B >= kSpanLimit;
   }
   __syncthreads();
   float (*xs)[C][C] = reinterpret_cast<float (*)[C][C]>(scratch);              // [NQ][C][C]
@@ -276,13 +295,8 @@ __global__ __launch_bounds__(NTP) void bwd_prep_kernel(Params p, const void* __r
 // States are stored in the accumulator's own order: the [dk][16] block of (head, chunk, columns
 // 16j .. 16j + 15) is contiguous, element (row 16w + 4g + i, column cl) at w*256 + i*64 + g*16 + cl.
 
-typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) void lds_void;
 typedef __attribute__((address_space(1))) void gbl_void;
-
-__device__ __forceinline__ f32x4 mfma4(float a, float b, f32x4 c) {
-  return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
-}
 
 __device__ __forceinline__ void compiler_fence() { __atomic_signal_fence(__ATOMIC_SEQ_CST); }
 
@@ -581,7 +595,7 @@ struct GradShared {
   union {
     float part[8][C][CH];                 // partial E (0..3) and Ktil dS' (4..7) of the tile; the
                                           // setup's partial pair sums before the tile loop
-    float dgk[DK];                        // sum_r dKtil o Ktil, after the tile loop
+    float kt[C][DK];                      // dKtil o Ktil per row, after the tile loop
   } v;
   static_assert(sizeof(float) * 8 * C * CH >= sizeof(float) * 2 * 4 * C * C, "setup scratch");
   float dO[C][CH + 4], E[C][CH + 4], U[C][CH + 4], dU[C][CH + 4], dR[C][CH + 4];
@@ -762,7 +776,6 @@ __global__ __launch_bounds__(NTG) __attribute__((amdgpu_waves_per_eu(4, 4))) voi
   // tid < 256: accT = dT[er][ed];  tid >= 256: accB = dP[er][ed];  tid 256..271: accT = dbeta share
   if (tid < 256) sm.dT[er][ed] = accT;
   else sm.dP[er][ed] = accB;
-  if (tid < DK) sm.v.dgk[tid] = 0.f;
   lds_barrier();
   if (tid < C * C) {   // M = T^T dT
     const int a = tid / C, bb = tid % C;
@@ -790,8 +803,45 @@ __global__ __launch_bounds__(NTG) __attribute__((amdgpu_waves_per_eu(4, 4))) voi
   float (*gq)[DK] = sm.u.g3[0];
   float (*gk)[DK] = sm.u.g3[1];
   float (*gG)[DK] = sm.u.g3[2];
-  {   // pair-by-pair terms of X (weights beta_r dA) and P (weights dP); thread (c, part) owns the rows
-      // x = part (mod NTG / DK) of channel c and sums every pair touching them
+  if (sm.cc.dense) {
+    // the pair terms as products of e^{+-(G - Gam/2)} factors (wavefront w: key channels 16w .. 16w + 15):
+    //   P1 = Wa Kinv', P2 = Wp Kinv', P3 = Wa^T Kbar', P4 = Wp^T Qbar'   (Wa = diag(beta) dA, Wp = dP)
+    //   dk_x = e^{G'_x} P1 + e^{-G'_x} (P3 + P4),  dq_x = e^{G'_x} P2,
+    //   dG_x = k_x e^{G'_x} P1 + q_x e^{G'_x} P2 - k_x e^{-G'_x} (P3 + P4)
+    if (w < NCB) {
+      const int c = 16 * w + col;
+      float eg[4], egi[4], kk[4], qq[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {     // rows 4g + i of channel c: B operands, and the output rows
+        const int r = 4 * g + i;
+        const float Gs = sm.cc.G[r][c] - 0.5f * sm.cc.gam[c];
+        eg[i] = ex2(Gs);
+        egi[i] = ex2(-Gs);
+        kk[i] = sm.cc.k[r][c];
+        qq[i] = sm.cc.q[r][c];
+      }
+      f32x4 p1 = {0.f, 0.f, 0.f, 0.f}, p2 = p1, p3 = p1, p4 = p1;
+      const float bc = sm.cc.beta[col];
+#pragma unroll
+      for (int s = 0; s < 4; ++s) {     // K order: j (or r) = 4g + s
+        const int r = 4 * g + s;
+        const float kinv = kk[s] * egi[s], kbar = kk[s] * eg[s], qbar = qq[s] * eg[s];
+        p1 = mfma4(bc * sm.dT[col][r], kinv, p1);
+        p2 = mfma4(sm.dP[col][r], kinv, p2);
+        p3 = mfma4(sm.cc.beta[r] * sm.dT[r][col], kbar, p3);
+        p4 = mfma4(sm.dP[r][col], qbar, p4);
+      }
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int x = 4 * g + i;
+        const float a = eg[i] * p1[i], bq = eg[i] * p2[i], e = egi[i] * (p3[i] + p4[i]);
+        gk[x][c] = a + e;
+        gq[x][c] = bq;
+        gG[x][c] = kk[i] * a + qq[i] * bq - kk[i] * e;
+      }
+    }
+  } else {   // pair-by-pair terms of X (weights beta_r dA) and P (weights dP); thread (c, part) owns the
+             // rows x = part (mod NTG / DK) of channel c and sums every pair touching them
     constexpr int NPART = NTG / DK;
     const int c = tid % DK, part = tid / DK;
     float Gc[C], kc[C];
@@ -829,7 +879,6 @@ __global__ __launch_bounds__(NTG) __attribute__((amdgpu_waves_per_eu(4, 4))) voi
     if (id < NTASK) {
       const int pr = id / NCB, c = 16 * (id % NCB) + col;
       const float gm = sm.cc.gam[c];
-      float red = 0.f;
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int r = 4 * g + i;
@@ -843,29 +892,35 @@ __global__ __launch_bounds__(NTG) __attribute__((amdgpu_waves_per_eu(4, 4))) voi
           atomicAdd(&gk[r][c], dKbar * eg);
           atomicAdd(&gG[r][c], dKbar * kr * eg);
         } else {
+          // the Ktil scaling enters dG_r with one sign and dGam with the other; kept apart, so that dg
+          // takes it as a sum over the earlier rows instead of a difference of two long sums
           const float et = ex2(gm - G);
           atomicAdd(&gk[r][c], x * et);
-          atomicAdd(&gG[r][c], -x * kr * et);
-          red += x * kr * et;
+          sm.v.kt[r][c] = x * kr * et;
         }
       }
-      if (pr == 2) atomicAdd(&sm.v.dgk[c], red);
     }
   }
   lds_barrier();
   if (tid < DK) {   // dGam, reverse prefix, outputs
     const int c = tid;
-    float acc = ex2(sm.cc.gam[c]) * accRS + sm.v.dgk[c];
+    // dg_u = e^{Gam} rowsum(dS' o S) + sum_{r >= u} dG_r + sum_{r < u} (dKtil o Ktil)_r
+    float acc = ex2(sm.cc.gam[c]) * accRS;
     const TIn* w_in = (const TIn*)p.w + bh * T * DK;
-    float wr[C];
+    float wr[C], pre[C];
+    float run = 0.f;
 #pragma unroll
-    for (int r = 0; r < C; ++r) wr[r] = r < len ? load_f32(w_in, (t0 + r) * DK + c) : 0.f;
+    for (int r = 0; r < C; ++r) {
+      wr[r] = r < len ? load_f32(w_in, (t0 + r) * DK + c) : 0.f;
+      pre[r] = run;
+      run += sm.v.kt[r][c];
+    }
 #pragma unroll
     for (int r = C - 1; r >= 0; --r) {
       acc += gG[r][c];
       if (r < len) {
         const int64_t o = bh * T * DK + (t0 + r) * DK + c;
-        dw[o] = acc * gate_deriv(wr[r], p.g_min, p.unbounded);
+        dw[o] = (acc + pre[r]) * gate_deriv(wr[r], p.g_min, p.unbounded);
         dq[o] = gq[r][c];
         dk[o] = gk[r][c];
       }

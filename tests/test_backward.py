@@ -47,7 +47,8 @@ def run_case(wl, seed, with_dSf=True, want_dS0=True):
     return got, ref
 
 
-def check(wl, seed, **kw):
+def check(wl, seed, tol=None, **kw):
+    tol = dict(tol or {})
     got, ref = run_case(wl, seed, **kw)
     errs = {}
     for name, g, r in zip(NAMES, got, ref):
@@ -56,9 +57,10 @@ def check(wl, seed, **kw):
         assert g.shape == r.shape, name
         assert np.isfinite(g).all(), f"{name} has non-finite entries"
         errs[name] = rel_err(g, r)
-    say("   " + "  ".join(f"{n}={e:.2e}" for n, e in errs.items()) + f"  (tol {BWD_TOL})")
+    say("   " + "  ".join(f"{n}={e:.2e}" for n, e in errs.items()) + f"  (tol {BWD_TOL}, {tol})")
     for n, e in errs.items():
-        assert e <= BWD_TOL, f"{n}: {e:.3e} > {BWD_TOL}"
+        t = tol.get(n, BWD_TOL)
+        assert e <= t, f"{n}: {e:.3e} > {t}"
     return got, ref
 
 
@@ -100,6 +102,21 @@ def test_unbounded_gate():
 def test_other_bounds(g_min):
     """A bound whose forward chunks get flagged (-8) and a mild one."""
     check(BF16.with_(B=1, H=2, T=100, g_min=g_min, s0_sd=0.5), seed=450)
+
+
+@pytest.mark.parametrize("w_mu,what", [(4.0, "every chunk past the span limit (pair-by-pair terms)"),
+                                       (-4.0, "no chunk near it (products of e^{+-G} factors)"),
+                                       (1.0, "a mix of both kinds of chunk")])
+def test_span_paths(w_mu, what):
+    """g_min = -8: chunks whose span is below -80 take the pair-by-pair terms, the others the dense
+    products; both against the oracle, separately and mixed in one sequence.
+
+    With every chunk decaying by about e^{-126} (w_mu = 4), dg per token is a small difference of
+    in-chunk terms, and the chunk form's fp32 rounding reaches about 3e-5 of max |dw| (a float32 numpy
+    model of the same formulas gives 3.0e-5 on these inputs, its float64 twin 1e-13 against the oracle);
+    dw is held to 1e-4 there, every other gradient to BWD_TOL."""
+    tol = {"dw": 1e-4} if w_mu > 2 else None
+    check(F32.with_(B=1, H=2, T=150, dk=64, dv=64, g_min=-8.0, w_mu=w_mu, w_sd=1.0, s0_sd=0.5), seed=455, tol=tol)
 
 
 def test_long_f32():
