@@ -1,5 +1,5 @@
 // Backward pass of the chunked KDA forward: gradients of a loss L with respect to q, k, v, w, beta
-// and S0, given dL/do and dL/dS_final, in fp32 on the vector ALUs.
+// and S0, given dL/do and dL/dS_final, in fp32 (matrix cores and vector ALUs).
 //
 // The forward of one 16-token chunk (entering state S, chunk-local inclusive prefix G of the
 // log-decay, span Gam = G at the last row; "From Numerical Stability to Load Balancing ..."
@@ -9,7 +9,8 @@
 //   E = V - Kbar S,  R = diag(beta) E,  U = T R,  O = Qbar S + P U,  S' = e^{Gam} S + Ktil^T U
 // with Kbar = k e^{G}, Qbar = q e^{G}, Ktil = k e^{Gam - G}.  X and P are formed pair by pair, every
 // factor exp(G_r - G_j) <= 1 (the per-position form the pages give for chunks whose reciprocal
-// factors would overflow), so the backward needs no span check and no reciprocal at all.
+// factors would overflow); the pair terms of the gradients use the same form for such chunks and
+// products of e^{+-(G - Gam/2)} factors (each at most e^{40}) for the others.
 //
 // With W = T diag(beta) Kbar and U0 = T diag(beta) V (the WY form: U = U0 - W S) the two chains
 // through the chunks are affine and cheap:

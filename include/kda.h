@@ -157,9 +157,12 @@ KDA_API int kda_decode(const void* q, const void* k, const void* v, const void* 
                        float* S, float g_min, const kda_shape_t* shape, void* o, void* stream);
 
 /* Backward pass of the chunked forward: gradients of a loss L given dL/do and dL/dS_final.
- * The reverse mode of the chunk form (each 16-token chunk's in-chunk blocks formed pair by pair
- * with factors exp(G_r - G_j) <= 1, so no chunk needs a span check), evaluated in fp32 on the
- * vector ALUs from the chunk entering states that a first pass recomputes into the workspace.
+ * The reverse mode of the 16-token chunk form ("From Numerical Stability to Load Balancing ..."
+ * section 2.1), all in fp32: a chunk-parallel pass writes each chunk's WY record, two sequential
+ * passes walk the chunk-to-chunk state forwards (entering states) and backwards (leaving adjoints),
+ * and a chunk-parallel pass forms every gradient.  In-chunk pair terms use factors exp(+-(G - Gam/2))
+ * when every channel's span is >= -80 and pair-by-pair factors exp(G_r - G_j) <= 1 otherwise, so
+ * no input overflows.
  * Arguments: the forward's q, k, v, w, beta, S0 (nullable), g_min, chunk (16) and shape (dk in
  *   {32, 64, 128}, dv in {32, 64, 128});
  *   dO [B,H,T,dv] in shape->dtype; dS_final [B,H,dk,dv] fp32 or NULL (zero);
@@ -173,8 +176,10 @@ KDA_API int kda_chunk_bwd(const void* q, const void* k, const void* v, const voi
                           const void* dO, const float* dS_final, float* dq, float* dk, float* dv, float* dw,
                           float* dbeta, float* dS0, void* workspace, size_t workspace_bytes, void* stream);
 
-/* Scratch bytes kda_chunk_bwd needs: the fp32 entering state of every 16-token chunk,
- * B*H*ceil(T/16)*dk*dv*4.  (size_t)-1 for an invalid shape or chunk.  Host-only. */
+/* Scratch bytes kda_chunk_bwd needs: per 16-token chunk its record (3*16*dk + 2*16*dv + dk floats),
+ * entering state and leaving adjoint (dk*dv floats each), all fp32:
+ * B*H*ceil(T/16)*(3*16*dk + 2*16*dv + dk + 2*dk*dv)*4.  (size_t)-1 for an invalid shape or chunk.
+ * Host-only. */
 KDA_API size_t kda_bwd_workspace_bytes(const kda_shape_t* shape, int chunk);
 
 /* Gate and in-chunk prefix stage on its own (for checking that stage, and for the chunk-size
