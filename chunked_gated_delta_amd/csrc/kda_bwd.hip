@@ -75,6 +75,17 @@ __device__ __forceinline__ float ex2(float x) { return __builtin_amdgcn_exp2f(x)
 
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 
+// value of lane src (0..3) of this lane's group of four, through a DPP quad permute
+__device__ __forceinline__ float quad_bcast(float v, int src) {   // src is a constant after unrolling
+  const int b = __float_as_int(v);
+  switch (src) {
+    case 0: return __int_as_float(__builtin_amdgcn_update_dpp(0, b, 0x00, 0xF, 0xF, false));
+    case 1: return __int_as_float(__builtin_amdgcn_update_dpp(0, b, 0x55, 0xF, 0xF, false));
+    case 2: return __int_as_float(__builtin_amdgcn_update_dpp(0, b, 0xAA, 0xF, 0xF, false));
+    default: return __int_as_float(__builtin_amdgcn_update_dpp(0, b, 0xFF, 0xF, 0xF, false));
+  }
+}
+
 // one 16 x 16 x 4 fp32 matrix-core step: lane l supplies A[l % 16][l / 16] and B[l / 16][l % 16]; the
 // accumulator holds D[4 (l / 16) + i][l % 16] in register i
 __device__ __forceinline__ f32x4 mfma4(float a, float b, f32x4 c) {
@@ -163,49 +174,84 @@ __device__ void chunk_setup(ChunkCore<DK>& cc, float* scratch, const Params& p, 
     if (tid == 0) cc.dense = m * kLn2B >= kSpanLimit;
   }
   __syncthreads();
-  float (*xs)[C][C] = reinterpret_cast<float (*)[C][C]>(scratch);              // [NQ][C][C]
+  float (*xs)[C][C] = reinterpret_cast<float (*)[C][C]>(scratch);              // [4][C][C] partial sums
   float (*ps)[C][C] = reinterpret_cast<float (*)[C][C]>(scratch + 4 * C * C);
-  for (int task = tid; task < NPAIR * NQ; task += NT) {
-    const int pr = task % NPAIR, qq = task / NPAIR;
-    int r, j;
-    pair_of(pr, r, j);
-    float x = 0.f, pp = 0.f;
+  const bool dense = cc.dense;
+  if (dense) {
+    // X = Kbar' Kinv'^T, P = Qbar' Kinv'^T with Kbar' = k e^{G - Gam/2}, Kinv' = k e^{Gam/2 - G} (every
+    // factor at most e^{40}): wavefront wq < 4 takes key blocks wq and wq + 4, K order c = 16 cb + 4g + i
+    const int wq = tid / 64, lane = tid % 64, li = lane % 16, g = lane / 16;
+    if (wq < 4) {
+      f32x4 xa = {0.f, 0.f, 0.f, 0.f}, pa = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int bb = 0; bb < 2; ++bb) {
+        const int cb = wq + 4 * bb;
+        if (cb < DK / 16) {
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const int c = 16 * cb + 4 * g + i;
+            const float Gs = cc.G[li][c] - 0.5f * cc.gam[c];
+            const float e = ex2(Gs), ei = ex2(-Gs), kv = cc.k[li][c];
+            xa = mfma4(kv * e, kv * ei, xa);
+            pa = mfma4(cc.q[li][c] * e, kv * ei, pa);
+          }
+        }
+      }
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {   // lane (li, g) holds row 4g + i, column li
+        xs[wq][4 * g + i][li] = xa[i];
+        ps[wq][4 * g + i][li] = pa[i];
+      }
+    }
+  } else {
+    for (int task = tid; task < NPAIR * NQ; task += NT) {
+      const int pr = task % NPAIR, qq = task / NPAIR;
+      int r, j;
+      pair_of(pr, r, j);
+      float x = 0.f, pp = 0.f;
 #pragma unroll 8
-    for (int c = qq; c < DK; c += NQ) {
-      const float kj = cc.k[j][c] * ex2(cc.G[r][c] - cc.G[j][c]);
-      x += cc.k[r][c] * kj;
-      pp += cc.q[r][c] * kj;
+      for (int c = qq; c < DK; c += NQ) {
+        const float kj = cc.k[j][c] * ex2(cc.G[r][c] - cc.G[j][c]);
+        x += cc.k[r][c] * kj;
+        pp += cc.q[r][c] * kj;
+      }
+      xs[qq][r][j] = x;
+      ps[qq][r][j] = pp;
     }
-    xs[qq][r][j] = x;
-    ps[qq][r][j] = pp;
   }
   __syncthreads();
-  if (tid < C * C) {
-    const int r = tid / C, j = tid % C;
-    float x = 0.f, pp = 0.f;
-    if (j <= r) {
-#pragma unroll
-      for (int qq = 0; qq < NQ; ++qq) { x += xs[qq][r][j]; pp += ps[qq][r][j]; }
+  {
+    const int nq = dense ? 4 : NQ;
+    for (int e = tid; e < 2 * C * C; e += NT) {   // X from threads 0..255, P from 256..511
+      const int which = e / (C * C), r = (e % (C * C)) / C, j = e % C;
+      float (*src)[C][C] = which ? ps : xs;
+      float x = 0.f;
+      if (j <= r)
+        for (int qq = 0; qq < nq; ++qq) x += src[qq][r][j];
+      if (which) cc.P[r][j] = x;
+      else cc.X[r][j] = j < r ? x : 0.f;
     }
-    cc.X[r][j] = j < r ? x : 0.f;
-    cc.P[r][j] = pp;
   }
   __syncthreads();
-  if (tid < C) {   // T = (I + diag(beta) X)^{-1}, column j
-    const int j = tid;
-    float tc[C];
+  if (tid < 64) {
+    // T = (I + A)^{-1}, A = diag(beta) X: the four lanes of quad li own row li of T, lane q of the quad
+    // columns 4q .. 4q+3.  Row t of T satisfies t (I + A) = e_li, so its entries follow from the last one
+    // backwards: once t_m is final (lane m/4 of the quad, broadcast inside the quad), t_k -= t_m A[m][k].
+    const int li = tid >> 2, q = tid & 3;
+    float t[4];
 #pragma unroll
-    for (int r = 0; r < C; ++r) {
-      float x = (r == j) ? 1.f : 0.f;
-      const float br = cc.beta[r];
+    for (int c = 0; c < 4; ++c) t[c] = (li == 4 * q + c) ? 1.f : 0.f;
 #pragma unroll
-      for (int i = 0; i < r; ++i) x -= br * cc.X[r][i] * tc[i];   // tc[i] = 0 for i < j
-      tc[r] = (r < j) ? 0.f : x;
+    for (int m = C - 1; m >= 1; --m) {
+      const float x = quad_bcast(t[m & 3], m >> 2) * cc.beta[m];
+#pragma unroll
+      for (int c = 0; c < 4; ++c)
+        if (4 * q + c < m) t[c] -= x * cc.X[m][4 * q + c];
     }
 #pragma unroll
-    for (int r = 0; r < C; ++r) {
-      cc.T[r][j] = tc[r];
-      cc.Tb[r][j] = tc[r] * cc.beta[j];
+    for (int c = 0; c < 4; ++c) {
+      cc.T[li][4 * q + c] = t[c];
+      cc.Tb[li][4 * q + c] = t[c] * cc.beta[4 * q + c];
     }
   }
   __syncthreads();
@@ -601,6 +647,7 @@ struct GradShared {
   static_assert(sizeof(float) * 8 * C * CH >= sizeof(float) * 2 * 4 * C * C, "setup scratch");
   float dO[C][CH + 4], E[C][CH + 4], U[C][CH + 4], dU[C][CH + 4], dR[C][CH + 4];
   float dT[C][C + 1], dP[C][C + 1], M[C][C + 1];
+  float rs[DK];                           // rowsum(dS' o S) per channel
 };
 
 template <typename TIn, int DK>
@@ -634,6 +681,17 @@ __global__ __launch_bounds__(NTG) __attribute__((amdgpu_waves_per_eu(4, 4))) voi
     }
   };
   copy_tile(0, 0);
+  // w of the rows this thread finishes in the last phase (channel tid / NPC, rows (tid % NPC) * RPT ..)
+  constexpr int NPC = NTG / DK, RPT = C / NPC;
+  float wr[RPT];
+  {
+    const TIn* w_in = (const TIn*)p.w + bh * T * DK;
+#pragma unroll
+    for (int i = 0; i < RPT; ++i) {
+      const int r = (tid % NPC) * RPT + i;
+      wr[i] = r < len ? load_f32(w_in, (t0 + r) * DK + tid / NPC) : 0.f;
+    }
+  }
   // V and dO of every tile, element (er, ed) of each (threads < 256), loaded before the setup
   const int er = (tid % 256) / CH, ed = tid % CH;   // element (row, column) of a 16 x 16 tile
   constexpr int MAXT = 128 / CH;
@@ -697,27 +755,29 @@ __global__ __launch_bounds__(NTG) __attribute__((amdgpu_waves_per_eu(4, 4))) voi
       for (int i = 0; i < 4; ++i) sm.v.part[w][4 * g + i][col] = pp[i];
     }
     lds_barrier();
-    if (tid < 256) {   // E = V - Kbar S;  dU = Ktil dS' + P^T dO
-      float e = vrd, du = 0.f;
+    if (tid < 256) {   // E = V - Kbar S
+      float e = vrd;
 #pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        e -= sm.v.part[q][er][ed];
-        du += sm.v.part[4 + q][er][ed];
-      }
+      for (int q = 0; q < 4; ++q) e -= sm.v.part[q][er][ed];
+      sm.E[er][ed] = e;
+    } else {           // dU = Ktil dS' + P^T dO
+      float du = 0.f;
+#pragma unroll
+      for (int q = 0; q < 4; ++q) du += sm.v.part[4 + q][er][ed];
 #pragma unroll
       for (int i = 0; i < C; ++i) du += sm.cc.P[i][er] * sm.dO[i][ed];   // P[i][er] = 0 for i < er
-      sm.E[er][ed] = e;
       sm.dU[er][ed] = du;
     }
     lds_barrier();
-    if (tid < 256) {   // U = T diag(beta) E;  dR = T^T dU;  dv = diag(beta) dR
-      float u = 0.f, dr = 0.f;     // T is lower triangular (zeros above the diagonal)
+    if (tid < 256) {   // U = T diag(beta) E (T is lower triangular: zeros above the diagonal)
+      float u = 0.f;
 #pragma unroll
-      for (int j = 0; j < C; ++j) {
-        u += sm.cc.Tb[er][j] * sm.E[j][ed];
-        dr += sm.cc.T[j][er] * sm.dU[j][ed];
-      }
+      for (int j = 0; j < C; ++j) u += sm.cc.Tb[er][j] * sm.E[j][ed];
       sm.U[er][ed] = u;
+    } else {           // dR = T^T dU;  dv = diag(beta) dR
+      float dr = 0.f;
+#pragma unroll
+      for (int j = 0; j < C; ++j) dr += sm.cc.T[j][er] * sm.dU[j][ed];
       sm.dR[er][ed] = dr;
       dvr[t] = sm.cc.beta[er] * dr;
     }
@@ -769,11 +829,12 @@ __global__ __launch_bounds__(NTG) __attribute__((amdgpu_waves_per_eu(4, 4))) voi
     lds_barrier();
   }
 
-  if (tid < 256 && er < len) {
+  if (tid >= 256 && er < len) {
 #pragma unroll
     for (int t = 0; t < MAXT; ++t)
       if (t < nsl) dvo[(bh * T + t0 + er) * dv + CH * t + ed] = dvr[t];
   }
+  if (tid < DK) sm.rs[tid] = accRS;
   // tid < 256: accT = dT[er][ed];  tid >= 256: accB = dP[er][ed];  tid 256..271: accT = dbeta share
   if (tid < 256) sm.dT[er][ed] = accT;
   else sm.dP[er][ed] = accB;
@@ -874,6 +935,23 @@ __global__ __launch_bounds__(NTG) __attribute__((amdgpu_waves_per_eu(4, 4))) voi
   }
   lds_barrier();
   // the K = 16 products through the scalings of Qbar, Kbar, Ktil (lane: rows 4g + i, key 16 cb + col)
+  if (NCB == 8) {   // wavefront w holds all three products of key block w: plain updates
+    const int c = 16 * w + col;
+    const float gm = sm.cc.gam[c];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int r = 4 * g + i;
+      const float G = sm.cc.G[r][c], kr = sm.cc.k[r][c];
+      const float eg = ex2(G), et = ex2(gm - G);
+      const float a = tacc[0][i], dKbar = -sm.cc.beta[r] * tacc[1][i], t = tacc[2][i];
+      gq[r][c] += a * eg;
+      gk[r][c] += dKbar * eg + t * et;
+      gG[r][c] += a * sm.cc.q[r][c] * eg + dKbar * kr * eg;
+      // the Ktil scaling enters dG_r with one sign and dGam with the other; kept apart, so that dg
+      // takes it as a sum over the earlier rows instead of a difference of two long sums
+      sm.v.kt[r][c] = t * kr * et;
+    }
+  } else {
 #pragma unroll
   for (int j = 0; j < 3; ++j) {
     const int id = w + 8 * j;
@@ -902,26 +980,43 @@ __global__ __launch_bounds__(NTG) __attribute__((amdgpu_waves_per_eu(4, 4))) voi
       }
     }
   }
+  }
   lds_barrier();
-  if (tid < DK) {   // dGam, reverse prefix, outputs
-    const int c = tid;
-    // dg_u = e^{Gam} rowsum(dS' o S) + sum_{r >= u} dG_r + sum_{r < u} (dKtil o Ktil)_r
-    float acc = ex2(sm.cc.gam[c]) * accRS;
-    const TIn* w_in = (const TIn*)p.w + bh * T * DK;
-    float wr[C], pre[C];
-    float run = 0.f;
+  {   // dg and the outputs; NPC threads per channel, thread p of channel c owning rows p*RPT .. p*RPT + RPT-1:
+      // dg_u = e^{Gam} rowsum(dS' o S) + sum_{r >= u} dG_r + sum_{r < u} (dKtil o Ktil)_r
+    const int c = tid / NPC, pp = tid % NPC, r0 = pp * RPT;
+    float gv[RPT], kv[RPT];
+    float sg = 0.f, sk = 0.f;
 #pragma unroll
-    for (int r = 0; r < C; ++r) {
-      wr[r] = r < len ? load_f32(w_in, (t0 + r) * DK + c) : 0.f;
-      pre[r] = run;
-      run += sm.v.kt[r][c];
+    for (int i = 0; i < RPT; ++i) {
+      const int r = r0 + i;
+      gv[i] = gG[r][c];
+      kv[i] = sm.v.kt[r][c];
+      sg += gv[i];
+      sk += kv[i];
     }
+    // over the channel's NPC threads (consecutive lanes): dG of the later rows, Ktil terms of the earlier
+    float later = 0.f, earlier = 0.f;
 #pragma unroll
-    for (int r = C - 1; r >= 0; --r) {
-      acc += gG[r][c];
+    for (int o = 1; o < NPC; o <<= 1) {
+      const float a = __shfl_down(sg, o, NPC), b = __shfl_up(sk, o, NPC);
+      if (pp + o < NPC) later += a;
+      if (pp >= o) earlier += b;
+      sg += (pp + o < NPC) ? a : 0.f;
+      sk += (pp >= o) ? b : 0.f;
+    }
+    float acc = ex2(sm.cc.gam[c]) * sm.rs[c] + later;     // suffix from the rows after this thread's
+    float pre[RPT];
+    float run = earlier;
+#pragma unroll
+    for (int i = 0; i < RPT; ++i) { pre[i] = run; run += kv[i]; }
+#pragma unroll
+    for (int i = RPT - 1; i >= 0; --i) {
+      const int r = r0 + i;
+      acc += gv[i];
       if (r < len) {
         const int64_t o = bh * T * DK + (t0 + r) * DK + c;
-        dw[o] = (acc + pre[r]) * gate_deriv(wr[r], p.g_min, p.unbounded);
+        dw[o] = (acc + pre[i]) * gate_deriv(wr[i], p.g_min, p.unbounded);
         dq[o] = gq[r][c];
         dk[o] = gk[r][c];
       }
