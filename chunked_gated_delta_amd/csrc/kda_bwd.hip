@@ -40,7 +40,7 @@ namespace {
 constexpr int C = kChunk;      // 16
 constexpr int NPAIR = C * (C + 1) / 2;
 constexpr int CH = 16;         // value columns per chain workgroup
-constexpr int kDepth = 3;      // chunks of chain operands in flight (LDS ring of kDepth + 1 slots)
+constexpr int kDepth = 4;      // chunks of chain operands in flight (an LDS ring of kDepth slots)
 constexpr int NTP = 512;       // prep threads
 constexpr int NTG = 512;       // grad threads
 
@@ -327,14 +327,17 @@ __global__ __launch_bounds__(NTP) void bwd_prep_kernel(Params p, const void* __r
 // ---------------------------------------------------------------- chains
 // One workgroup per (head, 16 value columns); wavefront w holds rows 16w .. 16w + 15 of the block as
 // an fp32 matrix-core accumulator tile (lane l: rows 16w + 4(l/16) + i, i < 4, column l % 16).  Per
-// chunk: a 16 x 16 x 16 product per wavefront into LDS, a cross-wavefront sum, then the update as
-// one more product on the tile.  The K index of each 16 x 16 x 4 step is taken in the order the
-// accumulator already holds its rows (row 4(l/16) + i at step i), so the state needs no reshuffle.
+// chunk: a 16 x 16 x 16 product per wavefront (its 16-key share of a K = dk contraction), written to
+// LDS; after one barrier every wavefront sums all shares itself, in the same lane layout, and the
+// update is one more product on the tile.  The K index of each 16 x 16 x 4 step is taken in the
+// order the accumulator already holds its rows (row 4(l/16) + i at step i), so neither the state
+// nor the summed shares need a reshuffle to serve as the B operand.
 //
 // Roles: compute wavefronts do the products and store the chain's states (stores only, never
 // waited on); loader wavefronts copy each chunk's operands from its record straight into a ring of
-// LDS slots (16-byte global-to-LDS loads, kDepth chunks ahead) and wait for exactly the oldest chunk
-// in flight.  Both roles meet at two barriers per chunk.
+// LDS slots (16-byte global-to-LDS loads, kDepth chunks ahead).  All reads of a chunk's slot come
+// before the step's barrier, so right after it the loaders refill that slot with the chunk kDepth
+// steps ahead, having made sure (before the barrier) that the next step's chunk has landed.
 //
 // Operand matrices [16][dk] sit in a slot as float4 units, row r's unit c4 at r * dk/4 + (c4 ^ r % (dk/4)),
 // so that the 16 rows a matrix-core operand read touches fall on distinct LDS banks.
@@ -370,8 +373,7 @@ __device__ __forceinline__ void dma16(const void* src, void* dst_base) {
 }
 
 // blocks of one head on one XCD (consecutive block ids go round-robin over the 8 XCDs)
-__device__ __forceinline__ int64_t xcd_block(int64_t nblocks) {
-  const int64_t b = blockIdx.x;
+__device__ __forceinline__ int64_t xcd_block(int64_t b, int64_t nblocks) {
   return (nblocks % 8) ? b : (b % 8) * (nblocks / 8) + b / 8;
 }
 
@@ -401,57 +403,89 @@ struct ChainDims {
   static constexpr int NT = (NW + NL) * 64;
 };
 
-// Issues this loader wave's share of one chunk's operand copies into LDS slot `slot` (float4 units).
-// Unit u of the slot comes from: matrix rows of the record (un-swizzled), the 16 x 16 vector block
-// (U0 or Z0), the dO rows of tokens t0 .. t0 + 15 (clamped to the last token; the compute side
-// ignores rows past the end), e^{Gam}.  Every loader wave issues exactly PER instructions, one per
-// unrolled iteration, with the source chosen without branches.
+// One loader lane's share of a chunk's operand copies into an LDS slot (float4 units).  Unit u of
+// the slot comes from: matrix rows of the record (un-swizzled), the 16 x 16 vector block (U0 or Z0),
+// the dO rows of tokens t0 .. t0 + 15 (clamped to the last token; the compute side zeroes rows past
+// the end), e^{Gam}.  Every loader wave issues exactly PER instructions per chunk.  Where each of
+// this lane's units comes from is the same for every chunk up to the chunk's base (its record, or
+// its first token's dO row), so the offsets are worked out once.
 template <int DK, int NMAT, bool WITH_DO, typename TIn>
-__device__ __forceinline__ void load_slot(float4* slot, const float* rec, int64_t off_vec, int64_t off_eg,
-                                          const TIn* dO_head, int64_t t0, int64_t T, int dv, int d0, int lw,
-                                          int lane) {
+struct SlotPlan {
   using SL = ChainSlot<DK, NMAT, WITH_DO, TIn>;
-  constexpr int Q = SL::Q, NL = ChainDims<DK>::NL;
-  constexpr int PER = (SL::NI + NL - 1) / NL;
-  constexpr int UPR = CH * (int)sizeof(TIn) / 16;          // dO units per row
-#pragma unroll
-  for (int k = 0; k < PER; ++k) {
-    int ins = lw + k * NL;
-    if (ins >= SL::NI) ins = SL::NI - 1;       // the last instruction again: same bytes, same place
-    const int u = ins * 64 + lane;
-    const int um = u < SL::O_VEC ? u : 0;
-    const int mat = um / SL::MAT, vm = um % SL::MAT, r = vm / Q, c4 = (vm % Q) ^ (r % Q);
-    const char* s_mat = reinterpret_cast<const char*>(rec + (int64_t)mat * C * DK + r * DK + 4 * c4);
-    const int vv = min(max(u - SL::O_VEC, 0), SL::VEC - 1);
-    const char* s_vec = reinterpret_cast<const char*>(rec + off_vec + (vv / 4) * dv + d0 + 4 * (vv % 4));
-    const char* s_do = s_vec;
-    if (WITH_DO) {
-      const int vd = min(max(u - SL::O_DO, 0), (SL::DOU > 0 ? SL::DOU : 1) - 1);
-      const int64_t t = min(t0 + vd / UPR, T - 1);
-      s_do = reinterpret_cast<const char*>(dO_head + t * dv + d0) + 16 * (vd % UPR);
-    }
-    const int ve = min(max(u - SL::O_EG, 0), Q - 1);
-    const char* s_eg = reinterpret_cast<const char*>(rec + off_eg + 4 * ve);
-    const char* src = u < SL::O_VEC ? s_mat : (u < SL::O_DO ? s_vec : (u < SL::O_EG ? s_do : s_eg));
-    if (u < SL::UNITS) dma16(src, slot + ins * 64);
-  }
-}
+  static constexpr int NL = ChainDims<DK>::NL;
+  static constexpr int PER = (SL::NI + NL - 1) / NL;
+  int off[PER];    // bytes from the record, or (row >= 0) from the start of dO row t0 + row
+  int row[PER];
+  bool on[PER];
+  int lw;
 
-// forward chain: states[n] = S entering chunk n
-template <int DK>
-__global__ __launch_bounds__(ChainDims<DK>::NT) void bwd_state_kernel(Params p, const float* __restrict__ recs,
-                                                                     float* __restrict__ states) {
+  __device__ __forceinline__ SlotPlan(int64_t off_vec, int64_t off_eg, int dv, int d0, int lw_, int lane) : lw(lw_) {
+    constexpr int Q = SL::Q;
+    constexpr int UPR = CH * (int)sizeof(TIn) / 16;          // dO units per row
+#pragma unroll
+    for (int k = 0; k < PER; ++k) {
+      const int u = ins(k) * 64 + lane;
+      on[k] = u < SL::UNITS;
+      row[k] = -1;
+      if (u < SL::O_VEC) {
+        const int mat = u / SL::MAT, vm = u % SL::MAT, r = vm / Q, c4 = (vm % Q) ^ (r % Q);
+        off[k] = 4 * (mat * C * DK + r * DK + 4 * c4);
+      } else if (u < SL::O_DO) {
+        const int vv = u - SL::O_VEC;
+        off[k] = 4 * ((int)off_vec + (vv / 4) * dv + d0 + 4 * (vv % 4));
+      } else if (u < SL::O_EG) {
+        const int vd = u - SL::O_DO;
+        row[k] = vd / UPR;
+        off[k] = (int)sizeof(TIn) * d0 + 16 * (vd % UPR);
+      } else {
+        off[k] = 4 * ((int)off_eg + 4 * min(u - SL::O_EG, Q - 1));
+      }
+    }
+  }
+  // instruction k of this wave (the last one repeated where the waves' shares are uneven: same
+  // bytes to the same place)
+  __device__ __forceinline__ int ins(int k) const { return min(lw + k * NL, SL::NI - 1); }
+
+  __device__ __forceinline__ void issue(float4* slot, const float* rec, const TIn* dO_head, int64_t t0, int64_t T,
+                                        int dv) const {
+    const char* rb = reinterpret_cast<const char*>(rec);
+#pragma unroll
+    for (int k = 0; k < PER; ++k) {
+      const char* src = rb + off[k];
+      if (WITH_DO && row[k] >= 0) {
+        const int64_t t = min(t0 + row[k], T - 1);
+        src = reinterpret_cast<const char*>(dO_head + t * dv) + off[k];
+      }
+      if (on[k]) dma16(src, slot + ins(k) * 64);
+    }
+  }
+};
+
+template <typename TIn, int DK>
+struct ChainLds {   // float4 units of LDS: the ring (sized for the reverse chain's larger slot), partial sums
+  using Dm = ChainDims<DK>;
+  static constexpr int R = kDepth;
+  static constexpr int SLOT = ChainSlot<DK, 3, true, TIn>::UNITS;
+  static constexpr int PART = 2 * Dm::NW * 64;   // [step parity][wavefront][lane]
+  static constexpr int UNITS = R * SLOT + PART;
+};
+
+// forward chain: states[n] = S entering chunk n.  Per chunk, with S held as described above:
+//   Y = U0 - W S (16 x 16 x dk, one 16-key share per wavefront, partials summed by every wavefront)
+//   S <- e^{Gam} S + Ktil^T Y
+// The operands of step n + 1 are read from LDS right after step n's barrier, while step n's update runs.
+template <typename TIn, int DK>
+__device__ __forceinline__ void state_chain(const Params& p, const float* __restrict__ recs,
+                                            float* __restrict__ states, float4* smem, int64_t L) {
   using Dm = ChainDims<DK>;
   using SL = ChainSlot<DK, 2, false, float>;
-  constexpr int NW = Dm::NW, NL = Dm::NL, NCT = NW * 64, R = kDepth + 1;
-  constexpr int PER = (SL::NI + NL - 1) / NL;
-  __shared__ __align__(16) float4 ring[R][SL::UNITS];
-  __shared__ float part[NW][C][CH + 1];
-  __shared__ float Y[C][CH + 1];
+  using LD = ChainLds<TIn, DK>;
+  using Plan = SlotPlan<DK, 2, false, float>;
+  constexpr int NW = Dm::NW, R = LD::R, PER = Plan::PER;
+  float4 (*part)[NW][64] = reinterpret_cast<float4 (*)[NW][64]>(smem + R * LD::SLOT);
   const int tid = threadIdx.x, lane = tid % 64, w = tid / 64;
   const bool loader = w >= NW;
   const int dv = (int)p.dv, nsl = dv / CH;
-  const int64_t nblk = p.B * p.H * nsl, L = xcd_block(nblk);
   const int64_t bh = L / nsl;
   const int sl = (int)(L % nsl), d0 = sl * CH;
   const int64_t NC = p.n_chunks();
@@ -459,86 +493,96 @@ __global__ __launch_bounds__(ChainDims<DK>::NT) void bwd_state_kernel(Params p, 
   const float* rec_bh = recs + bh * NC * RF;
   const int col = lane % 16, g = lane / 16;
 
+  if (loader) {
+    const Plan plan(off_u0(DK), off_eg(DK, dv), dv, d0, w - NW, lane);
+    auto issue = [&](int64_t m) {           // chunk m (clamped) into its ring slot
+      const int64_t mc = m < NC ? m : NC - 1;
+      plan.issue(smem + (m % R) * LD::SLOT, rec_bh + mc * RF, (const float*)nullptr, 0, 1, dv);
+    };
+#pragma unroll
+    for (int k = 0; k < kDepth; ++k) issue(k);
+    vm_wait<PER * (kDepth - 2)>();            // chunks 0 and 1 have landed
+    lds_barrier();
+    for (int64_t n = 0; n < NC; ++n) {
+      vm_wait<PER * (kDepth - 2)>();          // chunk n + 1 has landed (n + 2 .. n + kDepth - 1 may not)
+      lds_barrier();
+      issue(n + kDepth);                      // into the slot chunk n used (all its reads were before)
+    }
+    vm_wait<0>();
+    return;
+  }
+
   f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-  if (!loader && p.S0) {
+  if (p.S0) {
 #pragma unroll
     for (int i = 0; i < 4; ++i) acc[i] = p.S0[(bh * DK + 16 * w + 4 * g + i) * dv + d0 + col];
   }
-  auto issue = [&](int64_t m) {             // loader: chunk m (clamped) into its ring slot
-    const int64_t mc = m < NC ? m : NC - 1;
-    load_slot<DK, 2, false, float>(ring[m % R], rec_bh + mc * RF, off_u0(DK), off_eg(DK, dv), (const float*)nullptr,
-                                   0, 1, dv, d0, w - NW, lane);
-  };
-
-  if (loader) {
-#pragma unroll
-    for (int k = 0; k < kDepth; ++k) issue(k);
-    vm_wait<PER * (kDepth - 1)>();
-  }
-  lds_barrier();
-  for (int64_t n = 0; n < NC; ++n) {
-    const float4* sv = ring[n % R];
+  float4 wv, e4;
+  f32x4 u0;
+  float ka[4];
+  auto operands = [&](int64_t n) {          // step n's operands from its slot
+    const float4* sv = smem + (n % R) * LD::SLOT;
     const float* sf = reinterpret_cast<const float*>(sv);
-    if (!loader) {
-      float* st = states + ((bh * NC + n) * nsl + sl) * DK * CH + w * 256 + lane;
+    const float* kt = sf + 4 * SL::MAT;
+    const int c = 16 * w + col;
+    wv = sv[swz<DK>(col, 4 * w + g)];                        // W[col][16w + 4g + s]
+    e4 = sv[SL::O_EG + 4 * w + g];
 #pragma unroll
-      for (int i = 0; i < 4; ++i) st[i * 64] = acc[i];
-      const float4 wv = sv[swz<DK>(col, 4 * w + g)];
-      f32x4 yp = {0.f, 0.f, 0.f, 0.f};
-      yp = mfma4(wv.x, acc[0], yp);
-      yp = mfma4(wv.y, acc[1], yp);
-      yp = mfma4(wv.z, acc[2], yp);
-      yp = mfma4(wv.w, acc[3], yp);
-#pragma unroll
-      for (int i = 0; i < 4; ++i) part[w][4 * g + i][col] = yp[i];
+    for (int s = 0; s < 4; ++s) {
+      ka[s] = kt[4 * swz<DK>(4 * g + s, c / 4) + c % 4];    // Ktil[4g + s][16w + col]
+      u0[s] = sf[4 * SL::O_VEC + (4 * g + s) * CH + col];
     }
+  };
+  lds_barrier();
+  operands(0);
+  for (int64_t n = 0; n < NC; ++n) {
+    const int pb = (int)(n & 1);
+    float* st = states + ((bh * NC + n) * nsl + sl) * DK * CH + w * 256 + lane;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) st[i * 64] = acc[i];
+    f32x4 yp = {0.f, 0.f, 0.f, 0.f};
+    yp = mfma4(wv.x, acc[0], yp);
+    yp = mfma4(wv.y, acc[1], yp);
+    yp = mfma4(wv.z, acc[2], yp);
+    yp = mfma4(wv.w, acc[3], yp);
+    part[pb][w][lane] = make_float4(yp[0], yp[1], yp[2], yp[3]);
     lds_barrier();
-    if (!loader) {
-      for (int e = tid; e < C * CH; e += NCT) {
-        const int r = e / CH, d = e % CH;
-        float y = sf[4 * SL::O_VEC + e];
+    f32x4 y = u0;
+    const f32x4 eg = {e4.x, e4.y, e4.z, e4.w};
+    float kc[4];
 #pragma unroll
-        for (int v = 0; v < NW; ++v) y -= part[v][r][d];
-        Y[r][d] = y;
-      }
-    } else {
-      issue(n + kDepth);
-      vm_wait<PER * (kDepth - 1)>();           // chunk n + 1 has landed
+    for (int s = 0; s < 4; ++s) kc[s] = ka[s];
+#pragma unroll
+    for (int v = 0; v < NW; ++v) {
+      const float4 pv = part[pb][v][lane];
+      y[0] -= pv.x; y[1] -= pv.y; y[2] -= pv.z; y[3] -= pv.w;
     }
-    lds_barrier();
-    if (!loader) {
-      const float* eg = sf + 4 * SL::O_EG;
+    operands(n + 1);                         // landed before this barrier (a clamped copy past the end)
 #pragma unroll
-      for (int i = 0; i < 4; ++i) acc[i] *= eg[16 * w + 4 * g + i];
-      const float* kt = sf + 4 * SL::MAT;
+    for (int i = 0; i < 4; ++i) acc[i] *= eg[i];
 #pragma unroll
-      for (int s4 = 0; s4 < 4; ++s4) {
-        const int r = 4 * s4 + g, c = 16 * w + col;
-        acc = mfma4(kt[4 * swz<DK>(r, c / 4) + c % 4], Y[r][col], acc);
-      }
-    }
+    for (int s = 0; s < 4; ++s) acc = mfma4(kc[s], y[s], acc);
   }
-  if (loader) vm_wait<0>();
 }
 
-// reverse chain: dstates[n] = dL/dS leaving chunk n; dS0 = dL/dS entering chunk 0
+// reverse chain: dstates[n] = dL/dS leaving chunk n; dS0 = dL/dS entering chunk 0.  Per chunk:
+//   Z = Z0 + Ktil dS'  (partials summed by every wavefront as above)
+//   dS <- e^{Gam} dS' + Qbar^T dO - W^T Z
+// Qbar^T dO does not depend on the chain: it is formed for step it + 1 while step it's update runs.
 template <typename TIn, int DK>
-__global__ __launch_bounds__(ChainDims<DK>::NT) void bwd_dstate_kernel(Params p, const void* __restrict__ dO_in,
-                                                                      const float* __restrict__ dSf,
-                                                                      const float* __restrict__ recs,
-                                                                      float* __restrict__ dstates,
-                                                                      float* __restrict__ dS0) {
+__device__ __forceinline__ void dstate_chain(const Params& p, const void* __restrict__ dO_in,
+                                             const float* __restrict__ dSf, const float* __restrict__ recs,
+                                             float* __restrict__ dstates, float* __restrict__ dS0, float4* smem,
+                                             int64_t L) {
   using Dm = ChainDims<DK>;
   using SL = ChainSlot<DK, 3, true, TIn>;
-  constexpr int NW = Dm::NW, NL = Dm::NL, NCT = NW * 64, R = kDepth + 1;
-  constexpr int PER = (SL::NI + NL - 1) / NL;
-  __shared__ __align__(16) float4 ring[R][SL::UNITS];
-  __shared__ float part[NW][C][CH + 1];
-  __shared__ float Z[C][CH + 1];
+  using LD = ChainLds<TIn, DK>;
+  using Plan = SlotPlan<DK, 3, true, TIn>;
+  constexpr int NW = Dm::NW, R = LD::R, PER = Plan::PER;
+  float4 (*part)[NW][64] = reinterpret_cast<float4 (*)[NW][64]>(smem + R * LD::SLOT);
   const int tid = threadIdx.x, lane = tid % 64, w = tid / 64;
   const bool loader = w >= NW;
   const int dv = (int)p.dv, nsl = dv / CH;
-  const int64_t nblk = p.B * p.H * nsl, L = xcd_block(nblk);
   const int64_t bh = L / nsl;
   const int sl = (int)(L % nsl), d0 = sl * CH;
   const int64_t T = p.T, NC = p.n_chunks();
@@ -547,81 +591,109 @@ __global__ __launch_bounds__(ChainDims<DK>::NT) void bwd_dstate_kernel(Params p,
   const TIn* dO = (const TIn*)dO_in + bh * T * dv;
   const int col = lane % 16, g = lane / 16;
 
+  if (loader) {
+    const Plan plan(off_z0(DK, dv), off_eg(DK, dv), dv, d0, w - NW, lane);
+    auto issue = [&](int64_t it) {          // step it (chunk NC - 1 - it, clamped)
+      int64_t m = NC - 1 - it;
+      if (m < 0) m = 0;
+      plan.issue(smem + (it % R) * LD::SLOT, rec_bh + m * RF, dO, m * C, T, dv);
+    };
+#pragma unroll
+    for (int k = 0; k < kDepth; ++k) issue(k);
+    vm_wait<PER * (kDepth - 2)>();
+    lds_barrier();
+    for (int64_t it = 0; it < NC; ++it) {
+      vm_wait<PER * (kDepth - 2)>();
+      lds_barrier();
+      issue(it + kDepth);
+    }
+    vm_wait<0>();
+    return;
+  }
+
   f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-  if (!loader && dSf) {
+  if (dSf) {
 #pragma unroll
     for (int i = 0; i < 4; ++i) acc[i] = dSf[(bh * DK + 16 * w + 4 * g + i) * dv + d0 + col];
   }
-  auto issue = [&](int64_t it) {            // loader: step it (chunk NC - 1 - it, clamped)
-    int64_t m = NC - 1 - it;
-    if (m < 0) m = 0;
-    load_slot<DK, 3, true, TIn>(ring[it % R], rec_bh + m * RF, off_z0(DK, dv), off_eg(DK, dv), dO, m * C, T, dv, d0,
-                                w - NW, lane);
-  };
-
-  if (loader) {
+  float4 kv, e4;
+  f32x4 z0, qd;
+  float wa[4];
+  auto operands = [&](int64_t it) {         // step it's operands from its slot, and its Qbar^T dO
+    const float4* sv = smem + (it % R) * LD::SLOT;
+    const float* sf = reinterpret_cast<const float*>(sv);
+    const float* qb = sf + 4 * 2 * SL::MAT;
+    const TIn* dOl = reinterpret_cast<const TIn*>(sv + SL::O_DO);
+    const int64_t t0 = (NC - 1 - it) * C;
+    const int c = 16 * w + col;
+    kv = sv[SL::MAT + swz<DK>(col, 4 * w + g)];               // Ktil[col][16w + 4g + s]
+    e4 = sv[SL::O_EG + 4 * w + g];
+    float qa[4], ob[4];
 #pragma unroll
-    for (int k = 0; k < kDepth; ++k) issue(k);
-    vm_wait<PER * (kDepth - 1)>();
-  }
+    for (int s = 0; s < 4; ++s) {
+      const int r = 4 * g + s;
+      const float o = load_f32(dOl, r * CH + col);
+      ob[s] = t0 + r < T ? o : 0.f;                           // rows past the end hold a clamped copy
+      qa[s] = qb[4 * swz<DK>(r, c / 4) + c % 4];
+      wa[s] = -sf[4 * swz<DK>(r, c / 4) + c % 4];
+      z0[s] = sf[4 * SL::O_VEC + r * CH + col];
+    }
+    qd = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int s = 0; s < 4; ++s) qd = mfma4(qa[s], ob[s], qd);
+  };
   lds_barrier();
+  operands(0);
   for (int64_t it = 0; it < NC; ++it) {
     const int64_t n = NC - 1 - it;
-    const float4* sv = ring[it % R];
-    const float* sf = reinterpret_cast<const float*>(sv);
-    if (!loader) {
-      float* st = dstates + ((bh * NC + n) * nsl + sl) * DK * CH + w * 256 + lane;
+    const int pb = (int)(it & 1);
+    float* st = dstates + ((bh * NC + n) * nsl + sl) * DK * CH + w * 256 + lane;
 #pragma unroll
-      for (int i = 0; i < 4; ++i) st[i * 64] = acc[i];
-      const float4 kv = sv[SL::MAT + swz<DK>(col, 4 * w + g)];
-      f32x4 zp = {0.f, 0.f, 0.f, 0.f};
-      zp = mfma4(kv.x, acc[0], zp);
-      zp = mfma4(kv.y, acc[1], zp);
-      zp = mfma4(kv.z, acc[2], zp);
-      zp = mfma4(kv.w, acc[3], zp);
-#pragma unroll
-      for (int i = 0; i < 4; ++i) part[w][4 * g + i][col] = zp[i];
-    }
+    for (int i = 0; i < 4; ++i) st[i * 64] = acc[i];
+    f32x4 zp = {0.f, 0.f, 0.f, 0.f};
+    zp = mfma4(kv.x, acc[0], zp);
+    zp = mfma4(kv.y, acc[1], zp);
+    zp = mfma4(kv.z, acc[2], zp);
+    zp = mfma4(kv.w, acc[3], zp);
+    part[pb][w][lane] = make_float4(zp[0], zp[1], zp[2], zp[3]);
     lds_barrier();
-    if (!loader) {
-      for (int e = tid; e < C * CH; e += NCT) {
-        const int r = e / CH, d = e % CH;
-        float z = sf[4 * SL::O_VEC + e];
+    f32x4 z = z0;
+    const f32x4 eg = {e4.x, e4.y, e4.z, e4.w};
+    const f32x4 qc = qd;
+    float wc[4];
 #pragma unroll
-        for (int v = 0; v < NW; ++v) z += part[v][r][d];
-        Z[r][d] = z;
-      }
-    } else {
-      issue(it + kDepth);
-      vm_wait<PER * (kDepth - 1)>();           // the next step's chunk has landed
+    for (int s = 0; s < 4; ++s) wc[s] = wa[s];
+#pragma unroll
+    for (int v = 0; v < NW; ++v) {
+      const float4 pv = part[pb][v][lane];
+      z[0] += pv.x; z[1] += pv.y; z[2] += pv.z; z[3] += pv.w;
     }
-    lds_barrier();
-    if (!loader) {
-      const float* eg = sf + 4 * SL::O_EG;
+    operands(it + 1);
 #pragma unroll
-      for (int i = 0; i < 4; ++i) acc[i] *= eg[16 * w + 4 * g + i];
-      const float* qb = sf + 4 * 2 * SL::MAT;
-      const float* wm = sf;
-      const TIn* dOl = reinterpret_cast<const TIn*>(sv + SL::O_DO);
-      const int64_t t0 = n * C;
+    for (int i = 0; i < 4; ++i) acc[i] = acc[i] * eg[i] + qc[i];
 #pragma unroll
-      for (int s4 = 0; s4 < 4; ++s4) {
-        const int r = 4 * s4 + g, c = 16 * w + col;
-        const float o = t0 + r < T ? load_f32(dOl, r * CH + col) : 0.f;
-        acc = mfma4(qb[4 * swz<DK>(r, c / 4) + c % 4], o, acc);
-      }
-#pragma unroll
-      for (int s4 = 0; s4 < 4; ++s4) {
-        const int r = 4 * s4 + g, c = 16 * w + col;
-        acc = mfma4(-wm[4 * swz<DK>(r, c / 4) + c % 4], Z[r][col], acc);
-      }
-    }
+    for (int s = 0; s < 4; ++s) acc = mfma4(wc[s], z[s], acc);
   }
-  if (loader) vm_wait<0>();
-  if (dS0 && !loader) {
+  if (dS0) {
 #pragma unroll
     for (int i = 0; i < 4; ++i) dS0[(bh * DK + 16 * w + 4 * g + i) * dv + d0 + col] = acc[i];
   }
+}
+
+// both chains in one launch (they are independent): blocks [0, nchain) run the forward chain,
+// [nchain, 2 nchain) the reverse one
+template <typename TIn, int DK>
+__global__ __launch_bounds__(ChainDims<DK>::NT) void bwd_chain_kernel(Params p, const void* __restrict__ dO_in,
+                                                                      const float* __restrict__ dSf,
+                                                                      const float* __restrict__ recs,
+                                                                      float* __restrict__ states,
+                                                                      float* __restrict__ dstates,
+                                                                      float* __restrict__ dS0) {
+  __shared__ __align__(16) float4 smem[ChainLds<TIn, DK>::UNITS];
+  const int64_t nchain = p.B * p.H * (p.dv / CH);
+  const int64_t b = blockIdx.x;
+  if (b < nchain) state_chain<TIn, DK>(p, recs, states, smem, xcd_block(b, nchain));
+  else dstate_chain<TIn, DK>(p, dO_in, dSf, recs, dstates, dS0, smem, xcd_block(b - nchain, nchain));
 }
 
 // ---------------------------------------------------------------- grad: one workgroup per chunk
@@ -1040,11 +1112,8 @@ hipError_t launch_bwd_dk(const BwdParams& b, hipStream_t s) {
   hipLaunchKernelGGL((bwd_prep_kernel<TIn, DK>), dim3(nchunks), dim3(NTP), 0, s, p, b.dO, L.recs);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL((bwd_state_kernel<DK>), dim3(nchain), dim3(ChainDims<DK>::NT), 0, s, p, (const float*)L.recs,
-                     L.states);
-  if ((e = hipGetLastError()) != hipSuccess) return e;
-  hipLaunchKernelGGL((bwd_dstate_kernel<TIn, DK>), dim3(nchain), dim3(ChainDims<DK>::NT), 0, s, p, b.dO, b.dSf,
-                     (const float*)L.recs, L.dstates, b.dS0);
+  hipLaunchKernelGGL((bwd_chain_kernel<TIn, DK>), dim3(2 * nchain), dim3(ChainDims<DK>::NT), 0, s, p, b.dO, b.dSf,
+                     (const float*)L.recs, L.states, L.dstates, b.dS0);
   if ((e = hipGetLastError()) != hipSuccess) return e;
   hipLaunchKernelGGL((bwd_grad_kernel<TIn, DK>), dim3(nchunks), dim3(NTG), sizeof(GradShared<DK>), s, p, b.dO,
                      (const float*)L.states, (const float*)L.dstates, b.dq, b.dk, b.dv, b.dw, b.dbeta);
