@@ -75,6 +75,26 @@ __device__ __forceinline__ float ex2(float x) { return __builtin_amdgcn_exp2f(x)
 
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 
+__device__ __forceinline__ void compiler_fence() { __atomic_signal_fence(__ATOMIC_SEQ_CST); }
+
+// barrier that waits for this wave's LDS operations only (global loads and stores stay in flight)
+__device__ __forceinline__ void lds_barrier() {
+  compiler_fence();
+  __builtin_amdgcn_s_waitcnt(0xF | (0x3 << 14) | (0x7 << 4) | (0x0 << 8));   // lgkmcnt(0)
+  __builtin_amdgcn_s_barrier();
+  compiler_fence();
+}
+
+// four consecutive elements p[i .. i + 3] as fp32 (i a multiple of 4; rows start 16-byte aligned)
+__device__ __forceinline__ float4 load4_f32(const float* p, int64_t i) {
+  return *reinterpret_cast<const float4*>(p + i);
+}
+__device__ __forceinline__ float4 load4_f32(const uint16_t* p, int64_t i) {
+  const uint2 u = *reinterpret_cast<const uint2*>(p + i);
+  return make_float4(__uint_as_float(u.x << 16), __uint_as_float(u.x & 0xFFFF0000u), __uint_as_float(u.y << 16),
+                     __uint_as_float(u.y & 0xFFFF0000u));
+}
+
 // value of lane src (0..3) of this lane's group of four, through a DPP quad permute
 __device__ __forceinline__ float quad_bcast(float v, int src) {   // src is a constant after unrolling
   const int b = __float_as_int(v);
@@ -130,31 +150,38 @@ __device__ void chunk_setup(ChunkCore<DK>& cc, float* scratch, const Params& p, 
   const TIn* k = (const TIn*)p.k + bh * T * DK;
   const TIn* w = (const TIn*)p.w + bh * T * DK;
   const TIn* beta = (const TIn*)p.beta + bh * T;
-  {   // every load issued before the first use (one memory latency, not one per element)
-    constexpr int PER = (C * DK + NT - 1) / NT;
-    float lq[PER], lk[PER], lw[PER];
+  {   // every load issued before the first use, four channels per thread, with no branch around a load
+      // (addresses clamped into the chunk, rows past its end zeroed afterwards)
+    constexpr int N4 = C * DK / 4, PER = (N4 + NT - 1) / NT;
+    float4 lq[PER], lk[PER], lw[PER];
 #pragma unroll
     for (int m = 0; m < PER; ++m) {
-      const int i = tid + m * NT;
-      const int r = i / DK, c = i % DK;
-      const bool ok = i < C * DK && r < len;
-      const int64_t idx = ok ? (t0 + r) * DK + c : 0;
-      lq[m] = ok ? load_f32(q, idx) : 0.f;
-      lk[m] = ok ? load_f32(k, idx) : 0.f;
-      lw[m] = ok ? load_f32(w, idx) : 0.f;
+      const int i = min(tid + m * NT, N4 - 1);
+      const int r = min(4 * i / DK, len - 1), c = 4 * i % DK;
+      const int64_t idx = (t0 + r) * DK + c;
+      lq[m] = load4_f32(q, idx);
+      lk[m] = load4_f32(k, idx);
+      lw[m] = load4_f32(w, idx);
     }
-    const float lb = (tid < C && tid < len) ? load_f32(beta, t0 + tid) : 0.f;
+    const float lb = load_f32(beta, t0 + min(tid % C, len - 1));
 #pragma unroll
     for (int m = 0; m < PER; ++m) {
       const int i = tid + m * NT;
-      if (i < C * DK) {
-        const int r = i / DK, c = i % DK;
-        cc.q[r][c] = lq[m];
-        cc.k[r][c] = lk[m];
-        cc.G[r][c] = r < len ? gate_f32(lw[m], p.g_min, p.unbounded) * kLog2eB : 0.f;
+      if (i < N4) {
+        const int r = 4 * i / DK, c = 4 * i % DK;
+        const bool ok = r < len;
+        const float qv[4] = {lq[m].x, lq[m].y, lq[m].z, lq[m].w};
+        const float kv[4] = {lk[m].x, lk[m].y, lk[m].z, lk[m].w};
+        const float wv[4] = {lw[m].x, lw[m].y, lw[m].z, lw[m].w};
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          cc.q[r][c + j] = ok ? qv[j] : 0.f;
+          cc.k[r][c + j] = ok ? kv[j] : 0.f;
+          cc.G[r][c + j] = ok ? gate_f32(wv[j], p.g_min, p.unbounded) * kLog2eB : 0.f;
+        }
       }
     }
-    if (tid < C) cc.beta[tid] = lb;
+    if (tid < C) cc.beta[tid] = tid < len ? lb : 0.f;
   }
   __syncthreads();
   if (tid < DK) {
@@ -245,8 +272,7 @@ __device__ void chunk_setup(ChunkCore<DK>& cc, float* scratch, const Params& p, 
     for (int m = C - 1; m >= 1; --m) {
       const float x = quad_bcast(t[m & 3], m >> 2) * cc.beta[m];
 #pragma unroll
-      for (int c = 0; c < 4; ++c)
-        if (4 * q + c < m) t[c] -= x * cc.X[m][4 * q + c];
+      for (int c = 0; c < 4; ++c) t[c] -= x * cc.X[m][4 * q + c];   // X[m][j] = 0 for j >= m
     }
 #pragma unroll
     for (int c = 0; c < 4; ++c) {
@@ -275,10 +301,21 @@ __global__ __launch_bounds__(NTP) void bwd_prep_kernel(Params p, const void* __r
   const int64_t T = p.T, t0 = n * C;
   const int len = (int)((T - t0) < C ? (T - t0) : C);
   const int dv = (int)p.dv;
-  chunk_setup<TIn, DK, NTP>(sm.cc, &sm.bv[0][0], p, bh, n, len);   // bv, go: 2 * 4 * 256 floats of scratch
-  float* rec = recs + (bh * NC + n) * rec_floats(DK, dv);
   const TIn* v = (const TIn*)p.v + bh * T * dv;
   const TIn* dO = (const TIn*)dO_in + bh * T * dv;
+  constexpr int PER = C * 128 / NTP;          // dv <= 128
+  float lv[PER], lo[PER];
+#pragma unroll
+  for (int m = 0; m < PER; ++m) {             // issued with the setup's loads: one memory latency
+    const int i = tid + m * NTP, r = i / dv, d = i % dv;
+    const bool ok = i < C * dv && r < len;
+    const int64_t o = (t0 + min(r, len - 1)) * dv + (i < C * dv ? d : 0);   // no branch around the load
+    const float x = load_f32(v, o), y = load_f32(dO, o);
+    lv[m] = ok ? x : 0.f;
+    lo[m] = ok ? y : 0.f;
+  }
+  chunk_setup<TIn, DK, NTP>(sm.cc, &sm.bv[0][0], p, bh, n, len);   // bv, go: 2 * 4 * 256 floats of scratch
+  float* rec = recs + (bh * NC + n) * rec_floats(DK, dv);
   for (int i = tid; i < C * DK; i += NTP) {
     const int r = i / DK, c = i % DK;
     const float G = sm.cc.G[r][c], eG = ex2(G);
@@ -286,41 +323,38 @@ __global__ __launch_bounds__(NTP) void bwd_prep_kernel(Params p, const void* __r
     rec[off_kt(DK) + i] = sm.cc.k[r][c] * ex2(sm.cc.gam[c] - G);
     rec[off_qb(DK) + i] = sm.cc.q[r][c] * eG;
   }
-  {
-    constexpr int PER = C * 128 / NTP;        // dv <= 128
-    float lv[PER], lo[PER];
 #pragma unroll
-    for (int m = 0; m < PER; ++m) {
-      const int i = tid + m * NTP, r = i / dv, d = i % dv;
-      const bool ok = i < C * dv && r < len;
-      lv[m] = ok ? load_f32(v, (t0 + r) * dv + d) : 0.f;
-      lo[m] = ok ? load_f32(dO, (t0 + r) * dv + d) : 0.f;
-    }
-#pragma unroll
-    for (int m = 0; m < PER; ++m) {
-      const int i = tid + m * NTP, r = i / dv, d = i % dv;
-      if (i < C * dv) {
-        sm.bv[r][d] = sm.cc.beta[r] * lv[m];
-        sm.go[r][d] = lo[m];
-      }
+  for (int m = 0; m < PER; ++m) {
+    const int i = tid + m * NTP, r = i / dv, d = i % dv;
+    if (i < C * dv) {
+      sm.bv[r][d] = sm.cc.beta[r] * lv[m];
+      sm.go[r][d] = lo[m];
     }
   }
   if (tid < DK) rec[off_eg(DK, dv) + tid] = ex2(sm.cc.gam[tid]);
-  __syncthreads();
-  for (int i = tid; i < C * DK; i += NTP) {
-    const int r = i / DK, c = i % DK;
-    float acc = 0.f;
-    for (int j = 0; j <= r; ++j) acc += sm.cc.T[r][j] * sm.kb[j][c];
-    rec[i] = acc;
-  }
-  for (int i = tid; i < C * dv; i += NTP) {
-    const int r = i / dv, d = i % dv;
-    float acc = 0.f;
-    for (int j = 0; j <= r; ++j) acc += sm.cc.T[r][j] * sm.bv[j][d];
-    rec[off_u0(DK) + i] = acc;
-    float z = 0.f;
-    for (int j = r; j < C; ++j) z += sm.cc.P[j][r] * sm.go[j][d];
-    rec[off_z0(DK, dv) + i] = z;
+  lds_barrier();                              // orders LDS only: the record stores stay in flight
+  // W = T diag(beta) Kbar, U0 = T diag(beta) V, Z0 = P^T dO on the fp32 matrix cores, one 16 x 16 output
+  // tile per task (T and P are triangular with zeros stored outside), K index 4s + g at step s
+  {
+    const int lane = tid % 64, wv = tid / 64, col = lane % 16, g = lane / 16;
+    const int nk = DK / 16, nvb = dv / 16;
+    for (int task = wv; task < nk + 2 * nvb; task += NTP / 64) {
+      const int kind = task < nk ? 0 : (task < nk + nvb ? 1 : 2);
+      const int cb = kind == 0 ? task : (kind == 1 ? task - nk : task - nk - nvb);
+      const int c = 16 * cb + col;
+      f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int s4 = 0; s4 < 4; ++s4) {
+        const int kk = 4 * s4 + g;
+        const float a = kind == 2 ? sm.cc.P[kk][col] : sm.cc.T[col][kk];
+        const float b = kind == 0 ? sm.kb[kk][c] : (kind == 1 ? sm.bv[kk][c] : sm.go[kk][c]);
+        acc = mfma4(a, b, acc);
+      }
+      float* dst = rec + (kind == 0 ? 0 : (kind == 1 ? off_u0(DK) : off_z0(DK, dv)));
+      const int N = kind == 0 ? DK : dv;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) dst[(4 * g + i) * N + c] = acc[i];
+    }
   }
 }
 
@@ -347,16 +381,6 @@ __global__ __launch_bounds__(NTP) void bwd_prep_kernel(Params p, const void* __r
 
 typedef __attribute__((address_space(3))) void lds_void;
 typedef __attribute__((address_space(1))) void gbl_void;
-
-__device__ __forceinline__ void compiler_fence() { __atomic_signal_fence(__ATOMIC_SEQ_CST); }
-
-// barrier that waits for this wave's LDS operations only (global loads and stores stay in flight)
-__device__ __forceinline__ void lds_barrier() {
-  compiler_fence();
-  __builtin_amdgcn_s_waitcnt(0xF | (0x3 << 14) | (0x7 << 4) | (0x0 << 8));   // lgkmcnt(0)
-  __builtin_amdgcn_s_barrier();
-  compiler_fence();
-}
 
 // wait until at most N of this wave's vector-memory operations are outstanding
 template <int N>
@@ -761,7 +785,8 @@ __global__ __launch_bounds__(NTG) __attribute__((amdgpu_waves_per_eu(4, 4))) voi
 #pragma unroll
     for (int i = 0; i < RPT; ++i) {
       const int r = (tid % NPC) * RPT + i;
-      wr[i] = r < len ? load_f32(w_in, (t0 + r) * DK + tid / NPC) : 0.f;
+      const float x = load_f32(w_in, (t0 + min(r, len - 1)) * DK + tid / NPC);   // no branch around the load
+      wr[i] = r < len ? x : 0.f;
     }
   }
   // V and dO of every tile, element (er, ed) of each (threads < 256), loaded before the setup
@@ -770,11 +795,12 @@ __global__ __launch_bounds__(NTG) __attribute__((amdgpu_waves_per_eu(4, 4))) voi
   float vr[MAXT], orr[MAXT], dvr[MAXT];
 #pragma unroll
   for (int t = 0; t < MAXT; ++t) {
-    vr[t] = orr[t] = dvr[t] = 0.f;
-    if (tid < 256 && t < nsl && er < len) {
-      vr[t] = load_f32(v, (t0 + er) * dv + CH * t + ed);
-      orr[t] = load_f32(dO, (t0 + er) * dv + CH * t + ed);
-    }
+    dvr[t] = 0.f;
+    const bool ok = tid < 256 && t < nsl && er < len;   // loads in bounds for every thread, then selected
+    const int64_t o = (t0 + min(er, len - 1)) * dv + CH * min(t, nsl - 1) + ed;
+    const float x = load_f32(v, o), y = load_f32(dO, o);
+    vr[t] = ok ? x : 0.f;
+    orr[t] = ok ? y : 0.f;
   }
   chunk_setup<TIn, DK, NTG>(sm.cc, &sm.v.part[0][0][0], p, bh, n, len);   // part: 2 * 4 * 256 floats
 
