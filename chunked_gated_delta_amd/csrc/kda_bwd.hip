@@ -731,17 +731,18 @@ __global__ __launch_bounds__(ChainDims<DK>::NT) void bwd_chain_kernel(Params p, 
 template <int DK>
 struct GradShared {
   ChunkCore<DK> cc;
-  union {
+  union alignas(16) {                     // 16-byte aligned: read as float4
     float tile[2][2][DK * CH];            // [buffer][S, dS'] tiles in stored order, during the tile loop
     float g3[3][C][DK];                   // dq, dk, dG after it
   } u;
-  union {
+  union alignas(16) {
     float part[8][C][CH];                 // partial E (0..3) and Ktil dS' (4..7) of the tile; the
                                           // setup's partial pair sums before the tile loop
     float kt[C][DK];                      // dKtil o Ktil per row, after the tile loop
   } v;
   static_assert(sizeof(float) * 8 * C * CH >= sizeof(float) * 2 * 4 * C * C, "setup scratch");
-  float dO[C][CH + 4], E[C][CH + 4], U[C][CH + 4], dU[C][CH + 4], dR[C][CH + 4];
+  alignas(16) float dO[C][CH + 4];        // rows of 80 bytes: float4 reads stay aligned
+  float E[C][CH + 4], U[C][CH + 4], dU[C][CH + 4], dR[C][CH + 4];
   float dT[C][C + 1], dP[C][C + 1], M[C][C + 1];
   float rs[DK];                           // rowsum(dS' o S) per channel
 };
@@ -825,7 +826,8 @@ __global__ __launch_bounds__(NTG) __attribute__((amdgpu_waves_per_eu(4, 4))) voi
   f32x4 tacc[3];
 #pragma unroll
   for (int j = 0; j < 3; ++j) tacc[j] = f32x4{0.f, 0.f, 0.f, 0.f};
-  float accT = 0.f, accB = 0.f, accRS = 0.f;
+  float accT = 0.f, accRS = 0.f;
+  f32x4 tdp = {0.f, 0.f, 0.f, 0.f};   // wavefront 6: dT (before the diag(beta) scaling), 7: dP
 
   vm_wait<0>();
   lds_barrier();
@@ -895,32 +897,36 @@ __global__ __launch_bounds__(NTG) __attribute__((amdgpu_waves_per_eu(4, 4))) voi
         tacc[j] = mfma4(av.w, bv.w, tacc[j]);
       }
     }
-    if (tid < 256) {   // dT += dU R^T (lower part)
-      const int r = er, jj = ed;
-      if (jj <= r) {
-        float a = 0.f;
-#pragma unroll
-        for (int d = 0; d < CH; ++d) a += sm.dU[r][d] * sm.E[jj][d];
-        accT += sm.cc.beta[jj] * a;
-      }
-    } else {           // dP += dO U^T (lower part, diagonal included)
-      const int r = er, jj = ed;
-      if (jj <= r) {
-#pragma unroll
-        for (int d = 0; d < CH; ++d) accB += sm.dO[r][d] * sm.U[jj][d];
-      }
+    if (w >= 6) {      // dT += dU E^T (wavefront 6), dP += dO U^T (7): K = the tile's 16 columns, order 4g + s
+      const float(*A)[CH + 4] = w == 6 ? sm.dU : sm.dO;
+      const float(*B)[CH + 4] = w == 6 ? sm.E : sm.U;
+      const float4 av = *reinterpret_cast<const float4*>(&A[col][4 * g]);
+      const float4 bv = *reinterpret_cast<const float4*>(&B[col][4 * g]);
+      tdp = mfma4(av.x, bv.x, tdp);
+      tdp = mfma4(av.y, bv.y, tdp);
+      tdp = mfma4(av.z, bv.z, tdp);
+      tdp = mfma4(av.w, bv.w, tdp);
     }
-    if (tid < DK) {    // rowsum(dS' o S) over the tile's columns
+    if (tid < DK) {    // rowsum(dS' o S) over the tile's columns (16 consecutive floats of each block)
       const int c = tid;
       const int o = (c / 16) * 256 + (c % 4) * 64 + ((c % 16) / 4) * 16;
+      const float4* s4 = reinterpret_cast<const float4*>(St + o);
+      const float4* d4 = reinterpret_cast<const float4*>(dSt + o);
 #pragma unroll
-      for (int d = 0; d < CH; ++d) accRS += St[o + d] * dSt[o + d];
+      for (int q4 = 0; q4 < 4; ++q4) {
+        const float4 a = s4[q4], bq = d4[q4];
+        accRS += a.x * bq.x + a.y * bq.y + a.z * bq.z + a.w * bq.w;
+      }
     }
-    if (tid >= 256 && tid < 256 + C) {   // dbeta share: sum_d dR E (kept apart from dP's accumulator)
+    if (tid >= 256 && tid < 256 + C) {   // dbeta share: sum_d dR E, in accT of threads 256 .. 271
       const int r = tid - 256;
       float a = 0.f;
 #pragma unroll
-      for (int d = 0; d < CH; ++d) a += sm.dR[r][d] * sm.E[r][d];
+      for (int d = 0; d < CH; d += 4) {
+        const float4 x = *reinterpret_cast<const float4*>(&sm.dR[r][d]);
+        const float4 y = *reinterpret_cast<const float4*>(&sm.E[r][d]);
+        a += x.x * y.x + x.y * y.y + x.z * y.z + x.w * y.w;
+      }
       accT += a;
     }
     vm_wait<0>();      // the next tile pair has landed
@@ -933,9 +939,16 @@ __global__ __launch_bounds__(NTG) __attribute__((amdgpu_waves_per_eu(4, 4))) voi
       if (t < nsl) dvo[(bh * T + t0 + er) * dv + CH * t + ed] = dvr[t];
   }
   if (tid < DK) sm.rs[tid] = accRS;
-  // tid < 256: accT = dT[er][ed];  tid >= 256: accB = dP[er][ed];  tid 256..271: accT = dbeta share
-  if (tid < 256) sm.dT[er][ed] = accT;
-  else sm.dP[er][ed] = accB;
+  // wavefronts 6 and 7 hold dT and dP (lane: rows 4g + i, column col), lower parts kept;
+  // tid 256..271: accT = dbeta share
+  if (w >= 6) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int r = 4 * g + i;
+      if (w == 6) sm.dT[r][col] = col <= r ? sm.cc.beta[col] * tdp[i] : 0.f;
+      else sm.dP[r][col] = col <= r ? tdp[i] : 0.f;
+    }
+  }
   lds_barrier();
   if (tid < C * C) {   // M = T^T dT
     const int a = tid / C, bb = tid % C;
