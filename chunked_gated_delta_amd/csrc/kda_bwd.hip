@@ -743,9 +743,14 @@ struct GradShared {
   static_assert(sizeof(float) * 8 * C * CH >= sizeof(float) * 2 * 4 * C * C, "setup scratch");
   alignas(16) float dO[C][CH + 4];        // rows of 80 bytes: float4 reads stay aligned
   float E[C][CH + 4], U[C][CH + 4], dU[C][CH + 4], dR[C][CH + 4];
-  float dT[C][C + 1], dP[C][C + 1], M[C][C + 1];
+  float dT[C][C + 1], dP[C][C + 1];
+  union {
+    float Vt[C][CH + 4];                  // the value tile, during the tile loop
+    float M[C][C + 1];                    // T^T dT, after it
+  } vt;
   float rs[DK];                           // rowsum(dS' o S) per channel
 };
+static_assert(sizeof(GradShared<128>) <= 80 * 1024, "two gradient workgroups per compute unit (160 KiB of LDS)");
 
 template <typename TIn, int DK>
 __global__ __launch_bounds__(NTG) __attribute__((amdgpu_waves_per_eu(4, 4))) void bwd_grad_kernel(Params p, const void* __restrict__ dO_in,
@@ -793,10 +798,9 @@ __global__ __launch_bounds__(NTG) __attribute__((amdgpu_waves_per_eu(4, 4))) voi
   // V and dO of every tile, element (er, ed) of each (threads < 256), loaded before the setup
   const int er = (tid % 256) / CH, ed = tid % CH;   // element (row, column) of a 16 x 16 tile
   constexpr int MAXT = 128 / CH;
-  float vr[MAXT], orr[MAXT], dvr[MAXT];
+  float vr[MAXT], orr[MAXT];
 #pragma unroll
   for (int t = 0; t < MAXT; ++t) {
-    dvr[t] = 0.f;
     const bool ok = tid < 256 && t < nsl && er < len;   // loads in bounds for every thread, then selected
     const int64_t o = (t0 + min(er, len - 1)) * dv + CH * min(t, nsl - 1) + ed;
     const float x = load_f32(v, o), y = load_f32(dO, o);
@@ -838,8 +842,10 @@ __global__ __launch_bounds__(NTG) __attribute__((amdgpu_waves_per_eu(4, 4))) voi
     const float* St = sm.u.tile[b][0];
     const float* dSt = sm.u.tile[b][1];
     if (t + 1 < nsl) copy_tile(t + 1, b ^ 1);
-    const float vrd = vr[t];
-    if (tid < 256) sm.dO[er][ed] = orr[t];
+    if (tid < 256) {
+      sm.dO[er][ed] = orr[t];
+      sm.vt.Vt[er][ed] = vr[t];
+    }
     {   // partial E (Kbar S) or Ktil dS' over this wavefront's key blocks
       const float* B = eW ? St : dSt;
       f32x4 pp = {0.f, 0.f, 0.f, 0.f};
@@ -855,31 +861,56 @@ __global__ __launch_bounds__(NTG) __attribute__((amdgpu_waves_per_eu(4, 4))) voi
       for (int i = 0; i < 4; ++i) sm.v.part[w][4 * g + i][col] = pp[i];
     }
     lds_barrier();
-    if (tid < 256) {   // E = V - Kbar S
-      float e = vrd;
+    // One wavefront each, on 16 x 16 tiles in the accumulator layout (lane: rows 4g + i, column col), so
+    // that the first product's result is the second one's B operand (K index 4g + s at step s):
+    if (w == 0) {          // E = V - Kbar S;  U = T diag(beta) E
+      f32x4 e, u = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int q = 0; q < 4; ++q) e -= sm.v.part[q][er][ed];
-      sm.E[er][ed] = e;
-    } else {           // dU = Ktil dS' + P^T dO
-      float du = 0.f;
+      for (int i = 0; i < 4; ++i) {
+        const int r = 4 * g + i;
+        float x = sm.vt.Vt[r][col];
 #pragma unroll
-      for (int q = 0; q < 4; ++q) du += sm.v.part[4 + q][er][ed];
+        for (int q = 0; q < 4; ++q) x -= sm.v.part[q][r][col];
+        e[i] = x;
+      }
 #pragma unroll
-      for (int i = 0; i < C; ++i) du += sm.cc.P[i][er] * sm.dO[i][ed];   // P[i][er] = 0 for i < er
-      sm.dU[er][ed] = du;
-    }
-    lds_barrier();
-    if (tid < 256) {   // U = T diag(beta) E (T is lower triangular: zeros above the diagonal)
-      float u = 0.f;
+      for (int s4 = 0; s4 < 4; ++s4) u = mfma4(sm.cc.Tb[col][4 * g + s4], e[s4], u);
 #pragma unroll
-      for (int j = 0; j < C; ++j) u += sm.cc.Tb[er][j] * sm.E[j][ed];
-      sm.U[er][ed] = u;
-    } else {           // dR = T^T dU;  dv = diag(beta) dR
-      float dr = 0.f;
+      for (int i = 0; i < 4; ++i) {
+        sm.E[4 * g + i][col] = e[i];
+        sm.U[4 * g + i][col] = u[i];
+      }
+    } else if (w == 1) {   // dU = Ktil dS' + P^T dO;  dR = T^T dU;  dv = diag(beta) dR
+      f32x4 du, dr = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int j = 0; j < C; ++j) dr += sm.cc.T[j][er] * sm.dU[j][ed];
-      sm.dR[er][ed] = dr;
-      dvr[t] = sm.cc.beta[er] * dr;
+      for (int i = 0; i < 4; ++i) {
+        const int r = 4 * g + i;
+        float x = 0.f;
+#pragma unroll
+        for (int q = 0; q < 4; ++q) x += sm.v.part[4 + q][r][col];
+        du[i] = x;
+      }
+#pragma unroll
+      for (int s4 = 0; s4 < 4; ++s4) du = mfma4(sm.cc.P[4 * g + s4][col], sm.dO[4 * g + s4][col], du);
+#pragma unroll
+      for (int s4 = 0; s4 < 4; ++s4) dr = mfma4(sm.cc.T[4 * g + s4][col], du[s4], dr);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int r = 4 * g + i;
+        sm.dU[r][col] = du[i];
+        sm.dR[r][col] = dr[i];
+        if (r < len) dvo[(bh * T + t0 + r) * dv + CH * t + col] = sm.cc.beta[r] * dr[i];
+      }
+    } else if ((w == 2 || w == 3) && tid - 128 < DK) {   // rowsum(dS' o S) over the tile's columns
+      const int c = tid - 128;
+      const int o = (c / 16) * 256 + (c % 4) * 64 + ((c % 16) / 4) * 16;
+      const float4* s4 = reinterpret_cast<const float4*>(St + o);
+      const float4* d4 = reinterpret_cast<const float4*>(dSt + o);
+#pragma unroll
+      for (int q4 = 0; q4 < 4; ++q4) {
+        const float4 a = s4[q4], bq = d4[q4];
+        accRS += a.x * bq.x + a.y * bq.y + a.z * bq.z + a.w * bq.w;
+      }
     }
     lds_barrier();
     // K = 16 products: task id = w + 8 j -> (product id / NCB, key block id % NCB)
@@ -907,17 +938,6 @@ __global__ __launch_bounds__(NTG) __attribute__((amdgpu_waves_per_eu(4, 4))) voi
       tdp = mfma4(av.z, bv.z, tdp);
       tdp = mfma4(av.w, bv.w, tdp);
     }
-    if (tid < DK) {    // rowsum(dS' o S) over the tile's columns (16 consecutive floats of each block)
-      const int c = tid;
-      const int o = (c / 16) * 256 + (c % 4) * 64 + ((c % 16) / 4) * 16;
-      const float4* s4 = reinterpret_cast<const float4*>(St + o);
-      const float4* d4 = reinterpret_cast<const float4*>(dSt + o);
-#pragma unroll
-      for (int q4 = 0; q4 < 4; ++q4) {
-        const float4 a = s4[q4], bq = d4[q4];
-        accRS += a.x * bq.x + a.y * bq.y + a.z * bq.z + a.w * bq.w;
-      }
-    }
     if (tid >= 256 && tid < 256 + C) {   // dbeta share: sum_d dR E, in accT of threads 256 .. 271
       const int r = tid - 256;
       float a = 0.f;
@@ -933,12 +953,7 @@ __global__ __launch_bounds__(NTG) __attribute__((amdgpu_waves_per_eu(4, 4))) voi
     lds_barrier();
   }
 
-  if (tid >= 256 && er < len) {
-#pragma unroll
-    for (int t = 0; t < MAXT; ++t)
-      if (t < nsl) dvo[(bh * T + t0 + er) * dv + CH * t + ed] = dvr[t];
-  }
-  if (tid < DK) sm.rs[tid] = accRS;
+  if ((w == 2 || w == 3) && tid - 128 < DK) sm.rs[tid - 128] = accRS;
   // wavefronts 6 and 7 hold dT and dP (lane: rows 4g + i, column col), lower parts kept;
   // tid 256..271: accT = dbeta share
   if (w >= 6) {
@@ -955,14 +970,14 @@ __global__ __launch_bounds__(NTG) __attribute__((amdgpu_waves_per_eu(4, 4))) voi
     float acc = 0.f;
 #pragma unroll
     for (int r = 0; r < C; ++r) acc += sm.cc.T[r][a] * sm.dT[r][bb];
-    sm.M[a][bb] = acc;
+    sm.vt.M[a][bb] = acc;
   }
   lds_barrier();
   if (tid < C * C) {   // dA = -(M T^T), strictly lower, into dT
     const int a = tid / C, bb = tid % C;
     float acc = 0.f;
 #pragma unroll
-    for (int j = 0; j < C; ++j) acc += sm.M[a][j] * sm.cc.T[bb][j];
+    for (int j = 0; j < C; ++j) acc += sm.vt.M[a][j] * sm.cc.T[bb][j];
     sm.dT[a][bb] = bb < a ? -acc : 0.f;
   }
   lds_barrier();
