@@ -25,12 +25,13 @@
 // (the Ktil scaling's share of dG, -dKtil o Ktil per row, and of dGam, its column sum, are combined
 // into the sum over the earlier rows: in strongly decaying chunks the two long sums nearly cancel)
 //
-// Four launches:
+// Three launches:
 //   prep   (one workgroup per chunk)            G, X, P, T -> W, Ktil, Qbar, U0, P^T dO, e^{Gam} records
-//   state  (one per head and 16 value columns)  forward chain, stores every chunk's entering state
-//   dstate (one per head and 16 value columns)  reverse chain, stores every chunk's exit adjoint, dS0
+//   chain  (one per head, 16 value columns and  forward chain: stores every chunk's entering state;
+//           chain; both chains in one launch)   reverse chain: stores every chunk's exit adjoint, dS0
 //   grad   (one per chunk)                      all gradients of the chunk, written once (no atomics)
-// Only the two chains are sequential, and each does two small contractions per chunk.
+// Only the chains are sequential; they are independent of each other, and each does two small
+// contractions per chunk (three in the reverse one).
 #include "kda_internal.h"
 
 namespace kda {
