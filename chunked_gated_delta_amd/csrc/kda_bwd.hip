@@ -360,11 +360,11 @@ __global__ __launch_bounds__(NTP) void bwd_prep_kernel(Params p, const void* __r
 }
 
 // ---------------------------------------------------------------- chains
-// One workgroup per (head, 16 value columns); wavefront w holds rows 16w .. 16w + 15 of the block as
-// an fp32 matrix-core accumulator tile (lane l: rows 16w + 4(l/16) + i, i < 4, column l % 16).  Per
-// chunk: a 16 x 16 x 16 product per wavefront (its 16-key share of a K = dk contraction), written to
-// LDS; after one barrier every wavefront sums all shares itself, in the same lane layout, and the
-// update is one more product on the tile.  The K index of each 16 x 16 x 4 step is taken in the
+// One workgroup per (head, 16 value columns); compute wavefront w holds rows 32w .. 32w + 31 of the
+// block as two fp32 matrix-core accumulator tiles (tile b, lane l: rows 32w + 16b + 4(l/16) + i, i < 4,
+// column l % 16).  Per chunk: a 16 x 16 x 32 product per wavefront (its 32-key share of a K = dk
+// contraction), written to LDS; after one barrier every wavefront sums all shares itself, in the
+// same lane layout, and the update is one more product on each tile.  The K index of each 16 x 16 x 4 step is taken in the
 // order the accumulator already holds its rows (row 4(l/16) + i at step i), so neither the state
 // nor the summed shares need a reshuffle to serve as the B operand.
 //
@@ -423,7 +423,8 @@ struct ChainSlot {
 
 template <int DK>
 struct ChainDims {
-  static constexpr int NW = DK / 16;          // compute wavefronts (one 16-row tile each)
+  static constexpr int RT = 2;                // 16-row tiles per compute wavefront
+  static constexpr int NW = DK / (16 * RT);   // compute wavefronts
   static constexpr int NL = 4;                // loader wavefronts
   static constexpr int NT = (NW + NL) * 64;
 };
@@ -537,46 +538,63 @@ __device__ __forceinline__ void state_chain(const Params& p, const float* __rest
     return;
   }
 
-  f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-  if (p.S0) {
+  constexpr int RT = Dm::RT;
+  f32x4 acc[RT];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) acc[i] = p.S0[(bh * DK + 16 * w + 4 * g + i) * dv + d0 + col];
+  for (int b = 0; b < RT; ++b) {
+    acc[b] = f32x4{0.f, 0.f, 0.f, 0.f};
+    if (p.S0) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) acc[b][i] = p.S0[(bh * DK + 16 * (RT * w + b) + 4 * g + i) * dv + d0 + col];
+    }
   }
-  float4 wv, e4;
-  f32x4 u0;
-  float ka[4];
+  float wv[RT][4], ka[RT][4];
+  f32x4 e4[RT], u0;
   auto operands = [&](int64_t n) {          // step n's operands from its slot
     const float4* sv = smem + (n % R) * LD::SLOT;
     const float* sf = reinterpret_cast<const float*>(sv);
     const float* kt = sf + 4 * SL::MAT;
-    const int c = 16 * w + col;
-    wv = sv[swz<DK>(col, 4 * w + g)];                        // W[col][16w + 4g + s]
-    e4 = sv[SL::O_EG + 4 * w + g];
 #pragma unroll
-    for (int s = 0; s < 4; ++s) {
-      ka[s] = kt[4 * swz<DK>(4 * g + s, c / 4) + c % 4];    // Ktil[4g + s][16w + col]
-      u0[s] = sf[4 * SL::O_VEC + (4 * g + s) * CH + col];
+    for (int b = 0; b < RT; ++b) {
+      const int tb = RT * w + b, c = 16 * tb + col;
+      const float4 x = sv[swz<DK>(col, 4 * tb + g)];          // W[col][16 tb + 4g + s]
+      wv[b][0] = x.x; wv[b][1] = x.y; wv[b][2] = x.z; wv[b][3] = x.w;
+      const float4 e = sv[SL::O_EG + 4 * tb + g];
+      e4[b] = f32x4{e.x, e.y, e.z, e.w};
+#pragma unroll
+      for (int s4 = 0; s4 < 4; ++s4) ka[b][s4] = kt[4 * swz<DK>(4 * g + s4, c / 4) + c % 4];   // Ktil[4g + s][c]
     }
+#pragma unroll
+    for (int s4 = 0; s4 < 4; ++s4) u0[s4] = sf[4 * SL::O_VEC + (4 * g + s4) * CH + col];
   };
   lds_barrier();
   operands(0);
   for (int64_t n = 0; n < NC; ++n) {
     const int pb = (int)(n & 1);
-    float* st = states + ((bh * NC + n) * nsl + sl) * DK * CH + w * 256 + lane;
+    float* st = states + ((bh * NC + n) * nsl + sl) * DK * CH + RT * w * 256 + lane;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) st[i * 64] = acc[i];
-    f32x4 yp = {0.f, 0.f, 0.f, 0.f};
-    yp = mfma4(wv.x, acc[0], yp);
-    yp = mfma4(wv.y, acc[1], yp);
-    yp = mfma4(wv.z, acc[2], yp);
-    yp = mfma4(wv.w, acc[3], yp);
-    part[pb][w][lane] = make_float4(yp[0], yp[1], yp[2], yp[3]);
+    for (int b = 0; b < RT; ++b)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) st[b * 256 + i * 64] = acc[b][i];
+    f32x4 yp[RT];
+#pragma unroll
+    for (int b = 0; b < RT; ++b) yp[b] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int s4 = 0; s4 < 4; ++s4)
+#pragma unroll
+      for (int b = 0; b < RT; ++b) yp[b] = mfma4(wv[b][s4], acc[b][s4], yp[b]);
+#pragma unroll
+    for (int b = 1; b < RT; ++b) yp[0] += yp[b];
+    part[pb][w][lane] = make_float4(yp[0][0], yp[0][1], yp[0][2], yp[0][3]);
     lds_barrier();
-    f32x4 y = u0;
-    const f32x4 eg = {e4.x, e4.y, e4.z, e4.w};
-    float kc[4];
+    f32x4 y = u0, eg[RT];
+    float kc[RT][4];
 #pragma unroll
-    for (int s = 0; s < 4; ++s) kc[s] = ka[s];
+    for (int b = 0; b < RT; ++b) {
+      eg[b] = e4[b];
+#pragma unroll
+      for (int s4 = 0; s4 < 4; ++s4) kc[b][s4] = ka[b][s4];
+    }
 #pragma unroll
     for (int v = 0; v < NW; ++v) {
       const float4 pv = part[pb][v][lane];
@@ -584,9 +602,13 @@ __device__ __forceinline__ void state_chain(const Params& p, const float* __rest
     }
     operands(n + 1);                         // landed before this barrier (a clamped copy past the end)
 #pragma unroll
-    for (int i = 0; i < 4; ++i) acc[i] *= eg[i];
+    for (int b = 0; b < RT; ++b)
 #pragma unroll
-    for (int s = 0; s < 4; ++s) acc = mfma4(kc[s], y[s], acc);
+      for (int i = 0; i < 4; ++i) acc[b][i] *= eg[b][i];
+#pragma unroll
+    for (int s4 = 0; s4 < 4; ++s4)
+#pragma unroll
+      for (int b = 0; b < RT; ++b) acc[b] = mfma4(kc[b][s4], y[s4], acc[b]);
   }
 }
 
@@ -636,58 +658,78 @@ __device__ __forceinline__ void dstate_chain(const Params& p, const void* __rest
     return;
   }
 
-  f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-  if (dSf) {
+  constexpr int RT = Dm::RT;
+  f32x4 acc[RT];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) acc[i] = dSf[(bh * DK + 16 * w + 4 * g + i) * dv + d0 + col];
+  for (int b = 0; b < RT; ++b) {
+    acc[b] = f32x4{0.f, 0.f, 0.f, 0.f};
+    if (dSf) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) acc[b][i] = dSf[(bh * DK + 16 * (RT * w + b) + 4 * g + i) * dv + d0 + col];
+    }
   }
-  float4 kv, e4;
-  f32x4 z0, qd;
-  float wa[4];
+  float kv[RT][4], wa[RT][4];
+  f32x4 e4[RT], qd[RT], z0;
   auto operands = [&](int64_t it) {         // step it's operands from its slot, and its Qbar^T dO
     const float4* sv = smem + (it % R) * LD::SLOT;
     const float* sf = reinterpret_cast<const float*>(sv);
     const float* qb = sf + 4 * 2 * SL::MAT;
     const TIn* dOl = reinterpret_cast<const TIn*>(sv + SL::O_DO);
     const int64_t t0 = (NC - 1 - it) * C;
-    const int c = 16 * w + col;
-    kv = sv[SL::MAT + swz<DK>(col, 4 * w + g)];               // Ktil[col][16w + 4g + s]
-    e4 = sv[SL::O_EG + 4 * w + g];
-    float qa[4], ob[4];
+    float ob[4];
 #pragma unroll
-    for (int s = 0; s < 4; ++s) {
-      const int r = 4 * g + s;
+    for (int s4 = 0; s4 < 4; ++s4) {
+      const int r = 4 * g + s4;
       const float o = load_f32(dOl, r * CH + col);
-      ob[s] = t0 + r < T ? o : 0.f;                           // rows past the end hold a clamped copy
-      qa[s] = qb[4 * swz<DK>(r, c / 4) + c % 4];
-      wa[s] = -sf[4 * swz<DK>(r, c / 4) + c % 4];
-      z0[s] = sf[4 * SL::O_VEC + r * CH + col];
+      ob[s4] = t0 + r < T ? o : 0.f;                          // rows past the end hold a clamped copy
+      z0[s4] = sf[4 * SL::O_VEC + r * CH + col];
     }
-    qd = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int s = 0; s < 4; ++s) qd = mfma4(qa[s], ob[s], qd);
+    for (int b = 0; b < RT; ++b) {
+      const int tb = RT * w + b, c = 16 * tb + col;
+      const float4 x = sv[SL::MAT + swz<DK>(col, 4 * tb + g)];   // Ktil[col][16 tb + 4g + s]
+      kv[b][0] = x.x; kv[b][1] = x.y; kv[b][2] = x.z; kv[b][3] = x.w;
+      const float4 e = sv[SL::O_EG + 4 * tb + g];
+      e4[b] = f32x4{e.x, e.y, e.z, e.w};
+      qd[b] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int s4 = 0; s4 < 4; ++s4) {
+        const int r = 4 * g + s4;
+        wa[b][s4] = -sf[4 * swz<DK>(r, c / 4) + c % 4];
+        qd[b] = mfma4(qb[4 * swz<DK>(r, c / 4) + c % 4], ob[s4], qd[b]);
+      }
+    }
   };
   lds_barrier();
   operands(0);
   for (int64_t it = 0; it < NC; ++it) {
     const int64_t n = NC - 1 - it;
     const int pb = (int)(it & 1);
-    float* st = dstates + ((bh * NC + n) * nsl + sl) * DK * CH + w * 256 + lane;
+    float* st = dstates + ((bh * NC + n) * nsl + sl) * DK * CH + RT * w * 256 + lane;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) st[i * 64] = acc[i];
-    f32x4 zp = {0.f, 0.f, 0.f, 0.f};
-    zp = mfma4(kv.x, acc[0], zp);
-    zp = mfma4(kv.y, acc[1], zp);
-    zp = mfma4(kv.z, acc[2], zp);
-    zp = mfma4(kv.w, acc[3], zp);
-    part[pb][w][lane] = make_float4(zp[0], zp[1], zp[2], zp[3]);
+    for (int b = 0; b < RT; ++b)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) st[b * 256 + i * 64] = acc[b][i];
+    f32x4 zp[RT];
+#pragma unroll
+    for (int b = 0; b < RT; ++b) zp[b] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int s4 = 0; s4 < 4; ++s4)
+#pragma unroll
+      for (int b = 0; b < RT; ++b) zp[b] = mfma4(kv[b][s4], acc[b][s4], zp[b]);
+#pragma unroll
+    for (int b = 1; b < RT; ++b) zp[0] += zp[b];
+    part[pb][w][lane] = make_float4(zp[0][0], zp[0][1], zp[0][2], zp[0][3]);
     lds_barrier();
-    f32x4 z = z0;
-    const f32x4 eg = {e4.x, e4.y, e4.z, e4.w};
-    const f32x4 qc = qd;
-    float wc[4];
+    f32x4 z = z0, eg[RT], qc[RT];
+    float wc[RT][4];
 #pragma unroll
-    for (int s = 0; s < 4; ++s) wc[s] = wa[s];
+    for (int b = 0; b < RT; ++b) {
+      eg[b] = e4[b];
+      qc[b] = qd[b];
+#pragma unroll
+      for (int s4 = 0; s4 < 4; ++s4) wc[b][s4] = wa[b][s4];
+    }
 #pragma unroll
     for (int v = 0; v < NW; ++v) {
       const float4 pv = part[pb][v][lane];
@@ -695,13 +737,19 @@ __device__ __forceinline__ void dstate_chain(const Params& p, const void* __rest
     }
     operands(it + 1);
 #pragma unroll
-    for (int i = 0; i < 4; ++i) acc[i] = acc[i] * eg[i] + qc[i];
+    for (int b = 0; b < RT; ++b)
 #pragma unroll
-    for (int s = 0; s < 4; ++s) acc = mfma4(wc[s], z[s], acc);
+      for (int i = 0; i < 4; ++i) acc[b][i] = acc[b][i] * eg[b][i] + qc[b][i];
+#pragma unroll
+    for (int s4 = 0; s4 < 4; ++s4)
+#pragma unroll
+      for (int b = 0; b < RT; ++b) acc[b] = mfma4(wc[b][s4], z[s4], acc[b]);
   }
   if (dS0) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i) dS0[(bh * DK + 16 * w + 4 * g + i) * dv + d0 + col] = acc[i];
+    for (int b = 0; b < RT; ++b)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) dS0[(bh * DK + 16 * (RT * w + b) + 4 * g + i) * dv + d0 + col] = acc[b][i];
   }
 }
 
