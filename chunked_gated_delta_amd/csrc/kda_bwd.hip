@@ -7,10 +7,11 @@
 //   X[r][j] = sum_c k_rc k_jc e^{G_rc - G_jc}   (j < r)      A = diag(beta) X
 //   P[r][j] = sum_c q_rc k_jc e^{G_rc - G_jc}   (j <= r)     T = (I + A)^{-1}
 //   E = V - Kbar S,  R = diag(beta) E,  U = T R,  O = Qbar S + P U,  S' = e^{Gam} S + Ktil^T U
-// with Kbar = k e^{G}, Qbar = q e^{G}, Ktil = k e^{Gam - G}.  X and P are formed pair by pair, every
-// factor exp(G_r - G_j) <= 1 (the per-position form the pages give for chunks whose reciprocal
-// factors would overflow); the pair terms of the gradients use the same form for such chunks and
-// products of e^{+-(G - Gam/2)} factors (each at most e^{40}) for the others.
+// with Kbar = k e^{G}, Qbar = q e^{G}, Ktil = k e^{Gam - G}.  X, P and the pair terms of the
+// gradients through them are products of e^{+-(G - Gam/2)} factors (each at most e^{40}) for chunks
+// whose every channel spans at least -80, and are formed pair by pair with factors
+// exp(G_r - G_j) <= 1 (the per-position form the pages give for chunks whose reciprocal factors
+// would overflow) for the others.
 //
 // With W = T diag(beta) Kbar and U0 = T diag(beta) V (the WY form: U = U0 - W S) the two chains
 // through the chunks are affine and cheap:
@@ -20,7 +21,7 @@
 //   dU = P^T dO + Ktil dS'        dR = T^T dU        dv = diag(beta) dR
 //   dT = dU R^T  ->  dA = -T^T dT T^T (strictly lower)      dP = dO U^T (lower, diagonal included)
 //   dbeta_r = sum_d dR[r][d] E[r][d] + sum_j dA[r][j] X[r][j]
-//   X, P pair by pair -> dk, dq, dG;   dQbar = dO S^T,  dKbar = -diag(beta) dR S^T,  dKtil = U dS'^T
+//   X, P (pair terms) -> dk, dq, dG;   dQbar = dO S^T,  dKbar = -diag(beta) dR S^T,  dKtil = U dS'^T
 //   dg_u = e^{Gam} . rowsum(dS' o S) + sum_{r >= u} dG_r + sum_{r < u} (dKtil o Ktil)_r,  dw = dg gate'(w)
 // (the Ktil scaling's share of dG, -dKtil o Ktil per row, and of dGam, its column sum, are combined
 // into the sum over the earlier rows: in strongly decaying chunks the two long sums nearly cancel)
@@ -139,9 +140,10 @@ struct ChunkCore {
 
 // Loads chunk n (rows past the end are zero: k = q = beta = 0 and g = 0, which reproduces the
 // shorter last chunk exactly), forms the prefix G and Gam, the chunk's span flag (dense: every
-// channel's span >= -80), X and P pair by pair (each pair's sums
-// split over four quarters of the key channels, partial sums through `scratch`, 2 * 4 * 256 floats),
-// and T by forward substitution (one column per thread, held in registers).  Ends with a barrier.
+// channel's span >= -80), X and P (dense chunks: fp32 matrix-core products of e^{+-(G - Gam/2)}
+// factors, four wavefronts with two key blocks each; other chunks: pair by pair, each pair's sums
+// split over groups of key channels; partial sums through `scratch`, 2 * 4 * 256 floats), and T by
+// back substitution, the four lanes of a quad owning one row.  Ends with a barrier.
 template <typename TIn, int DK, int NT>
 __device__ void chunk_setup(ChunkCore<DK>& cc, float* scratch, const Params& p, int64_t bh, int64_t n, int len) {
   constexpr int NQ = NT >= 4 * NPAIR ? 4 : (NT >= 3 * NPAIR ? 3 : (NT >= 2 * NPAIR ? 2 : 1));   // channel groups
