@@ -17,6 +17,11 @@ last.
 `cpu_baseline` times the fp64 oracle on the host on a bounded sample of the
 same workload (all heads, the first tokens of the sequence).
 
+Defaults: 40 untimed warm-up calls, then 50 timed ones.  The GPU needs about
+30 ms of back-to-back calls before their duration settles (the first forward
+calls after start-up take up to 1.1 ms, the settled ones about 0.92 ms), so
+the warm-up spans that ramp and the timed calls do not.
+
 Other modes print a line of the same form for other entry points:
 `--mode decode` one recurrent decode call over a serving batch (kda_decode,
 HBM roofline over the state read and written), `--mode bwd` one backward call
@@ -343,8 +348,8 @@ def gen_bwd_ws(wl) -> int:
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=40)
     ap.add_argument("--workload", default="headline")
     ap.add_argument("--path", default="auto", choices=["auto", "vector", "mfma", "fused"])
     ap.add_argument("--seed", type=int, default=0)
