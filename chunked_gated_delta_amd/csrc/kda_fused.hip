@@ -113,12 +113,6 @@ __device__ __forceinline__ float dpp(float old, float src) {
   return __int_as_float(__builtin_amdgcn_update_dpp(__float_as_int(old), __float_as_int(src), CTRL, ROW_MASK, 0xF, false));
 }
 
-__device__ __forceinline__ void lgkm_wait() {
-  compiler_fence();
-  __builtin_amdgcn_s_waitcnt(0xF | (0x3 << 14) | (0x7 << 4) | (0x0 << 8));   // lgkmcnt(0)
-  compiler_fence();
-}
-
 // gate in log2 units (g * log2 e), with the kind of gate fixed at compile time
 template <bool UNB> __device__ __forceinline__ float gate2(float w, float g_min_log2);
 template <> __device__ __forceinline__ float gate2<false>(float w, float g_min_log2) {
