@@ -83,6 +83,12 @@ def test_f32_dims(dk, dv):
     check(F32.with_(B=1, H=2, T=83, dk=dk, dv=dv, s0_sd=0.3), seed=420 + dk + dv)
 
 
+@pytest.mark.parametrize("dk,dv", [(32, 64), (64, 32), (64, 128)])
+def test_bf16_dims(dk, dv):
+    """bf16 inputs at the smaller key and value widths (each width has its own kernel instances)."""
+    check(BF16.with_(B=1, H=2, T=83, dk=dk, dv=dv, s0_sd=0.3), seed=425 + dk + dv)
+
+
 def test_bf16_multi_head():
     check(BF16.with_(B=2, H=3, T=203, s0_sd=0.5), seed=430)
 
