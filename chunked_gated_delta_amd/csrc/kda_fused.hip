@@ -78,6 +78,7 @@ static_assert(pQ + 4096 <= kOps, "per-pair inputs fit the borrowed buffer");
 
 constexpr int kOpT00 = 0, kOpT11 = 512, kOpA10 = 1024;   // byte offsets of the three blocks within rT
 static_assert(kOpA10 + 512 <= 2 * kBlk, "the T operands fit their region");
+constexpr int kORow = D * 2 + 16;   // bytes per staged output row (256 of data, 16 of pad)
 constexpr int kRowA = 20;     // row stride (floats) of the fp32 diagonal blocks: 16-byte aligned rows
 
 struct StepInfo {
@@ -94,6 +95,9 @@ struct FusedShared {
   float pwA[2][16][16], pwP[2][16][16];   // per-pair diagonal blocks [chunk][r][j]
   float gam[2][D];                        // chunk totals (log2 units) of the step in E
   float spanw[kEWaves];                   // per-E-wave minimum of the chunk totals
+  // o of the step in C as bf16 rows (padded to 272 bytes so the column-slice writes spread over
+  // the banks): written by each C wavefront in the first half, stored as whole rows in the second
+  alignas(16) unsigned char ostage[STEP][kORow];
 };
 constexpr size_t kFusedSmem = sizeof(FusedShared);
 static_assert(kFusedSmem <= 163840, "LDS budget");
@@ -595,7 +599,6 @@ __global__ __launch_bounds__(kThreads) void fused_kernel(Params p, int64_t n_ste
   uint32_t vin[8];
   uint32_t nonfinite = 0, n_valid = 0, n_flagged = 0;
   float min_span = __int_as_float(0x7f800000);
-  uint16_t* o = OUT ? (uint16_t*)p.o + bh * T * D + li * D + 16 * w + 4 * lg : nullptr;
 
   int slotC = 0;   // record slot of step it (it mod 3), advanced at the top of each pass
 #pragma unroll 1
@@ -639,12 +642,13 @@ __global__ __launch_bounds__(kThreads) void fused_kernel(Params p, int64_t n_ste
           for (int mt = 0; mt < 2; ++mt) O[mt] = mfma(sb[u], ld8(recC + rQb + (mt * 4 + u) * kBlk + sl), O[mt]);
 #pragma unroll
         for (int mt = 0; mt < 2; ++mt) O[mt] = mfma(ub, ld8(recC + rP + mt * kBlk + sl), O[mt]);
-        uint16_t* os = o + (int64_t)st * STEP * D;
+        // this wavefront's 16 columns of every row into the stage; whole rows go out in the second half
         uint32_t mx = 0;
 #pragma unroll
         for (int mt = 0; mt < 2; ++mt) {
+          *reinterpret_cast<uint2*>(&sm.ostage[16 * mt + li][(16 * w + 4 * lg) * 2]) =
+              uint2{pk_bf16(O[mt][0], O[mt][1]), pk_bf16(O[mt][2], O[mt][3])};
           if (nrows == STEP || 16 * mt + li < nrows) {
-            *reinterpret_cast<uint2*>(os + (16 * mt) * D) = uint2{pk_bf16(O[mt][0], O[mt][1]), pk_bf16(O[mt][2], O[mt][3])};
 #pragma unroll
             for (int r = 0; r < 4; ++r) mx = max(mx, abs_bits(O[mt][r]));
           }
@@ -700,7 +704,21 @@ __global__ __launch_bounds__(kThreads) void fused_kernel(Params p, int64_t n_ste
     if (doS) tiles<OUT>(sm, recS, opsF, reinterpret_cast<const StepInfo*>(recS + rMeta)->pairwise, (int)((it + 1) & 1), w, ln);
     v_load(vin, vw, s0 + (it + 1 < 0 ? 0 : (it + 1 < ns ? it + 1 : ns - 1)), v_voff);
     block_barrier();
-    // ---- second half: per-pair blocks of step it + 2 (if any), T of step it + 1
+    // ---- second half: o of step it out of the stage as whole rows (wavefronts 0-3, eight rows each,
+    // 16 bytes per lane: 256 contiguous bytes per row), per-pair blocks of step it + 2 (if any), T of
+    // step it + 1
+    if (OUT && doC && w < 4) {
+      const int st = s0 + it;
+      const int nrows = rows_left((int)T, st);
+      uint16_t* ob = (uint16_t*)p.o + bh * T * D + (int64_t)st * STEP * D;
+      const int c16 = lane & 15;
+#pragma unroll
+      for (int i = 0; i < 2; ++i) {
+        const int row = 8 * w + 4 * i + (lane >> 4);
+        const uint4 v = *reinterpret_cast<const uint4*>(&sm.ostage[row][c16 * 16]);
+        if (row < nrows) *reinterpret_cast<uint4*>(ob + row * D + c16 * 8) = v;
+      }
+    }
     if (doE) {
       const uint32_t pwmask = pairwise_mask(sm, p, s0 + it + 2);
       if (pwmask) pairwise_blocks<OUT, false>(sm, nullptr, recE, opsF, pwmask, 0, ln, tid);
