@@ -95,8 +95,10 @@ struct FusedShared {
   float pwA[2][16][16], pwP[2][16][16];   // per-pair diagonal blocks [chunk][r][j]
   float gam[2][D];                        // chunk totals (log2 units) of the step in E
   float spanw[kEWaves];                   // per-E-wave minimum of the chunk totals
-  // o of the step in C as bf16 rows (padded to 272 bytes so the column-slice writes spread over
-  // the banks): written by each C wavefront in the first half, stored as whole rows in the second
+  // bf16 rows of the step in C, padded to 272 bytes so that column-slice accesses spread over the
+  // banks.  First half: each C wavefront reads V and then writes o, both in its own 16 columns.
+  // Second half: wavefronts 0-3 store eight rows of o each as whole rows, then fill the same rows
+  // with V of the next step (loaded as whole rows at the end of the first half).
   alignas(16) unsigned char ostage[STEP][kORow];
 };
 constexpr size_t kFusedSmem = sizeof(FusedShared);
@@ -474,21 +476,26 @@ __device__ __forceinline__ void solve_block(FusedShared& sm, unsigned char* rec,
 // V of one step in D layout for column col: rows 16mt + 4lg + r.  Each value is widened to 32 bits as
 // it is loaded: with 16-bit values the compiler packs two loads into one register at once, waiting
 // for them (and for every load issued before them, among them the next step's prefetch).
-__device__ __forceinline__ void v_load(uint32_t (&vin)[8], const Views& vw, int step, int voff) {
-  const int so = step * (STEP * D * 2);
-#pragma unroll
-  for (int mt = 0; mt < 2; ++mt)
-#pragma unroll
-    for (int r = 0; r < 4; ++r) vin[mt * 4 + r] = __builtin_amdgcn_raw_buffer_load_b16(vw.v, voff + (16 * mt + r) * D * 2, so, 0);
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+
+// 16 bytes of V: step `step`, row `row` of it, columns 8 c8 .. 8 c8 + 7 (zero past the end of the view)
+__device__ __forceinline__ uint4 v_load16(const Views& vw, int step, int row, int c8) {
+  const u32x4 x = __builtin_amdgcn_raw_buffer_load_b128(vw.v, (row * D + 8 * c8) * 2, step * (STEP * D * 2), 0);
+  return uint4{x[0], x[1], x[2], x[3]};
 }
 
-__device__ __forceinline__ void beta_v(floatx4 (&bv)[2], const uint32_t (&vin)[8], const unsigned char* rec, int lg) {
+// diag(beta) V of this lane's accumulator places (rows 16 mt + 4 lg + r, column col), V read from the stage
+__device__ __forceinline__ void beta_v(floatx4 (&bv)[2], const FusedShared& sm, const unsigned char* rec, int lg,
+                                       int col) {
   const float* bt = reinterpret_cast<const float*>(rec + rBeta);
 #pragma unroll
   for (int mt = 0; mt < 2; ++mt) {
     const floatx4 b = *reinterpret_cast<const floatx4*>(bt + 16 * mt + 4 * lg);
 #pragma unroll
-    for (int r = 0; r < 4; ++r) bv[mt][r] = b[r] * __uint_as_float(vin[mt * 4 + r] << 16);
+    for (int r = 0; r < 4; ++r) {
+      const uint32_t x = *reinterpret_cast<const uint16_t*>(&sm.ostage[16 * mt + 4 * lg + r][2 * col]);
+      bv[mt][r] = b[r] * __uint_as_float(x << 16);
+    }
   }
 }
 
@@ -563,7 +570,6 @@ __global__ __launch_bounds__(kThreads) void fused_kernel(Params p, int64_t n_ste
     vw.v = view((const uint16_t*)p.v + bh * T * D, nb);
     vw.beta = view((const uint16_t*)p.beta + bh * T, T * 2);
   }
-  const int v_voff = ((4 * lg) * D + col) * 2;
 
   // The two kinds of wavefront run separate copies of the step loop (same trip count, same barriers in
   // the same order), so that each copy holds only its own kind's values in registers.
@@ -596,7 +602,7 @@ __global__ __launch_bounds__(kThreads) void fused_kernel(Params p, int64_t n_ste
       for (int r = 0; r < 4; ++r) M[t][r] = (16 * t + 4 * lg + r == col) ? 1.f : 0.f;
     }
   }
-  uint32_t vin[8];
+  uint4 vq[2];   // wavefronts 0-3: V rows of the next step, 16 bytes per lane
   uint32_t nonfinite = 0, n_valid = 0, n_flagged = 0;
   float min_span = __int_as_float(0x7f800000);
 
@@ -619,7 +625,7 @@ __global__ __launch_bounds__(kThreads) void fused_kernel(Params p, int64_t n_ste
 #pragma unroll
       for (int u = 0; u < 4; ++u) sb[u] = pack2(S[2 * u], S[2 * u + 1]);
       floatx4 bv[2];
-      beta_v(bv, vin, recC, lg);
+      beta_v(bv, sm, recC, lg, col);
       floatx4 R[2];
 #pragma unroll
       for (int mt = 0; mt < 2; ++mt) R[mt] = bv[mt];
@@ -702,7 +708,11 @@ __global__ __launch_bounds__(kThreads) void fused_kernel(Params p, int64_t n_ste
     }
     // ---- the causal tiles of step it + 1 (their chunk flags are in its information record)
     if (doS) tiles<OUT>(sm, recS, opsF, reinterpret_cast<const StepInfo*>(recS + rMeta)->pairwise, (int)((it + 1) & 1), w, ln);
-    v_load(vin, vw, s0 + (it + 1 < 0 ? 0 : (it + 1 < ns ? it + 1 : ns - 1)), v_voff);
+    if (w < 4) {
+      const int sn = s0 + (it + 1 < 0 ? 0 : (it + 1 < ns ? it + 1 : ns - 1));
+#pragma unroll
+      for (int i = 0; i < 2; ++i) vq[i] = v_load16(vw, sn, 8 * w + 4 * i + (lane >> 4), lane & 15);
+    }
     block_barrier();
     // ---- second half: o of step it out of the stage as whole rows (wavefronts 0-3, eight rows each,
     // 16 bytes per lane: 256 contiguous bytes per row), per-pair blocks of step it + 2 (if any), T of
@@ -718,6 +728,11 @@ __global__ __launch_bounds__(kThreads) void fused_kernel(Params p, int64_t n_ste
         const uint4 v = *reinterpret_cast<const uint4*>(&sm.ostage[row][c16 * 16]);
         if (row < nrows) *reinterpret_cast<uint4*>(ob + row * D + c16 * 8) = v;
       }
+    }
+    if (w < 4 && it + 1 >= 0 && it + 1 < ns) {   // V of step it + 1 over the rows just stored
+#pragma unroll
+      for (int i = 0; i < 2; ++i)
+        *reinterpret_cast<uint4*>(&sm.ostage[8 * w + 4 * i + (lane >> 4)][(lane & 15) * 16]) = vq[i];
     }
     if (doE) {
       const uint32_t pwmask = pairwise_mask(sm, p, s0 + it + 2);
