@@ -130,6 +130,11 @@ def test_long_f32():
     check(F32.with_(B=1, H=1, T=4000, dk=128, dv=128, s0_sd=0.5), seed=460)
 
 
+def test_long_ragged_bf16():
+    """A few hundred chunks with a ragged last one (3001 = 187 * 16 + 9) on two heads."""
+    check(BF16.with_(B=1, H=2, T=3001, s0_sd=0.5), seed=465)
+
+
 def test_zero_length():
     """T = 0: dS0 = dS_final, nothing else to write."""
     wl = F32.with_(B=2, H=2, T=0, dk=64, dv=32)
