@@ -548,6 +548,13 @@ __global__ __launch_bounds__(kThreads) void fused_kernel(Params p, int64_t n_ste
   // the wavefront index through a scalar register: branches on it (and on the chunk and role derived
   // from it) are then uniform, rather than masked paths that every wavefront would step through
   const int lane = tid & 63, w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  // the segment-map pass runs before the output pass that accumulates the statistics: it resets them
+  if (!OUT && p.stats && blockIdx.x == 0 && tid == 0) {
+    p.stats->n_chunks = 0;
+    p.stats->n_flagged = 0;
+    p.stats->n_nonfinite = 0;
+    p.stats->min_span = __int_as_float(0x7f800000);
+  }
   const bool is_e = w >= kCWaves;
   const int we = w - kCWaves;                 // E wavefront index (valid when is_e)
   const int li = lane & 15, lg = lane >> 4;

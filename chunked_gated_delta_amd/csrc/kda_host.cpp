@@ -167,7 +167,8 @@ int kda_chunk_fwd_ex(const void* q, const void* k, const void* v, const void* w,
   hipEvent_t ev0 = opts ? reinterpret_cast<hipEvent_t>(opts->ev_begin) : nullptr;
   hipEvent_t ev1 = opts ? reinterpret_cast<hipEvent_t>(opts->ev_end) : nullptr;
   hipError_t e;
-  if (stats && (e = kda::launch_stats_init(stats, s)) != hipSuccess) return hip_fail(e);
+  // statistics reset here for the vector path and T = 0; the matrix-core paths do it themselves
+  if (stats && (T == 0 || path < 2) && (e = kda::launch_stats_init(stats, s)) != hipSuccess) return hip_fail(e);
   if (T == 0) {
     if (ev0 && (e = hipEventRecord(ev0, s)) != hipSuccess) return hip_fail(e);
     if ((e = kda::launch_state_copy(p, s)) != hipSuccess) return hip_fail(e);

@@ -894,6 +894,11 @@ hipError_t launch_mfma(const Params& p, hipStream_t s, hipEvent_t ev_begin, hipE
   const int64_t BH = p.B * p.H;
   fused = fused && fused_supported(p.dtype, p.dk, p.dv, p.T);
   const SegPlan sg = make_plan(BH, p.T, p.seg_steps, !fused);
+  // statistics reset: by the segment-map pass of the fused path when there is one, else its own launch
+  if (p.stats && !(fused && sg.P > 1)) {
+    const hipError_t e = launch_stats_init(p.stats, s);
+    if (e != hipSuccess) return e;
+  }
   if (fused) {
     hipError_t e;
     if (ev_begin && (e = hipEventRecord(ev_begin, s)) != hipSuccess) return e;
