@@ -157,15 +157,23 @@ def cpu_baseline(inp, wl, target_s: float = 15.0):
     Ts = int(min(wl.T, max(cal_T, cal_T * target_s / max(cal, 1e-3))))
     Ts = max(16, (Ts // 16) * 16)
     f = {k: inp[k][:, :, :Ts].float().cpu().numpy().astype(np.float64) for k in ("q", "k", "v", "w", "beta")}
-    t0 = time.perf_counter()
-    orc.kda_reference(f["q"], f["k"], f["v"], f["w"], f["beta"], S0, wl.g_min, nthreads=threads)
-    dt = time.perf_counter() - t0
+
+    def run():
+        t0 = time.perf_counter()
+        orc.kda_reference(f["q"], f["k"], f["v"], f["w"], f["beta"], S0, wl.g_min, nthreads=threads)
+        return time.perf_counter() - t0
+
+    # where the whole sequence takes less than the target, the sample is run again back to back
+    dt, reps = run(), 1
+    while dt < target_s and reps < 100:
+        dt += run()
+        reps += 1
     return {
-        "value": wl.B * Ts / dt,
+        "value": wl.B * Ts * reps / dt,
         "unit": "tokens/s",
         "cores": threads,
         "kind": "oracle",
-        "sample": f"all {wl.B * wl.H} (b,h) recurrences over the first {Ts} of {wl.T} tokens "
+        "sample": f"all {wl.B * wl.H} (b,h) recurrences over the first {Ts} of {wl.T} tokens, {reps} runs "
                   f"(fp64 token-by-token, {threads} threads, {dt:.1f} s wall)",
     }
 

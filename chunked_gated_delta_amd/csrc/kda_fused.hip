@@ -72,9 +72,13 @@ constexpr int oQb1 = oKb1 + 4 * kBlk; // q e^{L}, chunk 1                       
 constexpr int oKt0 = oQb1 + 4 * kBlk; // k e^{Gam_0 - L}, chunk 0
 constexpr int kOps = oKt0 + 4 * kBlk;
 // the per-pair path of a flagged chunk borrows the tile-operand buffer of step s+1 (free during the
-// second half of interval s): L (fp32 [16][128]), raw k and raw q (bf16 [16][128])
-constexpr int pL = 0, pK = 8192, pQ = 12288;
-static_assert(pQ + 4096 <= kOps, "per-pair inputs fit the borrowed buffer");
+// second half of interval s): L (fp32 [16][128]), raw k and raw q (bf16 [16][128]), rows padded so
+// that the rows one pass of 16 lanes reads start 16 banks apart
+constexpr int kPL = 144;    // floats per L row (128 + 16)
+constexpr int kPK = 160;    // bf16 per k or q row (128 + 32)
+constexpr int pL = 0, pK = 16 * kPL * 4, pQ = pK + 16 * kPK * 2;
+static_assert(pQ + 16 * kPK * 2 <= kOps, "per-pair inputs fit the borrowed buffer");
+static_assert(pK % 16 == 0 && pQ % 16 == 0 && kOps % 16 == 0, "16-byte reads of the per-pair inputs");
 
 constexpr int kOpT00 = 0, kOpT11 = 512, kOpA10 = 1024;   // byte offsets of the three blocks within rT
 static_assert(kOpA10 + 512 <= 2 * kBlk, "the T operands fit their region");
@@ -351,16 +355,16 @@ __device__ __forceinline__ void pairwise_blocks(FusedShared& sm, const EKeep* kp
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
         const int row = 4 * h + j;
-        Ls[row * D + c0] = kp->L0[j];
-        Ls[row * D + c1] = kp->L1[j];
-        *reinterpret_cast<uint32_t*>(scratch + pK + (row * D + c0) * 2) = kp->k[j];
-        if (OUT) *reinterpret_cast<uint32_t*>(scratch + pQ + (row * D + c0) * 2) = kp->q[j];
+        Ls[row * kPL + c0] = kp->L0[j];
+        Ls[row * kPL + c1] = kp->L1[j];
+        *reinterpret_cast<uint32_t*>(scratch + pK + (row * kPK + c0) * 2) = kp->k[j];
+        if (OUT) *reinterpret_cast<uint32_t*>(scratch + pQ + (row * kPK + c0) * 2) = kp->q[j];
       }
     }
     block_barrier();
     const float* Ls = reinterpret_cast<const float*>(scratch + pL);
-    const uint16_t* Ks = reinterpret_cast<const uint16_t*>(scratch + pK);
-    const uint16_t* Qs = reinterpret_cast<const uint16_t*>(scratch + pQ);
+    const unsigned char* Ks = scratch + pK;
+    const unsigned char* Qs = scratch + pQ;
     const float* bt = reinterpret_cast<const float*>(rec + rBeta);
     {   // 136 pairs x 4 channel quarters over the workgroup's threads; all lanes run the shuffles
       const int pi = tid >> 2, cq = tid & 3;
@@ -368,11 +372,29 @@ __device__ __forceinline__ void pairwise_blocks(FusedShared& sm, const EKeep* kp
       int r = 0, j = 0;
       if (pi < 136) {
         pair_of(pi, r, j);
-        for (int c = 32 * cq; c < 32 * cq + 32; ++c) {
-          const float e = __builtin_amdgcn_exp2f(Ls[r * D + c] - Ls[j * D + c]);
-          const float kj = bf16_to_f32(Ks[j * D + c]) * e;
-          a += bf16_to_f32(Ks[r * D + c]) * kj;
-          if (OUT) pq += bf16_to_f32(Qs[r * D + c]) * kj;
+        // eight channels at a time, blocks cq, cq + 4, cq + 8, cq + 12 (the four quarter threads of a
+        // pair read adjacent pieces): 16-byte reads of L, k and q
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int c = 8 * (cq + 4 * i);
+          const float4 lr0 = *reinterpret_cast<const float4*>(Ls + r * kPL + c);
+          const float4 lr1 = *reinterpret_cast<const float4*>(Ls + r * kPL + c + 4);
+          const float4 lj0 = *reinterpret_cast<const float4*>(Ls + j * kPL + c);
+          const float4 lj1 = *reinterpret_cast<const float4*>(Ls + j * kPL + c + 4);
+          const uint4 kr = *reinterpret_cast<const uint4*>(Ks + (r * kPK + c) * 2);
+          const uint4 kj = *reinterpret_cast<const uint4*>(Ks + (j * kPK + c) * 2);
+          const uint4 qr = OUT ? *reinterpret_cast<const uint4*>(Qs + (r * kPK + c) * 2) : uint4{0, 0, 0, 0};
+          const float dl[8] = {lr0.x - lj0.x, lr0.y - lj0.y, lr0.z - lj0.z, lr0.w - lj0.w,
+                               lr1.x - lj1.x, lr1.y - lj1.y, lr1.z - lj1.z, lr1.w - lj1.w};
+          const uint32_t kru[4] = {kr.x, kr.y, kr.z, kr.w}, kju[4] = {kj.x, kj.y, kj.z, kj.w};
+          const uint32_t qru[4] = {qr.x, qr.y, qr.z, qr.w};
+#pragma unroll
+          for (int m = 0; m < 8; ++m) {
+            const uint32_t sh = (m & 1) ? 0u : 16u;   // element 2n in the low half of dword n
+            const float kjm = __uint_as_float((kju[m >> 1] << sh) & 0xFFFF0000u) * __builtin_amdgcn_exp2f(dl[m]);
+            a += __uint_as_float((kru[m >> 1] << sh) & 0xFFFF0000u) * kjm;
+            if (OUT) pq += __uint_as_float((qru[m >> 1] << sh) & 0xFFFF0000u) * kjm;
+          }
         }
       }
       a += __shfl_xor(a, 1); a += __shfl_xor(a, 2);
