@@ -650,8 +650,12 @@ __global__ __launch_bounds__(256) void seg_combine_kernel(Params p, SegPlan sg) 
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
   const int li = lane & 15, lg = lane >> 4;
-  const int64_t bh = blockIdx.x >> 3;
-  const int slice = blockIdx.x & 7;
+  // the grid is 8 slices x B*H: consecutive block ids go round-robin over the 8 XCDs, so block b
+  // takes logical id (b % 8) (grid / 8) + b / 8, and the 8 slices of a head, which all read the same
+  // M_j, share one XCD's L2 (whole heads whenever B*H is a multiple of 8)
+  const int64_t lb = (int64_t)(blockIdx.x & 7) * (gridDim.x >> 3) + (blockIdx.x >> 3);
+  const int64_t bh = lb >> 3;
+  const int slice = (int)(lb & 7);
   const int64_t nseg = sg.P - 1;
   floatx4 cur[2];
 #pragma unroll

@@ -48,6 +48,15 @@ def test_segments_with_initial_state(seg, path):
 
 
 @pytest.mark.parametrize("path", SEG_PATHS)
+@pytest.mark.parametrize("B,H", [(1, 3), (3, 5), (2, 8)])
+def test_chaining_block_order_over_heads(B, H, path):
+    """The chaining pass spreads the eight 16-column slices of every head over its grid in an
+    XCD-aware order; with S0 present and B*H not a multiple of 8 (and one that is), every head's
+    slices must still pick up that head's own S0, M_j and X_j."""
+    check(BF16.with_(B=B, H=H, T=330, s0_sd=0.5), seed=30 + 7 * B + H, path=path, seg_steps=3)
+
+
+@pytest.mark.parametrize("path", SEG_PATHS)
 def test_segments_no_decay(path):
     """g_min = 0: nothing is forgotten, so each segment transition is a pure
     product of (I - beta k k^T) factors, far from zero.  A nonzero S0 flows
