@@ -42,6 +42,7 @@ namespace {
 constexpr int D = 128;
 constexpr int STEP = 32;
 constexpr int kCWaves = 8;                    // wavefronts 0-7: state slices, tiles, solve
+static_assert(kCWaves == kRecChunks - kRecNonfinite, "one non-finite count per state wavefront in the record");
 constexpr int kEWaves = 8;                    // wavefronts 8-15: the E stage
 constexpr int kThreads = 64 * (kCWaves + kEWaves);
 
@@ -559,31 +560,25 @@ __device__ __forceinline__ void e_loop(FusedShared& sm, const Params& p, const V
   }
 }
 
-// ---------------------------------------------------------------- the kernel
+// ---------------------------------------------------------------- one segment, and the kernel
 // Wavefronts 0-7 (C) own the state slices (slice w: 16 columns) and run the tiles and the solve;
 // wavefronts 8-15 (E) run the E stage.  Both kinds meet at the same two barriers per interval.
+//
+// One workgroup's segment.  OUT: segment j from its entering state, with the outputs; !OUT: the map of
+// segment j.  `early` (OUT only): segment 0 running inside the map pass; its leaving state is then the
+// entering state of segment 1, where the chaining pass starts, and its statistics go to a per-head
+// record that the chaining pass folds into the call's counters.
 template <bool OUT, bool UNB>
-__global__ __launch_bounds__(kThreads) void fused_kernel(Params p, int64_t n_steps, SegPlan sg) {
-  extern __shared__ __align__(16) unsigned char smem_raw[];
-  FusedShared& sm = *reinterpret_cast<FusedShared*>(smem_raw);
+__device__ __forceinline__ void fused_body(FusedShared& sm, const Params& p, int64_t n_steps, const SegPlan& sg,
+                                           int64_t bh, int j, bool early) {
   const int tid = threadIdx.x;
   // the wavefront index through a scalar register: branches on it (and on the chunk and role derived
   // from it) are then uniform, rather than masked paths that every wavefront would step through
   const int lane = tid & 63, w = __builtin_amdgcn_readfirstlane(tid >> 6);
-  // the segment-map pass runs before the output pass that accumulates the statistics: it resets them
-  if (!OUT && p.stats && blockIdx.x == 0 && tid == 0) {
-    p.stats->n_chunks = 0;
-    p.stats->n_flagged = 0;
-    p.stats->n_nonfinite = 0;
-    p.stats->min_span = __int_as_float(0x7f800000);
-  }
   const bool is_e = w >= kCWaves;
   const int we = w - kCWaves;                 // E wavefront index (valid when is_e)
   const int li = lane & 15, lg = lane >> 4;
   // step indices fit 32 bits (T < 2^23), which keeps the scalar index arithmetic short
-  const int nseg = (int)(OUT ? sg.P : sg.P - 1);
-  const int64_t bh = blockIdx.x / nseg;
-  const int j = blockIdx.x % nseg;
   const int s0 = j * (int)sg.L;
   const int ns = ((int)n_steps - s0 < (int)sg.L) ? (int)n_steps - s0 : (int)sg.L;
   const int64_t T = p.T;
@@ -771,7 +766,12 @@ __global__ __launch_bounds__(kThreads) void fused_kernel(Params p, int64_t n_ste
   }
 
   if (OUT) {
-    if (j == sg.P - 1) {
+    if (early) {
+      // segment 0 ran inside the map pass: its leaving state enters segment 1, in the layout of the
+      // chaining pass's states
+      float* so = (float*)((unsigned char*)p.workspace + sg.off_s + (bh * sg.P + 1) * (int64_t)kSegState) + w * 8 * 64 * 4;
+      store_slice(so, S, lane);
+    } else if (j == sg.P - 1) {
 #pragma unroll
       for (int t = 0; t < 8; ++t)
 #pragma unroll
@@ -783,7 +783,19 @@ __global__ __launch_bounds__(kThreads) void fused_kernel(Params p, int64_t n_ste
     if (p.stats) {
 #pragma unroll
       for (int off = 32; off > 0; off >>= 1) nonfinite += __shfl_xor(nonfinite, off);
-      if (lane == 0) {
+      if (early) {
+        // plain stores into the head's record (the unused entering-state block of segment 0): the
+        // counters are reset only after this pass, by the chaining pass, which adds these in
+        uint32_t* rec = (uint32_t*)((unsigned char*)p.workspace + sg.off_s + bh * sg.P * (int64_t)kSegState);
+        if (lane == 0) {
+          rec[kRecNonfinite + w] = nonfinite;
+          if (w == 0) {
+            rec[kRecChunks] = n_valid;
+            rec[kRecFlagged] = n_flagged;
+            rec[kRecMinSpan] = __float_as_uint(min_span);
+          }
+        }
+      } else if (lane == 0) {
         if (nonfinite) atomicAdd(&p.stats->n_nonfinite, nonfinite);
         if (w == 0) {
           atomicAdd(&p.stats->n_chunks, n_valid);
@@ -791,8 +803,7 @@ __global__ __launch_bounds__(kThreads) void fused_kernel(Params p, int64_t n_ste
           if (n_valid) atomic_min_float(&p.stats->min_span, min_span);
         }
       }
-    }
-  } else {
+    }  } else {
     // X_j in slice-major D layout; M_j split into bf16 hi + lo parts, each arranged as the chaining
     // kernel's A operands: [mo 8][u 4][lane 64][8] <-> M[16 mo + (lane & 15)][32 u + {0,16} + 4 (lane >> 4) + r]
     const int64_t blk = bh * sg.P + j;
@@ -814,6 +825,25 @@ __global__ __launch_bounds__(kThreads) void fused_kernel(Params p, int64_t n_ste
   }
 }
 
+// OUT: the output pass, segments 1 .. P-1 (segment 0 ran in the map pass), or the only segment of a
+// one-segment plan.  !OUT (plans of two or more segments): the map pass, segment 0 with its outputs
+// (it needs no map: its entering state is S0) beside the maps of segments 1 .. P-2.
+template <bool OUT, bool UNB>
+__global__ __launch_bounds__(kThreads) void fused_kernel(Params p, int64_t n_steps, SegPlan sg) {
+  extern __shared__ __align__(16) unsigned char smem_raw[];
+  FusedShared& sm = *reinterpret_cast<FusedShared*>(smem_raw);
+  const int nb = sg.P > 1 ? (int)sg.P - 1 : 1;   // workgroups per head
+  const int64_t bh = blockIdx.x / nb;
+  const int i = (int)(blockIdx.x % nb);
+  if (OUT) {
+    fused_body<true, UNB>(sm, p, n_steps, sg, bh, sg.P > 1 ? i + 1 : 0, false);
+  } else if (i == 0) {
+    fused_body<true, UNB>(sm, p, n_steps, sg, bh, 0, true);
+  } else {
+    fused_body<false, UNB>(sm, p, n_steps, sg, bh, i, false);
+  }
+}
+
 template <bool OUT, bool UNB>
 hipError_t launch_one(const Params& p, hipStream_t s, int64_t n_steps, const SegPlan& sg) {
   static bool attr_set = false;
@@ -823,8 +853,9 @@ hipError_t launch_one(const Params& p, hipStream_t s, int64_t n_steps, const Seg
     if (e != hipSuccess) return e;
     attr_set = true;
   }
-  const int64_t nseg = OUT ? sg.P : sg.P - 1;
-  hipLaunchKernelGGL((fused_kernel<OUT, UNB>), dim3((unsigned)(p.B * p.H * nseg)), dim3(kThreads), kFusedSmem, s, p,
+  if (!OUT && sg.P < 2) return hipErrorInvalidValue;   // a one-segment plan has no map pass
+  const int64_t nb = sg.P > 1 ? sg.P - 1 : 1;
+  hipLaunchKernelGGL((fused_kernel<OUT, UNB>), dim3((unsigned)(p.B * p.H * nb)), dim3(kThreads), kFusedSmem, s, p,
                      n_steps, sg);
   return hipGetLastError();
 }

@@ -630,6 +630,10 @@ __global__ __launch_bounds__(kSegThreads) void seg_state_kernel(Params p, int64_
 // which leaves a relative error near 2^-16, with fp32 accumulation.  Wavefront w owns the output row
 // tiles 2w, 2w+1; the D-layout tiles of S feed the B operands directly through the permuted
 // contraction order.  M_j and X_j are fetched two segments ahead.
+// first = 0: the chain starts from S0 at segment 0 (records path).  first = 1 (fused path): the map
+// pass already ran segment 0 with its outputs and left its leaving state in the block of segment 1,
+// where the chain starts, and a statistics record per head, which workgroup 0 turns into the call's
+// counters before the output pass adds to them.
 __device__ __forceinline__ void split_bf16(floatx4 a, floatx4 b, bf16x8& hi, bf16x8& lo) {
 #pragma unroll
   for (int r = 0; r < 4; ++r) {
@@ -645,7 +649,7 @@ struct CombineOps {
   floatx4 x[2];
 };
 
-__global__ __launch_bounds__(256) void seg_combine_kernel(Params p, SegPlan sg) {
+__global__ __launch_bounds__(256) void seg_combine_kernel(Params p, SegPlan sg, int first) {
   __shared__ floatx4 Sx[2][8][64];
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
@@ -656,16 +660,62 @@ __global__ __launch_bounds__(256) void seg_combine_kernel(Params p, SegPlan sg) 
   const int64_t lb = (int64_t)(blockIdx.x & 7) * (gridDim.x >> 3) + (blockIdx.x >> 3);
   const int64_t bh = lb >> 3;
   const int slice = (int)(lb & 7);
-  const int64_t nseg = sg.P - 1;
-  floatx4 cur[2];
-#pragma unroll
-  for (int h = 0; h < 2; ++h) {
-    const int mo = 2 * wave + h;
-#pragma unroll
-    for (int r = 0; r < 4; ++r)
-      cur[h][r] = p.S0 ? p.S0[(bh * D + 16 * mo + 4 * lg + r) * D + 16 * slice + li] : 0.f;
-  }
+  const int64_t nseg = sg.P - 1;   // maps first .. P-2 are chained
   const unsigned char* ws = (const unsigned char*)p.workspace;
+  if (first && p.stats && blockIdx.x == 0) {   // uniform over workgroup 0: one head per thread, then a reduction
+    const int64_t BH = p.B * p.H;
+    uint32_t n_chunks = 0, n_flagged = 0, n_nonfinite = 0;
+    float min_span = __int_as_float(0x7f800000);
+    for (int64_t b = tid; b < BH; b += 256) {
+      const uint32_t* rec = (const uint32_t*)(ws + sg.off_s + b * sg.P * (int64_t)kSegState);
+#pragma unroll
+      for (int i = kRecNonfinite; i < kRecChunks; ++i) n_nonfinite += rec[i];
+      n_chunks += rec[kRecChunks];
+      n_flagged += rec[kRecFlagged];
+      if (rec[kRecChunks]) min_span = fminf(min_span, __uint_as_float(rec[kRecMinSpan]));
+    }
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) {
+      n_chunks += __shfl_xor(n_chunks, off);
+      n_flagged += __shfl_xor(n_flagged, off);
+      n_nonfinite += __shfl_xor(n_nonfinite, off);
+      min_span = fminf(min_span, __shfl_xor(min_span, off));
+    }
+    __shared__ uint32_t red[4][4];
+    if (lane == 0) {
+      red[wave][0] = n_chunks;
+      red[wave][1] = n_flagged;
+      red[wave][2] = n_nonfinite;
+      red[wave][3] = __float_as_uint(min_span);
+    }
+    __syncthreads();
+    if (tid == 0) {
+      for (int v = 1; v < 4; ++v) {
+        n_chunks += red[v][0];
+        n_flagged += red[v][1];
+        n_nonfinite += red[v][2];
+        min_span = fminf(min_span, __uint_as_float(red[v][3]));
+      }
+      p.stats->n_chunks = n_chunks;
+      p.stats->n_flagged = n_flagged;
+      p.stats->n_nonfinite = n_nonfinite;
+      p.stats->min_span = min_span;
+    }
+  }
+  floatx4 cur[2];
+  if (first) {
+    const float* s1 = (const float*)(ws + sg.off_s + (bh * sg.P + 1) * (int64_t)kSegState) + slice * 8 * 64 * 4;
+#pragma unroll
+    for (int h = 0; h < 2; ++h) cur[h] = *reinterpret_cast<const floatx4*>(s1 + ((2 * wave + h) * 64 + lane) * 4);
+  } else {
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const int mo = 2 * wave + h;
+#pragma unroll
+      for (int r = 0; r < 4; ++r)
+        cur[h][r] = p.S0 ? p.S0[(bh * D + 16 * mo + 4 * lg + r) * D + 16 * slice + li] : 0.f;
+    }
+  }
   auto fetch = [&](CombineOps& c, int64_t j) {
     const int64_t blk = bh * sg.P + j;
     const unsigned char* mb = ws + sg.off_m + blk * (int64_t)kSegState;
@@ -706,9 +756,9 @@ __global__ __launch_bounds__(256) void seg_combine_kernel(Params p, SegPlan sg) 
     }
   };
   CombineOps c0, c1;
-  fetch(c0, 0);
-  if (nseg > 1) fetch(c1, 1);
-  for (int64_t j = 0; j < nseg; j += 2) {
+  if (first < nseg) fetch(c0, first);
+  if (first + 1 < nseg) fetch(c1, first + 1);
+  for (int64_t j = first; j < nseg; j += 2) {
     step(c0, j);
     if (j + 2 < nseg) fetch(c0, j + 2);
     if (j + 1 < nseg) {
@@ -849,8 +899,11 @@ __global__ __launch_bounds__(kSegThreads) void seg_out_kernel(Params p, int64_t 
 
 int64_t n_steps_of(int64_t T) { return (T + STEP - 1) / STEP; }
 
-// Segment plan.  Automatic: about 256 workgroups (one per compute unit) over (b, h, segment), at least
-// 8 steps per segment and at most kMaxSeg segments.  seg_steps > 0 fixes the segment length.  With
+// Segment plan.  Automatic: about 256 workgroups (one per compute unit) per pass over (b, h, segment),
+// at least 8 steps per segment and at most kMaxSeg segments.  The fused path's passes hold P - 1
+// workgroups per head (segment 0 runs with outputs beside the maps of segments 1 .. P-2, then
+// segments 1 .. P-1 run with outputs), so it takes one segment more, when that leaves at least three;
+// the records path's output pass holds all P.  seg_steps > 0 fixes the segment length.  With
 // `records`, the per-step records precede the segment blocks in the workspace.
 SegPlan make_plan(int64_t BH, int64_t T, int64_t seg_steps, bool records) {
   const int64_t n = n_steps_of(T);
@@ -861,6 +914,7 @@ SegPlan make_plan(int64_t BH, int64_t T, int64_t seg_steps, bool records) {
     P = (n + seg_steps - 1) / seg_steps;
   } else {
     P = 256 / BH;
+    if (!records) P = P >= 2 ? P + 1 : 1;
     const int64_t by_len = n / 8;
     P = P < by_len ? P : by_len;
     P = P < kMaxSeg ? P : kMaxSeg;
@@ -898,7 +952,7 @@ hipError_t launch_mfma(const Params& p, hipStream_t s, hipEvent_t ev_begin, hipE
   const int64_t BH = p.B * p.H;
   fused = fused && fused_supported(p.dtype, p.dk, p.dv, p.T);
   const SegPlan sg = make_plan(BH, p.T, p.seg_steps, !fused);
-  // statistics reset: by the segment-map pass of the fused path when there is one, else its own launch
+  // statistics reset: by the chaining pass of the fused path when there is one, else its own launch
   if (p.stats && !(fused && sg.P > 1)) {
     const hipError_t e = launch_stats_init(p.stats, s);
     if (e != hipSuccess) return e;
@@ -908,7 +962,7 @@ hipError_t launch_mfma(const Params& p, hipStream_t s, hipEvent_t ev_begin, hipE
     if (ev_begin && (e = hipEventRecord(ev_begin, s)) != hipSuccess) return e;
     if (sg.P > 1) {
       if ((e = launch_fused_segments(p, s, n_steps, sg, false)) != hipSuccess) return e;
-      hipLaunchKernelGGL(seg_combine_kernel, dim3((unsigned)(BH * 8)), dim3(256), 0, s, p, sg);
+      hipLaunchKernelGGL(seg_combine_kernel, dim3((unsigned)(BH * 8)), dim3(256), 0, s, p, sg, 1);
       if ((e = hipGetLastError()) != hipSuccess) return e;
     }
     if ((e = launch_fused_segments(p, s, n_steps, sg, true)) != hipSuccess) return e;
@@ -934,7 +988,7 @@ hipError_t launch_mfma(const Params& p, hipStream_t s, hipEvent_t ev_begin, hipE
     hipLaunchKernelGGL(seg_state_kernel, dim3((unsigned)(BH * (sg.P - 1))), dim3(kSegThreads), kStSmem, s, p,
                        n_steps, sg);
     if ((e = hipGetLastError()) != hipSuccess) return e;
-    hipLaunchKernelGGL(seg_combine_kernel, dim3((unsigned)(BH * 8)), dim3(256), 0, s, p, sg);
+    hipLaunchKernelGGL(seg_combine_kernel, dim3((unsigned)(BH * 8)), dim3(256), 0, s, p, sg, 0);
     if ((e = hipGetLastError()) != hipSuccess) return e;
   }
   hipLaunchKernelGGL(seg_out_kernel, dim3((unsigned)(BH * sg.P)), dim3(kSegThreads), kOutSmem, s, p, n_steps, sg);

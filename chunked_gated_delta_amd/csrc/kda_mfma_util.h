@@ -96,6 +96,10 @@ struct SegPlan {
 constexpr int kSegState = 128 * 128 * 4;    // bytes of one block (64 KiB)
 constexpr int kMHalf = 8 * 4 * 64 * 16;     // bytes of one bf16 part (hi or lo) of a transition M
 constexpr int kMaxSeg = 32;                 // segments per (b, h)
+// the fused path's per-head statistics record of segment 0, in the (otherwise unused) entering-state
+// block of segment 0, as uint32: the non-finite counts of the 8 state wavefronts, then chunks, flagged
+// chunks and the bits of the minimum span
+constexpr int kRecNonfinite = 0, kRecChunks = 8, kRecFlagged = 9, kRecMinSpan = 10;
 
 // the fused segment kernels take this configuration (bf16, dk = dv = 128, 32-bit buffer offsets)
 // the fused segment kernels (one launch: every segment's map when !out, every segment's outputs when out)
