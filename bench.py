@@ -10,8 +10,8 @@ The default workload is B=1, H=16, T=65536, dk=dv=128, bf16, g_min=-5,
 chunk 16, S0 = 0 (synthetic inputs, seeded).  `roofline` uses the algorithmic
 bytes of one launch (q, k, v, w, beta read, o written: 1282 B per token-head at
 d = 128 in bf16, plus the fp32 final state) over the average duration of the
-call's kernels (on the fused path: the segment-map pass, the segment chaining
-and the output pass, back to back on one stream), timed with HIP events that
+call's kernels (on the fused path: the map pass, the segment chaining and the
+output pass, back to back on one stream), timed with HIP events that
 the library records on the launch stream before the first kernel and after the
 last.
 `cpu_baseline` times the fp64 oracle on the host on a bounded sample of the
@@ -50,12 +50,26 @@ KERNEL_SOURCES = ["chunked_gated_delta_amd/csrc/kda_mfma.hip", "chunked_gated_de
                   "chunked_gated_delta_amd/csrc/kda_host.cpp", "chunked_gated_delta_amd/csrc/kda_internal.h"]
 
 
-def source_hash() -> str:
+def code_text(src: str) -> str:
+    """C++/HIP source without its comments and with whitespace runs collapsed: what the compiler
+    sees, so that an edit of a comment leaves the hash of the kernels alone."""
+    import re
+    src = re.sub(r"/\*.*?\*/", " ", src, flags=re.S)
+    src = re.sub(r"//[^\n]*", " ", src)
+    return " ".join(src.split())
+
+
+def source_hash(read=None) -> str:
+    """Hash of the code (comments aside) of the kernel sources the committed counters describe."""
     import hashlib
     h = hashlib.sha256()
     for rel in KERNEL_SOURCES:
-        with open(os.path.join(ROOT, rel), "rb") as f:
-            h.update(f.read())
+        if read is None:
+            with open(os.path.join(ROOT, rel), encoding="utf-8") as f:
+                text = f.read()
+        else:
+            text = read(rel)
+        h.update(code_text(text).encode())
     return h.hexdigest()[:16]
 
 

@@ -29,10 +29,13 @@
 // chunk 0 uses factors referenced to the chunk boundary, e^{L_r} e^{Gam_0 - L_j}, both <= 1.  A
 // chunk whose span falls below -80 gets its diagonal blocks from per-pair factors exp(L_r - L_j) <= 1.
 //
-// Two workgroup kinds share the pipeline (template argument OUT):
-//   OUT = true   a segment from its true entering state, with the outputs o (and S_final at the end)
-//   OUT = false  a segment's affine map S_end = M S_start + X: wavefront w carries column slice w
-//                of X (from zero, with V) and of M (from the identity, without V)
+// Two workgroup kinds share the pipeline:
+//   output   a segment from its true entering state, with the outputs o (and S_final at the end)
+//   map      a segment's affine map S_end = M S_start + X: wavefront w carries column slice w
+//            of X (from zero, with V) and of M (from the identity, without V)
+// The map pass (kernel argument OUT = false) runs segment 0 as an output segment, from S0, beside
+// the maps of segments 1 .. P-2; after the chaining, the output pass (OUT = true) runs segments
+// 1 .. P-1.  Both passes hold P - 1 workgroups per head.
 #include "kda_mfma_util.h"
 
 namespace kda {

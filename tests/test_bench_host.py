@@ -68,3 +68,17 @@ def test_committed_traffic_matches_sources():
     d = json.load(open(os.path.join(ROOT, "profiles", "traffic_headline.json")))
     assert d["source_hash"] == bench.source_hash()
     assert bench.measured_traffic("headline") == d["bytes_per_call"]
+
+
+def test_source_hash_ignores_comments_only():
+    """The hash that ties the counters to the kernels covers code, not comments: editing a comment
+    keeps it, editing code (an operator, a constant) changes it."""
+    base = {rel: open(os.path.join(ROOT, rel), encoding="utf-8").read() for rel in bench.KERNEL_SOURCES}
+    rel = bench.KERNEL_SOURCES[1]
+    h0 = bench.source_hash(lambda r: base[r])
+    commented = dict(base)
+    commented[rel] = "// a new comment line\n" + base[rel].replace("\n", "  /* note */\n", 1)
+    assert bench.source_hash(lambda r: commented[r]) == h0
+    changed = dict(base)
+    changed[rel] = base[rel] + "\nconstexpr int kUnusedProbe = 1;\n"
+    assert bench.source_hash(lambda r: changed[r]) != h0
