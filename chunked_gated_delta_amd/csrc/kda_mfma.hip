@@ -755,16 +755,19 @@ __global__ __launch_bounds__(256) void seg_combine_kernel(Params p, SegPlan sg, 
       *reinterpret_cast<floatx4*>(sn + ((2 * wave + h) * 64 + lane) * 4) = acc;
     }
   };
+  // Every fetch is issued, its segment clamped to the last map (a valid block whose values are then
+  // unused): fetches under a branch would make the memory-counter wait before each use also wait for
+  // the loads issued after it, the prefetch of the next segment included.
+  const int64_t last = nseg - 1;   // nseg >= 1: the kernel runs for plans of two or more segments
+  auto ahead = [&](int64_t j) { return j < last ? j : last; };
   CombineOps c0, c1;
-  if (first < nseg) fetch(c0, first);
-  if (first + 1 < nseg) fetch(c1, first + 1);
+  fetch(c0, ahead(first));
+  fetch(c1, ahead(first + 1));
   for (int64_t j = first; j < nseg; j += 2) {
     step(c0, j);
-    if (j + 2 < nseg) fetch(c0, j + 2);
-    if (j + 1 < nseg) {
-      step(c1, j + 1);
-      if (j + 3 < nseg) fetch(c1, j + 3);
-    }
+    fetch(c0, ahead(j + 2));
+    if (j + 1 < nseg) step(c1, j + 1);
+    fetch(c1, ahead(j + 3));
   }
 }
 
