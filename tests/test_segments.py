@@ -56,6 +56,17 @@ def test_chaining_block_order_over_heads(B, H, path):
     check(BF16.with_(B=B, H=H, T=330, s0_sd=0.5), seed=30 + 7 * B + H, path=path, seg_steps=3)
 
 
+def test_statistics_fold_over_many_heads():
+    """300 heads (B3 H100), segments of 2 steps, g_min = -8: segment 0 runs inside the map pass and
+    leaves one statistics record per head, which the chaining pass folds with a strided loop over
+    more heads than its workgroup has threads; the call's counters must still count every chunk and
+    exactly the flagged ones."""
+    wl = BF16.with_(B=3, H=100, T=160, g_min=-8.0, w_mu=0.0, w_sd=1.0, s0_sd=0.3)   # 1928 of 3000 flagged
+    st = check(wl, seed=19, path="fused", seg_steps=2)
+    pred = orc.predicted_flags(gen.make_numpy(wl, 19)["w"], -8.0)
+    assert st["n_flagged"] == int(pred.sum()) and 0 < st["n_flagged"] < pred.size
+
+
 @pytest.mark.parametrize("path", SEG_PATHS)
 def test_segments_no_decay(path):
     """g_min = 0: nothing is forgotten, so each segment transition is a pure
