@@ -7,7 +7,8 @@ import os
 import re
 
 PKG = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(PKG, "libkda.so")
+# KDA_LIB_PATH: another build of this library (the sanitizer test's host-only instrumented build)
+LIB_PATH = os.environ.get("KDA_LIB_PATH") or os.path.join(PKG, "libkda.so")
 HEADER = os.path.join(os.path.dirname(PKG), "include", "kda.h")
 
 KDA_OK = 0

@@ -41,6 +41,17 @@ def _check(t: torch.Tensor, name: str, shape, dtype, device):
         raise ValueError(f"{name} must be contiguous")
 
 
+def _on_stream(stream, *tensors):
+    """Tell torch's caching allocator that `stream` uses these tensors: memory allocated on the
+    current stream but written by kernels on another one must not be handed out again before
+    that stream's work on it is done."""
+    if stream == torch.cuda.current_stream(stream.device):
+        return
+    for t in tensors:
+        if t is not None:
+            t.record_stream(stream)
+
+
 def make_shape(B, H, T, dk, dv, dtype_code) -> KdaShape:
     return KdaShape(int(B), int(H), int(T), int(dk), int(dv), int(dtype_code), 0)
 
@@ -91,21 +102,25 @@ def chunk_fwd(q, k, v, w, beta, S0=None, g_min: float = -5.0, chunk: int = 16, *
     shape = make_shape(B, H, T, dk, dv, _dtype_code(q))
     opts = KdaOpts(int(bool(disable_fallback)), int(bool(force_fallback)), _PATHS[path], int(seg_steps),
                    events[0].handle if events else None, events[1].handle if events else None)
-    ws_need = _lib.workspace_bytes(shape, chunk, opts)
+    plain = not (disable_fallback or force_fallback or path != "auto" or seg_steps or events)
+    ws_need = _lib.workspace_bytes(shape, chunk, None if plain else opts)
     if workspace is None and ws_need > 0:
         workspace = torch.empty(ws_need, dtype=torch.uint8, device=dev)
     st = torch.empty(4, dtype=torch.int32, device=dev) if stats else None
     if stream is None:
         stream = torch.cuda.current_stream(dev)
+    _on_stream(stream, out, S_final, workspace, st)
+    ws_len = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    args = (_ptr(q), _ptr(k), _ptr(v), _ptr(w), _ptr(beta), _ptr(S0), ctypes.c_float(g_min), int(chunk),
+            ctypes.byref(shape), _ptr(out), _ptr(S_final), _ptr(workspace), ws_len, _ptr(st),
+            ctypes.c_void_p(stream.cuda_stream))
     with torch.cuda.device(dev):
-        rc = _lib.load().kda_chunk_fwd_ex(
-            _ptr(q), _ptr(k), _ptr(v), _ptr(w), _ptr(beta), _ptr(S0),
-            ctypes.c_float(g_min), int(chunk), ctypes.byref(shape),
-            _ptr(out), _ptr(S_final), _ptr(workspace),
-            0 if workspace is None else workspace.numel() * workspace.element_size(),
-            _ptr(st), ctypes.c_void_p(stream.cuda_stream), ctypes.byref(opts))
+        if plain:   # no option set: the plain entry point
+            rc, where = _lib.load().kda_chunk_fwd(*args), "kda_chunk_fwd"
+        else:
+            rc, where = _lib.load().kda_chunk_fwd_ex(*args, ctypes.byref(opts)), "kda_chunk_fwd_ex"
     if rc != 0:
-        raise KdaError(rc, "kda_chunk_fwd_ex", _lib.last_hip_error() if rc == _lib.KDA_ERR_HIP else "")
+        raise KdaError(rc, where, _lib.last_hip_error() if rc == _lib.KDA_ERR_HIP else "")
     return out, S_final, st
 
 
@@ -122,8 +137,14 @@ def decode_stats(st: torch.Tensor) -> dict:
 
 def gate_prefix(w, g_min: float = -5.0, chunk: int = 16, stream=None):
     """Gate / in-chunk prefix stage alone: returns (g, G, span, flags) device tensors."""
+    if not isinstance(w, torch.Tensor) or w.dim() != 4:
+        raise ValueError("w must be a [B,H,T,dk] tensor")
     B, H, T, dk = w.shape
     dev = w.device
+    if dev.type != "cuda":
+        raise ValueError("w must live on a GPU (the library has no CPU path)")
+    _check(w, "w", (B, H, T, dk), w.dtype, dev)
+    _dtype_code(w)
     NC = (T + chunk - 1) // chunk
     g = torch.empty((B, H, T, dk), dtype=torch.float32, device=dev)
     G = torch.empty_like(g)
@@ -132,6 +153,7 @@ def gate_prefix(w, g_min: float = -5.0, chunk: int = 16, stream=None):
     shape = make_shape(B, H, T, dk, dk, _dtype_code(w))
     if stream is None:
         stream = torch.cuda.current_stream(dev)
+    _on_stream(stream, g, G, span, flags)
     with torch.cuda.device(dev):
         rc = _lib.load().kda_gate_prefix(_ptr(w), ctypes.c_float(g_min), int(chunk), ctypes.byref(shape),
                                          _ptr(g), _ptr(G), _ptr(span), _ptr(flags),
@@ -166,6 +188,7 @@ def decode(q, k, v, w, beta, S, g_min: float = -5.0, *, out=None, stream=None):
     shape = make_shape(B, H, T, dk, dv, _dtype_code(q))
     if stream is None:
         stream = torch.cuda.current_stream(dev)
+    _on_stream(stream, out)
     with torch.cuda.device(dev):
         rc = _lib.load().kda_decode(_ptr(q), _ptr(k), _ptr(v), _ptr(w), _ptr(beta), _ptr(S),
                                     ctypes.c_float(g_min), ctypes.byref(shape), _ptr(out),
@@ -215,6 +238,7 @@ def chunk_bwd(q, k, v, w, beta, dO, S0=None, dS_final=None, g_min: float = -5.0,
         raise ValueError(f"workspace holds {workspace.numel() * workspace.element_size()} bytes, {need} needed")
     if stream is None:
         stream = torch.cuda.current_stream(dev)
+    _on_stream(stream, dq, dk_, dv_, dw, dbeta, dS0, workspace)
     with torch.cuda.device(dev):
         if events is not None:
             events[0].record(stream)

@@ -8,8 +8,8 @@
 //   o_t = S^T q_t
 // which is the recurrence the chunk form evaluates in blocks ("From Numerical Stability to Load
 // Balancing ..." section 2.1: a fixed-size state, forgotten per channel and written with key/value
-// outer products, read by the query; the delta-rule correction is named there and on "Architecting
-// Long-Context LLMs ..." section 2.2, the bounded gate in both pages' section 2.2).  Token by token
+// outer products, read by the query; delta-rule models are named there and in "Architecting
+// Long-Context LLMs ..." section 2.1, the bounded gate in both pages' section 2.2).  Token by token
 // there is no reciprocal decay factor, so no span check is needed.
 //
 // Value columns of S are independent, so a workgroup owns one (b, h) and a block of CB columns:

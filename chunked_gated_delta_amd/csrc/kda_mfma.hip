@@ -708,12 +708,17 @@ __global__ __launch_bounds__(256) void seg_combine_kernel(Params p, SegPlan sg, 
 #pragma unroll
     for (int h = 0; h < 2; ++h) cur[h] = *reinterpret_cast<const floatx4*>(s1 + ((2 * wave + h) * 64 + lane) * 4);
   } else {
+    // records path: the chain starts from S0, which is also copied into segment 0's entering-state
+    // block, where the output pass reads it (S_final may be S0: the output pass's last segment
+    // overwrites S0 while its first segment would still be reading it)
+    float* s0b = (float*)((unsigned char*)p.workspace + sg.off_s + bh * sg.P * (int64_t)kSegState) + slice * 8 * 64 * 4;
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
       const int mo = 2 * wave + h;
 #pragma unroll
       for (int r = 0; r < 4; ++r)
         cur[h][r] = p.S0 ? p.S0[(bh * D + 16 * mo + 4 * lg + r) * D + 16 * slice + li] : 0.f;
+      *reinterpret_cast<floatx4*>(s0b + (mo * 64 + lane) * 4) = cur[h];
     }
   }
   auto fetch = [&](CombineOps& c, int64_t j) {
@@ -799,7 +804,7 @@ __global__ __launch_bounds__(kSegThreads) void seg_out_kernel(Params p, int64_t 
 
   const floatx4 zero = {0, 0, 0, 0};
   floatx4 S[8];
-  if (j > 0) {
+  if (sg.P > 1) {   // every entering state, segment 0's (a copy of S0) included, from the chaining pass
     load_slice(S, (const float*)((const unsigned char*)p.workspace + sg.off_s) +
                       (bh * sg.P + j) * (int64_t)(kSegState / 4) + wave * 8 * 64 * 4, lane);
   } else if (p.S0) {

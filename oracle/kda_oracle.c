@@ -9,12 +9,14 @@
  * What it computes: the token-by-token gated delta rule with per-channel
  * log-decay, one independent recurrence per (batch, head).
  *
- *   "Architecting Long-Context LLMs ..." section 2.1 and "From Numerical
- *   Stability to Load Balancing ..." section 2.1: a fixed-shape state matrix
- *   S is decayed by a per-step factor and then receives key/value outer
- *   products.  The pages name the delta rule (Delta networks / Delta Net-like
- *   / delta-rule-based models) but never write it out; the reading used here
- *   is the plainest one consistent with a per-key-channel decay:
+ *   "From Numerical Stability to Load Balancing ..." section 2.1: a
+ *   fixed-shape state matrix S is decayed by a per-step factor and then
+ *   receives key/value outer products.  The pages name the delta rule (Delta
+ *   networks in "Architecting Long-Context LLMs ..." section 2.1, Delta
+ *   Net-like in "Architecture Analysis ..." section 2.1, delta-rule-based
+ *   models in "From Numerical Stability ..." section 1) but never write it
+ *   out; the reading used here is the plainest one consistent with a
+ *   per-key-channel decay:
  *
  *     g_t   = gate(w_t)                          (dk values, one per key channel)
  *     S     = Diag(exp(g_t)) S                   (forget: row c of S scaled by e^{g_tc})

@@ -41,7 +41,8 @@ def build(force: bool = False) -> str:
 def _load():
     global _lib
     if _lib is None:
-        lib = ctypes.CDLL(build())
+        # KDA_ORACLE_LIB: an already built copy of this oracle (the sanitizer test's instrumented build)
+        lib = ctypes.CDLL(os.environ.get("KDA_ORACLE_LIB") or build())
         dp = ctypes.POINTER(ctypes.c_double)
         i64 = ctypes.c_int64
         lib.kda_oracle_f64.argtypes = [dp, dp, dp, dp, dp, dp, ctypes.c_double,

@@ -110,3 +110,24 @@ def test_segment_plans_agree(path):
     for o, S, _ in outs[1:]:
         assert rel_err(o.float().cpu().numpy(), o0.float().cpu().numpy()) < 1e-2
         assert rel_err(S.cpu().numpy(), S0_.cpu().numpy()) < 5e-3
+
+
+@pytest.mark.parametrize("path", SEG_PATHS)
+def test_in_place_state_with_many_segments(path):
+    """S_final == S0 (the in-place update kda.h allows) with at least three segments: the last
+    segment's S_final write must not reach the first segment's read of S0."""
+    from chunked_gated_delta_amd import chunk_fwd
+    need_path(path)
+    wl = BF16.with_(B=1, H=2, T=700, s0_sd=0.3)
+    inp = gen.make_numpy(wl, 61)
+    t = gen.numpy_to_torch(inp, "cuda")
+    say(f"[case] in-place state {wl} path={path} seg_steps=3 (8 segments)")
+    args = [t[n] for n in ("q", "k", "v", "w", "beta")]
+    oa, Sa, _ = chunk_fwd(*args, t["S0"], path=path, seg_steps=3)
+    state = t["S0"].clone()
+    ob, _, _ = chunk_fwd(*args, state, S_final=state, path=path, seg_steps=3)
+    torch.cuda.synchronize()
+    assert torch.equal(oa, ob) and torch.equal(Sa, state)
+    o_ref, S_ref = orc.kda_reference(*(gen.all_to_f64(inp)[n] for n in ("q", "k", "v", "w", "beta", "S0")), wl.g_min)
+    assert rel_err(ob.float().cpu().numpy(), o_ref) <= TOL["bf16"][0]
+    assert rel_err(state.cpu().numpy(), S_ref) <= TOL["bf16"][1]
