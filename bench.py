@@ -192,6 +192,72 @@ def cpu_baseline(inp, wl, target_s: float = 15.0):
     }
 
 
+def sampled_heads(wl):
+    """(b, h) pairs checked against the oracle at full size: every head of a small workload, else the
+    first and the last."""
+    if wl.B * wl.H <= 2:
+        return [(b, h) for b in range(wl.B) for h in range(wl.H)]
+    return [(0, 0), (wl.B - 1, wl.H - 1)]
+
+
+def _tok_f64(x, heads, lo, hi):
+    """Tokens [lo, hi) of the sampled heads of a [B,H,T,...] tensor, stacked as a batch of one-head
+    sequences, in fp64."""
+    import numpy as np
+    return np.stack([x[b, h, lo:hi].float().cpu().numpy() for b, h in heads])[:, None].astype(np.float64)
+
+
+def _state_f64(S, heads):
+    """The sampled heads of a [B,H,dk,dv] state (None stays None), in fp64."""
+    import numpy as np
+    if S is None:
+        return None
+    return np.stack([S[b, h].float().cpu().numpy() for b, h in heads])[:, None].astype(np.float64)
+
+
+def accuracy(inp, wl, o, S, threads):
+    """err(o), err(S_final) = max |x - ref| / max |ref| on the sampled heads, against the fp64 oracle."""
+    import numpy as np
+    from oracle import oracle as orc
+    heads = sampled_heads(wl)
+    T = wl.T
+    f = {n: _tok_f64(inp[n], heads, 0, T) for n in ("q", "k", "v", "w", "beta")}
+    S0 = _state_f64(inp["S0"], heads)
+    t0 = time.perf_counter()
+    o_ref, S_ref = orc.kda_reference(f["q"], f["k"], f["v"], f["w"], f["beta"], S0, wl.g_min,
+                                     nthreads=min(threads, len(heads)))
+    dt = time.perf_counter() - t0
+    og = np.stack([o[b, h].float().cpu().numpy() for b, h in heads])[:, None]
+    Sg = np.stack([S[b, h].cpu().numpy() for b, h in heads])[:, None]
+    err = lambda x, r: float(np.max(np.abs(x - r)) / np.max(np.abs(r)))
+    return {"heads": [list(x) for x in heads], "err_o": err(og, o_ref), "err_S": err(Sg, S_ref),
+            "oracle_s": round(dt, 1)}
+
+
+def state_drift(inp, wl, threads, checkpoints):
+    """S at each checkpoint T_i from chained GPU calls (the state of one call is the S0 of the next),
+    against the fp64 oracle chained the same way (exact in fp64), on the sampled heads:
+    [(T_i, err(S(T_i)), max |S_ref(T_i)|)]."""
+    import numpy as np
+    import torch
+    from chunked_gated_delta_amd import chunk_fwd
+    from oracle import oracle as orc
+    heads = sampled_heads(wl)
+    out, S_gpu, S_ref, lo = [], inp["S0"], _state_f64(inp["S0"], heads), 0
+    for hi in checkpoints:
+        sl = {n: inp[n][:, :, lo:hi].contiguous() for n in ("q", "k", "v", "w", "beta")}
+        _, S_gpu, _ = chunk_fwd(sl["q"], sl["k"], sl["v"], sl["w"], sl["beta"], S_gpu, g_min=wl.g_min)
+        torch.cuda.synchronize()
+        f = {n: _tok_f64(inp[n], heads, lo, hi) for n in ("q", "k", "v", "w", "beta")}
+        _, S_ref = orc.kda_reference(f["q"], f["k"], f["v"], f["w"], f["beta"], S_ref, wl.g_min,
+                                     nthreads=min(threads, len(heads)))
+        Sg = np.stack([S_gpu[b, h].cpu().numpy() for b, h in heads])[:, None]
+        out.append([hi, float(np.max(np.abs(Sg - S_ref)) / np.max(np.abs(S_ref))), float(np.max(np.abs(S_ref)))])
+        log(f"[bench] drift T={hi}: err(S)={out[-1][1]:.3e} max|S_ref|={out[-1][2]:.3e}")
+        lo = hi
+    return out
+
+
 def decode_bytes(wl) -> int:
     """HBM bytes one decode call must move: the fp32 state read and written, plus the token's inputs
     and output (q, k, w, v, beta in, o out)."""
@@ -367,6 +433,39 @@ def gen_bwd_ws(wl) -> int:
     return max(1, _lib.bwd_workspace_bytes(make_shape(wl.B, wl.H, wl.T, wl.dk, wl.dv, code), 16))
 
 
+def oracle_threads(wl) -> int:
+    try:
+        cores = len(os.sched_getaffinity(0))
+    except AttributeError:
+        cores = os.cpu_count() or 1
+    return max(1, min(cores, 16, wl.B * wl.H))
+
+
+def time_forward(torch, inp, wl, g_min, steps, warmup, kw):
+    """`warmup` untimed calls, then `steps` timed ones; returns (average kernel ms over the call's
+    kernels from HIP events on the launch stream, per-call kernel ms, wall seconds of the timed calls,
+    statistics, o, S_final)."""
+    from chunked_gated_delta_amd import HipEvent, chunk_fwd, decode_stats
+    q, k, v, w, beta, S0 = (inp[n] for n in ("q", "k", "v", "w", "beta", "S0"))
+    o = torch.empty_like(v)
+    S = torch.empty((wl.B, wl.H, wl.dk, wl.dv), dtype=torch.float32, device="cuda")
+    st = None
+    for _ in range(warmup):
+        _, _, st = chunk_fwd(q, k, v, w, beta, S0, out=o, S_final=S, g_min=g_min, **kw)
+    torch.cuda.synchronize()
+    if st is not None:
+        log(f"[bench] warmup stats {decode_stats(st)}")
+    evs = [(HipEvent(), HipEvent()) for _ in range(steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(steps):
+        _, _, st = chunk_fwd(q, k, v, w, beta, S0, out=o, S_final=S, g_min=g_min, events=evs[i], **kw)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    kern_ms = [b.elapsed_ms(e) for b, e in evs]
+    return sum(kern_ms) / len(kern_ms), kern_ms, wall, decode_stats(st), o, S
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -376,6 +475,9 @@ def main():
     ap.add_argument("--path", default="auto", choices=["auto", "vector", "mfma", "fused"])
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-accuracy", action="store_true",
+                    help="skip the check of the sampled heads against the fp64 oracle (and, for the "
+                         "million workload, the state drift curve)")
     ap.add_argument("--force-fallback", action="store_true")
     ap.add_argument("--mode", default="forward", choices=["forward", "decode", "bwd"],
                     help="forward: the chunked forward (the headline); decode: one recurrent decode "
@@ -407,7 +509,6 @@ def main():
         log(f"copy_calib: copied {n} bytes x3")
         return
 
-    from chunked_gated_delta_amd import HipEvent, chunk_fwd, decode_stats
     from chunked_gated_delta_amd import inputs as gen
 
     if args.mode == "decode":
@@ -421,29 +522,28 @@ def main():
     log(f"[bench] workload {wl}")
     inp = gen.make_torch(wl, seed=args.seed, device="cuda")
     torch.cuda.synchronize()
-    kw = dict(g_min=wl.g_min, path=args.path, force_fallback=args.force_fallback)
-    q, k, v, w, beta, S0 = (inp[n] for n in ("q", "k", "v", "w", "beta", "S0"))
-    o = torch.empty_like(v)
-    S = torch.empty((wl.B, wl.H, wl.dk, wl.dv), dtype=torch.float32, device="cuda")
-    st = None
-    for _ in range(args.warmup):
-        _, _, st = chunk_fwd(q, k, v, w, beta, S0, out=o, S_final=S, **kw)
-    torch.cuda.synchronize()
-    if st is not None:
-        log(f"[bench] warmup stats {decode_stats(st)}")
-
-    evs = [(HipEvent(), HipEvent()) for _ in range(args.steps)]
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for i in range(args.steps):
-        _, _, st = chunk_fwd(q, k, v, w, beta, S0, out=o, S_final=S, events=evs[i], **kw)
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
-    kern_ms = [b.elapsed_ms(e) for b, e in evs]
-    kern_avg = sum(kern_ms) / len(kern_ms)
-    stats = decode_stats(st)
+    kw = dict(path=args.path, force_fallback=args.force_fallback)
+    kern_avg, kern_ms, wall, stats, o, S = time_forward(torch, inp, wl, wl.g_min, args.steps, args.warmup, kw)
     log(f"[bench] kernel ms: avg {kern_avg:.4f} min {min(kern_ms):.4f} max {max(kern_ms):.4f}; wall/step "
         f"{1e3 * wall / args.steps:.4f} ms; stats {stats}")
+    extra = {}
+    if not math.isfinite(wl.g_min):
+        # the same inputs with the bounded gate: the cost of the flagged chunks' per-position blocks
+        b_avg, _, b_wall, b_stats, _, _ = time_forward(torch, inp, wl, -5.0, args.steps, args.warmup, kw)
+        extra["unbounded"] = {
+            "flagged_frac": stats["n_flagged"] / max(1, stats["n_chunks"]),
+            "bounded_kernel_ms": round(b_avg, 5), "bounded_value": round(wl.B * wl.T / (b_wall / args.steps), 1),
+            "bounded_flagged": b_stats["n_flagged"],
+            "throughput_loss": round(1.0 - (b_wall / wall), 4),
+            "kernel_time_ratio": round(kern_avg / b_avg, 4)}
+        log(f"[bench] bounded gate on the same w: {extra['unbounded']}")
+    threads = oracle_threads(wl)
+    if not args.no_accuracy:
+        extra["accuracy"] = accuracy(inp, wl, o, S, threads)
+        log(f"[bench] accuracy {extra['accuracy']}")
+    if wl.name == "million" and not args.no_accuracy:
+        extra["drift"] = state_drift(inp, wl, threads, [1 << 16, 1 << 18, 1 << 20])
+    del o, S
 
     ms_per_step = 1e3 * wall / args.steps
     tokens = wl.B * wl.T
@@ -481,6 +581,7 @@ def main():
         "roofline": roofline,
         "cpu_baseline": cpu,
         "stats": stats,
+        **extra,
     }
     print(json.dumps(line), flush=True)
 
