@@ -11,10 +11,7 @@ namespace {
 
 thread_local char g_last_hip_error[256] = "";
 
-int hip_fail(hipError_t e) {
-  std::snprintf(g_last_hip_error, sizeof(g_last_hip_error), "%s (%d)", hipGetErrorString(e), (int)e);
-  return KDA_ERR_HIP;
-}
+int hip_fail(hipError_t e) { return kda::record_hip_error(e); }
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
@@ -63,12 +60,26 @@ int pick_path(const kda_shape_t* sh, const kda_opts_t* opts) {
   return kda::fused_supported(sh->dtype, sh->dk, sh->dv, sh->T) ? 3 : 2;
 }
 
-size_t workspace_for(const kda_shape_t* sh, int path) {
+size_t workspace_for(const kda_shape_t* sh, int path, int64_t seg_steps) {
   if (path < 2) return 0;
-  return kda::mfma_workspace_bytes(sh->B, sh->H, sh->T, sh->dk, sh->dv, path == 2);
+  return kda::mfma_workspace_bytes(sh->B, sh->H, sh->T, sh->dk, sh->dv, path == 2, seg_steps);
 }
 
 }  // namespace
+
+namespace kda {
+
+int record_hip_error(hipError_t e) {
+  std::snprintf(g_last_hip_error, sizeof(g_last_hip_error), "%s (%d)", hipGetErrorString(e), (int)e);
+  return KDA_ERR_HIP;
+}
+
+int record_error_text(const char* text) {
+  std::snprintf(g_last_hip_error, sizeof(g_last_hip_error), "%s", text);
+  return KDA_ERR_HIP;
+}
+
+}  // namespace kda
 
 extern "C" {
 
@@ -96,7 +107,10 @@ size_t kda_workspace_bytes_ex(const kda_shape_t* shape, int chunk, const kda_opt
   if (check_shape(shape) != KDA_OK || chunk != kda::kChunk) return (size_t)-1;
   if (opts && (opts->path < 0 || opts->path > 3)) return (size_t)-1;
   const int path = pick_path(shape, opts);
-  return path < 0 ? (size_t)-1 : workspace_for(shape, path);
+  if (path < 0) return (size_t)-1;
+  const int64_t seg_steps = opts ? opts->seg_steps : 0;
+  if (path >= 2 && !kda::mfma_seg_steps_ok(shape->T, seg_steps)) return (size_t)-1;
+  return workspace_for(shape, path, seg_steps);
 }
 
 int kda_chunk_fwd_ex(const void* q, const void* k, const void* v, const void* w, const void* beta,
@@ -158,9 +172,9 @@ int kda_chunk_fwd_ex(const void* q, const void* k, const void* v, const void* w,
 
   const int path = T > 0 ? pick_path(shape, opts) : 1;
   if (path < 0) return KDA_ERR_UNSUPPORTED;
-  const size_t need_ws = workspace_for(shape, path);
-  if (need_ws > 0 && (!workspace || workspace_bytes < need_ws)) return KDA_ERR_ARG;
   if (path >= 2 && !kda::mfma_seg_steps_ok(T, p.seg_steps)) return KDA_ERR_ARG;
+  const size_t need_ws = workspace_for(shape, path, p.seg_steps);
+  if (need_ws > 0 && (!workspace || workspace_bytes < need_ws)) return KDA_ERR_ARG;
 
   // ---- launches (first HIP call of the entry point)
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);

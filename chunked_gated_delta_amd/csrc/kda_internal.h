@@ -47,6 +47,10 @@ struct BwdParams {
   float *dq, *dk, *dv, *dw, *dbeta, *dS0;   // dS0 nullable
 };
 
+// Error text for kda_last_hip_error(): both store the text for the calling thread and return KDA_ERR_HIP.
+int record_hip_error(hipError_t e);
+int record_error_text(const char* text);
+
 // Launchers (each returns the hipError_t of its launch).
 hipError_t launch_stats_init(kda_stats_t* stats, hipStream_t s);
 hipError_t launch_state_copy(const Params& p, hipStream_t s);          // T == 0
@@ -57,9 +61,11 @@ hipError_t launch_vec(const Params& p, hipStream_t s);                 // plain 
 hipError_t launch_decode(const DecodeParams& p, hipStream_t s);        // per-token recurrence on a resident state
 size_t bwd_workspace_bytes(int64_t B, int64_t H, int64_t T, int64_t dk, int64_t dv);
 hipError_t launch_bwd(const BwdParams& b, hipStream_t s);              // backward, fp32 vector ALUs
-// workspace of the matrix-core paths: with `records`, the per-step records of path 2 and the
-// segment blocks; without, the segment blocks of the fused path only
-size_t mfma_workspace_bytes(int64_t B, int64_t H, int64_t T, int64_t dk, int64_t dv, bool records);
+// workspace of the matrix-core paths for the segment plan that seg_steps (0: automatic) selects: with
+// `records`, the per-step records of path 2 and the segment blocks; without, the segment blocks of the
+// fused path only (none for a one-segment plan)
+size_t mfma_workspace_bytes(int64_t B, int64_t H, int64_t T, int64_t dk, int64_t dv, bool records,
+                            int64_t seg_steps);
 bool fused_supported(int dtype, int64_t dk, int64_t dv, int64_t T);
 bool mfma_seg_steps_ok(int64_t T, int64_t seg_steps);                    // forced segment length allowed?
 hipError_t launch_mfma(const Params& p, hipStream_t s, hipEvent_t ev_begin, hipEvent_t ev_end, bool fused);

@@ -932,7 +932,7 @@ SegPlan make_plan(int64_t BH, int64_t T, int64_t seg_steps, bool records) {
   }
   sg.P = P;
   const int64_t recs = records ? BH * n * (int64_t)kRecBytes : 0;
-  const int64_t blk = BH * (int64_t)(n < kMaxSeg ? n : kMaxSeg) * kSegState;
+  const int64_t blk = BH * P * (int64_t)kSegState;
   sg.off_x = recs;
   sg.off_m = recs + blk;
   sg.off_s = recs + 2 * blk;
@@ -941,11 +941,11 @@ SegPlan make_plan(int64_t BH, int64_t T, int64_t seg_steps, bool records) {
 
 }  // namespace
 
-size_t mfma_workspace_bytes(int64_t B, int64_t H, int64_t T, int64_t dk, int64_t dv, bool records) {
-  if (dk != D || dv != D) return 0;
-  const int64_t n = n_steps_of(T);
-  const int64_t nseg = n < kMaxSeg ? n : kMaxSeg;
-  return (records ? (size_t)(B * H * n) * kRecBytes : 0) + (size_t)(3 * B * H * nseg) * kSegState;
+size_t mfma_workspace_bytes(int64_t B, int64_t H, int64_t T, int64_t dk, int64_t dv, bool records, int64_t seg_steps) {
+  if (dk != D || dv != D || T <= 0) return 0;
+  const SegPlan sg = make_plan(B * H, T, seg_steps, records);
+  if (!records && sg.P == 1) return 0;   // the fused path's one-segment plan keeps nothing between kernels
+  return (size_t)(sg.off_s + B * H * sg.P * (int64_t)kSegState);
 }
 
 bool mfma_seg_steps_ok(int64_t T, int64_t seg_steps) {

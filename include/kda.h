@@ -194,14 +194,18 @@ KDA_API size_t kda_bwd_workspace_bytes(const kda_shape_t* shape, int chunk);
 KDA_API int kda_gate_prefix(const void* w, float g_min, int chunk, const kda_shape_t* shape,
                     float* g, float* G, float* span, uint8_t* flags, void* stream);
 
-/* Scratch bytes kda_chunk_fwd needs for this shape (0 means none): on the fused
- * path, three 64 KiB fp32 blocks per sequence segment (at most 32 segments per
- * (b, h)); on the records path (opts->path = 2, or T >= 2^23), also a 29 KiB
- * record per 32 tokens per (b, h).  Returns (size_t)-1 for an invalid shape,
- * chunk or path. Host-only, no HIP call.                                     */
+/* Scratch bytes kda_chunk_fwd needs for this shape (0 means none): three 64 KiB
+ * blocks (a segment's map X and M, and its entering state) per sequence segment
+ * of the plan the call takes (the automatic plan here, up to 32 segments per
+ * (b, h); the fused path keeps nothing when the plan has one segment); on the
+ * records path (opts->path = 2, or T >= 2^23), also a 29 KiB record per 32
+ * tokens per (b, h).  Returns (size_t)-1 for an invalid shape, chunk or path.
+ * Host-only, no HIP call.                                                    */
 KDA_API size_t kda_workspace_bytes(const kda_shape_t* shape, int chunk);
 
-/* Same for kda_chunk_fwd_ex with these options (opts may be NULL: the automatic path). */
+/* Same for kda_chunk_fwd_ex with these options (opts may be NULL: the automatic path and plan;
+ * opts->seg_steps fixes the segment length, and a length giving more than 32 segments per (b, h)
+ * returns (size_t)-1). */
 KDA_API size_t kda_workspace_bytes_ex(const kda_shape_t* shape, int chunk, const kda_opts_t* opts);
 
 /* Static description of an error code. Host-only. */

@@ -109,27 +109,33 @@ def test_overlaps_rejected():
 
 
 def test_workspace_per_path():
-    ex = lambda sh, path: lib.kda_workspace_bytes_ex(ctypes.byref(sh), 16, ctypes.byref(KdaOpts(0, 0, path, 0, None, None)))
-    sh = shape(B=1, H=2, T=64)                  # 2 steps of 32 tokens per (b, h)
-    seg = 3 * 2 * 2 * 128 * 128 * 4             # X, M, S_start per segment, at most one segment per step
-    assert lib.kda_workspace_bytes(ctypes.byref(sh), 16) == seg      # automatic: the fused path
-    assert ex(sh, 3) == seg
-    assert ex(sh, 2) == seg + 2 * 2 * 29696     # plus a 29 KiB record per step
+    ex = lambda sh, path, seg=0: lib.kda_workspace_bytes_ex(ctypes.byref(sh), 16,
+                                                            ctypes.byref(KdaOpts(0, 0, path, seg, None, None)))
+    blk = 128 * 128 * 4                         # one X, M or S_start block (64 KiB)
+    sh = shape(B=1, H=2, T=64)                  # 2 steps of 32 tokens per (b, h): one segment
+    assert lib.kda_workspace_bytes(ctypes.byref(sh), 16) == 0        # automatic: fused, nothing kept
+    assert ex(sh, 3) == 0
+    assert ex(sh, 2) == 2 * 2 * 29696 + 3 * 2 * blk                 # a 29 KiB record per step, one segment
     assert ex(sh, 1) == 0
     assert ex(sh, 7) == ctypes.c_size_t(-1).value
+    # 128 steps per head, two heads: the automatic plan cuts each sequence into 16 segments of 8 steps
+    sh = shape(B=1, H=2, T=4096)
+    assert ex(sh, 0) == ex(sh, 3) == 3 * 2 * 16 * blk
+    assert ex(sh, 3, seg=5) == 3 * 2 * 26 * blk                      # a forced length of 5 steps: 26 segments
+    assert ex(sh, 3, seg=3) == ctypes.c_size_t(-1).value             # 43 segments: more than 32
     assert ex(shape(dk=64, dv=64), 3) == ctypes.c_size_t(-1).value   # no matrix-core path at d = 64
     assert ex(shape(dk=64, dv=64), 0) == 0
     assert ex(shape(T=1 << 23), 0) == ex(shape(T=1 << 23), 2)         # past the fused path's range
     # the records path checks its own, larger size
-    assert call(sh, ws_bytes=seg, opts=KdaOpts(0, 0, 2, 0, None, None)) == -4
+    assert call(sh, ws_bytes=ex(sh, 3), opts=KdaOpts(0, 0, 2, 0, None, None)) == -4
 
 
 def test_workspace_too_small():
-    need = lib.kda_workspace_bytes(ctypes.byref(shape()), 16)
-    if need == 0:
-        pytest.skip("this shape needs no workspace")
-    assert call(ws_bytes=need - 1) == -4
-    assert call(workspace=None, ws_bytes=0) == -4
+    sh = shape(T=4096)                          # 16 segments per head: the fused path keeps its maps
+    need = lib.kda_workspace_bytes(ctypes.byref(sh), 16)
+    assert need > 0
+    assert call(sh, ws_bytes=need - 1) == -4
+    assert call(sh, workspace=None, ws_bytes=0) == -4
 
 
 def test_opts_validation():
@@ -217,3 +223,4 @@ def test_bwd_validation():
     # T = 0 with no dS0 wanted: nothing to do, no launch, no pointers needed
     assert bwd_call(shape(T=0), q=None, k=None, v=None, w=None, beta=None, dO=None, dq=None, dk=None, dv=None,
                     dw=None, dbeta=None, dS0=None, workspace=None, ws_bytes=0) == 0
+
