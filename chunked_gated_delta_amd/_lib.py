@@ -17,6 +17,8 @@ KDA_ERR_SHAPE = -2
 KDA_ERR_UNSUPPORTED = -3
 KDA_ERR_ARG = -4
 KDA_ERR_HIP = -5
+KDA_ERR_SCRATCH = -6
+NOALLOC_SCRATCH_BYTES = 64 << 20   # KDA_NOALLOC_SCRATCH_BYTES of include/kda.h
 
 DTYPE_F32 = 0
 DTYPE_BF16 = 1
@@ -70,6 +72,8 @@ def load():
     lib.kda_chunk_fwd.restype = i32
     lib.kda_chunk_fwd_ex.argtypes = fwd_args + [ctypes.POINTER(KdaOpts)]
     lib.kda_chunk_fwd_ex.restype = i32
+    lib.kda_chunk_fwd_noalloc.argtypes = [vp, vp, vp, vp, vp, vp, f32, i32, ctypes.POINTER(KdaShape), vp, vp, vp, vp]
+    lib.kda_chunk_fwd_noalloc.restype = i32
     lib.kda_decode.argtypes = [vp, vp, vp, vp, vp, vp, f32, ctypes.POINTER(KdaShape), vp, vp]
     lib.kda_decode.restype = i32
     lib.kda_chunk_bwd.argtypes = [vp, vp, vp, vp, vp, vp, f32, i32, ctypes.POINTER(KdaShape), vp, vp,

@@ -124,6 +124,49 @@ def chunk_fwd(q, k, v, w, beta, S0=None, g_min: float = -5.0, chunk: int = 16, *
     return out, S_final, st
 
 
+def chunk_fwd_noalloc(q, k, v, w, beta, S0=None, g_min: float = -5.0, chunk: int = 16, *,
+                      out=None, S_final=None, stats: bool = True, stream=None):
+    """KDA chunked forward through kda_chunk_fwd_noalloc: the library takes the call's scratch from its
+    own static device array (no workspace argument).  Same arguments and results as chunk_fwd without
+    the options; out, S_final and stats are allocated here when not given (the C entry point itself
+    allocates nothing).  Calls that overlap in time on one GPU share that array and race."""
+    if q.dim() != 4:
+        raise ValueError("q must be [B,H,T,dk]")
+    B, H, T, dk = q.shape
+    dv = v.shape[-1]
+    dt = q.dtype
+    dev = q.device
+    if dev.type != "cuda":
+        raise ValueError("inputs must live on a GPU (the library has no CPU path)")
+    _check(q, "q", (B, H, T, dk), dt, dev)
+    _check(k, "k", (B, H, T, dk), dt, dev)
+    _check(w, "w", (B, H, T, dk), dt, dev)
+    _check(v, "v", (B, H, T, dv), dt, dev)
+    _check(beta, "beta", (B, H, T), dt, dev)
+    if S0 is not None:
+        _check(S0, "S0", (B, H, dk, dv), torch.float32, dev)
+    if out is None:
+        out = torch.empty((B, H, T, dv), dtype=dt, device=dev)
+    else:
+        _check(out, "out", (B, H, T, dv), dt, dev)
+    if S_final is None:
+        S_final = torch.empty((B, H, dk, dv), dtype=torch.float32, device=dev)
+    else:
+        _check(S_final, "S_final", (B, H, dk, dv), torch.float32, dev)
+    shape = make_shape(B, H, T, dk, dv, _dtype_code(q))
+    st = torch.empty(4, dtype=torch.int32, device=dev) if stats else None
+    if stream is None:
+        stream = torch.cuda.current_stream(dev)
+    _on_stream(stream, out, S_final, st)
+    with torch.cuda.device(dev):
+        rc = _lib.load().kda_chunk_fwd_noalloc(
+            _ptr(q), _ptr(k), _ptr(v), _ptr(w), _ptr(beta), _ptr(S0), ctypes.c_float(g_min), int(chunk),
+            ctypes.byref(shape), _ptr(out), _ptr(S_final), _ptr(st), ctypes.c_void_p(stream.cuda_stream))
+    if rc != 0:
+        raise KdaError(rc, "kda_chunk_fwd_noalloc", _lib.last_hip_error() if rc == _lib.KDA_ERR_HIP else "")
+    return out, S_final, st
+
+
 def decode_stats(st: torch.Tensor) -> dict:
     """int32[4] device tensor -> dict (synchronises)."""
     a = st.cpu()

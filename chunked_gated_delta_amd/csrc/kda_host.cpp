@@ -91,6 +91,7 @@ const char* kda_strerror(int code) {
     case KDA_ERR_UNSUPPORTED: return "unsupported configuration (chunk must be 16; dk, dv in {32, 64, 128}; dtype f32 or bf16; path)";
     case KDA_ERR_ARG: return "invalid argument (g_min NaN or > 0, misaligned pointer, overlapping buffers, workspace too small, reserved field set)";
     case KDA_ERR_HIP: return "HIP runtime error (see kda_last_hip_error)";
+    case KDA_ERR_SCRATCH: return "the call needs more scratch than the static array of kda_chunk_fwd_noalloc holds (KDA_NOALLOC_SCRATCH_BYTES); use kda_chunk_fwd with a workspace";
     default: return "unknown error code";
   }
 }

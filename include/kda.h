@@ -117,7 +117,8 @@ enum {
   KDA_ERR_ARG = -4,         /* g_min NaN or > 0, misaligned pointer, forbidden overlap,
                                workspace too small, non-zero reserved field, both opts set,
                                bad seg_steps */
-  KDA_ERR_HIP = -5          /* a HIP call failed; kda_last_hip_error() has the text */
+  KDA_ERR_HIP = -5,         /* a HIP call failed; kda_last_hip_error() has the text */
+  KDA_ERR_SCRATCH = -6      /* kda_chunk_fwd_noalloc: the call needs more than KDA_NOALLOC_SCRATCH_BYTES */
 };
 
 /* Forward pass.  Computes o and S_final as defined above.
@@ -141,6 +142,27 @@ KDA_API int kda_chunk_fwd_ex(const void* q, const void* k, const void* v, const 
                      const float* S0, float g_min, int chunk, const kda_shape_t* shape,
                      void* o, float* S_final, void* workspace, size_t workspace_bytes,
                      kda_stats_t* stats, void* stream, const kda_opts_t* opts);
+
+/* Size of the static device array kda_chunk_fwd_noalloc takes its scratch from: 64 MiB per GPU the
+ * library runs on, held from the first call on that GPU until the process ends.  It holds the
+ * automatic segment plan of up to 341 (b, h, segment) triples of 192 KiB, e.g. B*H = 16 heads at
+ * any T below 2^23 (17 segments each) or B*H = 32 (9 segments each); the plan needs none (and any
+ * shape is accepted) where it keeps one segment per sequence or takes the vector path. */
+#define KDA_NOALLOC_SCRATCH_BYTES (64u * 1024u * 1024u)
+
+/* Forward pass that allocates nothing, for callers that cannot allocate device memory at call time
+ * (code under stream capture, tight serving loops, harnesses that forbid allocation).
+ * Same arguments, validation, results and asynchrony as kda_chunk_fwd without workspace and
+ * workspace_bytes: the scratch kda_workspace_bytes(shape, chunk) reports is taken from a static
+ * device array of the library (KDA_NOALLOC_SCRATCH_BYTES, one per GPU, looked up on the first call on
+ * each GPU with that GPU current).  Returns KDA_ERR_SCRATCH, launching nothing, when the call needs
+ * more than that; every other error as kda_chunk_fwd.  No hipMalloc or hipFree, no allocating
+ * library routine.  All calls on one GPU share its array: calls that overlap in time on one GPU
+ * (concurrent streams, or several host threads) race on it and must be serialised by the caller;
+ * calls queued one after another on one stream are safe. */
+KDA_API int kda_chunk_fwd_noalloc(const void* q, const void* k, const void* v, const void* w, const void* beta,
+                                  const float* S0, float g_min, int chunk, const kda_shape_t* shape,
+                                  void* o, float* S_final, kda_stats_t* stats, void* stream);
 
 /* Recurrent decode: advance a resident state by shape->T tokens (typically 1), token by
  * token, in place.  The per-token form of the same gated delta rule ("From Numerical

@@ -44,7 +44,7 @@ def test_exports_every_declared_symbol():
 
 def test_version_and_strings():
     assert _lib.version() == 100
-    for code in (0, -1, -2, -3, -4, -5):
+    for code in (0, -1, -2, -3, -4, -5, -6):
         assert len(_lib.strerror(code)) >= 2
     assert _lib.strerror(-99) == "unknown error code"
     assert isinstance(_lib.last_hip_error(), str)
@@ -224,3 +224,22 @@ def test_bwd_validation():
     assert bwd_call(shape(T=0), q=None, k=None, v=None, w=None, beta=None, dO=None, dq=None, dk=None, dv=None,
                     dw=None, dbeta=None, dS0=None, workspace=None, ws_bytes=0) == 0
 
+
+def test_noalloc_rejects_calls_beyond_its_scratch():
+    """kda_chunk_fwd_noalloc refuses, before any HIP call, a call whose automatic plan needs more than
+    the static array holds, and validates everything else as kda_chunk_fwd does."""
+    assert _lib.NOALLOC_SCRATCH_BYTES == 64 << 20
+    assert "#define KDA_NOALLOC_SCRATCH_BYTES (64u * 1024u * 1024u)" in open(_lib.HEADER).read()
+    p = ptrs()
+    big = shape(B=1, H=128, T=65536)            # 128 heads x 3 segments x 192 KiB = 72 MiB
+    assert lib.kda_workspace_bytes(ctypes.byref(big), 16) > _lib.NOALLOC_SCRATCH_BYTES
+    na = lambda sh, g_min=-5.0, chunk=16, S_final=p[6]: lib.kda_chunk_fwd_noalloc(
+        p[0], p[1], p[2], p[3], p[4], None, ctypes.c_float(g_min), chunk, ctypes.byref(sh), p[5], S_final,
+        p[8], None)
+    assert na(big) == _lib.KDA_ERR_SCRATCH == -6
+    assert na(shape(), chunk=32) == -3
+    assert na(shape(dk=48)) == -3
+    assert na(shape(), g_min=1.0) == -4
+    assert na(shape(), S_final=None) == -1
+    headline = shape(B=1, H=16, T=65536)
+    assert 0 < lib.kda_workspace_bytes(ctypes.byref(headline), 16) <= _lib.NOALLOC_SCRATCH_BYTES
