@@ -127,6 +127,21 @@ __device__ __forceinline__ float dpp(float old, float src) {
   return __int_as_float(__builtin_amdgcn_update_dpp(__float_as_int(old), __float_as_int(src), CTRL, ROW_MASK, 0xF, false));
 }
 
+// Lane n of this lane's row of 16 (DPP row_newbcast:n), n a constant after unrolling.  Folded into the
+// instruction that uses it, the broadcast costs no instruction of its own.
+__device__ __forceinline__ float row_bcast(float v, int n) {
+  switch (n) {
+#define KDA_ROW_BCAST_CASE(N) \
+  case N: return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x150 + N, 0xF, 0xF, false));
+    KDA_ROW_BCAST_CASE(0) KDA_ROW_BCAST_CASE(1) KDA_ROW_BCAST_CASE(2) KDA_ROW_BCAST_CASE(3)
+    KDA_ROW_BCAST_CASE(4) KDA_ROW_BCAST_CASE(5) KDA_ROW_BCAST_CASE(6) KDA_ROW_BCAST_CASE(7)
+    KDA_ROW_BCAST_CASE(8) KDA_ROW_BCAST_CASE(9) KDA_ROW_BCAST_CASE(10) KDA_ROW_BCAST_CASE(11)
+    KDA_ROW_BCAST_CASE(12) KDA_ROW_BCAST_CASE(13) KDA_ROW_BCAST_CASE(14)
+#undef KDA_ROW_BCAST_CASE
+    default: return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x150 + 15, 0xF, 0xF, false));
+  }
+}
+
 // gate in log2 units (g * log2 e), with the kind of gate fixed at compile time
 template <bool UNB> __device__ __forceinline__ float gate2(float w, float g_min_log2);
 template <> __device__ __forceinline__ float gate2<false>(float w, float g_min_log2) {
@@ -158,7 +173,6 @@ struct EIn {
 struct EKeep {                 // E's values carried from its first half to its second
   uint32_t k[4], q[4];         // two bf16 channels per word, tokens j
   float L0[4], L1[4];          // chunk-local inclusive prefix (log2 units)
-  float eL0[4], eL1[4];        // e^{L}
   float beta[4];
   float G0, G1;                // chunk totals of the two channels (log2 units)
 };
@@ -196,7 +210,7 @@ __device__ __forceinline__ float wave_min_totals(float g0, float g1) {
 }
 
 // First half of E for chunk CC of the step: gates, the in-chunk prefix L, the chunk totals, the span
-// of the wave's channels, beta, and e^{L}.
+// of the wave's channels, and beta.
 template <bool UNB, int CC>
 __device__ __forceinline__ void e_first(FusedShared& sm, const EIn& in, EKeep& kp, const Params& p, int step,
                                         unsigned char* rec, int w, int l) {
@@ -239,8 +253,6 @@ __device__ __forceinline__ void e_first(FusedShared& sm, const EIn& in, EKeep& k
   for (int j = 0; j < 4; ++j) {
     kp.L0[j] += x0;
     kp.L1[j] += x1;
-    kp.eL0[j] = __builtin_amdgcn_exp2f(kp.L0[j]);
-    kp.eL1[j] = __builtin_amdgcn_exp2f(kp.L1[j]);
   }
   if (h == 0) { sm.gam[CC][c0] = kp.G0; sm.gam[CC][c1] = kp.G1; }
   const float m = wave_min_totals(kp.G0, kp.G1);
@@ -258,7 +270,8 @@ __device__ __forceinline__ void pair_of(int pr, int& r, int& j) {   // pr -> (r,
   j = pr - r * (r + 1) / 2;
 }
 
-// Second half of E for chunk CC: every operand of the step built from k, q and the gate factors.
+// Second half of E for chunk CC: e^{L}, and every operand of the step built from k, q and the gate
+// factors (the exponentials sit here rather than in the first half, which the state wavefronts bound).
 //   chunk 0: k e^{-L} (tiles), -beta k e^{L} and q e^{L} (step-referenced = chunk-local), k e^{Gam_0 - L}
 //            (tiles), Ktil = k e^{Gam_0 - L} e^{Gam_1}, and e^{Gam_step}
 //   chunk 1: k e^{-L} (tiles), k e^{L} and q e^{L} (tiles), their step-referenced forms times e^{Gam_0}
@@ -274,20 +287,26 @@ __device__ __forceinline__ void e_second(FusedShared& sm, const EKeep& kp, const
   const float iG0 = __builtin_amdgcn_exp2f(-kp.G0), iG1 = __builtin_amdgcn_exp2f(-kp.G1);
   // e^{Gam} of the other chunk, per channel
   const float y0 = __builtin_amdgcn_exp2f(sm.gam[1 - CC][c0]), y1 = __builtin_amdgcn_exp2f(sm.gam[1 - CC][c1]);
+  float eL0[4], eL1[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    eL0[j] = __builtin_amdgcn_exp2f(kp.L0[j]);
+    eL1[j] = __builtin_amdgcn_exp2f(kp.L1[j]);
+  }
   float ktv0[4], ktv1[4];
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
     const int li = 4 * h + j;
     const float k0 = lo_bf16(kp.k[j]), k1 = hi_bf16(kp.k[j]);
     const float kg0 = k0 * __builtin_amdgcn_exp2f(kp.G0 - kp.L0[j]), kg1 = k1 * __builtin_amdgcn_exp2f(kp.G1 - kp.L1[j]);
-    const float ke0 = k0 * kp.eL0[j], ke1 = k1 * kp.eL1[j];
+    const float ke0 = k0 * eL0[j], ke1 = k1 * eL1[j];
     const float nb = -kp.beta[j];
     *reinterpret_cast<uint32_t*>(ops + oKh + rowk_off(CC, u, li, g, pos)) = pk_bf16(kg0 * iG0, kg1 * iG1);
     if (CC == 0) {
       *reinterpret_cast<uint32_t*>(rec + rKb + rowk_off(0, u, li, g, pos)) = pk_bf16(nb * ke0, nb * ke1);
       if (OUT)
         *reinterpret_cast<uint32_t*>(rec + rQb + rowk_off(0, u, li, g, pos)) =
-            pk_bf16(lo_bf16(kp.q[j]) * kp.eL0[j], hi_bf16(kp.q[j]) * kp.eL1[j]);
+            pk_bf16(lo_bf16(kp.q[j]) * eL0[j], hi_bf16(kp.q[j]) * eL1[j]);
       *reinterpret_cast<uint32_t*>(ops + oKt0 + rowk_off(0, u, li, g, pos)) = pk_bf16(kg0, kg1);
       ktv0[j] = kg0 * y0;
       ktv1[j] = kg1 * y1;
@@ -295,7 +314,7 @@ __device__ __forceinline__ void e_second(FusedShared& sm, const EKeep& kp, const
       *reinterpret_cast<uint32_t*>(ops + oKb1 + rowk_off(0, u, li, g, pos)) = pk_bf16(ke0, ke1);
       *reinterpret_cast<uint32_t*>(rec + rKb + rowk_off(1, u, li, g, pos)) = pk_bf16(nb * ke0 * y0, nb * ke1 * y1);
       if (OUT) {
-        const float qe0 = lo_bf16(kp.q[j]) * kp.eL0[j], qe1 = hi_bf16(kp.q[j]) * kp.eL1[j];
+        const float qe0 = lo_bf16(kp.q[j]) * eL0[j], qe1 = hi_bf16(kp.q[j]) * eL1[j];
         *reinterpret_cast<uint32_t*>(ops + oQb1 + rowk_off(0, u, li, g, pos)) = pk_bf16(qe0, qe1);
         *reinterpret_cast<uint32_t*>(rec + rQb + rowk_off(1, u, li, g, pos)) = pk_bf16(qe0 * y0, qe1 * y1);
       }
@@ -436,18 +455,28 @@ __device__ __forceinline__ void tiles(FusedShared& sm, unsigned char* rec, const
   floatx4 acc = {0, 0, 0, 0};
 #pragma unroll
   for (int u = 0; u < 4; ++u) acc = mfma(ld8(b + u * kBlk + slot16(lane)), ld8(a + u * kBlk + slot16(lane)), acc);
-  const bool pw0 = pwmask & 1u, pw1 = pwmask & 2u;
   floatx4 x;
+  const float b1 = (w == 1 || w == 2) ? bt[16 + li] : 0.f;
 #pragma unroll
   for (int r = 0; r < 4; ++r) {
     const int c = 4 * lg + r;   // element (li, c) of the block
     switch (w) {
-      case 0: x[r] = c < li ? (pw0 ? sm.pwA[0][li][c] : -acc[r]) : 0.f; break;
-      case 1: x[r] = c < li ? (pw1 ? sm.pwA[1][li][c] : bt[16 + li] * acc[r]) : 0.f; break;
-      case 2: x[r] = -bt[16 + li] * acc[r]; break;
-      case 3: x[r] = c <= li ? (pw0 ? sm.pwP[0][li][c] : acc[r]) : 0.f; break;
-      case 4: x[r] = c <= li ? (pw1 ? sm.pwP[1][li][c] : acc[r]) : 0.f; break;
+      case 0: x[r] = c < li ? -acc[r] : 0.f; break;
+      case 1: x[r] = c < li ? b1 * acc[r] : 0.f; break;
+      case 2: x[r] = -b1 * acc[r]; break;
+      case 3: case 4: x[r] = c <= li ? acc[r] : 0.f; break;
       default: x[r] = acc[r]; break;
+    }
+  }
+  // a flagged chunk's diagonal block comes from its per-pair values instead (the test is uniform, so
+  // the common step reads nothing more and takes no lane-dependent branch)
+  if (pwmask && ((w == 0 || w == 3) ? (pwmask & 1u) : (w == 1 || w == 4) ? (pwmask & 2u) : 0u)) {
+    const float (*pw)[16] = w == 0 ? sm.pwA[0] : w == 1 ? sm.pwA[1] : w == 3 ? sm.pwP[0] : sm.pwP[1];
+    const floatx4 v = *reinterpret_cast<const floatx4*>(&pw[li][4 * lg]);
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int c = 4 * lg + r;
+      x[r] = (w == 0 || w == 1) ? (c < li ? v[r] : 0.f) : (c <= li ? v[r] : 0.f);
     }
   }
   switch (w) {
@@ -510,17 +539,19 @@ __device__ __forceinline__ uint4 v_load16(const Views& vw, int step, int row, in
   return uint4{x[0], x[1], x[2], x[3]};
 }
 
-// diag(beta) V of this lane's accumulator places (rows 16 mt + 4 lg + r, column col), V read from the stage
+// diag(beta) V of this lane's accumulator places (rows 16 mt + 4 lg + r, column col), V read from the
+// stage.  The 16 lanes of a row share lg, hence their eight betas: lane li of the row reads the beta of
+// place (mt, r) = (li / 4, li % 4), and each place takes it by a row broadcast from that lane.
 __device__ __forceinline__ void beta_v(floatx4 (&bv)[2], const FusedShared& sm, const unsigned char* rec, int lg,
-                                       int col) {
+                                       int li, int col) {
   const float* bt = reinterpret_cast<const float*>(rec + rBeta);
+  const float bl = bt[16 * ((li >> 2) & 1) + 4 * lg + (li & 3)];
 #pragma unroll
   for (int mt = 0; mt < 2; ++mt) {
-    const floatx4 b = *reinterpret_cast<const floatx4*>(bt + 16 * mt + 4 * lg);
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
       const uint32_t x = *reinterpret_cast<const uint16_t*>(&sm.ostage[16 * mt + 4 * lg + r][2 * col]);
-      bv[mt][r] = b[r] * __uint_as_float(x << 16);
+      bv[mt][r] = row_bcast(bl, 4 * mt + r) * __uint_as_float(x << 16);
     }
   }
 }
@@ -646,13 +677,14 @@ __device__ __forceinline__ void fused_body(FusedShared& sm, const Params& p, int
     block_barrier();
     const int ln = opaque(lane);
     const int sl = slot16(ln);
-    // ---- first half: the whole recurrence step of step it
+    // ---- first half: the whole recurrence step of step it (map pass: of X and M together, each
+    // operand read once for both)
     if (doC) {
       bf16x8 sb[4];   // bf16 copies of the entering state, the B operands of this step
 #pragma unroll
       for (int u = 0; u < 4; ++u) sb[u] = pack2(S[2 * u], S[2 * u + 1]);
       floatx4 bv[2];
-      beta_v(bv, sm, recC, lg, col);
+      beta_v(bv, sm, recC, lg, li, col);
       floatx4 R[2];
 #pragma unroll
       for (int mt = 0; mt < 2; ++mt) R[mt] = bv[mt];
@@ -700,17 +732,21 @@ __device__ __forceinline__ void fused_body(FusedShared& sm, const Params& p, int
           min_span = fminf(min_span, fminf(si.span[0], si.span[1]));
         }
       }
-      // state update: S <- diag(e^{Gam}) S + Ktil^T U
+      // state update: S <- diag(e^{Gam}) S + Ktil^T U.  The 16 lanes of a row share lg, hence the 32 rows
+      // 16 t + 4 lg + r they hold: lane li reads the factors of places 2 li and 2 li + 1 (place 4 t + r),
+      // and each place takes its factor by a row broadcast.
+      {
+        const float2 egl = *reinterpret_cast<const float2*>(recC + rEg + (lg * 32 + 2 * li) * 4);
 #pragma unroll
-      for (int t = 0; t < 8; ++t) {
-        const floatx4 eg = *reinterpret_cast<const floatx4*>(recC + rEg + (lg * 32 + 4 * t) * 4);
+        for (int t = 0; t < 8; ++t) {
 #pragma unroll
-        for (int r = 0; r < 4; ++r) S[t][r] *= eg[r];
-        S[t] = mfma(ld8(recC + rKt + t * kBlk + sl), ub, S[t]);
+          for (int r = 0; r < 4; ++r) S[t][r] *= row_bcast((r & 1) ? egl.y : egl.x, 2 * t + (r >> 1));
+          S[t] = mfma(ld8(recC + rKt + t * kBlk + sl), ub, S[t]);
+        }
       }
       if (!OUT) {   // the transition slice, after the state slice so that the two need not be live at once
         // fresh offsets: reusing the state slice's loads would keep them live across both slices
-        const int sl = opaque(slot16(ln)), lgm = opaque(lg);
+        const int sl = opaque(slot16(ln)), lgm = opaque(lg), lim = opaque(li);
         bf16x8 mb[4];
 #pragma unroll
         for (int u = 0; u < 4; ++u) mb[u] = pack2(M[2 * u], M[2 * u + 1]);
@@ -724,11 +760,11 @@ __device__ __forceinline__ void fused_body(FusedShared& sm, const Params& p, int
         const floatx4 RM1 = mfma16(ld4(recC + rT + kOpA10 + l8), pack4(UM0), RM[1]);
         const floatx4 UM1 = mfma16(ld4(recC + rT + kOpT11 + l8), pack4(RM1), zero);
         const bf16x8 um = pack2(UM0, UM1);
+        const float2 egl = *reinterpret_cast<const float2*>(recC + rEg + (lgm * 32 + 2 * lim) * 4);
 #pragma unroll
         for (int t = 0; t < 8; ++t) {
-          const floatx4 eg = *reinterpret_cast<const floatx4*>(recC + rEg + (lgm * 32 + 4 * t) * 4);
 #pragma unroll
-          for (int r = 0; r < 4; ++r) M[t][r] *= eg[r];
+          for (int r = 0; r < 4; ++r) M[t][r] *= row_bcast((r & 1) ? egl.y : egl.x, 2 * t + (r >> 1));
           M[t] = mfma(ld8(recC + rKt + t * kBlk + sl), um, M[t]);
         }
       }

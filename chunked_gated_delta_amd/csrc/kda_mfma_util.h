@@ -58,9 +58,12 @@ __device__ __forceinline__ floatx4 mfma16(bf16x4 a, bf16x4 b, floatx4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a, b, c, 0, 0, 0);
 }
 __device__ __forceinline__ bf16x4 ld4(const void* p) { return *reinterpret_cast<const bf16x4*>(p); }
+typedef unsigned int u32x2v __attribute__((ext_vector_type(2)));
+// two v_cvt_pk_bf16_f32 (a four-wide vector conversion compiles to four one-value conversions and
+// two permutes)
 __device__ __forceinline__ bf16x4 pack4(floatx4 a) {
-  const float4v f = {a[0], a[1], a[2], a[3]};
-  return __builtin_bit_cast(bf16x4, __builtin_convertvector(f, bf16x4v));
+  const u32x2v w = {pk_bf16(a[0], a[1]), pk_bf16(a[2], a[3])};
+  return __builtin_bit_cast(bf16x4, w);
 }
 
 __device__ __forceinline__ uint32_t abs_bits(float x) { return __float_as_uint(x) & 0x7fffffffu; }
