@@ -677,6 +677,11 @@ __device__ __forceinline__ void fused_body(FusedShared& sm, const Params& p, int
     block_barrier();
     const int ln = opaque(lane);
     const int sl = slot16(ln);
+    if (OUT && w < 4) {   // V of step it + 1, issued first so that the whole first half covers its latency
+      const int sn = s0 + (it + 1 < 0 ? 0 : (it + 1 < ns ? it + 1 : ns - 1));
+#pragma unroll
+      for (int i = 0; i < 2; ++i) vq[i] = v_load16(vw, sn, 8 * w + 4 * i + (lane >> 4), lane & 15);
+    }
     // ---- first half: the whole recurrence step of step it (map pass: of X and M together, each
     // operand read once for both)
     if (doC) {
@@ -771,7 +776,7 @@ __device__ __forceinline__ void fused_body(FusedShared& sm, const Params& p, int
     }
     // ---- the causal tiles of step it + 1 (their chunk flags are in its information record)
     if (doS) tiles<OUT>(sm, recS, opsF, reinterpret_cast<const StepInfo*>(recS + rMeta)->pairwise, (int)((it + 1) & 1), w, ln);
-    if (w < 4) {
+    if (!OUT && w < 4) {   // V of step it + 1 (the map pass has no registers to carry it over the chain)
       const int sn = s0 + (it + 1 < 0 ? 0 : (it + 1 < ns ? it + 1 : ns - 1));
 #pragma unroll
       for (int i = 0; i < 2; ++i) vq[i] = v_load16(vw, sn, 8 * w + 4 * i + (lane >> 4), lane & 15);
