@@ -49,10 +49,12 @@ int check_gmin(float g_min) {
   return KDA_OK;
 }
 
+bool chunk_ok(int chunk) { return chunk == 16 || chunk == 32 || chunk == 64; }
+
 // path actually taken for a valid shape: 1 vector, 2 records, 3 fused; -1 for an unsupported request
-int pick_path(const kda_shape_t* sh, const kda_opts_t* opts) {
+int pick_path(const kda_shape_t* sh, int chunk, const kda_opts_t* opts) {
   const int req = opts ? opts->path : 0;
-  const bool mfma = sh->dtype == KDA_DTYPE_BF16 && sh->dk == 128 && sh->dv == 128;
+  const bool mfma = sh->dtype == KDA_DTYPE_BF16 && sh->dk == 128 && sh->dv == 128 && chunk == kda::kChunk;
   if (req == 1) return 1;
   if (req == 2) return mfma ? 2 : -1;
   if (req == 3 && !mfma) return -1;
@@ -88,7 +90,7 @@ const char* kda_strerror(int code) {
     case KDA_OK: return "ok";
     case KDA_ERR_NULL: return "a required pointer is NULL";
     case KDA_ERR_SHAPE: return "invalid shape (B, H >= 1, T >= 0, dk, dv >= 1, sizes must not overflow)";
-    case KDA_ERR_UNSUPPORTED: return "unsupported configuration (chunk must be 16; dk, dv in {32, 64, 128}; dtype f32 or bf16; path)";
+    case KDA_ERR_UNSUPPORTED: return "unsupported configuration (chunk 16, 32 or 64, and 16 on the matrix-core paths; dk, dv in {32, 64, 128}; dtype f32 or bf16; path)";
     case KDA_ERR_ARG: return "invalid argument (g_min NaN or > 0, misaligned pointer, overlapping buffers, workspace too small, reserved field set)";
     case KDA_ERR_HIP: return "HIP runtime error (see kda_last_hip_error)";
     case KDA_ERR_SCRATCH: return "the call needs more scratch than the static array of kda_chunk_fwd_noalloc holds (KDA_NOALLOC_SCRATCH_BYTES); use kda_chunk_fwd with a workspace";
@@ -105,9 +107,9 @@ size_t kda_workspace_bytes(const kda_shape_t* shape, int chunk) {
 }
 
 size_t kda_workspace_bytes_ex(const kda_shape_t* shape, int chunk, const kda_opts_t* opts) {
-  if (check_shape(shape) != KDA_OK || chunk != kda::kChunk) return (size_t)-1;
+  if (check_shape(shape) != KDA_OK || !chunk_ok(chunk)) return (size_t)-1;
   if (opts && (opts->path < 0 || opts->path > 3)) return (size_t)-1;
-  const int path = pick_path(shape, opts);
+  const int path = pick_path(shape, chunk, opts);
   if (path < 0) return (size_t)-1;
   const int64_t seg_steps = opts ? opts->seg_steps : 0;
   if (path >= 2 && !kda::mfma_seg_steps_ok(shape->T, seg_steps)) return (size_t)-1;
@@ -120,7 +122,7 @@ int kda_chunk_fwd_ex(const void* q, const void* k, const void* v, const void* w,
                      kda_stats_t* stats, void* stream, const kda_opts_t* opts) {
   int rc = check_shape(shape);
   if (rc != KDA_OK) return rc;
-  if (chunk != kda::kChunk) return KDA_ERR_UNSUPPORTED;
+  if (!chunk_ok(chunk)) return KDA_ERR_UNSUPPORTED;
   if ((rc = check_gmin(g_min)) != KDA_OK) return rc;
   if (opts) {
     if (opts->seg_steps < 0) return KDA_ERR_ARG;
@@ -170,8 +172,9 @@ int kda_chunk_fwd_ex(const void* q, const void* k, const void* v, const void* w,
   p.disable_fallback = opts ? opts->disable_fallback : 0;
   p.force_fallback = opts ? opts->force_fallback : 0;
   p.seg_steps = opts ? opts->seg_steps : 0;
+  p.chunk = chunk;
 
-  const int path = T > 0 ? pick_path(shape, opts) : 1;
+  const int path = T > 0 ? pick_path(shape, chunk, opts) : 1;
   if (path < 0) return KDA_ERR_UNSUPPORTED;
   if (path >= 2 && !kda::mfma_seg_steps_ok(T, p.seg_steps)) return KDA_ERR_ARG;
   const size_t need_ws = workspace_for(shape, path, p.seg_steps);

@@ -8,7 +8,7 @@
 
 namespace kda {
 
-constexpr int kChunk = 16;          // tokens per chunk (the tile the bounded gate is sized for)
+constexpr int kChunk = 16;          // tokens per chunk of the matrix-core path (the tile the bounded gate is sized for)
 constexpr float kSpanLimit = -80.f; // 16 * g_min for g_min = -5: below it exp(-G) may overflow
 
 struct Params {
@@ -24,6 +24,7 @@ struct Params {
   size_t workspace_bytes;
   kda_stats_t* stats;
   int disable_fallback, force_fallback;
+  int chunk;           // tokens per chunk: 16 (every path), 32 or 64 (the vector path)
   int64_t seg_steps;   // matrix-core path: steps of 32 tokens per segment, 0 = automatic
   __host__ __device__ int64_t n_chunks() const { return (T + kChunk - 1) / kChunk; }
 };

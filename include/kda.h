@@ -29,7 +29,7 @@
  * the pages (Delta networks / Delta Net-like / delta-rule-based models); the
  * form above is the plainest reading with per-key-channel decay.
  *
- * Evaluation.  Chunks of 16 tokens.  Inside a chunk the library uses the
+ * Evaluation.  Chunks of 16 tokens (32 or 64 on request).  Inside a chunk the library uses the
  * exp(+-G) reciprocal form (dense tiles) when the chunk's span, the minimum
  * over key channels of the chunk-local sum of g, is at or above -80; a chunk
  * whose span falls below -80 (possible only with the unbounded gate or
@@ -89,7 +89,7 @@ typedef struct {
 /* Device-resident counters, written with atomics by the kernels of one call.
  * The library resets them at the start of the call (stream-ordered).           */
 typedef struct {
-  uint32_t n_chunks;     /* B * H * ceil(T / 16) */
+  uint32_t n_chunks;     /* B * H * ceil(T / chunk) */
   uint32_t n_flagged;    /* chunks whose span fell below -80 (detected, whatever path ran) */
   uint32_t n_nonfinite;  /* non-finite values written to o or S_final */
   float min_span;        /* minimum chunk span seen; +INFINITY when T = 0 */
@@ -113,7 +113,8 @@ enum {
   KDA_OK = 0,
   KDA_ERR_NULL = -1,        /* a required pointer is NULL */
   KDA_ERR_SHAPE = -2,       /* B, H < 1, T < 0, dk or dv < 1, or sizes overflow */
-  KDA_ERR_UNSUPPORTED = -3, /* chunk != 16, dk or dv not in {32, 64, 128}, unknown dtype or path */
+  KDA_ERR_UNSUPPORTED = -3, /* chunk not in {16, 32, 64} (16 on the matrix-core paths), dk or dv not in
+                               {32, 64, 128}, unknown dtype or path */
   KDA_ERR_ARG = -4,         /* g_min NaN or > 0, misaligned pointer, forbidden overlap,
                                workspace too small, non-zero reserved field, both opts set,
                                bad seg_steps */
@@ -124,7 +125,11 @@ enum {
 /* Forward pass.  Computes o and S_final as defined above.
  *   g_min   finite and <= 0 selects g = g_min * sigmoid(w); -INFINITY selects
  *           g = -softplus(w).  NaN or > 0 is KDA_ERR_ARG.
- *   chunk   must be 16 (the tile the pages fix for g_min = -5).
+ *   chunk   tokens per chunk: 16 (the tile the pages fix for g_min = -5), or 32 or 64 (the
+ *           chunk-size and lower-bound co-design of "From Numerical Stability to Load Balancing ..."
+ *           section 2.3; evaluated on the fp32 vector path, where each chunk takes the reciprocal
+ *           exp(+-G) tiles when its span is at or above -80 and per-pair factors otherwise).  The
+ *           matrix-core paths (opts->path 2, 3) take 16 only.
  *   S0      may be NULL (zero initial state).
  *   workspace / workspace_bytes: device scratch of at least
  *           kda_workspace_bytes(shape, chunk) bytes (kda_workspace_bytes_ex with the same

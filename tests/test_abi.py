@@ -54,7 +54,7 @@ def test_workspace_bytes():
     assert lib.kda_workspace_bytes(ctypes.byref(shape(dtype=0)), 16) == 0
     n = lib.kda_workspace_bytes(ctypes.byref(shape()), 16)
     assert n < (1 << 40)
-    assert lib.kda_workspace_bytes(ctypes.byref(shape()), 32) == ctypes.c_size_t(-1).value
+    assert lib.kda_workspace_bytes(ctypes.byref(shape()), 24) == ctypes.c_size_t(-1).value
     assert lib.kda_workspace_bytes(ctypes.byref(shape(dk=48)), 16) == ctypes.c_size_t(-1).value
     assert lib.kda_workspace_bytes(None, 16) == ctypes.c_size_t(-1).value
 
@@ -83,9 +83,20 @@ def test_null_inputs_allowed_when_empty():
     assert call(shape(T=0), S_final=None, q=None, k=None, v=None, w=None, beta=None, o=None) == -1
 
 
-@pytest.mark.parametrize("chunk", [0, 8, 15, 17, 32, 64])
-def test_chunk_must_be_16(chunk):
+@pytest.mark.parametrize("chunk", [0, 8, 15, 17, 48, 128])
+def test_chunk_sizes(chunk):
+    """16, 32 or 64 tokens per chunk; anything else is unsupported."""
     assert call(chunk=chunk) == -3
+
+
+def test_chunk_32_64_only_on_the_vector_path():
+    """32- and 64-token chunks run on the vector path (no workspace); the matrix-core paths take 16."""
+    for chunk in (32, 64):
+        assert lib.kda_workspace_bytes(ctypes.byref(shape(T=4096)), chunk) == 0
+        for path in (2, 3):
+            assert call(chunk=chunk, opts=KdaOpts(0, 0, path, 0, None, None)) == -3
+            assert lib.kda_workspace_bytes_ex(ctypes.byref(shape()), chunk,
+                                              ctypes.byref(KdaOpts(0, 0, path, 0, None, None))) == ctypes.c_size_t(-1).value
 
 
 @pytest.mark.parametrize("g_min", [float("nan"), 0.5, 1e-30, float("inf")])
@@ -237,7 +248,7 @@ def test_noalloc_rejects_calls_beyond_its_scratch():
         p[0], p[1], p[2], p[3], p[4], None, ctypes.c_float(g_min), chunk, ctypes.byref(sh), p[5], S_final,
         p[8], None)
     assert na(big) == _lib.KDA_ERR_SCRATCH == -6
-    assert na(shape(), chunk=32) == -3
+    assert na(shape(), chunk=48) == -3
     assert na(shape(dk=48)) == -3
     assert na(shape(), g_min=1.0) == -4
     assert na(shape(), S_final=None) == -1
