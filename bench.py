@@ -478,7 +478,9 @@ def main():
     ap.add_argument("--no-accuracy", action="store_true",
                     help="skip the check of the sampled heads against the fp64 oracle (and, for the "
                          "million workload, the state drift curve)")
-    ap.add_argument("--force-fallback", action="store_true")
+    ap.add_argument("--force-fallback", action="store_true",
+                    help="every chunk takes a flagged chunk's handling (midpoint tiles or per-pair factors)")
+    ap.add_argument("--force-pairwise", action="store_true", help="every chunk takes the per-pair factors")
     ap.add_argument("--mode", default="forward", choices=["forward", "decode", "bwd"],
                     help="forward: the chunked forward (the headline); decode: one recurrent decode "
                          "step of a serving batch (workload decode_b512 unless --workload is given); "
@@ -522,7 +524,7 @@ def main():
     log(f"[bench] workload {wl}")
     inp = gen.make_torch(wl, seed=args.seed, device="cuda")
     torch.cuda.synchronize()
-    kw = dict(path=args.path, force_fallback=args.force_fallback)
+    kw = dict(path=args.path, force_fallback=2 if args.force_pairwise else int(args.force_fallback))
     kern_avg, kern_ms, wall, stats, o, S = time_forward(torch, inp, wl, wl.g_min, args.steps, args.warmup, kw)
     log(f"[bench] kernel ms: avg {kern_avg:.4f} min {min(kern_ms):.4f} max {max(kern_ms):.4f}; wall/step "
         f"{1e3 * wall / args.steps:.4f} ms; stats {stats}")

@@ -64,7 +64,7 @@ def workspace_bytes(B, H, T, dk, dv, dtype=torch.bfloat16, chunk=16, path: str =
 
 def chunk_fwd(q, k, v, w, beta, S0=None, g_min: float = -5.0, chunk: int = 16, *,
               out=None, S_final=None, stats: bool = True, workspace=None, stream=None,
-              disable_fallback: bool = False, force_fallback: bool = False,
+              disable_fallback: bool = False, force_fallback: int = 0,
               path: str = "auto", events=None, seg_steps: int = 0):
     """KDA chunked forward through kda_chunk_fwd_ex.
 
@@ -75,6 +75,8 @@ def chunk_fwd(q, k, v, w, beta, S0=None, g_min: float = -5.0, chunk: int = 16, *
     current torch stream).  `events` = (begin, end) HipEvent pair recorded
     before the first kernel of the call and after its last.  `seg_steps` > 0
     fixes the matrix-core path's sequence segment length (in 32-token steps).
+    `force_fallback` = 1 (or True) gives every chunk a flagged chunk's handling, 2 the per-pair
+    factors on every chunk; `disable_fallback` lets flagged chunks take the plain tiles.
     """
     if q.dim() != 4:
         raise ValueError("q must be [B,H,T,dk]")
@@ -100,7 +102,7 @@ def chunk_fwd(q, k, v, w, beta, S0=None, g_min: float = -5.0, chunk: int = 16, *
     else:
         _check(S_final, "S_final", (B, H, dk, dv), torch.float32, dev)
     shape = make_shape(B, H, T, dk, dv, _dtype_code(q))
-    opts = KdaOpts(int(bool(disable_fallback)), int(bool(force_fallback)), _PATHS[path], int(seg_steps),
+    opts = KdaOpts(int(bool(disable_fallback)), int(force_fallback), _PATHS[path], int(seg_steps),
                    events[0].handle if events else None, events[1].handle if events else None)
     plain = not (disable_fallback or force_fallback or path != "auto" or seg_steps or events)
     ws_need = _lib.workspace_bytes(shape, chunk, None if plain else opts)

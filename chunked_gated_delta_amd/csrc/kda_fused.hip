@@ -48,6 +48,9 @@ constexpr int kCWaves = 8;                    // wavefronts 0-7: state slices, t
 static_assert(kCWaves == kRecChunks - kRecNonfinite, "one non-finite count per state wavefront in the record");
 constexpr int kEWaves = 8;                    // wavefronts 8-15: the E stage
 constexpr int kThreads = 64 * (kCWaves + kEWaves);
+// gate kinds (kernel template argument): bounded with 16 g_min >= -80 (no chunk can need the flagged
+// forms), bounded past that or with the fallback forced, and the unbounded gate
+constexpr int kGatePlain = 0, kGateFlagged = 1, kGateUnbounded = 2;
 
 // ---- operand blocks: one MFMA operand (64 lanes x 16 B), with a 16-byte pad after every 16 lanes,
 // so that the 4-byte writes of the E stage (16 lanes 256 B apart) land in distinct LDS banks, while a
@@ -84,6 +87,10 @@ constexpr int pL = 0, pK = 16 * kPL * 4, pQ = pK + 16 * kPK * 2;
 static_assert(pQ + 16 * kPK * 2 <= kOps, "per-pair inputs fit the borrowed buffer");
 static_assert(pK % 16 == 0 && pQ % 16 == 0 && kOps % 16 == 0, "16-byte reads of the per-pair inputs");
 
+// the midpoint-referenced rows of flagged chunks (k e^{L - L_7}, q e^{L - L_7}) also go to the other
+// tile-operand buffer, same arrangement as rKb, written with the step's operands and read by its tiles
+constexpr int mK0 = 0, mQ0 = 4 * kBlk, mK1 = 8 * kBlk, mQ1 = 12 * kBlk;
+static_assert(mQ1 + 4 * kBlk <= kOps, "the midpoint rows fit the borrowed buffer");
 constexpr int kOpT00 = 0, kOpT11 = 512, kOpA10 = 1024;   // byte offsets of the three blocks within rT
 static_assert(kOpA10 + 512 <= 2 * kBlk, "the T operands fit their region");
 constexpr int kORow = D * 2 + 16;   // bytes per staged output row (256 of data, 16 of pad)
@@ -94,6 +101,7 @@ struct StepInfo {
   uint32_t n_valid;       // chunks with at least one token
   uint32_t n_flagged;     // of those, spans below -80
   uint32_t pairwise;      // bit c: chunk c's diagonal blocks come from per-pair factors
+  uint32_t midpoint;      // bit c: chunk c's diagonal blocks come from the midpoint-referenced tiles
 };
 
 struct FusedShared {
@@ -103,6 +111,7 @@ struct FusedShared {
   float pwA[2][16][16], pwP[2][16][16];   // per-pair diagonal blocks [chunk][r][j]
   float gam[2][D];                        // chunk totals (log2 units) of the step in E
   float spanw[kEWaves];                   // per-E-wave minimum of the chunk totals
+  uint32_t halfw[kEWaves];                // per E wave: 1 if one of its channels has a half-chunk span below -80
   // bf16 rows of the step in C, padded to 272 bytes so that column-slice accesses spread over the
   // banks.  First half: each C wavefront reads V and then writes o, both in its own 16 columns.
   // Second half: wavefronts 0-3 store eight rows of o each as whole rows, then fill the same rows
@@ -211,7 +220,7 @@ __device__ __forceinline__ float wave_min_totals(float g0, float g1) {
 
 // First half of E for chunk CC of the step: gates, the in-chunk prefix L, the chunk totals, the span
 // of the wave's channels, and beta.
-template <bool UNB, int CC>
+template <bool UNB, int CC, bool FLG>
 __device__ __forceinline__ void e_first(FusedShared& sm, const EIn& in, EKeep& kp, const Params& p, int step,
                                         unsigned char* rec, int w, int l) {
   const int pr = 16 * (w & 3) + (l >> 2), h = l & 3;
@@ -257,6 +266,16 @@ __device__ __forceinline__ void e_first(FusedShared& sm, const EIn& in, EKeep& k
   if (h == 0) { sm.gam[CC][c0] = kp.G0; sm.gam[CC][c1] = kp.G1; }
   const float m = wave_min_totals(kp.G0, kp.G1);
   if (l == 63) sm.spanw[w] = m;
+  // the prefix at token 7 (lane h = 1, j = 3 of the quarter group) and the spans of the two 8-token
+  // halves, L_7 and Gam - L_7: whether any of the wave's channels has a half below -80 decides between
+  // the midpoint-referenced tiles and the per-pair blocks for a flagged chunk
+  if (FLG) {
+    const float H0 = dpp<0x55>(0.f, kp.L0[3]), H1 = dpp<0x55>(0.f, kp.L1[3]);   // quad_perm [1,1,1,1]
+    const float lim = kSpanLimit * kLog2e;
+    const bool bad = fminf(fminf(H0, kp.G0 - H0), fminf(H1, kp.G1 - H1)) < lim;
+    const uint32_t anybad = __builtin_amdgcn_readfirstlane(__ballot(bad) != 0ull ? 1u : 0u);
+    if (l == 0) sm.halfw[w] = anybad;
+  }
   if ((w & 3) == 0 && (l >> 2) == 0) {
     float* bt = reinterpret_cast<float*>(rec + rBeta);
 #pragma unroll
@@ -270,6 +289,34 @@ __device__ __forceinline__ void pair_of(int pr, int& r, int& j) {   // pr -> (r,
   j = pr - r * (r + 1) / 2;
 }
 
+// How the diagonal blocks of the step in E are formed.  A chunk whose span falls below -80 (or every
+// chunk, when the fallback is forced) cannot take the chunk-start-referenced tiles, whose factor
+// e^{-L} would pass e^{80}.  When both of its 8-token halves span at least -80 it takes the same tiles
+// referenced to its token 7 instead: rows k e^{L - L_7} and q e^{L - L_7}, columns k e^{L_7 - L}, every
+// factor at most e^{80} (rows of the first half and columns of the second are the ones above 1), and
+// every kept product e^{L_r - L_j} exact.  Otherwise it takes the per-pair blocks.  The midpoint rows
+// live in the other tile-operand buffer, which the per-pair blocks also borrow, so a step with any
+// per-pair chunk takes the per-pair blocks for every chunk that needs more than the plain tiles.
+// force_fallback = 2 forces the per-pair blocks on every chunk.  Every thread of the workgroup reads
+// the same shared values, so the answer (and every branch on it) is uniform.
+struct Modes {
+  uint32_t pw, mid;   // bit c: chunk c takes the per-pair blocks / the midpoint-referenced tiles
+};
+__device__ __forceinline__ Modes step_modes(const FusedShared& sm, const Params& p, int step) {
+  const int t0 = step * STEP;
+  const bool valid0 = t0 < (int)p.T, valid1 = t0 + 16 < (int)p.T;
+  const float span0 = fminf(fminf(sm.spanw[0], sm.spanw[1]), fminf(sm.spanw[2], sm.spanw[3])) * kLn2;
+  const float span1 = fminf(fminf(sm.spanw[4], sm.spanw[5]), fminf(sm.spanw[6], sm.spanw[7])) * kLn2;
+  const bool x0 = p.force_fallback || (valid0 && span0 < kSpanLimit && !p.disable_fallback);
+  const bool x1 = p.force_fallback || (valid1 && span1 < kSpanLimit && !p.disable_fallback);
+  const uint32_t x = (x0 ? 1u : 0u) | (x1 ? 2u : 0u);
+  if (__builtin_expect(x == 0u, 1)) return Modes{0u, 0u};
+  const bool bad0 = (sm.halfw[0] | sm.halfw[1] | sm.halfw[2] | sm.halfw[3]) != 0u;
+  const bool bad1 = (sm.halfw[4] | sm.halfw[5] | sm.halfw[6] | sm.halfw[7]) != 0u;
+  const bool pair = p.force_fallback == 2 || (x0 && bad0) || (x1 && bad1);
+  return Modes{pair ? x : 0u, pair ? 0u : x};
+}
+
 // Second half of E for chunk CC: e^{L}, and every operand of the step built from k, q and the gate
 // factors (the exponentials sit here rather than in the first half, which the state wavefronts bound).
 //   chunk 0: k e^{-L} (tiles), -beta k e^{L} and q e^{L} (step-referenced = chunk-local), k e^{Gam_0 - L}
@@ -278,13 +325,16 @@ __device__ __forceinline__ void pair_of(int pr, int& r, int& j) {   // pr -> (r,
 //            (with -beta for k), Ktil = k e^{Gam_1 - L}
 // e^{-L} = e^{Gam - L} e^{-Gam}: finite wherever the dense tile is used (a chunk whose e^{-Gam}
 // overflows has a span below -80 and takes the per-pair blocks instead).
-template <bool OUT, int CC>
+template <bool OUT, int CC, bool MID>
 __device__ __forceinline__ void e_second(FusedShared& sm, const EKeep& kp, const Params& p, int step,
-                                         unsigned char* rec, unsigned char* ops, int w, int l) {
+                                         unsigned char* rec, unsigned char* ops, unsigned char* opsM, Modes md,
+                                         int w, int l) {
   const int pr = 16 * (w & 3) + (l >> 2), h = l & 3;
   const int u = w & 3, g = ((l >> 2) & 7) >> 1, pos = (l >> 5) * 4 + 2 * ((l >> 2) & 1);
   const int c0 = 2 * pr, c1 = 2 * pr + 1;
   const float iG0 = __builtin_amdgcn_exp2f(-kp.G0), iG1 = __builtin_amdgcn_exp2f(-kp.G1);
+  // midpoint reference: the prefix at token 7 (lane h = 1, j = 3 of the quarter group)
+  const float H0 = MID ? dpp<0x55>(0.f, kp.L0[3]) : 0.f, H1 = MID ? dpp<0x55>(0.f, kp.L1[3]) : 0.f;
   // e^{Gam} of the other chunk, per channel
   const float y0 = __builtin_amdgcn_exp2f(sm.gam[1 - CC][c0]), y1 = __builtin_amdgcn_exp2f(sm.gam[1 - CC][c1]);
   float eL0[4], eL1[4];
@@ -301,7 +351,17 @@ __device__ __forceinline__ void e_second(FusedShared& sm, const EKeep& kp, const
     const float kg0 = k0 * __builtin_amdgcn_exp2f(kp.G0 - kp.L0[j]), kg1 = k1 * __builtin_amdgcn_exp2f(kp.G1 - kp.L1[j]);
     const float ke0 = k0 * eL0[j], ke1 = k1 * eL1[j];
     const float nb = -kp.beta[j];
-    *reinterpret_cast<uint32_t*>(ops + oKh + rowk_off(CC, u, li, g, pos)) = pk_bf16(kg0 * iG0, kg1 * iG1);
+    if (MID) {   // midpoint-referenced tile operands: columns k e^{L_7 - L}, rows k e^{L - L_7}, q e^{L - L_7}
+      const float rf0 = __builtin_amdgcn_exp2f(kp.L0[j] - H0), rf1 = __builtin_amdgcn_exp2f(kp.L1[j] - H1);
+      const float cf0 = __builtin_amdgcn_exp2f(H0 - kp.L0[j]), cf1 = __builtin_amdgcn_exp2f(H1 - kp.L1[j]);
+      *reinterpret_cast<uint32_t*>(ops + oKh + rowk_off(CC, u, li, g, pos)) = pk_bf16(k0 * cf0, k1 * cf1);
+      *reinterpret_cast<uint32_t*>(opsM + (CC ? mK1 : mK0) + rowk_off(0, u, li, g, pos)) = pk_bf16(k0 * rf0, k1 * rf1);
+      if (OUT)
+        *reinterpret_cast<uint32_t*>(opsM + (CC ? mQ1 : mQ0) + rowk_off(0, u, li, g, pos)) =
+            pk_bf16(lo_bf16(kp.q[j]) * rf0, hi_bf16(kp.q[j]) * rf1);
+    } else {
+      *reinterpret_cast<uint32_t*>(ops + oKh + rowk_off(CC, u, li, g, pos)) = pk_bf16(kg0 * iG0, kg1 * iG1);
+    }
     if (CC == 0) {
       *reinterpret_cast<uint32_t*>(rec + rKb + rowk_off(0, u, li, g, pos)) = pk_bf16(nb * ke0, nb * ke1);
       if (OUT)
@@ -343,23 +403,11 @@ __device__ __forceinline__ void e_second(FusedShared& sm, const EKeep& kp, const
       si.span[1] = valid1 ? span1 : __int_as_float(0x7f800000);
       si.n_valid = (valid0 ? 1u : 0u) + (valid1 ? 1u : 0u);
       si.n_flagged = (flag0 ? 1u : 0u) + (flag1 ? 1u : 0u);
-      si.pairwise = (p.force_fallback || (flag0 && !p.disable_fallback) ? 1u : 0u) |
-                    (p.force_fallback || (flag1 && !p.disable_fallback) ? 2u : 0u);
+      si.pairwise = md.pw;
+      si.midpoint = md.mid;
       *reinterpret_cast<StepInfo*>(rec + rMeta) = si;
     }
   }
-}
-
-// Which chunks of the step in E take the per-pair blocks (bit c: chunk c).  Every thread of the
-// workgroup reads the same shared values, so the answer (and every branch on it) is uniform.
-__device__ __forceinline__ uint32_t pairwise_mask(const FusedShared& sm, const Params& p, int step) {
-  const int t0 = step * STEP;
-  const bool valid0 = t0 < (int)p.T, valid1 = t0 + 16 < (int)p.T;
-  const float span0 = fminf(fminf(sm.spanw[0], sm.spanw[1]), fminf(sm.spanw[2], sm.spanw[3])) * kLn2;
-  const float span1 = fminf(fminf(sm.spanw[4], sm.spanw[5]), fminf(sm.spanw[6], sm.spanw[7])) * kLn2;
-  const bool pw0 = p.force_fallback || (valid0 && span0 < kSpanLimit && !p.disable_fallback);
-  const bool pw1 = p.force_fallback || (valid1 && span1 < kSpanLimit && !p.disable_fallback);
-  return (pw0 ? 1u : 0u) | (pw1 ? 2u : 0u);
 }
 
 // Per-pair diagonal blocks of flagged chunks, by the whole workgroup: A_rj = beta_r sum_c k_rc k_jc
@@ -437,31 +485,36 @@ static_assert(136 * 4 <= kThreads, "one per-pair item per thread");
 // Each tile is formed transposed (operands swapped), so that lane (li, g) holds row li, columns
 // 4g .. 4g+3: the diagonal blocks of A go to the solver as fp32 rows, the coupling block -A_10 and
 // the blocks of P go straight into their bf16 operand places.
-template <bool OUT>
-__device__ __forceinline__ void tiles(FusedShared& sm, unsigned char* rec, const unsigned char* ops, uint32_t pwmask,
-                                      int par, int w, int lane) {
+template <bool OUT, bool MID>
+__device__ __forceinline__ void tiles(FusedShared& sm, unsigned char* rec, const unsigned char* ops,
+                                      const unsigned char* opsM, uint32_t pwmask, uint32_t mid_in, int par, int w,
+                                      int lane) {
+  const uint32_t mid = MID ? mid_in : 0u;
   const int li = lane & 15, lg = lane >> 4;
   if (w >= (OUT ? 6 : 3)) return;
   const float* bt = reinterpret_cast<const float*>(rec + rBeta);
   const unsigned char *a, *b;
+  // a chunk in midpoint mode (mid bit c) takes its diagonal blocks' rows from the midpoint buffer; its
+  // columns in oKh are then midpoint-referenced as well
   switch (w) {
-    case 0: a = rec + rKb; b = ops + oKh; break;             // A_00 (rows of -beta Kbar)
-    case 1: a = ops + oKb1; b = ops + oKh + 4 * kBlk; break; // A_11
-    case 2: a = ops + oKb1; b = ops + oKt0; break;           // A_10
-    case 3: a = rec + rQb; b = ops + oKh; break;             // P_00
-    case 4: a = ops + oQb1; b = ops + oKh + 4 * kBlk; break; // P_11
-    default: a = ops + oQb1; b = ops + oKt0; break;          // P_10
+    case 0: a = (mid & 1u) ? opsM + mK0 : rec + rKb; b = ops + oKh; break;              // A_00 (rows of -beta Kbar)
+    case 1: a = (mid & 2u) ? opsM + mK1 : ops + oKb1; b = ops + oKh + 4 * kBlk; break;  // A_11
+    case 2: a = ops + oKb1; b = ops + oKt0; break;                                      // A_10
+    case 3: a = (mid & 1u) ? opsM + mQ0 : rec + rQb; b = ops + oKh; break;              // P_00
+    case 4: a = (mid & 2u) ? opsM + mQ1 : ops + oQb1; b = ops + oKh + 4 * kBlk; break;  // P_11
+    default: a = ops + oQb1; b = ops + oKt0; break;                                     // P_10
   }
   floatx4 acc = {0, 0, 0, 0};
 #pragma unroll
   for (int u = 0; u < 4; ++u) acc = mfma(ld8(b + u * kBlk + slot16(lane)), ld8(a + u * kBlk + slot16(lane)), acc);
   floatx4 x;
-  const float b1 = (w == 1 || w == 2) ? bt[16 + li] : 0.f;
+  const bool mid0 = w == 0 && (mid & 1u);   // A_00 from midpoint rows, which carry no -beta
+  const float b1 = (w == 1 || w == 2) ? bt[16 + li] : mid0 ? bt[li] : 0.f;
 #pragma unroll
   for (int r = 0; r < 4; ++r) {
     const int c = 4 * lg + r;   // element (li, c) of the block
     switch (w) {
-      case 0: x[r] = c < li ? -acc[r] : 0.f; break;
+      case 0: x[r] = c < li ? (mid0 ? b1 * acc[r] : -acc[r]) : 0.f; break;
       case 1: x[r] = c < li ? b1 * acc[r] : 0.f; break;
       case 2: x[r] = -b1 * acc[r]; break;
       case 3: case 4: x[r] = c <= li ? acc[r] : 0.f; break;
@@ -563,7 +616,7 @@ __device__ __forceinline__ int rows_left(int T, int step) {
 
 // E wavefronts of chunk CC.  Interval s: first half E1(s+2), second half E2(s+2) and, for a flagged
 // chunk, the per-pair blocks of step s+2.
-template <bool OUT, bool UNB, int CC>
+template <bool OUT, int GK, int CC>
 __device__ __forceinline__ void e_loop(FusedShared& sm, const Params& p, const Views& vw, int s0, int ns, int we,
                                        int lane, int tid) {
   const int e_voff = ((16 * CC + 4 * (lane & 3)) * D + 2 * (16 * (we & 3) + (lane >> 2))) * 2;
@@ -581,15 +634,20 @@ __device__ __forceinline__ void e_loop(FusedShared& sm, const Params& p, const V
     unsigned char* opsF = sm.ops[(it + 3) & 1];           // step it + 1 (free once its tiles are formed)
     block_barrier();
     const int ln = opaque(lane);   // lane-derived offsets are recomputed in the loop rather than held
-    if (doE) e_first<UNB, CC>(sm, ein, ekeep, p, s0 + it + 2, recE, we, ln);
+    if (doE) e_first<GK == kGateUnbounded, CC, GK != kGatePlain>(sm, ein, ekeep, p, s0 + it + 2, recE, we, ln);
     // prefetches are issued on every path (clamped to the segment's last step) so that the memory
     // counter waits before their uses stay exact
     e_load<OUT>(ein, vw, s0 + (it + 3 < ns ? it + 3 : ns - 1), e_voff, e_boff);
     block_barrier();
     if (doE) {
-      e_second<OUT, CC>(sm, ekeep, p, s0 + it + 2, recE, opsE, we, ln);
-      const uint32_t pwmask = pairwise_mask(sm, p, s0 + it + 2);
-      if (pwmask) pairwise_blocks<OUT, true>(sm, &ekeep, recE, opsF, pwmask, we, ln, tid);
+      const Modes md = GK != kGatePlain ? step_modes(sm, p, s0 + it + 2) : Modes{0u, 0u};
+      // the midpoint operands in a copy of their own, so that the common step runs the plain one
+      if (GK != kGatePlain && __builtin_expect((md.mid >> CC) & 1u, 0))
+        e_second<OUT, CC, true>(sm, ekeep, p, s0 + it + 2, recE, opsE, opsF, md, we, ln);
+      else
+        e_second<OUT, CC, false>(sm, ekeep, p, s0 + it + 2, recE, opsE, opsF, md, we, ln);
+      if (GK != kGatePlain && __builtin_expect(md.pw != 0u, 0))
+        pairwise_blocks<OUT, true>(sm, &ekeep, recE, opsF, md.pw, we, ln, tid);
     }
   }
 }
@@ -602,7 +660,7 @@ __device__ __forceinline__ void e_loop(FusedShared& sm, const Params& p, const V
 // segment j.  `early` (OUT only): segment 0 running inside the map pass; its leaving state is then the
 // entering state of segment 1, where the chaining pass starts, and its statistics go to a per-head
 // record that the chaining pass folds into the call's counters.
-template <bool OUT, bool UNB>
+template <bool OUT, int GK>
 __device__ __forceinline__ void fused_body(FusedShared& sm, const Params& p, int64_t n_steps, const SegPlan& sg,
                                            int64_t bh, int j, bool early) {
   const int tid = threadIdx.x;
@@ -632,8 +690,8 @@ __device__ __forceinline__ void fused_body(FusedShared& sm, const Params& p, int
   // The two kinds of wavefront run separate copies of the step loop (same trip count, same barriers in
   // the same order), so that each copy holds only its own kind's values in registers.
   if (is_e) {
-    if (we < 4) e_loop<OUT, UNB, 0>(sm, p, vw, s0, ns, we, lane, tid);
-    else e_loop<OUT, UNB, 1>(sm, p, vw, s0, ns, we, lane, tid);
+    if (we < 4) e_loop<OUT, GK, 0>(sm, p, vw, s0, ns, we, lane, tid);
+    else e_loop<OUT, GK, 1>(sm, p, vw, s0, ns, we, lane, tid);
     return;
   }
 
@@ -775,7 +833,12 @@ __device__ __forceinline__ void fused_body(FusedShared& sm, const Params& p, int
       }
     }
     // ---- the causal tiles of step it + 1 (their chunk flags are in its information record)
-    if (doS) tiles<OUT>(sm, recS, opsF, reinterpret_cast<const StepInfo*>(recS + rMeta)->pairwise, (int)((it + 1) & 1), w, ln);
+    if (doS) {
+      const StepInfo* si = reinterpret_cast<const StepInfo*>(recS + rMeta);
+      const uint32_t mid = GK != kGatePlain ? si->midpoint : 0u;
+      if (GK != kGatePlain && __builtin_expect(mid != 0u, 0)) tiles<OUT, true>(sm, recS, opsF, sm.ops[(it + 2) & 1], si->pairwise, mid, (int)((it + 1) & 1), w, ln);
+      else tiles<OUT, false>(sm, recS, opsF, sm.ops[(it + 2) & 1], si->pairwise, 0u, (int)((it + 1) & 1), w, ln);
+    }
     if (!OUT && w < 4) {   // V of step it + 1 (the map pass has no registers to carry it over the chain)
       const int sn = s0 + (it + 1 < 0 ? 0 : (it + 1 < ns ? it + 1 : ns - 1));
 #pragma unroll
@@ -802,11 +865,13 @@ __device__ __forceinline__ void fused_body(FusedShared& sm, const Params& p, int
       for (int i = 0; i < 2; ++i)
         *reinterpret_cast<uint4*>(&sm.ostage[8 * w + 4 * i + (lane >> 4)][(lane & 15) * 16]) = vq[i];
     }
-    if (doE) {
-      const uint32_t pwmask = pairwise_mask(sm, p, s0 + it + 2);
-      if (pwmask) pairwise_blocks<OUT, false>(sm, nullptr, recE, opsF, pwmask, 0, ln, tid);
-    }
+    // T of step it + 1 first: it shares nothing with the per-pair blocks, so on a flagged step it
+    // overlaps the E stage instead of following the per-pair barriers
     if (doS && w >= 6) solve_block(sm, recS, (int)((it + 1) & 1), w - 6, ln);
+    if (GK != kGatePlain && doE) {
+      const uint32_t pwmask = step_modes(sm, p, s0 + it + 2).pw;
+      if (__builtin_expect(pwmask != 0u, 0)) pairwise_blocks<OUT, false>(sm, nullptr, recE, opsF, pwmask, 0, ln, tid);
+    }
   }
 
   if (OUT) {
@@ -872,7 +937,7 @@ __device__ __forceinline__ void fused_body(FusedShared& sm, const Params& p, int
 // OUT: the output pass, segments 1 .. P-1 (segment 0 ran in the map pass), or the only segment of a
 // one-segment plan.  !OUT (plans of two or more segments): the map pass, segment 0 with its outputs
 // (it needs no map: its entering state is S0) beside the maps of segments 1 .. P-2.
-template <bool OUT, bool UNB>
+template <bool OUT, int GK>
 __global__ __launch_bounds__(kThreads) void fused_kernel(Params p, int64_t n_steps, SegPlan sg) {
   extern __shared__ __align__(16) unsigned char smem_raw[];
   FusedShared& sm = *reinterpret_cast<FusedShared*>(smem_raw);
@@ -880,26 +945,26 @@ __global__ __launch_bounds__(kThreads) void fused_kernel(Params p, int64_t n_ste
   const int64_t bh = blockIdx.x / nb;
   const int i = (int)(blockIdx.x % nb);
   if (OUT) {
-    fused_body<true, UNB>(sm, p, n_steps, sg, bh, sg.P > 1 ? i + 1 : 0, false);
+    fused_body<true, GK>(sm, p, n_steps, sg, bh, sg.P > 1 ? i + 1 : 0, false);
   } else if (i == 0) {
-    fused_body<true, UNB>(sm, p, n_steps, sg, bh, 0, true);
+    fused_body<true, GK>(sm, p, n_steps, sg, bh, 0, true);
   } else {
-    fused_body<false, UNB>(sm, p, n_steps, sg, bh, i, false);
+    fused_body<false, GK>(sm, p, n_steps, sg, bh, i, false);
   }
 }
 
-template <bool OUT, bool UNB>
+template <bool OUT, int GK>
 hipError_t launch_one(const Params& p, hipStream_t s, int64_t n_steps, const SegPlan& sg) {
   static bool attr_set = false;
   if (!attr_set) {
-    hipError_t e = hipFuncSetAttribute((const void*)fused_kernel<OUT, UNB>, hipFuncAttributeMaxDynamicSharedMemorySize,
+    hipError_t e = hipFuncSetAttribute((const void*)fused_kernel<OUT, GK>, hipFuncAttributeMaxDynamicSharedMemorySize,
                                        (int)kFusedSmem);
     if (e != hipSuccess) return e;
     attr_set = true;
   }
   if (!OUT && sg.P < 2) return hipErrorInvalidValue;   // a one-segment plan has no map pass
   const int64_t nb = sg.P > 1 ? sg.P - 1 : 1;
-  hipLaunchKernelGGL((fused_kernel<OUT, UNB>), dim3((unsigned)(p.B * p.H * nb)), dim3(kThreads), kFusedSmem, s, p,
+  hipLaunchKernelGGL((fused_kernel<OUT, GK>), dim3((unsigned)(p.B * p.H * nb)), dim3(kThreads), kFusedSmem, s, p,
                      n_steps, sg);
   return hipGetLastError();
 }
@@ -911,9 +976,16 @@ bool fused_supported(int dtype, int64_t dk, int64_t dv, int64_t T) {
   return dtype == KDA_DTYPE_BF16 && dk == D && dv == D && T < ((int64_t)1 << 23);
 }
 
+// The gate kind of a call.  With a bounded gate and 16 g_min >= -80 every chunk's span is at least -80
+// (up to the rounding of its sum of 16 gates, which moves e^{-L} by a factor 1 + 2^-20 at most, far from
+// the fp32 limit e^{88.7}), so no chunk can need more than the plain tiles and the kernel is built
+// without the flagged-chunk forms; flags are still counted.  A deeper bound, a forced fallback or the
+// unbounded gate take the kernel with them.
 hipError_t launch_fused_segments(const Params& p, hipStream_t s, int64_t n_steps, const SegPlan& sg, bool out) {
-  if (out) return p.unbounded ? launch_one<true, true>(p, s, n_steps, sg) : launch_one<true, false>(p, s, n_steps, sg);
-  return p.unbounded ? launch_one<false, true>(p, s, n_steps, sg) : launch_one<false, false>(p, s, n_steps, sg);
+  const bool plain = !p.unbounded && !p.force_fallback && (p.disable_fallback || 16.f * p.g_min >= kSpanLimit);
+  if (p.unbounded) return out ? launch_one<true, kGateUnbounded>(p, s, n_steps, sg) : launch_one<false, kGateUnbounded>(p, s, n_steps, sg);
+  if (plain) return out ? launch_one<true, kGatePlain>(p, s, n_steps, sg) : launch_one<false, kGatePlain>(p, s, n_steps, sg);
+  return out ? launch_one<true, kGateFlagged>(p, s, n_steps, sg) : launch_one<false, kGateFlagged>(p, s, n_steps, sg);
 }
 
 }  // namespace kda

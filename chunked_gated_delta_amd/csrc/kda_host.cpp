@@ -127,6 +127,7 @@ int kda_chunk_fwd_ex(const void* q, const void* k, const void* v, const void* w,
   if (opts) {
     if (opts->seg_steps < 0) return KDA_ERR_ARG;
     if (opts->disable_fallback && opts->force_fallback) return KDA_ERR_ARG;
+    if (opts->force_fallback < 0 || opts->force_fallback > 2) return KDA_ERR_ARG;
     if (opts->path < 0 || opts->path > 3) return KDA_ERR_UNSUPPORTED;
   }
   const int64_t B = shape->B, H = shape->H, T = shape->T, dk = shape->dk, dv = shape->dv;

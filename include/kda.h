@@ -98,7 +98,11 @@ typedef struct {
 /* Measurement knobs for kda_chunk_fwd_ex. Zero-initialised means "default". */
 typedef struct {
   int32_t disable_fallback; /* 1: flagged chunks still take the dense exp(+-G) path (shows the overflow) */
-  int32_t force_fallback;   /* 1: every chunk takes the per-position path (measures its cost) */
+  int32_t force_fallback;   /* 1: every chunk takes the handling of a flagged chunk (measures its cost):
+                               on the fused path the tiles referenced to the chunk's token 7 where both
+                               8-token halves span at least -80, per-position factors otherwise; on the
+                               other paths per-position factors.  2: every chunk takes the per-position
+                               factors.  Other values are KDA_ERR_ARG. */
   int32_t path;             /* 0 auto (bf16 with dk = dv = 128: the fused matrix-core path, or the
                                records path past T = 2^23; anything else: the vector path),
                                1 the plain fp32 vector path, 2 the matrix-core path with per-step

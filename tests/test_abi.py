@@ -151,6 +151,8 @@ def test_workspace_too_small():
 
 def test_opts_validation():
     assert call(opts=KdaOpts(1, 1, 0, 0, None, None)) == -4     # both knobs
+    assert call(opts=KdaOpts(0, 3, 0, 0, None, None)) == -4     # force_fallback takes 0, 1 or 2
+    assert call(opts=KdaOpts(0, -1, 0, 0, None, None)) == -4
     assert call(opts=KdaOpts(0, 0, 0, -1, None, None)) == -4    # negative segment length
     # a forced segment length giving more than 32 segments per sequence (33 steps of 32 tokens)
     assert call(sh=shape(T=33 * 32), opts=KdaOpts(0, 0, 0, 1, None, None)) == -4

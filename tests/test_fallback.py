@@ -1,7 +1,8 @@
-"""Unbounded gates: chunks whose span falls below -80 are detected and take the
-per-position path; the flagged set is the one the oracle predicts, outputs
-match the oracle, turning the fallback off shows the overflow, and forcing it
-everywhere still matches."""
+"""Unbounded gates and deep lower bounds: chunks whose span falls below -80 are detected and take
+a flagged chunk's handling (on the fused path the tiles referenced to the chunk's token 7 when both
+8-token halves span at least -80, per-position factors otherwise); the flagged set is the one the
+oracle predicts, outputs match the oracle, turning the fallback off shows the overflow, and forcing
+either form everywhere still matches."""
 import math
 
 import numpy as np
@@ -51,10 +52,45 @@ def test_disabling_fallback_shows_overflow(path):
 
 @pytest.mark.parametrize("path", PATHS)
 @pytest.mark.parametrize("g_min", [-5.0, -math.inf])
-def test_forced_fallback_matches(path, g_min):
+@pytest.mark.parametrize("force", [1, 2])
+def test_forced_fallback_matches(path, g_min, force):
+    """force 1: every chunk takes a flagged chunk's handling (on the fused path the tiles referenced to
+    the chunk's token 7, or per-pair factors where a half spans below -80); force 2: per-pair factors."""
     wl = UNB.with_(B=1, H=2, T=300, g_min=g_min, w_mu=0.0 if g_min == -5.0 else 3.0)
-    eo, es, st, *_ = compare(wl, seed=1, path=path, force_fallback=True)
+    eo, es, st, *_ = compare(wl, seed=1, path=path, force_fallback=force)
     say(f"   err_o={eo:.3e} err_S={es:.3e} stats={st}")
+    assert eo <= TOL["bf16"][0] and es <= TOL["bf16"][1]
+    assert st["n_nonfinite"] == 0
+
+
+def half_spans(w, g_min):
+    """Per 16-token chunk, the minimum over channels of the spans of its two 8-token halves (fp64)."""
+    g = orc.gate(w, g_min)
+    B, H, T, D = g.shape
+    n = T // 16
+    L = np.cumsum(g[:, :, :16 * n].reshape(B, H, n, 16, D), axis=3)
+    return np.minimum(L[:, :, :, 7, :], L[:, :, :, 15, :] - L[:, :, :, 7, :]).min(-1)
+
+
+@pytest.mark.parametrize("g_min,mix", [(-8.0, False), (-12.0, True), (-20.0, True)])
+def test_flagged_chunk_forms(g_min, mix):
+    """Lower bounds past 16 x -5: at -8 every flagged chunk's halves stay within -80, so every step takes
+    the midpoint-referenced tiles; at -12 a fifth of the chunks have a half past -80, so steps with
+    per-pair chunks mix with midpoint steps; at -20 nearly every step takes the per-pair blocks.  Flags
+    follow the oracle's spans and the result the oracle."""
+    wl = gen.WORKLOADS["bf16_4k"].with_(B=1, H=2, T=1000, g_min=g_min, s0_sd=0.2)
+    w = gen.make_numpy(wl, 7)["w"]
+    spans = orc.chunk_spans(w, g_min, 16)
+    hs = half_spans(w, g_min)
+    flagged = spans[:, :, :hs.shape[2]] < -80.0
+    per_pair = flagged & (hs < -80.0)
+    say(f"   flagged {int(flagged.sum())} of {flagged.size}, halves past -80 {int(per_pair.sum())}")
+    assert flagged.mean() > 0.9
+    assert per_pair.any() == mix
+    eo, es, st, *_ = compare(wl, seed=7, path="fused")
+    ties = np.abs(spans + 80.0) <= 1e-3
+    say(f"   err_o={eo:.3e} err_S={es:.3e} stats={st}")
+    assert abs(st["n_flagged"] - int((spans < -80.0).sum())) <= int(ties.sum())
     assert eo <= TOL["bf16"][0] and es <= TOL["bf16"][1]
     assert st["n_nonfinite"] == 0
 
