@@ -101,3 +101,26 @@ def test_unbounded_f32():
     say(f"   err_o={eo:.3e} err_S={es:.3e} stats={st}")
     assert st["n_flagged"] > 0
     assert eo <= TOL["f32"][0] and es <= TOL["f32"][1]
+
+
+@pytest.mark.parametrize("path", ["fused", "vector"])
+def test_gates_at_the_bound(path):
+    """Every gate at g_min = -5 on some channels (w = 30 there, so sigmoid(w) = 1): those channels' 16-token
+    spans are -80 up to the rounding of their sums, the edge the bound promises never to pass.  The
+    fused path then runs its kernel without the flagged-chunk forms; the reciprocal factors reach e^80
+    and everything stays finite and matches the oracle.  Spans within 1e-3 of -80 count as ties."""
+    wl = gen.WORKLOADS["bf16_4k"].with_(B=1, H=2, T=200, s0_sd=0.2)
+
+    def mutate(inp):
+        inp["w"][..., ::7] = 30.0   # every seventh channel at the bound (exact in bf16)
+
+    eo, es, st, *_ = compare(wl, seed=11, path=path, mutate=mutate)
+    inp = gen.make_numpy(wl, 11)
+    mutate(inp)
+    spans = orc.chunk_spans(gen.all_to_f64(inp)["w"], wl.g_min, 16)
+    ties = np.abs(spans + 80.0) <= 1e-3
+    say(f"   err_o={eo:.3e} err_S={es:.3e} stats={st} oracle min span {spans.min():.6f} ties {int(ties.sum())}")
+    assert abs(spans.min() + 80.0) < 1e-9          # the oracle's span sits on the bound
+    assert abs(st["n_flagged"] - int((spans < -80.0).sum())) <= int(ties.sum())
+    assert st["n_nonfinite"] == 0
+    assert eo <= TOL["bf16"][0] and es <= TOL["bf16"][1]
