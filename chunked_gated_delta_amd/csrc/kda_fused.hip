@@ -674,8 +674,9 @@ __device__ __forceinline__ void fused_body(FusedShared& sm, const Params& p, int
   const int we = w - kCWaves;                 // E wavefront index (valid when is_e)
   const int li = lane & 15, lg = lane >> 4;
   // step indices fit 32 bits (T < 2^23), which keeps the scalar index arithmetic short
-  const int s0 = j * (int)sg.L;
-  const int ns = ((int)n_steps - s0 < (int)sg.L) ? (int)n_steps - s0 : (int)sg.L;
+  const int s0 = j == 0 ? 0 : (int)sg.L0 + (j - 1) * (int)sg.L;
+  const int len = j == 0 ? (int)sg.L0 : (int)sg.L;
+  const int ns = ((int)n_steps - s0 < len) ? (int)n_steps - s0 : len;
   const int64_t T = p.T;
   const int col = 16 * (w & 7) + li;
   const floatx4 zero = {0, 0, 0, 0};

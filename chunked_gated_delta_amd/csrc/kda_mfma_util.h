@@ -93,7 +93,8 @@ __device__ __forceinline__ void load_slice(floatx4 (&S)[8], const float* src, in
 // Segment plan shared by the scan kernels: P segments of L steps (32 tokens) per (b, h); workspace
 // byte offsets of the per-segment X, M and S_start blocks (128 x 128 fp32 each).
 struct SegPlan {
-  int64_t P, L;
+  int64_t P, L;   // segments per (b, h); steps per segment, segment 0 aside
+  int64_t L0;     // steps of segment 0 (segment j >= 1 starts at L0 + (j - 1) L; the last one takes the rest)
   int64_t off_x, off_m, off_s;
 };
 constexpr int kSegState = 128 * 128 * 4;    // bytes of one block (64 KiB)
