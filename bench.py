@@ -472,7 +472,7 @@ def main():
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=40)
     ap.add_argument("--workload", default="headline")
-    ap.add_argument("--path", default="auto", choices=["auto", "vector", "mfma", "fused"])
+    ap.add_argument("--path", default="auto", choices=["auto", "vector", "mfma", "fused", "corr"])
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-accuracy", action="store_true",

@@ -11,7 +11,7 @@ import torch
 from . import _lib
 from ._lib import KdaError, KdaOpts, KdaShape
 
-_PATHS = {"auto": 0, "vector": 1, "mfma": 2, "fused": 3}
+_PATHS = {"auto": 0, "vector": 1, "mfma": 2, "fused": 3, "corr": 4}
 
 
 def _dtype_code(t: torch.Tensor) -> int:

@@ -36,6 +36,16 @@
 // The map pass (kernel argument OUT = false) runs segment 0 as an output segment, from S0, beside
 // the maps of segments 1 .. P-2; after the chaining, the output pass (OUT = true) runs segments
 // 1 .. P-1.  Both passes hold P - 1 workgroups per head.
+//
+// The corrected plan has one pass over the sequence instead of two.  The outputs of a segment are
+// affine in its entering state: with S_t = X_t + M_t S_start the state entering step t,
+//   O_t = [Qbar X_t + P T diag(beta)(V - Kbar X_t)] + [Qbar M_t - P T diag(beta) Kbar M_t] S_start
+//       = O_t(from zero) + Qtil_t S_start.
+// Its pass runs segment 0 exactly, from S0, beside segments 1 .. P-1, each of which writes its
+// outputs from a zero entering state (the C wavefronts run the output body from S = 0) and carries
+// M_t on its E wavefronts, which otherwise wait through most of the first half: they write Qtil_t
+// (32 x 128, bf16) and, at the end, M, next to the C wavefronts' X.  After the chaining of the maps,
+// a memory-bound pass adds Qtil_t S_start to the outputs of segments 1 .. P-1.
 #include "kda_mfma_util.h"
 
 namespace kda {
@@ -617,11 +627,63 @@ __device__ __forceinline__ int rows_left(int T, int step) {
   return rem < STEP ? rem : STEP;
 }
 
+// One step of a corrected segment's transition, column slice 16 w' .. 16 w' + 15 of M (the E wavefront
+// w' = w - 8 carries it), from the step's record: R_M = -diag(beta) Kbar M, U_M = T R_M, then
+// Qtil = Qbar M + P U_M (the outputs' coefficient of the entering state, to this slice's 16 columns)
+// and M <- diag(e^{Gam}) M + Ktil^T U_M.  Same products, operand places and broadcasts as the state
+// step of the C wavefronts, with M for S and no V.  Lane (li, lg) writes Qtil[16 mt + li][16 w' + 4 lg + r],
+// mt = 0, 1, as 16 bytes to qo.
+__device__ __forceinline__ void transition_step(const unsigned char* rec, floatx4 (&M)[8], unsigned char* qo,
+                                                int lane) {
+  const floatx4 zero = {0, 0, 0, 0};
+  const int ln = opaque(lane);
+  const int sl = slot16(ln), lg = ln >> 4, li = ln & 15;
+  bf16x8 mb[4];
+#pragma unroll
+  for (int u = 0; u < 4; ++u) mb[u] = pack2(M[2 * u], M[2 * u + 1]);
+  floatx4 RM[2] = {zero, zero};
+#pragma unroll
+  for (int u = 0; u < 4; ++u)
+#pragma unroll
+    for (int mt = 0; mt < 2; ++mt) RM[mt] = mfma(ld8(rec + rKb + (mt * 4 + u) * kBlk + sl), mb[u], RM[mt]);
+  const int l8 = ln * 8;
+  const floatx4 UM0 = mfma16(ld4(rec + rT + kOpT00 + l8), pack4(RM[0]), zero);
+  const floatx4 RM1 = mfma16(ld4(rec + rT + kOpA10 + l8), pack4(UM0), RM[1]);
+  const floatx4 UM1 = mfma16(ld4(rec + rT + kOpT11 + l8), pack4(RM1), zero);
+  const bf16x8 um = pack2(UM0, UM1);
+  floatx4 Qt[2] = {zero, zero};
+#pragma unroll
+  for (int u = 0; u < 4; ++u)
+#pragma unroll
+    for (int mt = 0; mt < 2; ++mt) Qt[mt] = mfma(mb[u], ld8(rec + rQb + (mt * 4 + u) * kBlk + sl), Qt[mt]);
+#pragma unroll
+  for (int mt = 0; mt < 2; ++mt) Qt[mt] = mfma(um, ld8(rec + rP + mt * kBlk + sl), Qt[mt]);
+  *reinterpret_cast<uint4*>(qo) = uint4{pk_bf16(Qt[0][0], Qt[0][1]), pk_bf16(Qt[0][2], Qt[0][3]),
+                                        pk_bf16(Qt[1][0], Qt[1][1]), pk_bf16(Qt[1][2], Qt[1][3])};
+  const float2 egl = *reinterpret_cast<const float2*>(rec + rEg + (lg * 32 + 2 * li) * 4);
+#pragma unroll
+  for (int t = 0; t < 8; ++t) {
+#pragma unroll
+    for (int r = 0; r < 4; ++r) M[t][r] *= row_bcast((r & 1) ? egl.y : egl.x, 2 * t + (r >> 1));
+    M[t] = mfma(ld8(rec + rKt + t * kBlk + sl), um, M[t]);
+  }
+}
+
 // E wavefronts of chunk CC.  Interval s: first half E1(s+2), second half E2(s+2) and, for a flagged
-// chunk, the per-pair blocks of step s+2.
-template <bool OUT, int GK, int CC>
+// chunk, the per-pair blocks of step s+2.  COR (a corrected segment): the first half also advances the
+// wavefront's slice of the transition M over step s (its record is complete and stays in place until
+// the next barrier), while the C wavefronts advance the state over the same step; qdst: the
+// segment's first step of propagated queries.
+template <bool OUT, int GK, int CC, bool COR>
 __device__ __forceinline__ void e_loop(FusedShared& sm, const Params& p, const Views& vw, int s0, int ns, int we,
-                                       int lane, int tid) {
+                                       int lane, int tid, floatx4 (&M)[8], unsigned char* qdst) {
+  if (COR) {
+    const int li = lane & 15, lg = lane >> 4;
+#pragma unroll
+    for (int t = 0; t < 8; ++t)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) M[t][r] = (16 * t + 4 * lg + r == 16 * we + li) ? 1.f : 0.f;
+  }
   const int e_voff = ((16 * CC + 4 * (lane & 3)) * D + 2 * (16 * (we & 3) + (lane >> 2))) * 2;
   const int e_boff = (16 * CC + 4 * (lane & 3)) * 2;
   EIn ein;
@@ -641,6 +703,9 @@ __device__ __forceinline__ void e_loop(FusedShared& sm, const Params& p, const V
     // prefetches are issued on every path (clamped to the segment's last step) so that the memory
     // counter waits before their uses stay exact
     e_load<OUT>(ein, vw, s0 + (it + 3 < ns ? it + 3 : ns - 1), e_voff, e_boff);
+    if (COR && it >= 0)   // step it's record: the slot after step it + 2's
+      transition_step(sm.rec[slotE == kRecSlots - 1 ? 0 : slotE + 1], M, qdst + it * (int64_t)kQtStep + we * 1024 + lane * 16,
+                      lane);
     block_barrier();
     if (doE) {
       const Modes md = GK != kGatePlain ? step_modes(sm, p, s0 + it + 2) : Modes{0u, 0u};
@@ -659,13 +724,46 @@ __device__ __forceinline__ void e_loop(FusedShared& sm, const Params& p, const V
 // Wavefronts 0-7 (C) own the state slices (slice w: 16 columns) and run the tiles and the solve;
 // wavefronts 8-15 (E) run the E stage.  Both kinds meet at the same two barriers per interval.
 //
+// How segment 0 ends when other segments follow it in the same pass (OUT only): its leaving state is
+// the entering state of segment 1, where the chaining pass starts, and its statistics go either to a
+// per-head record that the chaining pass folds into the call's counters (the map pass, which runs
+// before the counters are reset) or straight into the counters (the corrected plan's pass).
+constexpr int kAlone = 0, kEarlyRecord = 1, kEarlyAtomic = 2;
+
+// Map of segment j, column slice w: X_j in slice-major D layout; M_j split into bf16 hi + lo parts,
+// each arranged as the chaining kernel's A operands:
+// [mo 8][u 4][lane 64][8] <-> M[16 mo + (lane & 15)][32 u + {0,16} + 4 (lane >> 4) + r]
+__device__ __forceinline__ void store_x(const Params& p, const SegPlan& sg, int64_t bh, int j, int w, int lane,
+                                        const floatx4 (&X)[8]) {
+  float* xo = (float*)((unsigned char*)p.workspace + sg.off_x + (bh * sg.P + j) * (int64_t)kSegState) + w * 8 * 64 * 4;
+  store_slice(xo, X, lane);
+}
+__device__ __forceinline__ void store_m(const Params& p, const SegPlan& sg, int64_t bh, int j, int w, int lane,
+                                        const floatx4 (&M)[8]) {
+  const int li = lane & 15, lg = lane >> 4;
+  const int64_t blk = bh * sg.P + j;
+  __bf16* mh = (__bf16*)((unsigned char*)p.workspace + sg.off_m + blk * (int64_t)kSegState);
+  __bf16* ml = mh + kMHalf / 2;
+  const int u = w >> 1, pos = (w & 1) * 4 + (li & 3);
+#pragma unroll
+  for (int t = 0; t < 8; ++t)
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int lane_c = (4 * lg + r) + 16 * (li >> 2);   // element M[16t + 4lg + r][16 w + li]
+      const int e = ((t * 4 + u) * 64 + lane_c) * 8 + pos;
+      const __bf16 hi = (__bf16)M[t][r];
+      mh[e] = hi;
+      ml[e] = (__bf16)(M[t][r] - (float)hi);
+    }
+}
+
 // One workgroup's segment.  OUT: segment j from its entering state, with the outputs; !OUT: the map of
-// segment j.  `early` (OUT only): segment 0 running inside the map pass; its leaving state is then the
-// entering state of segment 1, where the chaining pass starts, and its statistics go to a per-head
-// record that the chaining pass folds into the call's counters.
-template <bool OUT, int GK>
+// segment j.  COR (with OUT): segment j >= 1 of the corrected plan, with its outputs from a zero
+// entering state, its propagated queries Qtil and its map.  `early`: kAlone, or how segment 0 ends.
+template <bool OUT, int GK, bool COR = false>
 __device__ __forceinline__ void fused_body(FusedShared& sm, const Params& p, int64_t n_steps, const SegPlan& sg,
-                                           int64_t bh, int j, bool early) {
+                                           int64_t bh, int j, int early) {
+  static_assert(OUT || !COR, "the corrected segments write outputs");
   const int tid = threadIdx.x;
   // the wavefront index through a scalar register: branches on it (and on the chunk and role derived
   // from it) are then uniform, rather than masked paths that every wavefront would step through
@@ -694,14 +792,18 @@ __device__ __forceinline__ void fused_body(FusedShared& sm, const Params& p, int
   // The two kinds of wavefront run separate copies of the step loop (same trip count, same barriers in
   // the same order), so that each copy holds only its own kind's values in registers.
   if (is_e) {
-    if (we < 4) e_loop<OUT, GK, 0>(sm, p, vw, s0, ns, we, lane, tid);
-    else e_loop<OUT, GK, 1>(sm, p, vw, s0, ns, we, lane, tid);
+    floatx4 M[8];
+    unsigned char* qdst = COR ? (unsigned char*)p.workspace + sg.off_q + (bh * n_steps + s0) * (int64_t)kQtStep : nullptr;
+    if (we < 4) e_loop<OUT, GK, 0, COR>(sm, p, vw, s0, ns, we, lane, tid, M, qdst);
+    else e_loop<OUT, GK, 1, COR>(sm, p, vw, s0, ns, we, lane, tid, M, qdst);
+    if (COR) store_m(p, sg, bh, j, we, lane, M);
     return;
   }
 
-  // C wavefronts: OUT -> S (the slice of the true state); !OUT -> X (from zero) and M (from the identity)
+  // C wavefronts: OUT -> S (the slice of the true state; COR: from zero); !OUT -> X (from zero) and M
+  // (from the identity)
   floatx4 S[8], M[8];
-  if (OUT) {
+  if (OUT && !COR) {
     if (j > 0) {
       load_slice(S, (const float*)((const unsigned char*)p.workspace + sg.off_s) + (bh * sg.P + j) * (int64_t)(kSegState / 4) +
                         w * 8 * 64 * 4, lane);
@@ -780,7 +882,7 @@ __device__ __forceinline__ void fused_body(FusedShared& sm, const Params& p, int
         for (int mt = 0; mt < 2; ++mt) {
           *reinterpret_cast<uint2*>(&sm.ostage[16 * mt + li][(16 * w + 4 * lg) * 2]) =
               uint2{pk_bf16(O[mt][0], O[mt][1]), pk_bf16(O[mt][2], O[mt][3])};
-          if (nrows == STEP || 16 * mt + li < nrows) {
+          if (!COR && (nrows == STEP || 16 * mt + li < nrows)) {   // corrected outputs are counted when final
 #pragma unroll
             for (int r = 0; r < 4; ++r) mx = max(mx, abs_bits(O[mt][r]));
           }
@@ -879,8 +981,10 @@ __device__ __forceinline__ void fused_body(FusedShared& sm, const Params& p, int
   }
 
   if (OUT) {
-    if (early) {
-      // segment 0 ran inside the map pass: its leaving state enters segment 1, in the layout of the
+    if (COR) {
+      store_x(p, sg, bh, j, w, lane, S);
+    } else if (early != kAlone) {
+      // segment 0 ran beside other segments: its leaving state enters segment 1, in the layout of the
       // chaining pass's states
       float* so = (float*)((unsigned char*)p.workspace + sg.off_s + (bh * sg.P + 1) * (int64_t)kSegState) + w * 8 * 64 * 4;
       store_slice(so, S, lane);
@@ -896,7 +1000,7 @@ __device__ __forceinline__ void fused_body(FusedShared& sm, const Params& p, int
     if (p.stats) {
 #pragma unroll
       for (int off = 32; off > 0; off >>= 1) nonfinite += __shfl_xor(nonfinite, off);
-      if (early) {
+      if (early == kEarlyRecord) {
         // plain stores into the head's record (the unused entering-state block of segment 0): the
         // counters are reset only after this pass, by the chaining pass, which adds these in
         uint32_t* rec = (uint32_t*)((unsigned char*)p.workspace + sg.off_s + bh * sg.P * (int64_t)kSegState);
@@ -916,25 +1020,10 @@ __device__ __forceinline__ void fused_body(FusedShared& sm, const Params& p, int
           if (n_valid) atomic_min_float(&p.stats->min_span, min_span);
         }
       }
-    }  } else {
-    // X_j in slice-major D layout; M_j split into bf16 hi + lo parts, each arranged as the chaining
-    // kernel's A operands: [mo 8][u 4][lane 64][8] <-> M[16 mo + (lane & 15)][32 u + {0,16} + 4 (lane >> 4) + r]
-    const int64_t blk = bh * sg.P + j;
-    float* xo = (float*)((unsigned char*)p.workspace + sg.off_x + blk * (int64_t)kSegState) + w * 8 * 64 * 4;
-    store_slice(xo, S, lane);
-    __bf16* mh = (__bf16*)((unsigned char*)p.workspace + sg.off_m + blk * (int64_t)kSegState);
-    __bf16* ml = mh + kMHalf / 2;
-    const int u = w >> 1, pos = (w & 1) * 4 + (li & 3);
-#pragma unroll
-    for (int t = 0; t < 8; ++t)
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int lane_c = (4 * lg + r) + 16 * (li >> 2);   // element M[16t + 4lg + r][16 w + li]
-        const int e = ((t * 4 + u) * 64 + lane_c) * 8 + pos;
-        const __bf16 hi = (__bf16)M[t][r];
-        mh[e] = hi;
-        ml[e] = (__bf16)(M[t][r] - (float)hi);
-      }
+    }
+  } else {
+    store_x(p, sg, bh, j, w, lane, S);
+    store_m(p, sg, bh, j, w, lane, M);
   }
 }
 
@@ -949,12 +1038,39 @@ __global__ __launch_bounds__(kThreads) void fused_kernel(Params p, int64_t n_ste
   const int64_t bh = blockIdx.x / nb;
   const int i = (int)(blockIdx.x % nb);
   if (OUT) {
-    fused_body<true, GK>(sm, p, n_steps, sg, bh, sg.P > 1 ? i + 1 : 0, false);
+    fused_body<true, GK>(sm, p, n_steps, sg, bh, sg.P > 1 ? i + 1 : 0, kAlone);
   } else if (i == 0) {
-    fused_body<true, GK>(sm, p, n_steps, sg, bh, 0, true);
+    fused_body<true, GK>(sm, p, n_steps, sg, bh, 0, kEarlyRecord);
   } else {
-    fused_body<false, GK>(sm, p, n_steps, sg, bh, i, false);
+    fused_body<false, GK>(sm, p, n_steps, sg, bh, i, kAlone);
   }
+}
+
+// The corrected plan's pass: P workgroups per head, segment 0 exact from S0 (all of the sequence when
+// P = 1), segments 1 .. P-1 from a zero entering state with their propagated queries and maps.
+template <int GK>
+__global__ __launch_bounds__(kThreads) void fused_corr_kernel(Params p, int64_t n_steps, SegPlan sg) {
+  extern __shared__ __align__(16) unsigned char smem_raw[];
+  FusedShared& sm = *reinterpret_cast<FusedShared*>(smem_raw);
+  const int64_t bh = blockIdx.x / sg.P;
+  const int i = (int)(blockIdx.x % sg.P);
+  if (i == 0) fused_body<true, GK>(sm, p, n_steps, sg, bh, 0, sg.P > 1 ? kEarlyAtomic : kAlone);
+  else fused_body<true, GK, true>(sm, p, n_steps, sg, bh, i, kAlone);
+}
+
+template <int GK>
+hipError_t launch_corr(const Params& p, hipStream_t s, int64_t n_steps, const SegPlan& sg) {
+  static bool attr_set = false;
+  if (!attr_set) {
+    hipError_t e = hipFuncSetAttribute((const void*)fused_corr_kernel<GK>, hipFuncAttributeMaxDynamicSharedMemorySize,
+                                       (int)kFusedSmem);
+    if (e != hipSuccess) return e;
+    attr_set = true;
+  }
+  if (sg.P > 1 && sg.off_q == 0) return hipErrorInvalidValue;   // a plan without room for the queries
+  hipLaunchKernelGGL((fused_corr_kernel<GK>), dim3((unsigned)(p.B * p.H * sg.P)), dim3(kThreads), kFusedSmem, s, p,
+                     n_steps, sg);
+  return hipGetLastError();
 }
 
 template <bool OUT, int GK>
@@ -985,11 +1101,26 @@ bool fused_supported(int dtype, int64_t dk, int64_t dv, int64_t T) {
 // the fp32 limit e^{88.7}), so no chunk can need more than the plain tiles and the kernel is built
 // without the flagged-chunk forms; flags are still counted.  A deeper bound, a forced fallback or the
 // unbounded gate take the kernel with them.
+static int gate_kind(const Params& p) {
+  if (p.unbounded) return kGateUnbounded;
+  const bool plain = !p.force_fallback && (p.disable_fallback || 16.f * p.g_min >= kSpanLimit);
+  return plain ? kGatePlain : kGateFlagged;
+}
+
 hipError_t launch_fused_segments(const Params& p, hipStream_t s, int64_t n_steps, const SegPlan& sg, bool out) {
-  const bool plain = !p.unbounded && !p.force_fallback && (p.disable_fallback || 16.f * p.g_min >= kSpanLimit);
-  if (p.unbounded) return out ? launch_one<true, kGateUnbounded>(p, s, n_steps, sg) : launch_one<false, kGateUnbounded>(p, s, n_steps, sg);
-  if (plain) return out ? launch_one<true, kGatePlain>(p, s, n_steps, sg) : launch_one<false, kGatePlain>(p, s, n_steps, sg);
-  return out ? launch_one<true, kGateFlagged>(p, s, n_steps, sg) : launch_one<false, kGateFlagged>(p, s, n_steps, sg);
+  switch (gate_kind(p)) {
+    case kGateUnbounded: return out ? launch_one<true, kGateUnbounded>(p, s, n_steps, sg) : launch_one<false, kGateUnbounded>(p, s, n_steps, sg);
+    case kGatePlain: return out ? launch_one<true, kGatePlain>(p, s, n_steps, sg) : launch_one<false, kGatePlain>(p, s, n_steps, sg);
+    default: return out ? launch_one<true, kGateFlagged>(p, s, n_steps, sg) : launch_one<false, kGateFlagged>(p, s, n_steps, sg);
+  }
+}
+
+hipError_t launch_fused_corr(const Params& p, hipStream_t s, int64_t n_steps, const SegPlan& sg) {
+  switch (gate_kind(p)) {
+    case kGateUnbounded: return launch_corr<kGateUnbounded>(p, s, n_steps, sg);
+    case kGatePlain: return launch_corr<kGatePlain>(p, s, n_steps, sg);
+    default: return launch_corr<kGateFlagged>(p, s, n_steps, sg);
+  }
 }
 
 }  // namespace kda

@@ -51,20 +51,26 @@ int check_gmin(float g_min) {
 
 bool chunk_ok(int chunk) { return chunk == 16 || chunk == 32 || chunk == 64; }
 
-// path actually taken for a valid shape: 1 vector, 2 records, 3 fused; -1 for an unsupported request
+// path actually taken for a valid shape: 1 vector, 2 records, 3 fused, 4 corrected; -1 for an
+// unsupported request.  The fused and corrected paths fall back to the records path for shapes they
+// do not take (sequences of 2^23 tokens or more).
 int pick_path(const kda_shape_t* sh, int chunk, const kda_opts_t* opts) {
   const int req = opts ? opts->path : 0;
   const bool mfma = sh->dtype == KDA_DTYPE_BF16 && sh->dk == 128 && sh->dv == 128 && chunk == kda::kChunk;
+  const bool fused = mfma && kda::fused_supported(sh->dtype, sh->dk, sh->dv, sh->T);
   if (req == 1) return 1;
   if (req == 2) return mfma ? 2 : -1;
-  if (req == 3 && !mfma) return -1;
+  if (req == 3 || req == 4) return !mfma ? -1 : fused ? req : 2;
   if (!mfma) return 1;
-  return kda::fused_supported(sh->dtype, sh->dk, sh->dv, sh->T) ? 3 : 2;
+  return fused ? 3 : 2;
 }
+
+// the matrix-core paths' ids are their modes (kModeRecords, kModeFused, kModeCorr)
+static_assert(kda::kModeRecords == 2 && kda::kModeFused == 3 && kda::kModeCorr == 4, "path ids are the modes");
 
 size_t workspace_for(const kda_shape_t* sh, int path, int64_t seg_steps) {
   if (path < 2) return 0;
-  return kda::mfma_workspace_bytes(sh->B, sh->H, sh->T, sh->dk, sh->dv, path == 2, seg_steps);
+  return kda::mfma_workspace_bytes(sh->B, sh->H, sh->T, sh->dk, sh->dv, path, seg_steps);
 }
 
 }  // namespace
@@ -108,7 +114,7 @@ size_t kda_workspace_bytes(const kda_shape_t* shape, int chunk) {
 
 size_t kda_workspace_bytes_ex(const kda_shape_t* shape, int chunk, const kda_opts_t* opts) {
   if (check_shape(shape) != KDA_OK || !chunk_ok(chunk)) return (size_t)-1;
-  if (opts && (opts->path < 0 || opts->path > 3)) return (size_t)-1;
+  if (opts && (opts->path < 0 || opts->path > 4)) return (size_t)-1;
   const int path = pick_path(shape, chunk, opts);
   if (path < 0) return (size_t)-1;
   const int64_t seg_steps = opts ? opts->seg_steps : 0;
@@ -128,7 +134,7 @@ int kda_chunk_fwd_ex(const void* q, const void* k, const void* v, const void* w,
     if (opts->seg_steps < 0) return KDA_ERR_ARG;
     if (opts->disable_fallback && opts->force_fallback) return KDA_ERR_ARG;
     if (opts->force_fallback < 0 || opts->force_fallback > 2) return KDA_ERR_ARG;
-    if (opts->path < 0 || opts->path > 3) return KDA_ERR_UNSUPPORTED;
+    if (opts->path < 0 || opts->path > 4) return KDA_ERR_UNSUPPORTED;
   }
   const int64_t B = shape->B, H = shape->H, T = shape->T, dk = shape->dk, dv = shape->dv;
   const int64_t esz = shape->dtype == KDA_DTYPE_BF16 ? 2 : 4;
@@ -195,7 +201,7 @@ int kda_chunk_fwd_ex(const void* q, const void* k, const void* v, const void* w,
     return KDA_OK;
   }
   if (path >= 2) {
-    if ((e = kda::launch_mfma(p, s, ev0, ev1, path == 3)) != hipSuccess) return hip_fail(e);
+    if ((e = kda::launch_mfma(p, s, ev0, ev1, path)) != hipSuccess) return hip_fail(e);
   } else {
     if (ev0 && (e = hipEventRecord(ev0, s)) != hipSuccess) return hip_fail(e);
     if ((e = kda::launch_vec(p, s)) != hipSuccess) return hip_fail(e);

@@ -649,7 +649,11 @@ struct CombineOps {
   floatx4 x[2];
 };
 
-__global__ __launch_bounds__(256) void seg_combine_kernel(Params p, SegPlan sg, int first) {
+// Chains the maps of one (b, h): S_start(j + 1) = M_j S_start(j) + X_j, fp32 via bf16 hi/lo products.
+// first = 0 (records path): from S0 over maps 0 .. P-2.  first = 1: from S_start(1), which segment 0
+// wrote, over maps 1 .. P-2 (fused plan), or over maps 1 .. P-1 (corr = 1, the corrected plan, whose
+// last map gives S_final, written in the user's layout with its non-finite values counted).
+__global__ __launch_bounds__(256) void seg_combine_kernel(Params p, SegPlan sg, int first, int corr) {
   __shared__ floatx4 Sx[2][8][64];
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
@@ -660,9 +664,9 @@ __global__ __launch_bounds__(256) void seg_combine_kernel(Params p, SegPlan sg, 
   const int64_t lb = (int64_t)(blockIdx.x & 7) * (gridDim.x >> 3) + (blockIdx.x >> 3);
   const int64_t bh = lb >> 3;
   const int slice = (int)(lb & 7);
-  const int64_t nseg = sg.P - 1;   // maps first .. P-2 are chained
+  const int64_t nseg = corr ? sg.P : sg.P - 1;   // maps first .. nseg-1 are chained
   const unsigned char* ws = (const unsigned char*)p.workspace;
-  if (first && p.stats && blockIdx.x == 0) {   // uniform over workgroup 0: one head per thread, then a reduction
+  if (first && !corr && p.stats && blockIdx.x == 0) {   // uniform over workgroup 0: one head per thread, then a reduction
     const int64_t BH = p.B * p.H;
     uint32_t n_chunks = 0, n_flagged = 0, n_nonfinite = 0;
     float min_span = __int_as_float(0x7f800000);
@@ -745,8 +749,6 @@ __global__ __launch_bounds__(256) void seg_combine_kernel(Params p, SegPlan sg, 
     bf16x8 sh[4], sl[4];
 #pragma unroll
     for (int u = 0; u < 4; ++u) split_bf16(sx[2 * u][lane], sx[2 * u + 1][lane], sh[u], sl[u]);
-    float* sn = (float*)((unsigned char*)p.workspace + sg.off_s + (bh * sg.P + j + 1) * (int64_t)kSegState) +
-                slice * 8 * 64 * 4;
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
       floatx4 acc = c.x[h];
@@ -757,7 +759,27 @@ __global__ __launch_bounds__(256) void seg_combine_kernel(Params p, SegPlan sg, 
         acc = mfma(c.mh[h][u], sh[u], acc);
       }
       cur[h] = acc;
-      *reinterpret_cast<floatx4*>(sn + ((2 * wave + h) * 64 + lane) * 4) = acc;
+    }
+    if (j + 1 < sg.P) {
+      float* sn = (float*)((unsigned char*)p.workspace + sg.off_s + (bh * sg.P + j + 1) * (int64_t)kSegState) +
+                  slice * 8 * 64 * 4;
+#pragma unroll
+      for (int h = 0; h < 2; ++h) *reinterpret_cast<floatx4*>(sn + ((2 * wave + h) * 64 + lane) * 4) = cur[h];
+    } else {   // the corrected plan's last map: the final state
+      uint32_t bad = 0;
+#pragma unroll
+      for (int h = 0; h < 2; ++h)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int row = 16 * (2 * wave + h) + 4 * lg + r;
+          p.S_final[(bh * D + row) * D + 16 * slice + li] = cur[h][r];
+          bad += not_finite(cur[h][r]) ? 1u : 0u;
+        }
+      if (p.stats) {
+#pragma unroll
+        for (int off = 32; off > 0; off >>= 1) bad += __shfl_xor(bad, off);
+        if (lane == 0 && bad) atomicAdd(&p.stats->n_nonfinite, bad);
+      }
     }
   };
   // Every fetch is issued, its segment clamped to the last map (a valid block whose values are then
@@ -773,6 +795,106 @@ __global__ __launch_bounds__(256) void seg_combine_kernel(Params p, SegPlan sg, 
     fetch(c0, ahead(j + 2));
     if (j + 1 < nseg) step(c1, j + 1);
     fetch(c1, ahead(j + 3));
+  }
+}
+
+// ---- correct_kernel: the corrected plan's outputs of segments 1 .. P-1, o_t += Qtil_t S_start(j)
+// (Qtil_t: the propagated queries the segment pass stored, 32 x 128 bf16 per step; S_start(j): the
+// chained entering state, fp32, as bf16 hi + lo parts).  Each workgroup takes kCorSteps consecutive
+// steps of one segment; wavefront w owns output columns 16 w .. 16 w + 15.  Per step the workgroup
+// stages Qtil and the 32 output rows in LDS with 16-byte loads (whole 256-byte rows), each wavefront
+// adds its 32 x 16 block of the product, and the rows go back with 16-byte stores.  The next step's
+// loads are issued before the current step's products, so one step of loads is always in flight.
+constexpr int kCorSteps = 16;
+constexpr int kCorThreads = 512;
+constexpr int kCorRow = 272;   // staged output row: 256 bytes of data, 16 of pad (column reads spread over the banks)
+
+__device__ __forceinline__ int64_t xcd_logical(int64_t b, int64_t G) {
+  // blocks go round-robin over the 8 XCDs: number XCD x's blocks x (G / 8) + min(x, G % 8) onward, so
+  // that consecutive logical ids (steps of one segment, which read the same entering state) share an L2
+  const int64_t x = b & 7, i = b >> 3;
+  return x * (G >> 3) + (x < (G & 7) ? x : (G & 7)) + i;
+}
+
+__global__ __launch_bounds__(kCorThreads) void correct_kernel(Params p, int64_t n_steps, SegPlan sg, int64_t cps) {
+  __shared__ __align__(16) unsigned char qs[8 * 1024];
+  __shared__ __align__(16) unsigned char os[STEP * kCorRow];
+  const int tid = threadIdx.x;
+  const int lane = tid & 63, w = tid >> 6;
+  const int li = lane & 15, lg = lane >> 4;
+  const int64_t lb = xcd_logical(blockIdx.x, gridDim.x);
+  const int64_t seg = lb / cps, c = lb % cps;
+  const int64_t bh = seg / (sg.P - 1);
+  const int64_t j = 1 + seg % (sg.P - 1);
+  const int64_t s0 = sg.L0 + (j - 1) * sg.L;
+  const int64_t len = (n_steps - s0 < sg.L) ? n_steps - s0 : sg.L;
+  const int64_t a = c * kCorSteps;
+  if (a >= len) return;   // uniform over the workgroup: past the end of a short last segment
+  const int64_t cnt = (len - a < kCorSteps) ? len - a : kCorSteps;
+  const int64_t T = p.T;
+
+  // entering state, columns 16 w .. 16 w + 15 as the A operands (hi and lo)
+  bf16x8 sh[4], sl[4];
+  {
+    floatx4 S[8];
+    load_slice(S, (const float*)((const unsigned char*)p.workspace + sg.off_s) +
+                      (bh * sg.P + j) * (int64_t)(kSegState / 4) + w * 8 * 64 * 4, lane);
+#pragma unroll
+    for (int u = 0; u < 4; ++u) split_bf16(S[2 * u], S[2 * u + 1], sh[u], sl[u]);
+  }
+  const unsigned char* qbase = (const unsigned char*)p.workspace + sg.off_q + (bh * n_steps + s0 + a) * (int64_t)kQtStep;
+  uint16_t* obase = (uint16_t*)p.o + bh * T * D;
+  const int orow = tid >> 4, ocol = (tid & 15) * 8;   // this thread's 16 bytes of the staged rows
+  auto rows_of = [&](int64_t st) { const int64_t r = T - st * STEP; return r < STEP ? (int)r : STEP; };
+  uint4 qreg, oreg;
+  auto fetch = [&](int64_t i) {
+    const int64_t st = s0 + a + i;
+    qreg = *reinterpret_cast<const uint4*>(qbase + i * (int64_t)kQtStep + tid * 16);
+    oreg = orow < rows_of(st) ? *reinterpret_cast<const uint4*>(obase + (st * STEP + orow) * D + ocol) : uint4{0, 0, 0, 0};
+  };
+  fetch(0);
+  uint32_t bad = 0;
+#pragma unroll 1
+  for (int64_t i = 0; i < cnt; ++i) {
+    const int64_t st = s0 + a + i;
+    const int nrows = rows_of(st);
+    *reinterpret_cast<uint4*>(qs + tid * 16) = qreg;
+    *reinterpret_cast<uint4*>(os + orow * kCorRow + ocol * 2) = oreg;
+    __syncthreads();
+    if (i + 1 < cnt) fetch(i + 1);
+    // B operand (mt, u), lane (li, g): Qtil[16 mt + li][32 u + {4 g + r, 16 + 4 g + r}] = the mt-th
+    // 8 bytes of blocks [2 u][lane] and [2 u + 1][lane] as the segment pass stored them
+    floatx4 acc[2] = {{0, 0, 0, 0}, {0, 0, 0, 0}};
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const uint4 x = *reinterpret_cast<const uint4*>(qs + ((2 * u) * 64 + lane) * 16);
+      const uint4 y = *reinterpret_cast<const uint4*>(qs + ((2 * u + 1) * 64 + lane) * 16);
+      const bf16x8 b0 = __builtin_bit_cast(bf16x8, uint4{x.x, x.y, y.x, y.y});
+      const bf16x8 b1 = __builtin_bit_cast(bf16x8, uint4{x.z, x.w, y.z, y.w});
+      acc[0] = mfma(sl[u], b0, acc[0]);
+      acc[0] = mfma(sh[u], b0, acc[0]);
+      acc[1] = mfma(sl[u], b1, acc[1]);
+      acc[1] = mfma(sh[u], b1, acc[1]);
+    }
+    // lane (li, lg) holds the correction of row 16 mt + li, columns 16 w + 4 lg + r
+#pragma unroll
+    for (int mt = 0; mt < 2; ++mt) {
+      uint2* cell = reinterpret_cast<uint2*>(os + (16 * mt + li) * kCorRow + (16 * w + 4 * lg) * 2);
+      const uint2 ov = *cell;
+      const float r0 = lo_bf16(ov.x) + acc[mt][0], r1 = hi_bf16(ov.x) + acc[mt][1];
+      const float r2 = lo_bf16(ov.y) + acc[mt][2], r3 = hi_bf16(ov.y) + acc[mt][3];
+      *cell = uint2{pk_bf16(r0, r1), pk_bf16(r2, r3)};
+      if (16 * mt + li < nrows)
+        bad += (not_finite(r0) ? 1u : 0u) + (not_finite(r1) ? 1u : 0u) + (not_finite(r2) ? 1u : 0u) + (not_finite(r3) ? 1u : 0u);
+    }
+    __syncthreads();
+    if (orow < nrows) *reinterpret_cast<uint4*>(obase + (st * STEP + orow) * D + ocol) =
+                          *reinterpret_cast<const uint4*>(os + orow * kCorRow + ocol * 2);
+  }
+  if (p.stats) {
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) bad += __shfl_xor(bad, off);
+    if (lane == 0 && bad) atomicAdd(&p.stats->n_nonfinite, bad);
   }
 }
 
@@ -913,7 +1035,14 @@ int64_t n_steps_of(int64_t T) { return (T + STEP - 1) / STEP; }
 // segments 1 .. P-1 run with outputs), so it takes one segment more, when that leaves at least three;
 // the records path's output pass holds all P.  seg_steps > 0 fixes the segment length.  With
 // `records`, the per-step records precede the segment blocks in the workspace.
-SegPlan make_plan(int64_t BH, int64_t T, int64_t seg_steps, bool records) {
+// Segment 0 runs beside the other segments in the same pass but takes a different body: its own outputs
+// next to their maps (fused plan: a step with outputs takes about 100/93 of a map step, so segment 0 is
+// shorter), or its exact outputs next to their outputs from a zero entering state and their maps
+// (corrected plan: segment 0 does less per step, so it is longer).  Percent of the other segments' length.
+constexpr int64_t kSeg0PctFused = 93, kSeg0PctCorr = 110;
+
+SegPlan make_plan(int64_t BH, int64_t T, int64_t seg_steps, int mode) {
+  const bool records = mode == kModeRecords, corr = mode == kModeCorr;
   const int64_t n = n_steps_of(T);
   SegPlan sg{};
   int64_t P;
@@ -922,7 +1051,7 @@ SegPlan make_plan(int64_t BH, int64_t T, int64_t seg_steps, bool records) {
     P = (n + seg_steps - 1) / seg_steps;
   } else {
     P = 256 / BH;
-    if (!records) P = P >= 2 ? P + 1 : 1;
+    if (mode == kModeFused) P = P >= 2 ? P + 1 : 1;
     const int64_t by_len = n / 8;
     P = P < by_len ? P : by_len;
     P = P < kMaxSeg ? P : kMaxSeg;
@@ -932,12 +1061,12 @@ SegPlan make_plan(int64_t BH, int64_t T, int64_t seg_steps, bool records) {
   }
   sg.L0 = sg.L;
   if (!records && seg_steps == 0 && P >= 2) {
-    // Segment 0 runs with its outputs in the map pass, beside the maps of segments 1 .. P-2, and a
-    // step with outputs takes longer than a map step (about 100:93 on the headline shape), so segment 0
-    // is made shorter than the rest: L0 = 0.93 L, with L0 + (P - 1) L covering the sequence.
-    const int64_t L = (100 * n + 100 * (P - 1) + 92) / (100 * (P - 1) + 93);
-    int64_t L0 = 93 * L / 100;
+    // segment 0 of length r L (r = pct / 100) beside P - 1 segments of length L, covering the sequence
+    const int64_t pct = corr ? kSeg0PctCorr : kSeg0PctFused;
+    const int64_t L = (100 * n + 100 * (P - 1) + pct - 1) / (100 * (P - 1) + pct);
+    int64_t L0 = pct * L / 100;
     if (L0 < 1) L0 = 1;
+    if (L0 > n) L0 = n;
     if (L0 + (P - 1) * L < n) L0 = n - (P - 1) * L;
     sg.L = L;
     sg.L0 = L0;
@@ -950,15 +1079,27 @@ SegPlan make_plan(int64_t BH, int64_t T, int64_t seg_steps, bool records) {
   sg.off_x = recs;
   sg.off_m = recs + blk;
   sg.off_s = recs + 2 * blk;
+  sg.off_q = corr ? recs + 3 * blk : 0;
   return sg;
 }
 
 }  // namespace
 
-size_t mfma_workspace_bytes(int64_t B, int64_t H, int64_t T, int64_t dk, int64_t dv, bool records, int64_t seg_steps) {
+hipError_t launch_correct(const Params& p, hipStream_t s, int64_t n_steps, const SegPlan& sg) {
+  if (sg.P < 2) return hipSuccess;   // one segment: its outputs are exact
+  if (sg.off_q == 0) return hipErrorInvalidValue;
+  const int64_t cps = (sg.L + kCorSteps - 1) / kCorSteps;   // workgroups per segment
+  const int64_t grid = p.B * p.H * (sg.P - 1) * cps;
+  if (grid > 0x7fffffff) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(correct_kernel, dim3((unsigned)grid), dim3(kCorThreads), 0, s, p, n_steps, sg, cps);
+  return hipGetLastError();
+}
+
+size_t mfma_workspace_bytes(int64_t B, int64_t H, int64_t T, int64_t dk, int64_t dv, int mode, int64_t seg_steps) {
   if (dk != D || dv != D || T <= 0) return 0;
-  const SegPlan sg = make_plan(B * H, T, seg_steps, records);
-  if (!records && sg.P == 1) return 0;   // the fused path's one-segment plan keeps nothing between kernels
+  const SegPlan sg = make_plan(B * H, T, seg_steps, mode);
+  if (mode != kModeRecords && sg.P == 1) return 0;   // a one-segment fused plan keeps nothing between kernels
+  if (mode == kModeCorr) return (size_t)(sg.off_q + B * H * n_steps_of(T) * (int64_t)kQtStep);
   return (size_t)(sg.off_s + B * H * sg.P * (int64_t)kSegState);
 }
 
@@ -969,11 +1110,26 @@ bool mfma_seg_steps_ok(int64_t T, int64_t seg_steps) {
   return (n + seg_steps - 1) / seg_steps <= kMaxSeg;
 }
 
-hipError_t launch_mfma(const Params& p, hipStream_t s, hipEvent_t ev_begin, hipEvent_t ev_end, bool fused) {
+hipError_t launch_mfma(const Params& p, hipStream_t s, hipEvent_t ev_begin, hipEvent_t ev_end, int mode) {
   const int64_t n_steps = n_steps_of(p.T);
   const int64_t BH = p.B * p.H;
-  fused = fused && fused_supported(p.dtype, p.dk, p.dv, p.T);
-  const SegPlan sg = make_plan(BH, p.T, p.seg_steps, !fused);
+  if (mode != kModeRecords && !fused_supported(p.dtype, p.dk, p.dv, p.T)) mode = kModeRecords;
+  const bool fused = mode == kModeFused;
+  const SegPlan sg = make_plan(BH, p.T, p.seg_steps, mode);
+  if (mode == kModeCorr) {
+    // statistics reset first: every pass adds its counts with atomics
+    hipError_t e;
+    if (p.stats && (e = launch_stats_init(p.stats, s)) != hipSuccess) return e;
+    if (ev_begin && (e = hipEventRecord(ev_begin, s)) != hipSuccess) return e;
+    if ((e = launch_fused_corr(p, s, n_steps, sg)) != hipSuccess) return e;
+    if (sg.P > 1) {
+      hipLaunchKernelGGL(seg_combine_kernel, dim3((unsigned)(BH * 8)), dim3(256), 0, s, p, sg, 1, 1);
+      if ((e = hipGetLastError()) != hipSuccess) return e;
+      if ((e = launch_correct(p, s, n_steps, sg)) != hipSuccess) return e;
+    }
+    if (ev_end && (e = hipEventRecord(ev_end, s)) != hipSuccess) return e;
+    return hipSuccess;
+  }
   // statistics reset: by the chaining pass of the fused path when there is one, else its own launch
   if (p.stats && !(fused && sg.P > 1)) {
     const hipError_t e = launch_stats_init(p.stats, s);
@@ -984,7 +1140,7 @@ hipError_t launch_mfma(const Params& p, hipStream_t s, hipEvent_t ev_begin, hipE
     if (ev_begin && (e = hipEventRecord(ev_begin, s)) != hipSuccess) return e;
     if (sg.P > 1) {
       if ((e = launch_fused_segments(p, s, n_steps, sg, false)) != hipSuccess) return e;
-      hipLaunchKernelGGL(seg_combine_kernel, dim3((unsigned)(BH * 8)), dim3(256), 0, s, p, sg, 1);
+      hipLaunchKernelGGL(seg_combine_kernel, dim3((unsigned)(BH * 8)), dim3(256), 0, s, p, sg, 1, 0);
       if ((e = hipGetLastError()) != hipSuccess) return e;
     }
     if ((e = launch_fused_segments(p, s, n_steps, sg, true)) != hipSuccess) return e;
@@ -1010,7 +1166,7 @@ hipError_t launch_mfma(const Params& p, hipStream_t s, hipEvent_t ev_begin, hipE
     hipLaunchKernelGGL(seg_state_kernel, dim3((unsigned)(BH * (sg.P - 1))), dim3(kSegThreads), kStSmem, s, p,
                        n_steps, sg);
     if ((e = hipGetLastError()) != hipSuccess) return e;
-    hipLaunchKernelGGL(seg_combine_kernel, dim3((unsigned)(BH * 8)), dim3(256), 0, s, p, sg, 0);
+    hipLaunchKernelGGL(seg_combine_kernel, dim3((unsigned)(BH * 8)), dim3(256), 0, s, p, sg, 0, 0);
     if ((e = hipGetLastError()) != hipSuccess) return e;
   }
   hipLaunchKernelGGL(seg_out_kernel, dim3((unsigned)(BH * sg.P)), dim3(kSegThreads), kOutSmem, s, p, n_steps, sg);

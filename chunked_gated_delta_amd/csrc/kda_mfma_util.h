@@ -96,6 +96,7 @@ struct SegPlan {
   int64_t P, L;   // segments per (b, h); steps per segment, segment 0 aside
   int64_t L0;     // steps of segment 0 (segment j >= 1 starts at L0 + (j - 1) L; the last one takes the rest)
   int64_t off_x, off_m, off_s;
+  int64_t off_q;  // corrected plan: the propagated queries of every step (8 KiB each), 0 otherwise
 };
 constexpr int kSegState = 128 * 128 * 4;    // bytes of one block (64 KiB)
 constexpr int kMHalf = 8 * 4 * 64 * 16;     // bytes of one bf16 part (hi or lo) of a transition M
@@ -108,5 +109,11 @@ constexpr int kRecNonfinite = 0, kRecChunks = 8, kRecFlagged = 9, kRecMinSpan = 
 // the fused segment kernels take this configuration (bf16, dk = dv = 128, 32-bit buffer offsets)
 // the fused segment kernels (one launch: every segment's map when !out, every segment's outputs when out)
 hipError_t launch_fused_segments(const Params& p, hipStream_t s, int64_t n_steps, const SegPlan& sg, bool out);
+// the corrected plan: one pass over every segment (segment 0 exact from S0; segments 1 .. P-1 with outputs
+// from a zero entering state, their maps and their propagated queries), then, after the chaining, the
+// correction of their outputs by the true entering states
+hipError_t launch_fused_corr(const Params& p, hipStream_t s, int64_t n_steps, const SegPlan& sg);
+hipError_t launch_correct(const Params& p, hipStream_t s, int64_t n_steps, const SegPlan& sg);
+constexpr int kQtStep = 8 * 64 * 16;     // bytes of one step's propagated queries (8 wavefronts x 64 lanes x 16 B)
 
 }  // namespace kda

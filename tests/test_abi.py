@@ -93,7 +93,7 @@ def test_chunk_32_64_only_on_the_vector_path():
     """32- and 64-token chunks run on the vector path (no workspace); the matrix-core paths take 16."""
     for chunk in (32, 64):
         assert lib.kda_workspace_bytes(ctypes.byref(shape(T=4096)), chunk) == 0
-        for path in (2, 3):
+        for path in (2, 3, 4):
             assert call(chunk=chunk, opts=KdaOpts(0, 0, path, 0, None, None)) == -3
             assert lib.kda_workspace_bytes_ex(ctypes.byref(shape()), chunk,
                                               ctypes.byref(KdaOpts(0, 0, path, 0, None, None))) == ctypes.c_size_t(-1).value
@@ -141,6 +141,15 @@ def test_workspace_per_path():
     assert ex(shape(T=1 << 23), 0) == ex(shape(T=1 << 23), 2)         # past the fused path's range
     # the records path checks its own, larger size
     assert call(sh, ws_bytes=ex(sh, 3), opts=KdaOpts(0, 0, 2, 0, None, None)) == -4
+    # corrected plan: at most 16 segments of 8 steps (one pass holds every segment), its maps and
+    # entering states, and the propagated queries of every step (8 KiB each)
+    assert ex(shape(B=1, H=2, T=64), 4) == 0                          # one segment: nothing kept
+    assert ex(sh, 4) == 3 * 2 * 16 * blk + 2 * 128 * 8192
+    assert ex(sh, 4, seg=5) == 3 * 2 * 26 * blk + 2 * 128 * 8192
+    assert ex(sh, 4, seg=3) == ctypes.c_size_t(-1).value
+    assert ex(shape(dk=64, dv=64), 4) == ctypes.c_size_t(-1).value
+    assert ex(shape(T=1 << 23), 4) == ex(shape(T=1 << 23), 2)         # past the fused path's range
+    assert call(sh, ws_bytes=ex(sh, 3), opts=KdaOpts(0, 0, 4, 0, None, None)) == -4
 
 
 def test_workspace_too_small():

@@ -18,7 +18,7 @@ if not torch.cuda.is_available():
     pytest.skip("no GPU", allow_module_level=True)
 
 UNB = gen.WORKLOADS["unbounded"]
-PATHS = ["vector", "mfma", "fused"]
+PATHS = ["vector", "mfma", "fused", "corr"]
 
 
 @pytest.mark.parametrize("path", PATHS)
@@ -103,7 +103,7 @@ def test_unbounded_f32():
     assert eo <= TOL["f32"][0] and es <= TOL["f32"][1]
 
 
-@pytest.mark.parametrize("path", ["fused", "vector"])
+@pytest.mark.parametrize("path", ["fused", "corr", "vector"])
 def test_gates_at_the_bound(path):
     """Every gate at g_min = -5 on some channels (w = 30 there, so sigmoid(w) = 1): those channels' 16-token
     spans are -80 up to the rounding of their sums, the edge the bound promises never to pass.  The

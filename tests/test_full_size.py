@@ -40,13 +40,13 @@ def run_full(name, heads, seed=0, path="auto"):
     return wl, stats, inp
 
 
-@pytest.mark.parametrize("path", ["auto", "fused"])
+@pytest.mark.parametrize("path", ["auto", "fused", "corr"])
 def test_bf16_4k_full(path):
     wl, stats, _ = run_full("bf16_4k", [(0, 0), (1, 15), (0, 7)], path=path)
     assert stats["n_nonfinite"] == 0 and stats["n_flagged"] == 0
 
 
-@pytest.mark.parametrize("path", ["auto", "fused"])
+@pytest.mark.parametrize("path", ["auto", "fused", "corr"])
 def test_unbounded_full(path):
     wl, stats, inp = run_full("unbounded", [(0, 3), (1, 12)], path=path)
     assert stats["n_nonfinite"] == 0
@@ -57,13 +57,13 @@ def test_unbounded_full(path):
     assert abs(stats["n_flagged"] - int(pred.sum())) <= int(ties.sum())
 
 
-@pytest.mark.parametrize("path", ["auto", "fused"])
+@pytest.mark.parametrize("path", ["auto", "fused", "corr"])
 def test_headline_full(path):
     _, stats, _ = run_full("headline", [(0, 0), (0, 9)], path=path)
     assert stats["n_nonfinite"] == 0 and stats["n_flagged"] == 0
 
 
-@pytest.mark.parametrize("path", ["auto", "fused"])
+@pytest.mark.parametrize("path", ["auto", "fused", "corr"])
 def test_decay_stress_full(path):
     _, stats, _ = run_full("decay_stress", [(0, 5), (0, 31)], path=path)
     assert stats["n_nonfinite"] == 0 and stats["n_flagged"] == 0

@@ -17,7 +17,7 @@ if not torch.cuda.is_available():
     pytest.skip("no GPU", allow_module_level=True)
 
 BF16 = gen.WORKLOADS["bf16_4k"]
-PATHS = ["vector", "mfma", "fused"]
+PATHS = ["vector", "mfma", "fused", "corr"]
 
 
 def mfma_ok(wl):
@@ -29,7 +29,7 @@ def paths_for(wl):
 
 
 def check(wl, path, seed=0, **kw):
-    if path in ("mfma", "fused") and not mfma_ok(wl):
+    if path in ("mfma", "fused", "corr") and not mfma_ok(wl):
         pytest.skip("matrix-core path covers bf16 with dk = dv = 128")
     eo, es, st, *_ = compare(wl, seed=seed, path=path, **kw)
     tol_o, tol_s = TOL[wl.dtype]
