@@ -10,8 +10,9 @@ The default workload is B=1, H=16, T=65536, dk=dv=128, bf16, g_min=-5,
 chunk 16, S0 = 0 (synthetic inputs, seeded).  `roofline` uses the algorithmic
 bytes of one launch (q, k, v, w, beta read, o written: 1282 B per token-head at
 d = 128 in bf16, plus the fp32 final state) over the average duration of the
-call's kernels (on the fused path: the map pass, the segment chaining and the
-output pass, back to back on one stream), timed with HIP events that
+call's kernels (on the automatic path at this shape, the corrected plan: the
+segment pass, the chaining of the segment maps and the correction pass, back
+to back on one stream), timed with HIP events that
 the library records on the launch stream before the first kernel and after the
 last.
 `cpu_baseline` times the fp64 oracle on the host on a bounded sample of the
@@ -76,6 +77,7 @@ def source_hash(read=None) -> str:
 def kernel_short_name(name):
     """Short name of a library kernel (or of the calibration copy) in a rocprofv3 record."""
     for key, short in (("fused_kernel<true", "fused_out"), ("fused_kernel<false", "fused_state"),
+                       ("fused_corr_kernel", "corr_pass"), ("correct_kernel", "correct"),
                        ("seg_combine_kernel", "seg_combine"), ("seg_state_kernel", "seg_state"),
                        ("seg_out_kernel", "seg_out"), ("prep_kernel", "prep"), ("vec_", "vector")):
         if key in name:

@@ -51,19 +51,7 @@ int check_gmin(float g_min) {
 
 bool chunk_ok(int chunk) { return chunk == 16 || chunk == 32 || chunk == 64; }
 
-// path actually taken for a valid shape: 1 vector, 2 records, 3 fused, 4 corrected; -1 for an
-// unsupported request.  The fused and corrected paths fall back to the records path for shapes they
-// do not take (sequences of 2^23 tokens or more).
-int pick_path(const kda_shape_t* sh, int chunk, const kda_opts_t* opts) {
-  const int req = opts ? opts->path : 0;
-  const bool mfma = sh->dtype == KDA_DTYPE_BF16 && sh->dk == 128 && sh->dv == 128 && chunk == kda::kChunk;
-  const bool fused = mfma && kda::fused_supported(sh->dtype, sh->dk, sh->dv, sh->T);
-  if (req == 1) return 1;
-  if (req == 2) return mfma ? 2 : -1;
-  if (req == 3 || req == 4) return !mfma ? -1 : fused ? req : 2;
-  if (!mfma) return 1;
-  return fused ? 3 : 2;
-}
+int pick_path(const kda_shape_t* sh, int chunk, const kda_opts_t* opts) { return kda::forward_path(sh, chunk, opts); }
 
 // the matrix-core paths' ids are their modes (kModeRecords, kModeFused, kModeCorr)
 static_assert(kda::kModeRecords == 2 && kda::kModeFused == 3 && kda::kModeCorr == 4, "path ids are the modes");
@@ -76,6 +64,21 @@ size_t workspace_for(const kda_shape_t* sh, int path, int64_t seg_steps) {
 }  // namespace
 
 namespace kda {
+
+// path actually taken for a valid shape: 1 vector, 2 records, 3 fused, 4 corrected, 5 automatic
+// matrix-core plan (kModeAuto: corrected or fused by the gate); -1 for an unsupported request.  The
+// fused and corrected plans fall back to the records path for shapes they do not take (sequences of
+// 2^23 tokens or more).
+int forward_path(const kda_shape_t* sh, int chunk, const kda_opts_t* opts) {
+  const int req = opts ? opts->path : 0;
+  const bool mfma = sh->dtype == KDA_DTYPE_BF16 && sh->dk == 128 && sh->dv == 128 && chunk == kChunk;
+  const bool fused = mfma && fused_supported(sh->dtype, sh->dk, sh->dv, sh->T);
+  if (req == 1) return 1;
+  if (req == 2) return mfma ? kModeRecords : -1;
+  if (req == kModeFused || req == kModeCorr) return !mfma ? -1 : fused ? req : kModeRecords;
+  if (!mfma) return 1;
+  return fused ? kModeAuto : kModeRecords;
+}
 
 int record_hip_error(hipError_t e) {
   std::snprintf(g_last_hip_error, sizeof(g_last_hip_error), "%s (%d)", hipGetErrorString(e), (int)e);

@@ -28,12 +28,17 @@ extern "C" {
 int kda_chunk_fwd_noalloc(const void* q, const void* k, const void* v, const void* w, const void* beta,
                           const float* S0, float g_min, int chunk, const kda_shape_t* shape, void* o,
                           float* S_final, kda_stats_t* stats, void* stream) {
-  // the scratch this call needs (the automatic plan's workspace): host arithmetic, no HIP call
-  const size_t need = kda_workspace_bytes(shape, chunk);
-  if (need == (size_t)-1) {
-    // invalid shape or chunk: the full validation below returns the precise code
+  // the plan: the automatic one, except that where it would take the corrected plan (whose propagated
+  // queries need 8 KiB per 32 tokens per head) the fused plan runs instead (64 KiB blocks per segment)
+  if (kda_workspace_bytes(shape, chunk) == (size_t)-1) {
+    // invalid shape or chunk: the full validation of the plain entry point returns the precise code
     return kda_chunk_fwd(q, k, v, w, beta, S0, g_min, chunk, shape, o, S_final, nullptr, 0, stats, stream);
   }
+  kda_opts_t opts{};
+  if (kda::forward_path(shape, chunk, nullptr) == kda::kModeAuto) opts.path = kda::kModeFused;
+  // the scratch this call needs: host arithmetic, no HIP call
+  const size_t need = kda_workspace_bytes_ex(shape, chunk, &opts);
+  if (need == (size_t)-1) return KDA_ERR_ARG;
   if (need > (size_t)KDA_NOALLOC_SCRATCH_BYTES) return KDA_ERR_SCRATCH;
   void* ws = nullptr;
   if (need > 0) {
@@ -57,7 +62,8 @@ int kda_chunk_fwd_noalloc(const void* q, const void* k, const void* v, const voi
   }
   // every segment block of the fused path is written before it is read within the call, so the
   // previous call's contents need no clearing
-  return kda_chunk_fwd(q, k, v, w, beta, S0, g_min, chunk, shape, o, S_final, ws, ws ? need : 0, stats, stream);
+  return kda_chunk_fwd_ex(q, k, v, w, beta, S0, g_min, chunk, shape, o, S_final, ws, ws ? need : 0, stats, stream,
+                          &opts);
 }
 
 }  // extern "C"

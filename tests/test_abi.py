@@ -133,7 +133,7 @@ def test_workspace_per_path():
     # outputs beside the maps, is 0.93x the others, so the plan is 8 steps, then 9-step segments (the
     # last takes the remaining 3): 15 segments
     sh = shape(B=1, H=2, T=4096)
-    assert ex(sh, 0) == ex(sh, 3) == 3 * 2 * 15 * blk
+    assert ex(sh, 3) == 3 * 2 * 15 * blk
     assert ex(sh, 3, seg=5) == 3 * 2 * 26 * blk                      # a forced length of 5 steps: 26 segments
     assert ex(sh, 3, seg=3) == ctypes.c_size_t(-1).value             # 43 segments: more than 32
     assert ex(shape(dk=64, dv=64), 3) == ctypes.c_size_t(-1).value   # no matrix-core path at d = 64
@@ -145,6 +145,8 @@ def test_workspace_per_path():
     # entering states, and the propagated queries of every step (8 KiB each)
     assert ex(shape(B=1, H=2, T=64), 4) == 0                          # one segment: nothing kept
     assert ex(sh, 4) == 3 * 2 * 16 * blk + 2 * 128 * 8192
+    # automatic plan: room for the corrected plan (taken with the bounded gate), which holds the fused one
+    assert ex(sh, 0) == lib.kda_workspace_bytes(ctypes.byref(sh), 16) == ex(sh, 4) > ex(sh, 3)
     assert ex(sh, 4, seg=5) == 3 * 2 * 26 * blk + 2 * 128 * 8192
     assert ex(sh, 4, seg=3) == ctypes.c_size_t(-1).value
     assert ex(shape(dk=64, dv=64), 4) == ctypes.c_size_t(-1).value
@@ -265,5 +267,9 @@ def test_noalloc_rejects_calls_beyond_its_scratch():
     assert na(shape(dk=48)) == -3
     assert na(shape(), g_min=1.0) == -4
     assert na(shape(), S_final=None) == -1
+    # the entry point takes the fused plan where the automatic one is the corrected plan: the headline
+    # shape fits the array with the former (52 MiB), not with the latter (its 8 KiB per step of queries)
     headline = shape(B=1, H=16, T=65536)
-    assert 0 < lib.kda_workspace_bytes(ctypes.byref(headline), 16) <= _lib.NOALLOC_SCRATCH_BYTES
+    fused = lambda sh: lib.kda_workspace_bytes_ex(ctypes.byref(sh), 16, ctypes.byref(KdaOpts(0, 0, 3, 0, None, None)))
+    assert 0 < fused(headline) <= _lib.NOALLOC_SCRATCH_BYTES < lib.kda_workspace_bytes(ctypes.byref(headline), 16)
+    assert fused(big) > _lib.NOALLOC_SCRATCH_BYTES

@@ -72,7 +72,7 @@ def test_gmin_chunk_sweep():
             eo, es = max(e[0] for e in errs), max(e[1] for e in errs)
             assert eo <= TOL["bf16"][0] and es <= TOL["bf16"][1]
             row = {"chunk": chunk, "g_min": g_min, "chunk_times_gmin": chunk * g_min,
-                   "path": "fused (bf16 MFMA)" if fused else "vector (fp32)",
+                   "path": "matrix cores (bf16 MFMA)" if fused else "vector (fp32)",
                    "flagged_fraction": d["n_flagged"] / d["n_chunks"], "oracle_flagged": n_flag, "ties": n_tie,
                    "min_span": d["min_span"], "forward_ms": ms, "tokens_per_s": wl.B * wl.T / (ms * 1e-3),
                    "err_o": eo, "err_S": es}

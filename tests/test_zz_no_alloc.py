@@ -1,6 +1,8 @@
-"""kda_chunk_fwd_noalloc through the C ABI: the scratch-free entry point gives exactly what
-kda_chunk_fwd gives with a caller workspace, on calls in a row that reuse the library's static
-array (the second and later calls smaller than the first), and matches the fp64 oracle."""
+"""kda_chunk_fwd_noalloc through the C ABI: the scratch-free entry point gives exactly what the
+workspace entry point gives for the same plan (the fused plan where the automatic plan is the
+corrected one, whose queries would not fit the array), on calls in a row that reuse the library's
+static array (the second and later calls smaller than the first); it agrees with the automatic
+kda_chunk_fwd and with the fp64 oracle to the parity tolerance."""
 import ctypes
 
 import numpy as np
@@ -32,19 +34,26 @@ def _check_against_workspace_entry(wl, seed, with_oracle):
     from chunked_gated_delta_amd import chunk_fwd, decode_stats, workspace_bytes
     inp = gen.make_numpy(wl, seed)
     t = gen.numpy_to_torch(inp, "cuda")
-    need = workspace_bytes(wl.B, wl.H, wl.T, wl.dk, wl.dv, gen.torch_dtype(wl.dtype))
-    say(f"[case] noalloc {wl} seed={seed} scratch={need} bytes")
+    mfma = wl.dtype == "bf16" and wl.dk == wl.dv == 128
+    plan = "fused" if mfma else "auto"
+    need = workspace_bytes(wl.B, wl.H, wl.T, wl.dk, wl.dv, gen.torch_dtype(wl.dtype), path=plan)
+    say(f"[case] noalloc {wl} seed={seed} plan={plan} scratch={need} bytes")
     o = torch.empty_like(t["v"])
     S = torch.empty((wl.B, wl.H, wl.dk, wl.dv), dtype=torch.float32, device="cuda")
     st = torch.empty(4, dtype=torch.int32, device="cuda")
     rc = _noalloc_call(t, wl, o, S, st)
     assert rc == 0, rc
-    o_ref, S_ref, st_ref = chunk_fwd(t["q"], t["k"], t["v"], t["w"], t["beta"], t["S0"], g_min=wl.g_min)
+    o_ref, S_ref, st_ref = chunk_fwd(t["q"], t["k"], t["v"], t["w"], t["beta"], t["S0"], g_min=wl.g_min, path=plan)
+    o_auto, S_auto, st_auto = chunk_fwd(t["q"], t["k"], t["v"], t["w"], t["beta"], t["S0"], g_min=wl.g_min)
     torch.cuda.synchronize()
     assert torch.equal(o, o_ref) and torch.equal(S, S_ref)
     assert decode_stats(st) == decode_stats(st_ref)
-    eo = rel_err(o.float().cpu().numpy(), o_ref.float().cpu().numpy())
-    es = rel_err(S.cpu().numpy(), S_ref.cpu().numpy())
+    st_a = decode_stats(st_auto)
+    assert {k: st_a[k] for k in ("n_chunks", "n_flagged", "n_nonfinite")} == \
+        {k: decode_stats(st)[k] for k in ("n_chunks", "n_flagged", "n_nonfinite")}
+    eo = rel_err(o.float().cpu().numpy(), o_auto.float().cpu().numpy())
+    es = rel_err(S.cpu().numpy(), S_auto.cpu().numpy())
+    say(f"   against the automatic plan: err_o={eo:.3e} err_S={es:.3e}")
     assert eo <= TOL[wl.dtype][0] and es <= TOL[wl.dtype][1]
     if with_oracle:
         o64, S64 = oracle_run(inp, wl.g_min)
