@@ -43,9 +43,10 @@
 //       = O_t(from zero) + Qtil_t S_start.
 // Its pass runs segment 0 exactly, from S0, beside segments 1 .. P-1, each of which writes its
 // outputs from a zero entering state (the C wavefronts run the output body from S = 0) and carries
-// M_t on its E wavefronts, which otherwise wait through most of the first half: they write Qtil_t
-// (32 x 128, bf16) and, at the end, M, next to the C wavefronts' X.  After the chaining of the maps,
-// a memory-bound pass adds Qtil_t S_start to the outputs of segments 1 .. P-1.
+// the eight 16-column slices of M_t on the wavefronts with idle time in one of the halves (the
+// chunk-0 E wavefronts and state wavefronts 6-7 in the first, state wavefronts 4-5 in the second):
+// they write Qtil_t (32 x 128, bf16) and, at the end, M, next to the C wavefronts' X.  After the
+// chaining of the maps, a memory-bound pass adds Qtil_t S_start to the outputs of segments 1 .. P-1.
 #include "kda_mfma_util.h"
 
 namespace kda {
@@ -757,13 +758,25 @@ __device__ __forceinline__ void store_m(const Params& p, const SegPlan& sg, int6
     }
 }
 
-// One workgroup's segment.  OUT: segment j from its entering state, with the outputs; !OUT: the map of
-// segment j.  COR (with OUT): segment j >= 1 of the corrected plan, with its outputs from a zero
-// entering state, its propagated queries Qtil and its map.  `early`: kAlone, or how segment 0 ends.
-template <bool OUT, int GK, bool COR = false>
-__device__ __forceinline__ void fused_body(FusedShared& sm, const Params& p, int64_t n_steps, const SegPlan& sg,
+// Where a corrected segment carries the eight 16-column slices of its transition M: in the idle time
+// of the wavefronts that have it (per 32-token step, the first half lasts as long as the state chain
+// plus a causal tile, the second as long as the E stage's second half).
+//   slices 0-3   E wavefronts of chunk 0 (8-11), first half, after their share of E1
+//   slices 4-5   state wavefronts 6-7, first half, after the state chain (they form no tile)
+//   slices 6-7   state wavefronts 4-5, second half (they store nothing and solve nothing there)
+// The chunk-1 E wavefronts, the slowest of the first half, carry none.
+constexpr int kMNone = 0, kMFirst = 1, kMSecond = 2;   // a state wavefront's share of M
+
+// One workgroup's segment, for the wavefronts of M role MR (kMNone: every wavefront but state
+// wavefronts 4-7 of a corrected segment).  OUT: segment j from its entering state, with the outputs;
+// !OUT: the map of segment j.  COR (with OUT): segment j >= 1 of the corrected plan, with its outputs
+// from a zero entering state, its propagated queries Qtil and its map.  `early`: kAlone, or how
+// segment 0 ends.
+template <bool OUT, int GK, bool COR, int MR>
+__device__ __forceinline__ void fused_part(FusedShared& sm, const Params& p, int64_t n_steps, const SegPlan& sg,
                                            int64_t bh, int j, int early) {
   static_assert(OUT || !COR, "the corrected segments write outputs");
+  static_assert(COR || MR == kMNone, "only corrected segments carry M on their state wavefronts");
   const int tid = threadIdx.x;
   // the wavefront index through a scalar register: branches on it (and on the chunk and role derived
   // from it) are then uniform, rather than masked paths that every wavefront would step through
@@ -791,14 +804,20 @@ __device__ __forceinline__ void fused_body(FusedShared& sm, const Params& p, int
 
   // The two kinds of wavefront run separate copies of the step loop (same trip count, same barriers in
   // the same order), so that each copy holds only its own kind's values in registers.
-  if (is_e) {
+  unsigned char* qdst = COR ? (unsigned char*)p.workspace + sg.off_q + (bh * n_steps + s0) * (int64_t)kQtStep : nullptr;
+  if (MR == kMNone && is_e) {
     floatx4 M[8];
-    unsigned char* qdst = COR ? (unsigned char*)p.workspace + sg.off_q + (bh * n_steps + s0) * (int64_t)kQtStep : nullptr;
     if (we < 4) e_loop<OUT, GK, 0, COR>(sm, p, vw, s0, ns, we, lane, tid, M, qdst);
-    else e_loop<OUT, GK, 1, COR>(sm, p, vw, s0, ns, we, lane, tid, M, qdst);
-    if (COR) store_m(p, sg, bh, j, we, lane, M);
+    else e_loop<OUT, GK, 1, false>(sm, p, vw, s0, ns, we, lane, tid, M, qdst);
+    if (COR && we < 4) store_m(p, sg, bh, j, we, lane, M);
     return;
   }
+  // which wavefronts run this copy (lets the compiler drop the other wavefronts' tile and store forms)
+  if (MR == kMFirst) __builtin_assume(w == 6 || w == 7);
+  if (MR == kMSecond) __builtin_assume(w == 4 || w == 5);
+  if (COR && MR == kMNone) __builtin_assume(w < 4);
+  // this state wavefront's slice of M (state wavefronts 4-7 of a corrected segment; the map pass: its own)
+  const int mslice = MR == kMFirst ? w - 2 : MR == kMSecond ? w + 2 : (w & 7);
 
   // C wavefronts: OUT -> S (the slice of the true state; COR: from zero); !OUT -> X (from zero) and M
   // (from the identity)
@@ -821,7 +840,7 @@ __device__ __forceinline__ void fused_body(FusedShared& sm, const Params& p, int
     for (int t = 0; t < 8; ++t) {
       S[t] = zero;
 #pragma unroll
-      for (int r = 0; r < 4; ++r) M[t][r] = (16 * t + 4 * lg + r == col) ? 1.f : 0.f;
+      for (int r = 0; r < 4; ++r) M[t][r] = (16 * t + 4 * lg + r == 16 * mslice + li) ? 1.f : 0.f;
     }
   }
   uint4 vq[2];   // wavefronts 0-3: V rows of the next step, 16 bytes per lane
@@ -841,7 +860,8 @@ __device__ __forceinline__ void fused_body(FusedShared& sm, const Params& p, int
     block_barrier();
     const int ln = opaque(lane);
     const int sl = slot16(ln);
-    if (OUT && w < 4) {   // V of step it + 1, issued first so that the whole first half covers its latency
+    const bool low4 = MR == kMNone && w < 4;   // wavefronts 0-3 (the copies with M are wavefronts 4-7)
+    if (OUT && low4) {   // V of step it + 1, issued first so that the whole first half covers its latency
       const int sn = s0 + (it + 1 < 0 ? 0 : (it + 1 < ns ? it + 1 : ns - 1));
 #pragma unroll
       for (int i = 0; i < 2; ++i) vq[i] = v_load16(vw, sn, 8 * w + 4 * i + (lane >> 4), lane & 15);
@@ -938,14 +958,16 @@ __device__ __forceinline__ void fused_body(FusedShared& sm, const Params& p, int
         }
       }
     }
+    if (MR == kMFirst && doC)
+      transition_step(recC, M, qdst + it * (int64_t)kQtStep + mslice * 1024 + lane * 16, lane);
     // ---- the causal tiles of step it + 1 (their chunk flags are in its information record)
-    if (doS) {
+    if (doS && MR != kMFirst) {   // (wavefronts 6-7 form no tile)
       const StepInfo* si = reinterpret_cast<const StepInfo*>(recS + rMeta);
       const uint32_t mid = GK != kGatePlain ? si->midpoint : 0u;
       if (GK != kGatePlain && __builtin_expect(mid != 0u, 0)) tiles<OUT, true>(sm, recS, opsF, sm.ops[(it + 2) & 1], si->pairwise, mid, (int)((it + 1) & 1), w, ln);
       else tiles<OUT, false>(sm, recS, opsF, sm.ops[(it + 2) & 1], si->pairwise, 0u, (int)((it + 1) & 1), w, ln);
     }
-    if (!OUT && w < 4) {   // V of step it + 1 (the map pass has no registers to carry it over the chain)
+    if (!OUT && low4) {   // V of step it + 1 (the map pass has no registers to carry it over the chain)
       const int sn = s0 + (it + 1 < 0 ? 0 : (it + 1 < ns ? it + 1 : ns - 1));
 #pragma unroll
       for (int i = 0; i < 2; ++i) vq[i] = v_load16(vw, sn, 8 * w + 4 * i + (lane >> 4), lane & 15);
@@ -954,7 +976,7 @@ __device__ __forceinline__ void fused_body(FusedShared& sm, const Params& p, int
     // ---- second half: o of step it out of the stage as whole rows (wavefronts 0-3, eight rows each,
     // 16 bytes per lane: 256 contiguous bytes per row), per-pair blocks of step it + 2 (if any), T of
     // step it + 1
-    if (OUT && doC && w < 4) {
+    if (OUT && doC && low4) {
       const int st = s0 + it;
       const int nrows = rows_left((int)T, st);
       uint16_t* ob = (uint16_t*)p.o + bh * T * D + (int64_t)st * STEP * D;
@@ -966,23 +988,26 @@ __device__ __forceinline__ void fused_body(FusedShared& sm, const Params& p, int
         if (row < nrows) *reinterpret_cast<uint4*>(ob + row * D + c16 * 8) = v;
       }
     }
-    if (w < 4 && it + 1 >= 0 && it + 1 < ns) {   // V of step it + 1 over the rows just stored
+    if (low4 && it + 1 >= 0 && it + 1 < ns) {   // V of step it + 1 over the rows just stored
 #pragma unroll
       for (int i = 0; i < 2; ++i)
         *reinterpret_cast<uint4*>(&sm.ostage[8 * w + 4 * i + (lane >> 4)][(lane & 15) * 16]) = vq[i];
     }
     // T of step it + 1 first: it shares nothing with the per-pair blocks, so on a flagged step it
     // overlaps the E stage instead of following the per-pair barriers
-    if (doS && w >= 6) solve_block(sm, recS, (int)((it + 1) & 1), w - 6, ln);
+    if (doS && w >= 6 && MR != kMSecond) solve_block(sm, recS, (int)((it + 1) & 1), w - 6, ln);
     if (GK != kGatePlain && doE) {
       const uint32_t pwmask = step_modes(sm, p, s0 + it + 2).pw;
       if (__builtin_expect(pwmask != 0u, 0)) pairwise_blocks<OUT, false>(sm, nullptr, recE, opsF, pwmask, 0, ln, tid);
     }
+    if (MR == kMSecond && doC)
+      transition_step(recC, M, qdst + it * (int64_t)kQtStep + mslice * 1024 + lane * 16, lane);
   }
 
   if (OUT) {
     if (COR) {
       store_x(p, sg, bh, j, w, lane, S);
+      if (MR != kMNone) store_m(p, sg, bh, j, mslice, lane, M);
     } else if (early != kAlone) {
       // segment 0 ran beside other segments: its leaving state enters segment 1, in the layout of the
       // chaining pass's states
@@ -1025,6 +1050,19 @@ __device__ __forceinline__ void fused_body(FusedShared& sm, const Params& p, int
     store_x(p, sg, bh, j, w, lane, S);
     store_m(p, sg, bh, j, w, lane, M);
   }
+}
+
+// One workgroup's segment: state wavefronts 4-7 of a corrected segment take the copies of the step loop
+// that carry their slice of M, every other wavefront the copy without it.
+template <bool OUT, int GK, bool COR = false>
+__device__ __forceinline__ void fused_body(FusedShared& sm, const Params& p, int64_t n_steps, const SegPlan& sg,
+                                           int64_t bh, int j, int early) {
+  if constexpr (COR) {
+    const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    if (w == 6 || w == 7) return fused_part<OUT, GK, COR, kMFirst>(sm, p, n_steps, sg, bh, j, early);
+    if (w == 4 || w == 5) return fused_part<OUT, GK, COR, kMSecond>(sm, p, n_steps, sg, bh, j, early);
+  }
+  fused_part<OUT, GK, COR, kMNone>(sm, p, n_steps, sg, bh, j, early);
 }
 
 // OUT: the output pass, segments 1 .. P-1 (segment 0 ran in the map pass), or the only segment of a
