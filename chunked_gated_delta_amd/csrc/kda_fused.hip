@@ -1145,8 +1145,6 @@ static int gate_kind(const Params& p) {
   return plain ? kGatePlain : kGateFlagged;
 }
 
-bool plain_gate(const Params& p) { return gate_kind(p) == kGatePlain; }
-
 hipError_t launch_fused_segments(const Params& p, hipStream_t s, int64_t n_steps, const SegPlan& sg, bool out) {
   switch (gate_kind(p)) {
     case kGateUnbounded: return out ? launch_one<true, kGateUnbounded>(p, s, n_steps, sg) : launch_one<false, kGateUnbounded>(p, s, n_steps, sg);

@@ -65,10 +65,9 @@ size_t workspace_for(const kda_shape_t* sh, int path, int64_t seg_steps) {
 
 namespace kda {
 
-// path actually taken for a valid shape: 1 vector, 2 records, 3 fused, 4 corrected, 5 automatic
-// matrix-core plan (kModeAuto: corrected or fused by the gate); -1 for an unsupported request.  The
-// fused and corrected plans fall back to the records path for shapes they do not take (sequences of
-// 2^23 tokens or more).
+// path actually taken for a valid shape: 1 vector, 2 records, 3 fused, 4 corrected (the automatic
+// choice on the matrix cores); -1 for an unsupported request.  The fused and corrected plans fall back
+// to the records path for shapes they do not take (sequences of 2^23 tokens or more).
 int forward_path(const kda_shape_t* sh, int chunk, const kda_opts_t* opts) {
   const int req = opts ? opts->path : 0;
   const bool mfma = sh->dtype == KDA_DTYPE_BF16 && sh->dk == 128 && sh->dv == 128 && chunk == kChunk;
@@ -77,7 +76,7 @@ int forward_path(const kda_shape_t* sh, int chunk, const kda_opts_t* opts) {
   if (req == 2) return mfma ? kModeRecords : -1;
   if (req == kModeFused || req == kModeCorr) return !mfma ? -1 : fused ? req : kModeRecords;
   if (!mfma) return 1;
-  return fused ? kModeAuto : kModeRecords;
+  return fused ? kModeCorr : kModeRecords;
 }
 
 int record_hip_error(hipError_t e) {

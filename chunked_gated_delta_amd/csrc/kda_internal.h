@@ -63,12 +63,11 @@ hipError_t launch_decode(const DecodeParams& p, hipStream_t s);        // per-to
 size_t bwd_workspace_bytes(int64_t B, int64_t H, int64_t T, int64_t dk, int64_t dv);
 hipError_t launch_bwd(const BwdParams& b, hipStream_t s);              // backward, fp32 vector ALUs
 // the matrix-core paths: 2 records, 3 fused (map pass, chaining, output pass), 4 fused with corrected
-// outputs (one pass over every segment, chaining, correction).  kModeAuto: the corrected plan for a bounded gate with 16 g_min >= -80 (no chunk can need the flagged
-// forms), the fused plan otherwise, in the corrected plan's workspace (which holds the fused plan's)
-enum MfmaMode { kModeRecords = 2, kModeFused = 3, kModeCorr = 4, kModeAuto = 5 };
+// outputs (one pass over every segment, chaining, correction)
+enum MfmaMode { kModeRecords = 2, kModeFused = 3, kModeCorr = 4 };
 // workspace of a matrix-core path for the segment plan that seg_steps (0: automatic) selects: the
 // per-step records of path 2 and the segment blocks; the segment blocks of path 3 (none for a
-// one-segment plan); the segment blocks and the propagated queries of path 4 (and of kModeAuto)
+// one-segment plan); the segment blocks and the propagated queries of path 4
 size_t mfma_workspace_bytes(int64_t B, int64_t H, int64_t T, int64_t dk, int64_t dv, int mode,
                             int64_t seg_steps);
 bool fused_supported(int dtype, int64_t dk, int64_t dv, int64_t T);

@@ -1042,7 +1042,7 @@ int64_t n_steps_of(int64_t T) { return (T + STEP - 1) / STEP; }
 constexpr int64_t kSeg0PctFused = 93, kSeg0PctCorr = 110;
 
 SegPlan make_plan(int64_t BH, int64_t T, int64_t seg_steps, int mode) {
-  const bool records = mode == kModeRecords, corr = mode == kModeCorr || mode == kModeAuto;
+  const bool records = mode == kModeRecords, corr = mode == kModeCorr;
   const int64_t n = n_steps_of(T);
   SegPlan sg{};
   int64_t P;
@@ -1100,11 +1100,6 @@ size_t mfma_workspace_bytes(int64_t B, int64_t H, int64_t T, int64_t dk, int64_t
   const SegPlan sg = make_plan(B * H, T, seg_steps, mode);
   if (mode != kModeRecords && sg.P == 1) return 0;   // a one-segment fused plan keeps nothing between kernels
   if (mode == kModeCorr) return (size_t)(sg.off_q + B * H * n_steps_of(T) * (int64_t)kQtStep);
-  if (mode == kModeAuto) {   // room for either plan (the corrected one's is the larger in practice)
-    const size_t c = mfma_workspace_bytes(B, H, T, dk, dv, kModeCorr, seg_steps);
-    const size_t f = mfma_workspace_bytes(B, H, T, dk, dv, kModeFused, seg_steps);
-    return c > f ? c : f;
-  }
   return (size_t)(sg.off_s + B * H * sg.P * (int64_t)kSegState);
 }
 
@@ -1119,7 +1114,6 @@ hipError_t launch_mfma(const Params& p, hipStream_t s, hipEvent_t ev_begin, hipE
   const int64_t n_steps = n_steps_of(p.T);
   const int64_t BH = p.B * p.H;
   if (mode != kModeRecords && !fused_supported(p.dtype, p.dk, p.dv, p.T)) mode = kModeRecords;
-  if (mode == kModeAuto) mode = plain_gate(p) ? kModeCorr : kModeFused;
   const bool fused = mode == kModeFused;
   const SegPlan sg = make_plan(BH, p.T, p.seg_steps, mode);
   if (mode == kModeCorr) {

@@ -114,9 +114,6 @@ hipError_t launch_fused_segments(const Params& p, hipStream_t s, int64_t n_steps
 // correction of their outputs by the true entering states
 hipError_t launch_fused_corr(const Params& p, hipStream_t s, int64_t n_steps, const SegPlan& sg);
 hipError_t launch_correct(const Params& p, hipStream_t s, int64_t n_steps, const SegPlan& sg);
-// true when the call's gate cannot produce a chunk that needs the flagged-chunk forms (a bounded gate
-// with 16 g_min >= -80, nothing forced): the kernels then run without those forms
-bool plain_gate(const Params& p);
 constexpr int kQtStep = 8 * 64 * 16;     // bytes of one step's propagated queries (8 wavefronts x 64 lanes x 16 B)
 
 }  // namespace kda

@@ -35,7 +35,7 @@ int kda_chunk_fwd_noalloc(const void* q, const void* k, const void* v, const voi
     return kda_chunk_fwd(q, k, v, w, beta, S0, g_min, chunk, shape, o, S_final, nullptr, 0, stats, stream);
   }
   kda_opts_t opts{};
-  if (kda::forward_path(shape, chunk, nullptr) == kda::kModeAuto) opts.path = kda::kModeFused;
+  if (kda::forward_path(shape, chunk, nullptr) == kda::kModeCorr) opts.path = kda::kModeFused;
   // the scratch this call needs: host arithmetic, no HIP call
   const size_t need = kda_workspace_bytes_ex(shape, chunk, &opts);
   if (need == (size_t)-1) return KDA_ERR_ARG;

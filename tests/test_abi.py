@@ -145,7 +145,7 @@ def test_workspace_per_path():
     # entering states, and the propagated queries of every step (8 KiB each)
     assert ex(shape(B=1, H=2, T=64), 4) == 0                          # one segment: nothing kept
     assert ex(sh, 4) == 3 * 2 * 16 * blk + 2 * 128 * 8192
-    # automatic plan: room for the corrected plan (taken with the bounded gate), which holds the fused one
+    # automatic plan: the corrected one
     assert ex(sh, 0) == lib.kda_workspace_bytes(ctypes.byref(sh), 16) == ex(sh, 4) > ex(sh, 3)
     assert ex(sh, 4, seg=5) == 3 * 2 * 26 * blk + 2 * 128 * 8192
     assert ex(sh, 4, seg=3) == ctypes.c_size_t(-1).value
