@@ -75,6 +75,9 @@ def chunk_fwd(q, k, v, w, beta, S0=None, g_min: float = -5.0, chunk: int = 16, *
     current torch stream).  `events` = (begin, end) HipEvent pair recorded
     before the first kernel of the call and after its last.  `seg_steps` > 0
     fixes the matrix-core path's sequence segment length (in 32-token steps).
+    `path`: "auto" (bf16 with dk = dv = 128: "corr"; otherwise "vector"), "vector" (fp32 vector
+    kernel), "mfma" (per-step records), "fused" (map pass, chaining, output pass) or "corr" (one pass
+    over every segment, chaining, correction of the outputs of segments >= 1).
     `force_fallback` = 1 (or True) gives every chunk a flagged chunk's handling, 2 the per-pair
     factors on every chunk; `disable_fallback` lets flagged chunks take the plain tiles.
     """
@@ -129,9 +132,12 @@ def chunk_fwd(q, k, v, w, beta, S0=None, g_min: float = -5.0, chunk: int = 16, *
 def chunk_fwd_noalloc(q, k, v, w, beta, S0=None, g_min: float = -5.0, chunk: int = 16, *,
                       out=None, S_final=None, stats: bool = True, stream=None):
     """KDA chunked forward through kda_chunk_fwd_noalloc: the library takes the call's scratch from its
-    own static device array (no workspace argument).  Same arguments and results as chunk_fwd without
-    the options; out, S_final and stats are allocated here when not given (the C entry point itself
-    allocates nothing).  Calls that overlap in time on one GPU share that array and race."""
+    own static device array (no workspace argument).  Same arguments as chunk_fwd without the options;
+    where chunk_fwd takes the corrected matrix-core plan this takes the fused one (whose scratch fits
+    the array), so the results equal chunk_fwd(..., path="fused") bit for bit and the automatic
+    chunk_fwd to the rounding of the two plans.  out, S_final and stats are allocated here when not
+    given (the C entry point itself allocates nothing).  Calls that overlap in time on one GPU share
+    that array and race."""
     if q.dim() != 4:
         raise ValueError("q must be [B,H,T,dk]")
     B, H, T, dk = q.shape

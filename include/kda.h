@@ -99,14 +99,20 @@ typedef struct {
 typedef struct {
   int32_t disable_fallback; /* 1: flagged chunks still take the dense exp(+-G) path (shows the overflow) */
   int32_t force_fallback;   /* 1: every chunk takes the handling of a flagged chunk (measures its cost):
-                               on the fused path the tiles referenced to the chunk's token 7 where both
+                               on the fused and corrected paths the tiles referenced to the chunk's token 7 where both
                                8-token halves span at least -80, per-position factors otherwise; on the
                                other paths per-position factors.  2: every chunk takes the per-position
                                factors.  Other values are KDA_ERR_ARG. */
-  int32_t path;             /* 0 auto (bf16 with dk = dv = 128: the fused matrix-core path, or the
+  int32_t path;             /* 0 auto (bf16 with dk = dv = 128: the corrected matrix-core path, or the
                                records path past T = 2^23; anything else: the vector path),
                                1 the plain fp32 vector path, 2 the matrix-core path with per-step
-                               records in the workspace, 3 the fused matrix-core path */
+                               records in the workspace, 3 the fused matrix-core path (a pass that
+                               maps every segment, the chaining of the maps, a pass that writes the
+                               outputs from the chained entering states), 4 the corrected
+                               matrix-core path (one pass over every segment: segment 0 from S0,
+                               the others from a zero entering state with the coefficient Qtil of
+                               their outputs on the entering state and their maps; the chaining; an
+                               HBM-bound pass adding Qtil S_start to the outputs of segments >= 1) */
   int32_t seg_steps;        /* matrix-core path: steps of 32 tokens per sequence segment (0 = automatic;
                                < 0, or more than 32 segments per sequence, is KDA_ERR_ARG) */
   void* ev_begin;           /* optional hipEvent_t recorded on `stream` before the call's first kernel */
@@ -133,7 +139,7 @@ enum {
  *           chunk-size and lower-bound co-design of "From Numerical Stability to Load Balancing ..."
  *           section 2.3; evaluated on the fp32 vector path, where each chunk takes the reciprocal
  *           exp(+-G) tiles when its span is at or above -80 and per-pair factors otherwise).  The
- *           matrix-core paths (opts->path 2, 3) take 16 only.
+ *           matrix-core paths (opts->path 2, 3, 4) take 16 only.
  *   S0      may be NULL (zero initial state).
  *   workspace / workspace_bytes: device scratch of at least
  *           kda_workspace_bytes(shape, chunk) bytes (kda_workspace_bytes_ex with the same
@@ -153,18 +159,22 @@ KDA_API int kda_chunk_fwd_ex(const void* q, const void* k, const void* v, const 
                      kda_stats_t* stats, void* stream, const kda_opts_t* opts);
 
 /* Size of the static device array kda_chunk_fwd_noalloc takes its scratch from: 64 MiB per GPU the
- * library runs on, held from the first call on that GPU until the process ends.  It holds the
- * automatic segment plan of up to 341 (b, h, segment) triples of 192 KiB, e.g. B*H = 16 heads at
- * any T below 2^23 (17 segments each) or B*H = 32 (9 segments each); the plan needs none (and any
- * shape is accepted) where it keeps one segment per sequence or takes the vector path. */
+ * library runs on, held from the first call on that GPU until the process ends.  It holds the fused
+ * path's segment plan (which the entry point takes where the automatic path is the corrected one) of
+ * up to 341 (b, h, segment) triples of 192 KiB, e.g. B*H = 16 heads at any T below 2^23 (17 segments
+ * each) or B*H = 32 (9 segments each); the plan needs none (and any shape is accepted) where it keeps
+ * one segment per sequence or takes the vector path. */
 #define KDA_NOALLOC_SCRATCH_BYTES (64u * 1024u * 1024u)
 
 /* Forward pass that allocates nothing, for callers that cannot allocate device memory at call time
  * (code under stream capture, tight serving loops, harnesses that forbid allocation).
- * Same arguments, validation, results and asynchrony as kda_chunk_fwd without workspace and
- * workspace_bytes: the scratch kda_workspace_bytes(shape, chunk) reports is taken from a static
- * device array of the library (KDA_NOALLOC_SCRATCH_BYTES, one per GPU, looked up on the first call on
- * each GPU with that GPU current).  Returns KDA_ERR_SCRATCH, launching nothing, when the call needs
+ * Same arguments, validation and asynchrony as kda_chunk_fwd without workspace and
+ * workspace_bytes.  Where kda_chunk_fwd would take the corrected matrix-core path, this entry point
+ * takes the fused one (opts->path = 3), whose scratch is 64 KiB blocks per segment, not 8 KiB per 32
+ * tokens: its results agree with kda_chunk_fwd's to the rounding of the two plans and equal, bit for
+ * bit, those of kda_chunk_fwd_ex with that path.  The scratch (kda_workspace_bytes_ex for that plan)
+ * is taken from a static device array of the library (KDA_NOALLOC_SCRATCH_BYTES, one per GPU, looked
+ * up on the first call on each GPU with that GPU current).  Returns KDA_ERR_SCRATCH, launching nothing, when the call needs
  * more than that; every other error as kda_chunk_fwd.  No hipMalloc or hipFree, no allocating
  * library routine.  All calls on one GPU share its array: calls that overlap in time on one GPU
  * (concurrent streams, or several host threads) race on it and must be serialised by the caller;
@@ -228,9 +238,11 @@ KDA_API int kda_gate_prefix(const void* w, float g_min, int chunk, const kda_sha
 /* Scratch bytes kda_chunk_fwd needs for this shape (0 means none): three 64 KiB
  * blocks (a segment's map X and M, and its entering state) per sequence segment
  * of the plan the call takes (the automatic plan here, up to 32 segments per
- * (b, h); the fused path keeps nothing when the plan has one segment); on the
- * records path (opts->path = 2, or T >= 2^23), also a 29 KiB record per 32
- * tokens per (b, h).  Returns (size_t)-1 for an invalid shape, chunk or path.
+ * (b, h); the fused and corrected paths keep nothing when the plan has one
+ * segment); on the corrected path (the automatic one at bf16, dk = dv = 128),
+ * also the propagated queries, 8 KiB per 32 tokens per (b, h); on the records
+ * path (opts->path = 2, or T >= 2^23), a 29 KiB record per 32 tokens per (b, h).
+ * Returns (size_t)-1 for an invalid shape, chunk or path.
  * Host-only, no HIP call.                                                    */
 KDA_API size_t kda_workspace_bytes(const kda_shape_t* shape, int chunk);
 
