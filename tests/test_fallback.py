@@ -63,6 +63,23 @@ def test_forced_fallback_matches(path, g_min, force):
     assert st["n_nonfinite"] == 0
 
 
+@pytest.mark.parametrize("path,seg", [("vector", 0), ("mfma", 3), ("fused", 0), ("fused", 3), ("corr", 0), ("corr", 3)])
+def test_nonfinite_count_matches_outputs(path, seg):
+    """With the fallback off, the overflowing chunks make outputs non-finite from that chunk on; the
+    count the forward reports is exactly the number of non-finite entries of o and S_final it
+    returns, on every path and segment plan.  The corrected plan counts in three places: segment 0's
+    outputs in its pass, the corrected outputs of the later segments in the correction, and S_final
+    in the chaining."""
+    wl = UNB.with_(B=1, H=2, T=640)
+    kw = dict(disable_fallback=True)
+    if seg:
+        kw["seg_steps"] = seg   # 7 segments of 3 steps
+    _, _, st, o, S, *_ = compare(wl, seed=0, path=path, **kw)
+    n = int((~np.isfinite(o)).sum() + (~np.isfinite(S)).sum())
+    say(f"   stats={st} non-finite in o and S_final: {n}")
+    assert n > 0 and st["n_nonfinite"] == n
+
+
 def half_spans(w, g_min):
     """Per 16-token chunk, the minimum over channels of the spans of its two 8-token halves (fp64)."""
     g = orc.gate(w, g_min)
