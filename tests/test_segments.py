@@ -39,6 +39,15 @@ def test_forced_segments(T, seg, path):
     check(BF16.with_(B=1, H=2, T=T), seed=200 + T + seg, path=path, seg_steps=seg)
 
 
+@pytest.mark.parametrize("T,seg", [(320, 3), (1440, 20), (1450, 20)])
+def test_correction_workgroup_boundaries(T, seg):
+    """The corrected plan's correction runs 16 steps per workgroup: T = 320 with segments of 3 steps
+    leaves a last segment of one step; segments of 20 steps take two workgroups each, the second
+    covering 4 steps, and the last segment (5 steps; 6 with the 10-token tail of T = 1450) leaves the
+    second workgroup of its segment empty.  S0 present, so every correction is non-zero."""
+    check(BF16.with_(B=1, H=2, T=T, s0_sd=0.5), seed=400 + T + seg, path="corr", seg_steps=seg)
+
+
 @pytest.mark.parametrize("path", SEG_PATHS)
 @pytest.mark.parametrize("seg", [1, 4])
 def test_segments_with_initial_state(seg, path):
