@@ -107,6 +107,14 @@ def test_automatic_plan_several_heads(path):
     check(BF16.with_(B=2, H=4, T=2048), seed=17, path=path)
 
 
+@pytest.mark.parametrize("path", ["auto", "fused"])
+def test_automatic_plan_odd_head_count(path):
+    """B3 H5 (15 heads) T8229 with S0: the corrected (automatic) plan takes 17 segments per head (255
+    workgroups in its pass), a first segment of 17 steps and a last one of a single, ragged step; the
+    fused plan 18 segments (17 workgroups per head in each pass)."""
+    check(BF16.with_(B=3, H=5, T=8229, s0_sd=0.3), seed=21, path=path)
+
+
 @pytest.mark.parametrize("path", SEG_PATHS)
 def test_segment_plans_agree(path):
     """Different segment plans change only the rounding."""
