@@ -174,8 +174,11 @@ template <> __device__ __forceinline__ float gate2<true>(float w, float) {
   return -(fmaxf(w, 0.f) * kLog2e + __builtin_amdgcn_logf(1.f + __builtin_amdgcn_exp2f(-fabsf(w) * kLog2e)));
 }
 
-// Raw buffer views of one (b, h) slice of a tensor: loads past the end of the slice return zero, so
-// tokens past the end of the sequence read as k = q = v = beta = 0 (their gates are masked in E).
+// Raw buffer views of one segment of one (b, h) slice of a tensor, from the segment's first token to
+// its last (or to the end of the sequence): loads past the end of a view return zero, so tokens past
+// the end of the sequence read as k = q = v = beta = 0 (their gates are masked in E).  A view's byte
+// count and the offsets inside it are 32-bit: a segment holds fewer than 2^18 steps (2 GiB of one
+// tensor), whatever the length of the sequence.
 struct Views {
   __amdgpu_buffer_rsrc_t k, w, q, beta, v;
 };
@@ -689,7 +692,7 @@ __device__ __forceinline__ void e_loop(FusedShared& sm, const Params& p, const V
   const int e_boff = (16 * CC + 4 * (lane & 3)) * 2;
   EIn ein;
   EKeep ekeep;
-  e_load<OUT>(ein, vw, s0, e_voff, e_boff);
+  e_load<OUT>(ein, vw, 0, e_voff, e_boff);   // steps relative to the segment's first
   int slotE = 2;   // record slot of step it + 2 (it + 2 mod 3), advanced at the top of each pass
 #pragma unroll 1
   for (int it = -2; it < ns; ++it) {
@@ -703,7 +706,7 @@ __device__ __forceinline__ void e_loop(FusedShared& sm, const Params& p, const V
     if (doE) e_first<GK == kGateUnbounded, CC, GK != kGatePlain>(sm, ein, ekeep, p, s0 + it + 2, recE, we, ln);
     // prefetches are issued on every path (clamped to the segment's last step) so that the memory
     // counter waits before their uses stay exact
-    e_load<OUT>(ein, vw, s0 + (it + 3 < ns ? it + 3 : ns - 1), e_voff, e_boff);
+    e_load<OUT>(ein, vw, it + 3 < ns ? it + 3 : ns - 1, e_voff, e_boff);
     if (COR && it >= 0)   // step it's record: the slot after step it + 2's
       transition_step(sm.rec[slotE == kRecSlots - 1 ? 0 : slotE + 1], M, qdst + it * (int64_t)kQtStep + we * 1024 + lane * 16,
                       lane);
@@ -784,7 +787,7 @@ __device__ __forceinline__ void fused_part(FusedShared& sm, const Params& p, int
   const bool is_e = w >= kCWaves;
   const int we = w - kCWaves;                 // E wavefront index (valid when is_e)
   const int li = lane & 15, lg = lane >> 4;
-  // step indices fit 32 bits (T < 2^23), which keeps the scalar index arithmetic short
+  // step and token indices fit 32 bits (T < 2^30), which keeps the scalar index arithmetic short
   const int s0 = j == 0 ? 0 : (int)sg.L0 + (j - 1) * (int)sg.L;
   const int len = j == 0 ? (int)sg.L0 : (int)sg.L;
   const int ns = ((int)n_steps - s0 < len) ? (int)n_steps - s0 : len;
@@ -792,14 +795,16 @@ __device__ __forceinline__ void fused_part(FusedShared& sm, const Params& p, int
   const int col = 16 * (w & 7) + li;
   const floatx4 zero = {0, 0, 0, 0};
 
-  Views vw;
+  Views vw;   // this segment's tokens; loads take steps relative to s0
   {
-    const int64_t nb = T * D * 2;
-    vw.k = view((const uint16_t*)p.k + bh * T * D, nb);
-    vw.w = view((const uint16_t*)p.w + bh * T * D, nb);
-    vw.q = view((const uint16_t*)p.q + bh * T * D, nb);
-    vw.v = view((const uint16_t*)p.v + bh * T * D, nb);
-    vw.beta = view((const uint16_t*)p.beta + bh * T, T * 2);
+    const int64_t tok0 = (int64_t)s0 * STEP;
+    const int64_t ntok = (T - tok0 < (int64_t)ns * STEP) ? T - tok0 : (int64_t)ns * STEP;
+    const int64_t nb = ntok * D * 2;
+    vw.k = view((const uint16_t*)p.k + (bh * T + tok0) * D, nb);
+    vw.w = view((const uint16_t*)p.w + (bh * T + tok0) * D, nb);
+    vw.q = view((const uint16_t*)p.q + (bh * T + tok0) * D, nb);
+    vw.v = view((const uint16_t*)p.v + (bh * T + tok0) * D, nb);
+    vw.beta = view((const uint16_t*)p.beta + bh * T + tok0, ntok * 2);
   }
 
   // The two kinds of wavefront run separate copies of the step loop (same trip count, same barriers in
@@ -862,7 +867,7 @@ __device__ __forceinline__ void fused_part(FusedShared& sm, const Params& p, int
     const int sl = slot16(ln);
     const bool low4 = MR == kMNone && w < 4;   // wavefronts 0-3 (the copies with M are wavefronts 4-7)
     if (OUT && low4) {   // V of step it + 1, issued first so that the whole first half covers its latency
-      const int sn = s0 + (it + 1 < 0 ? 0 : (it + 1 < ns ? it + 1 : ns - 1));
+      const int sn = it + 1 < 0 ? 0 : (it + 1 < ns ? it + 1 : ns - 1);   // relative to s0
 #pragma unroll
       for (int i = 0; i < 2; ++i) vq[i] = v_load16(vw, sn, 8 * w + 4 * i + (lane >> 4), lane & 15);
     }
@@ -968,7 +973,7 @@ __device__ __forceinline__ void fused_part(FusedShared& sm, const Params& p, int
       else tiles<OUT, false>(sm, recS, opsF, sm.ops[(it + 2) & 1], si->pairwise, 0u, (int)((it + 1) & 1), w, ln);
     }
     if (!OUT && low4) {   // V of step it + 1 (the map pass has no registers to carry it over the chain)
-      const int sn = s0 + (it + 1 < 0 ? 0 : (it + 1 < ns ? it + 1 : ns - 1));
+      const int sn = it + 1 < 0 ? 0 : (it + 1 < ns ? it + 1 : ns - 1);   // relative to s0
 #pragma unroll
       for (int i = 0; i < 2; ++i) vq[i] = v_load16(vw, sn, 8 * w + 4 * i + (lane >> 4), lane & 15);
     }
@@ -1130,8 +1135,8 @@ hipError_t launch_one(const Params& p, hipStream_t s, int64_t n_steps, const Seg
 }  // namespace
 
 bool fused_supported(int dtype, int64_t dk, int64_t dv, int64_t T) {
-  // 32-bit buffer offsets: a (b, h) slice of a [B,H,T,128] bf16 tensor must stay below 2^31 bytes
-  return dtype == KDA_DTYPE_BF16 && dk == D && dv == D && T < ((int64_t)1 << 23);
+  // token and step indices are 32-bit in the kernels (the segment length is checked with the plan)
+  return dtype == KDA_DTYPE_BF16 && dk == D && dv == D && T < ((int64_t)1 << 30);
 }
 
 // The gate kind of a call.  With a bounded gate and 16 g_min >= -80 every chunk's span is at least -80

@@ -67,16 +67,20 @@ namespace kda {
 
 // path actually taken for a valid shape: 1 vector, 2 records, 3 fused, 4 corrected (the automatic
 // choice on the matrix cores); -1 for an unsupported request.  The fused and corrected plans fall back
-// to the records path for shapes they do not take (sequences of 2^23 tokens or more).
+// to the records path where a segment of their plan would hold 2^18 steps or more (with one segment per
+// sequence, 2^23 tokens; with the automatic plan's 16 segments of 16 heads, 2^27).
 int forward_path(const kda_shape_t* sh, int chunk, const kda_opts_t* opts) {
   const int req = opts ? opts->path : 0;
   const bool mfma = sh->dtype == KDA_DTYPE_BF16 && sh->dk == 128 && sh->dv == 128 && chunk == kChunk;
-  const bool fused = mfma && fused_supported(sh->dtype, sh->dk, sh->dv, sh->T);
+  const int64_t seg = opts ? opts->seg_steps : 0;
+  auto fits = [&](int mode) {
+    return mfma && fused_supported(sh->dtype, sh->dk, sh->dv, sh->T) && plan_fits(sh->B * sh->H, sh->T, seg, mode);
+  };
   if (req == 1) return 1;
   if (req == 2) return mfma ? kModeRecords : -1;
-  if (req == kModeFused || req == kModeCorr) return !mfma ? -1 : fused ? req : kModeRecords;
+  if (req == kModeFused || req == kModeCorr) return !mfma ? -1 : fits(req) ? req : kModeRecords;
   if (!mfma) return 1;
-  return fused ? kModeCorr : kModeRecords;
+  return fits(kModeCorr) ? kModeCorr : kModeRecords;
 }
 
 int record_hip_error(hipError_t e) {

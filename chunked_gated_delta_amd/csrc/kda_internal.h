@@ -71,6 +71,10 @@ enum MfmaMode { kModeRecords = 2, kModeFused = 3, kModeCorr = 4 };
 size_t mfma_workspace_bytes(int64_t B, int64_t H, int64_t T, int64_t dk, int64_t dv, int mode,
                             int64_t seg_steps);
 bool fused_supported(int dtype, int64_t dk, int64_t dv, int64_t T);
+// whether every segment of the plan (mode kModeFused or kModeCorr) stays below kMaxSegSteps steps, the
+// limit of the fused kernels' 32-bit buffer views (2^18 steps of 32 tokens: 2 GiB of one bf16 tensor)
+constexpr int64_t kMaxSegSteps = (int64_t)1 << 18;
+bool plan_fits(int64_t BH, int64_t T, int64_t seg_steps, int mode);
 bool mfma_seg_steps_ok(int64_t T, int64_t seg_steps);                    // forced segment length allowed?
 hipError_t launch_mfma(const Params& p, hipStream_t s, hipEvent_t ev_begin, hipEvent_t ev_end, int mode);
 // the forward path a valid call takes: 1 vector, or a matrix-core mode; -1 for an unsupported request

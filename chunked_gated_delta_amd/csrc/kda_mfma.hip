@@ -1045,6 +1045,10 @@ SegPlan make_plan(int64_t BH, int64_t T, int64_t seg_steps, int mode) {
   const bool records = mode == kModeRecords, corr = mode == kModeCorr;
   const int64_t n = n_steps_of(T);
   SegPlan sg{};
+  if (n <= 0) {   // an empty sequence: one empty segment, nothing kept
+    sg.P = 1;
+    return sg;
+  }
   int64_t P;
   if (seg_steps > 0) {
     sg.L = seg_steps;
@@ -1103,6 +1107,11 @@ size_t mfma_workspace_bytes(int64_t B, int64_t H, int64_t T, int64_t dk, int64_t
   return (size_t)(sg.off_s + B * H * sg.P * (int64_t)kSegState);
 }
 
+bool plan_fits(int64_t BH, int64_t T, int64_t seg_steps, int mode) {
+  const SegPlan sg = make_plan(BH, T, seg_steps, mode);
+  return (sg.L > sg.L0 ? sg.L : sg.L0) < kMaxSegSteps;
+}
+
 bool mfma_seg_steps_ok(int64_t T, int64_t seg_steps) {
   if (seg_steps < 0) return false;
   if (seg_steps == 0) return true;
@@ -1113,7 +1122,8 @@ bool mfma_seg_steps_ok(int64_t T, int64_t seg_steps) {
 hipError_t launch_mfma(const Params& p, hipStream_t s, hipEvent_t ev_begin, hipEvent_t ev_end, int mode) {
   const int64_t n_steps = n_steps_of(p.T);
   const int64_t BH = p.B * p.H;
-  if (mode != kModeRecords && !fused_supported(p.dtype, p.dk, p.dv, p.T)) mode = kModeRecords;
+  if (mode != kModeRecords && !(fused_supported(p.dtype, p.dk, p.dv, p.T) && plan_fits(BH, p.T, p.seg_steps, mode)))
+    mode = kModeRecords;
   const bool fused = mode == kModeFused;
   const SegPlan sg = make_plan(BH, p.T, p.seg_steps, mode);
   if (mode == kModeCorr) {

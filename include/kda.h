@@ -104,7 +104,10 @@ typedef struct {
                                other paths per-position factors.  2: every chunk takes the per-position
                                factors.  Other values are KDA_ERR_ARG. */
   int32_t path;             /* 0 auto (bf16 with dk = dv = 128: the corrected matrix-core path, or the
-                               records path past T = 2^23; anything else: the vector path),
+                               records path where a segment of its plan would reach 2^18 steps of 32
+                               tokens: T >= P * 2^23 for a plan of P segments per sequence, P =
+                               min(256 / (B*H), 32) or 1, e.g. T >= 2^23 at B*H >= 256); anything
+                               else: the vector path),
                                1 the plain fp32 vector path, 2 the matrix-core path with per-step
                                records in the workspace, 3 the fused matrix-core path (a pass that
                                maps every segment, the chaining of the maps, a pass that writes the
@@ -241,7 +244,8 @@ KDA_API int kda_gate_prefix(const void* w, float g_min, int chunk, const kda_sha
  * (b, h); the fused and corrected paths keep nothing when the plan has one
  * segment); on the corrected path (the automatic one at bf16, dk = dv = 128),
  * also the propagated queries, 8 KiB per 32 tokens per (b, h); on the records
- * path (opts->path = 2, or T >= 2^23), a 29 KiB record per 32 tokens per (b, h).
+ * path (opts->path = 2, or where a plan segment would reach 2^18 steps), a 29 KiB record per 32
+ * tokens per (b, h).
  * Returns (size_t)-1 for an invalid shape, chunk or path.
  * Host-only, no HIP call.                                                    */
 KDA_API size_t kda_workspace_bytes(const kda_shape_t* shape, int chunk);

@@ -123,6 +123,8 @@ def test_workspace_per_path():
     ex = lambda sh, path, seg=0: lib.kda_workspace_bytes_ex(ctypes.byref(sh), 16,
                                                             ctypes.byref(KdaOpts(0, 0, path, seg, None, None)))
     blk = 128 * 128 * 4                         # one X, M or S_start block (64 KiB)
+    for path in (0, 2, 3, 4):                   # an empty sequence keeps nothing on any path
+        assert ex(shape(T=0), path) == 0
     sh = shape(B=1, H=2, T=64)                  # 2 steps of 32 tokens per (b, h): one segment
     assert lib.kda_workspace_bytes(ctypes.byref(sh), 16) == 0        # automatic: fused, nothing kept
     assert ex(sh, 3) == 0
@@ -138,7 +140,15 @@ def test_workspace_per_path():
     assert ex(sh, 3, seg=3) == ctypes.c_size_t(-1).value             # 43 segments: more than 32
     assert ex(shape(dk=64, dv=64), 3) == ctypes.c_size_t(-1).value   # no matrix-core path at d = 64
     assert ex(shape(dk=64, dv=64), 0) == 0
-    assert ex(shape(T=1 << 23), 0) == ex(shape(T=1 << 23), 2)         # past the fused path's range
+    # the fused kernels' views hold one segment of fewer than 2^18 steps: two heads of 2^23 tokens take
+    # the corrected plan (32 segments of 8192 steps); 256 heads keep one segment per sequence, 2^18 steps,
+    # and take the records path, one step fewer the corrected plan (its one segment keeps nothing)
+    big_t = shape(T=1 << 23)
+    assert ex(big_t, 0) == ex(big_t, 4) == 3 * 2 * 32 * blk + 2 * (1 << 18) * 8192
+    wide = shape(B=1, H=256, T=1 << 23)
+    assert ex(wide, 0) == ex(wide, 4) == ex(wide, 2) > 0
+    assert ex(shape(B=1, H=256, T=(1 << 23) - 32), 0) == 0
+    assert ex(big_t, 4, seg=1 << 18) == ex(big_t, 2, seg=1 << 18)      # a forced segment of 2^18 steps
     # the records path checks its own, larger size
     assert call(sh, ws_bytes=ex(sh, 3), opts=KdaOpts(0, 0, 2, 0, None, None)) == -4
     # corrected plan: at most 16 segments of 8 steps (one pass holds every segment), its maps and
@@ -150,7 +160,6 @@ def test_workspace_per_path():
     assert ex(sh, 4, seg=5) == 3 * 2 * 26 * blk + 2 * 128 * 8192
     assert ex(sh, 4, seg=3) == ctypes.c_size_t(-1).value
     assert ex(shape(dk=64, dv=64), 4) == ctypes.c_size_t(-1).value
-    assert ex(shape(T=1 << 23), 4) == ex(shape(T=1 << 23), 2)         # past the fused path's range
     assert call(sh, ws_bytes=ex(sh, 3), opts=KdaOpts(0, 0, 4, 0, None, None)) == -4
 
 

@@ -83,6 +83,41 @@ def test_decay_stress_full(path):
     assert -80.0 <= stats["min_span"] < -79.5
 
 
+@pytest.mark.timeout(400)
+def test_beyond_2_23_tokens():
+    """One head of T = 2^23 + 37 tokens with S0.  The fused kernels' buffer views cover one segment,
+    so the corrected plan (32 segments of 8192 steps) takes the whole sequence on the matrix cores.
+    Checked against the records path (64-bit addressing, an independent arrangement of the chunk
+    form) on every output and S_final, and against the fp64 oracle on the last 1024 tokens, run from
+    the state a call on the first T - 1024 tokens reaches."""
+    from chunked_gated_delta_amd import chunk_fwd, decode_stats
+    wl = gen.WORKLOADS["headline"].with_(B=1, H=1, T=(1 << 23) + 37, s0_sd=0.3)
+    say(f"[case] {wl} automatic plan against the records path and a 1024-token oracle window")
+    inp = gen.make_torch(wl, seed=7, device="cuda")
+    names = ("q", "k", "v", "w", "beta")
+    o, S, st = chunk_fwd(*(inp[n] for n in names), inp["S0"], g_min=wl.g_min)
+    stats = decode_stats(st)
+    assert stats["n_chunks"] == (wl.T + 15) // 16 and stats["n_nonfinite"] == 0
+    o_r, S_r, _ = chunk_fwd(*(inp[n] for n in names), inp["S0"], g_min=wl.g_min, path="mfma")
+    torch.cuda.synchronize()
+    eo = float((o.float() - o_r.float()).abs().max() / o_r.float().abs().max())
+    es = float((S - S_r).abs().max() / S_r.abs().max())
+    say(f"   against the records path: err_o={eo:.3e} err_S={es:.3e}")
+    del o_r, S_r
+    tol_o, tol_s = TOL["bf16"]
+    assert eo <= tol_o and es <= tol_s
+    tw = 1024
+    _, S_mid, _ = chunk_fwd(*(inp[n][:, :, :wl.T - tw].contiguous() for n in names), inp["S0"], g_min=wl.g_min)
+    torch.cuda.synchronize()
+    f = {n: inp[n][:, :, wl.T - tw:].float().cpu().numpy().astype(np.float64) for n in names}
+    o_ref, S_ref = orc.kda_reference(f["q"], f["k"], f["v"], f["w"], f["beta"],
+                                     S_mid.cpu().numpy().astype(np.float64), wl.g_min)
+    eo = rel_err(o[:, :, wl.T - tw:].float().cpu().numpy(), o_ref)
+    es = rel_err(S.cpu().numpy(), S_ref)
+    say(f"   last {tw} tokens against the oracle: err_o={eo:.3e} err_S={es:.3e}")
+    assert eo <= tol_o and es <= tol_s
+
+
 @pytest.mark.timeout(600)
 def test_million_token_share_full():
     from kda_testutil import mfma_available
