@@ -19,9 +19,13 @@ last.
 same workload (all heads, the first tokens of the sequence).
 
 Defaults: 40 untimed warm-up calls, then 50 timed ones.  The GPU needs about
-30 ms of back-to-back calls before their duration settles (the first forward
-calls after start-up take up to 1.1 ms, the settled ones about 0.92 ms), so
-the warm-up spans that ramp and the timed calls do not.
+35 ms of back-to-back calls before their duration settles (after start-up the
+first call takes about 1.3 ms, calls 4-8 0.72-0.81 ms, the settled ones about
+0.61-0.63 ms, as the clock settles to the load), so the warm-up spans that ramp
+and the timed calls do not.  `--heads H` runs the workload with H heads and
+`--seg-steps N` fixes the matrix-core plan's segment length (N steps of 32
+tokens): together they hold each workgroup's work fixed while the number of
+busy compute units changes.
 
 Other modes print a line of the same form for other entry points:
 `--mode decode` one recurrent decode call over a serving batch (kda_decode,
@@ -483,6 +487,10 @@ def main():
     ap.add_argument("--force-fallback", action="store_true",
                     help="every chunk takes a flagged chunk's handling (midpoint tiles or per-pair factors)")
     ap.add_argument("--force-pairwise", action="store_true", help="every chunk takes the per-pair factors")
+    ap.add_argument("--heads", type=int, default=0,
+                    help="run the workload with this many heads instead of its own (0: the workload's)")
+    ap.add_argument("--seg-steps", type=int, default=0,
+                    help="matrix-core paths: fix the segment length in 32-token steps (0: the automatic plan)")
     ap.add_argument("--mode", default="forward", choices=["forward", "decode", "bwd"],
                     help="forward: the chunked forward (the headline); decode: one recurrent decode "
                          "step of a serving batch (workload decode_b512 unless --workload is given); "
@@ -523,10 +531,13 @@ def main():
         return
 
     wl = gen.WORKLOADS[args.workload]
+    if args.heads:
+        wl = wl.with_(H=args.heads)
     log(f"[bench] workload {wl}")
     inp = gen.make_torch(wl, seed=args.seed, device="cuda")
     torch.cuda.synchronize()
-    kw = dict(path=args.path, force_fallback=2 if args.force_pairwise else int(args.force_fallback))
+    kw = dict(path=args.path, force_fallback=2 if args.force_pairwise else int(args.force_fallback),
+              seg_steps=args.seg_steps)
     kern_avg, kern_ms, wall, stats, o, S = time_forward(torch, inp, wl, wl.g_min, args.steps, args.warmup, kw)
     log(f"[bench] kernel ms: avg {kern_avg:.4f} min {min(kern_ms):.4f} max {max(kern_ms):.4f}; wall/step "
         f"{1e3 * wall / args.steps:.4f} ms; stats {stats}")
@@ -554,7 +565,8 @@ def main():
     value = tokens / (wall / args.steps)
     abytes = algorithmic_bytes(wl)
     achieved = abytes / (kern_avg * 1e-3) / 1e9
-    traffic = measured_traffic(wl.name) if args.path != "vector" else None
+    # the stored counters describe the workload's own shape and plan
+    traffic = measured_traffic(wl.name) if args.path != "vector" and not (args.heads or args.seg_steps) else None
     roofline = {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                 "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None if traffic is None else round(traffic),
                 "bytes_per_launch": abytes, "kernel_ms": round(kern_avg, 5),
@@ -581,7 +593,7 @@ def main():
         "data": "synthetic",
         "config": {"workload": wl.name, "B": wl.B, "H": wl.H, "T": wl.T, "dk": wl.dk, "dv": wl.dv,
                    "chunk": wl.chunk, "g_min": wl.g_min if math.isfinite(wl.g_min) else "-inf",
-                   "path": args.path, "parallelism": "single-gpu"},
+                   "path": args.path, "seg_steps": args.seg_steps or "auto", "parallelism": "single-gpu"},
         "roofline": roofline,
         "cpu_baseline": cpu,
         "stats": stats,
