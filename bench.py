@@ -82,8 +82,7 @@ def kernel_short_name(name):
     """Short name of a library kernel (or of the calibration copy) in a rocprofv3 record."""
     for key, short in (("fused_kernel<true", "fused_out"), ("fused_kernel<false", "fused_state"),
                        ("fused_corr_kernel", "corr_pass"), ("correct_kernel", "correct"),
-                       ("seg_combine_kernel", "seg_combine"), ("seg_state_kernel", "seg_state"),
-                       ("seg_out_kernel", "seg_out"), ("prep_kernel", "prep"), ("vec_", "vector")):
+                       ("seg_combine_kernel", "seg_combine"), ("vec_", "vector")):
         if key in name:
             return short
     if "copyBuffer" in name or "elementwise_kernel<16" in name:
@@ -478,7 +477,7 @@ def main():
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=40)
     ap.add_argument("--workload", default="headline")
-    ap.add_argument("--path", default="auto", choices=["auto", "vector", "mfma", "fused", "corr"])
+    ap.add_argument("--path", default="auto", choices=["auto", "vector", "fused", "corr"])
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-accuracy", action="store_true",

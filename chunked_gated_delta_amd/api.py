@@ -11,7 +11,7 @@ import torch
 from . import _lib
 from ._lib import KdaError, KdaOpts, KdaShape
 
-_PATHS = {"auto": 0, "vector": 1, "mfma": 2, "fused": 3, "corr": 4}
+_PATHS = {"auto": 0, "vector": 1, "fused": 3, "corr": 4}
 
 
 def _dtype_code(t: torch.Tensor) -> int:
@@ -76,7 +76,7 @@ def chunk_fwd(q, k, v, w, beta, S0=None, g_min: float = -5.0, chunk: int = 16, *
     before the first kernel of the call and after its last.  `seg_steps` > 0
     fixes the matrix-core path's sequence segment length (in 32-token steps).
     `path`: "auto" (bf16 with dk = dv = 128: "corr"; otherwise "vector"), "vector" (fp32 vector
-    kernel), "mfma" (per-step records), "fused" (map pass, chaining, output pass) or "corr" (one pass
+    kernel), "fused" (map pass, chaining, output pass) or "corr" (one pass
     over every segment, chaining, correction of the outputs of segments >= 1).
     `force_fallback` = 1 (or True) gives every chunk a flagged chunk's handling, 2 the per-pair
     factors on every chunk; `disable_fallback` lets flagged chunks take the plain tiles.

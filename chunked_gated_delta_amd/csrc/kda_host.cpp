@@ -53,11 +53,11 @@ bool chunk_ok(int chunk) { return chunk == 16 || chunk == 32 || chunk == 64; }
 
 int pick_path(const kda_shape_t* sh, int chunk, const kda_opts_t* opts) { return kda::forward_path(sh, chunk, opts); }
 
-// the matrix-core paths' ids are their modes (kModeRecords, kModeFused, kModeCorr)
-static_assert(kda::kModeRecords == 2 && kda::kModeFused == 3 && kda::kModeCorr == 4, "path ids are the modes");
+// the matrix-core paths' ids are their modes (kModeFused, kModeCorr)
+static_assert(kda::kModeFused == 3 && kda::kModeCorr == 4, "path ids are the modes");
 
 size_t workspace_for(const kda_shape_t* sh, int path, int64_t seg_steps) {
-  if (path < 2) return 0;
+  if (path < kda::kModeFused) return 0;
   return kda::mfma_workspace_bytes(sh->B, sh->H, sh->T, sh->dk, sh->dv, path, seg_steps);
 }
 
@@ -65,22 +65,17 @@ size_t workspace_for(const kda_shape_t* sh, int path, int64_t seg_steps) {
 
 namespace kda {
 
-// path actually taken for a valid shape: 1 vector, 2 records, 3 fused, 4 corrected (the automatic
-// choice on the matrix cores); -1 for an unsupported request.  The fused and corrected plans fall back
-// to the records path where a segment of their plan would hold 2^18 steps or more (with one segment per
-// sequence, 2^23 tokens; with the automatic plan's 16 segments of 16 heads, 2^27).
+// path actually taken for a valid shape: 1 vector, 3 fused, 4 corrected (the automatic choice on the
+// matrix cores); -1 for an unsupported request.  The matrix-core kernels index tokens in 32 bits, so
+// sequences of 2^30 tokens and more take the vector path (their inputs would not fit in HBM anyway).
 int forward_path(const kda_shape_t* sh, int chunk, const kda_opts_t* opts) {
   const int req = opts ? opts->path : 0;
-  const bool mfma = sh->dtype == KDA_DTYPE_BF16 && sh->dk == 128 && sh->dv == 128 && chunk == kChunk;
-  const int64_t seg = opts ? opts->seg_steps : 0;
-  auto fits = [&](int mode) {
-    return mfma && fused_supported(sh->dtype, sh->dk, sh->dv, sh->T) && plan_fits(sh->B * sh->H, sh->T, seg, mode);
-  };
+  const bool mfma = sh->dtype == KDA_DTYPE_BF16 && sh->dk == 128 && sh->dv == 128 && chunk == kChunk &&
+                    fused_supported(sh->dtype, sh->dk, sh->dv, sh->T);
   if (req == 1) return 1;
-  if (req == 2) return mfma ? kModeRecords : -1;
-  if (req == kModeFused || req == kModeCorr) return !mfma ? -1 : fits(req) ? req : kModeRecords;
-  if (!mfma) return 1;
-  return fits(kModeCorr) ? kModeCorr : kModeRecords;
+  if (req == kModeFused || req == kModeCorr) return mfma ? req : -1;
+  if (req != 0) return -1;
+  return mfma ? kModeCorr : 1;
 }
 
 int record_hip_error(hipError_t e) {
@@ -124,7 +119,7 @@ size_t kda_workspace_bytes_ex(const kda_shape_t* shape, int chunk, const kda_opt
   const int path = pick_path(shape, chunk, opts);
   if (path < 0) return (size_t)-1;
   const int64_t seg_steps = opts ? opts->seg_steps : 0;
-  if (path >= 2 && !kda::mfma_seg_steps_ok(shape->T, seg_steps)) return (size_t)-1;
+  if (path >= kda::kModeFused && !kda::mfma_seg_steps_ok(shape->T, seg_steps)) return (size_t)-1;
   return workspace_for(shape, path, seg_steps);
 }
 
@@ -189,7 +184,7 @@ int kda_chunk_fwd_ex(const void* q, const void* k, const void* v, const void* w,
 
   const int path = T > 0 ? pick_path(shape, chunk, opts) : 1;
   if (path < 0) return KDA_ERR_UNSUPPORTED;
-  if (path >= 2 && !kda::mfma_seg_steps_ok(T, p.seg_steps)) return KDA_ERR_ARG;
+  if (path >= kda::kModeFused && !kda::mfma_seg_steps_ok(T, p.seg_steps)) return KDA_ERR_ARG;
   const size_t need_ws = workspace_for(shape, path, p.seg_steps);
   if (need_ws > 0 && (!workspace || workspace_bytes < need_ws)) return KDA_ERR_ARG;
 
@@ -199,14 +194,14 @@ int kda_chunk_fwd_ex(const void* q, const void* k, const void* v, const void* w,
   hipEvent_t ev1 = opts ? reinterpret_cast<hipEvent_t>(opts->ev_end) : nullptr;
   hipError_t e;
   // statistics reset here for the vector path and T = 0; the matrix-core paths do it themselves
-  if (stats && (T == 0 || path < 2) && (e = kda::launch_stats_init(stats, s)) != hipSuccess) return hip_fail(e);
+  if (stats && (T == 0 || path < kda::kModeFused) && (e = kda::launch_stats_init(stats, s)) != hipSuccess) return hip_fail(e);
   if (T == 0) {
     if (ev0 && (e = hipEventRecord(ev0, s)) != hipSuccess) return hip_fail(e);
     if ((e = kda::launch_state_copy(p, s)) != hipSuccess) return hip_fail(e);
     if (ev1 && (e = hipEventRecord(ev1, s)) != hipSuccess) return hip_fail(e);
     return KDA_OK;
   }
-  if (path >= 2) {
+  if (path >= kda::kModeFused) {
     if ((e = kda::launch_mfma(p, s, ev0, ev1, path)) != hipSuccess) return hip_fail(e);
   } else {
     if (ev0 && (e = hipEventRecord(ev0, s)) != hipSuccess) return hip_fail(e);

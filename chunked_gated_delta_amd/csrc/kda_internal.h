@@ -62,19 +62,19 @@ hipError_t launch_vec(const Params& p, hipStream_t s);                 // plain 
 hipError_t launch_decode(const DecodeParams& p, hipStream_t s);        // per-token recurrence on a resident state
 size_t bwd_workspace_bytes(int64_t B, int64_t H, int64_t T, int64_t dk, int64_t dv);
 hipError_t launch_bwd(const BwdParams& b, hipStream_t s);              // backward, fp32 vector ALUs
-// the matrix-core paths: 2 records, 3 fused (map pass, chaining, output pass), 4 fused with corrected
-// outputs (one pass over every segment, chaining, correction)
-enum MfmaMode { kModeRecords = 2, kModeFused = 3, kModeCorr = 4 };
+// the matrix-core paths (path ids 3 and 4 of kda_opts_t): 3 fused (map pass, chaining, output pass),
+// 4 fused with corrected outputs (one pass over every segment, chaining, correction)
+enum MfmaMode { kModeFused = 3, kModeCorr = 4 };
 // workspace of a matrix-core path for the segment plan that seg_steps (0: automatic) selects: the
-// per-step records of path 2 and the segment blocks; the segment blocks of path 3 (none for a
-// one-segment plan); the segment blocks and the propagated queries of path 4
+// segment blocks of path 3 (none for a one-segment plan); the segment blocks and the propagated
+// queries of path 4
 size_t mfma_workspace_bytes(int64_t B, int64_t H, int64_t T, int64_t dk, int64_t dv, int mode,
                             int64_t seg_steps);
 bool fused_supported(int dtype, int64_t dk, int64_t dv, int64_t T);
-// whether every segment of the plan (mode kModeFused or kModeCorr) stays below kMaxSegSteps steps, the
-// limit of the fused kernels' 32-bit buffer views (2^18 steps of 32 tokens: 2 GiB of one bf16 tensor)
+// every segment of a plan stays below kMaxSegSteps steps, the limit of the fused kernels' 32-bit buffer
+// views (2^18 steps of 32 tokens: 2 GiB of one bf16 tensor): the automatic plan takes more segments
+// where needed, and a forced segment length must be shorter
 constexpr int64_t kMaxSegSteps = (int64_t)1 << 18;
-bool plan_fits(int64_t BH, int64_t T, int64_t seg_steps, int mode);
 bool mfma_seg_steps_ok(int64_t T, int64_t seg_steps);                    // forced segment length allowed?
 hipError_t launch_mfma(const Params& p, hipStream_t s, hipEvent_t ev_begin, hipEvent_t ev_end, int mode);
 // the forward path a valid call takes: 1 vector, or a matrix-core mode; -1 for an unsupported request

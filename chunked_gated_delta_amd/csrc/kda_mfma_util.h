@@ -24,13 +24,6 @@ __device__ __forceinline__ floatx4 mfma(bf16x8 a, bf16x8 b, floatx4 c) {
 
 __device__ __forceinline__ bf16x8 ld8(const void* p) { return *reinterpret_cast<const bf16x8*>(p); }
 
-// gate in log2 units: g * log2(e)
-__device__ __forceinline__ float gate_log2(float w, float g_min, int unbounded) {
-  if (unbounded) return -(fmaxf(w, 0.f) + log1pf(expf(-fabsf(w)))) * kLog2e;
-  const float s = __builtin_amdgcn_rcpf(1.f + __builtin_amdgcn_exp2f(-w * kLog2e));
-  return (g_min * kLog2e) * s;
-}
-
 typedef __bf16 bf16x2v __attribute__((ext_vector_type(2)));
 typedef float float2v __attribute__((ext_vector_type(2)));
 typedef __bf16 bf16x8v __attribute__((ext_vector_type(8)));
@@ -90,7 +83,7 @@ __device__ __forceinline__ void load_slice(floatx4 (&S)[8], const float* src, in
   for (int t = 0; t < 8; ++t) S[t] = *reinterpret_cast<const floatx4*>(src + (t * 64 + lane) * 4);
 }
 
-// Segment plan shared by the scan kernels: P segments of L steps (32 tokens) per (b, h); workspace
+// Segment plan shared by the segment kernels: P segments of L steps (32 tokens) per (b, h); workspace
 // byte offsets of the per-segment X, M and S_start blocks (128 x 128 fp32 each).
 struct SegPlan {
   int64_t P, L;   // segments per (b, h); steps per segment, segment 0 aside
@@ -100,7 +93,7 @@ struct SegPlan {
 };
 constexpr int kSegState = 128 * 128 * 4;    // bytes of one block (64 KiB)
 constexpr int kMHalf = 8 * 4 * 64 * 16;     // bytes of one bf16 part (hi or lo) of a transition M
-constexpr int kMaxSeg = 32;                 // segments per (b, h)
+constexpr int kMaxSeg = 32;                 // segments per (b, h), unless a segment would reach kMaxSegSteps
 // the fused path's per-head statistics record of segment 0, in the (otherwise unused) entering-state
 // block of segment 0, as uint32: the non-finite counts of the 8 state wavefronts, then chunks, flagged
 // chunks and the bits of the minimum span

@@ -67,7 +67,7 @@
 extern "C" {
 #endif
 
-#define KDA_VERSION 100 /* 1.0.0 */
+#define KDA_VERSION 110 /* 1.1.0: path 2 retired */
 
 #if defined(__GNUC__) || defined(__clang__)
 #define KDA_API __attribute__((visibility("default")))
@@ -103,21 +103,22 @@ typedef struct {
                                8-token halves span at least -80, per-position factors otherwise; on the
                                other paths per-position factors.  2: every chunk takes the per-position
                                factors.  Other values are KDA_ERR_ARG. */
-  int32_t path;             /* 0 auto (bf16 with dk = dv = 128: the corrected matrix-core path, or the
-                               records path where a segment of its plan would reach 2^18 steps of 32
-                               tokens: T >= P * 2^23 for a plan of P segments per sequence, P =
-                               min(256 / (B*H), 32) or 1, e.g. T >= 2^23 at B*H >= 256); anything
-                               else: the vector path),
-                               1 the plain fp32 vector path, 2 the matrix-core path with per-step
-                               records in the workspace, 3 the fused matrix-core path (a pass that
+  int32_t path;             /* 0 auto (bf16 with dk = dv = 128 and T < 2^30: the corrected matrix-core
+                               path; anything else: the vector path),
+                               1 the plain fp32 vector path, 3 the fused matrix-core path (a pass that
                                maps every segment, the chaining of the maps, a pass that writes the
                                outputs from the chained entering states), 4 the corrected
                                matrix-core path (one pass over every segment: segment 0 from S0,
                                the others from a zero entering state with the coefficient Qtil of
                                their outputs on the entering state and their maps; the chaining; an
-                               HBM-bound pass adding Qtil S_start to the outputs of segments >= 1) */
+                               HBM-bound pass adding Qtil S_start to the outputs of segments >= 1).
+                               2 (a retired path) and values above 4 are KDA_ERR_UNSUPPORTED, and so
+                               are 3 and 4 where the matrix-core paths do not apply.  The automatic
+                               segment plan of paths 3 and 4 has at most 32 segments per sequence,
+                               more only where a segment would otherwise reach 2^18 steps */
   int32_t seg_steps;        /* matrix-core path: steps of 32 tokens per sequence segment (0 = automatic;
-                               < 0, or more than 32 segments per sequence, is KDA_ERR_ARG) */
+                               < 0, 2^18 or more, or more than 32 segments per sequence, is
+                               KDA_ERR_ARG) */
   void* ev_begin;           /* optional hipEvent_t recorded on `stream` before the call's first kernel */
   void* ev_end;             /* optional hipEvent_t recorded on `stream` after the call's last kernel */
 } kda_opts_t;
@@ -142,7 +143,7 @@ enum {
  *           chunk-size and lower-bound co-design of "From Numerical Stability to Load Balancing ..."
  *           section 2.3; evaluated on the fp32 vector path, where each chunk takes the reciprocal
  *           exp(+-G) tiles when its span is at or above -80 and per-pair factors otherwise).  The
- *           matrix-core paths (opts->path 2, 3, 4) take 16 only.
+ *           matrix-core paths (opts->path 3, 4) take 16 only.
  *   S0      may be NULL (zero initial state).
  *   workspace / workspace_bytes: device scratch of at least
  *           kda_workspace_bytes(shape, chunk) bytes (kda_workspace_bytes_ex with the same
@@ -241,11 +242,9 @@ KDA_API int kda_gate_prefix(const void* w, float g_min, int chunk, const kda_sha
 /* Scratch bytes kda_chunk_fwd needs for this shape (0 means none): three 64 KiB
  * blocks (a segment's map X and M, and its entering state) per sequence segment
  * of the plan the call takes (the automatic plan here, up to 32 segments per
- * (b, h); the fused and corrected paths keep nothing when the plan has one
- * segment); on the corrected path (the automatic one at bf16, dk = dv = 128),
- * also the propagated queries, 8 KiB per 32 tokens per (b, h); on the records
- * path (opts->path = 2, or where a plan segment would reach 2^18 steps), a 29 KiB record per 32
- * tokens per (b, h).
+ * (b, h) unless a segment would reach 2^18 steps of 32 tokens; nothing when the
+ * plan has one segment); on the corrected path (the automatic one at bf16,
+ * dk = dv = 128), also the propagated queries, 8 KiB per 32 tokens per (b, h).
  * Returns (size_t)-1 for an invalid shape, chunk or path.
  * Host-only, no HIP call.                                                    */
 KDA_API size_t kda_workspace_bytes(const kda_shape_t* shape, int chunk);

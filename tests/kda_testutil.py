@@ -83,7 +83,7 @@ def mfma_available() -> bool:
         x = torch.zeros((1, 1, 16, 128), dtype=torch.bfloat16, device="cuda")
         b = torch.zeros((1, 1, 16), dtype=torch.bfloat16, device="cuda")
         try:
-            chunk_fwd(x, x, x, x, b, path="mfma")
+            chunk_fwd(x, x, x, x, b, path="corr")
             torch.cuda.synchronize()
             _MFMA = True
         except KdaError as e:
@@ -95,5 +95,5 @@ def mfma_available() -> bool:
 
 def need_path(path):
     import pytest
-    if path == "mfma" and not mfma_available():
+    if path in ("fused", "corr") and not mfma_available():
         pytest.skip("matrix-core path not available in this build")

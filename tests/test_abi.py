@@ -43,7 +43,7 @@ def test_exports_every_declared_symbol():
 
 
 def test_version_and_strings():
-    assert _lib.version() == 100
+    assert _lib.version() == 110
     for code in (0, -1, -2, -3, -4, -5, -6):
         assert len(_lib.strerror(code)) >= 2
     assert _lib.strerror(-99) == "unknown error code"
@@ -93,7 +93,7 @@ def test_chunk_32_64_only_on_the_vector_path():
     """32- and 64-token chunks run on the vector path (no workspace); the matrix-core paths take 16."""
     for chunk in (32, 64):
         assert lib.kda_workspace_bytes(ctypes.byref(shape(T=4096)), chunk) == 0
-        for path in (2, 3, 4):
+        for path in (3, 4):
             assert call(chunk=chunk, opts=KdaOpts(0, 0, path, 0, None, None)) == -3
             assert lib.kda_workspace_bytes_ex(ctypes.byref(shape()), chunk,
                                               ctypes.byref(KdaOpts(0, 0, path, 0, None, None))) == ctypes.c_size_t(-1).value
@@ -123,14 +123,14 @@ def test_workspace_per_path():
     ex = lambda sh, path, seg=0: lib.kda_workspace_bytes_ex(ctypes.byref(sh), 16,
                                                             ctypes.byref(KdaOpts(0, 0, path, seg, None, None)))
     blk = 128 * 128 * 4                         # one X, M or S_start block (64 KiB)
-    for path in (0, 2, 3, 4):                   # an empty sequence keeps nothing on any path
+    for path in (0, 1, 3, 4):                   # an empty sequence keeps nothing on any path
         assert ex(shape(T=0), path) == 0
     sh = shape(B=1, H=2, T=64)                  # 2 steps of 32 tokens per (b, h): one segment
     assert lib.kda_workspace_bytes(ctypes.byref(sh), 16) == 0        # automatic: fused, nothing kept
     assert ex(sh, 3) == 0
-    assert ex(sh, 2) == 2 * 2 * 29696 + 3 * 2 * blk                 # a 29 KiB record per step, one segment
     assert ex(sh, 1) == 0
-    assert ex(sh, 7) == ctypes.c_size_t(-1).value
+    for path in (2, 5, 7):                      # no such path (2 was the per-step records path)
+        assert ex(sh, path) == ex(shape(T=0), path) == ctypes.c_size_t(-1).value
     # 128 steps per head, two heads: at most 16 segments of 8 steps; segment 0, which runs with its
     # outputs beside the maps, is 0.93x the others, so the plan is 8 steps, then 9-step segments (the
     # last takes the remaining 3): 15 segments
@@ -141,16 +141,20 @@ def test_workspace_per_path():
     assert ex(shape(dk=64, dv=64), 3) == ctypes.c_size_t(-1).value   # no matrix-core path at d = 64
     assert ex(shape(dk=64, dv=64), 0) == 0
     # the fused kernels' views hold one segment of fewer than 2^18 steps: two heads of 2^23 tokens take
-    # the corrected plan (32 segments of 8192 steps); 256 heads keep one segment per sequence, 2^18 steps,
-    # and take the records path, one step fewer the corrected plan (its one segment keeps nothing)
+    # 32 segments of 8192 steps; 256 heads would keep one segment per sequence, 2^18 steps, so their
+    # plan takes two (a segment 0 of 1.1x the other's length on the corrected plan, 0.93x on the fused
+    # one), one step fewer keeps one segment (the corrected plan then keeps nothing)
     big_t = shape(T=1 << 23)
     assert ex(big_t, 0) == ex(big_t, 4) == 3 * 2 * 32 * blk + 2 * (1 << 18) * 8192
     wide = shape(B=1, H=256, T=1 << 23)
-    assert ex(wide, 0) == ex(wide, 4) == ex(wide, 2) > 0
+    assert ex(wide, 0) == ex(wide, 4) == 3 * 256 * 2 * blk + 256 * (1 << 18) * 8192
+    assert ex(wide, 3) == 3 * 256 * 2 * blk
     assert ex(shape(B=1, H=256, T=(1 << 23) - 32), 0) == 0
-    assert ex(big_t, 4, seg=1 << 18) == ex(big_t, 2, seg=1 << 18)      # a forced segment of 2^18 steps
-    # the records path checks its own, larger size
-    assert call(sh, ws_bytes=ex(sh, 3), opts=KdaOpts(0, 0, 2, 0, None, None)) == -4
+    # a forced segment of 2^18 steps is refused; one step shorter gives two segments
+    assert ex(big_t, 4, seg=1 << 18) == ex(big_t, 0, seg=1 << 18) == ctypes.c_size_t(-1).value
+    assert ex(big_t, 4, seg=(1 << 18) - 1) == 3 * 2 * 2 * blk + 2 * (1 << 18) * 8192
+    assert call(big_t, opts=KdaOpts(0, 0, 0, 1 << 18, None, None)) == -4
+    assert call(sh, opts=KdaOpts(0, 0, 2, 0, None, None)) == -3
     # corrected plan: at most 16 segments of 8 steps (one pass holds every segment), its maps and
     # entering states, and the propagated queries of every step (8 KiB each)
     assert ex(shape(B=1, H=2, T=64), 4) == 0                          # one segment: nothing kept

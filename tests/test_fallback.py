@@ -18,7 +18,7 @@ if not torch.cuda.is_available():
     pytest.skip("no GPU", allow_module_level=True)
 
 UNB = gen.WORKLOADS["unbounded"]
-PATHS = ["vector", "mfma", "fused", "corr"]
+PATHS = ["vector", "fused", "corr"]
 
 
 @pytest.mark.parametrize("path", PATHS)
@@ -63,7 +63,7 @@ def test_forced_fallback_matches(path, g_min, force):
     assert st["n_nonfinite"] == 0
 
 
-@pytest.mark.parametrize("path,seg", [("vector", 0), ("mfma", 3), ("fused", 0), ("fused", 3), ("corr", 0), ("corr", 3)])
+@pytest.mark.parametrize("path,seg", [("vector", 0), ("fused", 0), ("fused", 3), ("corr", 0), ("corr", 3)])
 def test_nonfinite_count_matches_outputs(path, seg):
     """With the fallback off, the overflowing chunks make outputs non-finite from that chunk on; the
     count the forward reports is exactly the number of non-finite entries of o and S_final it

@@ -87,22 +87,23 @@ def test_decay_stress_full(path):
 def test_beyond_2_23_tokens():
     """One head of T = 2^23 + 37 tokens with S0.  The fused kernels' buffer views cover one segment,
     so the corrected plan (32 segments of 8192 steps) takes the whole sequence on the matrix cores.
-    Checked against the records path (64-bit addressing, an independent arrangement of the chunk
-    form) on every output and S_final, and against the fp64 oracle on the last 1024 tokens, run from
-    the state a call on the first T - 1024 tokens reaches."""
+    Checked against the fused plan (32 segments: the maps chained before a second pass writes the
+    outputs from the true entering states, where the corrected plan adds Qtil S_start afterwards) on
+    every output and S_final, and against the fp64 oracle on the last 1024 tokens, run from the state
+    a call on the first T - 1024 tokens reaches."""
     from chunked_gated_delta_amd import chunk_fwd, decode_stats
     wl = gen.WORKLOADS["headline"].with_(B=1, H=1, T=(1 << 23) + 37, s0_sd=0.3)
-    say(f"[case] {wl} automatic plan against the records path and a 1024-token oracle window")
+    say(f"[case] {wl} automatic plan against the fused plan and a 1024-token oracle window")
     inp = gen.make_torch(wl, seed=7, device="cuda")
     names = ("q", "k", "v", "w", "beta")
     o, S, st = chunk_fwd(*(inp[n] for n in names), inp["S0"], g_min=wl.g_min)
     stats = decode_stats(st)
     assert stats["n_chunks"] == (wl.T + 15) // 16 and stats["n_nonfinite"] == 0
-    o_r, S_r, _ = chunk_fwd(*(inp[n] for n in names), inp["S0"], g_min=wl.g_min, path="mfma")
+    o_r, S_r, _ = chunk_fwd(*(inp[n] for n in names), inp["S0"], g_min=wl.g_min, path="fused")
     torch.cuda.synchronize()
     eo = float((o.float() - o_r.float()).abs().max() / o_r.float().abs().max())
     es = float((S - S_r).abs().max() / S_r.abs().max())
-    say(f"   against the records path: err_o={eo:.3e} err_S={es:.3e}")
+    say(f"   against the fused plan: err_o={eo:.3e} err_S={es:.3e}")
     del o_r, S_r
     tol_o, tol_s = TOL["bf16"]
     assert eo <= tol_o and es <= tol_s

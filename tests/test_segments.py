@@ -19,7 +19,7 @@ if not torch.cuda.is_available():
 BF16 = gen.WORKLOADS["bf16_4k"]
 
 
-SEG_PATHS = ["mfma", "fused", "corr"]
+SEG_PATHS = ["fused", "corr"]
 
 
 def check(wl, seed, path, **kw):
