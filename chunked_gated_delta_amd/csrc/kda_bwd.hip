@@ -1204,12 +1204,10 @@ __global__ __launch_bounds__(NTG) __attribute__((amdgpu_waves_per_eu(4, 4))) voi
 template <typename TIn, int DK>
 hipError_t launch_bwd_dk(const BwdParams& b, hipStream_t s) {
   const Params& p = b.p;
-  static bool attr_set = false;
-  if (!attr_set) {
-    hipError_t e = hipFuncSetAttribute((const void*)bwd_grad_kernel<TIn, DK>,
-                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)sizeof(GradShared<DK>));
+  static std::atomic<uint64_t> lds_set{0};
+  {
+    const hipError_t e = set_dyn_lds((const void*)bwd_grad_kernel<TIn, DK>, (int)sizeof(GradShared<DK>), lds_set);
     if (e != hipSuccess) return e;
-    attr_set = true;
   }
   const int64_t BH = p.B * p.H, NC = p.n_chunks();
   const WsLayout L = ws_layout(p.workspace, BH, NC, p.dk, p.dv);

@@ -1103,13 +1103,9 @@ __global__ __launch_bounds__(kThreads) void fused_corr_kernel(Params p, int64_t 
 
 template <int GK>
 hipError_t launch_corr(const Params& p, hipStream_t s, int64_t n_steps, const SegPlan& sg) {
-  static bool attr_set = false;
-  if (!attr_set) {
-    hipError_t e = hipFuncSetAttribute((const void*)fused_corr_kernel<GK>, hipFuncAttributeMaxDynamicSharedMemorySize,
-                                       (int)kFusedSmem);
-    if (e != hipSuccess) return e;
-    attr_set = true;
-  }
+  static std::atomic<uint64_t> lds_set{0};
+  const hipError_t e = set_dyn_lds((const void*)fused_corr_kernel<GK>, (int)kFusedSmem, lds_set);
+  if (e != hipSuccess) return e;
   if (sg.P > 1 && sg.off_q == 0) return hipErrorInvalidValue;   // a plan without room for the queries
   hipLaunchKernelGGL((fused_corr_kernel<GK>), dim3((unsigned)(p.B * p.H * sg.P)), dim3(kThreads), kFusedSmem, s, p,
                      n_steps, sg);
@@ -1118,13 +1114,9 @@ hipError_t launch_corr(const Params& p, hipStream_t s, int64_t n_steps, const Se
 
 template <bool OUT, int GK>
 hipError_t launch_one(const Params& p, hipStream_t s, int64_t n_steps, const SegPlan& sg) {
-  static bool attr_set = false;
-  if (!attr_set) {
-    hipError_t e = hipFuncSetAttribute((const void*)fused_kernel<OUT, GK>, hipFuncAttributeMaxDynamicSharedMemorySize,
-                                       (int)kFusedSmem);
-    if (e != hipSuccess) return e;
-    attr_set = true;
-  }
+  static std::atomic<uint64_t> lds_set{0};
+  const hipError_t e = set_dyn_lds((const void*)fused_kernel<OUT, GK>, (int)kFusedSmem, lds_set);
+  if (e != hipSuccess) return e;
   if (!OUT && sg.P < 2) return hipErrorInvalidValue;   // a one-segment plan has no map pass
   const int64_t nb = sg.P > 1 ? sg.P - 1 : 1;
   hipLaunchKernelGGL((fused_kernel<OUT, GK>), dim3((unsigned)(p.B * p.H * nb)), dim3(kThreads), kFusedSmem, s, p,

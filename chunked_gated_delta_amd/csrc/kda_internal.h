@@ -4,6 +4,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <atomic>
+
 #include "kda.h"
 
 namespace kda {
@@ -47,6 +49,20 @@ struct BwdParams {
   const float* dSf;
   float *dq, *dk, *dv, *dw, *dbeta, *dS0;   // dS0 nullable
 };
+
+// Raises kernel fn's dynamic LDS limit to `bytes` on the current device, once per device (the attribute
+// belongs to the device; `done` holds one bit per device id below 64, beyond which it is set every call).
+// Host-only and not a stream operation, so calls under graph capture keep it.
+inline hipError_t set_dyn_lds(const void* fn, int bytes, std::atomic<uint64_t>& done) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  const uint64_t bit = (dev >= 0 && dev < 64) ? (uint64_t)1 << dev : 0;
+  if (bit && (done.load(std::memory_order_acquire) & bit)) return hipSuccess;
+  e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, bytes);
+  if (e == hipSuccess && bit) done.fetch_or(bit, std::memory_order_release);
+  return e;
+}
 
 // Error text for kda_last_hip_error(): both store the text for the calling thread and return KDA_ERR_HIP.
 int record_hip_error(hipError_t e);

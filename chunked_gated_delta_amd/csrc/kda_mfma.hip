@@ -194,6 +194,15 @@ constexpr int kCorSteps = 16;
 constexpr int kCorThreads = 512;
 constexpr int kCorRow = 272;   // staged output row: 256 bytes of data, 16 of pad (column reads spread over the banks)
 
+typedef unsigned int u32x4v __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ uint4 nt_load16(const void* p) {
+  const u32x4v x = __builtin_nontemporal_load(reinterpret_cast<const u32x4v*>(p));
+  return uint4{x[0], x[1], x[2], x[3]};
+}
+__device__ __forceinline__ void nt_store16(void* p, uint4 v) {
+  __builtin_nontemporal_store(u32x4v{v.x, v.y, v.z, v.w}, reinterpret_cast<u32x4v*>(p));
+}
+
 __device__ __forceinline__ int64_t xcd_logical(int64_t b, int64_t G) {
   // blocks go round-robin over the 8 XCDs: number XCD x's blocks x (G / 8) + min(x, G % 8) onward, so
   // that consecutive logical ids (steps of one segment, which read the same entering state) share an L2
@@ -234,8 +243,10 @@ __global__ __launch_bounds__(kCorThreads) void correct_kernel(Params p, int64_t 
   uint4 qreg, oreg;
   auto fetch = [&](int64_t i) {
     const int64_t st = s0 + a + i;
-    qreg = *reinterpret_cast<const uint4*>(qbase + i * (int64_t)kQtStep + tid * 16);
-    oreg = orow < rows_of(st) ? *reinterpret_cast<const uint4*>(obase + (st * STEP + orow) * D + ocol) : uint4{0, 0, 0, 0};
+    // Qtil and the outputs stream through once (766 MB at the headline against 32 MB of L2): the
+    // non-temporal forms keep them from displacing lines that other work still reads
+    qreg = nt_load16(qbase + i * (int64_t)kQtStep + tid * 16);
+    oreg = orow < rows_of(st) ? nt_load16(obase + (st * STEP + orow) * D + ocol) : uint4{0, 0, 0, 0};
   };
   fetch(0);
   uint32_t bad = 0;
@@ -273,8 +284,7 @@ __global__ __launch_bounds__(kCorThreads) void correct_kernel(Params p, int64_t 
         bad += (not_finite(r0) ? 1u : 0u) + (not_finite(r1) ? 1u : 0u) + (not_finite(r2) ? 1u : 0u) + (not_finite(r3) ? 1u : 0u);
     }
     __syncthreads();
-    if (orow < nrows) *reinterpret_cast<uint4*>(obase + (st * STEP + orow) * D + ocol) =
-                          *reinterpret_cast<const uint4*>(os + orow * kCorRow + ocol * 2);
+    if (orow < nrows) nt_store16(obase + (st * STEP + orow) * D + ocol, *reinterpret_cast<const uint4*>(os + orow * kCorRow + ocol * 2));
   }
   if (p.stats) {
 #pragma unroll

@@ -407,13 +407,9 @@ template <typename TIn, int DK, int C>
 hipError_t launch_one(const Params& p, hipStream_t s) {
   using Cfg = VecCfg<DK, C>;
   static_assert(Cfg::kBytes <= 163840, "LDS budget");
-  static bool attr_set = false;
-  if (!attr_set) {
-    const hipError_t e = hipFuncSetAttribute((const void*)vec_kernel<TIn, DK, C>,
-                                             hipFuncAttributeMaxDynamicSharedMemorySize, (int)Cfg::kBytes);
-    if (e != hipSuccess) return e;
-    attr_set = true;
-  }
+  static std::atomic<uint64_t> lds_set{0};
+  const hipError_t e = set_dyn_lds((const void*)vec_kernel<TIn, DK, C>, (int)Cfg::kBytes, lds_set);
+  if (e != hipSuccess) return e;
   const int nslices = (int)((p.dv + kDvs - 1) / kDvs);
   hipLaunchKernelGGL((vec_kernel<TIn, DK, C>), dim3((unsigned)(p.B * p.H * nslices)), dim3(kThreads), Cfg::kBytes, s,
                      p);
