@@ -96,4 +96,4 @@ def mfma_available() -> bool:
 def need_path(path):
     import pytest
     if path in ("fused", "corr") and not mfma_available():
-        pytest.skip("matrix-core path not available in this build")
+        pytest.skip("the loaded library has no matrix-core path")
