@@ -438,6 +438,60 @@ def gen_bwd_ws(wl) -> int:
     return max(1, _lib.bwd_workspace_bytes(make_shape(wl.B, wl.H, wl.T, wl.dk, wl.dv, code), 16))
 
 
+def phase_stamps(args):
+    """--phase-stamps BLOCK: the workload's forward (automatic plan) through libkda_stamps.so, in which
+    lane 0 of every wavefront of the segment pass's workgroup BLOCK records the shader clock
+    (s_memtime) at six phase boundaries of each of the segment's first 48 intervals, into the end of
+    the workspace.  After `--warmup` calls one more call is stamped, and the median over intervals
+    6-46 of each phase's length (in shader-clock cycles) is printed per wavefront.  State wavefronts
+    0-7: chain (the state step of step s), tile+V (a causal tile of step s+1, the V copy, and on
+    wavefronts 6-7 of a corrected segment their transition slices), bar1 (wait at the first barrier),
+    store (output rows and V staging), solve (the diagonal solve, wavefronts 6-7), bar2 (the rest up to
+    the next interval: on wavefronts 4-5 of a corrected segment their transition slices, then the
+    wait).  E wavefronts 8-15: E1, load (issue of the next step's inputs), trans (the transition
+    slices of the chunk-0 group in a corrected segment), bar1, E2, bar2."""
+    os.environ["KDA_LIB_PATH"] = os.path.join(ROOT, "chunked_gated_delta_amd", "libkda_stamps.so")
+    os.environ["KDA_STAMP_BLOCK"] = str(args.phase_stamps)
+    import statistics
+    import torch
+    from chunked_gated_delta_amd import chunk_fwd, workspace_bytes
+    from chunked_gated_delta_amd import inputs as gen
+    wl = gen.WORKLOADS[args.workload]
+    if args.heads:
+        wl = wl.with_(H=args.heads)
+    t = gen.make_torch(wl, seed=args.seed, device="cuda")
+    ws_n = workspace_bytes(wl.B, wl.H, wl.T, wl.dk, wl.dv, gen.torch_dtype(wl.dtype))
+    ksteps, kk, nwaves = 48, 6, 16
+    stamp_bytes = nwaves * ksteps * kk * 8
+    if ws_n < stamp_bytes:
+        sys.exit("--phase-stamps needs the matrix-core path (bf16, dk = dv = 128)")
+    ws = torch.zeros(ws_n, dtype=torch.uint8, device="cuda")
+    names = ("q", "k", "v", "w", "beta")
+    for _ in range(max(1, args.warmup)):
+        chunk_fwd(*(t[n] for n in names), t["S0"], g_min=wl.g_min, workspace=ws, seg_steps=args.seg_steps)
+    torch.cuda.synchronize()
+    ws[ws_n - stamp_bytes:].zero_()
+    chunk_fwd(*(t[n] for n in names), t["S0"], g_min=wl.g_min, workspace=ws, seg_steps=args.seg_steps)
+    torch.cuda.synchronize()
+    pr = ws[ws_n - stamp_bytes:].view(torch.int64).cpu().tolist()
+    print(f"phase stamps: workload {wl.name} (B{wl.B} H{wl.H} T{wl.T}), segment-pass workgroup {args.phase_stamps}, "
+          f"median shader-clock cycles per 32-token step over intervals 6-46", flush=True)
+    for w in range(nwaves):
+        rows = []
+        for it in range(6, ksteps - 1):
+            a = pr[(w * ksteps + it) * kk:(w * ksteps + it + 1) * kk]
+            nxt = pr[(w * ksteps + it + 1) * kk]
+            if a[0] == 0 or a[3] == 0 or nxt == 0:
+                continue
+            rows.append([a[1] - a[0], a[2] - a[1], a[3] - a[2], a[4] - a[3], a[5] - a[4], nxt - a[5], nxt - a[0]])
+        if not rows:
+            continue
+        med = [int(statistics.median(c)) for c in zip(*rows)]
+        lab = (["chain", "tile+V", "bar1", "store", "solve", "bar2", "step"] if w < 8
+               else ["E1", "load", "trans", "bar1", "E2", "bar2", "step"])
+        print(f"wave {w:2d}: " + "  ".join(f"{l}={m}" for l, m in zip(lab, med)), flush=True)
+
+
 def oracle_threads(wl) -> int:
     try:
         cores = len(os.sched_getaffinity(0))
@@ -490,6 +544,9 @@ def main():
                     help="run the workload with this many heads instead of its own (0: the workload's)")
     ap.add_argument("--seg-steps", type=int, default=0,
                     help="matrix-core paths: fix the segment length in 32-token steps (0: the automatic plan)")
+    ap.add_argument("--phase-stamps", type=int, default=None, metavar="BLOCK",
+                    help="load libkda_stamps.so and print the median cycles of each phase of the segment pass's "
+                         "32-token step, per wavefront, in workgroup BLOCK (head times segments plus segment: 0 is segment 0 of head 0)")
     ap.add_argument("--mode", default="forward", choices=["forward", "decode", "bwd"],
                     help="forward: the chunked forward (the headline); decode: one recurrent decode "
                          "step of a serving batch (workload decode_b512 unless --workload is given); "
@@ -502,6 +559,10 @@ def main():
 
     if args.summarize_pmc:
         summarize_pmc(*args.summarize_pmc, os.path.join(PROFILES, f"traffic_{args.workload}.json"), args.workload)
+        return
+
+    if args.phase_stamps is not None:
+        phase_stamps(args)
         return
 
     if args.gpus != 1:

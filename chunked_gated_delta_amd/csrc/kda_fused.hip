@@ -132,6 +132,22 @@ struct FusedShared {
 constexpr size_t kFusedSmem = sizeof(FusedShared);
 static_assert(kFusedSmem <= 163840, "LDS budget");
 
+// Phase stamps (the phase-stamp build only, libkda_stamps.so; a no-op otherwise): lane 0 of wavefront w
+// of the chosen workgroup records the shader clock at phase boundary k of interval `it` (the interval
+// whose E stage handles step it, counted from the segment's first).
+// The product build compiles the calls away entirely (KDA_STAMP expands to nothing), so its code is
+// the same as without them.
+#if KDA_PHASE_STAMPS
+__device__ __forceinline__ void stamp(const Params& p, int w, int it, int k) {
+  if ((int)blockIdx.x != p.stamp_block || it < 0 || it >= kStampSteps || (threadIdx.x & 63) != 0) return;
+  unsigned long long* pr = (unsigned long long*)((unsigned char*)p.workspace + p.stamp_off);
+  pr[(w * kStampSteps + it) * kStampK + k] = __builtin_amdgcn_s_memtime();
+}
+#define KDA_STAMP(p, w, it, k) stamp(p, w, it, k)
+#else
+#define KDA_STAMP(p, w, it, k) ((void)0)
+#endif
+
 // x, hidden from the optimizer: values derived from it inside a loop are recomputed there instead of
 // being hoisted out of the loop and held in registers for its whole length
 __device__ __forceinline__ int opaque(int x) {
@@ -702,15 +718,20 @@ __device__ __forceinline__ void e_loop(FusedShared& sm, const Params& p, const V
     unsigned char* opsE = sm.ops[(it + 2) & 1];           // step it + 2
     unsigned char* opsF = sm.ops[(it + 3) & 1];           // step it + 1 (free once its tiles are formed)
     block_barrier();
+    KDA_STAMP(p, 8 + we, it + 2, 0);
     const int ln = opaque(lane);   // lane-derived offsets are recomputed in the loop rather than held
     if (doE) e_first<GK == kGateUnbounded, CC, GK != kGatePlain>(sm, ein, ekeep, p, s0 + it + 2, recE, we, ln);
+    KDA_STAMP(p, 8 + we, it + 2, 1);
     // prefetches are issued on every path (clamped to the segment's last step) so that the memory
     // counter waits before their uses stay exact
     e_load<OUT>(ein, vw, it + 3 < ns ? it + 3 : ns - 1, e_voff, e_boff);
+    KDA_STAMP(p, 8 + we, it + 2, 2);
     if (COR && it >= 0)   // step it's record: the slot after step it + 2's
       transition_step(sm.rec[slotE == kRecSlots - 1 ? 0 : slotE + 1], M, qdst + it * (int64_t)kQtStep + we * 1024 + lane * 16,
                       lane);
+    KDA_STAMP(p, 8 + we, it + 2, 3);
     block_barrier();
+    KDA_STAMP(p, 8 + we, it + 2, 4);
     if (doE) {
       const Modes md = GK != kGatePlain ? step_modes(sm, p, s0 + it + 2) : Modes{0u, 0u};
       // the midpoint operands in a copy of their own, so that the common step runs the plain one
@@ -718,6 +739,7 @@ __device__ __forceinline__ void e_loop(FusedShared& sm, const Params& p, const V
         e_second<OUT, CC, true>(sm, ekeep, p, s0 + it + 2, recE, opsE, opsF, md, we, ln);
       else
         e_second<OUT, CC, false>(sm, ekeep, p, s0 + it + 2, recE, opsE, opsF, md, we, ln);
+      KDA_STAMP(p, 8 + we, it + 2, 5);
       if (GK != kGatePlain && __builtin_expect(md.pw != 0u, 0))
         pairwise_blocks<OUT, true>(sm, &ekeep, recE, opsF, md.pw, we, ln, tid);
     }
@@ -863,6 +885,7 @@ __device__ __forceinline__ void fused_part(FusedShared& sm, const Params& p, int
     unsigned char* recE = sm.rec[slotE];   // step it + 2
     unsigned char* opsF = sm.ops[(it + 3) & 1];           // step it + 1
     block_barrier();
+    KDA_STAMP(p, w, it + 2, 0);
     const int ln = opaque(lane);
     const int sl = slot16(ln);
     const bool low4 = MR == kMNone && w < 4;   // wavefronts 0-3 (the copies with M are wavefronts 4-7)
@@ -963,6 +986,7 @@ __device__ __forceinline__ void fused_part(FusedShared& sm, const Params& p, int
         }
       }
     }
+    KDA_STAMP(p, w, it + 2, 1);
     if (MR == kMFirst && doC)
       transition_step(recC, M, qdst + it * (int64_t)kQtStep + mslice * 1024 + lane * 16, lane);
     // ---- the causal tiles of step it + 1 (their chunk flags are in its information record)
@@ -977,7 +1001,9 @@ __device__ __forceinline__ void fused_part(FusedShared& sm, const Params& p, int
 #pragma unroll
       for (int i = 0; i < 2; ++i) vq[i] = v_load16(vw, sn, 8 * w + 4 * i + (lane >> 4), lane & 15);
     }
+    KDA_STAMP(p, w, it + 2, 2);
     block_barrier();
+    KDA_STAMP(p, w, it + 2, 3);
     // ---- second half: o of step it out of the stage as whole rows (wavefronts 0-3, eight rows each,
     // 16 bytes per lane: 256 contiguous bytes per row), per-pair blocks of step it + 2 (if any), T of
     // step it + 1
@@ -1000,7 +1026,9 @@ __device__ __forceinline__ void fused_part(FusedShared& sm, const Params& p, int
     }
     // T of step it + 1 first: it shares nothing with the per-pair blocks, so on a flagged step it
     // overlaps the E stage instead of following the per-pair barriers
+    KDA_STAMP(p, w, it + 2, 4);
     if (doS && w >= 6 && MR != kMSecond) solve_block(sm, recS, (int)((it + 1) & 1), w - 6, ln);
+    KDA_STAMP(p, w, it + 2, 5);
     if (GK != kGatePlain && doE) {
       const uint32_t pwmask = step_modes(sm, p, s0 + it + 2).pw;
       if (__builtin_expect(pwmask != 0u, 0)) pairwise_blocks<OUT, false>(sm, nullptr, recE, opsF, pwmask, 0, ln, tid);

@@ -3,6 +3,7 @@
 // returns its error code without touching the device.
 #include <cmath>
 #include <cstdio>
+#include <cstdlib>
 #include <cstring>
 
 #include "kda_internal.h"
@@ -187,6 +188,16 @@ int kda_chunk_fwd_ex(const void* q, const void* k, const void* v, const void* w,
   if (path >= kda::kModeFused && !kda::mfma_seg_steps_ok(T, p.seg_steps)) return KDA_ERR_ARG;
   const size_t need_ws = workspace_for(shape, path, p.seg_steps);
   if (need_ws > 0 && (!workspace || workspace_bytes < need_ws)) return KDA_ERR_ARG;
+#if KDA_PHASE_STAMPS
+  // phase-stamp build: the segment pass's workgroup KDA_STAMP_BLOCK stamps into the workspace's last
+  // kStampBytes, which the matrix-core paths' workspace size includes in this build
+  {
+    const char* sb = std::getenv("KDA_STAMP_BLOCK");
+    const bool room = path >= kda::kModeFused && workspace && workspace_bytes >= (size_t)kda::kStampBytes;
+    p.stamp_off = room ? (int64_t)workspace_bytes - kda::kStampBytes : -1;
+    p.stamp_block = (room && sb) ? std::atoi(sb) : -1;
+  }
+#endif
 
   // ---- launches (first HIP call of the entry point)
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);

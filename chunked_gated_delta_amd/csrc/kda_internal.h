@@ -28,8 +28,21 @@ struct Params {
   int disable_fallback, force_fallback;
   int chunk;           // tokens per chunk: 16 (every path), 32 or 64 (the vector path)
   int64_t seg_steps;   // matrix-core path: steps of 32 tokens per segment, 0 = automatic
+#if KDA_PHASE_STAMPS
+  // the phase-stamp build (libkda_stamps.so) only: workgroup `stamp_block` of the segment pass writes
+  // s_memtime stamps to the workspace at byte offset stamp_off (-1: none)
+  int64_t stamp_off;
+  int stamp_block;
+#endif
   __host__ __device__ int64_t n_chunks() const { return (T + kChunk - 1) / kChunk; }
 };
+
+#if KDA_PHASE_STAMPS
+// stamps of the segment pass: per wavefront, per interval (the first kStampSteps), kStampK phase
+// boundaries, 8 bytes each, at the end of the workspace
+constexpr int kStampSteps = 48, kStampK = 6;
+constexpr int64_t kStampBytes = 16 * kStampSteps * kStampK * 8;
+#endif
 
 // Recurrent decode step (state in place)
 struct DecodeParams {

@@ -375,9 +375,14 @@ hipError_t launch_correct(const Params& p, hipStream_t s, int64_t n_steps, const
 size_t mfma_workspace_bytes(int64_t B, int64_t H, int64_t T, int64_t dk, int64_t dv, int mode, int64_t seg_steps) {
   if (dk != D || dv != D || T <= 0) return 0;
   const SegPlan sg = make_plan(B * H, T, seg_steps, mode);
-  if (sg.P == 1) return 0;   // a one-segment plan keeps nothing between kernels
-  if (mode == kModeCorr) return (size_t)(sg.off_q + B * H * n_steps_of(T) * (int64_t)kQtStep);
-  return (size_t)(sg.off_s + B * H * sg.P * (int64_t)kSegState);
+#if KDA_PHASE_STAMPS
+  const int64_t extra = kStampBytes;   // the stamps follow the plan's blocks
+#else
+  const int64_t extra = 0;
+#endif
+  if (sg.P == 1) return (size_t)extra;   // a one-segment plan keeps nothing between kernels
+  if (mode == kModeCorr) return (size_t)(sg.off_q + B * H * n_steps_of(T) * (int64_t)kQtStep + extra);
+  return (size_t)(sg.off_s + B * H * sg.P * (int64_t)kSegState + extra);
 }
 
 bool mfma_seg_steps_ok(int64_t T, int64_t seg_steps) {
