@@ -165,9 +165,10 @@ KDA_API int kda_chunk_fwd_ex(const void* q, const void* k, const void* v, const 
 /* Size of the static device array kda_chunk_fwd_noalloc takes its scratch from: 64 MiB per GPU the
  * library runs on, held from the first call on that GPU until the process ends.  It holds the fused
  * path's segment plan (which the entry point takes where the automatic path is the corrected one) of
- * up to 341 (b, h, segment) triples of 192 KiB, e.g. B*H = 16 heads at any T below 2^23 (17 segments
- * each) or B*H = 32 (9 segments each); the plan needs none (and any shape is accepted) where it keeps
- * one segment per sequence or takes the vector path. */
+ * up to 341 (b, h, segment) triples of 192 KiB: the plan holds at most 256 + B*H of them below 129
+ * heads (e.g. 16 heads: 17 segments each at any length), so every B*H up to 113 fits; it keeps none
+ * (and any shape is accepted) where it has one segment per sequence (B*H >= 129, or short sequences)
+ * or takes the vector path; 114 to 128 heads fit only where short sequences limit the segments. */
 #define KDA_NOALLOC_SCRATCH_BYTES (64u * 1024u * 1024u)
 
 /* Forward pass that allocates nothing, for callers that cannot allocate device memory at call time

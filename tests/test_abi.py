@@ -286,3 +286,10 @@ def test_noalloc_rejects_calls_beyond_its_scratch():
     fused = lambda sh: lib.kda_workspace_bytes_ex(ctypes.byref(sh), 16, ctypes.byref(KdaOpts(0, 0, 3, 0, None, None)))
     assert 0 < fused(headline) <= _lib.NOALLOC_SCRATCH_BYTES < lib.kda_workspace_bytes(ctypes.byref(headline), 16)
     assert fused(big) > _lib.NOALLOC_SCRATCH_BYTES
+    # every head count up to 113 fits at any length (the plan holds at most 256 + B*H segment triples),
+    # 114 does not, and from 129 heads on the plan has one segment per sequence and keeps nothing
+    for H in (1, 16, 32, 85, 100, 113):
+        for T in (65536, 1 << 20):
+            assert fused(shape(B=1, H=H, T=T)) <= _lib.NOALLOC_SCRATCH_BYTES, (H, T)
+    assert fused(shape(B=1, H=114, T=65536)) > _lib.NOALLOC_SCRATCH_BYTES
+    assert fused(shape(B=1, H=129, T=65536)) == fused(shape(B=3, H=100, T=1 << 20)) == 0
