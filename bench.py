@@ -492,6 +492,60 @@ def phase_stamps(args):
         print(f"wave {w:2d}: " + "  ".join(f"{l}={m}" for l, m in zip(lab, med)), flush=True)
 
 
+def phase_stamps_bwd(args):
+    """--mode bwd --phase-stamps BLOCK: the backward through libkda_stamps.so, in which lane 0 of every
+    wavefront of the chain kernel's workgroup BLOCK (blocks below B*H*dv/16 run the forward chain, the
+    rest the reverse one) records the shader clock at four points of each of the first 48 chunks.
+    After `--warmup` calls one more call is stamped, and the median over chunks 6-46 of each phase's
+    length (shader-clock cycles) is printed per wavefront.  Compute wavefronts (0-3 at dk = 128): work1
+    (the state store, the chunk's partial product and its LDS write), barrier, work2 (summing the
+    partials, the next chunk's operands, the update).  Loader wavefronts: landed (the wait until the
+    next chunk's copies have landed), barrier, issue (issuing the copies of a chunk kDepth ahead)."""
+    os.environ["KDA_LIB_PATH"] = os.path.join(ROOT, "chunked_gated_delta_amd", "libkda_stamps.so")
+    os.environ["KDA_STAMP_BLOCK"] = str(args.phase_stamps)
+    import statistics
+    import torch
+    from chunked_gated_delta_amd import chunk_bwd
+    from chunked_gated_delta_amd import inputs as gen
+    wl = gen.WORKLOADS[args.workload]
+    if args.heads:
+        wl = wl.with_(H=args.heads)
+    inp = gen.make_torch(wl, seed=args.seed, device="cuda")
+    g = torch.Generator(device="cuda").manual_seed(args.seed + 1)
+    dO = torch.randn((wl.B, wl.H, wl.T, wl.dv), generator=g, device="cuda").to(gen.torch_dtype(wl.dtype))
+    dSf = torch.randn((wl.B, wl.H, wl.dk, wl.dv), generator=g, device="cuda")
+    q, k, v, w, beta, S0 = (inp[n] for n in ("q", "k", "v", "w", "beta", "S0"))
+    ws_n = gen_bwd_ws(wl)
+    ksteps, kk, nwaves = 48, 6, 16
+    stamp_bytes = nwaves * ksteps * kk * 8
+    ws = torch.zeros(ws_n, dtype=torch.uint8, device="cuda")
+    for _ in range(max(1, args.warmup)):
+        chunk_bwd(q, k, v, w, beta, dO, S0=S0, dS_final=dSf, g_min=wl.g_min, workspace=ws)
+    torch.cuda.synchronize()
+    ws[ws_n - stamp_bytes:].zero_()
+    chunk_bwd(q, k, v, w, beta, dO, S0=S0, dS_final=dSf, g_min=wl.g_min, workspace=ws)
+    torch.cuda.synchronize()
+    pr = ws[ws_n - stamp_bytes:].view(torch.int64).cpu().tolist()
+    nchain = wl.B * wl.H * (wl.dv // 16)
+    nw = wl.dk // 32
+    kind = "forward" if args.phase_stamps < nchain else "reverse"
+    print(f"phase stamps: backward of {wl.name} (B{wl.B} H{wl.H} T{wl.T}), chain workgroup {args.phase_stamps} "
+          f"({kind} chain), median shader-clock cycles per 16-token chunk over chunks 6-46", flush=True)
+    for wv in range(nwaves):
+        rows = []
+        for n in range(6, ksteps - 1):
+            a = pr[(wv * ksteps + n) * kk:(wv * ksteps + n) * kk + 4]
+            nxt = pr[(wv * ksteps + n + 1) * kk]
+            if 0 in a or nxt == 0:
+                continue
+            rows.append([a[1] - a[0], a[2] - a[1], a[3] - a[2], nxt - a[3], nxt - a[0]])
+        if not rows:
+            continue
+        med = [int(statistics.median(c)) for c in zip(*rows)]
+        lab = ["work1", "barrier", "work2", "rest", "chunk"] if wv < nw else ["landed", "barrier", "issue", "rest", "chunk"]
+        print(f"wave {wv:2d}: " + "  ".join(f"{l}={m}" for l, m in zip(lab, med)), flush=True)
+
+
 def oracle_threads(wl) -> int:
     try:
         cores = len(os.sched_getaffinity(0))
@@ -562,7 +616,7 @@ def main():
         return
 
     if args.phase_stamps is not None:
-        phase_stamps(args)
+        (phase_stamps_bwd if args.mode == "bwd" else phase_stamps)(args)
         return
 
     if args.gpus != 1:

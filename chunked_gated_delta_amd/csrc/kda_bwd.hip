@@ -33,6 +33,8 @@
 //   grad   (one per chunk)                      all gradients of the chunk, written once (no atomics)
 // Only the chains are sequential; they are independent of each other, and each does two small
 // contractions per chunk (three in the reverse one).
+#include <cstdlib>
+
 #include "kda_internal.h"
 
 namespace kda {
@@ -423,6 +425,20 @@ struct ChainSlot {
   static constexpr int NI = (UNITS + 63) / 64;                    // wave instructions per chunk
 };
 
+// Phase stamps of one chain workgroup (the phase-stamp build, libkda_stamps.so, only; the product
+// build compiles the calls away): lane 0 of wavefront w records the shader clock at boundary k of step
+// n into the end of the workspace.
+#if KDA_PHASE_STAMPS
+__device__ __forceinline__ void bwd_stamp(const Params& p, int w, int64_t n, int k) {
+  if ((int)blockIdx.x != p.stamp_block || n < 0 || n >= kStampSteps || (threadIdx.x & 63) != 0) return;
+  unsigned long long* pr = (unsigned long long*)((unsigned char*)p.workspace + p.stamp_off);
+  pr[(w * kStampSteps + n) * kStampK + k] = __builtin_amdgcn_s_memtime();
+}
+#define KDA_BWD_STAMP(p, w, n, k) bwd_stamp(p, w, n, k)
+#else
+#define KDA_BWD_STAMP(p, w, n, k) ((void)0)
+#endif
+
 template <int DK>
 struct ChainDims {
   static constexpr int RT = 2;                // 16-row tiles per compute wavefront
@@ -532,9 +548,13 @@ __device__ __forceinline__ void state_chain(const Params& p, const float* __rest
     vm_wait<PER * (kDepth - 2)>();            // chunks 0 and 1 have landed
     lds_barrier();
     for (int64_t n = 0; n < NC; ++n) {
+      KDA_BWD_STAMP(p, w, n, 0);
       vm_wait<PER * (kDepth - 2)>();          // chunk n + 1 has landed (n + 2 .. n + kDepth - 1 may not)
+      KDA_BWD_STAMP(p, w, n, 1);
       lds_barrier();
+      KDA_BWD_STAMP(p, w, n, 2);
       issue(n + kDepth);                      // into the slot chunk n used (all its reads were before)
+      KDA_BWD_STAMP(p, w, n, 3);
     }
     vm_wait<0>();
     return;
@@ -572,6 +592,7 @@ __device__ __forceinline__ void state_chain(const Params& p, const float* __rest
   lds_barrier();
   operands(0);
   for (int64_t n = 0; n < NC; ++n) {
+    KDA_BWD_STAMP(p, w, n, 0);
     const int pb = (int)(n & 1);
     float* st = states + ((bh * NC + n) * nsl + sl) * DK * CH + RT * w * 256 + lane;
 #pragma unroll
@@ -588,7 +609,9 @@ __device__ __forceinline__ void state_chain(const Params& p, const float* __rest
 #pragma unroll
     for (int b = 1; b < RT; ++b) yp[0] += yp[b];
     part[pb][w][lane] = make_float4(yp[0][0], yp[0][1], yp[0][2], yp[0][3]);
+    KDA_BWD_STAMP(p, w, n, 1);
     lds_barrier();
+    KDA_BWD_STAMP(p, w, n, 2);
     f32x4 y = u0, eg[RT];
     float kc[RT][4];
 #pragma unroll
@@ -611,6 +634,7 @@ __device__ __forceinline__ void state_chain(const Params& p, const float* __rest
     for (int s4 = 0; s4 < 4; ++s4)
 #pragma unroll
       for (int b = 0; b < RT; ++b) acc[b] = mfma4(kc[b][s4], y[s4], acc[b]);
+    KDA_BWD_STAMP(p, w, n, 3);
   }
 }
 
@@ -652,9 +676,13 @@ __device__ __forceinline__ void dstate_chain(const Params& p, const void* __rest
     vm_wait<PER * (kDepth - 2)>();
     lds_barrier();
     for (int64_t it = 0; it < NC; ++it) {
+      KDA_BWD_STAMP(p, w, it, 0);
       vm_wait<PER * (kDepth - 2)>();
+      KDA_BWD_STAMP(p, w, it, 1);
       lds_barrier();
+      KDA_BWD_STAMP(p, w, it, 2);
       issue(it + kDepth);
+      KDA_BWD_STAMP(p, w, it, 3);
     }
     vm_wait<0>();
     return;
@@ -705,6 +733,7 @@ __device__ __forceinline__ void dstate_chain(const Params& p, const void* __rest
   lds_barrier();
   operands(0);
   for (int64_t it = 0; it < NC; ++it) {
+    KDA_BWD_STAMP(p, w, it, 0);
     const int64_t n = NC - 1 - it;
     const int pb = (int)(it & 1);
     float* st = dstates + ((bh * NC + n) * nsl + sl) * DK * CH + RT * w * 256 + lane;
@@ -722,7 +751,9 @@ __device__ __forceinline__ void dstate_chain(const Params& p, const void* __rest
 #pragma unroll
     for (int b = 1; b < RT; ++b) zp[0] += zp[b];
     part[pb][w][lane] = make_float4(zp[0][0], zp[0][1], zp[0][2], zp[0][3]);
+    KDA_BWD_STAMP(p, w, it, 1);
     lds_barrier();
+    KDA_BWD_STAMP(p, w, it, 2);
     f32x4 z = z0, eg[RT], qc[RT];
     float wc[RT][4];
 #pragma unroll
@@ -746,6 +777,7 @@ __device__ __forceinline__ void dstate_chain(const Params& p, const void* __rest
     for (int s4 = 0; s4 < 4; ++s4)
 #pragma unroll
       for (int b = 0; b < RT; ++b) acc[b] = mfma4(wc[b][s4], z[s4], acc[b]);
+    KDA_BWD_STAMP(p, w, it, 3);
   }
   if (dS0) {
 #pragma unroll
@@ -1236,10 +1268,25 @@ hipError_t launch_bwd_t(const BwdParams& b, hipStream_t s) {
 
 size_t bwd_workspace_bytes(int64_t B, int64_t H, int64_t T, int64_t dk, int64_t dv) {
   const int64_t NC = (T + C - 1) / C;
-  return (size_t)(B * H * NC * (rec_floats(dk, dv) + 2 * dk * dv)) * sizeof(float);
+#if KDA_PHASE_STAMPS
+  const int64_t extra = kStampBytes;   // the chain stamps follow the states and adjoints
+#else
+  const int64_t extra = 0;
+#endif
+  return (size_t)(B * H * NC * (rec_floats(dk, dv) + 2 * dk * dv)) * sizeof(float) + (size_t)extra;
 }
 
-hipError_t launch_bwd(const BwdParams& b, hipStream_t s) {
+hipError_t launch_bwd(const BwdParams& b_in, hipStream_t s) {
+#if KDA_PHASE_STAMPS
+  // phase-stamp build: the chain workgroup KDA_STAMP_BLOCK stamps into the workspace's last kStampBytes
+  BwdParams b = b_in;
+  const char* sb = std::getenv("KDA_STAMP_BLOCK");
+  const bool room = b.p.workspace && b.p.workspace_bytes >= (size_t)kStampBytes;
+  b.p.stamp_off = room ? (int64_t)b.p.workspace_bytes - kStampBytes : -1;
+  b.p.stamp_block = (room && sb) ? std::atoi(sb) : -1;
+#else
+  const BwdParams& b = b_in;
+#endif
   return b.p.dtype == KDA_DTYPE_BF16 ? launch_bwd_t<uint16_t>(b, s) : launch_bwd_t<float>(b, s);
 }
 
