@@ -503,6 +503,7 @@ def phase_stamps_bwd(args):
     next chunk's copies have landed), barrier, issue (issuing the copies of a chunk kDepth ahead)."""
     os.environ["KDA_LIB_PATH"] = os.path.join(ROOT, "chunked_gated_delta_amd", "libkda_stamps.so")
     os.environ["KDA_STAMP_BLOCK"] = str(args.phase_stamps)
+    os.environ["KDA_STAMP_KERNEL"] = "grad" if args.stamp_grad else "chain"
     import statistics
     import torch
     from chunked_gated_delta_amd import chunk_bwd
@@ -526,6 +527,9 @@ def phase_stamps_bwd(args):
     chunk_bwd(q, k, v, w, beta, dO, S0=S0, dS_final=dSf, g_min=wl.g_min, workspace=ws)
     torch.cuda.synchronize()
     pr = ws[ws_n - stamp_bytes:].view(torch.int64).cpu().tolist()
+    if args.stamp_grad:
+        grad_stamps(wl, args.phase_stamps, pr, ksteps, kk)
+        return
     nchain = wl.B * wl.H * (wl.dv // 16)
     nw = wl.dk // 32
     kind = "forward" if args.phase_stamps < nchain else "reverse"
@@ -544,6 +548,45 @@ def phase_stamps_bwd(args):
         med = [int(statistics.median(c)) for c in zip(*rows)]
         lab = ["work1", "barrier", "work2", "rest", "chunk"] if wv < nw else ["landed", "barrier", "issue", "rest", "chunk"]
         print(f"wave {wv:2d}: " + "  ".join(f"{l}={m}" for l, m in zip(lab, med)), flush=True)
+
+
+def grad_stamps(wl, block, pr, ksteps, kk):
+    """Per wavefront of the gradient kernel's workgroup `block` (one per 16-token chunk): the setup
+    (loads: issuing the chunk's w, v and dO loads; setup: the chunk's G, X, P and T; operands: the
+    first products' A operands; wait: until the first S and dS' tiles have landed), the median over
+    the value tiles of each tile phase (partial: the tile's K = dk partial products; bar1; single: E,
+    U, dU, dR and dv on one wavefront each; bar2; products: the K = 16 products, dT, dP and dbeta;
+    wait: until the next tile pair has landed, with the barrier), then the epilogue (dA: dT and dP
+    out of the accumulators, T^T dT, dA and dbeta; pairs: the pair terms of X and P; scalings: the
+    K = 16 products through the scalings of Qbar, Kbar and Ktil; outputs: dg, dw, dq and dk)."""
+    import statistics
+    nc = (wl.T + 15) // 16
+
+    def at(wv, n, k):
+        return pr[(wv * ksteps + n) * kk + k]
+
+    print(f"phase stamps: backward of {wl.name} (B{wl.B} H{wl.H} T{wl.T}), gradient workgroup {block} "
+          f"(head {block // nc}, chunk {block % nc}), shader-clock cycles", flush=True)
+    ntile = wl.dv // 16
+    lab = ["partial", "bar1", "single", "bar2", "products", "wait", "tile"]
+    for wv in range(8):
+        s = [at(wv, 8, k) for k in range(5)]
+        if 0 in s:
+            continue
+        rows = []
+        for t in range(ntile):
+            a = [at(wv, t, k) for k in range(6)]
+            nxt = at(wv, t + 1, 0) if t + 1 < ntile else at(wv, 9, 0)
+            if 0 in a or nxt == 0:
+                continue
+            rows.append([a[1] - a[0], a[2] - a[1], a[3] - a[2], a[4] - a[3], a[5] - a[4], nxt - a[5], nxt - a[0]])
+        med = [int(statistics.median(c)) for c in zip(*rows)] if rows else []
+        e = [at(wv, 9, k) for k in range(5)]
+        ep = (f"dA={e[1] - e[0]} pairs={e[2] - e[1]} scalings={e[3] - e[2]} outputs={e[4] - e[3]} "
+              f"total={e[4] - s[0]}") if 0 not in e else "-"
+        print(f"wave {wv}: loads={s[1] - s[0]} setup={s[2] - s[1]} operands={s[3] - s[2]} wait={s[4] - s[3]} | "
+              f"tiles (median of {len(rows)}): " + " ".join(f"{n}={m}" for n, m in zip(lab, med)) +
+              f" | epilogue: {ep}", flush=True)
 
 
 def oracle_threads(wl) -> int:
@@ -594,6 +637,9 @@ def main():
     ap.add_argument("--force-fallback", action="store_true",
                     help="every chunk takes a flagged chunk's handling (midpoint tiles or per-pair factors)")
     ap.add_argument("--force-pairwise", action="store_true", help="every chunk takes the per-pair factors")
+    ap.add_argument("--stamp-grad", action="store_true",
+                    help="with --mode bwd --phase-stamps BLOCK: stamp the gradient kernel's workgroup BLOCK "
+                         "instead of the chain kernel's")
     ap.add_argument("--heads", type=int, default=0,
                     help="run the workload with this many heads instead of its own (0: the workload's)")
     ap.add_argument("--seg-steps", type=int, default=0,

@@ -34,6 +34,7 @@
 // Only the chains are sequential; they are independent of each other, and each does two small
 // contractions per chunk (three in the reverse one).
 #include <cstdlib>
+#include <cstring>
 
 #include "kda_internal.h"
 
@@ -427,16 +428,21 @@ struct ChainSlot {
 
 // Phase stamps of one chain workgroup (the phase-stamp build, libkda_stamps.so, only; the product
 // build compiles the calls away): lane 0 of wavefront w records the shader clock at boundary k of step
-// n into the end of the workspace.
+// n into the end of the workspace.  Kernel 0 is the chain kernel (steps: chunks), 1 the gradient
+// kernel (steps 0-7: value tiles, 8: the setup, 9: the epilogue).
 #if KDA_PHASE_STAMPS
-__device__ __forceinline__ void bwd_stamp(const Params& p, int w, int64_t n, int k) {
-  if ((int)blockIdx.x != p.stamp_block || n < 0 || n >= kStampSteps || (threadIdx.x & 63) != 0) return;
+__device__ __forceinline__ void bwd_stamp(const Params& p, int kernel, int w, int64_t n, int k) {
+  if (p.stamp_kernel != kernel || (int)blockIdx.x != p.stamp_block || n < 0 || n >= kStampSteps ||
+      (threadIdx.x & 63) != 0)
+    return;
   unsigned long long* pr = (unsigned long long*)((unsigned char*)p.workspace + p.stamp_off);
   pr[(w * kStampSteps + n) * kStampK + k] = __builtin_amdgcn_s_memtime();
 }
-#define KDA_BWD_STAMP(p, w, n, k) bwd_stamp(p, w, n, k)
+#define KDA_BWD_STAMP(p, w, n, k) bwd_stamp(p, 0, w, n, k)
+#define KDA_GRAD_STAMP(p, w, n, k) bwd_stamp(p, 1, w, n, k)
 #else
 #define KDA_BWD_STAMP(p, w, n, k) ((void)0)
+#define KDA_GRAD_STAMP(p, w, n, k) ((void)0)
 #endif
 
 template <int DK>
@@ -856,6 +862,7 @@ __global__ __launch_bounds__(NTG) __attribute__((amdgpu_waves_per_eu(4, 4))) voi
   const TIn* dO = (const TIn*)dO_in + bh * T * dv;
   const float* Sg = states + (bh * NC + n) * DK * dv;      // nsl [dk][16] blocks in stored order
   const float* dSg = dstates + (bh * NC + n) * DK * dv;
+  KDA_GRAD_STAMP(p, w, 8, 0);
 
   auto copy_tile = [&](int t, int b) {          // S and dS' tiles t into buffer b
     float4* dst = reinterpret_cast<float4*>(sm.u.tile[b][0]);
@@ -890,7 +897,9 @@ __global__ __launch_bounds__(NTG) __attribute__((amdgpu_waves_per_eu(4, 4))) voi
     vr[t] = ok ? x : 0.f;
     orr[t] = ok ? y : 0.f;
   }
+  KDA_GRAD_STAMP(p, w, 8, 1);
   chunk_setup<TIn, DK, NTG>(sm.cc, &sm.v.part[0][0][0], p, bh, n, len);   // part: 2 * 4 * 256 floats
+  KDA_GRAD_STAMP(p, w, 8, 2);
 
   // A operands of the K = dk products: wavefronts 0..3 take Kbar, 4..7 Ktil, on key blocks wq, wq + 4
   const bool eW = w < 4;
@@ -916,11 +925,14 @@ __global__ __launch_bounds__(NTG) __attribute__((amdgpu_waves_per_eu(4, 4))) voi
   float accT = 0.f, accRS = 0.f;
   f32x4 tdp = {0.f, 0.f, 0.f, 0.f};   // wavefront 6: dT (before the diag(beta) scaling), 7: dP
 
+  KDA_GRAD_STAMP(p, w, 8, 3);
   vm_wait<0>();
   lds_barrier();
+  KDA_GRAD_STAMP(p, w, 8, 4);
 #pragma unroll
   for (int t = 0; t < MAXT; ++t) {
     if (t >= nsl) break;
+    KDA_GRAD_STAMP(p, w, t, 0);
     const int b = t & 1;
     const float* St = sm.u.tile[b][0];
     const float* dSt = sm.u.tile[b][1];
@@ -943,7 +955,9 @@ __global__ __launch_bounds__(NTG) __attribute__((amdgpu_waves_per_eu(4, 4))) voi
 #pragma unroll
       for (int i = 0; i < 4; ++i) sm.v.part[w][4 * g + i][col] = pp[i];
     }
+    KDA_GRAD_STAMP(p, w, t, 1);
     lds_barrier();
+    KDA_GRAD_STAMP(p, w, t, 2);
     // One wavefront each, on 16 x 16 tiles in the accumulator layout (lane: rows 4g + i, column col), so
     // that the first product's result is the second one's B operand (K index 4g + s at step s):
     if (w == 0) {          // E = V - Kbar S;  U = T diag(beta) E
@@ -995,7 +1009,9 @@ __global__ __launch_bounds__(NTG) __attribute__((amdgpu_waves_per_eu(4, 4))) voi
         accRS += a.x * bq.x + a.y * bq.y + a.z * bq.z + a.w * bq.w;
       }
     }
+    KDA_GRAD_STAMP(p, w, t, 3);
     lds_barrier();
+    KDA_GRAD_STAMP(p, w, t, 4);
     // K = 16 products: task id = w + 8 j -> (product id / NCB, key block id % NCB)
 #pragma unroll
     for (int j = 0; j < 3; ++j) {
@@ -1032,9 +1048,11 @@ __global__ __launch_bounds__(NTG) __attribute__((amdgpu_waves_per_eu(4, 4))) voi
       }
       accT += a;
     }
+    KDA_GRAD_STAMP(p, w, t, 5);
     vm_wait<0>();      // the next tile pair has landed
     lds_barrier();
   }
+  KDA_GRAD_STAMP(p, w, 9, 0);
 
   if ((w == 2 || w == 3) && tid - 128 < DK) sm.rs[tid - 128] = accRS;
   // wavefronts 6 and 7 hold dT and dP (lane: rows 4g + i, column col), lower parts kept;
@@ -1071,6 +1089,7 @@ __global__ __launch_bounds__(NTG) __attribute__((amdgpu_waves_per_eu(4, 4))) voi
     for (int j = 0; j < C; ++j) acc += sm.dT[r][j] * sm.cc.X[r][j];   // dA is strictly lower
     if (r < len) dbeta[bh * T + t0 + r] = acc;
   }
+  KDA_GRAD_STAMP(p, w, 9, 1);
   float (*gq)[DK] = sm.u.g3[0];
   float (*gk)[DK] = sm.u.g3[1];
   float (*gG)[DK] = sm.u.g3[2];
@@ -1143,6 +1162,7 @@ __global__ __launch_bounds__(NTG) __attribute__((amdgpu_waves_per_eu(4, 4))) voi
     }
   }
   lds_barrier();
+  KDA_GRAD_STAMP(p, w, 9, 2);
   // the K = 16 products through the scalings of Qbar, Kbar, Ktil (lane: rows 4g + i, key 16 cb + col)
   if (NCB == 8) {   // wavefront w holds all three products of key block w: plain updates
     const int c = 16 * w + col;
@@ -1191,6 +1211,7 @@ __global__ __launch_bounds__(NTG) __attribute__((amdgpu_waves_per_eu(4, 4))) voi
   }
   }
   lds_barrier();
+  KDA_GRAD_STAMP(p, w, 9, 3);
   {   // dg and the outputs; NPC threads per channel, thread p of channel c owning rows p*RPT .. p*RPT + RPT-1:
       // dg_u = e^{Gam} rowsum(dS' o S) + sum_{r >= u} dG_r + sum_{r < u} (dKtil o Ktil)_r
     const int c = tid / NPC, pp = tid % NPC, r0 = pp * RPT;
@@ -1231,6 +1252,7 @@ __global__ __launch_bounds__(NTG) __attribute__((amdgpu_waves_per_eu(4, 4))) voi
       }
     }
   }
+  KDA_GRAD_STAMP(p, w, 9, 4);
 }
 
 template <typename TIn, int DK>
@@ -1284,6 +1306,8 @@ hipError_t launch_bwd(const BwdParams& b_in, hipStream_t s) {
   const bool room = b.p.workspace && b.p.workspace_bytes >= (size_t)kStampBytes;
   b.p.stamp_off = room ? (int64_t)b.p.workspace_bytes - kStampBytes : -1;
   b.p.stamp_block = (room && sb) ? std::atoi(sb) : -1;
+  const char* sk = std::getenv("KDA_STAMP_KERNEL");   // "grad": the gradient kernel's workgroup stamps
+  b.p.stamp_kernel = (sk && std::strcmp(sk, "grad") == 0) ? 1 : 0;
 #else
   const BwdParams& b = b_in;
 #endif

@@ -196,6 +196,7 @@ int kda_chunk_fwd_ex(const void* q, const void* k, const void* v, const void* w,
     const bool room = path >= kda::kModeFused && workspace && workspace_bytes >= (size_t)kda::kStampBytes;
     p.stamp_off = room ? (int64_t)workspace_bytes - kda::kStampBytes : -1;
     p.stamp_block = (room && sb) ? std::atoi(sb) : -1;
+    p.stamp_kernel = 0;
   }
 #endif
 

@@ -30,9 +30,11 @@ struct Params {
   int64_t seg_steps;   // matrix-core path: steps of 32 tokens per segment, 0 = automatic
 #if KDA_PHASE_STAMPS
   // the phase-stamp build (libkda_stamps.so) only: workgroup `stamp_block` of the segment pass writes
-  // s_memtime stamps to the workspace at byte offset stamp_off (-1: none)
+  // s_memtime stamps to the workspace at byte offset stamp_off (-1: none); in the backward,
+  // stamp_kernel picks the kernel whose workgroup stamps (0: the chains, 1: the gradient kernel)
   int64_t stamp_off;
   int stamp_block;
+  int stamp_kernel;
 #endif
   __host__ __device__ int64_t n_chunks() const { return (T + kChunk - 1) / kChunk; }
 };
