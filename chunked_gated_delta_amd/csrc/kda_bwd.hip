@@ -835,7 +835,6 @@ struct GradShared {
   float dT[C][C + 1], dP[C][C + 1];
   union {
     float Vt[C][CH + 4];                  // the value tile, during the tile loop
-    float M[C][C + 1];                    // T^T dT, after it
   } vt;
   float rs[DK];                           // rowsum(dS' o S) per channel
 };
@@ -1057,29 +1056,24 @@ __global__ __launch_bounds__(NTG) __attribute__((amdgpu_waves_per_eu(4, 4))) voi
   if ((w == 2 || w == 3) && tid - 128 < DK) sm.rs[tid - 128] = accRS;
   // wavefronts 6 and 7 hold dT and dP (lane: rows 4g + i, column col), lower parts kept;
   // tid 256..271: accT = dbeta share
-  if (w >= 6) {
+  if (w == 6) {   // dA = -(M T^T) with M = T^T dT, strictly lower, into dT: two fp32 products on this wavefront
+    float at[4];  // dT[4g + s][col], the A operand of M^T = dT^T T at step s
+#pragma unroll
+    for (int s4 = 0; s4 < 4; ++s4) at[s4] = col <= 4 * g + s4 ? sm.cc.beta[col] * tdp[s4] : 0.f;
+    f32x4 mt = {0.f, 0.f, 0.f, 0.f};   // M^T (lane: rows 4g + i, column col), the B operand of T M^T
+#pragma unroll
+    for (int s4 = 0; s4 < 4; ++s4) mt = mfma4(at[s4], sm.cc.T[4 * g + s4][col], mt);
+    f32x4 d = {0.f, 0.f, 0.f, 0.f};    // T M^T = (M T^T)^T: d[i] = (M T^T)[col][4g + i]
+#pragma unroll
+    for (int s4 = 0; s4 < 4; ++s4) d = mfma4(sm.cc.T[col][4 * g + s4], mt[s4], d);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) sm.dT[col][4 * g + i] = 4 * g + i < col ? -d[i] : 0.f;
+  } else if (w == 7) {
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int r = 4 * g + i;
-      if (w == 6) sm.dT[r][col] = col <= r ? sm.cc.beta[col] * tdp[i] : 0.f;
-      else sm.dP[r][col] = col <= r ? tdp[i] : 0.f;
+      sm.dP[r][col] = col <= r ? tdp[i] : 0.f;
     }
-  }
-  lds_barrier();
-  if (tid < C * C) {   // M = T^T dT
-    const int a = tid / C, bb = tid % C;
-    float acc = 0.f;
-#pragma unroll
-    for (int r = 0; r < C; ++r) acc += sm.cc.T[r][a] * sm.dT[r][bb];
-    sm.vt.M[a][bb] = acc;
-  }
-  lds_barrier();
-  if (tid < C * C) {   // dA = -(M T^T), strictly lower, into dT
-    const int a = tid / C, bb = tid % C;
-    float acc = 0.f;
-#pragma unroll
-    for (int j = 0; j < C; ++j) acc += sm.vt.M[a][j] * sm.cc.T[bb][j];
-    sm.dT[a][bb] = bb < a ? -acc : 0.f;
   }
   lds_barrier();
   if (tid >= 256 && tid < 256 + C) {
