@@ -552,7 +552,9 @@ def phase_stamps_bwd(args):
 
 def grad_stamps(wl, block, pr, ksteps, kk):
     """Per wavefront of the gradient kernel's workgroup `block` (one per 16-token chunk): the setup
-    (loads: issuing the chunk's w, v and dO loads; setup: the chunk's G, X, P and T; operands: the
+    (loads: issuing the chunk's w, v and dO loads; setup: the chunk's G, X, P and T, split into the
+    loads of q, k, w and beta with the gates written to LDS, the barrier, the prefix, X and P, the
+    sums of their partials and the solve for T; operands: the
     first products' A operands; wait: until the first S and dS' tiles have landed), the median over
     the value tiles of each tile phase (partial: the tile's K = dk partial products; bar1; single: E,
     U, dU, dR and dv on one wavefront each; bar2; products: the K = 16 products, dT, dP and dbeta;
@@ -584,7 +586,10 @@ def grad_stamps(wl, block, pr, ksteps, kk):
         e = [at(wv, 9, k) for k in range(5)]
         ep = (f"dA={e[1] - e[0]} pairs={e[2] - e[1]} scalings={e[3] - e[2]} outputs={e[4] - e[3]} "
               f"total={e[4] - s[0]}") if 0 not in e else "-"
-        print(f"wave {wv}: loads={s[1] - s[0]} setup={s[2] - s[1]} operands={s[3] - s[2]} wait={s[4] - s[3]} | "
+        c = [at(wv, 10, k) for k in range(5)]
+        sub = (f" (inputs={c[0] - s[1]} bar={c[1] - c[0]} prefix={c[2] - c[1]} XP={c[3] - c[2]} sums={c[4] - c[3]} "
+               f"T={s[2] - c[4]})") if 0 not in c else ""
+        print(f"wave {wv}: loads={s[1] - s[0]} setup={s[2] - s[1]}{sub} operands={s[3] - s[2]} wait={s[4] - s[3]} | "
               f"tiles (median of {len(rows)}): " + " ".join(f"{n}={m}" for n, m in zip(lab, med)) +
               f" | epilogue: {ep}", flush=True)
 

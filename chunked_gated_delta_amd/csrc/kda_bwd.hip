@@ -129,6 +129,26 @@ __device__ __forceinline__ void pair_of(int pr, int& r, int& j) {   // pr -> (r,
   j = pr - r * (r + 1) / 2;
 }
 
+// Phase stamps of one chain workgroup (the phase-stamp build, libkda_stamps.so, only; the product
+// build compiles the calls away): lane 0 of wavefront w records the shader clock at boundary k of step
+// n into the end of the workspace.  Kernel 0 is the chain kernel (steps: chunks), 1 the gradient
+// kernel (steps 0-7: value tiles, 8: the setup, 9: the epilogue, 10: inside the chunk setup, which
+// the prep kernel's workgroup of the same index stamps too, before the gradient kernel overwrites it).
+#if KDA_PHASE_STAMPS
+__device__ __forceinline__ void bwd_stamp(const Params& p, int kernel, int w, int64_t n, int k) {
+  if (p.stamp_kernel != kernel || (int)blockIdx.x != p.stamp_block || n < 0 || n >= kStampSteps ||
+      (threadIdx.x & 63) != 0)
+    return;
+  unsigned long long* pr = (unsigned long long*)((unsigned char*)p.workspace + p.stamp_off);
+  pr[(w * kStampSteps + n) * kStampK + k] = __builtin_amdgcn_s_memtime();
+}
+#define KDA_BWD_STAMP(p, w, n, k) bwd_stamp(p, 0, w, n, k)
+#define KDA_GRAD_STAMP(p, w, n, k) bwd_stamp(p, 1, w, n, k)
+#else
+#define KDA_BWD_STAMP(p, w, n, k) ((void)0)
+#define KDA_GRAD_STAMP(p, w, n, k) ((void)0)
+#endif
+
 // G and gam are kept in log2 units (G * log2 e), so that every factor e^{G...} is one exp2; the
 // gradients stay with respect to the natural-unit G.  Rows are padded by one float so that reads of
 // one channel across rows fall on distinct LDS banks.
@@ -138,7 +158,15 @@ struct ChunkCore {
   float gam[DK];
   float beta[C];
   float X[C][C + 1], P[C][C + 1], T[C][C + 1], Tb[C][C + 1];   // Tb = T diag(beta)
-  int dense;   // every channel's span >= -80: pair terms as products of e^{+-(G - Gam/2)} factors
+  float spanw[(DK + 63) / 64];   // per wavefront of the prefix: the smallest chunk total of its channels
+  // every channel's span >= -80: pair terms as products of e^{+-(G - Gam/2)} factors (valid after the
+  // barrier that follows the prefix)
+  __device__ __forceinline__ bool dense() const {
+    float m = spanw[0];
+#pragma unroll
+    for (int i = 1; i < (DK + 63) / 64; ++i) m = fminf(m, spanw[i]);
+    return m * kLn2B >= kSpanLimit;
+  }
 };
 
 // Loads chunk n (rows past the end are zero: k = q = beta = 0 and g = 0, which reproduces the
@@ -189,7 +217,9 @@ __device__ void chunk_setup(ChunkCore<DK>& cc, float* scratch, const Params& p, 
     }
     if (tid < C) cc.beta[tid] = tid < len ? lb : 0.f;
   }
+  KDA_GRAD_STAMP(p, tid / 64, 10, 0);
   __syncthreads();
+  KDA_GRAD_STAMP(p, tid / 64, 10, 1);
   if (tid < DK) {
     float gv[C];
 #pragma unroll
@@ -198,18 +228,18 @@ __device__ void chunk_setup(ChunkCore<DK>& cc, float* scratch, const Params& p, 
 #pragma unroll
     for (int r = 0; r < C; ++r) { g += gv[r]; cc.G[r][tid] = g; }
     cc.gam[tid] = g;
-  }
-  if (tid < 64) {   // chunk flag: the smallest span over the channels, against the limit
-    float m = 0.f;
-    for (int c = tid; c < DK; c += 64) m = fminf(m, cc.gam[c]);
+    // the chunk flag: each wavefront's smallest total over its own channels (all of them active), the
+    // minimum over the wavefronts taken after the barrier
+    float m = fminf(g, 0.f);
 #pragma unroll
-    for (int off = 32; off > 0; off >>= 1) m = fminf(m, __shfl_xor(m, off));
-    if (tid == 0) cc.dense = m * kLn2B >= kSpanLimit;
+    for (int off = (DK < 64 ? DK : 64) / 2; off > 0; off >>= 1) m = fminf(m, __shfl_xor(m, off));
+    if ((tid & 63) == 0) cc.spanw[tid >> 6] = m;
   }
   __syncthreads();
+  KDA_GRAD_STAMP(p, tid / 64, 10, 2);
   float (*xs)[C][C] = reinterpret_cast<float (*)[C][C]>(scratch);              // [4][C][C] partial sums
   float (*ps)[C][C] = reinterpret_cast<float (*)[C][C]>(scratch + 4 * C * C);
-  const bool dense = cc.dense;
+  const bool dense = cc.dense();
   if (dense) {
     // X = Kbar' Kinv'^T, P = Qbar' Kinv'^T with Kbar' = k e^{G - Gam/2}, Kinv' = k e^{Gam/2 - G} (every
     // factor at most e^{40}): wavefront wq < 4 takes key blocks wq and wq + 4, K order c = 16 cb + 4g + i
@@ -253,6 +283,7 @@ __device__ void chunk_setup(ChunkCore<DK>& cc, float* scratch, const Params& p, 
     }
   }
   __syncthreads();
+  KDA_GRAD_STAMP(p, tid / 64, 10, 3);
   {
     const int nq = dense ? 4 : NQ;
     for (int e = tid; e < 2 * C * C; e += NT) {   // X from threads 0..255, P from 256..511
@@ -266,6 +297,7 @@ __device__ void chunk_setup(ChunkCore<DK>& cc, float* scratch, const Params& p, 
     }
   }
   __syncthreads();
+  KDA_GRAD_STAMP(p, tid / 64, 10, 4);
   if (tid < 64) {
     // T = (I + A)^{-1}, A = diag(beta) X: the four lanes of quad li own row li of T, lane q of the quad
     // columns 4q .. 4q+3.  Row t of T satisfies t (I + A) = e_li, so its entries follow from the last one
@@ -426,24 +458,6 @@ struct ChainSlot {
   static constexpr int NI = (UNITS + 63) / 64;                    // wave instructions per chunk
 };
 
-// Phase stamps of one chain workgroup (the phase-stamp build, libkda_stamps.so, only; the product
-// build compiles the calls away): lane 0 of wavefront w records the shader clock at boundary k of step
-// n into the end of the workspace.  Kernel 0 is the chain kernel (steps: chunks), 1 the gradient
-// kernel (steps 0-7: value tiles, 8: the setup, 9: the epilogue).
-#if KDA_PHASE_STAMPS
-__device__ __forceinline__ void bwd_stamp(const Params& p, int kernel, int w, int64_t n, int k) {
-  if (p.stamp_kernel != kernel || (int)blockIdx.x != p.stamp_block || n < 0 || n >= kStampSteps ||
-      (threadIdx.x & 63) != 0)
-    return;
-  unsigned long long* pr = (unsigned long long*)((unsigned char*)p.workspace + p.stamp_off);
-  pr[(w * kStampSteps + n) * kStampK + k] = __builtin_amdgcn_s_memtime();
-}
-#define KDA_BWD_STAMP(p, w, n, k) bwd_stamp(p, 0, w, n, k)
-#define KDA_GRAD_STAMP(p, w, n, k) bwd_stamp(p, 1, w, n, k)
-#else
-#define KDA_BWD_STAMP(p, w, n, k) ((void)0)
-#define KDA_GRAD_STAMP(p, w, n, k) ((void)0)
-#endif
 
 template <int DK>
 struct ChainDims {
@@ -1087,7 +1101,7 @@ __global__ __launch_bounds__(NTG) __attribute__((amdgpu_waves_per_eu(4, 4))) voi
   float (*gq)[DK] = sm.u.g3[0];
   float (*gk)[DK] = sm.u.g3[1];
   float (*gG)[DK] = sm.u.g3[2];
-  if (sm.cc.dense) {
+  if (sm.cc.dense()) {
     // the pair terms as products of e^{+-(G - Gam/2)} factors (wavefront w: key channels 16w .. 16w + 15):
     //   P1 = Wa Kinv', P2 = Wp Kinv', P3 = Wa^T Kbar', P4 = Wp^T Qbar'   (Wa = diag(beta) dA, Wp = dP)
     //   dk_x = e^{G'_x} P1 + e^{-G'_x} (P3 + P4),  dq_x = e^{G'_x} P2,
