@@ -303,14 +303,23 @@ __device__ void chunk_setup(ChunkCore<DK>& cc, float* scratch, const Params& p, 
     // columns 4q .. 4q+3.  Row t of T satisfies t (I + A) = e_li, so its entries follow from the last one
     // backwards: once t_m is final (lane m/4 of the quad, broadcast inside the quad), t_k -= t_m A[m][k].
     const int li = tid >> 2, q = tid & 3;
+    // every row of X this lane needs (its four columns) and beta, read before the serial steps so
+    // that no step waits on LDS
+    float xm[C][4], bm[C];
+#pragma unroll
+    for (int m = 1; m < C; ++m) {
+      bm[m] = cc.beta[m];
+#pragma unroll
+      for (int c = 0; c < 4; ++c) xm[m][c] = cc.X[m][4 * q + c];
+    }
     float t[4];
 #pragma unroll
     for (int c = 0; c < 4; ++c) t[c] = (li == 4 * q + c) ? 1.f : 0.f;
 #pragma unroll
     for (int m = C - 1; m >= 1; --m) {
-      const float x = quad_bcast(t[m & 3], m >> 2) * cc.beta[m];
+      const float x = quad_bcast(t[m & 3], m >> 2) * bm[m];
 #pragma unroll
-      for (int c = 0; c < 4; ++c) t[c] -= x * cc.X[m][4 * q + c];   // X[m][j] = 0 for j >= m
+      for (int c = 0; c < 4; ++c) t[c] -= x * xm[m][c];   // X[m][j] = 0 for j >= m
     }
 #pragma unroll
     for (int c = 0; c < 4; ++c) {
